@@ -1,0 +1,190 @@
+/*
+ * csa.h -- C ABI of the CSA / HCA layer step for AMD Instinct MI355X (gfx950).
+ *
+ * The method is DeepSeek-V4's hybrid attention as restated in
+ * "【论文解读】DeepSeek-V4" (wkq9411.github.io), section 一(三) "混合注意力架构：CSA + HCA":
+ *   (1) compressed KV entries, (2) lightning indexer + top-k selector,
+ *   (3) shared key-value MQA, and the "其他技术细节" part (RMSNorm on queries and
+ *   KV entries, partial RoPE with the output rotated back by -t, sliding window,
+ *   attention sink).  Cited below as [CSA], [HCA] and [details].
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller (hipMalloc /
+ *     torch); the library allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous on that stream and never synchronises.
+ *   - Shapes are row-major, innermost index last.  B = sequences, T = query rows
+ *     per sequence (1 for decode).  Query row r of sequence b sits at absolute
+ *     position t = pos0[b] + r, where pos0 is a DEVICE int64 array [B].
+ *   - Compressed entry s covers tokens m*s .. m*s+m-1 and is placed at position
+ *     m*s for RoPE.  Query t sees compressed entries s < floor(t/m) ([CSA] (2),
+ *     the visibility condition of the index score), capped at the cache size.
+ *   - Errors: every call validates its arguments on the host in O(1) before any
+ *     launch and returns a csa_status; no exception or abort crosses the ABI.
+ *     CSA_ERR_LAUNCH reports a failed launch (hipGetLastError); faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Calls are reentrant; calls on different streams that share a workspace race.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_F32 = 0,               /* IEEE binary32                                                    */
+  CSA_BF16 = 1,              /* bfloat16, stored as uint16                                        */
+  CSA_FP8_E4M3_ROWSCALE = 2, /* OCP fp8 E4M3 bytes + one float32 scale per row (value = code*scale) */
+  CSA_MXFP4_E8M0_B32 = 3     /* OCP MXFP4: e2m1 pairs (element 2i in the low nibble) + one E8M0    */
+                             /* scale byte per 32 elements (value = e2m1 * 2^(scale-127))          */
+} csa_dtype;
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  CSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range              */
+  CSA_ERR_UNSUPPORTED = 3, /* valid request this build does not implement     */
+  CSA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required      */
+  CSA_ERR_LAUNCH = 5       /* the kernel launch failed                        */
+} csa_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* csa_status_string(int status);
+/* ABI revision of this header (bumped on any signature change). */
+int csa_abi_version(void);
+
+/*
+ * csa_compress -- learned per-channel softmax pooling of per-token KV rows.
+ * [CSA] (1): entry i, channel j: softmax over the 2m logits
+ *   Z^a[mi+r][j] + B^a[r][j] and Z^b[m(i-1)+r][j] + B^b[r][j]   (r = 0..m-1)
+ * and C^Comp_i[j] = sum S^a C^a + sum S^b C^b; for i = 0 the b-side is padded
+ * with -inf logits / zero values.  [HCA] (1): pass cb = zb = bias_b = NULL to pool
+ * m (= m') rows of a single stream with no overlap.
+ *
+ *   ca, cb, za, zb : [B][rows][c] in in_t (CSA_F32 or CSA_BF16); row k holds the
+ *                    token at absolute position row0_pos + k.
+ *   bias_a, bias_b : [m][c] float32.
+ *   entries        : i = first_entry .. first_entry + num_entries - 1; every row
+ *                    they read must lie inside [row0_pos, row0_pos + rows).
+ *   out            : entry e of sequence b is row (b * out_batch_stride + e) of
+ *                    [..][c] values in out_t (0 for out_batch_stride means
+ *                    num_entries).  To append into a cache [B][Nmax][c] pass
+ *                    out = cache row first_entry and out_batch_stride = Nmax.
+ *                    CSA_F32 / CSA_BF16 (round to nearest even);
+ *                    CSA_FP8_E4M3_ROWSCALE: bytes, and out_scale (float32, same
+ *                    row indexing) = amax/448, codes = RNE(x/scale) saturated;
+ *                    CSA_MXFP4_E8M0_B32: c/2 bytes per row, and out_scale (uint8,
+ *                    c/32 per row) = floor(log2 amax) - 2 + 127, codes RNE,
+ *                    saturated at 6.  out_scale is ignored for F32 / BF16.
+ * Limits: 1 <= m <= 1024, c a multiple of 4 and <= 1024 (of 32 for MXFP4).
+ */
+csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb,
+                        const float* bias_a, const float* bias_b,
+                        int B, int rows, int c, int m,
+                        int64_t row0_pos, int64_t first_entry, int num_entries,
+                        int in_t,
+                        void* out, void* out_scale, int out_t, int64_t out_batch_stride,
+                        void* stream);
+
+/*
+ * csa_index -- lightning-indexer scores ([CSA] (2), the I_{t,s} equation):
+ *   I[b][r][s] = sum_h w[b][r][h] * ReLU( q^I[b][r][h] . K^IComp[b][s] )
+ * for s < min(floor(t/m), n_max) with t = pos0[b] + r; every other s in
+ * [0, n_max) is written as -inf.  No scale, norm or RoPE is applied.
+ *
+ *   q       : [B][T][HI][cI] in qk_t (MXFP4: [B][T][HI][cI/2] bytes)
+ *   q_scale : CSA_FP8_E4M3_ROWSCALE: float32 [B][T][HI]; CSA_MXFP4_E8M0_B32:
+ *             uint8 [B][T][HI][cI/32]; NULL otherwise.
+ *   w       : float32 [B][T][HI]
+ *   k       : [B][n_max][cI] in qk_t (MXFP4: cI/2 bytes per row)
+ *   k_scale : as q_scale with rows [B][n_max].
+ *   scores  : float32 [B][T][n_max]
+ * Products run on MFMA with float32 accumulation for BF16 / FP8 / MXFP4 (row
+ * scales are applied to the float32 dot products; MXFP4 block scales inside
+ * the MFMA), and on float32 FMA for CSA_F32.
+ * Limits: F32: cI a multiple of 4, cI <= 512, HI <= 128.  BF16 / FP8 / MXFP4:
+ * cI = 128 and HI in {16, 32, 64, 128}.
+ */
+csa_status csa_index(const void* q, const void* q_scale, const float* w,
+                     const void* k, const void* k_scale,
+                     int B, int T, int HI, int cI, int64_t n_max,
+                     const int64_t* pos0, int m, int qk_t,
+                     float* scores, void* stream);
+
+/*
+ * csa_topk -- top-k selector ([CSA] (2), the C^SprsComp_t equation).
+ * Row (b, r) keeps the min(k, V) largest of scores[b][r][0 .. V) with
+ * V = min(floor((pos0[b] + r)/m), n_max).  Larger score first; equal scores
+ * (+0 and -0 are equal) go to the lower index.  idx[b][r][0..k) receives the kept
+ * indices in ascending order followed by -1 padding; vals (nullable) receives
+ * their scores (NaN-free inputs assumed; padding slots get -inf).
+ *
+ *   workspace : device memory of csa_topk_workspace_bytes(B, T, n_max, k) bytes.
+ *               It must be zero-filled before its first use; every call leaves
+ *               it zero-filled again, so one buffer serves any later call on
+ *               the same stream.
+ * Limits: 1 <= k <= 2048, n_max < 2^31.
+ */
+size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k);
+csa_status csa_topk(const float* scores, int B, int T, int64_t n_max,
+                    const int64_t* pos0, int m, int k,
+                    int32_t* idx, float* vals,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * csa_attend -- CSA core attention ([CSA] (3) shared key-value MQA and [details]).
+ * For query row (b, r) at t = pos0[b] + r and head h:
+ *   entries  E = { comp_kv[b][s] : s = idx[b][r][j] >= 0 }  (position m*s)
+ *              u { window token p : max(0, t-n_win+1) <= p <= t }  (position p)
+ *   e^ = RoPE_pos(RMSNorm_gamma_kv(e)),  q^ = RoPE_t(RMSNorm_gamma_q(q[b][r][h]))
+ *   z_j = scale * q^ . e^_j,   p_j = exp(z_j) / (sum_i exp(z_i) + exp(sink[h]))
+ *   out[b][r][h] = RoPE_{-t}( sum_j p_j e^_j )
+ * RMSNorm: x / sqrt(mean(x^2) + eps) * gamma over all c dims (gamma NULL = 1).
+ * RoPE: pairs (c-R+2i, c-R+2i+1), R = rope_dims, angle pos * rope_base^(-2i/R).
+ *
+ *   q       : [B][T][H][c] in kv_t        comp_kv : [B][n_max][c] in kv_t
+ *   idx     : int32 [B][T][k]; entries < 0 or >= n_max are skipped
+ *   win_kv  : [B][T + n_win - 1][c] in kv_t; row j holds position pos0[b]-n_win+1+j
+ *   sink    : float32 [H]     gamma_q, gamma_kv : float32 [c] or NULL
+ *   out     : [B][T][H][c] in out_t (CSA_F32 or CSA_BF16)
+ *   workspace : csa_attend_workspace_bytes(B, T, H, c, k, n_win) bytes of device
+ *               memory (no initial contents needed); may be NULL if that is 0.
+ * kv_t is CSA_F32 (float32 FMA path) or CSA_BF16 (MFMA path, float32 softmax
+ * and accumulation).  Decode (T = 1) splits each query's entry list at fixed
+ * boundaries that depend only on that query's own list and merges the parts in a
+ * fixed order, so results do not depend on B or on the other rows.
+ * Limits: c in {128, 256, 512}; rope_dims even, a multiple of 8 and <= min(c, 128);
+ * H a multiple of 16 for CSA_BF16 (any H >= 1 for CSA_F32); 1 <= k <= 2048;
+ * 1 <= n_win <= 4096.
+ */
+size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win);
+csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
+                      const float* sink, const float* gamma_q, const float* gamma_kv,
+                      int B, int T, int H, int c, int rope_dims, int k, int n_win, int64_t n_max,
+                      const int64_t* pos0, int m, float scale, float eps, float rope_base,
+                      int kv_t, void* out, int out_t,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attend -- HCA core attention ([HCA] (2)): as csa_attend, with the
+ * compressed part dense: every visible entry s < min(floor(t/m_hca), n_max) of
+ * comp_kv, each at position m_hca * s.  Same layouts, limits and workspace rule
+ * (hca_attend_workspace_bytes).
+ */
+size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win);
+csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv,
+                      const float* sink, const float* gamma_q, const float* gamma_kv,
+                      int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
+                      const int64_t* pos0, int m_hca, float scale, float eps, float rope_base,
+                      int kv_t, void* out, int out_t,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

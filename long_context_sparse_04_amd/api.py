@@ -1,0 +1,146 @@
+"""Thin torch-facing binding of the C ABI (include/csa.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of libcsa.so; these wrappers check
+that tensors are contiguous device tensors, pass their pointers and the current
+stream, and raise CSAError on a non-zero status.  bf16 data travels as
+torch.bfloat16 (bit patterns), fp8 / MXFP4 data as torch.uint8.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import CSAError
+
+FMT = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3_ROWSCALE, "mxfp4": _lib.MXFP4_E8M0_B32}
+_TORCH_FMT = {torch.float32: "f32", torch.bfloat16: "bf16"}
+
+_ws_cache: dict = {}
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CSAError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise CSAError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace(nbytes: int, device, key: str, zero: bool = False) -> torch.Tensor | None:
+    """Reusable device workspace per (key, device); zero-filled once when asked."""
+    if nbytes == 0:
+        return None
+    k = (key, str(device))
+    ws = _ws_cache.get(k)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device) if zero else torch.empty(
+            nbytes, dtype=torch.uint8, device=device)
+        _ws_cache[k] = ws
+    return ws
+
+
+def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entries, out=None, out_scale=None,
+             out_fmt=None, out_batch_stride=0, stream=None):
+    """csa_compress.  ca/za (and cb/zb for CSA) are [B][rows][c] f32 or bf16 tensors."""
+    lib = _lib.load()
+    B, rows, c = ca.shape
+    in_fmt = _TORCH_FMT[ca.dtype]
+    out_fmt = out_fmt or in_fmt
+    dev = ca.device
+    if out is None:
+        if out_fmt == "f32":
+            out = torch.empty((B, num_entries, c), dtype=torch.float32, device=dev)
+        elif out_fmt == "bf16":
+            out = torch.empty((B, num_entries, c), dtype=torch.bfloat16, device=dev)
+        elif out_fmt == "fp8":
+            out = torch.empty((B, num_entries, c), dtype=torch.uint8, device=dev)
+            out_scale = torch.empty((B, num_entries), dtype=torch.float32, device=dev)
+        else:
+            out = torch.empty((B, num_entries, c // 2), dtype=torch.uint8, device=dev)
+            out_scale = torch.empty((B, num_entries, c // 32), dtype=torch.uint8, device=dev)
+    st = lib.csa_compress(_ptr(ca), _ptr(cb), _ptr(za), _ptr(zb), _ptr(bias_a), _ptr(bias_b), B, rows, c, m,
+                          row0_pos, first_entry, num_entries, FMT[in_fmt], out.data_ptr(),
+                          None if out_scale is None else out_scale.data_ptr(), FMT[out_fmt], out_batch_stride,
+                          _stream(stream))
+    _lib.check(st, "csa_compress")
+    return out, out_scale
+
+
+def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None):
+    """csa_index.  q [B][T][HI][row], k [B][N][row]; returns float32 scores [B][T][N]."""
+    lib = _lib.load()
+    B, T, HI = q.shape[0], q.shape[1], q.shape[2]
+    cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
+    N = k.shape[1] if n_max is None else n_max
+    if scores is None:
+        scores = torch.empty((B, T, N), dtype=torch.float32, device=q.device)
+    st = lib.csa_index(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), B, T, HI, cI, N, _ptr(pos0), m,
+                       FMT[fmt], _ptr(scores), _stream(stream))
+    _lib.check(st, "csa_index")
+    return scores
+
+
+def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_vals=False):
+    """csa_topk.  Returns (idx int32 [B][T][k], vals float32 or None)."""
+    lib = _lib.load()
+    B, T, N = scores.shape
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+    if vals is None and want_vals:
+        vals = torch.empty((B, T, k), dtype=torch.float32, device=dev)
+    nb = lib.csa_topk_workspace_bytes(B, T, N, k)
+    if ws is None:
+        ws = workspace(nb, dev, "topk", zero=True)
+    st = lib.csa_topk(_ptr(scores), B, T, N, _ptr(pos0), m, k, _ptr(idx), _ptr(vals), _ptr(ws), nb,
+                      _stream(stream))
+    _lib.check(st, "csa_topk")
+    return idx, vals
+
+
+def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
+           gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None):
+    """csa_attend.  q [B][T][H][c], comp_kv [B][N][c], idx int32 [B][T][k], win_kv [B][T+n_win-1][c]."""
+    lib = _lib.load()
+    B, T, H, c = q.shape
+    k = idx.shape[2]
+    N = comp_kv.shape[1]
+    kv_fmt = _TORCH_FMT[q.dtype]
+    out_fmt = out_fmt or kv_fmt
+    if out is None:
+        out = torch.empty((B, T, H, c), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=q.device)
+    nb = lib.csa_attend_workspace_bytes(B, T, H, c, k, n_win)
+    if ws is None:
+        ws = workspace(nb, q.device, "attend")
+    st = lib.csa_attend(_ptr(q), _ptr(comp_kv), _ptr(idx), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv),
+                        B, T, H, c, rope_dims, k, n_win, N, _ptr(pos0), m, scale, eps, rope_base, FMT[kv_fmt],
+                        _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+    _lib.check(st, "csa_attend")
+    return out
+
+
+def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
+               gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None):
+    """hca_attend: dense over every visible compressed entry s < floor(t/m_hca), plus the window."""
+    lib = _lib.load()
+    B, T, H, c = q.shape
+    N = comp_kv.shape[1]
+    kv_fmt = _TORCH_FMT[q.dtype]
+    out_fmt = out_fmt or kv_fmt
+    if out is None:
+        out = torch.empty((B, T, H, c), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=q.device)
+    nb = lib.hca_attend_workspace_bytes(B, T, H, c, N, n_win)
+    if ws is None:
+        ws = workspace(nb, q.device, "hca")
+    st = lib.hca_attend(_ptr(q), _ptr(comp_kv), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv), B, T, H, c,
+                        rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base, FMT[kv_fmt], _ptr(out),
+                        FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+    _lib.check(st, "hca_attend")
+    return out

@@ -1,0 +1,649 @@
+// csa_attend / hca_attend kernels: shared-KV multi-query attention over the
+// selected (CSA) or all visible (HCA) compressed entries plus the sliding window.
+//
+// "【论文解读】DeepSeek-V4" (wkq9411.github.io), section 一(三)1(3) (shared key-value
+// MQA: every entry is both key and value, all query heads share it), 一(三)2(2)
+// (HCA: dense over all compressed entries), and 一(三)3 (RMSNorm of query heads and
+// KV entries; RoPE on the last dims of queries, entries and outputs, the output
+// rotated at -t; the uncompressed sliding window; a per-head sink logit added to
+// the softmax denominator).
+//
+// BF16 path (MFMA).  A workgroup of 4 waves serves one query row and 64 heads
+// (16 per wave).  Entry slots are staged 32 at a time into LDS, once per
+// workgroup, in two layouts: entry-major (A operand of S^T = E Q^T) and dim-major
+// (B operand of O = P E).  RMSNorm is factored as a per-entry scalar r_e and a
+// per-query scalar r_q applied to the float32 logits, so the non-RoPE dims of q
+// and e enter the MFMA as their exact bf16 input bits; only the rotated RoPE dims
+// (and gains, if given) are rounded to bf16.  With S^T in the MFMA output layout
+// each lane holds one head's logits for 8 entries, so the online softmax needs
+// only in-lane work plus two cross-group shuffles, and the probabilities
+// (times r_e) are already in the A-operand layout of the PV MFMA.
+//
+// Decode (T = 1) splits each query's slot list at fixed 128-slot boundaries and
+// merges the parts in a fixed order in a second kernel; prefill (T > 1) runs one
+// part per query and finishes in place.
+//
+// F32 path (VALU): one workgroup per (query row, head group), waves take entries
+// round-robin with their own online softmax and are merged in a fixed order.
+#include "csa_common.h"
+#include "csa_internal.h"
+
+namespace {
+
+constexpr int kTile = 32;            // entry slots per staged tile
+constexpr int kSplitSlots = 128;     // decode split length (slots)
+constexpr int kE2Stride = 40;        // halfwords per dim-major LDS row (32 entries + pad)
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* comp;
+  const int32_t* idx;
+  const uint16_t* win;
+  const float* sink;
+  const float* gamma_q;
+  const float* gamma_kv;
+  const int64_t* pos0;
+  void* out;
+  float* ws_o;     // [rows][nsplit][H][C]
+  float* ws_ml;    // [rows][nsplit][H][2]
+  int T, H, R, k, n_win, m, out_t, mode, nsplit;
+  int64_t n_max;
+  float scale, eps;
+};
+
+struct Slot {
+  int64_t row;   // row index into comp (or window) array, -1 = empty
+  bool is_win;
+  double pos;
+};
+
+// slot j of query (b, r) at position t: CSA = idx slots then window; HCA = dense range then window
+CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vis, int64_t slot) {
+  Slot s;
+  s.is_win = false;
+  s.row = -1;
+  s.pos = 0.0;
+  const int64_t ncomp = (a.mode == 0) ? a.k : a.n_max;
+  if (slot < ncomp) {
+    int64_t e;
+    if (a.mode == 0) {
+      e = a.idx[((int64_t)b * a.T + r) * a.k + slot];
+      if (e < 0 || e >= a.n_max) return s;
+    } else {
+      e = slot;
+      if (e >= vis) return s;
+    }
+    s.row = e;
+    s.pos = (double)a.m * (double)e;
+    return s;
+  }
+  const int64_t w = slot - ncomp;
+  if (w >= a.n_win) return s;
+  const int64_t p = t - a.n_win + 1 + w;
+  if (p < 0) return s;
+  s.is_win = true;
+  s.row = r + w;
+  s.pos = (double)p;
+  return s;
+}
+
+CSA_DEV float bf(uint32_t word, int hi) { return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16)); }
+
+template <int C>
+__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt) {
+  constexpr int KS = C / 32;       // k-steps of S^T = E Q^T
+  constexpr int DT = C / 16;       // dim tiles of O
+  constexpr int NCH = C / 64;      // 16-byte chunks per staging lane
+  constexpr int E1S = C + 8;       // halfwords per entry-major LDS row
+  extern __shared__ __align__(16) uint16_t s_mem[];
+  uint16_t* E1 = s_mem;                                   // [32][E1S]
+  uint16_t* E2 = s_mem + kTile * E1S;                     // [C][kE2Stride]
+  float* s_re = reinterpret_cast<float*>(E2 + C * kE2Stride);  // [32]
+  __shared__ int s_any;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int sp = blockIdx.x;
+  const int row = blockIdx.z;
+  const int b = row / a.T;
+  const int r = row - b * a.T;
+  const int64_t t = a.pos0[b] + r;
+  const int64_t vis = visible_entries(t, a.m, a.n_max);
+  const int head = blockIdx.y * 64 + wave * 16 + (lane & 15);
+  const bool wave_active = (blockIdx.y * 64 + wave * 16) < a.H;
+  const int R = a.R;
+  const int rope_lo = C - R;
+  const int64_t nslots = ((a.mode == 0) ? a.k : a.n_max) + a.n_win;
+  const int64_t slot_lo = (int64_t)sp * (a.nsplit > 1 ? kSplitSlots : nslots);
+  const int64_t slot_hi = a.nsplit > 1 ? min(slot_lo + kSplitSlots, nslots) : nslots;
+  const double tpos = (double)t;
+
+  // ---- query fragment (B operand of S^T): head = lane&15, dims [32ks + 8g, +8)
+  bf16x8 qf[KS];
+  float r_q = 0.0f;
+  if (wave_active) {
+    const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C;
+    float ss = 0.0f;
+    u32x4 raw[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x0 = bf(raw[ks][j], 0), x1 = bf(raw[ks][j], 1);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    r_q = 1.0f / sqrtf(ss / (float)C + a.eps);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      if (d0 >= rope_lo || a.gamma_q || a.gamma_kv) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { x[2 * j] = bf(raw[ks][j], 0); x[2 * j + 1] = bf(raw[ks][j], 1); }
+        if (a.gamma_q) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] *= a.gamma_q[d0 + j];
+        }
+        if (d0 >= rope_lo) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            float cs, sn;
+            rope_cs(tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+            float x0 = x[2 * p], x1 = x[2 * p + 1];
+            x[2 * p] = x0 * cs - x1 * sn;
+            x[2 * p + 1] = x0 * sn + x1 * cs;
+          }
+        } else if (a.gamma_kv) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] *= a.gamma_kv[d0 + j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[ks][j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
+    }
+  }
+  const float zmul = a.scale * r_q;
+
+  f32x4 O[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15
+
+  for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kTile) {
+    // ---- stage 32 slots: wave w stages slots 8w..8w+7, 8 lanes per slot
+    {
+      const int es = 8 * wave + (lane >> 3);
+      const int sub = lane & 7;
+      const int64_t slot = s0 + es;
+      Slot sl;
+      sl.row = -1;
+      if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
+      const bool valid = sl.row >= 0;
+      const uint16_t* src = valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
+                                               : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
+                                  : nullptr;
+      u32x4 v[NCH];
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        if (valid) {
+          v[j] = *reinterpret_cast<const u32x4*>(src + 8 * (sub + 8 * j));
+        } else {
+          v[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x0 = bf(v[j][q], 0), x1 = bf(v[j][q], 1);
+          ss = fmaf(x0, x0, ss);
+          ss = fmaf(x1, x1, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if (sub == 0) s_re[es] = valid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int d0 = 8 * (sub + 8 * j);
+        if (valid && (d0 >= rope_lo || a.gamma_kv)) {
+          float x[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { x[2 * q] = bf(v[j][q], 0); x[2 * q + 1] = bf(v[j][q], 1); }
+          if (a.gamma_kv) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+          }
+          if (d0 >= rope_lo) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              float cs, sn;
+              rope_cs(sl.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+              float x0 = x[2 * p], x1 = x[2 * p + 1];
+              x[2 * p] = x0 * cs - x1 * sn;
+              x[2 * p + 1] = x0 * sn + x1 * cs;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[j][q] = (uint32_t)f32_to_bf16(x[2 * q]) | ((uint32_t)f32_to_bf16(x[2 * q + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(E1 + es * E1S + d0) = v[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          E2[(d0 + 2 * q) * kE2Stride + es] = (uint16_t)(v[j][q] & 0xFFFFu);
+          E2[(d0 + 2 * q + 1) * kE2Stride + es] = (uint16_t)(v[j][q] >> 16);
+        }
+      }
+      if (threadIdx.x == 0) s_any = 0;
+      __syncthreads();
+      if (valid && sub == 0) s_any = 1;
+      __syncthreads();
+    }
+    if (s_any && wave_active) {
+      // ---- S^T = E Q^T : lane holds entries 16nt + 4g + i, head lane&15
+      f32x4 st[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* ea = E1 + (16 * nt + (lane & 15)) * E1S + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          bf16x8 ef = *reinterpret_cast<const bf16x8*>(ea + 32 * ks);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], acc, 0, 0, 0);
+        }
+        st[nt] = acc;
+      }
+      float z[8], re[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 16 * nt + 4 * g + i;
+          const float rv = s_re[e];
+          re[4 * nt + i] = rv;
+          const float zz = rv > 0.0f ? st[nt][i] * zmul * rv : -INFINITY;
+          z[4 * nt + i] = zz;
+          tmax = fmaxf(tmax, zz);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float Mn = fmaxf(M, tmax);
+      const float alpha = (Mn == -INFINITY) ? 1.0f : expf(M - Mn);
+      float psum = 0.0f;
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        float p0 = (Mn == -INFINITY) ? 0.0f : expf(z[j] - Mn);
+        float p1 = (Mn == -INFINITY) ? 0.0f : expf(z[j + 1] - Mn);
+        psum += p0 + p1;
+        pw[j / 2] = (uint32_t)f32_to_bf16(p0 * re[j]) | ((uint32_t)f32_to_bf16(p1 * re[j + 1]) << 16);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      L = L * alpha + psum;
+      M = Mn;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      // alpha of the 4 heads this lane accumulates in O (rows 4g + i)
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+      // ---- O += P E : B operand = dims 16dt + lane&15, entries {4g..4g+3, 16+4g..16+4g+3}
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* eb = E2 + (16 * dt + (lane & 15)) * kE2Stride + 4 * g;
+        uint2 lo = *reinterpret_cast<const uint2*>(eb);
+        uint2 hi = *reinterpret_cast<const uint2*>(eb + 16);
+        const bf16x8 ef = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        f32x4 o = O[dt];
+        o[0] *= al[0]; o[1] *= al[1]; o[2] *= al[2]; o[3] *= al[3];
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, o, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  if (a.nsplit > 1) {
+    // partial state of (row, split, head): O[head][dim] unnormalized, plus M and L
+    const int64_t base = ((int64_t)row * a.nsplit + sp) * a.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = blockIdx.y * 64 + wave * 16 + 4 * g + i;
+      float* dst = a.ws_o + (base + h) * C + (lane & 15);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dst[16 * dt] = O[dt][i];
+    }
+    if (g == 0) {
+      a.ws_ml[(base + head) * 2 + 0] = M;
+      a.ws_ml[(base + head) * 2 + 1] = L;
+    }
+    return;
+  }
+  // ---- single part: add the sink, normalise, gains, rotate back by -t, write
+  const float zs = a.sink[head];
+  const float Mf = fmaxf(M, zs);
+  const float Lf = L * expf(M - Mf) + expf(zs - Mf);
+  const float f = (M == -INFINITY) ? 0.0f : expf(M - Mf) / Lf;
+  float fi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i, 64);
+  const int dcol = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d = 16 * dt + dcol;
+    float v[4], other[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = O[dt][i] * fi[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(v[i], 1, 64);  // pair partner: adjacent dim, adjacent lane
+    if (d < rope_lo) {
+      if (a.gamma_kv) {
+        const float gk = a.gamma_kv[d];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= gk;
+      }
+    } else {
+      float cs, sn;
+      rope_cs(-tpos, rt.theta[(d - rope_lo) / 2], cs, sn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (dcol & 1) ? (other[i] * sn + v[i] * cs) : (v[i] * cs - other[i] * sn);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = blockIdx.y * 64 + wave * 16 + 4 * g + i;
+      const int64_t o = ((int64_t)row * a.H + h) * C + d;
+      if (a.out_t == CSA_F32)
+        static_cast<float*>(a.out)[o] = v[i];
+      else
+        static_cast<uint16_t*>(a.out)[o] = f32_to_bf16(v[i]);
+    }
+  }
+}
+
+// merge the decode parts of one (row, head): fixed order, sink, gains, -t rotation
+__global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, RopeTable rt) {
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = row / a.T;
+  const int r = row - b * a.T;
+  const double tpos = (double)(a.pos0[b] + r);
+  const int64_t base = ((int64_t)row * a.nsplit) * a.H + h;
+  float Mx = a.sink[h];
+  for (int s = 0; s < a.nsplit; ++s) Mx = fmaxf(Mx, a.ws_ml[(base + (int64_t)s * a.H) * 2]);
+  float Lt = expf(a.sink[h] - Mx);
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.ws_ml[(base + (int64_t)s * a.H) * 2];
+    if (ms != -INFINITY) Lt = fmaf(a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1], expf(ms - Mx), Lt);
+  }
+  const int rope_lo = C - a.R;
+  for (int d0 = 4 * threadIdx.x; d0 < C; d0 += 4 * blockDim.x) {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ms = a.ws_ml[(base + (int64_t)s * a.H) * 2];
+      if (ms == -INFINITY) continue;
+      const float fs = expf(ms - Mx);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + d0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[i], fs, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] / Lt;
+    if (d0 < rope_lo) {
+      if (a.gamma_kv)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= a.gamma_kv[d0 + i];
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float cs, sn;
+        rope_cs(-tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+        const float x0 = v[2 * p], x1 = v[2 * p + 1];
+        v[2 * p] = x0 * cs - x1 * sn;
+        v[2 * p + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    const int64_t o = ((int64_t)row * a.H + h) * C + d0;
+    if (a.out_t == CSA_F32) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = pk;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ float32 path
+struct AttnArgsF32 {
+  const float* q;
+  const float* comp;
+  const int32_t* idx;
+  const float* win;
+  const float* sink;
+  const float* gamma_q;
+  const float* gamma_kv;
+  const int64_t* pos0;
+  void* out;
+  int T, H, C, R, k, n_win, m, out_t, mode, hg;
+  int64_t n_max;
+  float scale, eps;
+};
+
+constexpr int kF32MaxDPL = 8;  // dims per lane (c <= 512)
+
+// rotate the lane's dims [d0, d0+dpl) if they are RoPE dims (pairs are lane-local)
+CSA_DEV void rope_lane(float* x, int dpl, int d0, int rope_lo, double pos, const RopeTable& rt) {
+  for (int j = 0; j < dpl; j += 2) {
+    const int d = d0 + j;
+    if (d < rope_lo) continue;
+    float cs, sn;
+    rope_cs(pos, rt.theta[(d - rope_lo) / 2], cs, sn);
+    const float x0 = x[j], x1 = x[j + 1];
+    x[j] = x0 * cs - x1 * sn;
+    x[j + 1] = x0 * sn + x1 * cs;
+  }
+}
+
+__global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgsF32 a, RopeTable rt) {
+  extern __shared__ float s_f[];  // q^ [hg][C]  |  merge buffer [hg][C + 2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int b = row / a.T, r = row - b * a.T;
+  const int64_t t = a.pos0[b] + r;
+  const int64_t vis = visible_entries(t, a.m, a.n_max);
+  const int h0 = blockIdx.x * a.hg;
+  const int nh = min(a.hg, a.H - h0);
+  const int C = a.C, dpl = C / 64, d0 = lane * dpl, rope_lo = C - a.R;
+  float* sq = s_f;
+  float* sm = s_f + a.hg * C;
+
+  // q^ = RoPE_t(RMSNorm(q)) for the group's heads
+  for (int hh = wave; hh < nh; hh += 4) {
+    const float* qr = a.q + ((int64_t)row * a.H + h0 + hh) * C;
+    float x[kF32MaxDPL];
+    float ss = 0.f;
+    for (int j = 0; j < dpl; ++j) { x[j] = qr[d0 + j]; ss = fmaf(x[j], x[j], ss); }
+    ss = wave_sum(ss);
+    const float rn = 1.0f / sqrtf(ss / (float)C + a.eps);
+    for (int j = 0; j < dpl; ++j) x[j] = x[j] * rn * (a.gamma_q ? a.gamma_q[d0 + j] : 1.0f);
+    rope_lane(x, dpl, d0, rope_lo, (double)t, rt);
+    for (int j = 0; j < dpl; ++j) sq[hh * C + d0 + j] = x[j];
+  }
+  __syncthreads();
+
+  float acc[32][kF32MaxDPL];
+  float Mh[32], Lh[32];
+  for (int hh = 0; hh < 32; ++hh) {
+    Mh[hh] = -INFINITY;
+    Lh[hh] = 0.f;
+    for (int j = 0; j < kF32MaxDPL; ++j) acc[hh][j] = 0.f;
+  }
+  const int64_t nslots = ((a.mode == 0) ? a.k : a.n_max) + a.n_win;
+  for (int64_t slot = wave; slot < nslots; slot += 4) {
+    // resolve the slot (same rule as the bf16 path)
+    int64_t erow = -1;
+    bool is_win = false;
+    double pos = 0.0;
+    const int64_t ncomp = (a.mode == 0) ? a.k : a.n_max;
+    if (slot < ncomp) {
+      int64_t e = (a.mode == 0) ? (int64_t)a.idx[((int64_t)b * a.T + r) * a.k + slot] : slot;
+      bool ok = (a.mode == 0) ? (e >= 0 && e < a.n_max) : (e < vis);
+      if (ok) { erow = e; pos = (double)a.m * (double)e; }
+    } else {
+      const int64_t w = slot - ncomp;
+      const int64_t p = t - a.n_win + 1 + w;
+      if (p >= 0) { erow = r + w; is_win = true; pos = (double)p; }
+    }
+    if (erow < 0) continue;  // uniform across the wave
+    const float* src = is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + erow) * C
+                              : a.comp + ((int64_t)b * a.n_max + erow) * C;
+    float x[kF32MaxDPL];
+    float ss = 0.f;
+    for (int j = 0; j < dpl; ++j) { x[j] = src[d0 + j]; ss = fmaf(x[j], x[j], ss); }
+    ss = wave_sum(ss);
+    const float rn = 1.0f / sqrtf(ss / (float)C + a.eps);
+    for (int j = 0; j < dpl; ++j) x[j] = x[j] * rn * (a.gamma_kv ? a.gamma_kv[d0 + j] : 1.0f);
+    rope_lane(x, dpl, d0, rope_lo, pos, rt);
+    for (int hh = 0; hh < nh; ++hh) {
+      float d = 0.f;
+      for (int j = 0; j < dpl; ++j) d = fmaf(sq[hh * C + d0 + j], x[j], d);
+      const float z = wave_sum(d) * a.scale;
+      const float Mn = fmaxf(Mh[hh], z);
+      const float al = expf(Mh[hh] - Mn);
+      const float p = expf(z - Mn);
+      Lh[hh] = Lh[hh] * al + p;
+      for (int j = 0; j < dpl; ++j) acc[hh][j] = fmaf(p, x[j], acc[hh][j] * al);
+      Mh[hh] = Mn;
+    }
+  }
+  // merge waves 1..3 into wave 0 in a fixed order
+  for (int src_w = 1; src_w < 4; ++src_w) {
+    if (wave == src_w) {
+      for (int hh = 0; hh < nh; ++hh) {
+        for (int j = 0; j < dpl; ++j) sm[hh * (C + 2) + d0 + j] = acc[hh][j];
+        if (lane == 0) { sm[hh * (C + 2) + C] = Mh[hh]; sm[hh * (C + 2) + C + 1] = Lh[hh]; }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      for (int hh = 0; hh < nh; ++hh) {
+        const float Mo = sm[hh * (C + 2) + C], Lo = sm[hh * (C + 2) + C + 1];
+        const float Mn = fmaxf(Mh[hh], Mo);
+        if (Mn == -INFINITY) continue;
+        const float fa = expf(Mh[hh] - Mn), fb = expf(Mo - Mn);
+        Lh[hh] = Lh[hh] * fa + Lo * fb;
+        for (int j = 0; j < dpl; ++j) acc[hh][j] = acc[hh][j] * fa + sm[hh * (C + 2) + d0 + j] * fb;
+        Mh[hh] = Mn;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  for (int hh = 0; hh < nh; ++hh) {
+    const int h = h0 + hh;
+    const float zs = a.sink[h];
+    const float Mf = fmaxf(Mh[hh], zs);
+    const float Lf = Lh[hh] * expf(Mh[hh] - Mf) + expf(zs - Mf);
+    const float f = (Mh[hh] == -INFINITY) ? 0.0f : expf(Mh[hh] - Mf) / Lf;
+    float x[kF32MaxDPL];
+    for (int j = 0; j < dpl; ++j) x[j] = acc[hh][j] * f;
+    rope_lane(x, dpl, d0, rope_lo, -(double)t, rt);
+    const int64_t o = ((int64_t)row * a.H + h) * C + d0;
+    for (int j = 0; j < dpl; ++j) {
+      if (a.out_t == CSA_F32)
+        static_cast<float*>(a.out)[o + j] = x[j];
+      else
+        static_cast<uint16_t*>(a.out)[o + j] = f32_to_bf16(x[j]);
+    }
+  }
+}
+
+RopeTable make_rope(int R, float base) {
+  RopeTable rt;
+  for (int i = 0; i < 64; ++i) rt.theta[i] = (2 * i < R) ? pow((double)base, -(double)(2 * i) / (double)R) : 0.0;
+  return rt;
+}
+
+int decode_splits(int T, int64_t nslots) { return T == 1 ? ceil_div(nslots, kSplitSlots) : 1; }
+
+template <int C>
+size_t bf16_lds_bytes() {
+  return (size_t)kTile * (C + 8) * 2 + (size_t)C * kE2Stride * 2 + kTile * 4;
+}
+
+template <int C>
+csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
+  const size_t lds = bf16_lds_bytes<C>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return CSA_ERR_LAUNCH;
+    attr_set = true;
+  }
+  dim3 grid(a.nsplit, ceil_div(a.H, 64), rows);
+  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt);
+  if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t list_len) {
+  (void)mode;
+  const int ns = decode_splits(T, list_len);
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)B * T;
+  const size_t o = rows * ns * H * (size_t)c * 4;
+  return ((o + 255) & ~(size_t)255) + rows * ns * H * 2 * 4;
+}
+
+csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
+                         const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
+                         int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
+                         float scale, float eps, float rope_base, int kv_t, void* out, int out_t, void* ws,
+                         hipStream_t stream) {
+  const RopeTable rt = make_rope(rope_dims, rope_base);
+  const int rows = B * T;
+  if (kv_t == CSA_F32) {
+    AttnArgsF32 a;
+    a.q = (const float*)q; a.comp = (const float*)comp_kv; a.idx = idx; a.win = (const float*)win_kv;
+    a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
+    a.T = T; a.H = H; a.C = c; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t;
+    a.mode = mode; a.n_max = n_max; a.scale = scale; a.eps = eps;
+    a.hg = 4096 / c;  // heads per workgroup: hg * (c / 64) <= 64 accumulators per lane
+    if (a.hg > 32) a.hg = 32;
+    size_t lds = (size_t)a.hg * c * 4 + (size_t)a.hg * (c + 2) * 4;
+    dim3 grid(ceil_div(H, a.hg), rows);
+    hipLaunchKernelGGL(attend_f32_kernel, grid, dim3(256), lds, stream, a, rt);
+    return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+  }
+  AttnArgs a;
+  a.q = (const uint16_t*)q; a.comp = (const uint16_t*)comp_kv; a.idx = idx; a.win = (const uint16_t*)win_kv;
+  a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
+  a.T = T; a.H = H; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t; a.mode = mode;
+  a.n_max = n_max; a.scale = scale; a.eps = eps;
+  const int64_t nslots = (mode == 0 ? (int64_t)k : n_max) + n_win;
+  a.nsplit = decode_splits(T, nslots);
+  if (a.nsplit > 1) {
+    const size_t o = (size_t)rows * a.nsplit * H * (size_t)c * 4;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o + 255) & ~(size_t)255));
+  } else {
+    a.ws_o = nullptr;
+    a.ws_ml = nullptr;
+  }
+  switch (c) {
+    case 128: return launch_bf16<128>(a, rt, rows, stream);
+    case 256: return launch_bf16<256>(a, rt, rows, stream);
+    case 512: return launch_bf16<512>(a, rt, rows, stream);
+    default: return CSA_ERR_UNSUPPORTED;
+  }
+}

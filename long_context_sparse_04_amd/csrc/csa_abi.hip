@@ -1,0 +1,143 @@
+// C ABI of the CSA / HCA step: O(1) host-side validation, then launches on the
+// caller's stream.  No HIP runtime call is made before validation passes, so
+// argument errors are reported without touching a device.
+#include "csa_common.h"
+#include "csa_internal.h"
+
+namespace {
+bool is_pow2_dim(int c) { return c == 128 || c == 256 || c == 512; }
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_NULL: return "CSA_ERR_NULL: a required pointer is NULL";
+    case CSA_ERR_SHAPE: return "CSA_ERR_SHAPE: sizes are inconsistent or out of range";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: this dtype / size combination is not implemented";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
+    case CSA_ERR_LAUNCH: return "CSA_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown csa_status";
+  }
+}
+
+int csa_abi_version(void) { return 1; }
+
+csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
+                        const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
+                        int num_entries, int in_t, void* out, void* out_scale, int out_t, int64_t out_batch_stride,
+                        void* stream) {
+  if (B < 0 || rows < 0 || num_entries < 0 || m < 1 || m > 1024 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
+  if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (out_t < CSA_F32 || out_t > CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
+  if (out_t == CSA_MXFP4_E8M0_B32 && (c % 32)) return CSA_ERR_UNSUPPORTED;
+  if (B == 0 || num_entries == 0) return CSA_OK;
+  const bool overlap = cb != nullptr || zb != nullptr || bias_b != nullptr;
+  if (!ca || !za || !bias_a || !out) return CSA_ERR_NULL;
+  if (overlap && (!cb || !zb || !bias_b)) return CSA_ERR_NULL;
+  if ((out_t == CSA_FP8_E4M3_ROWSCALE || out_t == CSA_MXFP4_E8M0_B32) && !out_scale) return CSA_ERR_NULL;
+  if (first_entry < 0) return CSA_ERR_SHAPE;
+  if (out_batch_stride == 0) out_batch_stride = num_entries;
+  if (out_batch_stride < num_entries) return CSA_ERR_SHAPE;
+  // every row the entries read must be inside [row0_pos, row0_pos + rows)
+  const int64_t last = first_entry + num_entries - 1;
+  const int64_t lo_entry = (overlap && first_entry > 0) ? first_entry - 1 : first_entry;
+  if ((int64_t)m * lo_entry < row0_pos) return CSA_ERR_SHAPE;
+  if ((int64_t)m * (last + 1) - 1 >= row0_pos + rows) return CSA_ERR_SHAPE;
+  return launch_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry, num_entries, in_t, out,
+                         out_scale, out_t, out_batch_stride, (hipStream_t)stream);
+}
+
+csa_status csa_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
+                     int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, float* scores,
+                     void* stream) {
+  if (B < 0 || T < 0 || HI < 1 || cI < 1 || n_max < 0 || m < 1) return CSA_ERR_SHAPE;
+  if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if ((int64_t)B * T >= 65536) return CSA_ERR_UNSUPPORTED;  // grid.y limit
+  switch (qk_t) {
+    case CSA_F32:
+      if ((cI & 3) || cI > 512 || HI > 128 || HI * cI > 16384) return CSA_ERR_UNSUPPORTED;
+      break;
+    case CSA_BF16:
+    case CSA_FP8_E4M3_ROWSCALE:
+    case CSA_MXFP4_E8M0_B32:
+      if (cI != 128 || !(HI == 16 || HI == 32 || HI == 64 || HI == 128)) return CSA_ERR_UNSUPPORTED;
+      break;
+    default:
+      return CSA_ERR_UNSUPPORTED;
+  }
+  if (B == 0 || T == 0 || n_max == 0) return CSA_OK;
+  if (!q || !w || !k || !pos0 || !scores) return CSA_ERR_NULL;
+  if ((qk_t == CSA_FP8_E4M3_ROWSCALE || qk_t == CSA_MXFP4_E8M0_B32) && (!q_scale || !k_scale)) return CSA_ERR_NULL;
+  return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, (hipStream_t)stream);
+}
+
+size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
+  if (B <= 0 || T <= 0 || n_max <= 0 || k <= 0) return 0;
+  return topk_workspace_bytes(B, T, n_max, k);
+}
+
+csa_status csa_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
+                    int32_t* idx, float* vals, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0 || n_max < 0 || m < 1 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
+  if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if (B == 0 || T == 0) return CSA_OK;
+  if (!idx || !pos0 || (n_max > 0 && !scores)) return CSA_ERR_NULL;
+  const size_t need = csa_topk_workspace_bytes(B, T, n_max > 0 ? n_max : 1, k);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  return launch_topk(scores, B, T, n_max, pos0, m, k, idx, vals, workspace, (hipStream_t)stream);
+}
+
+static csa_status check_attend(int kv_t, int out_t, int B, int T, int H, int c, int rope_dims, int n_win, int m) {
+  if (B < 0 || T < 0 || H < 1 || m < 1 || n_win < 1 || n_win > 4096) return CSA_ERR_SHAPE;
+  if (!is_pow2_dim(c)) return CSA_ERR_UNSUPPORTED;
+  if (rope_dims < 0 || (rope_dims % 8) || rope_dims > c || rope_dims > 128) return CSA_ERR_UNSUPPORTED;
+  if (kv_t != CSA_F32 && kv_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (out_t != CSA_F32 && out_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (kv_t == CSA_BF16 && (H % 16)) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * T >= 65536) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
+size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win) {
+  if (B <= 0 || T <= 0 || H <= 0 || c <= 0 || k <= 0 || n_win <= 0) return 0;
+  return attend_workspace_bytes(0, B, T, H, c, (int64_t)k + n_win);
+}
+
+csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv, const float* sink,
+                      const float* gamma_q, const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int k,
+                      int n_win, int64_t n_max, const int64_t* pos0, int m, float scale, float eps, float rope_base,
+                      int kv_t, void* out, int out_t, void* workspace, size_t ws_bytes, void* stream) {
+  csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m);
+  if (st != CSA_OK) return st;
+  if (k < 1 || k > 2048 || n_max < 0 || n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if (B == 0 || T == 0) return CSA_OK;
+  if (!q || !idx || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
+  const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  return launch_attend(0, q, comp_kv, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, k, n_win, n_max,
+                       pos0, m, scale, eps, rope_base, kv_t, out, out_t, workspace, (hipStream_t)stream);
+}
+
+size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win) {
+  if (B <= 0 || T <= 0 || H <= 0 || c <= 0 || n_max < 0 || n_win <= 0) return 0;
+  return attend_workspace_bytes(1, B, T, H, c, n_max + n_win);
+}
+
+csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv, const float* sink, const float* gamma_q,
+                      const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
+                      const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t, void* out,
+                      int out_t, void* workspace, size_t ws_bytes, void* stream) {
+  csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m_hca);
+  if (st != CSA_OK) return st;
+  if (n_max < 0 || n_max >= ((int64_t)1 << 24)) return CSA_ERR_SHAPE;
+  if (B == 0 || T == 0) return CSA_OK;
+  if (!q || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
+  const size_t need = hca_attend_workspace_bytes(B, T, H, c, n_max, n_win);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  return launch_attend(1, q, comp_kv, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, 1, n_win,
+                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, out, out_t, workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal helpers shared by the gfx950 kernels of the CSA / HCA step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define CSA_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------- number formats
+CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bfloat16, round to nearest even (NaN stays NaN).
+CSA_DEV uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// float32 -> OCP fp8 E4M3, round to nearest even, saturating at +-448 (NaN -> 0x7F).
+CSA_DEV uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)rintf(a * 512.0f);  // multiples of 2^-9; 8 becomes the smallest normal
+  } else {
+    uint32_t au = __float_as_uint(a);
+    int e = (int)(au >> 23) - 127;
+    uint32_t mant = au & 0x7FFFFFu;
+    uint32_t keep = mant >> 20, rest = mant & 0xFFFFFu;
+    if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) keep++;
+    if (keep == 8u) { keep = 0u; e++; }
+    code = ((uint32_t)(e + 7) << 3) | keep;
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code ? (sign | code) : 0u;
+}
+
+// |v| (already divided by the block scale) -> e2m1 code, ties to even, saturating at 6.
+CSA_DEV uint32_t f32_to_e2m1(float v) {
+  float a = fabsf(v);
+  uint32_t code = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return (code && v < 0.0f) ? (code | 8u) : code;
+}
+
+// Order-preserving key of a float32 score (+0 and -0 map to the same key).
+CSA_DEV uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+CSA_DEV float key_to_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- cross-lane helpers
+// DPP row operations act inside 16-lane rows.
+template <int CTRL>
+CSA_DEV float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// max / sum over the 16 lanes of a row; every lane of the row receives the result
+CSA_DEV float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f32<0x128>(v));  // row_ror:8
+  return v;
+}
+CSA_DEV float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  v += dpp_f32<0x128>(v);
+  return v;
+}
+CSA_DEV float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, 64); }
+CSA_DEV float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- RoPE
+// theta_i = rope_base^(-2i/R) for the R/2 pairs, computed once on the host in double.
+struct RopeTable {
+  double theta[64];
+};
+
+// cos / sin of pos * theta with the angle reduced modulo 2*pi in double precision,
+// so that positions near 2^20 keep float32-level accuracy in the rotation.
+CSA_DEV void rope_cs(double pos, double theta, float& c, float& s) {
+  const double two_pi_hi = 6.283185307179586;      // nearest double to 2*pi
+  const double two_pi_lo = 2.4492935982947064e-16; // 2*pi - two_pi_hi
+  double ang = pos * theta;
+  double kq = rint(ang * 0.15915494309189535);
+  double red = fma(-kq, two_pi_hi, ang);
+  red = fma(-kq, two_pi_lo, red);
+  sincosf((float)red, &s, &c);
+}
+
+// ---------------------------------------------------------------- misc
+CSA_DEV int64_t visible_entries(int64_t t, int m, int64_t n_max) {
+  int64_t v = t >= 0 ? t / m : 0;
+  return v < n_max ? v : n_max;
+}
+
+static inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

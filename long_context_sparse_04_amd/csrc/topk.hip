@@ -1,0 +1,475 @@
+// csa_topk kernels: exact top-k with a lower-index tie-break, ascending output.
+//
+// "【论文解读】DeepSeek-V4" (wkq9411.github.io), section 一(三)1(2): the selector
+// keeps the compressed entries whose index scores are in Top-k(I_{t,:}); section
+// 二(四) notes the selector's cost (BF16 scores made it 2x faster).
+//
+// Scores become order-preserving uint32 keys (+0 == -0).  A three-digit radix
+// select (11 + 11 + 10 bits) finds the k-th key K*; the result is every key > K*
+// plus the lowest-index keys == K*, emitted by an ordered (index-order) block
+// compaction, so no sort is needed.
+//
+//  * Row path (many rows, e.g. prefill): one 512-thread workgroup per row; keys
+//    cached in LDS when the row fits (<= 32768 entries).
+//  * Split path (few long rows, decode): chunks of 4096 scores per workgroup.
+//    Kernel 1 builds the top-digit histogram (LDS, then integer atomics into a
+//    per-row global histogram); the last workgroup of a row picks the digit and
+//    clears the histogram.  Kernel 2 compacts each chunk's keys with a top digit
+//    >= that digit into its own segment, in index order; the last workgroup of a
+//    row loads all segments (chunk order = index order) into LDS and finishes the
+//    select and the ordered output there.  Integer atomics make the result
+//    independent of scheduling; the workspace is left zero-filled.
+#include "csa_common.h"
+#include "csa_internal.h"
+
+namespace {
+
+constexpr int kBins = 2048;
+constexpr int kChunk = 4096;          // scores per workgroup on the split path
+constexpr int kSplitThreads = 256;
+constexpr int kRowThreads = 512;
+constexpr int kRowKeyCap = 32768;     // keys cached in LDS on the row path
+constexpr int kSegCap = 6144;         // candidates cached in LDS by the finishing workgroup
+constexpr int kMaxChunks = 2048;
+
+// ------------------------------------------------------------------ block scans
+// Exclusive prefix of a 0/1 flag over the block (in thread order) and its total.
+template <int NT>
+CSA_DEV int block_flag_scan(bool flag, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t bal = __ballot(flag);
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+  if (lane == 0) s_w[wave] = __popcll(bal);
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    int v = s_w[w];
+    pre += (w < wave) ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + below;
+}
+
+// Exclusive prefix of an int over the block in thread order.
+template <int NT>
+CSA_DEV int block_int_scan(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    int s = s_w[w];
+    pre += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
+// Given hist[nb] (counts per digit) and need >= 1, find the digit d with
+// count(> d) < need <= count(>= d).  Writes d and count(> d) to out[0..1].
+template <int NT>
+CSA_DEV void select_digit(const uint32_t* hist, int nb, int need, int* s_w, int* out) {
+  const int bpt = nb / NT;  // nb is a multiple of NT
+  const int tid = threadIdx.x;
+  const int u = NT - 1 - tid;  // thread u owns the bins of thread tid counted from the top
+  int local = 0;
+  for (int j = 0; j < bpt; ++j) local += hist[tid * bpt + j];
+  // suffix sums: scan in reversed thread order
+  int total;
+  // exchange local through LDS to scan in reversed order
+  __shared__ int s_rev[kRowThreads];
+  s_rev[u] = local;
+  __syncthreads();
+  int mine = s_rev[tid];  // thread tid now holds the count of original thread NT-1-tid
+  int excl = block_int_scan<NT>(mine, s_w, total);
+  // original thread o = NT-1-tid has count(bins above its range) = excl
+  s_rev[NT - 1 - tid] = excl;
+  __syncthreads();
+  int above = s_rev[tid];
+  if (above < need && above + local >= need) {
+    for (int j = bpt - 1; j >= 0; --j) {
+      int h = hist[tid * bpt + j];
+      if (above + h >= need) {
+        out[0] = tid * bpt + j;
+        out[1] = above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+}
+
+// A candidate of the split path: its key and its index in the row.
+struct Cand {
+  uint32_t key;
+  int32_t idx;
+};
+
+// ------------------------------------------------------------------ row path
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int T,
+                                                               int64_t n_max, const int64_t* __restrict__ pos0,
+                                                               int m, int k, int32_t* __restrict__ idx,
+                                                               float* __restrict__ vals, int cache_keys) {
+  extern __shared__ uint32_t s_dyn[];
+  uint32_t* hist = s_dyn;           // kBins
+  uint32_t* keys = s_dyn + kBins;   // cache (when enabled)
+  __shared__ int s_w[kRowThreads / 64];
+  __shared__ int s_sel[2];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int64_t t = pos0[b] + r;
+  const int V = (int)visible_entries(t, m, n_max);
+  const int K = k < V ? k : V;
+  const float* srow = scores + (int64_t)row * n_max;
+  int32_t* orow = idx + (int64_t)row * k;
+  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
+
+  if (K == V) {  // everything visible is selected (also covers V == 0)
+    for (int j = tid; j < k; j += kRowThreads) {
+      orow[j] = j < V ? j : -1;
+      if (vrow) vrow[j] = j < V ? key_to_score(score_key(srow[j])) : -INFINITY;
+    }
+    return;
+  }
+
+  auto key_at = [&](int i) -> uint32_t { return cache_keys ? keys[i] : score_key(srow[i]); };
+
+  // digit 0: bits 31..21
+  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kRowThreads) {
+    uint32_t kk = score_key(srow[i]);
+    if (cache_keys) keys[i] = kk;
+    atomicAdd(&hist[kk >> 21], 1u);
+  }
+  __syncthreads();
+  select_digit<kRowThreads>(hist, kBins, K, s_w, s_sel);
+  const uint32_t d0 = s_sel[0];
+  int need = K - s_sel[1];
+  __syncthreads();
+
+  // digit 1: bits 20..10 among keys with digit 0 == d0
+  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kRowThreads) {
+    uint32_t kk = key_at(i);
+    if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<kRowThreads>(hist, kBins, need, s_w, s_sel);
+  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];  // top 22 bits
+  need -= s_sel[1];
+  __syncthreads();
+
+  // digit 2: bits 9..0 among keys with top 22 bits == p1
+  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kRowThreads) {
+    uint32_t kk = key_at(i);
+    if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<kRowThreads>(hist, 1024, need, s_w, s_sel);
+  const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
+  const int ties = need - s_sel[1];  // keys == K* to take, lowest indices first
+  __syncthreads();
+
+  // ordered compaction
+  int out_base = 0, tie_base = 0;
+  for (int c0 = 0; c0 < V && out_base < K; c0 += kRowThreads) {
+    const int i = c0 + tid;
+    uint32_t kk = i < V ? key_at(i) : 0u;
+    const bool eq = (i < V) && kk == kstar;
+    int eq_tot;
+    int eq_rank = tie_base + block_flag_scan<kRowThreads>(eq, s_w, eq_tot);
+    const bool sel = (i < V) && (kk > kstar || (eq && eq_rank < ties));
+    int sel_tot;
+    int pos = out_base + block_flag_scan<kRowThreads>(sel, s_w, sel_tot);
+    if (sel) {
+      orow[pos] = i;
+      if (vrow) vrow[pos] = key_to_score(kk);
+    }
+    out_base += sel_tot;
+    tie_base += eq_tot;
+  }
+  for (int j = K + tid; j < k; j += kRowThreads) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ split path
+struct SplitWs {
+  uint32_t* hist;     // [rows][kBins]   (zero at rest)
+  uint32_t* count1;   // [rows]          (zero at rest)
+  uint32_t* count2;   // [rows]          (zero at rest)
+  uint32_t* info;     // [rows][4]
+  uint32_t* cnt;      // [rows][nch]
+  Cand* seg;          // [rows][n_max]
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
+  char* p = static_cast<char*>(ws);
+  SplitWs s;
+  s.hist = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * kBins * 4);
+  s.count1 = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 4);
+  s.count2 = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 4);
+  s.info = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * 16);
+  s.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * nch * 4);
+  s.seg = reinterpret_cast<Cand*>(p);
+  return s;
+}
+
+static size_t split_bytes(int rows, int64_t n_max, int nch) {
+  return align256((size_t)rows * kBins * 4) + 2 * align256((size_t)rows * 4) + align256((size_t)rows * 16) +
+         align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand));
+}
+
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const float* __restrict__ scores, int T,
+                                                                        int64_t n_max,
+                                                                        const int64_t* __restrict__ pos0, int m,
+                                                                        int k, SplitWs ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ int s_sel[2];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const bool trivial = (K == V);
+  const float* srow = scores + (int64_t)row * n_max;
+  uint32_t* ghist = ws.hist + (int64_t)row * kBins;
+
+  if (!trivial) {
+    for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
+    __syncthreads();
+    const int lo = blockIdx.x * kChunk;
+    const int hi = min(lo + kChunk, V);
+    for (int i = lo + tid; i < hi; i += kSplitThreads) atomicAdd(&hist[score_key(srow[i]) >> 21], 1u);
+    __syncthreads();
+    for (int j = tid; j < kBins; j += kSplitThreads)
+      if (hist[j]) atomicAdd(&ghist[j], hist[j]);
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&ws.count1[row], 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (!trivial) {
+    for (int j = tid; j < kBins; j += kSplitThreads) {
+      hist[j] = __hip_atomic_load(&ghist[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ghist[j] = 0;  // leave the workspace zero-filled
+    }
+    __syncthreads();
+    select_digit<kSplitThreads>(hist, kBins, K, s_w, s_sel);
+    if (tid == 0) {
+      ws.info[row * 4 + 0] = (uint32_t)s_sel[0];
+      ws.info[row * 4 + 1] = (uint32_t)s_sel[1];
+    }
+  }
+  if (tid == 0) ws.count1[row] = 0;
+}
+
+__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(
+    const float* __restrict__ scores, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
+    int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+  __shared__ Cand s_c[kSegCap];
+  __shared__ uint32_t hist[kBins];
+  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ int s_sel[2];
+  __shared__ int s_last;
+  __shared__ int s_pre[kMaxChunks + 1];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int nch = gridDim.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const bool trivial = (K == V);
+  const float* srow = scores + (int64_t)row * n_max;
+  Cand* seg = ws.seg + (int64_t)row * n_max;
+  uint32_t* cnt = ws.cnt + (int64_t)row * nch;
+  int32_t* orow = idx + (int64_t)row * k;
+  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
+
+  const uint32_t d0 = ws.info[row * 4 + 0];
+  if (!trivial) {
+    // ordered compaction of keys whose top digit is >= d0
+    const int lo = blockIdx.x * kChunk;
+    const int hi = min(lo + kChunk, V);
+    int base = 0;
+    for (int c0 = lo; c0 < hi; c0 += kSplitThreads) {
+      const int i = c0 + tid;
+      uint32_t kk = i < hi ? score_key(srow[i]) : 0u;
+      const bool keep = (i < hi) && (kk >> 21) >= d0;
+      int tot;
+      int pos = base + block_flag_scan<kSplitThreads>(keep, s_w, tot);
+      if (keep) seg[lo + pos] = Cand{kk, i};
+      base += tot;
+    }
+    if (tid == 0) cnt[blockIdx.x] = base;
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&ws.count2[row], 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid == 0) ws.count2[row] = 0;
+
+  if (trivial) {
+    for (int j = tid; j < k; j += kSplitThreads) {
+      orow[j] = j < V ? j : -1;
+      if (vrow) vrow[j] = j < V ? key_to_score(score_key(srow[j])) : -INFINITY;
+    }
+    return;
+  }
+
+  // prefix over chunk counts (chunk order == index order)
+  if (tid == 0) {
+    int acc = 0;
+    for (int c = 0; c < nch; ++c) {
+      s_pre[c] = acc;
+      acc += (int)cnt[c];
+    }
+    s_pre[nch] = acc;
+  }
+  __syncthreads();
+  const int C = s_pre[nch];
+  const bool in_lds = C <= kSegCap;
+  if (in_lds) {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int c = wave; c < nch; c += kSplitThreads / 64) {
+      const int n = s_pre[c + 1] - s_pre[c];
+      for (int j = lane; j < n; j += 64) s_c[s_pre[c] + j] = seg[(int64_t)c * kChunk + j];
+    }
+  }
+  __syncthreads();
+  // flat candidate j -> (chunk, offset) when the list stays in global memory
+  auto cand = [&](int j) -> Cand {
+    if (in_lds) return s_c[j];
+    int lo = 0, hi = nch;  // find c with s_pre[c] <= j < s_pre[c+1]
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_pre[mid] <= j) lo = mid; else hi = mid;
+    }
+    return seg[(int64_t)lo * kChunk + (j - s_pre[lo])];
+  };
+
+  int need = K - (int)ws.info[row * 4 + 1];
+  // digit 1 among candidates with digit 0 == d0
+  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
+  __syncthreads();
+  for (int j = tid; j < C; j += kSplitThreads) {
+    uint32_t kk = cand(j).key;
+    if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
+  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];
+  need -= s_sel[1];
+  __syncthreads();
+  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
+  __syncthreads();
+  for (int j = tid; j < C; j += kSplitThreads) {
+    uint32_t kk = cand(j).key;
+    if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<kSplitThreads>(hist, 1024, need, s_w, s_sel);
+  const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
+  const int ties = need - s_sel[1];
+  __syncthreads();
+
+  int out_base = 0, tie_base = 0;
+  for (int c0 = 0; c0 < C && out_base < K; c0 += kSplitThreads) {
+    const int j = c0 + tid;
+    Cand cd = j < C ? cand(j) : Cand{0u, -1};
+    const bool eq = (j < C) && cd.key == kstar;
+    int eq_tot;
+    int eq_rank = tie_base + block_flag_scan<kSplitThreads>(eq, s_w, eq_tot);
+    const bool sel = (j < C) && (cd.key > kstar || (eq && eq_rank < ties));
+    int sel_tot;
+    int pos = out_base + block_flag_scan<kSplitThreads>(sel, s_w, sel_tot);
+    if (sel) {
+      orow[pos] = cd.idx;
+      if (vrow) vrow[pos] = key_to_score(cd.key);
+    }
+    out_base += sel_tot;
+    tie_base += eq_tot;
+  }
+  for (int j = K + tid; j < k; j += kSplitThreads) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
+}
+
+bool use_split(int rows, int64_t n_max) {
+  const int64_t nch = (n_max + kChunk - 1) / kChunk;
+  return rows < 128 && n_max > 16384 && nch <= kMaxChunks;
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
+  (void)k;
+  const int rows = B * T;
+  if (!use_split(rows, n_max)) return 0;
+  return split_bytes(rows, n_max, ceil_div(n_max, kChunk));
+}
+
+csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
+                       int32_t* idx, float* vals, void* ws, hipStream_t stream) {
+  const int rows = B * T;
+  if (use_split(rows, n_max)) {
+    const int nch = ceil_div(n_max, kChunk);
+    SplitWs s = carve(ws, rows, n_max, nch);
+    dim3 grid(nch, rows);
+    hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m, k,
+                       s);
+    hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+                       k, idx, vals, s);
+  } else {
+    const int cache = n_max <= kRowKeyCap ? 1 : 0;
+    size_t lds = (size_t)kBins * 4 + (cache ? (size_t)n_max * 4 : 0);
+    static bool attr_set = false;
+    if (!attr_set) {
+      if (hipFuncSetAttribute((const void*)topk_row_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((size_t)kBins * 4 + (size_t)kRowKeyCap * 4)) != hipSuccess)
+        return CSA_ERR_LAUNCH;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kRowThreads), lds, stream, scores, T, n_max, pos0, m, k,
+                       idx, vals, cache);
+  }
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}

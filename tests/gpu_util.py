@@ -1,0 +1,67 @@
+"""Helpers for the GPU parity tests: upload seeded host arrays, compare against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+DEV = "cuda:0"
+
+
+def dev(x: np.ndarray, fmt: str = None):
+    """Host storage array -> device tensor (uint16 bf16 bits become torch.bfloat16)."""
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(x).to(DEV)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return oracle.decode_bf16(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def values(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Exact float64 values of a host storage array (data only, no scales)."""
+    if fmt == "bf16":
+        return oracle.decode_bf16(x)
+    return np.asarray(x, np.float64)
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    num = np.linalg.norm((got - ref).ravel())
+    den = np.linalg.norm(ref.ravel())
+    return float(num / den) if den > 0 else float(num)
+
+
+def topk_agreement(gpu_idx, ref_idx, ref_scores, k_rows_tau_rule=1e-3):
+    """Set agreement between two [..., k] index arrays with the gap rule.
+
+    Returns (agreement fraction, number of mismatches outside the gap rule).
+    ref_scores holds the oracle's float64 scores of each row.
+    """
+    g = gpu_idx.reshape(-1, gpu_idx.shape[-1])
+    r = ref_idx.reshape(-1, ref_idx.shape[-1])
+    s = ref_scores.reshape(-1, ref_scores.shape[-1])
+    inter = total = bad = 0
+    for row in range(g.shape[0]):
+        rs = set(int(x) for x in r[row] if x >= 0)
+        gs = set(int(x) for x in g[row] if x >= 0)
+        inter += len(rs & gs)
+        total += len(rs)
+        if rs == gs:
+            continue
+        sel = sorted(rs, key=lambda j: s[row, j])
+        tau = s[row, sel[0]]
+        tol = k_rows_tau_rule * (abs(tau) if tau != 0 else np.max(np.abs(s[row][np.isfinite(s[row])])))
+        for j in gs - rs:
+            if not (tau - s[row, j] <= tol):
+                bad += 1
+        for j in rs - gs:
+            if not (s[row, j] - tau <= tol):
+                bad += 1
+    return inter / max(total, 1), bad

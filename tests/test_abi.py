@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every symbol include/csa.h declares, and rejects bad arguments
+on the host (no device work: these calls return before any HIP runtime call)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from long_context_sparse_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from long_context_sparse_04_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+char\s*\*|csa_status|size_t|int)\s+(\w+)\s*\(", text, flags=re.M)
+    return set(names)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+    raw = C.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.csa_abi_version() == 1
+    for code in range(6):
+        s = lib.csa_status_string(code).decode()
+        assert s.startswith(_lib.STATUS[code])
+    assert lib.csa_status_string(99).decode() == "unknown csa_status"
+
+
+DUMMY = C.c_void_p(0x1000)  # never dereferenced: validation fails before any launch
+
+
+def test_compress_validation(lib):
+    f = lib.csa_compress
+    args = dict(ca=DUMMY, cb=DUMMY, za=DUMMY, zb=DUMMY, ba=DUMMY, bb=DUMMY, B=1, rows=8, c=128, m=4, row0=0, first=1,
+                num=1, in_t=1, out=DUMMY, osc=None, out_t=1, stride=0, stream=None)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["ca"], a["cb"], a["za"], a["zb"], a["ba"], a["bb"], a["B"], a["rows"], a["c"], a["m"], a["row0"],
+                 a["first"], a["num"], a["in_t"], a["out"], a["osc"], a["out_t"], a["stride"], a["stream"])
+
+    assert call(B=-1) == 2
+    assert call(c=130) == 2
+    assert call(m=0) == 2
+    assert call(in_t=2) == 3
+    assert call(out_t=3, c=100) == 3
+    assert call(ca=None) == 1
+    assert call(cb=None) == 1                     # b-stream must be all or nothing
+    assert call(out_t=2, osc=None) == 1           # fp8 needs the scale output
+    assert call(first=2) == 2                     # entry 2 needs rows 4..11 but only 0..7 exist
+    assert call(row0=1) == 2                      # entry 1's b-rows start at 0 < row0
+    assert call(stride=0, num=0) == 0             # nothing to do
+    assert call(B=0) == 0
+
+
+def test_index_topk_attend_validation(lib):
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 64, 1000, DUMMY, 4, 2, DUMMY, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 2, DUMMY, None) == 1
+    assert lib.csa_index(None, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, None) == 1
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, -1, DUMMY, 4, 1, DUMMY, None) == 2
+    # top-k
+    nb = lib.csa_topk_workspace_bytes(4, 1, 262144, 1024)
+    assert nb >= 4 * 262144 * 8
+    assert lib.csa_topk_workspace_bytes(1, 4096, 17408, 512) == 0     # row path needs none
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, DUMMY, None, None, 0, None) == 4
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, DUMMY, None, DUMMY, nb - 1, None) == 4
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 0, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 4096, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, None, 4, 1024, DUMMY, None, DUMMY, nb, None) == 1
+    # attend
+    ws = lib.csa_attend_workspace_bytes(4, 1, 128, 512, 1024, 128)
+    assert ws > 0 and lib.csa_attend_workspace_bytes(1, 4096, 64, 512, 512, 128) == 0
+
+    def att(**kw):
+        a = dict(q=DUMMY, comp=DUMMY, idx=DUMMY, win=DUMMY, sink=DUMMY, B=4, T=1, H=128, c=512, R=64, k=1024,
+                 n_win=128, N=262144, pos=DUMMY, m=4, kv_t=1, out=DUMMY, out_t=1, ws=None, nb=0)
+        a.update(kw)
+        return lib.csa_attend(a["q"], a["comp"], a["idx"], a["win"], a["sink"], None, None, a["B"], a["T"], a["H"],
+                              a["c"], a["R"], a["k"], a["n_win"], a["N"], a["pos"], a["m"], 0.044, 1e-6, 1e4,
+                              a["kv_t"], a["out"], a["out_t"], a["ws"], a["nb"], None)
+    assert att() == 4                         # decode needs the split workspace
+    assert att(c=192) == 3
+    assert att(R=60) == 3
+    assert att(H=40) == 3                     # bf16 path: heads in multiples of 16
+    assert att(kv_t=2) == 3
+    assert att(k=0) == 2
+    assert att(q=None, ws=DUMMY, nb=ws) == 1
+    assert lib.hca_attend_workspace_bytes(8, 1, 128, 512, 8192, 128) > 0

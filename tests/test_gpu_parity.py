@@ -1,0 +1,398 @@
+"""GPU parity: every C-ABI call against the float64 oracle on seeded inputs.
+
+Sizes span several tiles plus ragged tails; the oracle finishes each case in
+seconds.  Tolerances: float32 paths rel-L2 <= 1e-4, bf16/fp8/MXFP4 paths
+rel-L2 <= 5e-3; top-k indices bit-exact wherever both sides rank the same
+float32 scores; index scores are compared on their exact inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs, formats, gen
+from tests.gpu_util import DEV, dev, host_f64, rel_l2, topk_agreement
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+LOWP_TOL = 5e-3
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def api():
+    from long_context_sparse_04_amd import api as a
+    from long_context_sparse_04_amd import _lib
+    _lib.load()
+    return a
+
+
+def _pos(arr):
+    return torch.tensor(np.asarray(arr, np.int64), device=DEV)
+
+
+# ----------------------------------------------------------------------------- compress
+def _compress_case(api, cfg, indexer=False, hca=False, out_fmt=None, seqs=None):
+    ci = gen.compress_inputs(cfg, indexer=indexer, hca=hca, seqs=seqs)
+    fmt = ci["dtype"]
+    say(f"compress {cfg.name} indexer={indexer} hca={hca} fmt={fmt} out={out_fmt} rows={ci['rows']}")
+    out, osc = api.compress(dev(ci["ca"]), dev(ci["cb"]), dev(ci["za"]), dev(ci["zb"]),
+                            dev(ci["bias_a"]), dev(ci["bias_b"]), ci["m"], ci["row0_pos"], ci["first_entry"],
+                            ci["num_entries"], out_fmt=out_fmt)
+    torch.cuda.synchronize()
+    v = lambda x: None if x is None else oracle.dequant_rows(x, None, fmt)
+    ref = oracle.compress(v(ci["ca"]), v(ci["cb"]), v(ci["za"]), v(ci["zb"]), ci["bias_a"].astype(np.float64),
+                          None if ci["bias_b"] is None else ci["bias_b"].astype(np.float64), ci["m"],
+                          ci["row0_pos"], ci["first_entry"], ci["num_entries"])
+    return out, osc, ref
+
+
+def test_compress_f32_c1(api):
+    for indexer in (False, True):
+        out, _, ref = _compress_case(api, configs.C1, indexer=indexer)
+        got = host_f64(out)
+        assert rel_l2(got, ref) <= 1e-6
+        assert np.max(np.abs(got - ref)) <= 1e-5
+
+
+def test_compress_hca_f32_c1(api):
+    out, _, ref = _compress_case(api, configs.C1, hca=True)
+    assert rel_l2(host_f64(out), ref) <= 1e-6
+
+
+def test_compress_bf16_c4_chunk(api):
+    for indexer in (False, True):
+        out, _, ref = _compress_case(api, configs.C4, indexer=indexer)
+        got = host_f64(out)
+        e = rel_l2(got, ref)
+        assert e <= LOWP_TOL, e
+        # error is bf16 output rounding only: every element within half a bf16 ulp (+ fp32 slack)
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-30)
+
+
+def test_compress_hca_bf16_c4(api):
+    out, _, ref = _compress_case(api, configs.C4, hca=True)
+    got = host_f64(out)
+    assert rel_l2(got, ref) <= LOWP_TOL
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-30)
+
+
+def _codes_close(got_codes, ref_codes, ref_vals_scaled, table):
+    """Codes must match except where the exact value sits within 1e-5 (relative) of a rounding midpoint."""
+    mism = got_codes != ref_codes
+    if not mism.any():
+        return True
+    a = np.abs(ref_vals_scaled[mism])
+    lo = np.abs(table[ref_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
+    hi = np.abs(table[got_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
+    mid = 0.5 * (lo + hi)
+    return bool(np.all(np.abs(a - mid) <= 1e-5 * np.maximum(mid, 1e-30)))
+
+
+def test_compress_quantized_indexer_keys(api):
+    cfg = configs.C3.scaled(B=64)     # decode geometry: one new entry per sequence, many sequences
+    out, osc, ref = _compress_case(api, cfg, indexer=True, out_fmt="fp8")
+    codes = out.cpu().numpy()
+    scale = osc.cpu().numpy().astype(np.float64)
+    rc, rs = oracle.encode_fp8_rows(ref)
+    assert np.allclose(scale, rs, rtol=1e-6, atol=0)
+    assert _codes_close(codes, rc, ref / rs[..., None], oracle.fp8_e4m3_values())
+    deq = oracle.dequant_rows(codes, scale.astype(np.float32), "fp8")
+    assert rel_l2(deq, ref) <= 0.05          # e4m3 has a 3-bit mantissa
+    cfg5 = configs.C5.scaled(B=64)
+    out, osc, ref = _compress_case(api, cfg5, indexer=True, out_fmt="mxfp4")
+    p, e = out.cpu().numpy(), osc.cpu().numpy()
+    rp, re_ = oracle.encode_mxfp4(ref)
+    assert np.array_equal(e, re_)
+    nib = lambda x: np.stack([x & 0xF, x >> 4], -1).reshape(x.shape[:-1] + (-1,))
+    scaled = ref / np.repeat(oracle.decode_e8m0(re_), 32, axis=-1)
+    assert _codes_close(nib(p), nib(rp), scaled, oracle.e2m1_values())
+
+
+def test_compress_into_cache_with_stride(api):
+    cfg = configs.C2.scaled(B=3)
+    ci = gen.compress_inputs(cfg)
+    say("compress into cache rows with out_batch_stride")
+    cache = torch.zeros((3, 10, cfg.c), dtype=torch.bfloat16, device=DEV)
+    api.compress(dev(ci["ca"]), dev(ci["cb"]), dev(ci["za"]), dev(ci["zb"]), dev(ci["bias_a"]), dev(ci["bias_b"]),
+                 ci["m"], ci["row0_pos"], ci["first_entry"], 1, out=cache[:, 7:], out_batch_stride=10)
+    torch.cuda.synchronize()
+    direct, _ = api.compress(dev(ci["ca"]), dev(ci["cb"]), dev(ci["za"]), dev(ci["zb"]), dev(ci["bias_a"]),
+                             dev(ci["bias_b"]), ci["m"], ci["row0_pos"], ci["first_entry"], 1)
+    c = cache.cpu()
+    assert torch.equal(c[:, 7], direct[:, 0].cpu())
+    assert torch.count_nonzero(c[:, :7].float()) == 0 and torch.count_nonzero(c[:, 8:].float()) == 0
+
+
+# ----------------------------------------------------------------------------- index
+def _index_case(api, cfg, pos0):
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    fmt = cfg.idx_dtype
+    say(f"index {cfg.name} fmt={fmt} B={cfg.B} T={cfg.T} N={cfg.n_comp} pos0={list(pos0)}")
+    sc = api.index(dev(qi["data"]), dev(qi.get("scale")), dev(w), dev(kc["data"]), dev(kc.get("scale")), _pos(pos0),
+                   cfg.m, fmt)
+    torch.cuda.synchronize()
+    qv = oracle.dequant_rows(qi["data"], qi.get("scale"), fmt)
+    kv = oracle.dequant_rows(kc["data"], kc.get("scale"), fmt)
+    ref = oracle.index(qv, w, kv, pos0, cfg.m)
+    return sc.cpu().numpy().astype(np.float64), ref
+
+
+def _check_scores(got, ref, rtol):
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(got[~fin] == -np.inf)
+    err = np.abs(got[fin] - ref[fin])
+    scale = np.abs(ref[fin]) + 1e-3 * np.max(np.abs(ref[fin]))
+    assert np.max(err / scale) <= rtol, np.max(err / scale)
+
+
+def test_index_f32_c1(api):
+    cfg = configs.C1
+    got, ref = _index_case(api, cfg, [0])
+    _check_scores(got, ref, 1e-5)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_index_mfma_ragged(api, fmt):
+    base = {"bf16": configs.C2, "fp8": configs.C3, "mxfp4": configs.C5}[fmt]
+    cfg = base.scaled(B=3, n_comp=5000 + 37)
+    pos0 = [4 * (5000 + 37), 4 * 3001 + 2, 4 * 17 + 3]   # full, partial, tiny visibility
+    got, ref = _index_case(api, cfg, pos0)
+    _check_scores(got, ref, 2e-5)
+
+
+def test_index_mfma_prefill_rows(api):
+    cfg = configs.C4.scaled(T=9, n_comp=2100, pos0=4 * 2000 - 5)
+    got, ref = _index_case(api, cfg, [cfg.pos0])
+    _check_scores(got, ref, 2e-5)
+
+
+@pytest.mark.parametrize("hi", [16, 32, 128])
+def test_index_head_counts(api, hi):
+    cfg = configs.C2.scaled(B=2, n_comp=1100, HI=hi)
+    got, ref = _index_case(api, cfg, [4 * 1100, 4 * 700])
+    _check_scores(got, ref, 2e-5)
+
+
+# ----------------------------------------------------------------------------- top-k
+def _topk_case(api, scores32, pos0, m, k, name):
+    say(f"topk {name} shape={scores32.shape} k={k}")
+    idx, vals = api.topk(dev(scores32), _pos(pos0), m, k, want_vals=True)
+    torch.cuda.synchronize()
+    ref = oracle.topk(scores32.astype(np.float64), pos0, m, k)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, ref), f"{name}: {np.argwhere(got != ref)[:5]}"
+    v = vals.cpu().numpy()
+    sc = scores32.astype(np.float64) + 0.0
+    for b in range(got.shape[0]):
+        for r in range(got.shape[1]):
+            sel = got[b, r][got[b, r] >= 0]
+            assert np.array_equal(v[b, r, :len(sel)], sc[b, r, sel].astype(np.float32) + np.float32(0.0))
+            assert np.all(v[b, r, len(sel):] == -np.inf)
+
+
+def test_topk_row_path_c1_scores(api):
+    cfg = configs.C1
+    qi, w = gen.indexer_queries(cfg)
+    kc = gen.indexer_key_cache(cfg)
+    ref = oracle.index(qi["data"].astype(np.float64), w, kc["data"].astype(np.float64), [0], cfg.m)
+    _topk_case(api, ref.astype(np.float32), [0], cfg.m, cfg.k, "c1 oracle scores")
+
+
+def test_topk_split_path_with_ties(api):
+    rng = np.random.default_rng(11)
+    N = 262144
+    s = (np.round(rng.standard_normal((4, 1, N)) * 64) / 64).astype(np.float32)  # heavy ties
+    s[0, 0, ::7] = 0.0
+    s[0, 0, 3::7] = -0.0
+    pos0 = [4 * N, 4 * (N - 1000) + 3, 4 * 20000, 4 * N + 100]
+    _topk_case(api, s, pos0, 4, 1024, "split path with ties")
+
+
+def test_topk_edge_cases(api):
+    rng = np.random.default_rng(12)
+    N = 40000
+    s = rng.standard_normal((3, 1, N)).astype(np.float32)
+    s[1, 0, :] = 1.5                          # all equal: candidates overflow the LDS cache
+    _topk_case(api, s, [4 * N, 4 * N, 4 * 100], 4, 2048, "split path edge cases (all-equal, k > V)")
+    s2 = rng.standard_normal((2, 70, 300)).astype(np.float32)
+    s2[1, :, :150] = 0.0
+    _topk_case(api, s2, [0, 4 * 299], 4, 1, "row path k=1")
+    _topk_case(api, s2, [0, 4 * 299], 4, 64, "row path k=64 with zeros")
+    s3 = rng.standard_normal((1, 2, 50000)).astype(np.float32)  # row path without LDS key cache
+    _topk_case(api, s3, [4 * 50000 - 1], 4, 700, "row path, uncached keys")
+
+
+# ----------------------------------------------------------------------------- attend
+def _rand_idx(rng, B, T, k, pos0, m, n_max, fill=0.9):
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for r in range(T):
+            vis = min((pos0[b] + r) // m, n_max)
+            n = min(k, vis, int(fill * k))
+            if n:
+                idx[b, r, :n] = np.sort(rng.choice(vis, size=n, replace=False))
+    return idx
+
+
+def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False):
+    q = gen.queries(cfg, hca=hca)
+    cache = gen.kv_cache(cfg, hca=hca)
+    win = gen.window(cfg, hca=hca)
+    sink = gen.sink(cfg, hca=hca)
+    fmt = cfg.kv_dtype
+    rng = np.random.default_rng(5)
+    gq = rng.uniform(0.5, 1.5, cfg.c).astype(np.float32) if gamma else None
+    gk = rng.uniform(0.5, 1.5, cfg.c).astype(np.float32) if gamma else None
+    say(f"{'hca' if hca else 'csa'}_attend {cfg.name} fmt={fmt} B={cfg.B} T={cfg.T} H={cfg.H} c={cfg.c} "
+        f"N={cache.shape[1]} gamma={gamma}")
+    if hca:
+        out = api.hca_attend(dev(q), dev(cache), dev(win), dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, cfg.rope_dims,
+                             cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk))
+    else:
+        out = api.attend(dev(q), dev(cache), dev(idx), dev(win), dev(sink), _pos(pos0), cfg.m, cfg.n_win,
+                         cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk))
+    torch.cuda.synchronize()
+    v = lambda x: oracle.dequant_rows(x, None, fmt)
+    if hca:
+        ref = oracle.hca_attend(v(q), v(cache), v(win), sink, pos0, cfg.m_hca, cfg.n_win, cfg.rope_dims, cfg.scale,
+                                cfg.eps, cfg.rope_base, gamma_q=gq, gamma_kv=gk)
+    else:
+        ref = oracle.attend(v(q), v(cache), idx, v(win), sink, pos0, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
+                            cfg.eps, cfg.rope_base, gamma_q=gq, gamma_kv=gk)
+    return host_f64(out), ref
+
+
+def test_attend_f32_c1(api):
+    cfg = configs.C1
+    rng = np.random.default_rng(1)
+    idx = _rand_idx(rng, 1, cfg.T, cfg.k, [0], cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, [0], idx)
+    assert rel_l2(got, ref) <= F32_TOL
+
+
+def test_attend_bf16_decode(api):
+    cfg = configs.C3.scaled(B=2, n_comp=3000)
+    pos0 = [4 * 3000, 4 * 2500 + 1]
+    idx = _rand_idx(np.random.default_rng(2), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, pos0, idx)
+    e = rel_l2(got, ref)
+    say(f"  rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+
+
+def test_attend_bf16_prefill(api):
+    cfg = configs.C4.scaled(T=40, n_comp=200, pos0=700, k=64)
+    idx = _rand_idx(np.random.default_rng(3), 1, cfg.T, cfg.k, [700], cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, [700], idx)
+    e = rel_l2(got, ref)
+    say(f"  rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+
+
+def test_attend_bf16_flash_heads_and_small_c(api):
+    cfg = configs.C2.scaled(B=3, n_comp=900, k=100)
+    pos0 = [4 * 900, 4 * 300, 40]
+    idx = _rand_idx(np.random.default_rng(4), 3, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, pos0, idx)
+    assert rel_l2(got, ref) <= LOWP_TOL
+    cfg = configs.C2.scaled(B=2, n_comp=300, k=50, c=128, H=16, rope_dims=32)
+    pos0 = [4 * 300, 4 * 11]
+    idx = _rand_idx(np.random.default_rng(6), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, pos0, idx)
+    assert rel_l2(got, ref) <= LOWP_TOL
+
+
+def test_attend_gains(api):
+    cfg = configs.C2.scaled(B=2, n_comp=500, k=64)
+    pos0 = [4 * 500, 4 * 123]
+    idx = _rand_idx(np.random.default_rng(7), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, pos0, idx, gamma=True)
+    assert rel_l2(got, ref) <= LOWP_TOL
+    cfg1 = configs.C1.scaled(T=64, n_comp=16)
+    idx = _rand_idx(np.random.default_rng(8), 1, 64, 64, [0], 4, 16)
+    got, ref = _attend_case(api, cfg1, [0], idx, gamma=True)
+    assert rel_l2(got, ref) <= F32_TOL
+
+
+def test_hca_attend_f32_c1(api):
+    cfg = configs.C1
+    got, ref = _attend_case(api, cfg, [0], None, hca=True)
+    assert rel_l2(got, ref) <= F32_TOL
+
+
+def test_hca_attend_bf16_decode_and_prefill(api):
+    cfg = configs.C5.scaled(B=2, n_hca=700)
+    pos0 = [128 * 700, 128 * 333 + 5]
+    got, ref = _attend_case(api, cfg, pos0, None, hca=True)
+    e = rel_l2(got, ref)
+    say(f"  decode rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+    cfg = configs.C4.scaled(T=48, n_hca=40, pos0=128 * 30 + 7)
+    got, ref = _attend_case(api, cfg, [cfg.pos0], None, hca=True)
+    e = rel_l2(got, ref)
+    say(f"  prefill rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+
+
+def test_attend_deterministic_and_batch_invariant(api):
+    cfg = configs.C3.scaled(B=4, n_comp=2000)
+    pos0 = [8000, 7000, 6000, 5000]
+    q = dev(gen.queries(cfg))
+    cache = dev(gen.kv_cache(cfg))
+    win = dev(gen.window(cfg))
+    sink = dev(gen.sink(cfg))
+    idx = dev(_rand_idx(np.random.default_rng(9), 4, 1, cfg.k, pos0, cfg.m, cfg.n_comp))
+    say("attend determinism / batch invariance")
+    a1 = api.attend(q, cache, idx, win, sink, _pos(pos0), cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale)
+    a2 = api.attend(q, cache, idx, win, sink, _pos(pos0), cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale)
+    one = api.attend(q[2:3].contiguous(), cache[2:3].contiguous(), idx[2:3].contiguous(), win[2:3].contiguous(),
+                     sink, _pos(pos0[2:3]), cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
+    assert torch.equal(a1[2:3].view(torch.int16), one.view(torch.int16))
+
+
+# ----------------------------------------------------------------------------- whole step
+def test_pipeline_c1_end_to_end(api):
+    """compress -> index -> top-k -> attend on the GPU against the oracle's own pipeline (fp32: exact top-k)."""
+    cfg = configs.C1
+    kv = gen.compress_inputs(cfg)
+    ik = gen.compress_inputs(cfg, indexer=True)
+    qi, w = gen.indexer_queries(cfg)
+    q = gen.queries(cfg)
+    win = gen.window(cfg)
+    sink = gen.sink(cfg)
+    say("c1 pipeline")
+    t = lambda a: dev(a)
+    ckv, _ = api.compress(t(kv["ca"]), t(kv["cb"]), t(kv["za"]), t(kv["zb"]), t(kv["bias_a"]), t(kv["bias_b"]), 4,
+                          0, 0, cfg.n_comp)
+    cik, _ = api.compress(t(ik["ca"]), t(ik["cb"]), t(ik["za"]), t(ik["zb"]), t(ik["bias_a"]), t(ik["bias_b"]), 4,
+                          0, 0, cfg.n_comp)
+    pos = _pos([0])
+    sc = api.index(t(qi["data"]), None, t(w), cik, None, pos, 4, "f32")
+    idx, _ = api.topk(sc, pos, 4, cfg.k)
+    out = api.attend(t(q), ckv, idx, t(win), t(sink), pos, 4, cfg.n_win, cfg.rope_dims, cfg.scale, cfg.eps,
+                     cfg.rope_base)
+    torch.cuda.synchronize()
+    f = lambda a: None if a is None else np.asarray(a, np.float64)
+    r_ckv = oracle.compress(f(kv["ca"]), f(kv["cb"]), f(kv["za"]), f(kv["zb"]), f(kv["bias_a"]), f(kv["bias_b"]), 4,
+                            0, 0, cfg.n_comp)
+    r_cik = oracle.compress(f(ik["ca"]), f(ik["cb"]), f(ik["za"]), f(ik["zb"]), f(ik["bias_a"]), f(ik["bias_b"]), 4,
+                            0, 0, cfg.n_comp)
+    r_sc = oracle.index(f(qi["data"]), w, r_cik, [0], 4)
+    r_idx = oracle.topk(r_sc, [0], 4, cfg.k)
+    r_out = oracle.attend(f(q), r_ckv, r_idx, f(win), sink, [0], 4, cfg.n_win, cfg.rope_dims, cfg.scale, cfg.eps,
+                          cfg.rope_base)
+    gi = idx.cpu().numpy()
+    # minimum relative gap at the k-th boundary, logged for diagnosis
+    agree, bad = topk_agreement(gi, r_idx, r_sc)
+    say(f"  top-k agreement {agree:.6f}, rows identical {np.mean(np.all(gi == r_idx, axis=-1)):.6f}")
+    assert np.array_equal(gi, r_idx)
+    assert rel_l2(host_f64(out), r_out) <= F32_TOL
