@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA decode layer step on one MI355X.
+
+One step = one pass of the whole CSA layer step over one decode batch:
+  csa_compress (KV entry that completes at this step)  ->  csa_compress (indexer
+  key, quantized to the cache format)  ->  csa_index  ->  csa_topk  ->  csa_attend
+(plus, for the Pro MXFP4 workload, the HCA layer: compress + hca_attend).
+
+Default workload: Pro-shaped decode at 1M context (B=4, 262,144 compressed
+entries, 128 heads x 512, fp8 e4m3 indexer with row scales, top-k 1024, window
+128).  `value` is per-layer decode tokens/s = B / step time, inputs resident in
+HBM.  Four input sets (distinct queries, and separate copies of the indexer-key
+cache, 4 x 138 MB) are rotated so that no step finds its working set in the
+256 MB Infinity Cache.
+
+Prints ONE JSON line (see --help for options).
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import configs, gen  # noqa: E402
+
+METRIC = "CSA decode tokens/s at 1M ctx (Pro shape) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+NSETS = 4
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="c3", help="c3 (default), c2 or c5")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- inputs
+def _gen_seq(args):
+    """Host arrays of one sequence (runs in a worker process)."""
+    name, b = args
+    cfg = configs.get_config(name)
+    out = {
+        "kv": gen.kv_cache(cfg, seqs=[b])[0],
+        "ik": {k: v[0] for k, v in gen.indexer_key_cache(cfg, seqs=[b]).items()},
+    }
+    if cfg.with_hca:
+        out["hca"] = gen.kv_cache(cfg, seqs=[b], hca=True)[0]
+    return b, out
+
+
+def host_inputs(cfg, seed):
+    c = cfg.scaled(seed=seed)
+    qi, w = gen.indexer_queries(c)
+    d = {
+        "q": gen.queries(c), "qi": qi, "w": w, "win": gen.window(c), "sink": gen.sink(c),
+        "ckv": gen.compress_inputs(c), "cik": gen.compress_inputs(c, indexer=True),
+    }
+    if cfg.with_hca:
+        d.update(hq=gen.queries(c, hca=True), hwin=gen.window(c, hca=True), hsink=gen.sink(c, hca=True),
+                 chca=gen.compress_inputs(c, hca=True))
+    return d
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_sparse_04_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- bench
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path: the decode "
+              "batch shards by sequence with no exchange, so N GPUs run N independent copies of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from long_context_sparse_04_amd import _lib, api
+
+    cfg = configs.get_config(a.config)
+    assert cfg.T == 1, "bench.py times the decode step"
+    _lib.load()
+    dev = "cuda:0"
+    B, N = cfg.B, cfg.n_comp
+    fmt = cfg.idx_dtype
+
+    def up(x):
+        if x is None:
+            return None
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.time()
+    nproc = max(1, min(B, len(os.sched_getaffinity(0)), 8))
+    kv_cache = torch.empty((B, N, cfg.c), dtype=torch.bfloat16, device=dev)
+    ik_rows = 64 if fmt == "mxfp4" else 128
+    ik_data = torch.empty((B, N, ik_rows), dtype=torch.uint8 if fmt != "bf16" else torch.bfloat16, device=dev)
+    if fmt == "bf16":
+        ik_data = torch.empty((B, N, cfg.cI), dtype=torch.bfloat16, device=dev)
+    ik_scale = None
+    if fmt == "fp8":
+        ik_scale = torch.empty((B, N), dtype=torch.float32, device=dev)
+    elif fmt == "mxfp4":
+        ik_scale = torch.empty((B, N, 4), dtype=torch.uint8, device=dev)
+    hca_cache = torch.empty((B, cfg.n_hca, cfg.c), dtype=torch.bfloat16, device=dev) if cfg.with_hca else None
+    host0 = {"kv": [None] * B, "ik_data": [None] * B, "ik_scale": [None] * B, "hca": [None] * B}
+    with cf.ProcessPoolExecutor(max_workers=nproc) as ex:
+        for b, out in ex.map(_gen_seq, [(cfg.name, b) for b in range(B)]):
+            kv_cache[b].copy_(up(out["kv"]))
+            ik_data[b].copy_(up(out["ik"]["data"]))
+            if ik_scale is not None:
+                ik_scale[b].copy_(up(out["ik"]["scale"]))
+            if cfg.with_hca:
+                hca_cache[b].copy_(up(out["hca"]))
+            if b == 0 or not a.no_cpu_baseline:
+                host0["kv"][b] = out["kv"]
+                host0["ik_data"][b] = out["ik"]["data"]
+                host0["ik_scale"][b] = out["ik"].get("scale")
+                host0["hca"][b] = out.get("hca")
+    # rotated sets: distinct queries (seed s), own copy of the indexer-key cache
+    sets = []
+    for s in range(NSETS):
+        h = host_inputs(cfg, s)
+        st = {k: up(v) for k, v in (("q", h["q"]), ("w", h["w"]), ("win", h["win"]), ("sink", h["sink"]))}
+        st["qi"] = up(h["qi"]["data"])
+        st["qi_scale"] = up(h["qi"].get("scale"))
+        st["ik"] = ik_data if s == 0 else ik_data.clone()
+        st["ik_scale"] = ik_scale if (s == 0 or ik_scale is None) else ik_scale.clone()
+        for nm in ("ckv", "cik") + (("chca",) if cfg.with_hca else ()):
+            st[nm] = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in h[nm].items()}
+        if cfg.with_hca:
+            st.update(hq=up(h["hq"]), hwin=up(h["hwin"]), hsink=up(h["hsink"]))
+        st["host"] = h if s == 0 else None
+        sets.append(st)
+    pos = torch.full((B,), cfg.pos0, dtype=torch.int64, device=dev)
+    scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, 1, cfg.k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, 1, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
+    hout = torch.empty_like(out) if cfg.with_hca else None
+    torch.cuda.synchronize()
+    t_setup = time.time() - t0
+
+    first = N - 1  # the entry completed by the block ending at pos0-1
+
+    def step(st, ev=None):
+        c = st["ckv"]
+        api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
+                     c["first_entry"], 1, out=kv_cache[:, first:], out_batch_stride=N)
+        c = st["cik"]
+        if fmt == "fp8":
+            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
+                         c["first_entry"], 1, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
+                         out_fmt="fp8", out_batch_stride=N)
+        elif fmt == "mxfp4":
+            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
+                         c["first_entry"], 1, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
+                         out_fmt="mxfp4", out_batch_stride=N)
+        else:
+            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
+                         c["first_entry"], 1, out=st["ik"][:, first:], out_batch_stride=N)
+        if ev is not None:
+            ev[0].record()
+        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
+        if ev is not None:
+            ev[1].record()
+        api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
+        api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
+                   cfg.eps, cfg.rope_base, out=out)
+        if cfg.with_hca:
+            c = st["chca"]
+            api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
+                         c["first_entry"], 1, out=hca_cache[:, c["first_entry"]:], out_batch_stride=cfg.n_hca)
+            api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
+                           cfg.scale, cfg.eps, cfg.rope_base, out=hout)
+
+    for i in range(a.warmup):
+        step(sets[i % NSETS])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(a.steps):
+        step(sets[i % NSETS], evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / a.steps
+    idx_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    # algorithmic bytes of one csa_index launch: every visible K^I row (+ its scales) read once,
+    # the queries / weights read once per sequence, one float32 score written per entry
+    row_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt]
+    q_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt] * cfg.HI + 4 * cfg.HI
+    idx_bytes = B * (N * row_bytes + q_bytes + N * 4)
+    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
+    if os.path.exists(tpath):
+        t = json.load(open(tpath))
+        if t.get("source_hash") == source_hash("index.hip"):
+            traffic = t.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC if cfg.name == configs.C3.name else f"CSA decode tokens/s ({cfg.name}) + % HBM roofline",
+        "value": B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"fp8": "fp8+bf16", "mxfp4": "mxfp4+bf16", "bf16": "bf16"}[fmt],
+        "data": "synthetic (seeded Gaussian, synth/gen.py recipe)",
+        "config": {"workload": cfg.name, "batch": B, "context": cfg.pos0, "compressed_entries": N, "heads": cfg.H,
+                   "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
+                   "hca_entries": cfg.n_hca if cfg.with_hca else 0, "input_sets_rotated": NSETS},
+        "roofline": {"kernel": "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms},
+        "setup_s": round(t_setup, 1),
+    }
+
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, sets[0]["host"], host0)
+    print(json.dumps(res), flush=True)
+
+
+class _Bf16Rows:
+    """Read-only view of a bf16 cache [1][N][c] that decodes only the rows indexed (plus overridden rows)."""
+
+    def __init__(self, bits, override):
+        self.bits, self.override = bits, override
+
+    def __getitem__(self, key):
+        import oracle
+        b, rows = key
+        out = oracle.decode_bf16(self.bits[b, rows])
+        for j, r in enumerate(rows):
+            if (b, int(r)) in self.override:
+                out[j] = self.override[(b, int(r))]
+        return out
+
+
+def cpu_baseline(cfg, h, host0):
+    """The float64 oracle, as it stands, on whole decode steps of the same workload (about 10 s of host work)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    fmt = cfg.idx_dtype
+    t0 = time.time()
+    B = cfg.B
+    pos0 = np.full(B, cfg.pos0)
+    deq = lambda d, s: oracle.dequant_rows(d, s, fmt)
+    ck = h["ckv"]
+    f = lambda x: None if x is None else oracle.decode_bf16(x)
+    new_kv = oracle.compress(f(ck["ca"]), f(ck["cb"]), f(ck["za"]), f(ck["zb"]), ck["bias_a"].astype(np.float64),
+                             ck["bias_b"].astype(np.float64), cfg.m, ck["row0_pos"], ck["first_entry"], 1)
+    ci = h["cik"]
+    new_ik = oracle.compress(f(ci["ca"]), f(ci["cb"]), f(ci["za"]), f(ci["zb"]), ci["bias_a"].astype(np.float64),
+                             ci["bias_b"].astype(np.float64), cfg.m, ci["row0_pos"], ci["first_entry"], 1)
+    done = 0
+    while True:  # whole decode steps (all B sequences) until >= 10 s of CPU work, bounded at ~30 s
+        for b in range(B):
+            kI = deq(host0["ik_data"][b], host0["ik_scale"][b])[None]
+            kI[0, -1] = new_ik[b, 0]
+            qI = deq(h["qi"]["data"][b:b + 1], None if h["qi"].get("scale") is None else h["qi"]["scale"][b:b + 1])
+            sc = oracle.index(qI, h["w"][b:b + 1], kI, pos0[b:b + 1], cfg.m)
+            sel = oracle.topk(sc, pos0[b:b + 1], cfg.m, cfg.k)
+            cache = _Bf16Rows(host0["kv"][b][None], {(0, cfg.n_comp - 1): new_kv[b, 0]})
+            oracle.attend(oracle.decode_bf16(h["q"][b:b + 1]), cache, sel, oracle.decode_bf16(h["win"][b:b + 1]),
+                          h["sink"], pos0[b:b + 1], cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, cfg.eps,
+                          cfg.rope_base)
+            done += 1
+        if time.time() - t0 > 10:
+            break
+    dt = time.time() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done // B} full decode steps x {B} sequences (compress, index, top-k, attend) in "
+                      f"float64, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -212,7 +212,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
         const int d0 = 8 * (sub + 8 * j);
-        if (valid && (d0 >= rope_lo || a.gamma_kv)) {
+        // non-RoPE dims stay raw (their gain is folded into q and the output); RoPE dims get gain + rotation
+        if (valid && d0 >= rope_lo) {
           float x[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) { x[2 * q] = bf(v[j][q], 0); x[2 * q + 1] = bf(v[j][q], 1); }
@@ -220,15 +221,13 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
             for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
           }
-          if (d0 >= rope_lo) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              float cs, sn;
-              rope_cs(sl.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
-              float x0 = x[2 * p], x1 = x[2 * p + 1];
-              x[2 * p] = x0 * cs - x1 * sn;
-              x[2 * p + 1] = x0 * sn + x1 * cs;
-            }
+          for (int p = 0; p < 4; ++p) {
+            float cs, sn;
+            rope_cs(sl.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+            float x0 = x[2 * p], x1 = x[2 * p + 1];
+            x[2 * p] = x0 * cs - x1 * sn;
+            x[2 * p + 1] = x0 * sn + x1 * cs;
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[j][q] = (uint32_t)f32_to_bf16(x[2 * q]) | ((uint32_t)f32_to_bf16(x[2 * q + 1]) << 16);
