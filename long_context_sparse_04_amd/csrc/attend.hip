@@ -8,10 +8,13 @@
 // rotated at -t; the uncompressed sliding window; a per-head sink logit added to
 // the softmax denominator).
 //
-// BF16 path (MFMA).  A workgroup of 4 waves serves one query row and 64 heads
-// (16 per wave).  Entry slots are staged 32 at a time into LDS, once per
-// workgroup, in two layouts: entry-major (A operand of S^T = E Q^T) and dim-major
-// (B operand of O = P E).  RMSNorm is factored as a per-entry scalar r_e and a
+// BF16 path (MFMA).  A workgroup of 4 waves serves one query row, one part of
+// its entry list and 16 heads; wave w owns a quarter of the c dims.  Entry slots
+// are staged 32 at a time into one entry-major LDS tile (the A operand of
+// S^T = E Q^T; the B operand of O = P E comes from the same tile through the
+// gfx950 transpose read), while the next tile's loads are in flight.  Each wave
+// forms a partial S^T over its dims; the four partials are summed through LDS in a
+// fixed order, so every wave holds the same logits.  RMSNorm is factored as a per-entry scalar r_e and a
 // per-query scalar r_q applied to the float32 logits, so the non-RoPE dims of q
 // and e enter the MFMA as their exact bf16 input bits; only the rotated RoPE dims
 // (and gains, if given) are rounded to bf16.  With S^T in the MFMA output layout
@@ -19,9 +22,10 @@
 // only in-lane work plus two cross-group shuffles, and the probabilities
 // (times r_e) are already in the A-operand layout of the PV MFMA.
 //
-// Decode (T = 1) splits each query's slot list at fixed 128-slot boundaries and
-// merges the parts in a fixed order in a second kernel; prefill (T > 1) runs one
-// part per query and finishes in place.
+// Decode (T = 1) splits each query's slot list into at most 16 parts at fixed
+// boundaries (a length that depends only on the list length) and merges the
+// parts in a fixed order in a second kernel; prefill (T > 1) runs one part per
+// query and finishes in place.
 //
 // F32 path (VALU): one workgroup per (query row, head group), waves take entries
 // round-robin with their own online softmax and are merged in a fixed order.
@@ -89,59 +93,147 @@ CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vi
 
 CSA_DEV float bf(uint32_t word, int hi) { return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16)); }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (gfx950): inside each 16-lane group, lane 4r+c supplies the
+// address of 4 consecutive bf16 of "row" r; lane i receives column i of the 4x16
+// block, i.e. element (i & 3) of lane 4r + (i >> 2)'s chunk, for r = 0..3.
+CSA_DEV i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// Staged-slot registers of one lane: 8 lanes per slot, NCH 16-byte chunks each.
+template <int NCH>
+struct StageRegs {
+  u32x4 v[NCH];
+  double pos;
+  bool valid;
+};
+
 template <int C>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt) {
-  constexpr int KS = C / 32;       // k-steps of S^T = E Q^T
-  constexpr int DT = C / 16;       // dim tiles of O
-  constexpr int NCH = C / 64;      // 16-byte chunks per staging lane
-  constexpr int E1S = C + 8;       // halfwords per entry-major LDS row
+CSA_DEV StageRegs<C / 64> stage_load(const AttnArgs& a, int b, int r, int64_t t, int64_t vis, int64_t slot,
+                                     int64_t slot_hi, int sub) {
+  StageRegs<C / 64> s;
+  Slot sl;
+  sl.row = -1;
+  if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
+  s.valid = sl.row >= 0;
+  s.pos = sl.pos;
+  const uint16_t* src = s.valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
+                                             : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
+                                : nullptr;
+#pragma unroll
+  for (int j = 0; j < C / 64; ++j)
+    s.v[j] = s.valid ? *reinterpret_cast<const u32x4*>(src + 8 * (sub + 8 * j)) : u32x4{0u, 0u, 0u, 0u};
+  return s;
+}
+
+// Per-entry RMS scalar, RoPE (and gain) of the RoPE dims, then the entry-major LDS row.
+template <int C>
+CSA_DEV void stage_store(const AttnArgs& a, const RopeTable& rt, StageRegs<C / 64>& s, uint16_t* E1, float* s_re,
+                         int es, int sub) {
+  constexpr int E1S = C + 8;
+  const int rope_lo = C - a.R;
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < C / 64; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = bf(s.v[j][q], 0), x1 = bf(s.v[j][q], 1);
+      ss = fmaf(x0, x0, ss);
+      ss = fmaf(x1, x1, ss);
+    }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  if (sub == 0) s_re[es] = s.valid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
+#pragma unroll
+  for (int j = 0; j < C / 64; ++j) *reinterpret_cast<u32x4*>(E1 + es * E1S + 8 * (sub + 8 * j)) = s.v[j];
+  if (!s.valid) return;
+  // RoPE dims (and their gain) in place, on this lane's own chunks; non-RoPE dims stay raw because
+  // their gain is folded into q and the output
+#pragma unroll 1
+  for (int j = 0; j < C / 64; ++j) {
+    const int d0 = 8 * (sub + 8 * j);
+    if (d0 < rope_lo) continue;
+    u32x4* cp = reinterpret_cast<u32x4*>(E1 + es * E1S + d0);
+    u32x4 w = *cp;
+    float x[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w[q], 0); x[2 * q + 1] = bf(w[q], 1); }
+    if (a.gamma_kv) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float cs, sn;
+      rope_cs(s.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+      const float x0 = x[2 * p], x1 = x[2 * p + 1];
+      x[2 * p] = x0 * cs - x1 * sn;
+      x[2 * p + 1] = x0 * sn + x1 * cs;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16(x[2 * q]) | ((uint32_t)f32_to_bf16(x[2 * q + 1]) << 16);
+    *cp = w;
+  }
+}
+
+// One workgroup = one query row x one decode part x 16 heads; wave w owns dims [w*C/4, (w+1)*C/4).
+template <int C>
+__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int split_slots, int nx) {
+  constexpr int DW = C / 4;    // dims per wave
+  constexpr int KSW = DW / 32; // k-steps of the wave's partial S^T = E Q^T
+  constexpr int DTW = DW / 16; // 16-dim output tiles of the wave
+  constexpr int E1S = C + 8;   // halfwords per entry-major LDS row
   extern __shared__ __align__(16) uint16_t s_mem[];
-  uint16_t* E1 = s_mem;                                   // [32][E1S]
-  uint16_t* E2 = s_mem + kTile * E1S;                     // [C][kE2Stride]
-  float* s_re = reinterpret_cast<float*>(E2 + C * kE2Stride);  // [32]
+  uint16_t* E1 = s_mem;                                              // [32][E1S]
+  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + kTile * E1S);     // [4 waves][2][64 lanes]
+  float* s_re = reinterpret_cast<float*>(s_part + 4 * 2 * 64);       // [32]
+  float* s_rq = s_re + kTile;                                        // [4][16]
   __shared__ int s_any;
 
+  if ((int)blockIdx.x >= nx) return;  // grid.x is padded to a multiple of 8 (XCD-aligned head groups)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;
-  const int sp = blockIdx.x;
-  const int row = blockIdx.z;
+  const int sp = blockIdx.x % a.nsplit;
+  const int row = blockIdx.x / a.nsplit;
   const int b = row / a.T;
   const int r = row - b * a.T;
   const int64_t t = a.pos0[b] + r;
   const int64_t vis = visible_entries(t, a.m, a.n_max);
-  const int head = blockIdx.y * 64 + wave * 16 + (lane & 15);
-  const bool wave_active = (blockIdx.y * 64 + wave * 16) < a.H;
-  const int R = a.R;
-  const int rope_lo = C - R;
+  const int h0 = blockIdx.y * 16;
+  const int head = h0 + (lane & 15);
+  const int rope_lo = C - a.R;
   const int64_t nslots = ((a.mode == 0) ? a.k : a.n_max) + a.n_win;
-  const int64_t slot_lo = (int64_t)sp * (a.nsplit > 1 ? kSplitSlots : nslots);
-  const int64_t slot_hi = a.nsplit > 1 ? min(slot_lo + kSplitSlots, nslots) : nslots;
+  const int64_t slot_lo = (int64_t)sp * split_slots;
+  const int64_t slot_hi = min(slot_lo + split_slots, nslots);
   const double tpos = (double)t;
+  const int dbase = wave * DW;
 
-  // ---- query fragment (B operand of S^T): head = lane&15, dims [32ks + 8g, +8)
-  bf16x8 qf[KS];
-  float r_q = 0.0f;
-  if (wave_active) {
-    const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C;
+  // ---- query fragment: head lane&15, the wave's dims [dbase + 32ks + 8g, +8)
+  bf16x8 qf[KSW];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C + dbase;
+    u32x4 raw[KSW];
     float ss = 0.0f;
-    u32x4 raw[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KSW; ++ks) {
       raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float x0 = bf(raw[ks][j], 0), x1 = bf(raw[ks][j], 1);
+        const float x0 = bf(raw[ks][j], 0), x1 = bf(raw[ks][j], 1);
         ss = fmaf(x0, x0, ss);
         ss = fmaf(x1, x1, ss);
       }
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    r_q = 1.0f / sqrtf(ss / (float)C + a.eps);
+    if (g == 0) s_rq[wave * 16 + (lane & 15)] = ss;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = 32 * ks + 8 * g;
+    for (int ks = 0; ks < KSW; ++ks) {
+      const int d0 = dbase + 32 * ks + 8 * g;
       if (d0 >= rope_lo || a.gamma_q || a.gamma_kv) {
         float x[8];
 #pragma unroll
@@ -155,7 +247,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
           for (int p = 0; p < 4; ++p) {
             float cs, sn;
             rope_cs(tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
-            float x0 = x[2 * p], x1 = x[2 * p + 1];
+            const float x0 = x[2 * p], x1 = x[2 * p + 1];
             x[2 * p] = x0 * cs - x1 * sn;
             x[2 * p + 1] = x0 * sn + x1 * cs;
           }
@@ -164,113 +256,67 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
           for (int j = 0; j < 8; ++j) x[j] *= a.gamma_kv[d0 + j];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw[ks][j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+        for (int j = 0; j < 4; ++j)
+          raw[ks][j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
       }
       qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
     }
   }
-  const float zmul = a.scale * r_q;
 
-  f32x4 O[DT];
+  f32x4 O[DTW];
 #pragma unroll
-  for (int d = 0; d < DT; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < DTW; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15
 
+  const int es = 8 * wave + (lane >> 3);  // slot this lane stages
+  const int sub = lane & 7;
+  StageRegs<C / 64> st = stage_load<C>(a, b, r, t, vis, slot_lo + es, slot_hi, sub);
+  __syncthreads();
+  const float zmul = a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
+                                      s_rq[48 + (lane & 15)]) / (float)C + a.eps);
+
   for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kTile) {
-    // ---- stage 32 slots: wave w stages slots 8w..8w+7, 8 lanes per slot
-    {
-      const int es = 8 * wave + (lane >> 3);
-      const int sub = lane & 7;
-      const int64_t slot = s0 + es;
-      Slot sl;
-      sl.row = -1;
-      if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
-      const bool valid = sl.row >= 0;
-      const uint16_t* src = valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
-                                               : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
-                                  : nullptr;
-      u32x4 v[NCH];
-      float ss = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        if (valid) {
-          v[j] = *reinterpret_cast<const u32x4*>(src + 8 * (sub + 8 * j));
-        } else {
-          v[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float x0 = bf(v[j][q], 0), x1 = bf(v[j][q], 1);
-          ss = fmaf(x0, x0, ss);
-          ss = fmaf(x1, x1, ss);
-        }
-      }
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
-      ss += __shfl_xor(ss, 4, 64);
-      if (sub == 0) s_re[es] = valid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int d0 = 8 * (sub + 8 * j);
-        // non-RoPE dims stay raw (their gain is folded into q and the output); RoPE dims get gain + rotation
-        if (valid && d0 >= rope_lo) {
-          float x[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { x[2 * q] = bf(v[j][q], 0); x[2 * q + 1] = bf(v[j][q], 1); }
-          if (a.gamma_kv) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
-          }
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            float cs, sn;
-            rope_cs(sl.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
-            float x0 = x[2 * p], x1 = x[2 * p + 1];
-            x[2 * p] = x0 * cs - x1 * sn;
-            x[2 * p + 1] = x0 * sn + x1 * cs;
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[j][q] = (uint32_t)f32_to_bf16(x[2 * q]) | ((uint32_t)f32_to_bf16(x[2 * q + 1]) << 16);
-        }
-        *reinterpret_cast<u32x4*>(E1 + es * E1S + d0) = v[j];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          E2[(d0 + 2 * q) * kE2Stride + es] = (uint16_t)(v[j][q] & 0xFFFFu);
-          E2[(d0 + 2 * q + 1) * kE2Stride + es] = (uint16_t)(v[j][q] >> 16);
-        }
-      }
-      if (threadIdx.x == 0) s_any = 0;
-      __syncthreads();
-      if (valid && sub == 0) s_any = 1;
-      __syncthreads();
-    }
-    if (s_any && wave_active) {
-      // ---- S^T = E Q^T : lane holds entries 16nt + 4g + i, head lane&15
-      f32x4 st[2];
+    if (threadIdx.x == 0) s_any = 0;
+    stage_store<C>(a, rt, st, E1, s_re, es, sub);
+    const bool any_mine = st.valid;
+    __syncthreads();
+    if (any_mine && sub == 0) s_any = 1;
+    // prefetch the next tile's slots while this one is computed
+    if (s0 + kTile < slot_hi) st = stage_load<C>(a, b, r, t, vis, s0 + kTile + es, slot_hi, sub);
+    __syncthreads();
+    if (s_any) {
+      // ---- partial S^T over the wave's dims: lane holds entries 16nt + 4g + i, head lane&15
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* ea = E1 + (16 * nt + (lane & 15)) * E1S + 8 * g;
+        const uint16_t* ea = E1 + (16 * nt + (lane & 15)) * E1S + dbase + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          bf16x8 ef = *reinterpret_cast<const bf16x8*>(ea + 32 * ks);
+        for (int ks = 0; ks < KSW; ++ks) {
+          const bf16x8 ef = *reinterpret_cast<const bf16x8*>(ea + 32 * ks);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], acc, 0, 0, 0);
         }
-        st[nt] = acc;
+        s_part[(wave * 2 + nt) * 64 + lane] = acc;
       }
+      __syncthreads();
       float z[8], re[8];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 sum = s_part[(0 * 2 + nt) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          const f32x4 pw = s_part[(w * 2 + nt) * 64 + lane];
+          sum[0] += pw[0]; sum[1] += pw[1]; sum[2] += pw[2]; sum[3] += pw[3];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int e = 16 * nt + 4 * g + i;
-          const float rv = s_re[e];
+          const float rv = s_re[16 * nt + 4 * g + i];
           re[4 * nt + i] = rv;
-          const float zz = rv > 0.0f ? st[nt][i] * zmul * rv : -INFINITY;
+          const float zz = rv > 0.0f ? sum[i] * zmul * rv : -INFINITY;
           z[4 * nt + i] = zz;
           tmax = fmaxf(tmax, zz);
         }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float Mn = fmaxf(M, tmax);
@@ -279,8 +325,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       uint32_t pw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        float p0 = (Mn == -INFINITY) ? 0.0f : expf(z[j] - Mn);
-        float p1 = (Mn == -INFINITY) ? 0.0f : expf(z[j + 1] - Mn);
+        const float p0 = (Mn == -INFINITY) ? 0.0f : expf(z[j] - Mn);
+        const float p1 = (Mn == -INFINITY) ? 0.0f : expf(z[j + 1] - Mn);
         psum += p0 + p1;
         pw[j / 2] = (uint32_t)f32_to_bf16(p0 * re[j]) | ((uint32_t)f32_to_bf16(p1 * re[j + 1]) << 16);
       }
@@ -289,17 +335,19 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       L = L * alpha + psum;
       M = Mn;
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      // alpha of the 4 heads this lane accumulates in O (rows 4g + i)
       float al[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
-      // ---- O += P E : B operand = dims 16dt + lane&15, entries {4g..4g+3, 16+4g..16+4g+3}
+      // ---- O += P E over the wave's dims; B operand by transpose reads of the entry-major rows
+      const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+      const uint16_t* e_lo = E1 + (4 * g + tr_r) * E1S + dbase + 4 * tr_c;
+      const uint16_t* e_hi = E1 + (16 + 4 * g + tr_r) * E1S + dbase + 4 * tr_c;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* eb = E2 + (16 * dt + (lane & 15)) * kE2Stride + 4 * g;
-        uint2 lo = *reinterpret_cast<const uint2*>(eb);
-        uint2 hi = *reinterpret_cast<const uint2*>(eb + 16);
-        const bf16x8 ef = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      for (int dt = 0; dt < DTW; ++dt) {
+        const i16x4 lo = lds_read_tr16(e_lo + 16 * dt);
+        const i16x4 hi = lds_read_tr16(e_hi + 16 * dt);
+        const bf16x8 ef = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         f32x4 o = O[dt];
         o[0] *= al[0]; o[1] *= al[1]; o[2] *= al[2]; o[3] *= al[3];
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, o, 0, 0, 0);
@@ -308,18 +356,16 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     __syncthreads();
   }
 
-  if (!wave_active) return;
   if (a.nsplit > 1) {
-    // partial state of (row, split, head): O[head][dim] unnormalized, plus M and L
+    // partial state of (row, part, head): O unnormalized over the wave's dims, plus M and L
     const int64_t base = ((int64_t)row * a.nsplit + sp) * a.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = blockIdx.y * 64 + wave * 16 + 4 * g + i;
-      float* dst = a.ws_o + (base + h) * C + (lane & 15);
+      float* dst = a.ws_o + (base + h0 + 4 * g + i) * C + dbase + (lane & 15);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) dst[16 * dt] = O[dt][i];
+      for (int dt = 0; dt < DTW; ++dt) dst[16 * dt] = O[dt][i];
     }
-    if (g == 0) {
+    if (wave == 0 && g == 0) {
       a.ws_ml[(base + head) * 2 + 0] = M;
       a.ws_ml[(base + head) * 2 + 1] = L;
     }
@@ -335,8 +381,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i, 64);
   const int dcol = lane & 15;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int d = 16 * dt + dcol;
+  for (int dt = 0; dt < DTW; ++dt) {
+    const int d = dbase + 16 * dt + dcol;
     float v[4], other[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = O[dt][i] * fi[i];
@@ -356,8 +402,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = blockIdx.y * 64 + wave * 16 + 4 * g + i;
-      const int64_t o = ((int64_t)row * a.H + h) * C + d;
+      const int64_t o = ((int64_t)row * a.H + h0 + 4 * g + i) * C + d;
       if (a.out_t == CSA_F32)
         static_cast<float*>(a.out)[o] = v[i];
       else
@@ -365,6 +410,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     }
   }
 }
+
+constexpr int kMaxSplits = 16;
 
 // merge the decode parts of one (row, head): fixed order, sink, gains, -t rotation
 __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, RopeTable rt) {
@@ -374,24 +421,42 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
   const int r = row - b * a.T;
   const double tpos = (double)(a.pos0[b] + r);
   const int64_t base = ((int64_t)row * a.nsplit) * a.H + h;
-  float Mx = a.sink[h];
-  for (int s = 0; s < a.nsplit; ++s) Mx = fmaxf(Mx, a.ws_ml[(base + (int64_t)s * a.H) * 2]);
-  float Lt = expf(a.sink[h] - Mx);
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float ms = a.ws_ml[(base + (int64_t)s * a.H) * 2];
-    if (ms != -INFINITY) Lt = fmaf(a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1], expf(ms - Mx), Lt);
+  const int ns = a.nsplit;
+  float ms[kMaxSplits], ls[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < ns) {
+      ms[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2];
+      ls[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1];
+    }
+  }
+  const float zs = a.sink[h];
+  float Mx = zs;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < ns) Mx = fmaxf(Mx, ms[s]);
+  float Lt = expf(zs - Mx);
+  float fs[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    fs[s] = 0.0f;
+    if (s < ns && ms[s] != -INFINITY) {
+      fs[s] = expf(ms[s] - Mx);
+      Lt = fmaf(ls[s], fs[s], Lt);
+    }
   }
   const int rope_lo = C - a.R;
   for (int d0 = 4 * threadIdx.x; d0 < C; d0 += 4 * blockDim.x) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.ws_ml[(base + (int64_t)s * a.H) * 2];
-      if (ms == -INFINITY) continue;
-      const float fs = expf(ms - Mx);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + d0);
+    f32x4 os[kMaxSplits];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(o[i], fs, v[i]);
-    }
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < ns) os[s] = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + d0);
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < ns && fs[s] != 0.0f)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = fmaf(os[s][i], fs[s], v[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = v[i] / Lt;
     if (d0 < rope_lo) {
@@ -571,24 +636,38 @@ RopeTable make_rope(int R, float base) {
   return rt;
 }
 
-int decode_splits(int T, int64_t nslots) { return T == 1 ? ceil_div(nslots, kSplitSlots) : 1; }
+// Decode (T = 1) splits each query's slot list into at most kMaxSplits parts of a
+// fixed length that depends only on the list length (multiples of the 32-slot
+// tile, at least 128); prefill queries are served by one part each.
+int split_slots(int T, int64_t nslots) {
+  if (T != 1) return (int)nslots;
+  int64_t len = (nslots + kMaxSplits - 1) / kMaxSplits;
+  len = ((len + kTile - 1) / kTile) * kTile;
+  return (int)(len < kSplitSlots ? kSplitSlots : len);
+}
+int decode_splits(int T, int64_t nslots) { return T == 1 ? ceil_div(nslots, split_slots(T, nslots)) : 1; }
 
 template <int C>
 size_t bf16_lds_bytes() {
-  return (size_t)kTile * (C + 8) * 2 + (size_t)C * kE2Stride * 2 + kTile * 4;
+  return (size_t)kTile * (C + 8) * 2 + 4 * 2 * 64 * 16 + kTile * 4 + 64 * 4;
 }
 
 template <int C>
-csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
+csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, int slots, hipStream_t stream) {
   const size_t lds = bf16_lds_bytes<C>();
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
       return CSA_ERR_LAUNCH;
     attr_set = true;
   }
-  dim3 grid(a.nsplit, ceil_div(a.H, 64), rows);
-  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt);
+  // grid.x = (part, row) padded to a multiple of 8 so that workgroups differing only in their
+  // head group have equal linear ids modulo 8 and land on the same XCD (shared L2 for the staged KV)
+  const int nx = a.nsplit * rows;
+  const int nx_pad = (nx + 7) & ~7;
+  dim3 grid(nx_pad, a.H / 16);
+  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt, slots, nx);
   if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
@@ -639,10 +718,11 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
   }
+  const int slots = split_slots(T, nslots);
   switch (c) {
-    case 128: return launch_bf16<128>(a, rt, rows, stream);
-    case 256: return launch_bf16<256>(a, rt, rows, stream);
-    case 512: return launch_bf16<512>(a, rt, rows, stream);
+    case 128: return launch_bf16<128>(a, rt, rows, slots, stream);
+    case 256: return launch_bf16<256>(a, rt, rows, slots, stream);
+    case 512: return launch_bf16<512>(a, rt, rows, slots, stream);
     default: return CSA_ERR_UNSUPPORTED;
   }
 }

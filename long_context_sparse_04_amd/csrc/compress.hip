@@ -18,21 +18,25 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Raw 4-channel loads (kept as bits until use, so that a batch of loads has no
+// dependent instruction between them) and their conversion to float32.
 template <typename TIn>
-CSA_DEV void load4(const TIn* p, float v[4]);
+struct Raw4;
 template <>
-CSA_DEV void load4<float>(const float* p, float v[4]) {
-  f32x4 x = *reinterpret_cast<const f32x4*>(p);
-  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-}
+struct Raw4<float> {
+  f32x4 v;
+  CSA_DEV void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  CSA_DEV float get(int q) const { return v[q]; }
+};
 template <>
-CSA_DEV void load4<uint16_t>(const uint16_t* p, float v[4]) {
-  uint2 x = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(x.x << 16);
-  v[1] = __uint_as_float(x.x & 0xFFFF0000u);
-  v[2] = __uint_as_float(x.y << 16);
-  v[3] = __uint_as_float(x.y & 0xFFFF0000u);
-}
+struct Raw4<uint16_t> {
+  uint2 v;
+  CSA_DEV void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  CSA_DEV float get(int q) const {
+    const uint32_t w = (q < 2) ? v.x : v.y;
+    return __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
 
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
@@ -63,29 +67,39 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   for (int q = 0; q < 4; ++q) { mx[q] = -INFINITY; sm[q] = 0.0f; ac[q] = 0.0f; }
 
   if (active) {
-    for (int rr = rs; rr < nrows; rr += nrs) {
-      const bool is_a = rr < m;
-      const int r = is_a ? rr : rr - m;
-      const int64_t row = (is_a ? m * i : m * (i - 1)) + r - row0_pos;
-      const TIn* zp = (is_a ? za : zb) + base + row * c + 4 * cg;
-      const TIn* cp = (is_a ? ca : cb) + base + row * c + 4 * cg;
-      const float* bp = (is_a ? bias_a : bias_b) + (int64_t)r * c + 4 * cg;
-      float z[4], v[4];
-      load4<TIn>(zp, z);
-      load4<TIn>(cp, v);
-      f32x4 bb = *reinterpret_cast<const f32x4*>(bp);
+    // rows of this thread's slice, 8 at a time: the loads of a batch are issued unconditionally
+    // (rows past the end are clamped to a valid row and masked afterwards)
+    constexpr int kBatch = 8;
+    for (int rr0 = rs; rr0 < nrows; rr0 += kBatch * nrs) {
+      Raw4<TIn> z[kBatch], v[kBatch];
+      f32x4 bb[kBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float lg = z[q] + bb[q];
-        if (lg > mx[q]) {
-          float sc = expf(mx[q] - lg);  // exp(-inf) = 0 on the first row
-          sm[q] = sm[q] * sc + 1.0f;
-          ac[q] = ac[q] * sc + v[q];
-          mx[q] = lg;
-        } else {
-          float p = expf(lg - mx[q]);
-          sm[q] += p;
-          ac[q] = fmaf(p, v[q], ac[q]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int rr = min(rr0 + u * nrs, nrows - 1);
+        const bool is_a = rr < m;
+        const int rw = is_a ? rr : rr - m;
+        const int64_t row = (is_a ? m * i : m * (i - 1)) + rw - row0_pos;
+        z[u].load((is_a ? za : zb) + base + row * c + 4 * cg);
+        v[u].load((is_a ? ca : cb) + base + row * c + 4 * cg);
+        bb[u] = *reinterpret_cast<const f32x4*>((is_a ? bias_a : bias_b) + (int64_t)rw * c + 4 * cg);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (rr0 + u * nrs >= nrows) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lg = z[u].get(q) + bb[u][q];
+          const float val = v[u].get(q);
+          if (lg > mx[q]) {
+            const float sc = expf(mx[q] - lg);  // exp(-inf) = 0 on the first row
+            sm[q] = sm[q] * sc + 1.0f;
+            ac[q] = ac[q] * sc + val;
+            mx[q] = lg;
+          } else {
+            const float p = expf(lg - mx[q]);
+            sm[q] += p;
+            ac[q] = fmaf(p, val, ac[q]);
+          }
         }
       }
     }

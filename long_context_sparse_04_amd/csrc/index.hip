@@ -9,10 +9,12 @@
 // HI x 128 indexer queries as the A operand, held in registers for the whole
 // launch (heads are MFMA rows), and streams 16-entry tiles of K^IComp straight
 // from HBM into the B operand (entries are MFMA columns).  Each lane loads one
-// contiguous slice of one entry row, so a wave reads 16 whole rows per tile.
-// K is used exactly once, so there is no LDS staging.  The epilogue applies
-// ReLU and the per-head weights in the MFMA output layout (lane = entry column,
-// 4 heads per lane per 16-head tile), then sums the 4 lane groups.
+// contiguous slice of one entry row, so a wave reads 16 whole rows per tile; a
+// wave issues the loads of 4 tiles before their MFMAs.  K is used exactly once,
+// so there is no LDS staging.  The epilogue applies ReLU and the per-head weights
+// in the MFMA output layout (lane = entry column, 4 heads per lane per 16-head
+// tile), then a reduce-scatter over the 4 lane groups leaves 64 consecutive
+// scores in the 64 lanes for one coalesced store.
 // Row scales of the FP8 format are applied to the float32 dot products
 // (w*sigma_q folded per head, sigma_k after the head sum, both positive);
 // MXFP4 block scales are operands of the scaled MFMA.
@@ -130,30 +132,52 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   }
 
   const uint8_t* kb = kI + (int64_t)b * n_max * Fmt<FMT>::kRowBytes;
-  for (int it = 0; it < kTilesPerWave; ++it) {
-    const int64_t e0 = wg_first + (int64_t)(it * kWaves + wave) * 16;
+  // wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) in groups of
+  // 4 tiles (64 entries): all loads of a group are issued before its MFMAs
+  const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
+  const int gl = lane >> 4;
+  for (int it = 0; it < kTilesPerWave; it += 4) {
+    const int64_t e0 = wave_first + (int64_t)it * 16;
     if (e0 >= n_max) break;
-    const int64_t e = e0 + (lane & 15);
-    if (e0 >= vis) {  // fully masked tile
-      if (lane < 16 && e < n_max) srow[e] = -INFINITY;
+    const int64_t eo = e0 + lane;  // entry this lane writes
+    if (e0 >= vis) {               // fully masked group
+      if (eo < n_max) srow[eo] = -INFINITY;
       continue;
     }
-    const int64_t el = e < n_max ? e : n_max - 1;
-    Frag<FMT> kf = load_frag<FMT>(kb + el * Fmt<FMT>::kRowBytes, lane);
-    int ksc = 127;
-    if constexpr (FMT == CSA_MXFP4_E8M0_B32)
-      ksc = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + (lane >> 4)];
-    float part = 0.0f;
+    Frag<FMT> kf[4];
+    int ksc[4];
+    float ksf[4];
 #pragma unroll
-    for (int g = 0; g < NT; ++g) {
-      f32x4 acc = mfma_tile<FMT>(qa[g], kf, qsc[g], ksc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part = fmaf(wq[g][i], fmaxf(acc[i], 0.0f), part);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t e = e0 + 16 * u + (lane & 15);
+      const int64_t el = e < n_max ? e : n_max - 1;
+      kf[u] = load_frag<FMT>(kb + el * Fmt<FMT>::kRowBytes, lane);
+      ksc[u] = 127;
+      ksf[u] = 1.0f;
+      if constexpr (FMT == CSA_MXFP4_E8M0_B32)
+        ksc[u] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
+      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE) ksf[u] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
     }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE) part *= static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
-    if (lane < 16 && e < n_max) srow[e] = (e < vis) ? part : -INFINITY;
+    float p[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float part = 0.0f;
+#pragma unroll
+      for (int g = 0; g < NT; ++g) {
+        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[u], qsc[g], ksc[u]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(wq[g][i], fmaxf(acc[i], 0.0f), part);
+      }
+      p[u] = part * ksf[u];  // the FP8 row scale is positive, so it factors out of every ReLU
+    }
+    // reduce-scatter over the 4 lane groups: lane 16u + e ends with the sum for tile u, entry e
+    const bool hi2 = gl >= 2;
+    const float s0 = hi2 ? p[0] : p[2], s1 = hi2 ? p[1] : p[3];
+    const float k0 = (hi2 ? p[2] : p[0]) + __shfl_xor(s0, 32, 64);
+    const float k1 = (hi2 ? p[3] : p[1]) + __shfl_xor(s1, 32, 64);
+    const bool odd = gl & 1;
+    const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
+    if (eo < n_max) srow[eo] = (eo < vis) ? val : -INFINITY;
   }
 }
 

@@ -13,12 +13,16 @@
 //    cached in LDS when the row fits (<= 32768 entries).
 //  * Split path (few long rows, decode): chunks of 4096 scores per workgroup.
 //    Kernel 1 builds the top-digit histogram (LDS, then integer atomics into a
-//    per-row global histogram); the last workgroup of a row picks the digit and
-//    clears the histogram.  Kernel 2 compacts each chunk's keys with a top digit
-//    >= that digit into its own segment, in index order; the last workgroup of a
-//    row loads all segments (chunk order = index order) into LDS and finishes the
-//    select and the ordered output there.  Integer atomics make the result
-//    independent of scheduling; the workspace is left zero-filled.
+//    per-row global histogram).  Kernel 2: each workgroup derives the threshold
+//    digit d0 from it and builds the second-digit histogram of the keys in that
+//    bin.  Kernel 3: each workgroup derives the 22-bit threshold prefix and
+//    compacts its chunk's keys at or above it into its own segment, in index
+//    order (about k candidates in total).  Kernel 4 (one workgroup per row) loads
+//    all segments (chunk order = index order) into LDS, resolves the last digit,
+//    writes the ordered output and clears the first histogram.  Kernel boundaries carry
+//    the cross-workgroup hand-offs, so no workgroup waits on another or issues a
+//    device-wide fence; integer atomics make the result independent of
+//    scheduling, and the workspace is left zero-filled.
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -216,9 +220,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
 
 // ------------------------------------------------------------------ split path
 struct SplitWs {
-  uint32_t* hist;     // [rows][kBins]   (zero at rest)
-  uint32_t* count1;   // [rows]          (zero at rest)
-  uint32_t* count2;   // [rows]          (zero at rest)
+  uint32_t* hist;     // [rows][kBins]   digit-0 histogram (zero at rest)
+  uint32_t* hist1;    // [rows][kBins]   digit-1 histogram (cleared by kernel 1 of every call)
   uint32_t* info;     // [rows][4]
   uint32_t* cnt;      // [rows][nch]
   Cand* seg;          // [rows][n_max]
@@ -231,10 +234,8 @@ static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   SplitWs s;
   s.hist = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins * 4);
-  s.count1 = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * 4);
-  s.count2 = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * 4);
+  s.hist1 = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)rows * kBins * 4);
   s.info = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * 16);
   s.cnt = reinterpret_cast<uint32_t*>(p);
@@ -244,69 +245,145 @@ static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
 }
 
 static size_t split_bytes(int rows, int64_t n_max, int nch) {
-  return align256((size_t)rows * kBins * 4) + 2 * align256((size_t)rows * 4) + align256((size_t)rows * 16) +
+  return 2 * align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
          align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand));
 }
 
+// Each thread of a split-path workgroup owns 16 scores of its 4096-score chunk:
+// round j (0..3) covers chunk positions [1024 j, 1024 j + 1024), thread t the 4
+// consecutive positions 1024 j + 4 t + q.  All 16 loads are issued before any use.
+constexpr int kPerThread = kChunk / kSplitThreads;  // 16
+constexpr int kRounds = kPerThread / 4;             // 4
+
+struct ChunkKeys {
+  uint32_t key[kPerThread];
+  bool valid[kPerThread];
+};
+
+CSA_DEV ChunkKeys load_chunk(const float* srow, int lo, int hi, int64_t n_max) {
+  // Addresses are clamped into the row so that every load is issued unconditionally (no branch
+  // between loads); validity is applied afterwards from the unclamped positions.
+  ChunkKeys c;
+  float v[kPerThread];
+  const int t = threadIdx.x;
+  if ((n_max & 3) == 0) {
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
+      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(srow + i0));
+      v[4 * j] = x[0]; v[4 * j + 1] = x[1]; v[4 * j + 2] = x[2]; v[4 * j + 3] = x[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) {
+      const int64_t i = min((int64_t)(lo + 1024 * (e / 4) + 4 * t + (e % 4)), n_max - 1);
+      v[e] = __builtin_nontemporal_load(srow + i);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = lo + 1024 * j + 4 * t + q;
+      c.valid[4 * j + q] = i < hi;
+      c.key[4 * j + q] = score_key(v[4 * j + q]);
+    }
+  return c;
+}
+
+// Kernel 1: per-chunk histogram of the top key digit (bits 31..21), added into the row histogram;
+// also clears the digit-1 histogram that kernel 2 fills.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const float* __restrict__ scores, int T,
                                                                         int64_t n_max,
                                                                         const int64_t* __restrict__ pos0, int m,
                                                                         int k, SplitWs ws) {
   __shared__ uint32_t hist[kBins];
-  __shared__ int s_w[kSplitThreads / 64];
-  __shared__ int s_sel[2];
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int b = row / T;
   const int r = row - b * T;
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
-  const bool trivial = (K == V);
+  const int lo = blockIdx.x * kChunk;
+  const int hi = min(lo + kChunk, V);
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int u = 0; u < kBins / kSplitThreads; ++u) ws.hist1[(int64_t)row * kBins + tid + u * kSplitThreads] = 0;
+  }
+  if (K == V || lo >= hi) return;  // trivial row or empty chunk (uniform per workgroup)
   const float* srow = scores + (int64_t)row * n_max;
   uint32_t* ghist = ws.hist + (int64_t)row * kBins;
-
-  if (!trivial) {
-    for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
-    __syncthreads();
-    const int lo = blockIdx.x * kChunk;
-    const int hi = min(lo + kChunk, V);
-    for (int i = lo + tid; i < hi; i += kSplitThreads) atomicAdd(&hist[score_key(srow[i]) >> 21], 1u);
-    __syncthreads();
-    for (int j = tid; j < kBins; j += kSplitThreads)
-      if (hist[j]) atomicAdd(&ghist[j], hist[j]);
-  }
-  __threadfence();
+  const ChunkKeys ck = load_chunk(srow, lo, hi, n_max);
+  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
   __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&ws.count1[row], 1u) == gridDim.x - 1);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (ck.valid[e]) atomicAdd(&hist[ck.key[e] >> 21], 1u);
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (!trivial) {
-    for (int j = tid; j < kBins; j += kSplitThreads) {
-      hist[j] = __hip_atomic_load(&ghist[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ghist[j] = 0;  // leave the workspace zero-filled
-    }
-    __syncthreads();
-    select_digit<kSplitThreads>(hist, kBins, K, s_w, s_sel);
-    if (tid == 0) {
-      ws.info[row * 4 + 0] = (uint32_t)s_sel[0];
-      ws.info[row * 4 + 1] = (uint32_t)s_sel[1];
-    }
-  }
-  if (tid == 0) ws.count1[row] = 0;
+  for (int j = tid; j < kBins; j += kSplitThreads)
+    if (hist[j]) atomicAdd(&ghist[j], hist[j]);
 }
 
-__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(
-    const float* __restrict__ scores, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
-    int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
-  __shared__ Cand s_c[kSegCap];
+// Load a row histogram (kBins counters) into LDS, all loads issued first.
+CSA_DEV void load_hist(const uint32_t* g, uint32_t* hist) {
+  const int tid = threadIdx.x;
+  uint32_t hv[kBins / kSplitThreads];
+#pragma unroll
+  for (int u = 0; u < kBins / kSplitThreads; ++u) hv[u] = g[tid + u * kSplitThreads];
+#pragma unroll
+  for (int u = 0; u < kBins / kSplitThreads; ++u) hist[tid + u * kSplitThreads] = hv[u];
+}
+
+// Kernel 2: every workgroup derives digit d0 from the complete digit-0 histogram, then adds the
+// histogram of digit 1 (bits 20..10) of its keys whose digit 0 equals d0.
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const float* __restrict__ scores, int T,
+                                                                         int64_t n_max,
+                                                                         const int64_t* __restrict__ pos0, int m,
+                                                                         int k, SplitWs ws) {
   __shared__ uint32_t hist[kBins];
   __shared__ int s_w[kSplitThreads / 64];
   __shared__ int s_sel[2];
-  __shared__ int s_last;
-  __shared__ int s_pre[kMaxChunks + 1];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  if (K == V) return;
+  const float* srow = scores + (int64_t)row * n_max;
+  const int lo = blockIdx.x * kChunk;
+  const int hi = min(lo + kChunk, V);
+  ChunkKeys ck;
+  if (lo < hi) ck = load_chunk(srow, lo, hi, n_max);
+  load_hist(ws.hist + (int64_t)row * kBins, hist);
+  __syncthreads();
+  select_digit<kSplitThreads>(hist, kBins, K, s_w, s_sel);
+  const uint32_t d0 = (uint32_t)s_sel[0];
+  if (blockIdx.x == 0 && tid == 0) {
+    ws.info[row * 4 + 0] = d0;
+    ws.info[row * 4 + 1] = (uint32_t)s_sel[1];
+  }
+  if (lo >= hi) return;
+  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (ck.valid[e] && (ck.key[e] >> 21) == d0) atomicAdd(&hist[(ck.key[e] >> 10) & 0x7FFu], 1u);
+  __syncthreads();
+  uint32_t* g1 = ws.hist1 + (int64_t)row * kBins;
+  for (int j = tid; j < kBins; j += kSplitThreads)
+    if (hist[j]) atomicAdd(&g1[j], hist[j]);
+}
 
+// Kernel 3: every workgroup derives the 22-bit prefix p1 = (d0, d1) from the digit-1 histogram and
+// compacts its chunk's keys with top 22 bits >= p1 into the chunk's own segment, in index order.
+__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const float* __restrict__ scores, int T,
+                                                                           int64_t n_max,
+                                                                           const int64_t* __restrict__ pos0, int m,
+                                                                           int k, SplitWs ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ int s_sel[2];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int nch = gridDim.x;
@@ -314,90 +391,142 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(
   const int r = row - b * T;
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
-  const bool trivial = (K == V);
+  if (K == V) return;
   const float* srow = scores + (int64_t)row * n_max;
-  Cand* seg = ws.seg + (int64_t)row * n_max;
-  uint32_t* cnt = ws.cnt + (int64_t)row * nch;
+  const int lo = blockIdx.x * kChunk;
+  const int hi = min(lo + kChunk, V);
+  ChunkKeys ck;
+  if (lo < hi) ck = load_chunk(srow, lo, hi, n_max);
+  const uint32_t d0 = ws.info[row * 4 + 0];
+  const int need = K - (int)ws.info[row * 4 + 1];
+  load_hist(ws.hist1 + (int64_t)row * kBins, hist);
+  __syncthreads();
+  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
+  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];
+  if (blockIdx.x == 0 && tid == 0) {
+    ws.info[row * 4 + 2] = p1;
+    ws.info[row * 4 + 3] = (uint32_t)(need - s_sel[1]);  // keys with prefix p1 still to take
+  }
+  int base = 0;
+  if (lo < hi) {
+    Cand* seg = ws.seg + (int64_t)row * n_max;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      int mine = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine += (ck.valid[4 * j + q] && (ck.key[4 * j + q] >> 10) >= p1) ? 1 : 0;
+      int tot;
+      int pos = base + block_int_scan<kSplitThreads>(mine, s_w, tot);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * j + q;
+        if (ck.valid[e] && (ck.key[e] >> 10) >= p1) seg[lo + pos++] = Cand{ck.key[e], lo + 1024 * j + 4 * tid + q};
+      }
+      base += tot;
+    }
+  }
+  if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = base;
+}
+
+// Kernel 4: one workgroup per row gathers the segments (chunk order == index order), resolves the
+// last digit among keys with prefix p1, writes the ascending index list, and clears the digit-0
+// histogram of the row.
+__global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
+    const float* __restrict__ scores, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
+    int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+  __shared__ Cand s_c[kSegCap];
+  __shared__ uint32_t hist[kBins];
+  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ int s_sel[2];
+  __shared__ int s_pre[kMaxChunks + 1];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const float* srow = scores + (int64_t)row * n_max;
+  const Cand* seg = ws.seg + (int64_t)row * n_max;
+  const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
   int32_t* orow = idx + (int64_t)row * k;
   float* vrow = vals ? vals + (int64_t)row * k : nullptr;
 
-  const uint32_t d0 = ws.info[row * 4 + 0];
-  if (!trivial) {
-    // ordered compaction of keys whose top digit is >= d0
-    const int lo = blockIdx.x * kChunk;
-    const int hi = min(lo + kChunk, V);
-    int base = 0;
-    for (int c0 = lo; c0 < hi; c0 += kSplitThreads) {
-      const int i = c0 + tid;
-      uint32_t kk = i < hi ? score_key(srow[i]) : 0u;
-      const bool keep = (i < hi) && (kk >> 21) >= d0;
-      int tot;
-      int pos = base + block_flag_scan<kSplitThreads>(keep, s_w, tot);
-      if (keep) seg[lo + pos] = Cand{kk, i};
-      base += tot;
-    }
-    if (tid == 0) cnt[blockIdx.x] = base;
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&ws.count2[row], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) ws.count2[row] = 0;
-
-  if (trivial) {
+  if (K == V) {
     for (int j = tid; j < k; j += kSplitThreads) {
       orow[j] = j < V ? j : -1;
       if (vrow) vrow[j] = j < V ? key_to_score(score_key(srow[j])) : -INFINITY;
     }
     return;
   }
+  {  // the digit-0 histogram is no longer needed: leave the workspace zero-filled
+    uint32_t* ghist = ws.hist + (int64_t)row * kBins;
+#pragma unroll
+    for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
+  }
+  const uint32_t p1 = ws.info[row * 4 + 2];
+  int need = (int)ws.info[row * 4 + 3];
 
-  // prefix over chunk counts (chunk order == index order)
-  if (tid == 0) {
-    int acc = 0;
-    for (int c = 0; c < nch; ++c) {
-      s_pre[c] = acc;
-      acc += (int)cnt[c];
-    }
-    s_pre[nch] = acc;
+  // prefix over chunk counts (chunk order == index order); every load is issued before use
+  {
+    constexpr int kCpt = kMaxChunks / kSplitThreads;  // chunk counts per thread (8)
+    const int cpt = (nch + kSplitThreads - 1) / kSplitThreads;
+    const int c0 = tid * cpt;
+    int cv[kCpt];
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u) cv[u] = (u < cpt && c0 + u < nch) ? (int)cnt[c0 + u] : 0;
+    int local = 0;
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u) local += cv[u];
+    int tot;
+    int pre = block_int_scan<kSplitThreads>(local, s_w, tot);
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u)
+      if (u < cpt && c0 + u < nch) {
+        s_pre[c0 + u] = pre;
+        pre += cv[u];
+      }
+    if (tid == 0) s_pre[nch] = tot;
   }
   __syncthreads();
   const int C = s_pre[nch];
   const bool in_lds = C <= kSegCap;
-  if (in_lds) {
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int c = wave; c < nch; c += kSplitThreads / 64) {
-      const int n = s_pre[c + 1] - s_pre[c];
-      for (int j = lane; j < n; j += 64) s_c[s_pre[c] + j] = seg[(int64_t)c * kChunk + j];
-    }
-  }
-  __syncthreads();
-  // flat candidate j -> (chunk, offset) when the list stays in global memory
-  auto cand = [&](int j) -> Cand {
-    if (in_lds) return s_c[j];
-    int lo = 0, hi = nch;  // find c with s_pre[c] <= j < s_pre[c+1]
+  auto chunk_of = [&](int j) -> int {  // c with s_pre[c] <= j < s_pre[c+1]
+    int lo = 0, hi = nch;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
       if (s_pre[mid] <= j) lo = mid; else hi = mid;
     }
-    return seg[(int64_t)lo * kChunk + (j - s_pre[lo])];
+    return lo;
   };
-
-  int need = K - (int)ws.info[row * 4 + 1];
-  // digit 1 among candidates with digit 0 == d0
-  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
-  __syncthreads();
-  for (int j = tid; j < C; j += kSplitThreads) {
-    uint32_t kk = cand(j).key;
-    if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
+  auto cand_global = [&](int j) -> Cand {
+    const int c = chunk_of(j);
+    return seg[(int64_t)c * kChunk + (j - s_pre[c])];
+  };
+  if (in_lds) {
+    constexpr int kGather = kSegCap / kSplitThreads;  // 24 candidates per thread at most
+    int64_t src[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) {
+      const int j = tid + u * kSplitThreads;
+      int64_t sidx = -1;
+      if (j < C) {
+        const int c = chunk_of(j);
+        sidx = (int64_t)c * kChunk + (j - s_pre[c]);
+      }
+      src[u] = sidx;
+    }
+    Cand cv[kGather];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u) cv[u] = seg[src[u] >= 0 ? src[u] : 0];
+#pragma unroll
+    for (int u = 0; u < kGather; ++u)
+      if (src[u] >= 0) s_c[tid + u * kSplitThreads] = cv[u];
   }
   __syncthreads();
-  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
-  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];
-  need -= s_sel[1];
-  __syncthreads();
+  auto cand = [&](int j) -> Cand { return in_lds ? s_c[j] : cand_global(j); };
+
+  // last digit (bits 9..0) among candidates whose top 22 bits equal p1
   for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
   __syncthreads();
   for (int j = tid; j < C; j += kSplitThreads) {
@@ -410,22 +539,29 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(
   const int ties = need - s_sel[1];
   __syncthreads();
 
-  int out_base = 0, tie_base = 0;
-  for (int c0 = 0; c0 < C && out_base < K; c0 += kSplitThreads) {
-    const int j = c0 + tid;
-    Cand cd = j < C ? cand(j) : Cand{0u, -1};
-    const bool eq = (j < C) && cd.key == kstar;
-    int eq_tot;
-    int eq_rank = tie_base + block_flag_scan<kSplitThreads>(eq, s_w, eq_tot);
-    const bool sel = (j < C) && (cd.key > kstar || (eq && eq_rank < ties));
-    int sel_tot;
-    int pos = out_base + block_flag_scan<kSplitThreads>(sel, s_w, sel_tot);
+  // ordered output: thread t owns the contiguous candidates [t*per, (t+1)*per)
+  const int per = (C + kSplitThreads - 1) / kSplitThreads;
+  const int j0 = min(tid * per, C), j1 = min(j0 + per, C);
+  int n_gt = 0, n_eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t kk = cand(j).key;
+    n_gt += kk > kstar;
+    n_eq += kk == kstar;
+  }
+  int tot;
+  const int eq_base = block_int_scan<kSplitThreads>(n_eq, s_w, tot);
+  const int take_eq = max(0, min(n_eq, ties - eq_base));
+  int pos = block_int_scan<kSplitThreads>(n_gt + take_eq, s_w, tot);
+  int eq_rank = eq_base;
+  for (int j = j0; j < j1; ++j) {
+    const Cand cd = cand(j);
+    bool sel = cd.key > kstar;
+    if (cd.key == kstar) sel = (eq_rank++ < ties);
     if (sel) {
       orow[pos] = cd.idx;
       if (vrow) vrow[pos] = key_to_score(cd.key);
+      ++pos;
     }
-    out_base += sel_tot;
-    tie_base += eq_tot;
   }
   for (int j = K + tid; j < k; j += kSplitThreads) {
     orow[j] = -1;
@@ -456,8 +592,12 @@ csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const i
     dim3 grid(nch, rows);
     hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m, k,
                        s);
+    hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+                       k, s);
     hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
-                       k, idx, vals, s);
+                       k, s);
+    hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0,
+                       m, k, nch, idx, vals, s);
   } else {
     const int cache = n_max <= kRowKeyCap ? 1 : 0;
     size_t lds = (size_t)kBins * 4 + (cache ? (size_t)n_max * 4 : 0);
