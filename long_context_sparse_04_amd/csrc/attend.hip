@@ -9,12 +9,13 @@
 // the softmax denominator).
 //
 // BF16 path (MFMA).  A workgroup of 4 waves serves one query row, one part of
-// its entry list and 16 heads; wave w owns a quarter of the c dims.  Entry slots
-// are staged 32 at a time into one entry-major LDS tile (the A operand of
-// S^T = E Q^T; the B operand of O = P E comes from the same tile through the
-// gfx950 transpose read), while the next tile's loads are in flight.  Each wave
-// forms a partial S^T over its dims; the four partials are summed through LDS in a
-// fixed order, so every wave holds the same logits.  RMSNorm is factored as a per-entry scalar r_e and a
+// its entry list and 16 heads; wave w owns a quarter of the c dims.  The rows of
+// up to 128 slots are fetched at once by direct global-to-LDS loads into one
+// entry-major LDS tile (the A operand of S^T = E Q^T; the B operand of O = P E
+// comes from the same tile through the gfx950 transpose read), so a part costs
+// one gather latency.  Each wave forms a partial S^T over its dims; the four
+// partials are summed through LDS in a fixed order, so every wave holds the same
+// logits.  RMSNorm is factored as a per-entry scalar r_e and a
 // per-query scalar r_q applied to the float32 logits, so the non-RoPE dims of q
 // and e enter the MFMA as their exact bf16 input bits; only the rotated RoPE dims
 // (and gains, if given) are rounded to bf16.  With S^T in the MFMA output layout
@@ -36,7 +37,7 @@ namespace {
 
 constexpr int kTile = 32;            // entry slots per staged tile
 constexpr int kSplitSlots = 128;     // decode split length (slots)
-constexpr int kE2Stride = 40;        // halfwords per dim-major LDS row (32 entries + pad)
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -61,7 +62,8 @@ struct Slot {
   double pos;
 };
 
-// slot j of query (b, r) at position t: CSA = idx slots then window; HCA = dense range then window
+// slot j of query (b, r) at position t: CSA = idx slots then window; HCA = dense range then window.
+// Only the CSA index-list value is read from memory.
 CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vis, int64_t slot) {
   Slot s;
   s.is_win = false;
@@ -94,6 +96,7 @@ CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vi
 CSA_DEV float bf(uint32_t word, int hi) { return __uint_as_float(hi ? (word & 0xFFFF0000u) : (word << 16)); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 // LDS transpose read (gfx950): inside each 16-lane group, lane 4r+c supplies the
 // address of 4 consecutive bf16 of "row" r; lane i receives column i of the 4x16
@@ -102,96 +105,34 @@ CSA_DEV i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
-// Staged-slot registers of one lane: 8 lanes per slot, NCH 16-byte chunks each.
-template <int NCH>
-struct StageRegs {
-  u32x4 v[NCH];
-  double pos;
-  bool valid;
-};
-
+// Entry-major LDS rows of C bf16 without padding; 16-byte chunk c of row e is stored at
+// chunk position c ^ (e & 15), which spreads the 16 rows an MFMA operand read touches
+// over all LDS banks.
 template <int C>
-CSA_DEV StageRegs<C / 64> stage_load(const AttnArgs& a, int b, int r, int64_t t, int64_t vis, int64_t slot,
-                                     int64_t slot_hi, int sub) {
-  StageRegs<C / 64> s;
-  Slot sl;
-  sl.row = -1;
-  if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
-  s.valid = sl.row >= 0;
-  s.pos = sl.pos;
-  const uint16_t* src = s.valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
-                                             : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
-                                : nullptr;
-#pragma unroll
-  for (int j = 0; j < C / 64; ++j)
-    s.v[j] = s.valid ? *reinterpret_cast<const u32x4*>(src + 8 * (sub + 8 * j)) : u32x4{0u, 0u, 0u, 0u};
-  return s;
-}
+CSA_DEV int swz(int e, int c) { return c ^ (e & 15); }
 
-// Per-entry RMS scalar, RoPE (and gain) of the RoPE dims, then the entry-major LDS row.
-template <int C>
-CSA_DEV void stage_store(const AttnArgs& a, const RopeTable& rt, StageRegs<C / 64>& s, uint16_t* E1, float* s_re,
-                         int es, int sub) {
-  constexpr int E1S = C + 8;
-  const int rope_lo = C - a.R;
-  float ss = 0.0f;
-#pragma unroll
-  for (int j = 0; j < C / 64; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float x0 = bf(s.v[j][q], 0), x1 = bf(s.v[j][q], 1);
-      ss = fmaf(x0, x0, ss);
-      ss = fmaf(x1, x1, ss);
-    }
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
-  ss += __shfl_xor(ss, 4, 64);
-  if (sub == 0) s_re[es] = s.valid ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
-#pragma unroll
-  for (int j = 0; j < C / 64; ++j) *reinterpret_cast<u32x4*>(E1 + es * E1S + 8 * (sub + 8 * j)) = s.v[j];
-  if (!s.valid) return;
-  // RoPE dims (and their gain) in place, on this lane's own chunks; non-RoPE dims stay raw because
-  // their gain is folded into q and the output
-#pragma unroll 1
-  for (int j = 0; j < C / 64; ++j) {
-    const int d0 = 8 * (sub + 8 * j);
-    if (d0 < rope_lo) continue;
-    u32x4* cp = reinterpret_cast<u32x4*>(E1 + es * E1S + d0);
-    u32x4 w = *cp;
-    float x[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w[q], 0); x[2 * q + 1] = bf(w[q], 1); }
-    if (a.gamma_kv) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
-    }
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float cs, sn;
-      rope_cs(s.pos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
-      const float x0 = x[2 * p], x1 = x[2 * p + 1];
-      x[2 * p] = x0 * cs - x1 * sn;
-      x[2 * p + 1] = x0 * sn + x1 * cs;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16(x[2 * q]) | ((uint32_t)f32_to_bf16(x[2 * q + 1]) << 16);
-    *cp = w;
-  }
-}
+constexpr int kStage = 64;  // slots fetched into LDS at once (2 compute tiles)
 
-// One workgroup = one query row x one decode part x 16 heads; wave w owns dims [w*C/4, (w+1)*C/4).
+// One workgroup = one query row x one part of its slot list x 16 heads; wave w owns dims
+// [w*C/4, (w+1)*C/4).  Per stage: (1) resolve 64 slots (row address, position, validity),
+// (2) DMA every row straight into LDS (global_load_lds, 16 B per lane, no registers),
+// (3) per-entry RMS scalar and RoPE in place, (4) two 32-slot tiles of MFMA work from LDS.
 template <int C>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int split_slots, int nx) {
-  constexpr int DW = C / 4;    // dims per wave
-  constexpr int KSW = DW / 32; // k-steps of the wave's partial S^T = E Q^T
-  constexpr int DTW = DW / 16; // 16-dim output tiles of the wave
-  constexpr int E1S = C + 8;   // halfwords per entry-major LDS row
+  constexpr int DW = C / 4;     // dims per wave
+  constexpr int KSW = DW / 32;  // k-steps of the wave's partial S^T = E Q^T
+  constexpr int DTW = DW / 16;  // 16-dim output tiles of the wave
+  constexpr int NCR = C / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / NCR; // rows per DMA instruction
   extern __shared__ __align__(16) uint16_t s_mem[];
-  uint16_t* E1 = s_mem;                                              // [32][E1S]
-  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + kTile * E1S);     // [4 waves][2][64 lanes]
-  float* s_re = reinterpret_cast<float*>(s_part + 4 * 2 * 64);       // [32]
-  float* s_rq = s_re + kTile;                                        // [4][16]
-  __shared__ int s_any;
+  uint16_t* E = s_mem;                                                     // [kStage][C]
+  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + kStage * C);            // [4 waves][2][64 lanes]
+  float* s_re = reinterpret_cast<float*>(s_part + 4 * 2 * 64);             // [kStage]
+  float* s_rq = s_re + kStage;                                             // [4][16]
+  double* s_theta = reinterpret_cast<double*>(s_rq + 64);                  // [64]
+  double* s_pos2 = s_theta + 64;                                           // [2][kStage]
+  const uint16_t** s_src2 = reinterpret_cast<const uint16_t**>(s_pos2 + 2 * kStage);  // [2][kStage]
+  int* s_flag2 = reinterpret_cast<int*>(s_src2 + 2 * kStage);              // [2][kStage]
 
   if ((int)blockIdx.x >= nx) return;  // grid.x is padded to a multiple of 8 (XCD-aligned head groups)
   const int lane = threadIdx.x & 63;
@@ -211,7 +152,26 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   const int64_t slot_hi = min(slot_lo + split_slots, nslots);
   const double tpos = (double)t;
   const int dbase = wave * DW;
+  const uint16_t* dummy = a.win + (int64_t)b * (a.T + a.n_win - 1) * C;  // a finite row for empty slots
+  if (threadIdx.x < 64) s_theta[threadIdx.x] = rt.theta[threadIdx.x];
+  // slot resolution of a stage into half h of the resolve arrays (threads < kStage)
+  auto resolve_stage = [&](int64_t st0, int h) {
+    if (threadIdx.x < kStage) {
+      const int64_t slot = st0 + threadIdx.x;
+      Slot sl;
+      sl.row = -1;
+      if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
+      const bool valid = sl.row >= 0;
+      s_src2[h * kStage + threadIdx.x] = valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
+                                                            : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
+                                               : dummy;
+      s_pos2[h * kStage + threadIdx.x] = sl.pos;
+      s_flag2[h * kStage + threadIdx.x] = valid;
+    }
+  };
+  resolve_stage(slot_lo, 0);
 
+  __syncthreads();  // s_theta (and the first stage's slots) visible
   // ---- query fragment: head lane&15, the wave's dims [dbase + 32ks + 8g, +8)
   bf16x8 qf[KSW];
   {
@@ -222,11 +182,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     for (int ks = 0; ks < KSW; ++ks) {
       raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = bf(raw[ks][j], 0), x1 = bf(raw[ks][j], 1);
-        ss = fmaf(x0, x0, ss);
-        ss = fmaf(x1, x1, ss);
-      }
+      for (int j = 0; j < 4; ++j) ss = sumsq_bf16x2(raw[ks][j], ss);
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
@@ -246,7 +202,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             float cs, sn;
-            rope_cs(tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+            rope_cs(tpos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
             const float x0 = x[2 * p], x1 = x[2 * p + 1];
             x[2 * p] = x0 * cs - x1 * sn;
             x[2 * p + 1] = x0 * sn + x1 * cs;
@@ -256,8 +212,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
           for (int j = 0; j < 8; ++j) x[j] *= a.gamma_kv[d0 + j];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          raw[ks][j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+        for (int j = 0; j < 4; ++j) raw[ks][j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
       }
       qf[ks] = __builtin_bit_cast(bf16x8, raw[ks]);
     }
@@ -266,33 +221,102 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   f32x4 O[DTW];
 #pragma unroll
   for (int d = 0; d < DTW; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15
-
-  const int es = 8 * wave + (lane >> 3);  // slot this lane stages
-  const int sub = lane & 7;
-  StageRegs<C / 64> st = stage_load<C>(a, b, r, t, vis, slot_lo + es, slot_hi, sub);
+  float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15 (base-2 units)
   __syncthreads();
-  const float zmul = a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
-                                      s_rq[48 + (lane & 15)]) / (float)C + a.eps);
+  // logits are kept in base-2 units (times log2 e) so that exponentials are single v_exp_f32
+  const float zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
+                                               s_rq[48 + (lane & 15)]) / (float)C + a.eps);
 
-  for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kTile) {
-    if (threadIdx.x == 0) s_any = 0;
-    stage_store<C>(a, rt, st, E1, s_re, es, sub);
-    const bool any_mine = st.valid;
+  int half = 0;
+  for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, half ^= 1) {
+    const uint16_t** s_src = s_src2 + half * kStage;
+    const double* s_pos = s_pos2 + half * kStage;
+    const int* s_flag = s_flag2 + half * kStage;
+    // ---- (2) DMA: instruction j of wave w fills rows RPI*(w + 4j) .. +RPI-1; lane l writes LDS chunk
+    // position (l % NCR) of row e = RPI*(w + 4j) + l / NCR, so it loads the logical chunk stored there
+#pragma unroll
+    for (int j = 0; j < kStage / RPI / 4; ++j) {
+      const int e0 = RPI * (wave + 4 * j);
+      const int e = e0 + lane / NCR;
+      const int cpos = lane % NCR;
+      const uint16_t* src = s_src[e] + 8 * swz<C>(e, cpos);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(E + e0 * C), 16, 0, 0);
+    }
+    // the next stage's slot resolution (index-list loads) overlaps this stage's fetch and compute
+    if (s0 + kStage < slot_hi) resolve_stage(s0 + kStage, half ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (any_mine && sub == 0) s_any = 1;
-    // prefetch the next tile's slots while this one is computed
-    if (s0 + kTile < slot_hi) st = stage_load<C>(a, b, r, t, vis, s0 + kTile + es, slot_hi, sub);
+    // ---- (3a) per-entry RMS scalar: 8 lanes per entry, two accumulators
+#pragma unroll 1
+    for (int rd = 0; rd < kStage / 32; ++rd) {
+      const int e = 32 * rd + (threadIdx.x >> 3);
+      const int sub = threadIdx.x & 7;
+      const uint16_t* er = E + e * C;
+      float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCR / 8; ++j) {
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(er + 8 * swz<C>(e, sub + 8 * j));
+        ss0 = sumsq_bf16x2(w4[0], ss0);
+        ss1 = sumsq_bf16x2(w4[1], ss1);
+        ss0 = sumsq_bf16x2(w4[2], ss0);
+        ss1 = sumsq_bf16x2(w4[3], ss1);
+      }
+      float ss = ss0 + ss1;
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if (sub == 0) s_re[e] = s_flag[e] ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
+    }
+    // ---- (3b) RoPE (and gain) of the RoPE dims, in place: items (entry, 4-pair chunk), four
+    // independent rotations per item so that their dependent sin/cos chains overlap
+    {
+      const int nrc = a.R / 8;  // RoPE chunks per entry
+#pragma unroll 1
+      for (int it = threadIdx.x; it < kStage * nrc; it += 256) {
+        const int e = it / nrc;
+        if (!s_flag[e]) continue;
+        const int c = (rope_lo >> 3) + (it - e * nrc);
+        const int d0 = 8 * c;
+        u32x4* cp = reinterpret_cast<u32x4*>(E + e * C + 8 * swz<C>(e, c));
+        u32x4 w4 = *cp;
+        const double pos = s_pos[e];
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w4[q], 0); x[2 * q + 1] = bf(w4[q], 1); }
+        if (a.gamma_kv) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          float cs, sn;
+          rope_cs(pos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * cs - x1 * sn;
+          x[2 * p + 1] = x0 * sn + x1 * cs;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w4[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+        *cp = w4;
+      }
+    }
     __syncthreads();
-    if (s_any) {
-      // ---- partial S^T over the wave's dims: lane holds entries 16nt + 4g + i, head lane&15
+    // ---- (4) compute tiles of 32 slots
+    const int ntile = (int)min((int64_t)kStage / kTile, (slot_hi - s0 + kTile - 1) / kTile);
+#pragma unroll 1
+    for (int tl = 0; tl < ntile; ++tl) {
+      const int eb = kTile * tl;
+      // partial S^T over the wave's dims: lane holds entries eb + 16nt + 4g + i, head lane&15
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* ea = E1 + (16 * nt + (lane & 15)) * E1S + dbase + 8 * g;
+        const int e = eb + 16 * nt + (lane & 15);
+        const uint16_t* er = E + e * C;
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
-          const bf16x8 ef = *reinterpret_cast<const bf16x8*>(ea + 32 * ks);
+          const int c = (dbase + 32 * ks + 8 * g) >> 3;
+          const bf16x8 ef = *reinterpret_cast<const bf16x8*>(er + 8 * swz<C>(e, c));
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], acc, 0, 0, 0);
         }
         s_part[(wave * 2 + nt) * 64 + lane] = acc;
@@ -310,7 +334,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float rv = s_re[16 * nt + 4 * g + i];
+          const float rv = s_re[eb + 16 * nt + 4 * g + i];
           re[4 * nt + i] = rv;
           const float zz = rv > 0.0f ? sum[i] * zmul * rv : -INFINITY;
           z[4 * nt + i] = zz;
@@ -320,40 +344,44 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float Mn = fmaxf(M, tmax);
-      const float alpha = (Mn == -INFINITY) ? 1.0f : expf(M - Mn);
+      const bool live = Mn != -INFINITY;
+      const float alpha = live ? __builtin_amdgcn_exp2f(M - Mn) : 1.0f;
       float psum = 0.0f;
       uint32_t pw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = (Mn == -INFINITY) ? 0.0f : expf(z[j] - Mn);
-        const float p1 = (Mn == -INFINITY) ? 0.0f : expf(z[j + 1] - Mn);
+        const float p0 = live ? __builtin_amdgcn_exp2f(z[j] - Mn) : 0.0f;
+        const float p1 = live ? __builtin_amdgcn_exp2f(z[j + 1] - Mn) : 0.0f;
         psum += p0 + p1;
-        pw[j / 2] = (uint32_t)f32_to_bf16(p0 * re[j]) | ((uint32_t)f32_to_bf16(p1 * re[j + 1]) << 16);
+        pw[j / 2] = pack_bf16x2(p0 * re[j], p1 * re[j + 1]);
       }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       L = L * alpha + psum;
       M = Mn;
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+      // rescale O only when some head's running max moved in this tile
+      const bool rescale = __any(alpha != 1.0f);
       float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
-      // ---- O += P E over the wave's dims; B operand by transpose reads of the entry-major rows
+      for (int i = 0; i < 4; ++i) al[i] = rescale ? __shfl(alpha, 4 * g + i, 64) : 1.0f;
+      // O += P E over the wave's dims; B operand by transpose reads of the entry-major rows
       const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
-      const uint16_t* e_lo = E1 + (4 * g + tr_r) * E1S + dbase + 4 * tr_c;
-      const uint16_t* e_hi = E1 + (16 + 4 * g + tr_r) * E1S + dbase + 4 * tr_c;
+      const int e_lo = eb + 4 * g + tr_r, e_hi = e_lo + 16;
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) {
-        const i16x4 lo = lds_read_tr16(e_lo + 16 * dt);
-        const i16x4 hi = lds_read_tr16(e_hi + 16 * dt);
-        const bf16x8 ef = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        const int hw = dbase + 16 * dt + 4 * tr_c;  // first of the 4 halfwords this lane addresses
+        const i16x4 lo = lds_read_tr16(E + e_lo * C + 8 * swz<C>(e_lo, hw >> 3) + (hw & 7));
+        const i16x4 hi = lds_read_tr16(E + e_hi * C + 8 * swz<C>(e_hi, hw >> 3) + (hw & 7));
+        const bf16x8 ef = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         f32x4 o = O[dt];
-        o[0] *= al[0]; o[1] *= al[1]; o[2] *= al[2]; o[3] *= al[3];
+        if (rescale) {
+          o[0] *= al[0]; o[1] *= al[1]; o[2] *= al[2]; o[3] *= al[3];
+        }
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, o, 0, 0, 0);
       }
+      __syncthreads();  // s_part is rewritten by the next tile; E and the resolve half by the next stage
     }
-    __syncthreads();
   }
 
   if (a.nsplit > 1) {
@@ -372,10 +400,10 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     return;
   }
   // ---- single part: add the sink, normalise, gains, rotate back by -t, write
-  const float zs = a.sink[head];
+  const float zs = kLog2e * a.sink[head];
   const float Mf = fmaxf(M, zs);
-  const float Lf = L * expf(M - Mf) + expf(zs - Mf);
-  const float f = (M == -INFINITY) ? 0.0f : expf(M - Mf) / Lf;
+  const float Lf = L * __builtin_amdgcn_exp2f(M - Mf) + __builtin_amdgcn_exp2f(zs - Mf);
+  const float f = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mf) / Lf;
   float fi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i, 64);
@@ -396,7 +424,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       }
     } else {
       float cs, sn;
-      rope_cs(-tpos, rt.theta[(d - rope_lo) / 2], cs, sn);
+      rope_cs(-tpos, s_theta[(d - rope_lo) / 2], cs, sn);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (dcol & 1) ? (other[i] * sn + v[i] * cs) : (v[i] * cs - other[i] * sn);
     }
@@ -430,18 +458,18 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
       ls[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1];
     }
   }
-  const float zs = a.sink[h];
+  const float zs = kLog2e * a.sink[h];  // the parts' maxima are in base-2 units
   float Mx = zs;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < ns) Mx = fmaxf(Mx, ms[s]);
-  float Lt = expf(zs - Mx);
+  float Lt = __builtin_amdgcn_exp2f(zs - Mx);
   float fs[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     fs[s] = 0.0f;
     if (s < ns && ms[s] != -INFINITY) {
-      fs[s] = expf(ms[s] - Mx);
+      fs[s] = __builtin_amdgcn_exp2f(ms[s] - Mx);
       Lt = fmaf(ls[s], fs[s], Lt);
     }
   }
@@ -478,8 +506,8 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
       *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
     } else {
       uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-      pk.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = pk;
     }
   }
@@ -649,7 +677,8 @@ int decode_splits(int T, int64_t nslots) { return T == 1 ? ceil_div(nslots, spli
 
 template <int C>
 size_t bf16_lds_bytes() {
-  return (size_t)kTile * (C + 8) * 2 + 4 * 2 * 64 * 16 + kTile * 4 + 64 * 4;
+  return (size_t)kStage * C * 2 + 4 * 2 * 64 * 16 + kStage * 4 + 64 * 4 + 64 * 8 + 2 * kStage * 8 + 2 * kStage * 8 +
+         2 * kStage * 4;
 }
 
 template <int C>

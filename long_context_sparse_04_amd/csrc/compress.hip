@@ -8,9 +8,10 @@
 // Design: one workgroup (256 threads) per (entry, sequence).  Thread tid owns
 // channel group cg = tid % (c/4) (4 adjacent channels, one 16-byte / 8-byte load
 // per row) and row slice rs = tid / (c/4); each thread runs an online softmax
-// over its rows, the slices are merged in LDS in a fixed order, and the rs == 0
-// threads write the entry (optionally quantized).  Loads are contiguous across
-// the channel groups of a row, so every row read is coalesced.
+// over its rows (branch-free, base-2 exponentials), the slices are merged in LDS
+// in a fixed order, and the rs == 0 threads write the entry (optionally
+// quantized).  Loads are contiguous across the channel groups of a row, so every
+// row read is coalesced.
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -38,16 +39,34 @@ struct Raw4<uint16_t> {
   }
 };
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Online softmax state of 4 channels in base-2 units (logits scaled by log2 e).
+struct Soft4 {
+  float mx[4], sm[4], ac[4];
+  CSA_DEV void init() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { mx[q] = -INFINITY; sm[q] = 0.0f; ac[q] = 0.0f; }
+  }
+  // branch-free update with one row: logit lg2 (finite, base 2) and value v
+  CSA_DEV void add(int q, float lg2, float v) {
+    const float mn = fmaxf(mx[q], lg2);
+    const float sc = __builtin_amdgcn_exp2f(mx[q] - mn);  // 0 while the state is empty
+    const float p = __builtin_amdgcn_exp2f(lg2 - mn);
+    sm[q] = fmaf(sm[q], sc, p);
+    ac[q] = fmaf(ac[q], sc, p * v);
+    mx[q] = mn;
+  }
+};
+
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void compress_kernel(
     const TIn* __restrict__ ca, const TIn* __restrict__ cb, const TIn* __restrict__ za,
     const TIn* __restrict__ zb, const float* __restrict__ bias_a, const float* __restrict__ bias_b,
     int rows, int c, int m, int64_t row0_pos, int64_t first_entry, void* __restrict__ out,
     void* __restrict__ out_scale, int out_t, int64_t out_bstride) {
-  __shared__ float s_m[kThreads][4];
-  __shared__ float s_l[kThreads][4];
-  __shared__ float s_a[kThreads][4];
-  __shared__ float s_red[kThreads];
+  __shared__ f32x4 s_m[kThreads], s_l[kThreads], s_a[kThreads];
+  __shared__ float s_red[kThreads / 64];
 
   const int e = blockIdx.x;
   const int b = blockIdx.y;
@@ -56,20 +75,17 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
   const int nrs = kThreads / ncg;  // row slices (>= 1 because c <= 1024)
   const int cg = tid % ncg;
   const int rs = tid / ncg;
-  const bool active = rs < nrs;
   const int64_t i = first_entry + e;
   const bool overlap = (cb != nullptr);
-  const int nrows = (overlap && i > 0) ? 2 * m : m;  // i == 0: b-side is -inf / 0
+  const int nrows = (overlap && i > 0) ? 2 * m : m;  // i == 0: the b-side is -inf / 0
   const int64_t base = (int64_t)b * rows * c;
 
-  float mx[4], sm[4], ac[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { mx[q] = -INFINITY; sm[q] = 0.0f; ac[q] = 0.0f; }
-
-  if (active) {
-    // rows of this thread's slice, 8 at a time: the loads of a batch are issued unconditionally
-    // (rows past the end are clamped to a valid row and masked afterwards)
-    constexpr int kBatch = 8;
+  Soft4 st;
+  st.init();
+  if (rs < nrs) {
+    // rows of this thread's slice, 4 at a time: loads issued unconditionally (rows past the end
+    // are clamped to a valid row and skipped afterwards)
+    constexpr int kBatch = 4;
     for (int rr0 = rs; rr0 < nrows; rr0 += kBatch * nrs) {
       Raw4<TIn> z[kBatch], v[kBatch];
       f32x4 bb[kBatch];
@@ -87,80 +103,66 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
       for (int u = 0; u < kBatch; ++u) {
         if (rr0 + u * nrs >= nrows) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lg = z[u].get(q) + bb[u][q];
-          const float val = v[u].get(q);
-          if (lg > mx[q]) {
-            const float sc = expf(mx[q] - lg);  // exp(-inf) = 0 on the first row
-            sm[q] = sm[q] * sc + 1.0f;
-            ac[q] = ac[q] * sc + val;
-            mx[q] = lg;
-          } else {
-            const float p = expf(lg - mx[q]);
-            sm[q] += p;
-            ac[q] = fmaf(p, val, ac[q]);
-          }
-        }
+        for (int q = 0; q < 4; ++q) st.add(q, (z[u].get(q) + bb[u][q]) * kLog2e, v[u].get(q));
       }
     }
   }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { s_m[tid][q] = mx[q]; s_l[tid][q] = sm[q]; s_a[tid][q] = ac[q]; }
+  s_m[tid] = f32x4{st.mx[0], st.mx[1], st.mx[2], st.mx[3]};
+  s_l[tid] = f32x4{st.sm[0], st.sm[1], st.sm[2], st.sm[3]};
+  s_a[tid] = f32x4{st.ac[0], st.ac[1], st.ac[2], st.ac[3]};
   __syncthreads();
 
+  // merge the row slices in a fixed order (slice 0 first)
   float y[4] = {0.f, 0.f, 0.f, 0.f};
   const bool writer = (tid < ncg);
   if (writer) {
+    f32x4 M = s_m[cg];
+    for (int sl = 1; sl < nrs; ++sl) {
+      const f32x4 mo = s_m[sl * ncg + cg];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float M = -INFINITY;
-      for (int s = 0; s < nrs; ++s) M = fmaxf(M, s_m[s * ncg + cg][q]);
-      float L = 0.f, A = 0.f;
-      for (int s = 0; s < nrs; ++s) {
-        float ms = s_m[s * ncg + cg][q];
-        if (ms == -INFINITY) continue;  // slice saw no row
-        float f = expf(ms - M);
-        L = fmaf(s_l[s * ncg + cg][q], f, L);
-        A = fmaf(s_a[s * ncg + cg][q], f, A);
-      }
-      y[q] = A / L;
+      for (int q = 0; q < 4; ++q) M[q] = fmaxf(M[q], mo[q]);
     }
+    float L[4] = {0.f, 0.f, 0.f, 0.f}, A[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int sl = 0; sl < nrs; ++sl) {
+      const f32x4 ms = s_m[sl * ncg + cg], ls = s_l[sl * ncg + cg], as = s_a[sl * ncg + cg];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float f = (ms[q] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[q] - M[q]);  // empty slice
+        L[q] = fmaf(ls[q], f, L[q]);
+        A[q] = fmaf(as[q], f, A[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = A[q] / L[q];
   }
 
   const int64_t orow = (int64_t)b * out_bstride + e;
   if (out_t == CSA_F32) {
-    if (writer) {
-      f32x4 o = {y[0], y[1], y[2], y[3]};
-      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = o;
-    }
+    if (writer) *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
     return;
   }
   if (out_t == CSA_BF16) {
     if (writer) {
       uint2 o;
-      o.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-      o.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+      o.x = pack_bf16x2(y[0], y[1]);
+      o.y = pack_bf16x2(y[2], y[3]);
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * c + 4 * cg) = o;
     }
     return;
   }
   if (out_t == CSA_FP8_E4M3_ROWSCALE) {
-    // row amax over all c channels (fixed-order tree in LDS)
+    // row amax over all c channels: wave maxima, then the block maximum through LDS
     float am = writer ? fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))) : 0.0f;
-    s_red[tid] = am;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if ((tid & 63) == 0) s_red[tid >> 6] = am;
     __syncthreads();
-    for (int w = kThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-      __syncthreads();
-    }
-    const float scale = s_red[0] / 448.0f;
+    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float scale = am / 448.0f;
     if (writer) {
       uint32_t pk = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v = scale > 0.0f ? y[q] / scale : 0.0f;
-        pk |= f32_to_e4m3(v) << (8 * q);
-      }
+      for (int q = 0; q < 4; ++q) pk |= f32_to_e4m3(scale > 0.0f ? y[q] / scale : 0.0f) << (8 * q);
       *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow * c + 4 * cg) = pk;
       if (tid == 0) static_cast<float*>(out_scale)[orow] = scale;
     }
@@ -172,14 +174,12 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(
     am = fmaxf(am, __shfl_xor(am, 1, 8));
     am = fmaxf(am, __shfl_xor(am, 2, 8));
     am = fmaxf(am, __shfl_xor(am, 4, 8));
-    int X;
+    int X = -127;
     if (am > 0.0f) {
       int ex;
       frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
       X = ex - 1 - 2;
       X = X < -127 ? -127 : (X > 127 ? 127 : X);
-    } else {
-      X = -127;
     }
     uint32_t codes = 0;
 #pragma unroll

@@ -11,6 +11,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 #define CSA_DEV __device__ __forceinline__
 
@@ -23,6 +25,16 @@ CSA_DEV uint16_t f32_to_bf16(float x) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Two float32 -> packed bf16 pair (low half = lo), hardware round to nearest even.
+CSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// acc + x.lo^2 + x.hi^2 for a packed bf16 pair (products are exact in float32).
+CSA_DEV float sumsq_bf16x2(uint32_t w, float acc) {
+  const bf16x2 x = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
 }
 
 // float32 -> OCP fp8 E4M3, round to nearest even, saturating at +-448 (NaN -> 0x7F).
@@ -99,16 +111,29 @@ struct RopeTable {
   double theta[64];
 };
 
-// cos / sin of pos * theta with the angle reduced modulo 2*pi in double precision,
-// so that positions near 2^20 keep float32-level accuracy in the rotation.
+// cos / sin of pos * theta.  The angle is formed and reduced to [-pi/4, pi/4] plus a
+// quadrant in double precision (Cody-Waite style, pi/2 split into two doubles), so
+// positions near 2^20 keep float32-level accuracy; sin and cos of the reduced
+// argument are their Taylor series through x^9 / x^10 (truncation < 2e-9 on
+// [-pi/4, pi/4]), evaluated in float32 by Horner's rule.
 CSA_DEV void rope_cs(double pos, double theta, float& c, float& s) {
-  const double two_pi_hi = 6.283185307179586;      // nearest double to 2*pi
-  const double two_pi_lo = 2.4492935982947064e-16; // 2*pi - two_pi_hi
-  double ang = pos * theta;
-  double kq = rint(ang * 0.15915494309189535);
-  double red = fma(-kq, two_pi_hi, ang);
-  red = fma(-kq, two_pi_lo, red);
-  sincosf((float)red, &s, &c);
+  const double pio2_hi = 1.5707963267948966;     // nearest double to pi/2
+  const double pio2_lo = 6.123233995736766e-17;  // pi/2 - pio2_hi
+  const double ang = pos * theta;
+  const double kq = rint(ang * 0.6366197723675814);  // 2/pi
+  double red = fma(-kq, pio2_hi, ang);
+  red = fma(-kq, pio2_lo, red);
+  const float x = (float)red, x2 = x * x;
+  const float sp = fmaf(x * x2, fmaf(x2, fmaf(x2, fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f), 1.0f / 120.0f),
+                                     -1.0f / 6.0f), x);
+  const float cp = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f),
+                                                   -1.0f / 720.0f), 1.0f / 24.0f), -0.5f), 1.0f);
+  switch ((int)((long long)kq & 3)) {  // angle = red + q * pi/2
+    case 0: s = sp; c = cp; break;
+    case 1: s = cp; c = -sp; break;
+    case 2: s = -sp; c = -cp; break;
+    default: s = -cp; c = sp; break;
+  }
 }
 
 // ---------------------------------------------------------------- misc

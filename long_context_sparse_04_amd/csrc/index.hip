@@ -10,7 +10,8 @@
 // launch (heads are MFMA rows), and streams 16-entry tiles of K^IComp straight
 // from HBM into the B operand (entries are MFMA columns).  Each lane loads one
 // contiguous slice of one entry row, so a wave reads 16 whole rows per tile; a
-// wave issues the loads of 4 tiles before their MFMAs.  K is used exactly once,
+// wave loads 4 tiles at a time, double-buffered so that the next 4 are in flight
+// during the MFMAs and epilogue of the current ones.  K is used exactly once,
 // so there is no LDS staging.  The epilogue applies ReLU and the per-head weights
 // in the MFMA output layout (lane = entry column, 4 heads per lane per 16-head
 // tile), then a reduce-scatter over the 4 lane groups leaves 64 consecutive
@@ -133,30 +134,38 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
 
   const uint8_t* kb = kI + (int64_t)b * n_max * Fmt<FMT>::kRowBytes;
   // wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) in groups of
-  // 4 tiles (64 entries): all loads of a group are issued before its MFMAs
+  // 4 tiles (64 entries), double-buffered: the loads of group i+1 are in flight during group i
   const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
   const int gl = lane >> 4;
-  for (int it = 0; it < kTilesPerWave; it += 4) {
-    const int64_t e0 = wave_first + (int64_t)it * 16;
-    if (e0 >= n_max) break;
-    const int64_t eo = e0 + lane;  // entry this lane writes
-    if (e0 >= vis) {               // fully masked group
-      if (eo < n_max) srow[eo] = -INFINITY;
-      continue;
-    }
-    Frag<FMT> kf[4];
-    int ksc[4];
-    float ksf[4];
+  constexpr int NG = kTilesPerWave / 4;
+  Frag<FMT> kf[2][4];
+  int ksc[2][4];
+  float ksf[2][4];
+  auto load_group = [&](int buf, int64_t e0) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t e = e0 + 16 * u + (lane & 15);
       const int64_t el = e < n_max ? e : n_max - 1;
-      kf[u] = load_frag<FMT>(kb + el * Fmt<FMT>::kRowBytes, lane);
-      ksc[u] = 127;
-      ksf[u] = 1.0f;
+      kf[buf][u] = load_frag<FMT>(kb + el * Fmt<FMT>::kRowBytes, lane);
+      ksc[buf][u] = 127;
+      ksf[buf][u] = 1.0f;
       if constexpr (FMT == CSA_MXFP4_E8M0_B32)
-        ksc[u] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
-      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE) ksf[u] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
+        ksc[buf][u] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
+      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE)
+        ksf[buf][u] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
+    }
+  };
+  if (wave_first < vis) load_group(0, wave_first);
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int buf = gi & 1;
+    const int64_t e0 = wave_first + (int64_t)gi * 64;
+    if (e0 >= n_max) break;
+    if (gi + 1 < NG && e0 + 64 < vis) load_group(buf ^ 1, e0 + 64);
+    const int64_t eo = e0 + lane;  // entry this lane writes
+    if (e0 >= vis) {               // fully masked group
+      if (eo < n_max) srow[eo] = -INFINITY;
+      continue;
     }
     float p[4];
 #pragma unroll
@@ -164,11 +173,11 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
       float part = 0.0f;
 #pragma unroll
       for (int g = 0; g < NT; ++g) {
-        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[u], qsc[g], ksc[u]);
+        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[buf][u], qsc[g], ksc[buf][u]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wq[g][i], fmaxf(acc[i], 0.0f), part);
       }
-      p[u] = part * ksf[u];  // the FP8 row scale is positive, so it factors out of every ReLU
+      p[u] = part * ksf[buf][u];  // the FP8 row scale is positive, so it factors out of every ReLU
     }
     // reduce-scatter over the 4 lane groups: lane 16u + e ends with the sum for tile u, entry e
     const bool hi2 = gl >= 2;

@@ -1,0 +1,50 @@
+"""A decode step captured in a HIP graph and replayed repeatedly matches the eager step on every replay."""
+import numpy as np
+import pytest
+import torch
+
+from synth import configs, gen
+from tests.gpu_util import DEV, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    from long_context_sparse_04_amd import api
+    cfg = configs.C3.scaled(B=2, n_comp=40000)
+    print("[gpu-case] graph replay of a decode step", flush=True)
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    pos = torch.full((cfg.B,), 4 * cfg.n_comp, dtype=torch.int64, device=DEV)
+    kv = dev(gen.kv_cache(cfg))
+    q, win, sink = dev(gen.queries(cfg)), dev(gen.window(cfg)), dev(gen.sink(cfg))
+    ik, iks, qd, qs, wd = dev(kc["data"]), dev(kc["scale"]), dev(qi["data"]), dev(qi["scale"]), dev(w)
+    ci = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in gen.compress_inputs(cfg, indexer=True).items()}
+    scores = torch.empty((cfg.B, 1, cfg.n_comp), device=DEV)
+    idx = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device=DEV)
+    out = torch.empty((cfg.B, 1, cfg.H, cfg.c), dtype=torch.bfloat16, device=DEV)
+    first = cfg.n_comp - 1
+
+    def step():
+        api.compress(ci["ca"], ci["cb"], ci["za"], ci["zb"], ci["bias_a"], ci["bias_b"], cfg.m, 4 * cfg.n_comp - 8,
+                     first, 1, out=ik[:, first:], out_scale=iks[:, first:], out_fmt="fp8",
+                     out_batch_stride=cfg.n_comp)
+        api.index(qd, qs, wd, ik, iks, pos, cfg.m, "fp8", scores=scores)
+        api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
+        api.attend(q, kv, idx, win, sink, pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref_idx, ref_out = idx.clone(), out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        idx.fill_(-7)
+        out.zero_()
+        scores.zero_()          # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), f"replay {rep}: top-k differs"
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep}: output differs"
