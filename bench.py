@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--config", default="c3", help="c3 (default), c2 or c5")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch the step's calls one by one (no HIP graph)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -161,7 +163,7 @@ def main():
 
     first = N - 1  # the entry completed by the block ending at pos0-1
 
-    def step(st, ev=None):
+    def step(st):
         c = st["ckv"]
         api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
                      c["first_entry"], 1, out=kv_cache[:, first:], out_batch_stride=N)
@@ -177,11 +179,7 @@ def main():
         else:
             api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
                          c["first_entry"], 1, out=st["ik"][:, first:], out_batch_stride=N)
-        if ev is not None:
-            ev[0].record()
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
-        if ev is not None:
-            ev[1].record()
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
         api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
                    cfg.eps, cfg.rope_base, out=out)
@@ -192,6 +190,13 @@ def main():
             api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
                            cfg.scale, cfg.eps, cfg.rope_base, out=hout)
 
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(a.warmup):
         step(sets[i % NSETS])
     torch.cuda.synchronize()
@@ -218,12 +223,21 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / a.steps
-    # csa_index launch durations, HIP events on the launch stream, same inputs and rotation
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for i in range(a.steps):
-        step(sets[i % NSETS], evs[i])
+    # csa_index launch duration: HIP events recorded on the launch stream around back-to-back index
+    # launches over the same input rotation, so that the average is the kernel's own time
+    def index_only(st):
+        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
+
+    for i in range(NSETS):
+        index_only(sets[i])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    idx_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    e0.record()
+    for i in range(a.steps):
+        index_only(sets[i % NSETS])
+    e1.record()
+    torch.cuda.synchronize()
+    idx_ms = e0.elapsed_time(e1) / a.steps
 
     # algorithmic bytes of one csa_index launch: every visible K^I row (+ its scales) read once,
     # the queries / weights read once per sequence, one float32 score written per entry

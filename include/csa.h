@@ -123,10 +123,12 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  * indices in ascending order followed by -1 padding; vals (nullable) receives
  * their scores (NaN-free inputs assumed; padding slots get -inf).
  *
- *   workspace : device memory of csa_topk_workspace_bytes(B, T, n_max, k) bytes.
- *               It must be zero-filled before its first use; every call leaves
- *               it zero-filled again, so one buffer serves any later call on
- *               the same stream.
+ *   workspace : device memory of csa_topk_workspace_bytes(B, T, n_max, k) bytes
+ *               (0 means none is needed).  It must be zero-filled before its
+ *               first use.  Every call leaves the part that has to start at zero
+ *               zero-filled again, at the same place for every shape, so one
+ *               buffer (of the largest size needed) serves later calls of any
+ *               shape on the same stream.
  * Limits: 1 <= k <= 2048, n_max < 2^31.
  */
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k);

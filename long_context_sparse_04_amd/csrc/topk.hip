@@ -229,11 +229,17 @@ struct SplitWs {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The split path serves fewer than kSplitMaxRows rows.  Its digit-0 histograms, the one region that
+// must be zero at rest, take a fixed slot for that many rows at the start of the workspace, so that
+// no call of another shape ever places them over memory that a previous call left dirty.
+constexpr int kSplitMaxRows = 128;
+constexpr size_t kHistSlot = (size_t)kSplitMaxRows * kBins * 4;
+
 static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   char* p = static_cast<char*>(ws);
   SplitWs s;
   s.hist = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)rows * kBins * 4);
+  p += kHistSlot;
   s.hist1 = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins * 4);
   s.info = reinterpret_cast<uint32_t*>(p);
@@ -245,7 +251,7 @@ static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
 }
 
 static size_t split_bytes(int rows, int64_t n_max, int nch) {
-  return 2 * align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
+  return kHistSlot + align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
          align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand));
 }
 
@@ -571,7 +577,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 
 bool use_split(int rows, int64_t n_max) {
   const int64_t nch = (n_max + kChunk - 1) / kChunk;
-  return rows < 128 && n_max > 16384 && nch <= kMaxChunks;
+  return rows < kSplitMaxRows && n_max > 16384 && nch <= kMaxChunks;
 }
 
 }  // namespace

@@ -25,6 +25,20 @@ def decode_bf16(bits) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def encode_bf16(x) -> np.ndarray:
+    """float64 -> bf16 bits of the nearest bfloat16 value (8 significant bits), ties to the even significand.
+
+    Used where the step stores a float32 result in a bf16 cache: the oracle keeps
+    the same storage format, rounding its own float64 value once.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, ex = np.frexp(x)                                   # |x| = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -126)         # binade; subnormals share the 2^-126 ulp grid
+    ulp = np.ldexp(1.0, e - 7)
+    v = np.rint(x / ulp) * ulp                             # rint rounds half to even
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def _fp8_e4m3_table() -> np.ndarray:
     vals = np.empty(256, dtype=np.float64)
     for code in range(256):

@@ -65,3 +65,15 @@ def topk_agreement(gpu_idx, ref_idx, ref_scores, k_rows_tau_rule=1e-3):
             if not (s[row, j] - tau <= tol):
                 bad += 1
     return inter / max(total, 1), bad
+
+
+def codes_close(got_codes, ref_codes, ref_vals_scaled, table):
+    """Codes must match except where the exact value sits within 1e-5 (relative) of a rounding midpoint."""
+    mism = got_codes != ref_codes
+    if not mism.any():
+        return True
+    a = np.abs(ref_vals_scaled[mism])
+    lo = np.abs(table[ref_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
+    hi = np.abs(table[got_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
+    mid = 0.5 * (lo + hi)
+    return bool(np.all(np.abs(a - mid) <= 1e-5 * np.maximum(mid, 1e-30)))

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from synth import configs, formats, gen
-from tests.gpu_util import DEV, dev, host_f64, rel_l2, topk_agreement
+from tests.gpu_util import DEV, codes_close, dev, host_f64, rel_l2, topk_agreement
 
 pytestmark = pytest.mark.gpu
 
@@ -92,18 +92,6 @@ def test_compress_hca_bf16_c4(api):
     assert np.all(np.abs(got - ref) <= _half_ulp_bound(ref, _compress_case.absref))
 
 
-def _codes_close(got_codes, ref_codes, ref_vals_scaled, table):
-    """Codes must match except where the exact value sits within 1e-5 (relative) of a rounding midpoint."""
-    mism = got_codes != ref_codes
-    if not mism.any():
-        return True
-    a = np.abs(ref_vals_scaled[mism])
-    lo = np.abs(table[ref_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
-    hi = np.abs(table[got_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
-    mid = 0.5 * (lo + hi)
-    return bool(np.all(np.abs(a - mid) <= 1e-5 * np.maximum(mid, 1e-30)))
-
-
 def test_compress_quantized_indexer_keys(api):
     cfg = configs.C3.scaled(B=64)     # decode geometry: one new entry per sequence, many sequences
     out, osc, ref = _compress_case(api, cfg, indexer=True, out_fmt="fp8")
@@ -111,7 +99,7 @@ def test_compress_quantized_indexer_keys(api):
     scale = osc.cpu().numpy().astype(np.float64)
     rc, rs = oracle.encode_fp8_rows(ref)
     assert np.allclose(scale, rs, rtol=1e-6, atol=0)
-    assert _codes_close(codes, rc, ref / rs[..., None], oracle.fp8_e4m3_values())
+    assert codes_close(codes, rc, ref / rs[..., None], oracle.fp8_e4m3_values())
     deq = oracle.dequant_rows(codes, scale.astype(np.float32), "fp8")
     assert rel_l2(deq, ref) <= 0.05          # e4m3 has a 3-bit mantissa
     cfg5 = configs.C5.scaled(B=64)
@@ -121,7 +109,7 @@ def test_compress_quantized_indexer_keys(api):
     assert np.array_equal(e, re_)
     nib = lambda x: np.stack([x & 0xF, x >> 4], -1).reshape(x.shape[:-1] + (-1,))
     scaled = ref / np.repeat(oracle.decode_e8m0(re_), 32, axis=-1)
-    assert _codes_close(nib(p), nib(rp), scaled, oracle.e2m1_values())
+    assert codes_close(nib(p), nib(rp), scaled, oracle.e2m1_values())
 
 
 def test_compress_into_cache_with_stride(api):
@@ -226,6 +214,24 @@ def test_topk_split_path_with_ties(api):
     s[0, 0, 3::7] = -0.0
     pos0 = [4 * N, 4 * (N - 1000) + 3, 4 * 20000, 4 * N + 100]
     _topk_case(api, s, pos0, 4, 1024, "split path with ties")
+
+
+def test_topk_workspace_reused_across_shapes(api):
+    """One workspace serves split-path calls of different shapes: a call with more rows must not find the
+    previous call's dirty regions where its zero-at-rest histograms live."""
+    from long_context_sparse_04_amd import _lib
+    lib = _lib.load()
+    rng = np.random.default_rng(5)
+    shapes = [(2, 40000), (8, 20000), (3, 65536), (8, 20000)]
+    nb = max(lib.csa_topk_workspace_bytes(B, 1, n, 256) for B, n in shapes)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    for B, n in shapes:
+        say(f"topk workspace reuse B={B} N={n}")
+        sc = rng.standard_normal((B, 1, n)).astype(np.float32)
+        pos0 = [4 * n] * B
+        idx, _ = api.topk(dev(sc), _pos(pos0), 4, 256, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oracle.topk(sc.astype(np.float64), pos0, 4, 256))
 
 
 def test_topk_edge_cases(api):

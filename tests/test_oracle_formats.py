@@ -44,6 +44,22 @@ def test_bf16_decode():
     assert np.array_equal(oracle.decode_bf16(bits), x.astype(np.float64))
 
 
+def test_bf16_encode_matches_torch_and_ties_to_even():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1e-40, -3e-39, 2.0 ** -126, 3.3895313892515355e38]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.encode_bf16(x.astype(np.float64)), ref)
+    # exact midpoints between neighbours: 1 + 2^-8 lies between 1 and 1 + 2^-7 -> even significand (1.0);
+    # 1 + 3*2^-8 lies between 1 + 2^-7 (odd) and 1 + 2^-6 (even) -> 1 + 2^-6
+    mids = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 1 + 2.0 ** -8 + 2.0 ** -40])
+    got = oracle.decode_bf16(oracle.encode_bf16(mids))
+    assert list(got) == [1.0, 1 + 2.0 ** -6, -1.0, 1 + 2.0 ** -7]
+    # a float64 value just above a float32 midpoint rounds up even where float32 would tie to even first
+    v = 1 + 2.0 ** -8 + 2.0 ** -30
+    assert oracle.decode_bf16(oracle.encode_bf16(np.array([v])))[0] == 1 + 2.0 ** -7
+
+
 def test_fp8_encoders_agree_and_match_torch():
     rng = np.random.default_rng(1)
     x = (rng.standard_normal((300, 128)) * rng.uniform(0.01, 100, (300, 1))).astype(np.float32)
