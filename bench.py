@@ -34,6 +34,7 @@ from synth import configs, gen  # noqa: E402
 
 METRIC = "CSA decode tokens/s at 1M ctx (Pro shape) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 10100.0}   # dense, MI355X
 NSETS = 4
 
 
@@ -42,7 +43,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", default="c3", help="c3 (default), c2 or c5")
+    p.add_argument("--config", default="c3", help="c3 (default), c2 or c5 (decode), c4 (chunked prefill)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch the step's calls one by one (no HIP graph)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -97,7 +98,7 @@ def main():
     from long_context_sparse_04_amd import _lib, api
 
     cfg = configs.get_config(a.config)
-    assert cfg.T == 1, "bench.py times the decode step"
+    prefill = cfg.T > 1
     _lib.load()
     dev = "cuda:0"
     B, N = cfg.B, cfg.n_comp
@@ -154,41 +155,54 @@ def main():
         st["host"] = h if s == 0 else None
         sets.append(st)
     pos = torch.full((B,), cfg.pos0, dtype=torch.int64, device=dev)
-    scores = torch.empty((B, 1, N), dtype=torch.float32, device=dev)
-    idx = torch.empty((B, 1, cfg.k), dtype=torch.int32, device=dev)
-    out = torch.empty((B, 1, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
+    T = cfg.T
+    scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
+    out = torch.empty((B, T, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
     hout = torch.empty_like(out) if cfg.with_hca else None
+    # the HCA attention runs on its own stream, so it gets its own workspace
+    hca_ws = None
+    if cfg.with_hca:
+        nb = _lib.load().hca_attend_workspace_bytes(B, T, cfg.H, cfg.c, cfg.n_hca, cfg.n_win)
+        hca_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t_setup = time.time() - t0
 
-    first = N - 1  # the entry completed by the block ending at pos0-1
+    # decode: the entry completed by the block that ends at pos0-1; prefill: every entry of the chunk
+    first, n_new = sets[0]["ckv"]["first_entry"], sets[0]["ckv"]["num_entries"]
+
+    # the HCA layer does not depend on the CSA chain: it runs on a side stream that joins at the step's end
+    # (a cross-stream join inside a HIP graph costs a few microseconds, which only work of this size repays)
+    side = torch.cuda.Stream() if cfg.with_hca else None
 
     def step(st):
+        main_s = torch.cuda.current_stream()
+        if side is not None:
+            side.wait_stream(main_s)
+            with torch.cuda.stream(side):
+                c = st["chca"]
+                api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
+                             c["first_entry"], c["num_entries"], out=hca_cache[:, c["first_entry"]:],
+                             out_batch_stride=cfg.n_hca, stream=side)
+                api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
+                               cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side)
         c = st["ckv"]
         api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                     c["first_entry"], 1, out=kv_cache[:, first:], out_batch_stride=N)
+                     first, n_new, out=kv_cache[:, first:], out_batch_stride=N)
         c = st["cik"]
-        if fmt == "fp8":
+        if fmt in ("fp8", "mxfp4"):
             api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                         c["first_entry"], 1, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
-                         out_fmt="fp8", out_batch_stride=N)
-        elif fmt == "mxfp4":
-            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                         c["first_entry"], 1, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
-                         out_fmt="mxfp4", out_batch_stride=N)
+                         first, n_new, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
+                         out_fmt=fmt, out_batch_stride=N)
         else:
             api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                         c["first_entry"], 1, out=st["ik"][:, first:], out_batch_stride=N)
+                         first, n_new, out=st["ik"][:, first:], out_batch_stride=N)
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
         api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
                    cfg.eps, cfg.rope_base, out=out)
-        if cfg.with_hca:
-            c = st["chca"]
-            api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
-                         c["first_entry"], 1, out=hca_cache[:, c["first_entry"]:], out_batch_stride=cfg.n_hca)
-            api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                           cfg.scale, cfg.eps, cfg.rope_base, out=hout)
+        if side is not None:
+            main_s.wait_stream(side)
 
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -239,22 +253,40 @@ def main():
     torch.cuda.synchronize()
     idx_ms = e0.elapsed_time(e1) / a.steps
 
-    # algorithmic bytes of one csa_index launch: every visible K^I row (+ its scales) read once,
-    # the queries / weights read once per sequence, one float32 score written per entry
+    # algorithmic bytes of one csa_index launch: every K^I row (+ its scales) read once, the queries /
+    # weights read once per query row, one float32 score written per (row, entry)
     row_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt]
-    q_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt] * cfg.HI + 4 * cfg.HI
-    idx_bytes = B * (N * row_bytes + q_bytes + N * 4)
-    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    q_bytes = row_bytes * cfg.HI + 4 * cfg.HI
+    idx_bytes = B * (N * row_bytes + T * q_bytes + T * N * 4)
+    # algorithmic FLOPs: 2 HI cI per visible (row, entry) pair
+    pairs = sum(min((cfg.pos0 + r) // cfg.m, N) for r in range(T)) * B
+    idx_flops = 2 * cfg.HI * cfg.cI * pairs
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
     if os.path.exists(tpath):
         t = json.load(open(tpath))
         if t.get("source_hash") == source_hash("index.hip"):
             traffic = t.get("hbm_bytes_per_launch")
+    if prefill:   # a dense contraction with K^I reused across 4,096 query rows: MFMA-bound
+        achieved = idx_flops / (idx_ms * 1e-3) / 1e12
+        roofline = {"kernel": "csa_index", "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[fmt],
+                    "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS[fmt], "traffic": traffic,
+                    "algorithmic_flops_per_launch": idx_flops, "avg_launch_ms": idx_ms}
+    else:
+        achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+        roofline = {"kernel": "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                    "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms}
+    if cfg.name == configs.C3.name:
+        metric = METRIC
+    elif prefill:
+        metric = f"CSA+HCA chunked prefill tokens/s ({cfg.name}) + % MFMA roofline"
+    else:
+        metric = f"CSA decode tokens/s ({cfg.name}) + % HBM roofline"
 
     res = {
-        "metric": METRIC if cfg.name == configs.C3.name else f"CSA decode tokens/s ({cfg.name}) + % HBM roofline",
-        "value": B / (ms_step * 1e-3),
+        "metric": metric,
+        "value": B * T / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -265,18 +297,17 @@ def main():
         "vs_baseline": None,
         "dtype": {"fp8": "fp8+bf16", "mxfp4": "mxfp4+bf16", "bf16": "bf16"}[fmt],
         "data": "synthetic (seeded Gaussian, synth/gen.py recipe)",
-        "config": {"workload": cfg.name, "batch": B, "context": cfg.pos0, "compressed_entries": N, "heads": cfg.H,
+        "config": {"workload": cfg.name, "batch": B, "query_rows": T, "context": cfg.pos0, "compressed_entries": N,
+                   "heads": cfg.H,
                    "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
                    "hca_entries": cfg.n_hca if cfg.with_hca else 0, "input_sets_rotated": NSETS},
-        "roofline": {"kernel": "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms},
+        "roofline": roofline,
         "setup_s": round(t_setup, 1),
         "launch": "eager" if a.eager else "hip_graph (one graph per rotated input set)",
     }
 
     if not a.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, sets[0]["host"], host0)
+        res["cpu_baseline"] = (cpu_baseline_prefill if prefill else cpu_baseline)(cfg, sets[0]["host"], host0)
     print(json.dumps(res), flush=True)
 
 
@@ -339,3 +370,47 @@ def cpu_baseline(cfg, h, host0):
 
 if __name__ == "__main__":
     main()
+
+
+def cpu_baseline_prefill(cfg, h, host0):
+    """The float64 oracle, as it stands, on the chunked-prefill workload: the chunk's compression once, then
+    sampled query rows (index, top-k, attend, hca_attend) until about 10 s of host work, scaled to tokens/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    f = lambda x: None if x is None else oracle.decode_bf16(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+    t0 = time.time()
+    caches = {}
+    for nm, key, mm in (("ckv", "kv", cfg.m), ("cik", "ik_data", cfg.m), ("chca", "hca", cfg.m_hca)):
+        ci = h[nm]
+        new = oracle.compress(f(ci["ca"]), f(ci["cb"]), f(ci["za"]), f(ci["zb"]), f(ci["bias_a"]), f(ci["bias_b"]),
+                              mm, ci["row0_pos"], ci["first_entry"], ci["num_entries"])[0]
+        cache = oracle.decode_bf16(host0[key][0])
+        cache[ci["first_entry"]:ci["first_entry"] + ci["num_entries"]] = oracle.decode_bf16(oracle.encode_bf16(new))
+        caches[key] = cache
+    t_comp = time.time() - t0
+    qv, q, win, hq, hwin = f(h["qi"]["data"]), f(h["q"]), f(h["win"]), f(h["hq"]), f(h["hwin"])
+    rng = np.random.default_rng(0)
+    t1 = time.time()
+    done = 0
+    while time.time() - t1 < 10.0:
+        r = int(rng.integers(0, cfg.T))
+        t = cfg.pos0 + r
+        sc = oracle.index(qv[:, r:r + 1], h["w"][:, r:r + 1], caches["ik_data"][None], [t], cfg.m)
+        sel = oracle.topk(sc, [t], cfg.m, cfg.k)
+        full = np.full((1, cfg.T, cfg.k), -1, np.int32)
+        full[0, r] = sel[0, 0]
+        oracle.attend(q, caches["kv"][None], full, win, h["sink"], [cfg.pos0], cfg.m, cfg.n_win, cfg.rope_dims,
+                      cfg.scale, cfg.eps, cfg.rope_base, rows=[(0, r)])
+        oracle.hca_attend(hq, caches["hca"][None], hwin, h["hsink"], [cfg.pos0], cfg.m_hca, cfg.n_win,
+                          cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, rows=[(0, r)])
+        done += 1
+    t_rows = time.time() - t1
+    per_token = t_rows / done + t_comp / cfg.T
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} sampled query rows of the {cfg.T}-row chunk (index, top-k, attend, hca_attend; "
+                      f"{t_rows:.1f} s) plus the chunk's compression ({t_comp:.1f} s, amortised over {cfg.T} rows), "
+                      f"float64"}

@@ -103,6 +103,7 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
  *   k       : [B][n_max][cI] in qk_t (MXFP4: cI/2 bytes per row)
  *   k_scale : as q_scale with rows [B][n_max].
  *   scores  : float32 [B][T][n_max]
+ * All pointers 16-byte aligned (the MXFP4 q_scale at least 4-byte aligned).
  * Products run on MFMA with float32 accumulation for BF16 / FP8 / MXFP4 (row
  * scales are applied to the float32 dot products; MXFP4 block scales inside
  * the MFMA), and on float32 FMA for CSA_F32.

@@ -49,9 +49,14 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
                          out_scale, out_t, out_batch_stride, (hipStream_t)stream);
 }
 
-csa_status csa_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
-                     int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, float* scores,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+// shape / dtype / pointer checks of csa_index; CSA_OK with `empty` set means nothing to launch
+csa_status check_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
+                       int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, const float* scores,
+                       bool& empty) {
+  empty = false;
   if (B < 0 || T < 0 || HI < 1 || cI < 1 || n_max < 0 || m < 1) return CSA_ERR_SHAPE;
   if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
   if ((int64_t)B * T >= 65536) return CSA_ERR_UNSUPPORTED;  // grid.y limit
@@ -67,9 +72,26 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w, const v
     default:
       return CSA_ERR_UNSUPPORTED;
   }
-  if (B == 0 || T == 0 || n_max == 0) return CSA_OK;
+  if (B == 0 || T == 0 || n_max == 0) {
+    empty = true;
+    return CSA_OK;
+  }
   if (!q || !w || !k || !pos0 || !scores) return CSA_ERR_NULL;
   if ((qk_t == CSA_FP8_E4M3_ROWSCALE || qk_t == CSA_MXFP4_E8M0_B32) && (!q_scale || !k_scale)) return CSA_ERR_NULL;
+  // the MXFP4 query scales are read as one 32-bit word per head
+  if (qk_t == CSA_MXFP4_E8M0_B32 && (reinterpret_cast<uintptr_t>(q_scale) & 3)) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
+                     int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, float* scores,
+                     void* stream) {
+  bool empty;
+  const csa_status st = check_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, empty);
+  if (st != CSA_OK || empty) return st;
   return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, (hipStream_t)stream);
 }
 

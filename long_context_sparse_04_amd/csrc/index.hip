@@ -27,6 +27,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 16;                      // 4 waves x 16 tiles x 16 entries = 1024 entries / WG
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 16;
+constexpr int kRing = 4;                               // tiles in flight per wave
 
 template <int FMT>
 struct Fmt;
@@ -101,92 +102,112 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
     const int64_t* __restrict__ pos0, int m, float* __restrict__ scores) {
   constexpr int HI = NT * 16;
+  constexpr int RB = Fmt<FMT>::kRowBytes;
+  __shared__ __align__(16) uint8_t s_q[HI * RB];  // this query row's HI indexer queries
+  __shared__ float s_wq[HI];                      // w (times the fp8 query row scale) per head
+  __shared__ uint32_t s_qsc[HI];                  // MXFP4: the 4 E8M0 block scales of each head
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int gl = lane >> 4;
   const int row = blockIdx.y;  // b * T + r
   const int b = row / T;
   const int r = row - b * T;
-  const int64_t t = pos0[b] + r;
-  const int64_t vis = visible_entries(t, m, n_max);
   const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
   float* srow = scores + (int64_t)row * n_max;
 
-  // ---- A operand: this query row's HI heads, and the per-head epilogue weights
+  // wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) tile by tile
+  // through a ring of kRing + 1 tile buffers: the load of tile i + kRing is issued before tile i's
+  // MFMAs, into the buffer tile i - 1 has released, so kRing tiles are always in flight
+  const uint8_t* kb = kI + (int64_t)b * n_max * RB;
+  const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
+  constexpr int kSlots = kRing + 1;
+  Frag<FMT> kf[kSlots];
+  int ksc[kSlots];
+  float ksf[kSlots];
+  auto load_tile = [&](int slot, int64_t e0) {
+    const int64_t e = e0 + (lane & 15);
+    const int64_t el = e < n_max ? e : n_max - 1;
+    kf[slot] = load_frag<FMT>(kb + el * RB, lane);
+    ksc[slot] = 127;
+    ksf[slot] = 1.0f;
+    if constexpr (FMT == CSA_MXFP4_E8M0_B32)
+      ksc[slot] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
+    if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE)
+      ksf[slot] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
+  };
+  // the first kRing tiles go out before anything else (they do not wait for the query position;
+  // past the visible range they are simply not used)
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) load_tile(u, wave_first + 16 * u);
+
+  // ---- this row's queries and weights, loaded once per workgroup into LDS
+  const int64_t t = pos0[b] + r;
+  const int64_t vis = visible_entries(t, m, n_max);
+  {
+    const i32x4* src = reinterpret_cast<const i32x4*>(q + (int64_t)row * HI * RB);
+    i32x4* dst = reinterpret_cast<i32x4*>(s_q);
+#pragma unroll
+    for (int i = threadIdx.x; i < HI * RB / 16; i += kWaves * 64) dst[i] = src[i];
+    if (threadIdx.x < HI) {
+      float wv = w[(int64_t)row * HI + threadIdx.x];
+      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE)
+        wv *= static_cast<const float*>(q_scale)[(int64_t)row * HI + threadIdx.x];
+      s_wq[threadIdx.x] = wv;
+      if constexpr (FMT == CSA_MXFP4_E8M0_B32)
+        s_qsc[threadIdx.x] = reinterpret_cast<const uint32_t*>(q_scale)[(int64_t)row * HI + threadIdx.x];
+    }
+  }
+  __syncthreads();
+  // A operand (heads are MFMA rows) and the epilogue weights of the 4 heads of each lane's output rows
   Frag<FMT> qa[NT];
   int qsc[NT];
   float wq[NT][4];
 #pragma unroll
   for (int g = 0; g < NT; ++g) {
     const int head = 16 * g + (lane & 15);
-    qa[g] = load_frag_cached<FMT>(q + ((int64_t)row * HI + head) * Fmt<FMT>::kRowBytes, lane);
-    if constexpr (FMT == CSA_MXFP4_E8M0_B32)
-      qsc[g] = static_cast<const uint8_t*>(q_scale)[((int64_t)row * HI + head) * 4 + (lane >> 4)];
-    else
-      qsc[g] = 127;
+    const i32x4* p = reinterpret_cast<const i32x4*>(s_q + head * RB + gl * Fmt<FMT>::kLaneBytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h2 = 16 * g + 4 * (lane >> 4) + i;  // head of output row i in this lane
-      float wv = w[(int64_t)row * HI + h2];
-      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE) wv *= static_cast<const float*>(q_scale)[(int64_t)row * HI + h2];
-      wq[g][i] = wv;
-    }
+    for (int j = 0; j < Fmt<FMT>::kLaneBytes / 16; ++j) qa[g].v[j] = p[j];
+    qsc[g] = (FMT == CSA_MXFP4_E8M0_B32) ? (int)((s_qsc[head] >> (8 * gl)) & 0xFFu) : 127;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wq[g][i] = s_wq[16 * g + 4 * gl + i];  // head of output row i in this lane
   }
 
-  const uint8_t* kb = kI + (int64_t)b * n_max * Fmt<FMT>::kRowBytes;
-  // wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) in groups of
-  // 4 tiles (64 entries), double-buffered: the loads of group i+1 are in flight during group i
-  const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
-  const int gl = lane >> 4;
-  constexpr int NG = kTilesPerWave / 4;
-  Frag<FMT> kf[2][4];
-  int ksc[2][4];
-  float ksf[2][4];
-  auto load_group = [&](int buf, int64_t e0) {
+  // tiles past the visible range are not computed (their scores are -inf)
+  const int ntiles = (int)max((int64_t)0, min((int64_t)kTilesPerWave, (vis - wave_first + 15) / 16));
+  float p[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t e = e0 + 16 * u + (lane & 15);
-      const int64_t el = e < n_max ? e : n_max - 1;
-      kf[buf][u] = load_frag<FMT>(kb + el * Fmt<FMT>::kRowBytes, lane);
-      ksc[buf][u] = 127;
-      ksf[buf][u] = 1.0f;
-      if constexpr (FMT == CSA_MXFP4_E8M0_B32)
-        ksc[buf][u] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
-      if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE)
-        ksf[buf][u] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
-    }
-  };
-  if (wave_first < vis) load_group(0, wave_first);
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int buf = gi & 1;
-    const int64_t e0 = wave_first + (int64_t)gi * 64;
-    if (e0 >= n_max) break;
-    if (gi + 1 < NG && e0 + 64 < vis) load_group(buf ^ 1, e0 + 64);
-    const int64_t eo = e0 + lane;  // entry this lane writes
-    if (e0 >= vis) {               // fully masked group
-      if (eo < n_max) srow[eo] = -INFINITY;
-      continue;
-    }
-    float p[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+  for (int ti = 0; ti < kTilesPerWave; ++ti) {
+    const int slot = ti % kSlots;
+    const int u = ti & 3;
+    const int64_t e0 = wave_first + (int64_t)ti * 16;
+    if (ti + kRing < ntiles) load_tile((ti + kRing) % kSlots, e0 + 16 * kRing);
+    if (ti < ntiles) {
       float part = 0.0f;
 #pragma unroll
       for (int g = 0; g < NT; ++g) {
-        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[buf][u], qsc[g], ksc[buf][u]);
+        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[slot], qsc[g], ksc[slot]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wq[g][i], fmaxf(acc[i], 0.0f), part);
       }
-      p[u] = part * ksf[buf][u];  // the FP8 row scale is positive, so it factors out of every ReLU
+      p[u] = part * ksf[slot];  // the FP8 row scale is positive, so it factors out of every ReLU
+    } else {
+      p[u] = 0.0f;
     }
-    // reduce-scatter over the 4 lane groups: lane 16u + e ends with the sum for tile u, entry e
-    const bool hi2 = gl >= 2;
-    const float s0 = hi2 ? p[0] : p[2], s1 = hi2 ? p[1] : p[3];
-    const float k0 = (hi2 ? p[2] : p[0]) + __shfl_xor(s0, 32, 64);
-    const float k1 = (hi2 ? p[3] : p[1]) + __shfl_xor(s1, 32, 64);
-    const bool odd = gl & 1;
-    const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
-    if (eo < n_max) srow[eo] = (eo < vis) ? val : -INFINITY;
+    if (u == 3) {
+      // reduce-scatter over the 4 lane groups: lane 16u + e ends with the sum for tile u, entry e
+      const int64_t eg = e0 - 48;  // first entry of this group of 4 tiles
+      if (eg >= n_max) break;
+      const bool hi2 = gl >= 2;
+      const float s0 = hi2 ? p[0] : p[2], s1 = hi2 ? p[1] : p[3];
+      const float k0 = (hi2 ? p[2] : p[0]) + __shfl_xor(s0, 32, 64);
+      const float k1 = (hi2 ? p[3] : p[1]) + __shfl_xor(s1, 32, 64);
+      const bool odd = gl & 1;
+      const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
+      const int64_t eo = eg + lane;  // entry this lane writes
+      if (eo < n_max) srow[eo] = (eo < vis) ? val : -INFINITY;
+    }
   }
 }
 

@@ -86,6 +86,8 @@ def test_index_topk_attend_validation(lib):
     assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 0, DUMMY, None, DUMMY, nb, None) == 2
     assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 4096, DUMMY, None, DUMMY, nb, None) == 2
     assert lib.csa_topk(DUMMY, 4, 1, 262144, None, 4, 1024, DUMMY, None, DUMMY, nb, None) == 1
+    assert lib.csa_index(DUMMY, C.c_void_p(0x1002), DUMMY, DUMMY, DUMMY, 1, 1, 64, 128, 1000, DUMMY, 4, 3, DUMMY,
+                         None) == 2                 # MXFP4 query scales are read as aligned 32-bit words
     # attend
     ws = lib.csa_attend_workspace_bytes(4, 1, 128, 512, 1024, 128)
     assert ws > 0 and lib.csa_attend_workspace_bytes(1, 4096, 64, 512, 512, 128) == 0
