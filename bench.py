@@ -2,7 +2,7 @@
 """Benchmark of the CSA decode layer step on one MI355X.
 
 One step = one pass of the whole CSA layer step over one decode batch:
-  csa_compress (KV entry that completes at this step)  ->  csa_compress (indexer
+  csa_compress_pair (the KV entry that completes at this step and its indexer
   key, quantized to the cache format)  ->  csa_index  ->  csa_topk  ->  csa_attend
 (plus, for the Pro MXFP4 workload, the HCA layer: compress + hca_attend).
 
@@ -150,6 +150,8 @@ def main():
         st["ik_scale"] = ik_scale if (s == 0 or ik_scale is None) else ik_scale.clone()
         for nm in ("ckv", "cik") + (("chca",) if cfg.with_hca else ()):
             st[nm] = {k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in h[nm].items()}
+        for nm in ("ckv", "cik"):
+            st[nm + "_t"] = {k: st[nm][k] for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
         if cfg.with_hca:
             st.update(hq=up(h["hq"]), hwin=up(h["hwin"]), hsink=up(h["hsink"]))
         st["host"] = h if s == 0 else None
@@ -186,17 +188,13 @@ def main():
                              out_batch_stride=cfg.n_hca, stream=side)
                 api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
                                cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side)
-        c = st["ckv"]
-        api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                     first, n_new, out=kv_cache[:, first:], out_batch_stride=N)
+        # the block's KV entry and its indexer-key entry (quantized to the cache format) in one launch
         c = st["cik"]
-        if fmt in ("fp8", "mxfp4"):
-            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                         first, n_new, out=st["ik"][:, first:], out_scale=st["ik_scale"][:, first:],
-                         out_fmt=fmt, out_batch_stride=N)
-        else:
-            api.compress(c["ca"], c["cb"], c["za"], c["zb"], c["bias_a"], c["bias_b"], cfg.m, c["row0_pos"],
-                         first, n_new, out=st["ik"][:, first:], out_batch_stride=N)
+        ik_job = dict(st["cik_t"], out=st["ik"][:, first:], out_batch_stride=N,
+                      out_fmt=fmt if fmt in ("fp8", "mxfp4") else None,
+                      out_scale=st["ik_scale"][:, first:] if fmt in ("fp8", "mxfp4") else None)
+        api.compress_pair(dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N), ik_job, cfg.m,
+                          c["row0_pos"], first, n_new)
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
         api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,

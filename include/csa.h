@@ -91,6 +91,25 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
                         void* stream);
 
 /*
+ * csa_compress_pair -- two csa_compress problems in one launch: the same batch,
+ * token rows, ratio and entries, each with its own streams, biases, width,
+ * output format and output rows.  Meant for a block's KV entry and its
+ * indexer-key entry, which [CSA] (2) forms by the same compression from their
+ * own streams.  Arguments of problem 0 then problem 1 as in csa_compress
+ * (ca .. bias_b, c, out, out_scale, out_t, out_batch_stride), then the shared
+ * B, rows, m, row0_pos, first_entry, num_entries, in_t.  Same limits and errors
+ * as two csa_compress calls; nothing is launched if either is rejected.
+ */
+csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, const void* zb0,
+                             const float* bias_a0, const float* bias_b0, int c0,
+                             void* out0, void* out_scale0, int out_t0, int64_t out_batch_stride0,
+                             const void* ca1, const void* cb1, const void* za1, const void* zb1,
+                             const float* bias_a1, const float* bias_b1, int c1,
+                             void* out1, void* out_scale1, int out_t1, int64_t out_batch_stride1,
+                             int B, int rows, int m, int64_t row0_pos, int64_t first_entry,
+                             int num_entries, int in_t, void* stream);
+
+/*
  * csa_index -- lightning-indexer scores ([CSA] (2), the I_{t,s} equation):
  *   I[b][r][s] = sum_h w[b][r][h] * ReLU( q^I[b][r][h] . K^IComp[b][s] )
  * for s < min(floor(t/m), n_max) with t = pos0[b] + r; every other s in

@@ -20,6 +20,8 @@ SIGNATURES = {
     "csa_status_string": (C.c_char_p, [_I]),
     "csa_abi_version": (_I, []),
     "csa_compress": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _I, _I64, _P]),
+    "csa_compress_pair": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I,
+                               _I64, _I, _I, _I, _I64, _I64, _I, _I, _P]),
     "csa_index": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _I, _P, _P]),
     "csa_topk_workspace_bytes": (_SZ, [_I, _I, _I64, _I]),
     "csa_topk": (_I, [_P, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _SZ, _P]),

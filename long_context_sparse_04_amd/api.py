@@ -73,6 +73,41 @@ def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entri
     return out, out_scale
 
 
+def _compress_out(B, num_entries, c, fmt, dev):
+    if fmt == "f32":
+        return torch.empty((B, num_entries, c), dtype=torch.float32, device=dev), None
+    if fmt == "bf16":
+        return torch.empty((B, num_entries, c), dtype=torch.bfloat16, device=dev), None
+    if fmt == "fp8":
+        return (torch.empty((B, num_entries, c), dtype=torch.uint8, device=dev),
+                torch.empty((B, num_entries), dtype=torch.float32, device=dev))
+    return (torch.empty((B, num_entries, c // 2), dtype=torch.uint8, device=dev),
+            torch.empty((B, num_entries, c // 32), dtype=torch.uint8, device=dev))
+
+
+def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
+    """csa_compress_pair: two compression problems (dicts with ca, cb, za, zb, bias_a, bias_b and optional out,
+    out_scale, out_fmt, out_batch_stride) of the same rows and entries in one launch.  Returns
+    ((out0, scale0), (out1, scale1))."""
+    lib = _lib.load()
+    B, rows, _ = p0["ca"].shape
+    in_fmt = _TORCH_FMT[p0["ca"].dtype]
+    args, outs = [], []
+    for p in (p0, p1):
+        c = p["ca"].shape[2]
+        fmt = p.get("out_fmt") or in_fmt
+        out, osc = p.get("out"), p.get("out_scale")
+        if out is None:
+            out, osc = _compress_out(B, num_entries, c, fmt, p["ca"].device)
+        args += [_ptr(p["ca"]), _ptr(p.get("cb")), _ptr(p["za"]), _ptr(p.get("zb")), _ptr(p["bias_a"]),
+                 _ptr(p.get("bias_b")), c, out.data_ptr(), None if osc is None else osc.data_ptr(), FMT[fmt],
+                 p.get("out_batch_stride", 0)]
+        outs.append((out, osc))
+    st = lib.csa_compress_pair(*args, B, rows, m, row0_pos, first_entry, num_entries, FMT[in_fmt], _stream(stream))
+    _lib.check(st, "csa_compress_pair")
+    return tuple(outs)
+
+
 def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None):
     """csa_index.  q [B][T][HI][row], k [B][N][row]; returns float32 scores [B][T][N]."""
     lib = _lib.load()

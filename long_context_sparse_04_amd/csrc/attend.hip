@@ -153,6 +153,11 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   const double tpos = (double)t;
   const int dbase = wave * DW;
   const uint16_t* dummy = a.win + (int64_t)b * (a.T + a.n_win - 1) * C;  // a finite row for empty slots
+  // this wave's raw query fragments go out first: they depend on nothing
+  const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C + dbase;
+  u32x4 qraw[KSW];
+#pragma unroll
+  for (int ks = 0; ks < KSW; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
   if (threadIdx.x < 64) s_theta[threadIdx.x] = rt.theta[threadIdx.x];
   // slot resolution of a stage into half h of the resolve arrays (threads < kStage)
   auto resolve_stage = [&](int64_t st0, int h) {
@@ -170,17 +175,30 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     }
   };
   resolve_stage(slot_lo, 0);
+  // DMA of a stage's rows into E: instruction j of wave w fills rows RPI*(w + 4j) .. +RPI-1; lane l
+  // writes LDS chunk position (l % NCR) of row e = RPI*(w + 4j) + l / NCR, so it loads the logical
+  // chunk stored there
+  auto issue_dma = [&](const uint16_t* const* src_rows) {
+#pragma unroll
+    for (int j = 0; j < kStage / RPI / 4; ++j) {
+      const int e0 = RPI * (wave + 4 * j);
+      const int e = e0 + lane / NCR;
+      const int cpos = lane % NCR;
+      const uint16_t* src = src_rows[e] + 8 * swz<C>(e, cpos);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(E + e0 * C), 16, 0, 0);
+    }
+  };
+  __syncthreads();  // s_theta and the first stage's slots visible
+  issue_dma(s_src2);  // the first stage's rows land while the query is prepared
 
-  __syncthreads();  // s_theta (and the first stage's slots) visible
   // ---- query fragment: head lane&15, the wave's dims [dbase + 32ks + 8g, +8)
   bf16x8 qf[KSW];
   {
-    const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C + dbase;
-    u32x4 raw[KSW];
+    u32x4* raw = qraw;
     float ss = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
-      raw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
 #pragma unroll
       for (int j = 0; j < 4; ++j) ss = sumsq_bf16x2(raw[ks][j], ss);
     }
@@ -222,31 +240,24 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
   for (int d = 0; d < DTW; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15 (base-2 units)
-  __syncthreads();
-  // logits are kept in base-2 units (times log2 e) so that exponentials are single v_exp_f32
-  const float zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
-                                               s_rq[48 + (lane & 15)]) / (float)C + a.eps);
+  float zmul = 0.0f;              // set once the query norms of all four waves are in s_rq
 
   int half = 0;
   for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, half ^= 1) {
     const uint16_t** s_src = s_src2 + half * kStage;
     const double* s_pos = s_pos2 + half * kStage;
     const int* s_flag = s_flag2 + half * kStage;
-    // ---- (2) DMA: instruction j of wave w fills rows RPI*(w + 4j) .. +RPI-1; lane l writes LDS chunk
-    // position (l % NCR) of row e = RPI*(w + 4j) + l / NCR, so it loads the logical chunk stored there
-#pragma unroll
-    for (int j = 0; j < kStage / RPI / 4; ++j) {
-      const int e0 = RPI * (wave + 4 * j);
-      const int e = e0 + lane / NCR;
-      const int cpos = lane % NCR;
-      const uint16_t* src = s_src[e] + 8 * swz<C>(e, cpos);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(E + e0 * C), 16, 0, 0);
-    }
+    // ---- (2) DMA of this stage's rows (the first stage's went out before the query was prepared)
+    if (s0 != slot_lo) issue_dma(s_src);
     // the next stage's slot resolution (index-list loads) overlaps this stage's fetch and compute
     if (s0 + kStage < slot_hi) resolve_stage(s0 + kStage, half ^ 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (s0 == slot_lo) {
+      // logits are kept in base-2 units (times log2 e) so that exponentials are single v_exp_f32
+      zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
+                                       s_rq[48 + (lane & 15)]) / (float)C + a.eps);
+    }
     // ---- (3a) per-entry RMS scalar: 8 lanes per entry, two accumulators
 #pragma unroll 1
     for (int rd = 0; rd < kStage / 32; ++rd) {

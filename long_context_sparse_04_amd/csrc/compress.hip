@@ -59,15 +59,44 @@ struct Soft4 {
   }
 };
 
+// One compression problem: its streams, biases, width and output.  A launch serves one or two of
+// them (blockIdx.z), with the same batch, rows, ratio and entries, e.g. a block's KV entry and its
+// indexer-key entry.
+struct Job {
+  const void* ca;
+  const void* cb;
+  const void* za;
+  const void* zb;
+  const float* bias_a;
+  const float* bias_b;
+  int c;
+  void* out;
+  void* out_scale;
+  int out_t;
+  int64_t out_bstride;
+};
+struct Jobs {
+  Job j[2];
+};
+
 template <typename TIn>
-__global__ __launch_bounds__(kThreads) void compress_kernel(
-    const TIn* __restrict__ ca, const TIn* __restrict__ cb, const TIn* __restrict__ za,
-    const TIn* __restrict__ zb, const float* __restrict__ bias_a, const float* __restrict__ bias_b,
-    int rows, int c, int m, int64_t row0_pos, int64_t first_entry, void* __restrict__ out,
-    void* __restrict__ out_scale, int out_t, int64_t out_bstride) {
+__global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows, int m, int64_t row0_pos,
+                                                            int64_t first_entry) {
   __shared__ f32x4 s_m[kThreads], s_l[kThreads], s_a[kThreads];
   __shared__ float s_red[kThreads / 64];
 
+  const Job jb = blockIdx.z ? jobs.j[1] : jobs.j[0];  // uniform select (no indexed kernel-argument copy)
+  const TIn* __restrict__ ca = static_cast<const TIn*>(jb.ca);
+  const TIn* __restrict__ cb = static_cast<const TIn*>(jb.cb);
+  const TIn* __restrict__ za = static_cast<const TIn*>(jb.za);
+  const TIn* __restrict__ zb = static_cast<const TIn*>(jb.zb);
+  const float* __restrict__ bias_a = jb.bias_a;
+  const float* __restrict__ bias_b = jb.bias_b;
+  const int c = jb.c;
+  void* __restrict__ out = jb.out;
+  void* __restrict__ out_scale = jb.out_scale;
+  const int out_t = jb.out_t;
+  const int64_t out_bstride = jb.out_bstride;
   const int e = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -195,15 +224,21 @@ csa_status launch_compress(const void* ca, const void* cb, const void* za, const
                            const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos,
                            int64_t first_entry, int num_entries, int in_t, void* out, void* out_scale, int out_t,
                            int64_t out_bstride, hipStream_t stream) {
-  dim3 grid(num_entries, B);
-  if (in_t == CSA_F32) {
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)ca, (const float*)cb,
-                       (const float*)za, (const float*)zb, bias_a, bias_b, rows, c, m, row0_pos, first_entry, out,
-                       out_scale, out_t, out_bstride);
-  } else {
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)ca,
-                       (const uint16_t*)cb, (const uint16_t*)za, (const uint16_t*)zb, bias_a, bias_b, rows, c, m,
-                       row0_pos, first_entry, out, out_scale, out_t, out_bstride);
-  }
+  CompressJob j{ca, cb, za, zb, bias_a, bias_b, c, out, out_scale, out_t, out_bstride};
+  return launch_compress_jobs(&j, 1, B, rows, m, row0_pos, first_entry, num_entries, in_t, stream);
+}
+
+csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
+                                int64_t first_entry, int num_entries, int in_t, hipStream_t stream) {
+  Jobs js;
+  for (int i = 0; i < njobs; ++i)
+    js.j[i] = Job{jobs[i].ca, jobs[i].cb, jobs[i].za, jobs[i].zb, jobs[i].bias_a, jobs[i].bias_b, jobs[i].c,
+                  jobs[i].out, jobs[i].out_scale, jobs[i].out_t, jobs[i].out_bstride};
+  dim3 grid(num_entries, B, njobs);
+  if (in_t == CSA_F32)
+    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos, first_entry);
+  else
+    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos,
+                       first_entry);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

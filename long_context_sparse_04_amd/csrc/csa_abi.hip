@@ -24,15 +24,23 @@ const char* csa_status_string(int status) {
 
 int csa_abi_version(void) { return 1; }
 
-csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
-                        const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
-                        int num_entries, int in_t, void* out, void* out_scale, int out_t, int64_t out_batch_stride,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+// checks of one compression problem; CSA_OK with `empty` set means nothing to launch
+csa_status check_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
+                          const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
+                          int num_entries, int in_t, void* out, void* out_scale, int out_t,
+                          int64_t& out_batch_stride, bool& empty) {
+  empty = false;
   if (B < 0 || rows < 0 || num_entries < 0 || m < 1 || m > 1024 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
   if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (out_t < CSA_F32 || out_t > CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
   if (out_t == CSA_MXFP4_E8M0_B32 && (c % 32)) return CSA_ERR_UNSUPPORTED;
-  if (B == 0 || num_entries == 0) return CSA_OK;
+  if (B == 0 || num_entries == 0) {
+    empty = true;
+    return CSA_OK;
+  }
   const bool overlap = cb != nullptr || zb != nullptr || bias_b != nullptr;
   if (!ca || !za || !bias_a || !out) return CSA_ERR_NULL;
   if (overlap && (!cb || !zb || !bias_b)) return CSA_ERR_NULL;
@@ -45,8 +53,41 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
   const int64_t lo_entry = (overlap && first_entry > 0) ? first_entry - 1 : first_entry;
   if ((int64_t)m * lo_entry < row0_pos) return CSA_ERR_SHAPE;
   if ((int64_t)m * (last + 1) - 1 >= row0_pos + rows) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
+                        const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
+                        int num_entries, int in_t, void* out, void* out_scale, int out_t, int64_t out_batch_stride,
+                        void* stream) {
+  bool empty;
+  const csa_status st = check_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry,
+                                       num_entries, in_t, out, out_scale, out_t, out_batch_stride, empty);
+  if (st != CSA_OK || empty) return st;
   return launch_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry, num_entries, in_t, out,
                          out_scale, out_t, out_batch_stride, (hipStream_t)stream);
+}
+
+csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, const void* zb0,
+                             const float* bias_a0, const float* bias_b0, int c0, void* out0, void* out_scale0,
+                             int out_t0, int64_t out_batch_stride0, const void* ca1, const void* cb1,
+                             const void* za1, const void* zb1, const float* bias_a1, const float* bias_b1, int c1,
+                             void* out1, void* out_scale1, int out_t1, int64_t out_batch_stride1, int B, int rows,
+                             int m, int64_t row0_pos, int64_t first_entry, int num_entries, int in_t, void* stream) {
+  bool e0, e1;
+  csa_status st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry,
+                                 num_entries, in_t, out0, out_scale0, out_t0, out_batch_stride0, e0);
+  if (st != CSA_OK) return st;
+  st = check_compress(ca1, cb1, za1, zb1, bias_a1, bias_b1, B, rows, c1, m, row0_pos, first_entry, num_entries, in_t,
+                      out1, out_scale1, out_t1, out_batch_stride1, e1);
+  if (st != CSA_OK || e0) return st;  // both problems share B and num_entries, so both are empty or neither
+  const CompressJob jobs[2] = {
+      {ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, out_scale0, out_t0, out_batch_stride0},
+      {ca1, cb1, za1, zb1, bias_a1, bias_b1, c1, out1, out_scale1, out_t1, out_batch_stride1}};
+  return launch_compress_jobs(jobs, 2, B, rows, m, row0_pos, first_entry, num_entries, in_t, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -12,6 +12,23 @@ csa_status launch_compress(const void* ca, const void* cb, const void* za, const
                            int64_t first_entry, int num_entries, int in_t, void* out, void* out_scale, int out_t,
                            int64_t out_bstride, hipStream_t stream);
 
+// one problem of a compression launch (see csa_compress_pair)
+struct CompressJob {
+  const void* ca;
+  const void* cb;
+  const void* za;
+  const void* zb;
+  const float* bias_a;
+  const float* bias_b;
+  int c;
+  void* out;
+  void* out_scale;
+  int out_t;
+  int64_t out_bstride;
+};
+csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
+                                int64_t first_entry, int num_entries, int in_t, hipStream_t stream);
+
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
                         float* scores, hipStream_t stream);

@@ -510,24 +510,34 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     return seg[(int64_t)c * kChunk + (j - s_pre[c])];
   };
   if (in_lds) {
-    constexpr int kGather = kSegCap / kSplitThreads;  // 24 candidates per thread at most
-    int64_t src[kGather];
+    // wave w copies the segments of chunks w, w + 4, ...: lane i takes element i (and i + 64, ... of
+    // the rare chunk with more than 64 candidates); a batch of kBatch chunks is loaded before storing
+    constexpr int kBatch = 16;
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int c0 = wave; c0 < nch; c0 += 4 * kBatch) {
+      Cand cv[kBatch];
+      int dst[kBatch];
+      int nmax = 0;
 #pragma unroll
-    for (int u = 0; u < kGather; ++u) {
-      const int j = tid + u * kSplitThreads;
-      int64_t sidx = -1;
-      if (j < C) {
-        const int c = chunk_of(j);
-        sidx = (int64_t)c * kChunk + (j - s_pre[c]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = c0 + 4 * u;
+        const int n = c < nch ? s_pre[c + 1] - s_pre[c] : 0;
+        nmax = max(nmax, n);
+        dst[u] = lane < n ? s_pre[c] + lane : -1;
+        cv[u] = seg[(int64_t)(c < nch ? c : 0) * kChunk + (lane < n ? lane : 0)];
       }
-      src[u] = sidx;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (dst[u] >= 0) s_c[dst[u]] = cv[u];
+      if (nmax > 64) {  // (wave-uniform) a chunk of this batch holds more than 64 candidates
+#pragma unroll 1
+        for (int u = 0; u < kBatch; ++u) {
+          const int c = c0 + 4 * u;
+          const int n = c < nch ? s_pre[c + 1] - s_pre[c] : 0;
+          for (int i = 64 + lane; i < n; i += 64) s_c[s_pre[c] + i] = seg[(int64_t)c * kChunk + i];
+        }
+      }
     }
-    Cand cv[kGather];
-#pragma unroll
-    for (int u = 0; u < kGather; ++u) cv[u] = seg[src[u] >= 0 ? src[u] : 0];
-#pragma unroll
-    for (int u = 0; u < kGather; ++u)
-      if (src[u] >= 0) s_c[tid + u * kSplitThreads] = cv[u];
   }
   __syncthreads();
   auto cand = [&](int j) -> Cand { return in_lds ? s_c[j] : cand_global(j); };

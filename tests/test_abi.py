@@ -70,6 +70,23 @@ def test_compress_validation(lib):
     assert call(B=0) == 0
 
 
+def test_compress_pair_validation(lib):
+    P = DUMMY
+
+    def pair(**kw):
+        a = dict(c0=512, c1=128, t0=1, t1=2, os1=P, B=4, rows=8, m=4, r0=1048568, first=262143, n=1, in_t=1)
+        a.update(kw)
+        return lib.csa_compress_pair(P, P, P, P, P, P, a["c0"], P, None, a["t0"], 262144,
+                                     P, P, P, P, P, P, a["c1"], P, a["os1"], a["t1"], 262144,
+                                     a["B"], a["rows"], a["m"], a["r0"], a["first"], a["n"], a["in_t"], None)
+    assert pair(os1=None) == 1          # fp8 output of problem 1 needs its scales
+    assert pair(c1=130) == 2
+    assert pair(t1=3, c1=48) == 3       # MXFP4 needs a width in multiples of 32
+    assert pair(r0=1048569) == 2        # entry 262143 reads rows from 1048568 on
+    assert pair(in_t=2) == 3
+    assert pair(n=0) == 0 and pair(B=0) == 0
+
+
 def test_index_topk_attend_validation(lib):
     assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, None) == 3
     assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, None) == 3

@@ -151,9 +151,11 @@ def test_decode_step_full_size(api, name):
     ik = dev(cc["ik"])
     ik_scale = dev(cc["ik_scale"])
     first = N - 1
-    _gpu_compress(api, ckv, kv_cache[:, first:], stride=N)
-    _gpu_compress(api, cik, ik[:, first:], None if ik_scale is None else ik_scale[:, first:],
-                  fmt if fmt != "bf16" else None, stride=N)
+    d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    api.compress_pair(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N),
+                      dict(d(cik), out=ik[:, first:], out_batch_stride=N, out_fmt=fmt if fmt != "bf16" else None,
+                           out_scale=None if ik_scale is None else ik_scale[:, first:]),
+                      ckv["m"], ckv["row0_pos"], first, 1)
     scores = api.index(dev(qi["data"]), dev(qi.get("scale")), dev(w), ik, ik_scale, pos, cfg.m, fmt)
     idx, _ = api.topk(scores, pos, cfg.m, cfg.k)
     out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,

@@ -112,6 +112,36 @@ def test_compress_quantized_indexer_keys(api):
     assert codes_close(nib(p), nib(rp), scaled, oracle.e2m1_values())
 
 
+@pytest.mark.parametrize("name,fmt", [("c3", "fp8"), ("c5", "mxfp4"), ("c2", "bf16"), ("c1", "f32")])
+def test_compress_pair_matches_two_calls(api, name, fmt):
+    """csa_compress_pair (a block's KV entry and indexer-key entry in one launch) writes exactly what two
+    csa_compress calls write, also into cache rows with a batch stride."""
+    cfg = configs.get_config(name)
+    if cfg.T == 1:
+        cfg = cfg.scaled(B=6)
+    kv, ik = gen.compress_inputs(cfg), gen.compress_inputs(cfg, indexer=True)
+    say(f"compress_pair {name} kv + indexer keys ({fmt})")
+    d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    geo = (kv["m"], kv["row0_pos"], kv["first_entry"], kv["num_entries"])
+    ik_fmt = None if fmt in ("bf16", "f32") else fmt
+    (o0, _), (o1, s1) = api.compress_pair(d(kv), dict(d(ik), out_fmt=ik_fmt), *geo)
+    r0, _ = api.compress(*d(kv).values(), *geo)
+    r1, t1 = api.compress(*d(ik).values(), *geo, out_fmt=ik_fmt)
+    # into strided cache rows
+    n = geo[3]
+    cache = torch.zeros((cfg.B, n + 5, cfg.c), dtype=o0.dtype, device=DEV)
+    (o2, _), _ = api.compress_pair(dict(d(kv), out=cache[:, 3:], out_batch_stride=n + 5),
+                                   dict(d(ik), out_fmt=ik_fmt), *geo)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.uint8)
+    assert torch.equal(bits(o0), bits(r0)) and torch.equal(bits(o1), bits(r1))
+    if s1 is not None:
+        assert torch.equal(s1.view(torch.uint8), t1.view(torch.uint8))
+    assert torch.equal(bits(cache[:, 3:3 + n]), bits(r0))
+    assert torch.count_nonzero(bits(cache[:, :3]).to(torch.int32)) == 0
+    assert torch.count_nonzero(bits(cache[:, 3 + n:]).to(torch.int32)) == 0
+
+
 def test_compress_into_cache_with_stride(api):
     cfg = configs.C2.scaled(B=3)
     ci = gen.compress_inputs(cfg)
