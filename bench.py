@@ -2,8 +2,9 @@
 """Benchmark of the CSA decode layer step on one MI355X.
 
 One step = one pass of the whole CSA layer step over one decode batch:
-  csa_compress_pair (the KV entry that completes at this step and its indexer
-  key, quantized to the cache format)  ->  csa_index  ->  csa_topk  ->  csa_attend
+  csa_compress_pair (the KV entry that completes at this step, stored prepared
+  for attention, and its indexer key, quantized to the cache format)  ->
+  csa_index  ->  csa_topk  ->  csa_attend (prepared compressed entries, raw window)
 (plus, for the Pro MXFP4 workload, the HCA layer: compress + hca_attend).
 
 Default workload: Pro-shaped decode at 1M context (B=4, 262,144 compressed
@@ -157,6 +158,12 @@ def main():
         st["host"] = h if s == 0 else None
         sets.append(st)
     pos = torch.full((B,), cfg.pos0, dtype=torch.int64, device=dev)
+    # compressed entries are stored prepared for attention (RMSNorm + RoPE at their positions, done once when
+    # an entry is written); the synthetic context caches are prepared here, outside the timed region
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)
+    if cfg.with_hca:
+        api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
     T = cfg.T
     scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
     idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
@@ -185,20 +192,21 @@ def main():
                 c = st["chca"]
                 api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
                              c["first_entry"], c["num_entries"], out=hca_cache[:, c["first_entry"]:],
-                             out_batch_stride=cfg.n_hca, stream=side)
+                             out_batch_stride=cfg.n_hca, prep=prep, stream=side)
                 api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
-                               cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side)
+                               cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side,
+                               kv_prepared=True)
         # the block's KV entry and its indexer-key entry (quantized to the cache format) in one launch
         c = st["cik"]
         ik_job = dict(st["cik_t"], out=st["ik"][:, first:], out_batch_stride=N,
                       out_fmt=fmt if fmt in ("fp8", "mxfp4") else None,
                       out_scale=st["ik_scale"][:, first:] if fmt in ("fp8", "mxfp4") else None)
-        api.compress_pair(dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N), ik_job, cfg.m,
+        api.compress_pair(dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep), ik_job, cfg.m,
                           c["row0_pos"], first, n_new)
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
         api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
-                   cfg.eps, cfg.rope_base, out=out)
+                   cfg.eps, cfg.rope_base, out=out, kv_prepared=True)
         if side is not None:
             main_s.wait_stream(side)
 

@@ -52,6 +52,21 @@ typedef enum {
   CSA_ERR_LAUNCH = 5       /* the kernel launch failed                        */
 } csa_status;
 
+/*
+ * Preparation of a KV row for core attention ([details] (1) and (2)):
+ *   x -> RoPE_pos( x / sqrt(mean(x^2) + eps) * gamma ), RoPE on the pairs
+ *   (c-R+2i, c-R+2i+1), R = rope_dims, angle pos * rope_base^(-2i/R).
+ * A compressed entry or a token row keeps its position for good, so its prepared
+ * form can be stored once (csa_compress with a csa_kv_prep, csa_prepare_kv) and
+ * reused by every later query (csa_attend / hca_attend with kv_prepared = 1).
+ */
+typedef struct {
+  const float* gamma; /* device float32 [c] RMSNorm gain, NULL = 1 */
+  float eps;          /* RMSNorm epsilon */
+  int rope_dims;      /* R: even, a multiple of 8, <= min(c, 128); 0 = no rotation */
+  float rope_base;    /* RoPE base */
+} csa_kv_prep;
+
 /* Static, NUL-terminated description of a status code. */
 const char* csa_status_string(int status);
 /* ABI revision of this header (bumped on any signature change). */
@@ -80,6 +95,9 @@ int csa_abi_version(void);
  *                    CSA_MXFP4_E8M0_B32: c/2 bytes per row, and out_scale (uint8,
  *                    c/32 per row) = floor(log2 amax) - 2 + 127, codes RNE,
  *                    saturated at 6.  out_scale is ignored for F32 / BF16.
+ *   prep           : NULL, or the entries are stored prepared for attention
+ *                    (see csa_kv_prep) at position m * i; CSA_F32 / CSA_BF16
+ *                    outputs only.
  * Limits: 1 <= m <= 1024, c a multiple of 4 and <= 1024 (of 32 for MXFP4).
  */
 csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb,
@@ -88,7 +106,7 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
                         int64_t row0_pos, int64_t first_entry, int num_entries,
                         int in_t,
                         void* out, void* out_scale, int out_t, int64_t out_batch_stride,
-                        void* stream);
+                        const csa_kv_prep* prep, void* stream);
 
 /*
  * csa_compress_pair -- two csa_compress problems in one launch: the same batch,
@@ -96,18 +114,35 @@ csa_status csa_compress(const void* ca, const void* cb, const void* za, const vo
  * output format and output rows.  Meant for a block's KV entry and its
  * indexer-key entry, which [CSA] (2) forms by the same compression from their
  * own streams.  Arguments of problem 0 then problem 1 as in csa_compress
- * (ca .. bias_b, c, out, out_scale, out_t, out_batch_stride), then the shared
- * B, rows, m, row0_pos, first_entry, num_entries, in_t.  Same limits and errors
- * as two csa_compress calls; nothing is launched if either is rejected.
+ * (ca .. bias_b, c, out, out_scale, out_t, out_batch_stride, prep), then the
+ * shared B, rows, m, row0_pos, first_entry, num_entries, in_t.  Same limits and
+ * errors as two csa_compress calls; nothing is launched if either is rejected.
  */
 csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, const void* zb0,
                              const float* bias_a0, const float* bias_b0, int c0,
                              void* out0, void* out_scale0, int out_t0, int64_t out_batch_stride0,
+                             const csa_kv_prep* prep0,
                              const void* ca1, const void* cb1, const void* za1, const void* zb1,
                              const float* bias_a1, const float* bias_b1, int c1,
                              void* out1, void* out_scale1, int out_t1, int64_t out_batch_stride1,
+                             const csa_kv_prep* prep1,
                              int B, int rows, int m, int64_t row0_pos, int64_t first_entry,
                              int num_entries, int in_t, void* stream);
+
+/*
+ * csa_prepare_kv -- prepares KV rows for attention (see csa_kv_prep).
+ *   in  : [B] blocks of `rows` rows of c values in in_t (CSA_F32 / CSA_BF16);
+ *         row j of sequence b at in + (b * in_batch_stride + j) * c.
+ *   out : the same layout with out_batch_stride, in out_t; may alias `in`.
+ *   position of row j of sequence b: (pos_base ? pos_base[b] : 0) + pos_first
+ *   + j * pos_stride (pos_base a device int64 [B] array), e.g. pos_stride = m
+ *   for a compressed cache, 1 for token rows.  prep must not be NULL.
+ * Limits: c a multiple of 4 and <= 1024; R as in csa_kv_prep.
+ */
+csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, int64_t out_batch_stride,
+                          int B, int rows, int c, int in_t, int out_t,
+                          const int64_t* pos_base, int64_t pos_first, int64_t pos_stride,
+                          const csa_kv_prep* prep, void* stream);
 
 /*
  * csa_index -- lightning-indexer scores ([CSA] (2), the I_{t,s} equation):
@@ -172,13 +207,19 @@ csa_status csa_topk(const float* scores, int B, int T, int64_t n_max,
  *   idx     : int32 [B][T][k]; entries < 0 or >= n_max are skipped
  *   win_kv  : [B][T + n_win - 1][c] in kv_t; row j holds position pos0[b]-n_win+1+j
  *   sink    : float32 [H]     gamma_q, gamma_kv : float32 [c] or NULL
+ *   kv_prepared : 0 = comp_kv holds pooled entries e; 1 = comp_kv holds the
+ *               prepared e^ (csa_compress with a csa_kv_prep of the same gamma_kv,
+ *               eps, rope_dims and rope_base, or csa_prepare_kv with
+ *               pos_stride = m), which are then used as they are.  Window rows
+ *               are always the raw token rows.
  *   out     : [B][T][H][c] in out_t (CSA_F32 or CSA_BF16)
  *   workspace : csa_attend_workspace_bytes(B, T, H, c, k, n_win) bytes of device
  *               memory (no initial contents needed); may be NULL if that is 0.
  * kv_t is CSA_F32 (float32 FMA path) or CSA_BF16 (MFMA path, float32 softmax
- * and accumulation).  Decode (T = 1) splits each query's entry list at fixed
- * boundaries that depend only on that query's own list and merges the parts in a
- * fixed order, so results do not depend on B or on the other rows.
+ * and accumulation).  Decode (T = 1) splits each query's entry list (compressed
+ * part and window part separately) at fixed boundaries that depend only on the
+ * list lengths and merges the parts in a fixed order, so results do not depend
+ * on B or on the other rows.
  * Limits: c in {128, 256, 512}; rope_dims even, a multiple of 8 and <= min(c, 128);
  * H a multiple of 16 for CSA_BF16 (any H >= 1 for CSA_F32); 1 <= k <= 2048;
  * 1 <= n_win <= 4096.
@@ -188,13 +229,14 @@ csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, co
                       const float* sink, const float* gamma_q, const float* gamma_kv,
                       int B, int T, int H, int c, int rope_dims, int k, int n_win, int64_t n_max,
                       const int64_t* pos0, int m, float scale, float eps, float rope_base,
-                      int kv_t, void* out, int out_t,
+                      int kv_t, int kv_prepared, void* out, int out_t,
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * hca_attend -- HCA core attention ([HCA] (2)): as csa_attend, with the
  * compressed part dense: every visible entry s < min(floor(t/m_hca), n_max) of
- * comp_kv, each at position m_hca * s.  Same layouts, limits and workspace rule
+ * comp_kv, each at position m_hca * s.  Same layouts, limits, kv_prepared rule
+ * (prepared entries at pos_stride = m_hca) and workspace rule
  * (hca_attend_workspace_bytes).
  */
 size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win);
@@ -202,7 +244,7 @@ csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv,
                       const float* sink, const float* gamma_q, const float* gamma_kv,
                       int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
                       const int64_t* pos0, int m_hca, float scale, float eps, float rope_base,
-                      int kv_t, void* out, int out_t,
+                      int kv_t, int kv_prepared, void* out, int out_t,
                       void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -14,23 +14,32 @@ F32, BF16, FP8_E4M3_ROWSCALE, MXFP4_E8M0_B32 = 0, 1, 2, 3
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_UNSUPPORTED", 4: "CSA_ERR_WORKSPACE",
           5: "CSA_ERR_LAUNCH"}
 
+
+
+class KvPrep(C.Structure):
+    """csa_kv_prep: RMSNorm gain / epsilon and RoPE dims / base of the KV preparation."""
+    _fields_ = [("gamma", C.c_void_p), ("eps", C.c_float), ("rope_dims", C.c_int), ("rope_base", C.c_float)]
+
+
 # name -> (restype, argtypes); must match include/csa.h
 _P, _I, _I64, _F, _SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+_PREP = C.POINTER(KvPrep)
 SIGNATURES = {
     "csa_status_string": (C.c_char_p, [_I]),
     "csa_abi_version": (_I, []),
-    "csa_compress": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _I, _I64, _P]),
-    "csa_compress_pair": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I,
-                               _I64, _I, _I, _I, _I64, _I64, _I, _I, _P]),
+    "csa_compress": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _I, _I64, _PREP, _P]),
+    "csa_compress_pair": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _PREP, _P, _P, _P, _P, _P, _P, _I, _P,
+                               _P, _I, _I64, _PREP, _I, _I, _I, _I64, _I64, _I, _I, _P]),
+    "csa_prepare_kv": (_I, [_P, _I64, _P, _I64, _I, _I, _I, _I, _I, _P, _I64, _I64, _PREP, _P]),
     "csa_index": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _I, _P, _P]),
     "csa_topk_workspace_bytes": (_SZ, [_I, _I, _I64, _I]),
     "csa_topk": (_I, [_P, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _P,
-                        _I, _P, _SZ, _P]),
+    "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I,
+                        _P, _I, _P, _SZ, _P]),
     "hca_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I64, _I]),
-    "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _P, _I, _P,
-                        _SZ, _P]),
+    "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _P, _I,
+                        _P, _SZ, _P]),
 }
 
 _lib = None

@@ -7,6 +7,8 @@ torch.bfloat16 (bit patterns), fp8 / MXFP4 data as torch.uint8.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
 from . import _lib
@@ -46,9 +48,21 @@ def workspace(nbytes: int, device, key: str, zero: bool = False) -> torch.Tensor
     return ws
 
 
+def kv_prep(rope_dims, eps=1e-6, rope_base=10000.0, gamma=None):
+    """A csa_kv_prep (keep the returned object alive while the call that uses it is made)."""
+    p = _lib.KvPrep(_ptr(gamma), eps, rope_dims, rope_base)
+    p._gamma = gamma
+    return p
+
+
+def _prep_arg(prep):
+    return None if prep is None else C.byref(prep)
+
+
 def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entries, out=None, out_scale=None,
-             out_fmt=None, out_batch_stride=0, stream=None):
-    """csa_compress.  ca/za (and cb/zb for CSA) are [B][rows][c] f32 or bf16 tensors."""
+             out_fmt=None, out_batch_stride=0, prep=None, stream=None):
+    """csa_compress.  ca/za (and cb/zb for CSA) are [B][rows][c] f32 or bf16 tensors; prep (kv_prep) stores the
+    entries prepared for attention."""
     lib = _lib.load()
     B, rows, c = ca.shape
     in_fmt = _TORCH_FMT[ca.dtype]
@@ -68,7 +82,7 @@ def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entri
     st = lib.csa_compress(_ptr(ca), _ptr(cb), _ptr(za), _ptr(zb), _ptr(bias_a), _ptr(bias_b), B, rows, c, m,
                           row0_pos, first_entry, num_entries, FMT[in_fmt], out.data_ptr(),
                           None if out_scale is None else out_scale.data_ptr(), FMT[out_fmt], out_batch_stride,
-                          _stream(stream))
+                          _prep_arg(prep), _stream(stream))
     _lib.check(st, "csa_compress")
     return out, out_scale
 
@@ -87,7 +101,7 @@ def _compress_out(B, num_entries, c, fmt, dev):
 
 def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
     """csa_compress_pair: two compression problems (dicts with ca, cb, za, zb, bias_a, bias_b and optional out,
-    out_scale, out_fmt, out_batch_stride) of the same rows and entries in one launch.  Returns
+    out_scale, out_fmt, out_batch_stride, prep) of the same rows and entries in one launch.  Returns
     ((out0, scale0), (out1, scale1))."""
     lib = _lib.load()
     B, rows, _ = p0["ca"].shape
@@ -101,7 +115,7 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
             out, osc = _compress_out(B, num_entries, c, fmt, p["ca"].device)
         args += [_ptr(p["ca"]), _ptr(p.get("cb")), _ptr(p["za"]), _ptr(p.get("zb")), _ptr(p["bias_a"]),
                  _ptr(p.get("bias_b")), c, out.data_ptr(), None if osc is None else osc.data_ptr(), FMT[fmt],
-                 p.get("out_batch_stride", 0)]
+                 p.get("out_batch_stride", 0), _prep_arg(p.get("prep"))]
         outs.append((out, osc))
     st = lib.csa_compress_pair(*args, B, rows, m, row0_pos, first_entry, num_entries, FMT[in_fmt], _stream(stream))
     _lib.check(st, "csa_compress_pair")
@@ -140,8 +154,23 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
     return idx, vals
 
 
+def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_fmt=None, stream=None):
+    """csa_prepare_kv: rows x [B][rows][c] -> RoPE_pos(RMSNorm(x)), row j of sequence b at position
+    (pos_base[b] if given) + pos_first + j * pos_stride.  out may be x itself (in place)."""
+    lib = _lib.load()
+    B, rows, c = x.shape
+    in_fmt = _TORCH_FMT[x.dtype]
+    out_fmt = out_fmt or in_fmt
+    if out is None:
+        out = torch.empty((B, rows, c), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=x.device)
+    st = lib.csa_prepare_kv(_ptr(x), rows, _ptr(out), rows, B, rows, c, FMT[in_fmt], FMT[out_fmt], _ptr(pos_base),
+                            pos_first, pos_stride, _prep_arg(prep), _stream(stream))
+    _lib.check(st, "csa_prepare_kv")
+    return out
+
+
 def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-           gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None):
+           gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False):
     """csa_attend.  q [B][T][H][c], comp_kv [B][N][c], idx int32 [B][T][k], win_kv [B][T+n_win-1][c]."""
     lib = _lib.load()
     B, T, H, c = q.shape
@@ -156,13 +185,13 @@ def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=
         ws = workspace(nb, q.device, "attend")
     st = lib.csa_attend(_ptr(q), _ptr(comp_kv), _ptr(idx), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv),
                         B, T, H, c, rope_dims, k, n_win, N, _ptr(pos0), m, scale, eps, rope_base, FMT[kv_fmt],
-                        _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+                        int(kv_prepared), _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
     _lib.check(st, "csa_attend")
     return out
 
 
 def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-               gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None):
+               gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False):
     """hca_attend: dense over every visible compressed entry s < floor(t/m_hca), plus the window."""
     lib = _lib.load()
     B, T, H, c = q.shape
@@ -175,7 +204,7 @@ def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, e
     if ws is None:
         ws = workspace(nb, q.device, "hca")
     st = lib.hca_attend(_ptr(q), _ptr(comp_kv), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv), B, T, H, c,
-                        rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base, FMT[kv_fmt], _ptr(out),
-                        FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+                        rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base, FMT[kv_fmt],
+                        int(kv_prepared), _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
     _lib.check(st, "hca_attend")
     return out

@@ -52,6 +52,8 @@ struct AttnArgs {
   float* ws_o;     // [rows][nsplit][H][C]
   float* ws_ml;    // [rows][nsplit][H][2]
   int T, H, R, k, n_win, m, out_t, mode, nsplit;
+  int prepared;           // compressed entries are stored prepared (RMSNorm + RoPE done)
+  int ns_c, s_c, s_w;     // split layout: ns_c compressed parts of s_c slots, then window parts of s_w
   int64_t n_max;
   float scale, eps;
 };
@@ -118,7 +120,7 @@ constexpr int kStage = 64;  // slots fetched into LDS at once (2 compute tiles)
 // (2) DMA every row straight into LDS (global_load_lds, 16 B per lane, no registers),
 // (3) per-entry RMS scalar and RoPE in place, (4) two 32-slot tiles of MFMA work from LDS.
 template <int C>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int split_slots, int nx) {
+__global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int nx) {
   constexpr int DW = C / 4;     // dims per wave
   constexpr int KSW = DW / 32;  // k-steps of the wave's partial S^T = E Q^T
   constexpr int DTW = DW / 16;  // 16-dim output tiles of the wave
@@ -132,7 +134,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   double* s_theta = reinterpret_cast<double*>(s_rq + 64);                  // [64]
   double* s_pos2 = s_theta + 64;                                           // [2][kStage]
   const uint16_t** s_src2 = reinterpret_cast<const uint16_t**>(s_pos2 + 2 * kStage);  // [2][kStage]
-  int* s_flag2 = reinterpret_cast<int*>(s_src2 + 2 * kStage);              // [2][kStage]
+  int* s_flag2 = reinterpret_cast<int*>(s_src2 + 2 * kStage);              // [2][kStage] 1 valid | 2 raw
+  int* s_raw2 = s_flag2 + 2 * kStage;                                      // [2] stage holds a raw row
 
   if ((int)blockIdx.x >= nx) return;  // grid.x is padded to a multiple of 8 (XCD-aligned head groups)
   const int lane = threadIdx.x & 63;
@@ -148,8 +151,15 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   const int head = h0 + (lane & 15);
   const int rope_lo = C - a.R;
   const int64_t nslots = ((a.mode == 0) ? a.k : a.n_max) + a.n_win;
-  const int64_t slot_lo = (int64_t)sp * split_slots;
-  const int64_t slot_hi = min(slot_lo + split_slots, nslots);
+  const int64_t ncomp = (a.mode == 0) ? a.k : a.n_max;
+  int64_t slot_lo, slot_hi;
+  if (sp < a.ns_c) {  // a part of the compressed slots (or, with one part per query, of all slots)
+    slot_lo = (int64_t)sp * a.s_c;
+    slot_hi = min(slot_lo + a.s_c, a.nsplit > a.ns_c ? ncomp : nslots);
+  } else {            // a part of the window slots
+    slot_lo = ncomp + (int64_t)(sp - a.ns_c) * a.s_w;
+    slot_hi = min(slot_lo + a.s_w, nslots);
+  }
   const double tpos = (double)t;
   const int dbase = wave * DW;
   const uint16_t* dummy = a.win + (int64_t)b * (a.T + a.n_win - 1) * C;  // a finite row for empty slots
@@ -171,7 +181,11 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
                                                             : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
                                                : dummy;
       s_pos2[h * kStage + threadIdx.x] = sl.pos;
-      s_flag2[h * kStage + threadIdx.x] = valid;
+      // raw rows (window tokens, or compressed entries not stored prepared) get RMSNorm and RoPE here
+      const bool raw = valid && (sl.is_win || !a.prepared);
+      s_flag2[h * kStage + threadIdx.x] = valid ? (raw ? 3 : 1) : 0;
+      const uint64_t rm = __ballot(raw);  // threads < kStage are exactly wave 0
+      if (threadIdx.x == 0) s_raw2[h] = rm != 0;
     }
   };
   resolve_stage(slot_lo, 0);
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
       const int d0 = dbase + 32 * ks + 8 * g;
-      if (d0 >= rope_lo || a.gamma_q || a.gamma_kv) {
+      if (d0 >= rope_lo || a.gamma_q || (a.gamma_kv && !a.prepared)) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) { x[2 * j] = bf(raw[ks][j], 0); x[2 * j + 1] = bf(raw[ks][j], 1); }
@@ -225,7 +239,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
             x[2 * p] = x0 * cs - x1 * sn;
             x[2 * p + 1] = x0 * sn + x1 * cs;
           }
-        } else if (a.gamma_kv) {
+        } else if (a.gamma_kv && !a.prepared) {  // raw entries' gain on the non-RoPE dims, moved to q
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] *= a.gamma_kv[d0 + j];
         }
@@ -258,59 +272,72 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
                                        s_rq[48 + (lane & 15)]) / (float)C + a.eps);
     }
-    // ---- (3a) per-entry RMS scalar: 8 lanes per entry, two accumulators
+    if (s_raw2[half]) {
+      // ---- (3a) per-entry RMS scalar of the raw rows: 8 lanes per entry, two accumulators
+      // (prepared entries are already normalised: scalar 1)
 #pragma unroll 1
-    for (int rd = 0; rd < kStage / 32; ++rd) {
-      const int e = 32 * rd + (threadIdx.x >> 3);
-      const int sub = threadIdx.x & 7;
-      const uint16_t* er = E + e * C;
-      float ss0 = 0.0f, ss1 = 0.0f;
+      for (int rd = 0; rd < kStage / 32; ++rd) {
+        const int e = 32 * rd + (threadIdx.x >> 3);
+        const int sub = threadIdx.x & 7;
+        const int fl = s_flag[e];
+        const uint16_t* er = E + e * C;
+        float ss0 = 0.0f, ss1 = 0.0f;
+        if (fl & 2) {
 #pragma unroll
-      for (int j = 0; j < NCR / 8; ++j) {
-        const u32x4 w4 = *reinterpret_cast<const u32x4*>(er + 8 * swz<C>(e, sub + 8 * j));
-        ss0 = sumsq_bf16x2(w4[0], ss0);
-        ss1 = sumsq_bf16x2(w4[1], ss1);
-        ss0 = sumsq_bf16x2(w4[2], ss0);
-        ss1 = sumsq_bf16x2(w4[3], ss1);
+          for (int j = 0; j < NCR / 8; ++j) {
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(er + 8 * swz<C>(e, sub + 8 * j));
+            ss0 = sumsq_bf16x2(w4[0], ss0);
+            ss1 = sumsq_bf16x2(w4[1], ss1);
+            ss0 = sumsq_bf16x2(w4[2], ss0);
+            ss1 = sumsq_bf16x2(w4[3], ss1);
+          }
+        }
+        float ss = ss0 + ss1;
+        ss += __shfl_xor(ss, 1, 64);
+        ss += __shfl_xor(ss, 2, 64);
+        ss += __shfl_xor(ss, 4, 64);
+        if (sub == 0) s_re[e] = (fl & 2) ? 1.0f / sqrtf(ss / (float)C + a.eps) : (fl ? 1.0f : 0.0f);
       }
-      float ss = ss0 + ss1;
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
-      ss += __shfl_xor(ss, 4, 64);
-      if (sub == 0) s_re[e] = s_flag[e] ? 1.0f / sqrtf(ss / (float)C + a.eps) : 0.0f;
-    }
-    // ---- (3b) RoPE (and gain) of the RoPE dims, in place: items (entry, 4-pair chunk), four
-    // independent rotations per item so that their dependent sin/cos chains overlap
-    {
-      const int nrc = a.R / 8;  // RoPE chunks per entry
+      // ---- (3b) RoPE (and gain) of the raw rows, in place: items (entry, 4-pair chunk), four
+      // independent rotations per item so that their dependent sin/cos chains overlap.  With prepared
+      // compressed entries the raw (window) rows also take the gain on their non-RoPE dims here.
+      {
+        const bool all_dims = a.prepared && a.gamma_kv;
+        const int c_lo = all_dims ? 0 : (rope_lo >> 3);
+        const int nrc = NCR - c_lo;  // chunks per entry
 #pragma unroll 1
-      for (int it = threadIdx.x; it < kStage * nrc; it += 256) {
-        const int e = it / nrc;
-        if (!s_flag[e]) continue;
-        const int c = (rope_lo >> 3) + (it - e * nrc);
-        const int d0 = 8 * c;
-        u32x4* cp = reinterpret_cast<u32x4*>(E + e * C + 8 * swz<C>(e, c));
-        u32x4 w4 = *cp;
-        const double pos = s_pos[e];
-        float x[8];
+        for (int it = threadIdx.x; it < kStage * nrc; it += 256) {
+          const int e = it / nrc;
+          if (!(s_flag[e] & 2)) continue;
+          const int c = c_lo + (it - e * nrc);
+          const int d0 = 8 * c;
+          u32x4* cp = reinterpret_cast<u32x4*>(E + e * C + 8 * swz<C>(e, c));
+          u32x4 w4 = *cp;
+          const double pos = s_pos[e];
+          float x[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w4[q], 0); x[2 * q + 1] = bf(w4[q], 1); }
-        if (a.gamma_kv) {
+          for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w4[q], 0); x[2 * q + 1] = bf(w4[q], 1); }
+          if (a.gamma_kv) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+            for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+          }
+          if (d0 >= rope_lo) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              float cs, sn;
+              rope_cs(pos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
+              const float x0 = x[2 * p], x1 = x[2 * p + 1];
+              x[2 * p] = x0 * cs - x1 * sn;
+              x[2 * p + 1] = x0 * sn + x1 * cs;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w4[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+          *cp = w4;
         }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          float cs, sn;
-          rope_cs(pos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
-          const float x0 = x[2 * p], x1 = x[2 * p + 1];
-          x[2 * p] = x0 * cs - x1 * sn;
-          x[2 * p + 1] = x0 * sn + x1 * cs;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w4[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
-        *cp = w4;
       }
+    } else if (threadIdx.x < kStage) {
+      s_re[threadIdx.x] = s_flag[threadIdx.x] ? 1.0f : 0.0f;
     }
     __syncthreads();
     // ---- (4) compute tiles of 32 slots
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
     for (int i = 0; i < 4; ++i) other[i] = __shfl_xor(v[i], 1, 64);  // pair partner: adjacent dim, adjacent lane
     if (d < rope_lo) {
-      if (a.gamma_kv) {
+      if (a.gamma_kv && !a.prepared) {  // raw entries' gain on the non-RoPE dims, applied to the output
         const float gk = a.gamma_kv[d];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= gk;
@@ -453,74 +480,71 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 constexpr int kMaxSplits = 16;
 
 // merge the decode parts of one (row, head): fixed order, sink, gains, -t rotation
+// One workgroup per (query row, head); thread t owns dims [4t, 4t + 4) (C <= 512).  Every load (the
+// parts' maxima / denominators and their partial outputs) is issued before any use.
 __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, RopeTable rt) {
   const int row = blockIdx.x;
   const int h = blockIdx.y;
   const int b = row / a.T;
   const int r = row - b * a.T;
-  const double tpos = (double)(a.pos0[b] + r);
   const int64_t base = ((int64_t)row * a.nsplit) * a.H + h;
   const int ns = a.nsplit;
+  const int d0 = 4 * threadIdx.x;
+  const bool active = d0 < C;
+  const int dl = active ? d0 : 0;  // loads stay in the head's row
+  f32x4 os[kMaxSplits];
   float ms[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < ns) {
+      os[s] = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
       ms[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2];
       ls[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1];
     }
   }
+  const double tpos = (double)(a.pos0[b] + r);
   const float zs = kLog2e * a.sink[h];  // the parts' maxima are in base-2 units
   float Mx = zs;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < ns) Mx = fmaxf(Mx, ms[s]);
   float Lt = __builtin_amdgcn_exp2f(zs - Mx);
-  float fs[kMaxSplits];
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
-    fs[s] = 0.0f;
-    if (s < ns && ms[s] != -INFINITY) {
-      fs[s] = __builtin_amdgcn_exp2f(ms[s] - Mx);
-      Lt = fmaf(ls[s], fs[s], Lt);
+    if (s < ns && ms[s] != -INFINITY) {  // fixed order over the parts
+      const float f = __builtin_amdgcn_exp2f(ms[s] - Mx);
+      Lt = fmaf(ls[s], f, Lt);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaf(os[s][i], f, v[i]);
     }
   }
+  if (!active) return;
   const int rope_lo = C - a.R;
-  for (int d0 = 4 * threadIdx.x; d0 < C; d0 += 4 * blockDim.x) {
-    f32x4 os[kMaxSplits];
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-      if (s < ns) os[s] = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + d0);
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) v[i] = v[i] / Lt;
+  if (d0 < rope_lo) {
+    if (a.gamma_kv && !a.prepared)
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-      if (s < ns && fs[s] != 0.0f)
+      for (int i = 0; i < 4; ++i) v[i] *= a.gamma_kv[d0 + i];
+  } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = fmaf(os[s][i], fs[s], v[i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = v[i] / Lt;
-    if (d0 < rope_lo) {
-      if (a.gamma_kv)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] *= a.gamma_kv[d0 + i];
-    } else {
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        float cs, sn;
-        rope_cs(-tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
-        const float x0 = v[2 * p], x1 = v[2 * p + 1];
-        v[2 * p] = x0 * cs - x1 * sn;
-        v[2 * p + 1] = x0 * sn + x1 * cs;
-      }
+    for (int p = 0; p < 2; ++p) {
+      float cs, sn;
+      rope_cs(-tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+      const float x0 = v[2 * p], x1 = v[2 * p + 1];
+      v[2 * p] = x0 * cs - x1 * sn;
+      v[2 * p + 1] = x0 * sn + x1 * cs;
     }
-    const int64_t o = ((int64_t)row * a.H + h) * C + d0;
-    if (a.out_t == CSA_F32) {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
-    } else {
-      uint2 pk;
-      pk.x = pack_bf16x2(v[0], v[1]);
-      pk.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = pk;
-    }
+  }
+  const int64_t o = ((int64_t)row * a.H + h) * C + d0;
+  if (a.out_t == CSA_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(v[0], v[1]);
+    pk.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + o) = pk;
   }
 }
 
@@ -535,7 +559,7 @@ struct AttnArgsF32 {
   const float* gamma_kv;
   const int64_t* pos0;
   void* out;
-  int T, H, C, R, k, n_win, m, out_t, mode, hg;
+  int T, H, C, R, k, n_win, m, out_t, mode, hg, prepared;
   int64_t n_max;
   float scale, eps;
 };
@@ -609,12 +633,16 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgsF32 a, RopeTabl
     const float* src = is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + erow) * C
                               : a.comp + ((int64_t)b * a.n_max + erow) * C;
     float x[kF32MaxDPL];
-    float ss = 0.f;
-    for (int j = 0; j < dpl; ++j) { x[j] = src[d0 + j]; ss = fmaf(x[j], x[j], ss); }
-    ss = wave_sum(ss);
-    const float rn = 1.0f / sqrtf(ss / (float)C + a.eps);
-    for (int j = 0; j < dpl; ++j) x[j] = x[j] * rn * (a.gamma_kv ? a.gamma_kv[d0 + j] : 1.0f);
-    rope_lane(x, dpl, d0, rope_lo, pos, rt);
+    if (!is_win && a.prepared) {  // stored prepared: used as it is
+      for (int j = 0; j < dpl; ++j) x[j] = src[d0 + j];
+    } else {
+      float ss = 0.f;
+      for (int j = 0; j < dpl; ++j) { x[j] = src[d0 + j]; ss = fmaf(x[j], x[j], ss); }
+      ss = wave_sum(ss);
+      const float rn = 1.0f / sqrtf(ss / (float)C + a.eps);
+      for (int j = 0; j < dpl; ++j) x[j] = x[j] * rn * (a.gamma_kv ? a.gamma_kv[d0 + j] : 1.0f);
+      rope_lane(x, dpl, d0, rope_lo, pos, rt);
+    }
     for (int hh = 0; hh < nh; ++hh) {
       float d = 0.f;
       for (int j = 0; j < dpl; ++j) d = fmaf(sq[hh * C + d0 + j], x[j], d);
@@ -669,31 +697,36 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgsF32 a, RopeTabl
   }
 }
 
-RopeTable make_rope(int R, float base) {
-  RopeTable rt;
-  for (int i = 0; i < 64; ++i) rt.theta[i] = (2 * i < R) ? pow((double)base, -(double)(2 * i) / (double)R) : 0.0;
-  return rt;
+// Decode (T = 1) splits each query's slot list into parts whose boundaries depend only on the list
+// lengths: the compressed slots into at most kMaxSplits - 4 parts of at least 128 slots, the window
+// slots into at most 4 parts of at least 64 (multiples of the 32-slot tile).  Window rows are always
+// normalised and rotated in the kernel, so keeping them apart keeps the parts of similar cost when
+// the compressed entries are stored prepared.  Prefill queries are served by one part each.
+struct SplitLayout {
+  int nsplit, ns_c, s_c, s_w;
+};
+SplitLayout split_layout(int T, int64_t ncomp, int64_t n_win) {
+  if (T != 1) return SplitLayout{1, 1, (int)(ncomp + n_win), 0};
+  auto len = [](int64_t n, int parts, int minimum) -> int64_t {
+    int64_t l = (n + parts - 1) / parts;
+    l = ((l + kTile - 1) / kTile) * kTile;
+    return l < minimum ? minimum : l;
+  };
+  const int64_t sw = len(n_win, 4, 64);
+  const int nsw = ceil_div(n_win, sw);
+  const int64_t sc = len(ncomp, kMaxSplits - 4, kSplitSlots);
+  const int nsc = ncomp > 0 ? ceil_div(ncomp, sc) : 0;
+  return SplitLayout{nsc + nsw, nsc, (int)sc, (int)sw};
 }
-
-// Decode (T = 1) splits each query's slot list into at most kMaxSplits parts of a
-// fixed length that depends only on the list length (multiples of the 32-slot
-// tile, at least 128); prefill queries are served by one part each.
-int split_slots(int T, int64_t nslots) {
-  if (T != 1) return (int)nslots;
-  int64_t len = (nslots + kMaxSplits - 1) / kMaxSplits;
-  len = ((len + kTile - 1) / kTile) * kTile;
-  return (int)(len < kSplitSlots ? kSplitSlots : len);
-}
-int decode_splits(int T, int64_t nslots) { return T == 1 ? ceil_div(nslots, split_slots(T, nslots)) : 1; }
 
 template <int C>
 size_t bf16_lds_bytes() {
   return (size_t)kStage * C * 2 + 4 * 2 * 64 * 16 + kStage * 4 + 64 * 4 + 64 * 8 + 2 * kStage * 8 + 2 * kStage * 8 +
-         2 * kStage * 4;
+         2 * kStage * 4 + 2 * 4;
 }
 
 template <int C>
-csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, int slots, hipStream_t stream) {
+csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
   const size_t lds = bf16_lds_bytes<C>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -707,16 +740,16 @@ csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, int slo
   const int nx = a.nsplit * rows;
   const int nx_pad = (nx + 7) & ~7;
   dim3 grid(nx_pad, a.H / 16);
-  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt, slots, nx);
+  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt, nx);
   if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 
 }  // namespace
 
-size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t list_len) {
+size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win) {
   (void)mode;
-  const int ns = decode_splits(T, list_len);
+  const int ns = split_layout(T, ncomp, n_win).nsplit;
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * T;
   const size_t o = rows * ns * H * (size_t)c * 4;
@@ -726,16 +759,16 @@ size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t list
 csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
-                         float scale, float eps, float rope_base, int kv_t, void* out, int out_t, void* ws,
-                         hipStream_t stream) {
-  const RopeTable rt = make_rope(rope_dims, rope_base);
+                         float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,
+                         void* ws, hipStream_t stream) {
+  const RopeTable rt = make_rope_table(rope_dims, rope_base);
   const int rows = B * T;
   if (kv_t == CSA_F32) {
     AttnArgsF32 a;
     a.q = (const float*)q; a.comp = (const float*)comp_kv; a.idx = idx; a.win = (const float*)win_kv;
     a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
     a.T = T; a.H = H; a.C = c; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t;
-    a.mode = mode; a.n_max = n_max; a.scale = scale; a.eps = eps;
+    a.mode = mode; a.n_max = n_max; a.scale = scale; a.eps = eps; a.prepared = kv_prepared;
     a.hg = 4096 / c;  // heads per workgroup: hg * (c / 64) <= 64 accumulators per lane
     if (a.hg > 32) a.hg = 32;
     size_t lds = (size_t)a.hg * c * 4 + (size_t)a.hg * (c + 2) * 4;
@@ -747,9 +780,12 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
   a.q = (const uint16_t*)q; a.comp = (const uint16_t*)comp_kv; a.idx = idx; a.win = (const uint16_t*)win_kv;
   a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
   a.T = T; a.H = H; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t; a.mode = mode;
-  a.n_max = n_max; a.scale = scale; a.eps = eps;
-  const int64_t nslots = (mode == 0 ? (int64_t)k : n_max) + n_win;
-  a.nsplit = decode_splits(T, nslots);
+  a.n_max = n_max; a.scale = scale; a.eps = eps; a.prepared = kv_prepared;
+  const SplitLayout lay = split_layout(T, mode == 0 ? (int64_t)k : n_max, n_win);
+  a.nsplit = lay.nsplit;
+  a.ns_c = lay.ns_c;
+  a.s_c = lay.s_c;
+  a.s_w = lay.s_w;
   if (a.nsplit > 1) {
     const size_t o = (size_t)rows * a.nsplit * H * (size_t)c * 4;
     a.ws_o = static_cast<float*>(ws);
@@ -758,11 +794,10 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
   }
-  const int slots = split_slots(T, nslots);
   switch (c) {
-    case 128: return launch_bf16<128>(a, rt, rows, slots, stream);
-    case 256: return launch_bf16<256>(a, rt, rows, slots, stream);
-    case 512: return launch_bf16<512>(a, rt, rows, slots, stream);
+    case 128: return launch_bf16<128>(a, rt, rows, stream);
+    case 256: return launch_bf16<256>(a, rt, rows, stream);
+    case 512: return launch_bf16<512>(a, rt, rows, stream);
     default: return CSA_ERR_UNSUPPORTED;
   }
 }

@@ -74,9 +74,14 @@ struct Job {
   void* out_scale;
   int out_t;
   int64_t out_bstride;
+  int prep;            // store the entry prepared for attention (RMSNorm + RoPE at m * i)
+  const float* gamma;
+  float eps;
+  int R;
 };
 struct Jobs {
   Job j[2];
+  double theta[2][64];  // RoPE frequencies of each job
 };
 
 template <typename TIn>
@@ -97,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
   void* __restrict__ out_scale = jb.out_scale;
   const int out_t = jb.out_t;
   const int64_t out_bstride = jb.out_bstride;
+  const double* theta = jobs.theta[blockIdx.z];
   const int e = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -165,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
     for (int q = 0; q < 4; ++q) y[q] = A[q] / L[q];
   }
 
+  if (jb.prep) prep_row4<kThreads>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
   const int64_t orow = (int64_t)b * out_bstride + e;
   if (out_t == CSA_F32) {
     if (writer) *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
@@ -223,22 +230,81 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
 csa_status launch_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
                            const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos,
                            int64_t first_entry, int num_entries, int in_t, void* out, void* out_scale, int out_t,
-                           int64_t out_bstride, hipStream_t stream) {
-  CompressJob j{ca, cb, za, zb, bias_a, bias_b, c, out, out_scale, out_t, out_bstride};
+                           int64_t out_bstride, const csa_kv_prep* prep, hipStream_t stream) {
+  CompressJob j{ca, cb, za, zb, bias_a, bias_b, c, out, out_scale, out_t, out_bstride, prep};
   return launch_compress_jobs(&j, 1, B, rows, m, row0_pos, first_entry, num_entries, in_t, stream);
 }
 
 csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
                                 int64_t first_entry, int num_entries, int in_t, hipStream_t stream) {
   Jobs js;
-  for (int i = 0; i < njobs; ++i)
+  for (int i = 0; i < njobs; ++i) {
+    const csa_kv_prep* pp = jobs[i].prep;
     js.j[i] = Job{jobs[i].ca, jobs[i].cb, jobs[i].za, jobs[i].zb, jobs[i].bias_a, jobs[i].bias_b, jobs[i].c,
-                  jobs[i].out, jobs[i].out_scale, jobs[i].out_t, jobs[i].out_bstride};
+                  jobs[i].out, jobs[i].out_scale, jobs[i].out_t, jobs[i].out_bstride, pp ? 1 : 0,
+                  pp ? pp->gamma : nullptr, pp ? pp->eps : 0.0f, pp ? pp->rope_dims : 0};
+    const RopeTable rt = make_rope_table(pp ? pp->rope_dims : 0, pp ? pp->rope_base : 1.0f);
+    for (int t = 0; t < 64; ++t) js.theta[i][t] = rt.theta[t];
+  }
   dim3 grid(num_entries, B, njobs);
   if (in_t == CSA_F32)
     hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos, first_entry);
   else
     hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos,
                        first_entry);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+namespace {
+
+// csa_prepare_kv: one workgroup per (row, sequence); thread t < c/4 owns channels [4t, 4t + 4).
+template <typename TIn>
+__global__ __launch_bounds__(kThreads) void prepare_kernel(const TIn* __restrict__ in, int64_t in_bstride,
+                                                           void* __restrict__ out, int64_t out_bstride, int c,
+                                                           int out_t, const int64_t* __restrict__ pos_base,
+                                                           int64_t pos_first, int64_t pos_stride,
+                                                           const float* __restrict__ gamma, float eps, int R,
+                                                           RopeTable rt) {
+  __shared__ float s_red[kThreads / 64];
+  const int j = blockIdx.x;
+  const int b = blockIdx.y;
+  const int cg = threadIdx.x;
+  const bool holder = cg < (c >> 2);
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  if (holder) {
+    Raw4<TIn> v;
+    v.load(in + ((int64_t)b * in_bstride + j) * c + 4 * cg);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = v.get(q);
+  }
+  const int64_t pos = (pos_base ? pos_base[b] : 0) + pos_first + (int64_t)j * pos_stride;
+  prep_row4<kThreads>(y, holder, cg, c, (double)pos, gamma, eps, R, rt.theta, s_red);
+  if (!holder) return;
+  const int64_t o = ((int64_t)b * out_bstride + j) * c + 4 * cg;
+  if (out_t == CSA_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + o) = f32x4{y[0], y[1], y[2], y[3]};
+  } else {
+    uint2 pk;
+    pk.x = pack_bf16x2(y[0], y[1]);
+    pk.y = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = pk;
+  }
+}
+
+}  // namespace
+
+csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, int64_t out_bstride, int B, int rows,
+                             int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
+                             int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream) {
+  const RopeTable rt = make_rope_table(prep->rope_dims, prep->rope_base);
+  dim3 grid(rows, B);
+  if (in_t == CSA_F32)
+    hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)in, in_bstride, out,
+                       out_bstride, c, out_t, pos_base, pos_first, pos_stride, prep->gamma, prep->eps,
+                       prep->rope_dims, rt);
+  else
+    hipLaunchKernelGGL(prepare_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)in, in_bstride,
+                       out, out_bstride, c, out_t, pos_base, pos_first, pos_stride, prep->gamma, prep->eps,
+                       prep->rope_dims, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

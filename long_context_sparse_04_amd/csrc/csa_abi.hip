@@ -22,7 +22,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 1; }
+int csa_abi_version(void) { return 2; }
 
 }  // extern "C"
 
@@ -31,8 +31,12 @@ namespace {
 csa_status check_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
                           const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
                           int num_entries, int in_t, void* out, void* out_scale, int out_t,
-                          int64_t& out_batch_stride, bool& empty) {
+                          int64_t& out_batch_stride, const csa_kv_prep* prep, bool& empty) {
   empty = false;
+  if (prep && (out_t != CSA_F32 && out_t != CSA_BF16)) return CSA_ERR_UNSUPPORTED;
+  if (prep && (prep->rope_dims < 0 || (prep->rope_dims % 8) || prep->rope_dims > c || prep->rope_dims > 128))
+    return CSA_ERR_UNSUPPORTED;
+  if (prep && !(prep->eps >= 0.0f)) return CSA_ERR_SHAPE;
   if (B < 0 || rows < 0 || num_entries < 0 || m < 1 || m > 1024 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
   if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (out_t < CSA_F32 || out_t > CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
@@ -62,32 +66,52 @@ extern "C" {
 csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
                         const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos, int64_t first_entry,
                         int num_entries, int in_t, void* out, void* out_scale, int out_t, int64_t out_batch_stride,
-                        void* stream) {
+                        const csa_kv_prep* prep, void* stream) {
   bool empty;
   const csa_status st = check_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry,
-                                       num_entries, in_t, out, out_scale, out_t, out_batch_stride, empty);
+                                       num_entries, in_t, out, out_scale, out_t, out_batch_stride, prep, empty);
   if (st != CSA_OK || empty) return st;
   return launch_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry, num_entries, in_t, out,
-                         out_scale, out_t, out_batch_stride, (hipStream_t)stream);
+                         out_scale, out_t, out_batch_stride, prep, (hipStream_t)stream);
 }
 
 csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, const void* zb0,
                              const float* bias_a0, const float* bias_b0, int c0, void* out0, void* out_scale0,
-                             int out_t0, int64_t out_batch_stride0, const void* ca1, const void* cb1,
-                             const void* za1, const void* zb1, const float* bias_a1, const float* bias_b1, int c1,
-                             void* out1, void* out_scale1, int out_t1, int64_t out_batch_stride1, int B, int rows,
-                             int m, int64_t row0_pos, int64_t first_entry, int num_entries, int in_t, void* stream) {
+                             int out_t0, int64_t out_batch_stride0, const csa_kv_prep* prep0, const void* ca1,
+                             const void* cb1, const void* za1, const void* zb1, const float* bias_a1,
+                             const float* bias_b1, int c1, void* out1, void* out_scale1, int out_t1,
+                             int64_t out_batch_stride1, const csa_kv_prep* prep1, int B, int rows, int m,
+                             int64_t row0_pos, int64_t first_entry, int num_entries, int in_t, void* stream) {
   bool e0, e1;
   csa_status st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry,
-                                 num_entries, in_t, out0, out_scale0, out_t0, out_batch_stride0, e0);
+                                 num_entries, in_t, out0, out_scale0, out_t0, out_batch_stride0, prep0, e0);
   if (st != CSA_OK) return st;
   st = check_compress(ca1, cb1, za1, zb1, bias_a1, bias_b1, B, rows, c1, m, row0_pos, first_entry, num_entries, in_t,
-                      out1, out_scale1, out_t1, out_batch_stride1, e1);
+                      out1, out_scale1, out_t1, out_batch_stride1, prep1, e1);
   if (st != CSA_OK || e0) return st;  // both problems share B and num_entries, so both are empty or neither
   const CompressJob jobs[2] = {
-      {ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, out_scale0, out_t0, out_batch_stride0},
-      {ca1, cb1, za1, zb1, bias_a1, bias_b1, c1, out1, out_scale1, out_t1, out_batch_stride1}};
+      {ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, out_scale0, out_t0, out_batch_stride0, prep0},
+      {ca1, cb1, za1, zb1, bias_a1, bias_b1, c1, out1, out_scale1, out_t1, out_batch_stride1, prep1}};
   return launch_compress_jobs(jobs, 2, B, rows, m, row0_pos, first_entry, num_entries, in_t, (hipStream_t)stream);
+}
+
+csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, int64_t out_batch_stride, int B,
+                          int rows, int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
+                          int64_t pos_stride, const csa_kv_prep* prep, void* stream) {
+  if (B < 0 || rows < 0 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
+  if ((in_t != CSA_F32 && in_t != CSA_BF16) || (out_t != CSA_F32 && out_t != CSA_BF16)) return CSA_ERR_UNSUPPORTED;
+  if (!prep) return CSA_ERR_NULL;
+  if (prep->rope_dims < 0 || (prep->rope_dims % 8) || prep->rope_dims > c || prep->rope_dims > 128)
+    return CSA_ERR_UNSUPPORTED;
+  if (!(prep->eps >= 0.0f)) return CSA_ERR_SHAPE;
+  if (B == 0 || rows == 0) return CSA_OK;
+  if (!in || !out) return CSA_ERR_NULL;
+  if (in_batch_stride < rows || out_batch_stride < rows) return CSA_ERR_SHAPE;
+  if (rows >= 2147483647 || B >= 65536) return CSA_ERR_UNSUPPORTED;
+  // in place only with the same element type and the same layout
+  if (in == out && (in_t != out_t || in_batch_stride != out_batch_stride)) return CSA_ERR_SHAPE;
+  return launch_prepare_kv(in, in_batch_stride, out, out_batch_stride, B, rows, c, in_t, out_t, pos_base, pos_first,
+                           pos_stride, prep, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -165,13 +189,14 @@ static csa_status check_attend(int kv_t, int out_t, int B, int T, int H, int c, 
 
 size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win) {
   if (B <= 0 || T <= 0 || H <= 0 || c <= 0 || k <= 0 || n_win <= 0) return 0;
-  return attend_workspace_bytes(0, B, T, H, c, (int64_t)k + n_win);
+  return attend_workspace_bytes(0, B, T, H, c, (int64_t)k, n_win);
 }
 
 csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv, const float* sink,
                       const float* gamma_q, const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int k,
                       int n_win, int64_t n_max, const int64_t* pos0, int m, float scale, float eps, float rope_base,
-                      int kv_t, void* out, int out_t, void* workspace, size_t ws_bytes, void* stream) {
+                      int kv_t, int kv_prepared, void* out, int out_t, void* workspace, size_t ws_bytes,
+                      void* stream) {
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m);
   if (st != CSA_OK) return st;
   if (k < 1 || k > 2048 || n_max < 0 || n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
@@ -180,17 +205,19 @@ csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, co
   const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   return launch_attend(0, q, comp_kv, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, k, n_win, n_max,
-                       pos0, m, scale, eps, rope_base, kv_t, out, out_t, workspace, (hipStream_t)stream);
+                       pos0, m, scale, eps, rope_base, kv_t, kv_prepared ? 1 : 0, out, out_t, workspace,
+                       (hipStream_t)stream);
 }
 
 size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win) {
   if (B <= 0 || T <= 0 || H <= 0 || c <= 0 || n_max < 0 || n_win <= 0) return 0;
-  return attend_workspace_bytes(1, B, T, H, c, n_max + n_win);
+  return attend_workspace_bytes(1, B, T, H, c, n_max, n_win);
 }
 
 csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv, const float* sink, const float* gamma_q,
                       const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
-                      const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t, void* out,
+                      const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t,
+                      int kv_prepared, void* out,
                       int out_t, void* workspace, size_t ws_bytes, void* stream) {
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m_hca);
   if (st != CSA_OK) return st;
@@ -200,7 +227,8 @@ csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv, co
   const size_t need = hca_attend_workspace_bytes(B, T, H, c, n_max, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   return launch_attend(1, q, comp_kv, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, 1, n_win,
-                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, out, out_t, workspace, (hipStream_t)stream);
+                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared ? 1 : 0, out, out_t, workspace,
+                       (hipStream_t)stream);
 }
 
 }  // extern "C"

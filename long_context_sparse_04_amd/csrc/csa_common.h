@@ -115,7 +115,8 @@ struct RopeTable {
 // quadrant in double precision (Cody-Waite style, pi/2 split into two doubles), so
 // positions near 2^20 keep float32-level accuracy; sin and cos of the reduced
 // argument are their Taylor series through x^9 / x^10 (truncation < 2e-9 on
-// [-pi/4, pi/4]), evaluated in float32 by Horner's rule.
+// [-pi/4, pi/4]), evaluated in float32 by Horner's rule.  |pos * theta| < 2^31 * pi/2
+// (positions below 2^31 with theta <= 1).
 CSA_DEV void rope_cs(double pos, double theta, float& c, float& s) {
   const double pio2_hi = 1.5707963267948966;     // nearest double to pi/2
   const double pio2_lo = 6.123233995736766e-17;  // pi/2 - pio2_hi
@@ -128,12 +129,50 @@ CSA_DEV void rope_cs(double pos, double theta, float& c, float& s) {
                                      -1.0f / 6.0f), x);
   const float cp = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f),
                                                    -1.0f / 720.0f), 1.0f / 24.0f), -0.5f), 1.0f);
-  switch ((int)((long long)kq & 3)) {  // angle = red + q * pi/2
-    case 0: s = sp; c = cp; break;
-    case 1: s = cp; c = -sp; break;
-    case 2: s = -sp; c = -cp; break;
-    default: s = -cp; c = sp; break;
+  // angle = red + q * pi/2: odd quadrants swap sin and cos; the signs follow the quadrant
+  const int q = (int)kq & 3;
+  const float s1 = (q & 1) ? cp : sp, c1 = (q & 1) ? sp : cp;
+  s = (q & 2) ? -s1 : s1;
+  c = ((q + 1) & 2) ? -c1 : c1;
+}
+
+// RMSNorm (gain gamma, epsilon eps) and then RoPE at position pos of one c-dim row held 4 channels
+// per thread: thread t < c/4 (the holder) owns channels [4t, 4t + 4) in y.  Every thread of the
+// NT-thread block calls it (it holds two barriers); s_red has room for NT/64 floats.
+template <int NT>
+CSA_DEV void prep_row4(float* y, bool holder, int cg, int c, double pos, const float* gamma, float eps, int R,
+                       const double* theta, float* s_red) {
+  float ss = holder ? fmaf(y[0], y[0], fmaf(y[1], y[1], fmaf(y[2], y[2], y[3] * y[3]))) : 0.0f;
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) tot += s_red[w];
+  __syncthreads();  // s_red is free again for the caller
+  if (!holder) return;
+  const float rn = 1.0f / sqrtf(tot / (float)c + eps);
+  const int d = 4 * cg;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) y[q] = gamma ? y[q] * rn * gamma[d + q] : y[q] * rn;
+  const int rope_lo = c - R;
+  if (d >= rope_lo) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float cs, sn;
+      rope_cs(pos, theta[(d + 2 * p - rope_lo) / 2], cs, sn);
+      const float x0 = y[2 * p], x1 = y[2 * p + 1];
+      y[2 * p] = x0 * cs - x1 * sn;
+      y[2 * p + 1] = x0 * sn + x1 * cs;
+    }
   }
+}
+
+// theta_i = rope_base^(-2i/R), i < R/2 <= 64, in double on the host
+static inline RopeTable make_rope_table(int R, float base) {
+  RopeTable rt;
+  for (int i = 0; i < 64; ++i) rt.theta[i] = (2 * i < R) ? pow((double)base, -(double)(2 * i) / (double)R) : 0.0;
+  return rt;
 }
 
 // ---------------------------------------------------------------- misc

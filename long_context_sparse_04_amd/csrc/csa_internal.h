@@ -10,7 +10,7 @@
 csa_status launch_compress(const void* ca, const void* cb, const void* za, const void* zb, const float* bias_a,
                            const float* bias_b, int B, int rows, int c, int m, int64_t row0_pos,
                            int64_t first_entry, int num_entries, int in_t, void* out, void* out_scale, int out_t,
-                           int64_t out_bstride, hipStream_t stream);
+                           int64_t out_bstride, const csa_kv_prep* prep, hipStream_t stream);
 
 // one problem of a compression launch (see csa_compress_pair)
 struct CompressJob {
@@ -25,9 +25,14 @@ struct CompressJob {
   void* out_scale;
   int out_t;
   int64_t out_bstride;
+  const csa_kv_prep* prep;  // NULL: store the pooled entry as it is
 };
 csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
                                 int64_t first_entry, int num_entries, int in_t, hipStream_t stream);
+
+csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, int64_t out_bstride, int B, int rows,
+                             int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
+                             int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream);
 
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
@@ -38,9 +43,9 @@ csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const i
                        int32_t* idx, float* vals, void* ws, hipStream_t stream);
 
 // mode 0: CSA (index list), mode 1: HCA (dense range)
-size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t list_len);
+size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win);
 csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
-                         float scale, float eps, float rope_base, int kv_t, void* out, int out_t, void* ws,
-                         hipStream_t stream);
+                         float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,
+                         void* ws, hipStream_t stream);

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -49,12 +49,12 @@ DUMMY = C.c_void_p(0x1000)  # never dereferenced: validation fails before any la
 def test_compress_validation(lib):
     f = lib.csa_compress
     args = dict(ca=DUMMY, cb=DUMMY, za=DUMMY, zb=DUMMY, ba=DUMMY, bb=DUMMY, B=1, rows=8, c=128, m=4, row0=0, first=1,
-                num=1, in_t=1, out=DUMMY, osc=None, out_t=1, stride=0, stream=None)
+                num=1, in_t=1, out=DUMMY, osc=None, out_t=1, stride=0, prep=None, stream=None)
 
     def call(**kw):
         a = {**args, **kw}
         return f(a["ca"], a["cb"], a["za"], a["zb"], a["ba"], a["bb"], a["B"], a["rows"], a["c"], a["m"], a["row0"],
-                 a["first"], a["num"], a["in_t"], a["out"], a["osc"], a["out_t"], a["stride"], a["stream"])
+                 a["first"], a["num"], a["in_t"], a["out"], a["osc"], a["out_t"], a["stride"], a["prep"], a["stream"])
 
     assert call(B=-1) == 2
     assert call(c=130) == 2
@@ -62,6 +62,18 @@ def test_compress_validation(lib):
     assert call(in_t=2) == 3
     assert call(out_t=3, c=100) == 3
     assert call(ca=None) == 1
+    prep = C.byref(_lib.KvPrep(None, 1e-6, 64, 1e4))
+    assert call(prep=prep, out_t=2, osc=DUMMY) == 3        # prepared entries are stored as F32 / BF16 only
+    assert call(prep=C.byref(_lib.KvPrep(None, 1e-6, 60, 1e4))) == 3
+    assert call(prep=C.byref(_lib.KvPrep(None, -1.0, 64, 1e4))) == 2
+    # csa_prepare_kv
+    pk = lib.csa_prepare_kv
+    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 1, 1, None, 0, 4, None, None) == 1
+    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 510, 1, 1, None, 0, 4, prep, None) == 2
+    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 2, 1, None, 0, 4, prep, None) == 3
+    assert pk(DUMMY, 4, DUMMY, 8, 2, 8, 512, 1, 1, None, 0, 4, prep, None) == 2   # batch stride below rows
+    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 1, 0, None, 0, 4, prep, None) == 2   # in place needs one layout
+    assert pk(DUMMY, 8, DUMMY, 8, 0, 8, 512, 1, 1, None, 0, 4, prep, None) == 0
     assert call(cb=None) == 1                     # b-stream must be all or nothing
     assert call(out_t=2, osc=None) == 1           # fp8 needs the scale output
     assert call(first=2) == 2                     # entry 2 needs rows 4..11 but only 0..7 exist
@@ -76,8 +88,8 @@ def test_compress_pair_validation(lib):
     def pair(**kw):
         a = dict(c0=512, c1=128, t0=1, t1=2, os1=P, B=4, rows=8, m=4, r0=1048568, first=262143, n=1, in_t=1)
         a.update(kw)
-        return lib.csa_compress_pair(P, P, P, P, P, P, a["c0"], P, None, a["t0"], 262144,
-                                     P, P, P, P, P, P, a["c1"], P, a["os1"], a["t1"], 262144,
+        return lib.csa_compress_pair(P, P, P, P, P, P, a["c0"], P, None, a["t0"], 262144, None,
+                                     P, P, P, P, P, P, a["c1"], P, a["os1"], a["t1"], 262144, None,
                                      a["B"], a["rows"], a["m"], a["r0"], a["first"], a["n"], a["in_t"], None)
     assert pair(os1=None) == 1          # fp8 output of problem 1 needs its scales
     assert pair(c1=130) == 2
@@ -115,7 +127,7 @@ def test_index_topk_attend_validation(lib):
         a.update(kw)
         return lib.csa_attend(a["q"], a["comp"], a["idx"], a["win"], a["sink"], None, None, a["B"], a["T"], a["H"],
                               a["c"], a["R"], a["k"], a["n_win"], a["N"], a["pos"], a["m"], 0.044, 1e-6, 1e4,
-                              a["kv_t"], a["out"], a["out_t"], a["ws"], a["nb"], None)
+                              a["kv_t"], 0, a["out"], a["out_t"], a["ws"], a["nb"], None)
     assert att() == 4                         # decode needs the split workspace
     assert att(c=192) == 3
     assert att(R=60) == 3

@@ -10,6 +10,10 @@ and every (row, head) of the attention output, on its own index list.
 The chunked-prefill workload (4,096 query rows over a 65,536-token context) is
 checked on sampled query rows that the oracle computes one by one.
 
+As in the benchmark, the compressed caches are stored prepared for attention
+(RMSNorm and RoPE applied once per entry) and read with kv_prepared; the oracle
+takes the raw entries and applies both itself.
+
 Bars: compressed rows equal to the oracle's own bf16 rounding or within half an
 ulp plus float32 summation error; scores within 1e-5 of sum_h |w| |q|.|K| (the natural scale of
 float32 dot-product error); top-k >= 99.9% set agreement with every mismatch
@@ -75,11 +79,21 @@ def _oracle_compress(ci):
     return ref, absref
 
 
-def _gpu_compress(api, ci, out, out_scale=None, fmt=None, stride=None):
+def _gpu_compress(api, ci, out, out_scale=None, fmt=None, stride=None, prep=None):
     d = lambda k: dev(ci[k])
     api.compress(d("ca"), d("cb"), d("za"), d("zb"), d("bias_a"), d("bias_b"), ci["m"], ci["row0_pos"],
                  ci["first_entry"], ci["num_entries"], out=out, out_scale=out_scale, out_fmt=fmt,
-                 out_batch_stride=stride)
+                 out_batch_stride=stride, prep=prep)
+
+
+def _check_prepared_rows(got_bits, ref, pos, cfg):
+    """Entries stored prepared (bf16 of float32 RoPE(RMSNorm(pooled))) against the oracle's preparation of its
+    own float64 entries at their positions (pos: the first row's; rows follow at the cache stride)."""
+    want = oracle.rope(oracle.rmsnorm(ref, None, cfg.eps), pos, cfg.rope_dims, cfg.rope_base)
+    got = oracle.decode_bf16(got_bits)
+    err = np.abs(got - want)
+    assert np.all(err <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.max(np.abs(want))), err.max()
+    assert rel_l2(got, want) <= LOWP_TOL
 
 
 def _check_bf16_rows(got_bits, ref, absref):
@@ -150,30 +164,34 @@ def test_decode_step_full_size(api, name):
     kv_cache = dev(cc["kv"])
     ik = dev(cc["ik"])
     ik_scale = dev(cc["ik_scale"])
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)     # the context cache, stored prepared
     first = N - 1
     d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
-    api.compress_pair(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N),
+    api.compress_pair(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N, prep=prep),
                       dict(d(cik), out=ik[:, first:], out_batch_stride=N, out_fmt=fmt if fmt != "bf16" else None,
                            out_scale=None if ik_scale is None else ik_scale[:, first:]),
                       ckv["m"], ckv["row0_pos"], first, 1)
     scores = api.index(dev(qi["data"]), dev(qi.get("scale")), dev(w), ik, ik_scale, pos, cfg.m, fmt)
     idx, _ = api.topk(scores, pos, cfg.m, cfg.k)
     out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base)
+                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     if cfg.with_hca:
         chca = gen.compress_inputs(cfg, hca=True)
         hq, hwin, hsink = gen.queries(cfg, hca=True), gen.window(cfg, hca=True), gen.sink(cfg, hca=True)
         hca_cache = dev(cc["hca"])
-        _gpu_compress(api, chca, hca_cache[:, chca["first_entry"]:], stride=cfg.n_hca)
+        api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
+        _gpu_compress(api, chca, hca_cache[:, chca["first_entry"]:], stride=cfg.n_hca, prep=prep)
         hout = api.hca_attend(dev(hq), hca_cache, dev(hwin), dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                              cfg.scale, cfg.eps, cfg.rope_base)
+                              cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     torch.cuda.synchronize()
 
     # ---- compression of this step's entries
     say(f"{cfg.name}: oracle compress")
     (r_kv, a_kv), (r_ik, a_ik) = _oracle_compress(ckv), _oracle_compress(cik)
     r_kv, a_kv, r_ik, a_ik = r_kv[:, 0], a_kv[:, 0], r_ik[:, 0], a_ik[:, 0]
-    _check_bf16_rows(kv_cache[:, first].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_kv, a_kv)
+    _check_prepared_rows(kv_cache[:, first].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_kv,
+                         cfg.m * first, cfg)
     g_ik = ik[:, first].contiguous()
     g_ik = g_ik.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16" else g_ik.cpu().numpy()
     g_iks = None if ik_scale is None else ik_scale[:, first].cpu().numpy()
@@ -205,7 +223,7 @@ def test_decode_step_full_size(api, name):
     # ---- attention on the oracle's own list (isolated) and on the GPU's list (end to end)
     say(f"{cfg.name}: oracle attend, {B} rows x {cfg.H} heads")
     out_iso = api.attend(dev(q), kv_cache, dev(r_idx), dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                         cfg.scale, cfg.eps, cfg.rope_base)
+                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     torch.cuda.synchronize()
     r_cache = Bf16Rows(cc["kv"], {(b, first): oracle.decode_bf16(oracle.encode_bf16(r_kv[b])) for b in range(B)})
     r_out = oracle.attend(_f64(q), r_cache, r_idx, _f64(win), sink, pos0, cfg.m, cfg.n_win, cfg.rope_dims,
@@ -221,7 +239,8 @@ def test_decode_step_full_size(api, name):
         r_h, a_h = _oracle_compress(chca)
         r_h, a_h = r_h[:, 0], a_h[:, 0]
         hf = chca["first_entry"]
-        _check_bf16_rows(hca_cache[:, hf].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_h, a_h)
+        _check_prepared_rows(hca_cache[:, hf].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_h,
+                             cfg.m_hca * hf, cfg)
         r_hcache = Bf16Rows(cc["hca"], {(b, hf): oracle.decode_bf16(oracle.encode_bf16(r_h[b])) for b in range(B)})
         r_hout = oracle.hca_attend(_f64(hq), r_hcache, _f64(hwin), hsink, pos0, cfg.m_hca, cfg.n_win, cfg.rope_dims,
                                    cfg.scale, cfg.eps, cfg.rope_base)
@@ -248,24 +267,27 @@ def test_chunked_prefill_full_size_sampled(api):
 
     # ---- the whole chunk on the GPU
     kv_cache, ik, hca_cache = dev(cc["kv"]), dev(cc["ik"]), dev(cc["hca"])
-    _gpu_compress(api, ckv, kv_cache[:, f0:], stride=N)
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)        # context caches, stored prepared
+    api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
+    _gpu_compress(api, ckv, kv_cache[:, f0:], stride=N, prep=prep)
     _gpu_compress(api, cik, ik[:, f0:], stride=N)
-    _gpu_compress(api, chca, hca_cache[:, hf0:], stride=cfg.n_hca)
+    _gpu_compress(api, chca, hca_cache[:, hf0:], stride=cfg.n_hca, prep=prep)
     scores = api.index(dev(qi["data"]), None, dev(w), ik, None, pos, cfg.m, fmt)
     idx, _ = api.topk(scores, pos, cfg.m, cfg.k)
     out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base)
+                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     hout = api.hca_attend(dev(hq), hca_cache, dev(hwin), dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base)
+                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     torch.cuda.synchronize()
 
     # ---- every compressed entry of the chunk
     (r_kv, a_kv), (r_ik, a_ik), (r_h, a_h) = _oracle_compress(ckv), _oracle_compress(cik), _oracle_compress(chca)
     r_kv, a_kv, r_ik, a_ik, r_h, a_h = r_kv[0], a_kv[0], r_ik[0], a_ik[0], r_h[0], a_h[0]
     bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    _check_bf16_rows(bits(kv_cache[0, f0:f0 + nn]), r_kv, a_kv)
+    _check_prepared_rows(bits(kv_cache[0, f0:f0 + nn]), r_kv, cfg.m * (f0 + np.arange(nn)), cfg)
     _check_bf16_rows(bits(ik[0, f0:f0 + nn]), r_ik, a_ik)
-    _check_bf16_rows(bits(hca_cache[0, hf0:hf0 + hn]), r_h, a_h)
+    _check_prepared_rows(bits(hca_cache[0, hf0:hf0 + hn]), r_h, cfg.m_hca * (hf0 + np.arange(hn)), cfg)
 
     # the oracle's caches: generated context rows plus its own bf16-stored chunk entries
     kcache = oracle.decode_bf16(cc["ik"][0])
@@ -302,7 +324,7 @@ def test_chunked_prefill_full_size_sampled(api):
     mixed = gi.copy()
     mixed[0, rows] = r_idx_all[0, rows]
     out_iso = api.attend(dev(q), kv_cache, dev(mixed), dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                         cfg.scale, cfg.eps, cfg.rope_base)
+                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
     torch.cuda.synchronize()
     pairs = [(0, r) for r in rows]
     r_out = oracle.attend(_f64(q), vcache[None], r_idx_all, _f64(win), sink, pos0, cfg.m, cfg.n_win,

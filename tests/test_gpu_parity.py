@@ -290,7 +290,10 @@ def _rand_idx(rng, B, T, k, pos0, m, n_max, fill=0.9):
     return idx
 
 
-def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False):
+def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False, prepared=False):
+    """GPU attention against the oracle on the same raw inputs.  prepared: the GPU cache is first stored
+    prepared (csa_prepare_kv at the entries' positions) and read with kv_prepared; the oracle still takes
+    the raw entries."""
     q = gen.queries(cfg, hca=hca)
     cache = gen.kv_cache(cfg, hca=hca)
     win = gen.window(cfg, hca=hca)
@@ -300,13 +303,19 @@ def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False):
     gq = rng.uniform(0.5, 1.5, cfg.c).astype(np.float32) if gamma else None
     gk = rng.uniform(0.5, 1.5, cfg.c).astype(np.float32) if gamma else None
     say(f"{'hca' if hca else 'csa'}_attend {cfg.name} fmt={fmt} B={cfg.B} T={cfg.T} H={cfg.H} c={cfg.c} "
-        f"N={cache.shape[1]} gamma={gamma}")
+        f"N={cache.shape[1]} gamma={gamma} prepared={prepared}")
+    dcache = dev(cache)
+    if prepared:
+        prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base, gamma=dev(gk))
+        dcache = api.prepare_kv(dcache, prep, pos_stride=cfg.m_hca if hca else cfg.m)
     if hca:
-        out = api.hca_attend(dev(q), dev(cache), dev(win), dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                             cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk))
+        out = api.hca_attend(dev(q), dcache, dev(win), dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, cfg.rope_dims,
+                             cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk),
+                             kv_prepared=prepared)
     else:
-        out = api.attend(dev(q), dev(cache), dev(idx), dev(win), dev(sink), _pos(pos0), cfg.m, cfg.n_win,
-                         cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk))
+        out = api.attend(dev(q), dcache, dev(idx), dev(win), dev(sink), _pos(pos0), cfg.m, cfg.n_win,
+                         cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk),
+                         kv_prepared=prepared)
     torch.cuda.synchronize()
     v = lambda x: oracle.dequant_rows(x, None, fmt)
     if hca:
@@ -318,28 +327,31 @@ def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False):
     return host_f64(out), ref
 
 
-def test_attend_f32_c1(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_attend_f32_c1(api, prepared):
     cfg = configs.C1
     rng = np.random.default_rng(1)
     idx = _rand_idx(rng, 1, cfg.T, cfg.k, [0], cfg.m, cfg.n_comp)
-    got, ref = _attend_case(api, cfg, [0], idx)
+    got, ref = _attend_case(api, cfg, [0], idx, prepared=prepared)
     assert rel_l2(got, ref) <= F32_TOL
 
 
-def test_attend_bf16_decode(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_attend_bf16_decode(api, prepared):
     cfg = configs.C3.scaled(B=2, n_comp=3000)
     pos0 = [4 * 3000, 4 * 2500 + 1]
     idx = _rand_idx(np.random.default_rng(2), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
-    got, ref = _attend_case(api, cfg, pos0, idx)
+    got, ref = _attend_case(api, cfg, pos0, idx, prepared=prepared)
     e = rel_l2(got, ref)
     say(f"  rel-L2 {e:.3e}")
     assert e <= LOWP_TOL
 
 
-def test_attend_bf16_prefill(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_attend_bf16_prefill(api, prepared):
     cfg = configs.C4.scaled(T=40, n_comp=200, pos0=700, k=64)
     idx = _rand_idx(np.random.default_rng(3), 1, cfg.T, cfg.k, [700], cfg.m, cfg.n_comp)
-    got, ref = _attend_case(api, cfg, [700], idx)
+    got, ref = _attend_case(api, cfg, [700], idx, prepared=prepared)
     e = rel_l2(got, ref)
     say(f"  rel-L2 {e:.3e}")
     assert e <= LOWP_TOL
@@ -358,36 +370,83 @@ def test_attend_bf16_flash_heads_and_small_c(api):
     assert rel_l2(got, ref) <= LOWP_TOL
 
 
-def test_attend_gains(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_attend_gains(api, prepared):
     cfg = configs.C2.scaled(B=2, n_comp=500, k=64)
     pos0 = [4 * 500, 4 * 123]
     idx = _rand_idx(np.random.default_rng(7), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
-    got, ref = _attend_case(api, cfg, pos0, idx, gamma=True)
+    got, ref = _attend_case(api, cfg, pos0, idx, gamma=True, prepared=prepared)
+    assert rel_l2(got, ref) <= LOWP_TOL
+    cfg = configs.C4.scaled(T=24, n_comp=300, pos0=900, k=64)          # prefill: one part per query
+    idx = _rand_idx(np.random.default_rng(10), 1, cfg.T, cfg.k, [900], cfg.m, cfg.n_comp)
+    got, ref = _attend_case(api, cfg, [900], idx, gamma=True, prepared=prepared)
     assert rel_l2(got, ref) <= LOWP_TOL
     cfg1 = configs.C1.scaled(T=64, n_comp=16)
     idx = _rand_idx(np.random.default_rng(8), 1, 64, 64, [0], 4, 16)
-    got, ref = _attend_case(api, cfg1, [0], idx, gamma=True)
+    got, ref = _attend_case(api, cfg1, [0], idx, gamma=True, prepared=prepared)
     assert rel_l2(got, ref) <= F32_TOL
 
 
-def test_hca_attend_f32_c1(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_hca_attend_f32_c1(api, prepared):
     cfg = configs.C1
-    got, ref = _attend_case(api, cfg, [0], None, hca=True)
+    got, ref = _attend_case(api, cfg, [0], None, hca=True, prepared=prepared)
     assert rel_l2(got, ref) <= F32_TOL
 
 
-def test_hca_attend_bf16_decode_and_prefill(api):
+@pytest.mark.parametrize("prepared", [False, True])
+def test_hca_attend_bf16_decode_and_prefill(api, prepared):
     cfg = configs.C5.scaled(B=2, n_hca=700)
     pos0 = [128 * 700, 128 * 333 + 5]
-    got, ref = _attend_case(api, cfg, pos0, None, hca=True)
+    got, ref = _attend_case(api, cfg, pos0, None, hca=True, prepared=prepared)
     e = rel_l2(got, ref)
     say(f"  decode rel-L2 {e:.3e}")
     assert e <= LOWP_TOL
     cfg = configs.C4.scaled(T=48, n_hca=40, pos0=128 * 30 + 7)
-    got, ref = _attend_case(api, cfg, [cfg.pos0], None, hca=True)
+    got, ref = _attend_case(api, cfg, [cfg.pos0], None, hca=True, prepared=prepared)
     e = rel_l2(got, ref)
     say(f"  prefill rel-L2 {e:.3e}")
     assert e <= LOWP_TOL
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_prepare_kv_and_prepared_compress(api, fmt):
+    """csa_prepare_kv and csa_compress with a csa_kv_prep against the oracle's RoPE(RMSNorm(x)) of the same
+    rows, at the rows' positions."""
+    base = configs.C1 if fmt == "f32" else configs.C3.scaled(B=3)
+    rng = np.random.default_rng(12)
+    gk = rng.uniform(0.5, 1.5, base.c).astype(np.float32)
+    prep = api.kv_prep(base.rope_dims, base.eps, base.rope_base, gamma=dev(gk))
+    x = gen.window(base)                      # token rows [B][T + n_win - 1][c]
+    pos_base = np.array([1000 + 37 * b for b in range(base.B)], np.int64)
+    say(f"prepare_kv {fmt} rows {x.shape}")
+    got = api.prepare_kv(dev(x), prep, pos_first=5, pos_stride=3, pos_base=_pos(pos_base))
+    xin = dev(x)
+    inplace = api.prepare_kv(xin, prep, pos_first=5, pos_stride=3, pos_base=_pos(pos_base), out=xin)
+    torch.cuda.synchronize()
+    xv = oracle.dequant_rows(x, None, fmt)
+    pos = pos_base[:, None] + 5 + 3 * np.arange(x.shape[1])[None, :]
+    ref = oracle.rope(oracle.rmsnorm(xv, gk, base.eps), pos, base.rope_dims, base.rope_base)
+    g = host_f64(got)
+    tol = 2e-6 if fmt == "f32" else 2.0 ** -8
+    assert np.all(np.abs(g - ref) <= tol * np.abs(ref) + 1e-6 * np.max(np.abs(ref)))
+    assert torch.equal(got.view(torch.int32) if fmt == "f32" else got.view(torch.int16),
+                       inplace.view(torch.int32) if fmt == "f32" else inplace.view(torch.int16))
+    # compression straight into the prepared form (the entry's position is m * i)
+    ci = gen.compress_inputs(base)
+    d = {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    out, _ = api.compress(*d.values(), ci["m"], ci["row0_pos"], ci["first_entry"], ci["num_entries"], prep=prep)
+    torch.cuda.synchronize()
+    f = lambda k: None if ci[k] is None else oracle.dequant_rows(ci[k], None, fmt) if ci[k].dtype == np.uint16 \
+        else np.asarray(ci[k], np.float64)
+    pooled = oracle.compress(f("ca"), f("cb"), f("za"), f("zb"), np.asarray(ci["bias_a"], np.float64),
+                             np.asarray(ci["bias_b"], np.float64), ci["m"], ci["row0_pos"], ci["first_entry"],
+                             ci["num_entries"])
+    epos = ci["m"] * (ci["first_entry"] + np.arange(ci["num_entries"]))
+    ref = oracle.rope(oracle.rmsnorm(pooled, gk, base.eps), epos[None, :], base.rope_dims, base.rope_base)
+    e = rel_l2(host_f64(out), ref)
+    say(f"  prepared compress rel-L2 {e:.3e}")
+    assert e <= (F32_TOL if fmt == "f32" else LOWP_TOL)
 
 
 def test_attend_deterministic_and_batch_invariant(api):
