@@ -374,8 +374,6 @@ def cpu_baseline(cfg, h, host0):
                       f"float64, {dt:.1f} s"}
 
 
-if __name__ == "__main__":
-    main()
 
 
 def cpu_baseline_prefill(cfg, h, host0):
@@ -420,3 +418,7 @@ def cpu_baseline_prefill(cfg, h, host0):
             "sample": f"{done} sampled query rows of the {cfg.T}-row chunk (index, top-k, attend, hca_attend; "
                       f"{t_rows:.1f} s) plus the chunk's compression ({t_comp:.1f} s, amortised over {cfg.T} rows), "
                       f"float64"}
+
+
+if __name__ == "__main__":
+    main()
