@@ -19,19 +19,23 @@ def test_graph_replay_matches_eager():
     kv = dev(gen.kv_cache(cfg))
     q, win, sink = dev(gen.queries(cfg)), dev(gen.window(cfg)), dev(gen.sink(cfg))
     ik, iks, qd, qs, wd = dev(kc["data"]), dev(kc["scale"]), dev(qi["data"]), dev(qi["scale"]), dev(w)
-    ci = {k: (dev(v) if isinstance(v, np.ndarray) else v) for k, v in gen.compress_inputs(cfg, indexer=True).items()}
+    t = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    cik, ckv = t(gen.compress_inputs(cfg, indexer=True)), t(gen.compress_inputs(cfg))
     scores = torch.empty((cfg.B, 1, cfg.n_comp), device=DEV)
     idx = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device=DEV)
     out = torch.empty((cfg.B, 1, cfg.H, cfg.c), dtype=torch.bfloat16, device=DEV)
     first = cfg.n_comp - 1
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    api.prepare_kv(kv, prep, pos_stride=cfg.m, out=kv)
 
-    def step():
-        api.compress(ci["ca"], ci["cb"], ci["za"], ci["zb"], ci["bias_a"], ci["bias_b"], cfg.m, 4 * cfg.n_comp - 8,
-                     first, 1, out=ik[:, first:], out_scale=iks[:, first:], out_fmt="fp8",
-                     out_batch_stride=cfg.n_comp)
+    def step():  # the benchmark's step: one launch for both compressed entries, prepared KV cache
+        api.compress_pair(dict(ckv, out=kv[:, first:], out_batch_stride=cfg.n_comp, prep=prep),
+                          dict(cik, out=ik[:, first:], out_scale=iks[:, first:], out_fmt="fp8",
+                               out_batch_stride=cfg.n_comp), cfg.m, 4 * cfg.n_comp - 8, first, 1)
         api.index(qd, qs, wd, ik, iks, pos, cfg.m, "fp8", scores=scores)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
-        api.attend(q, kv, idx, win, sink, pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, out=out)
+        api.attend(q, kv, idx, win, sink, pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, out=out,
+                   kv_prepared=True)
 
     step()
     torch.cuda.synchronize()
