@@ -211,6 +211,135 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   }
 }
 
+// Prefill (many query rows, bf16): the indexer is a dense contraction
+// [rows x heads] x [c^I x entries].  A workgroup serves kPRows consecutive query
+// rows of one sequence, kPRowsPerWave per wave, each wave holding its rows'
+// HI x 128 queries in registers as MFMA A operands.  Entries stream through LDS
+// in tiles of 64 rows (global_load_lds, double-buffered, 16-byte chunk c of
+// entry e stored at chunk c ^ (e & 15) so that the B-operand reads of 16 entries
+// hit all banks), and every tile is shared by the workgroup's kPRows rows.  The
+// epilogue is the decode kernel's: weighted ReLU head sum per lane, then a
+// reduce-scatter over the 4 lane groups for one coalesced 256-byte store per row
+// and tile.
+constexpr int kPRowsPerWave = 2;
+constexpr int kPRows = kWaves * kPRowsPerWave;  // 8 query rows per workgroup
+constexpr int kPTile = 64;                      // entries per LDS tile
+constexpr int kPRowBytes = 256;                 // bf16 c^I = 128
+constexpr int kPDmaPerWave = kPTile * kPRowBytes / 1024 / kWaves;  // 1 KB per DMA instruction: 4 per wave
+
+template <int NT>
+__global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kI, int T,
+    int64_t n_max, const int64_t* __restrict__ pos0, int m, float* __restrict__ scores) {
+  constexpr int HI = NT * 16;
+  __shared__ __align__(16) uint8_t s_k[2][kPTile * kPRowBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int gl = lane >> 4;
+  const int b = blockIdx.y;
+  const int r_first = blockIdx.x * kPRows;
+  const uint8_t* kb = kI + (int64_t)b * n_max * kPRowBytes;
+
+  // tile DMA: instruction j of wave w fills entries 4 (w + 4 j) .. +3 of the tile; lane i writes chunk
+  // position i % 16 of entry 4 (w + 4 j) + i / 16 and so loads the logical chunk stored there
+  auto issue_tile = [&](int buf, int64_t e_base) {
+#pragma unroll
+    for (int j = 0; j < kPDmaPerWave; ++j) {
+      const int e0 = 4 * (wave + 4 * j);
+      const int e = e0 + (lane >> 4);
+      const int64_t ge = min(e_base + e, n_max - 1);
+      const uint8_t* src = kb + ge * kPRowBytes + 16 * ((lane & 15) ^ (e & 15));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(&s_k[buf][e0 * kPRowBytes]), 16,
+                                       0, 0);
+    }
+  };
+
+  // the rows of this wave: queries (A operands) and per-head weights
+  bf16x8 qa[kPRowsPerWave][NT][4];
+  float wq[kPRowsPerWave][NT][4];
+  int64_t vis[kPRowsPerWave];
+  bool live[kPRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kPRowsPerWave; ++rr) {
+    const int r = r_first + wave * kPRowsPerWave + rr;
+    live[rr] = r < T;
+    const int rc = live[rr] ? r : T - 1;
+    const int64_t row = (int64_t)b * T + rc;
+#pragma unroll
+    for (int g = 0; g < NT; ++g) {
+      const int head = 16 * g + (lane & 15);
+      const i32x4* src = reinterpret_cast<const i32x4*>(q + (row * HI + head) * kPRowBytes + gl * 16);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qa[rr][g][ks] = as_bf16x8(src[4 * ks]);  // dims 32 ks + 8 gl .. +8
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[rr][g][i] = w[row * HI + 16 * g + 4 * gl + i];
+    }
+    vis[rr] = visible_entries(pos0[b] + rc, m, n_max);
+  }
+  // entries up to the largest visibility of the workgroup's rows are computed; the rest are -inf
+  const int r_last = min(r_first + kPRows, T) - 1;
+  const int64_t vis_max = visible_entries(pos0[b] + r_last, m, n_max);
+  const int ntiles = (int)((vis_max + kPTile - 1) / kPTile);
+
+  if (ntiles > 0) issue_tile(0, 0);
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti & 1;
+    if (ti + 1 < ntiles) {
+      issue_tile(buf ^ 1, (int64_t)(ti + 1) * kPTile);
+      // this tile has landed once only the next tile's kPDmaPerWave loads are outstanding (vector memory
+      // operations complete in issue order)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPDmaPerWave) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    const uint8_t* tb = s_k[buf];
+#pragma unroll
+    for (int rr = 0; rr < kPRowsPerWave; ++rr) {
+      float p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // 16-entry sub-tile u: B operands from LDS, then NT x 4 MFMAs
+        const int e = 16 * u + (lane & 15);
+        bf16x8 kbf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kbf[ks] = *reinterpret_cast<const bf16x8*>(tb + e * kPRowBytes + 16 * ((4 * ks + gl) ^ (e & 15)));
+        float part = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NT; ++g) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rr][g][ks], kbf[ks], acc, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = fmaf(wq[rr][g][i], fmaxf(acc[i], 0.0f), part);
+        }
+        p[u] = part;
+      }
+      // reduce-scatter over the 4 lane groups: lane 16u + e ends with the sum for sub-tile u, entry e
+      const bool hi2 = gl >= 2;
+      const float s0 = hi2 ? p[0] : p[2], s1 = hi2 ? p[1] : p[3];
+      const float k0 = (hi2 ? p[2] : p[0]) + __shfl_xor(s0, 32, 64);
+      const float k1 = (hi2 ? p[3] : p[1]) + __shfl_xor(s1, 32, 64);
+      const bool odd = gl & 1;
+      const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
+      const int64_t eo = (int64_t)ti * kPTile + lane;
+      if (live[rr] && eo < n_max) {
+        const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
+        scores[row * n_max + eo] = eo < vis[rr] ? val : -INFINITY;
+      }
+    }
+    __syncthreads();  // the buffer is refilled by the next-but-one tile
+  }
+  // entries past every row's visibility
+#pragma unroll
+  for (int rr = 0; rr < kPRowsPerWave; ++rr) {
+    if (!live[rr]) continue;
+    const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
+    for (int64_t eo = (int64_t)ntiles * kPTile + lane; eo < n_max; eo += 64) scores[row * n_max + eo] = -INFINITY;
+  }
+}
+
 // float32 path: one thread per (query row, entry), FMA over dims then heads.
 constexpr int kF32Threads = 256;
 __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __restrict__ q,
@@ -252,6 +381,12 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
                       int T, int HI, int64_t n_max, const int64_t* pos0, int m, float* scores, hipStream_t stream) {
+  if (FMT == CSA_BF16 && T >= kPRows && HI == 64) {  // many query rows: the tiled contraction
+    dim3 grid(ceil_div(T, kPRows), B);
+    hipLaunchKernelGGL((index_prefill_bf16_kernel<4>), grid, dim3(kWaves * 64), 0, stream, (const uint8_t*)q, w,
+                       (const uint8_t*)k, T, n_max, pos0, m, scores);
+    return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+  }
   dim3 grid(ceil_div(n_max, kEntriesPerWG), B * T);
   dim3 block(kWaves * 64);
 #define CSA_IDX_LAUNCH(NT)                                                                                  \

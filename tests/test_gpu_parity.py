@@ -204,6 +204,15 @@ def test_index_mfma_prefill_rows(api):
     _check_scores(got, ref, absref, 1e-5)
 
 
+@pytest.mark.parametrize("T,n_comp,pos0", [(37, 3001, 4 * 2990 - 20), (16, 700, 2), (64, 4160, 4 * 4100)])
+def test_index_prefill_tiled(api, T, n_comp, pos0):
+    """The tiled many-row bf16 kernel: ragged row blocks, a ragged last entry tile, rows that see no entry,
+    and rows whose visible ranges end inside a tile."""
+    cfg = configs.C4.scaled(T=T, n_comp=n_comp, pos0=pos0)
+    got, ref, absref = _index_case(api, cfg, [cfg.pos0])
+    _check_scores(got, ref, absref, 1e-5)
+
+
 @pytest.mark.parametrize("hi", [16, 32, 128])
 def test_index_head_counts(api, hi):
     cfg = configs.C2.scaled(B=2, n_comp=1100, HI=hi)
