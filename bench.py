@@ -4,8 +4,10 @@
 One step = one pass of the whole CSA layer step over one decode batch:
   csa_compress_pair (the KV entry that completes at this step, stored prepared
   for attention, and its indexer key, quantized to the cache format)  ->
-  csa_index  ->  csa_topk  ->  csa_attend (prepared compressed entries, raw window)
-(plus, for the Pro MXFP4 workload, the HCA layer: compress + hca_attend).
+  csa_index  ->  csa_topk  ->  csa_attend (prepared compressed entries; decode reads
+  raw window rows, prefill prepares the chunk's token rows first and reads them prepared)
+(plus, for the workloads with an HCA layer: compress, preparation of the step's
+window rows, hca_attend).
 
 Default workload: Pro-shaped decode at 1M context (B=4, 262,144 compressed
 entries, 128 heads x 512, fp8 e4m3 indexer with row scales, top-k 1024, window
@@ -165,6 +167,15 @@ def main():
     if cfg.with_hca:
         api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
     T = cfg.T
+    # window rows: prefill (CSA) and the HCA layer also keep the token rows prepared (each row once, at its own
+    # position, when it is written); rows of earlier steps are prepared here, the step's own T rows in the step
+    csa_mode = 2 if T > 1 else 1
+    win_new = dict(pos_base=pos, pos_first=0)
+    for st in sets:
+        st["pwin"] = api.prepare_kv(st["win"], prep, pos_base=pos, pos_first=-(cfg.n_win - 1)) if csa_mode == 2 \
+            else st["win"]
+        if cfg.with_hca:
+            st["phwin"] = api.prepare_kv(st["hwin"], prep, pos_base=pos, pos_first=-(cfg.n_win - 1))
     scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
     idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
     out = torch.empty((B, T, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
@@ -193,9 +204,11 @@ def main():
                 api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
                              c["first_entry"], c["num_entries"], out=hca_cache[:, c["first_entry"]:],
                              out_batch_stride=cfg.n_hca, prep=prep, stream=side)
-                api.hca_attend(st["hq"], hca_cache, st["hwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
+                api.prepare_kv(st["hwin"][:, cfg.n_win - 1:], prep, out=st["phwin"][:, cfg.n_win - 1:],
+                               stream=side, **win_new)
+                api.hca_attend(st["hq"], hca_cache, st["phwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
                                cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side,
-                               kv_prepared=True)
+                               kv_prepared=2)
         # the block's KV entry and its indexer-key entry (quantized to the cache format) in one launch
         c = st["cik"]
         ik_job = dict(st["cik_t"], out=st["ik"][:, first:], out_batch_stride=N,
@@ -203,10 +216,12 @@ def main():
                       out_scale=st["ik_scale"][:, first:] if fmt in ("fp8", "mxfp4") else None)
         api.compress_pair(dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep), ik_job, cfg.m,
                           c["row0_pos"], first, n_new)
+        if csa_mode == 2:
+            api.prepare_kv(st["win"][:, cfg.n_win - 1:], prep, out=st["pwin"][:, cfg.n_win - 1:], **win_new)
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
-        api.attend(st["q"], kv_cache, idx, st["win"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
-                   cfg.eps, cfg.rope_base, out=out, kv_prepared=True)
+        api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
+                   cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode)
         if side is not None:
             main_s.wait_stream(side)
 

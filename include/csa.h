@@ -58,7 +58,7 @@ typedef enum {
  *   (c-R+2i, c-R+2i+1), R = rope_dims, angle pos * rope_base^(-2i/R).
  * A compressed entry or a token row keeps its position for good, so its prepared
  * form can be stored once (csa_compress with a csa_kv_prep, csa_prepare_kv) and
- * reused by every later query (csa_attend / hca_attend with kv_prepared = 1).
+ * reused by every later query (csa_attend / hca_attend with kv_prepared >= 1).
  */
 typedef struct {
   const float* gamma; /* device float32 [c] RMSNorm gain, NULL = 1 */
@@ -210,8 +210,12 @@ csa_status csa_topk(const float* scores, int B, int T, int64_t n_max,
  *   kv_prepared : 0 = comp_kv holds pooled entries e; 1 = comp_kv holds the
  *               prepared e^ (csa_compress with a csa_kv_prep of the same gamma_kv,
  *               eps, rope_dims and rope_base, or csa_prepare_kv with
- *               pos_stride = m), which are then used as they are.  Window rows
- *               are always the raw token rows.
+ *               pos_stride = m), which are then used as they are, window rows
+ *               raw token rows; 2 = as 1, and the window rows are prepared too
+ *               (csa_prepare_kv of the token rows at their positions: pos_base =
+ *               pos0, pos_first = -(n_win - 1), pos_stride = 1).  Any other value
+ *               is CSA_ERR_UNSUPPORTED.  With 2 and H a multiple of 64, prefill
+ *               (T > 1) runs a kernel variant with 64 heads per workgroup.
  *   out     : [B][T][H][c] in out_t (CSA_F32 or CSA_BF16)
  *   workspace : csa_attend_workspace_bytes(B, T, H, c, k, n_win) bytes of device
  *               memory (no initial contents needed); may be NULL if that is 0.
@@ -236,7 +240,8 @@ csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, co
  * hca_attend -- HCA core attention ([HCA] (2)): as csa_attend, with the
  * compressed part dense: every visible entry s < min(floor(t/m_hca), n_max) of
  * comp_kv, each at position m_hca * s.  Same layouts, limits, kv_prepared rule
- * (prepared entries at pos_stride = m_hca) and workspace rule
+ * (prepared entries at pos_stride = m_hca; with 2 and H a multiple of 64, decode
+ * also runs the 64-head variant) and workspace rule
  * (hca_attend_workspace_bytes).
  */
 size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win);

@@ -163,8 +163,16 @@ def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_
     out_fmt = out_fmt or in_fmt
     if out is None:
         out = torch.empty((B, rows, c), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=x.device)
-    st = lib.csa_prepare_kv(_ptr(x), rows, _ptr(out), rows, B, rows, c, FMT[in_fmt], FMT[out_fmt], _ptr(pos_base),
-                            pos_first, pos_stride, _prep_arg(prep), _stream(stream))
+    if out.shape != x.shape:
+        raise CSAError(f"prepare_kv: out shape {tuple(out.shape)} differs from {tuple(x.shape)}")
+    for t in (x, out):   # rows of one sequence contiguous; sequences may sit at any row stride (views)
+        if t.stride(2) != 1 or t.stride(1) != c or t.stride(0) % c:
+            raise CSAError("prepare_kv: rows must be contiguous with a whole-row batch stride")
+    for t in (x, out):
+        if not t.is_cuda:
+            raise CSAError("tensor must live on the GPU")
+    st = lib.csa_prepare_kv(x.data_ptr(), x.stride(0) // c, out.data_ptr(), out.stride(0) // c, B, rows, c, FMT[in_fmt],
+                            FMT[out_fmt], _ptr(pos_base), pos_first, pos_stride, _prep_arg(prep), _stream(stream))
     _lib.check(st, "csa_prepare_kv")
     return out
 

@@ -30,6 +30,8 @@
 //
 // F32 path (VALU): one workgroup per (query row, head group), waves take entries
 // round-robin with their own online softmax and are merged in a fixed order.
+#include <utility>
+
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -38,6 +40,9 @@ namespace {
 constexpr int kTile = 32;            // entry slots per staged tile
 constexpr int kSplitSlots = 128;     // decode split length (slots)
 constexpr float kLog2e = 1.4426950408889634f;
+// the running maximum moves (and the accumulators are rescaled) only once a tile's logit exceeds it by
+// this much (base-2 units), so later tiles rarely rescale; probabilities stay below 2^8
+constexpr float kLazyMax = 8.0f;
 
 struct AttnArgs {
   const uint16_t* q;
@@ -52,7 +57,7 @@ struct AttnArgs {
   float* ws_o;     // [rows][nsplit][H][C]
   float* ws_ml;    // [rows][nsplit][H][2]
   int T, H, R, k, n_win, m, out_t, mode, nsplit;
-  int prepared;           // compressed entries are stored prepared (RMSNorm + RoPE done)
+  int prepared;           // 0 raw rows; 1 compressed entries stored prepared; 2 window rows prepared too
   int ns_c, s_c, s_w;     // split layout: ns_c compressed parts of s_c slots, then window parts of s_w
   int64_t n_max;
   float scale, eps;
@@ -64,9 +69,16 @@ struct Slot {
   double pos;
 };
 
+// The CSA index-list value of a slot of query (b, r), or 0 where no list value is read (HCA, window
+// slots, slots past the part's end).  Loaded apart from the slot's resolution so that it can be fetched
+// a stage ahead.
+CSA_DEV int32_t slot_idx(const AttnArgs& a, int b, int r, int64_t slot, int64_t slot_hi) {
+  return (a.mode == 0 && slot < slot_hi && slot < a.k) ? a.idx[((int64_t)b * a.T + r) * a.k + slot] : 0;
+}
+
 // slot j of query (b, r) at position t: CSA = idx slots then window; HCA = dense range then window.
-// Only the CSA index-list value is read from memory.
-CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vis, int64_t slot) {
+// e_idx is the slot's index-list value (slot_idx) for CSA.
+CSA_DEV Slot resolve_slot(const AttnArgs& a, int r, int64_t t, int64_t vis, int64_t slot, int32_t e_idx) {
   Slot s;
   s.is_win = false;
   s.row = -1;
@@ -75,7 +87,7 @@ CSA_DEV Slot resolve_slot(const AttnArgs& a, int b, int r, int64_t t, int64_t vi
   if (slot < ncomp) {
     int64_t e;
     if (a.mode == 0) {
-      e = a.idx[((int64_t)b * a.T + r) * a.k + slot];
+      e = e_idx;
       if (e < 0 || e >= a.n_max) return s;
     } else {
       e = slot;
@@ -107,11 +119,123 @@ CSA_DEV i16x4 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// LDS byte address of a pointer into dynamic shared memory
+CSA_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The batched LDS reads below are written as asm blocks that wait for their own reads before they end,
+// so no read is in flight outside the block; the outputs are early-clobber, so that no output register
+// can share an address register that a later read of the block still uses.  They are kept out of the
+// compiler's sight on purpose: for the builtin transpose read the compiler first waits for every
+// outstanding global-to-LDS fetch, which would stall on the next stage's prefetch.
+//
+// Sixteen transpose reads: rows lo / hi of eight base addresses (dims tiles 8J .. 8J + 7).
+template <int OFF_LO, int OFF_HI>
+CSA_DEV void lds_read_tr16_x16(i16x4 (&o)[16], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %2, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %4, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %6, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF_LO),
+        "i"(OFF_HI)
+      : "memory");
+}
+
+// Eight 16-byte reads, o[4j + v] at a[v] + OFF_j, in one block that waits for them.
+template <int OFF0, int OFF1>
+CSA_DEV void lds_read_b128_x8(u32x4 (&o)[8], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%12\n\t"
+      "ds_read_b128 %1, %9 offset:%12\n\t"
+      "ds_read_b128 %2, %10 offset:%12\n\t"
+      "ds_read_b128 %3, %11 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %9 offset:%13\n\t"
+      "ds_read_b128 %6, %10 offset:%13\n\t"
+      "ds_read_b128 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF0), "i"(OFF1)
+      : "memory");
+}
+
+// Four 16-byte reads, o[v] at a[v] + OFF0.
+template <int OFF0>
+CSA_DEV void lds_read_b128_x4(u32x4 (&o)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF0)
+      : "memory");
+}
+
+// Reductions over the lane pairs (l, l ^ 16) and (l, l ^ 32) with the gfx950 lane-swap instructions (VALU,
+// no LDS round trip); both lanes of a pair get the same value
+CSA_DEV float pair16_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+CSA_DEV float pair32_max(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+CSA_DEV float pair16_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+CSA_DEV float pair32_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <typename F, int... I>
+CSA_DEV void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int N, typename F>
+CSA_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Entry-major LDS rows of C bf16 without padding; 16-byte chunk c of row e is stored at
-// chunk position c ^ (e & 15), which spreads the 16 rows an MFMA operand read touches
-// over all LDS banks.
+// chunk position c ^ swz_key(e & 15), which spreads the rows an MFMA operand read touches
+// over the LDS banks.
+#ifndef CSA_SWZ_VARIANT
+#define CSA_SWZ_VARIANT 0
+#endif
+CSA_DEV constexpr int swz_key(int e) {
+#if CSA_SWZ_VARIANT == 1
+  return ((e & 7) << 1) | ((e >> 3) & 1);
+#elif CSA_SWZ_VARIANT == 2
+  return ((e & 3) << 1) | ((e >> 2) & 1) | (e & 8);
+#else
+  return e & 15;
+#endif
+}
 template <int C>
-CSA_DEV int swz(int e, int c) { return c ^ (e & 15); }
+CSA_DEV int swz(int e, int c) { return c ^ swz_key(e & 15); }
 
 constexpr int kStage = 64;  // slots fetched into LDS at once (2 compute tiles)
 
@@ -119,23 +243,33 @@ constexpr int kStage = 64;  // slots fetched into LDS at once (2 compute tiles)
 // [w*C/4, (w+1)*C/4).  Per stage: (1) resolve 64 slots (row address, position, validity),
 // (2) DMA every row straight into LDS (global_load_lds, 16 B per lane, no registers),
 // (3) per-entry RMS scalar and RoPE in place, (4) two 32-slot tiles of MFMA work from LDS.
-template <int C>
+template <int C, bool WIDE, bool RAW>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int nx) {
-  constexpr int DW = C / 4;     // dims per wave
+  // RAW: rows may need RMSNorm / RoPE here (raw compressed entries or raw window rows); without it every
+  // row is stored prepared and the kernel has no normalisation or rotation of entries at all
+  // narrow: 16 heads per workgroup, wave w owns dims [w C/4, (w+1) C/4) of all 16 (logits summed across
+  // waves through LDS); wide: 64 heads per workgroup, wave w owns heads 16w .. 16w+15 over all dims
+  constexpr int DW = WIDE ? C : C / 4;  // dims per wave
   constexpr int KSW = DW / 32;  // k-steps of the wave's partial S^T = E Q^T
   constexpr int DTW = DW / 16;  // 16-dim output tiles of the wave
   constexpr int NCR = C / 8;    // 16-byte chunks per row
   constexpr int RPI = 64 / NCR; // rows per DMA instruction
+  static_assert(!(WIDE && RAW), "the wide variant reads prepared rows only");
+  // the wide variant runs one workgroup per CU (its registers), so it can hold two stages in LDS and
+  // fetch stage s + 1 while it computes stage s; slot resolution then runs two stages ahead (3 buffers)
+  constexpr int NE = WIDE ? 2 : 1;  // LDS stage buffers
+  constexpr int NR = WIDE ? 3 : 2;  // slot-resolution buffers
   extern __shared__ __align__(16) uint16_t s_mem[];
-  uint16_t* E = s_mem;                                                     // [kStage][C]
-  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + kStage * C);            // [4 waves][2][64 lanes]
-  float* s_re = reinterpret_cast<float*>(s_part + 4 * 2 * 64);             // [kStage]
+  uint16_t* E0 = s_mem;                                                    // [NE][kStage][C]
+  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + NE * kStage * C);       // [4 waves][2][64 lanes] (narrow)
+  float* s_re = reinterpret_cast<float*>(s_part + (WIDE ? 0 : 4 * 2 * 64));  // [kStage]
   float* s_rq = s_re + kStage;                                             // [4][16]
   double* s_theta = reinterpret_cast<double*>(s_rq + 64);                  // [64]
-  double* s_pos2 = s_theta + 64;                                           // [2][kStage]
-  const uint16_t** s_src2 = reinterpret_cast<const uint16_t**>(s_pos2 + 2 * kStage);  // [2][kStage]
-  int* s_flag2 = reinterpret_cast<int*>(s_src2 + 2 * kStage);              // [2][kStage] 1 valid | 2 raw
-  int* s_raw2 = s_flag2 + 2 * kStage;                                      // [2] stage holds a raw row
+  double* s_pos2 = s_theta + 64;                                           // [NR][kStage]
+  const uint16_t** s_src2 = reinterpret_cast<const uint16_t**>(s_pos2 + NR * kStage);  // [NR][kStage]
+  int* s_flag2 = reinterpret_cast<int*>(s_src2 + NR * kStage);             // [NR][kStage] 1 valid | 2 raw
+  int* s_raw2 = s_flag2 + NR * kStage;                                     // [NR] stage holds a raw row
+  int* s_idx3 = s_raw2 + NR;  // [3][kStage] (wide, CSA) index-list values, fetched two stages ahead
 
   if ((int)blockIdx.x >= nx) return;  // grid.x is padded to a multiple of 8 (XCD-aligned head groups)
   const int lane = threadIdx.x & 63;
@@ -147,7 +281,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   const int r = row - b * a.T;
   const int64_t t = a.pos0[b] + r;
   const int64_t vis = visible_entries(t, a.m, a.n_max);
-  const int h0 = blockIdx.y * 16;
+  const int h0 = blockIdx.y * (WIDE ? 64 : 16) + (WIDE ? 16 * wave : 0);  // first head of this wave
   const int head = h0 + (lane & 15);
   const int rope_lo = C - a.R;
   const int64_t nslots = ((a.mode == 0) ? a.k : a.n_max) + a.n_win;
@@ -161,7 +295,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     slot_hi = min(slot_lo + a.s_w, nslots);
   }
   const double tpos = (double)t;
-  const int dbase = wave * DW;
+  const int dbase = WIDE ? 0 : wave * DW;
   const uint16_t* dummy = a.win + (int64_t)b * (a.T + a.n_win - 1) * C;  // a finite row for empty slots
   // this wave's raw query fragments go out first: they depend on nothing
   const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C + dbase;
@@ -169,45 +303,76 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
   for (int ks = 0; ks < KSW; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
   if (threadIdx.x < 64) s_theta[threadIdx.x] = rt.theta[threadIdx.x];
-  // slot resolution of a stage into half h of the resolve arrays (threads < kStage)
-  auto resolve_stage = [&](int64_t st0, int h) {
-    if (threadIdx.x < kStage) {
+  // slot resolution of a stage into buffer h of the resolve arrays, from the slots' index-list values
+  // (threads < kStage, i.e. all of wave 0)
+  auto commit_stage = [&](int64_t st0, int h, int32_t e_idx) {
+    {
       const int64_t slot = st0 + threadIdx.x;
       Slot sl;
       sl.row = -1;
-      if (slot < slot_hi) sl = resolve_slot(a, b, r, t, vis, slot);
+      if (slot < slot_hi) sl = resolve_slot(a, r, t, vis, slot, e_idx);
       const bool valid = sl.row >= 0;
       s_src2[h * kStage + threadIdx.x] = valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
                                                             : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
                                                : dummy;
       s_pos2[h * kStage + threadIdx.x] = sl.pos;
       // raw rows (window tokens, or compressed entries not stored prepared) get RMSNorm and RoPE here
-      const bool raw = valid && (sl.is_win || !a.prepared);
+      const bool raw = RAW && valid && (sl.is_win ? a.prepared < 2 : a.prepared == 0);
       s_flag2[h * kStage + threadIdx.x] = valid ? (raw ? 3 : 1) : 0;
       const uint64_t rm = __ballot(raw);  // threads < kStage are exactly wave 0
       if (threadIdx.x == 0) s_raw2[h] = rm != 0;
     }
   };
+  auto resolve_stage = [&](int64_t st0, int h) {
+    if (threadIdx.x < kStage) commit_stage(st0, h, slot_idx(a, b, r, st0 + threadIdx.x, slot_hi));
+  };
   resolve_stage(slot_lo, 0);
   // DMA of a stage's rows into E: instruction j of wave w fills rows RPI*(w + 4j) .. +RPI-1; lane l
   // writes LDS chunk position (l % NCR) of row e = RPI*(w + 4j) + l / NCR, so it loads the logical
   // chunk stored there
-  auto issue_dma = [&](const uint16_t* const* src_rows) {
+  // The wave's 16 row addresses are read from LDS at once (lane l % 16 holds that of row
+  // RPI (wave + 4 (l / RPI)) + l % RPI) and handed to each instruction's lanes by a lane read.
+  auto issue_dma = [&](const uint16_t* const* src_rows, uint16_t* E) {
+    const int l16 = lane & 15;
+    const uint64_t mine = reinterpret_cast<uint64_t>(src_rows[RPI * (wave + 4 * (l16 / RPI)) + l16 % RPI]);
+    const int mlo = (int)(uint32_t)mine, mhi = (int)(uint32_t)(mine >> 32);
 #pragma unroll
     for (int j = 0; j < kStage / RPI / 4; ++j) {
       const int e0 = RPI * (wave + 4 * j);
       const int e = e0 + lane / NCR;
       const int cpos = lane % NCR;
-      const uint16_t* src = src_rows[e] + 8 * swz<C>(e, cpos);
+      uint32_t rlo, rhi;
+      if constexpr (RPI == 1) {  // one row per instruction: a wave-uniform address
+        rlo = (uint32_t)__builtin_amdgcn_readlane(mlo, j);
+        rhi = (uint32_t)__builtin_amdgcn_readlane(mhi, j);
+      } else {
+        const int srcl = j * RPI + lane / NCR;  // the lane that holds row e's address
+        rlo = (uint32_t)__shfl(mlo, srcl, 64);
+        rhi = (uint32_t)__shfl(mhi, srcl, 64);
+      }
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)rhi << 32) | rlo) + 8 * swz<C>(e, cpos);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(E + e0 * C), 16, 0, 0);
     }
   };
   __syncthreads();  // s_theta and the first stage's slots visible
-  issue_dma(s_src2);  // the first stage's rows land while the query is prepared
+  issue_dma(s_src2, E0);  // the first stage's rows land while the query is prepared
+  // wide, CSA: the index-list values of a later stage travel like the rows, straight into LDS (wave 0,
+  // lane i -> slot st0 + i, clamped into the list), so that no register load is pending across the
+  // stage's compute
+  auto fetch_idx = [&](int64_t st0, int buf) {
+    if (a.mode == 0 && wave == 0 && st0 < a.k) {
+      const int64_t slot = min(st0 + lane, (int64_t)a.k - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(a.idx + ((int64_t)b * a.T + r) * a.k + slot),
+          (__attribute__((address_space(3))) void*)(s_idx3 + buf * kStage), 4, 0, 0);
+    }
+  };
+  if (WIDE && slot_lo + kStage < slot_hi) fetch_idx(slot_lo + kStage, 1);
 
   // ---- query fragment: head lane&15, the wave's dims [dbase + 32ks + 8g, +8)
   bf16x8 qf[KSW];
+  float qss;
   {
     u32x4* raw = qraw;
     float ss = 0.0f;
@@ -218,7 +383,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    if (g == 0) s_rq[wave * 16 + (lane & 15)] = ss;
+    if (!WIDE && g == 0) s_rq[wave * 16 + (lane & 15)] = ss;  // a wide wave holds the whole sum
+    qss = ss;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
       const int d0 = dbase + 32 * ks + 8 * g;
@@ -254,171 +420,271 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
   for (int d = 0; d < DTW; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   float M = -INFINITY, L = 0.0f;  // running max / denominator of head lane&15 (base-2 units)
-  float zmul = 0.0f;              // set once the query norms of all four waves are in s_rq
+  // logits are kept in base-2 units (times log2 e) so that exponentials are single v_exp_f32; the narrow
+  // variant sets the factor once the four waves' partial query norms are in s_rq
+  float zmul = WIDE ? kLog2e * a.scale / sqrtf(qss / (float)C + a.eps) : 0.0f;
 
-  int half = 0;
-  for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, half ^= 1) {
-    const uint16_t** s_src = s_src2 + half * kStage;
-    const double* s_pos = s_pos2 + half * kStage;
-    const int* s_flag = s_flag2 + half * kStage;
-    // ---- (2) DMA of this stage's rows (the first stage's went out before the query was prepared)
-    if (s0 != slot_lo) issue_dma(s_src);
-    // the next stage's slot resolution (index-list loads) overlaps this stage's fetch and compute
-    if (s0 + kStage < slot_hi) resolve_stage(s0 + kStage, half ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (s0 == slot_lo) {
-      // logits are kept in base-2 units (times log2 e) so that exponentials are single v_exp_f32
-      zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
-                                       s_rq[48 + (lane & 15)]) / (float)C + a.eps);
-    }
-    if (s_raw2[half]) {
-      // ---- (3a) per-entry RMS scalar of the raw rows: 8 lanes per entry, two accumulators
-      // (prepared entries are already normalised: scalar 1)
-#pragma unroll 1
-      for (int rd = 0; rd < kStage / 32; ++rd) {
-        const int e = 32 * rd + (threadIdx.x >> 3);
-        const int sub = threadIdx.x & 7;
-        const int fl = s_flag[e];
-        const uint16_t* er = E + e * C;
-        float ss0 = 0.0f, ss1 = 0.0f;
-        if (fl & 2) {
+  // Wide variant: LDS offsets of this lane's operand reads, so that every read in a tile is one of a few
+  // per-lane bases plus an immediate (the swizzle key of an entry depends on its index mod 16 only, and
+  // eb + 16 nt is a multiple of 16).  QK (A operand): entry eb + 16nt + l (l = lane & 15), 16-byte chunk
+  // 4ks + g, whose swizzled position splits as 16 (ks >> 2) + ((4 (ks & 3) + g) ^ key(l)).  PV (transpose
+  // reads): entry eb + 4g + tr_r (+16), dims 16dt + 4tr_c .. +3, i.e. chunk 2dt + (tr_c >> 1) at swizzled
+  // position 16 (dt >> 3) + ((2 (dt & 7) + (tr_c >> 1)) ^ key(4g + tr_r)).
+  int qoff[4];        // elements, v = ks & 3
+  uint32_t toff[8];   // bytes, u = dt & 7
+  if constexpr (WIDE) {
+    const int l = lane & 15, tr_r = l >> 2, tr_c = lane & 3, x = 4 * g + tr_r;
 #pragma unroll
-          for (int j = 0; j < NCR / 8; ++j) {
-            const u32x4 w4 = *reinterpret_cast<const u32x4*>(er + 8 * swz<C>(e, sub + 8 * j));
-            ss0 = sumsq_bf16x2(w4[0], ss0);
-            ss1 = sumsq_bf16x2(w4[1], ss1);
-            ss0 = sumsq_bf16x2(w4[2], ss0);
-            ss1 = sumsq_bf16x2(w4[3], ss1);
-          }
-        }
-        float ss = ss0 + ss1;
-        ss += __shfl_xor(ss, 1, 64);
-        ss += __shfl_xor(ss, 2, 64);
-        ss += __shfl_xor(ss, 4, 64);
-        if (sub == 0) s_re[e] = (fl & 2) ? 1.0f / sqrtf(ss / (float)C + a.eps) : (fl ? 1.0f : 0.0f);
-      }
-      // ---- (3b) RoPE (and gain) of the raw rows, in place: items (entry, 4-pair chunk), four
-      // independent rotations per item so that their dependent sin/cos chains overlap.  With prepared
-      // compressed entries the raw (window) rows also take the gain on their non-RoPE dims here.
-      {
-        const bool all_dims = a.prepared && a.gamma_kv;
-        const int c_lo = all_dims ? 0 : (rope_lo >> 3);
-        const int nrc = NCR - c_lo;  // chunks per entry
-#pragma unroll 1
-        for (int it = threadIdx.x; it < kStage * nrc; it += 256) {
-          const int e = it / nrc;
-          if (!(s_flag[e] & 2)) continue;
-          const int c = c_lo + (it - e * nrc);
-          const int d0 = 8 * c;
-          u32x4* cp = reinterpret_cast<u32x4*>(E + e * C + 8 * swz<C>(e, c));
-          u32x4 w4 = *cp;
-          const double pos = s_pos[e];
-          float x[8];
+    for (int v = 0; v < 4; ++v) qoff[v] = l * C + 8 * ((4 * v + g) ^ swz_key(l));
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w4[q], 0); x[2 * q + 1] = bf(w4[q], 1); }
-          if (a.gamma_kv) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
-          }
-          if (d0 >= rope_lo) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              float cs, sn;
-              rope_cs(pos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
-              const float x0 = x[2 * p], x1 = x[2 * p + 1];
-              x[2 * p] = x0 * cs - x1 * sn;
-              x[2 * p + 1] = x0 * sn + x1 * cs;
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) w4[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
-          *cp = w4;
-        }
-      }
-    } else if (threadIdx.x < kStage) {
-      s_re[threadIdx.x] = s_flag[threadIdx.x] ? 1.0f : 0.0f;
-    }
-    __syncthreads();
-    // ---- (4) compute tiles of 32 slots
+    for (int u = 0; u < 8; ++u)
+      toff[u] = 2u * (uint32_t)(x * C + 8 * ((2 * u + (tr_c >> 1)) ^ swz_key(x)) + 4 * (tr_c & 1));
+  }
+
+  // ---- (4) the compute tiles of 32 slots of a stage held in E (slot flags in s_flag)
+  auto compute_stage = [&](const uint16_t* E, int64_t s0, const int* s_flag) {
     const int ntile = (int)min((int64_t)kStage / kTile, (slot_hi - s0 + kTile - 1) / kTile);
 #pragma unroll 1
     for (int tl = 0; tl < ntile; ++tl) {
       const int eb = kTile * tl;
-      // partial S^T over the wave's dims: lane holds entries eb + 16nt + 4g + i, head lane&15
+      // wide: byte addresses of this tile's operand reads (entries eb + 16 nt + (lane & 15) for QK)
+      uint32_t qb[2][4];
+      uint32_t ebase = 0;
+      if constexpr (WIDE) {
+        ebase = lds_addr(E) + (uint32_t)(eb * C * 2);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) qb[nt][v] = ebase + (uint32_t)(nt * 32 * C + 2 * qoff[v]);
+      }
+      // S^T over the wave's dims: lane holds entries eb + 16nt + 4g + i, head lane&15
+      f32x4 accs[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int e = eb + 16 * nt + (lane & 15);
-        const uint16_t* er = E + e * C;
+        if constexpr (WIDE) {
+          // batches of 8 k-steps (4 for c = 128): ks = 8 BI + 4 j + v at qb[nt][v] + 256 (2 BI + j) bytes
+          static_for<(KSW + 7) / 8>([&](auto bc) {
+            constexpr int BI = decltype(bc)::value;
+            if constexpr (KSW >= 8) {
+              u32x4 rd[8];
+              lds_read_b128_x8<512 * BI, 512 * BI + 256>(rd, qb[nt]);
 #pragma unroll
-        for (int ks = 0; ks < KSW; ++ks) {
-          const int c = (dbase + 32 * ks + 8 * g) >> 3;
-          const bf16x8 ef = *reinterpret_cast<const bf16x8*>(er + 8 * swz<C>(e, c));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], acc, 0, 0, 0);
+              for (int q = 0; q < 8; ++q)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[8 * BI + q], acc,
+                                                              0, 0, 0);
+            } else {
+              u32x4 rd[4];
+              lds_read_b128_x4<0>(rd, qb[nt]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[q], acc, 0, 0, 0);
+            }
+          });
+          accs[nt] = acc;
+        } else {
+          const int e = eb + 16 * nt + (lane & 15);
+          const uint16_t* er = E + e * C;
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks) {
+            const int c = (dbase + 32 * ks + 8 * g) >> 3;
+            const bf16x8 ef = *reinterpret_cast<const bf16x8*>(er + 8 * swz<C>(e, c));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ef, qf[ks], acc, 0, 0, 0);
+          }
+          s_part[(wave * 2 + nt) * 64 + lane] = acc;
         }
-        s_part[(wave * 2 + nt) * 64 + lane] = acc;
       }
-      __syncthreads();
+      if (!WIDE) __syncthreads();
       float z[8], re[8];
       float tmax = -INFINITY;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        f32x4 sum = s_part[(0 * 2 + nt) * 64 + lane];
+        f32x4 sum;
+        if (WIDE) {
+          sum = accs[nt];
+        } else {  // the four waves' partial logits, summed in a fixed order
+          sum = s_part[(0 * 2 + nt) * 64 + lane];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          const f32x4 pw = s_part[(w * 2 + nt) * 64 + lane];
-          sum[0] += pw[0]; sum[1] += pw[1]; sum[2] += pw[2]; sum[3] += pw[3];
+          for (int w = 1; w < 4; ++w) {
+            const f32x4 pw = s_part[(w * 2 + nt) * 64 + lane];
+            sum[0] += pw[0]; sum[1] += pw[1]; sum[2] += pw[2]; sum[3] += pw[3];
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float rv = s_re[eb + 16 * nt + 4 * g + i];
+          const float rv = WIDE ? (s_flag[eb + 16 * nt + 4 * g + i] ? 1.0f : 0.0f) : s_re[eb + 16 * nt + 4 * g + i];
           re[4 * nt + i] = rv;
           const float zz = rv > 0.0f ? sum[i] * zmul * rv : -INFINITY;
           z[4 * nt + i] = zz;
           tmax = fmaxf(tmax, zz);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float Mn = fmaxf(M, tmax);
-      const bool live = Mn != -INFINITY;
-      const float alpha = live ? __builtin_amdgcn_exp2f(M - Mn) : 1.0f;
+      tmax = pair32_max(pair16_max(tmax));
+      // lazy running maximum: moved (with O and L rescaled) only when some head of the wave has a logit
+      // more than kLazyMax above its current one; a first finite logit always moves it
+      if (__any(tmax > M + kLazyMax)) {
+        const float Mn = fmaxf(M, tmax);
+        const float alpha = Mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mn);
+        L *= alpha;
+        M = Mn;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) {
+          O[dt][0] *= al[0]; O[dt][1] *= al[1]; O[dt][2] *= al[2]; O[dt][3] *= al[3];
+        }
+      }
+      const bool live = M != -INFINITY;
       float psum = 0.0f;
       uint32_t pw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = live ? __builtin_amdgcn_exp2f(z[j] - Mn) : 0.0f;
-        const float p1 = live ? __builtin_amdgcn_exp2f(z[j + 1] - Mn) : 0.0f;
+        const float p0 = live ? __builtin_amdgcn_exp2f(z[j] - M) : 0.0f;
+        const float p1 = live ? __builtin_amdgcn_exp2f(z[j + 1] - M) : 0.0f;
         psum += p0 + p1;
         pw[j / 2] = pack_bf16x2(p0 * re[j], p1 * re[j + 1]);
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      L = L * alpha + psum;
-      M = Mn;
+      psum = pair32_sum(pair16_sum(psum));
+      L += psum;
       const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
-      // rescale O only when some head's running max moved in this tile
-      const bool rescale = __any(alpha != 1.0f);
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = rescale ? __shfl(alpha, 4 * g + i, 64) : 1.0f;
       // O += P E over the wave's dims; B operand by transpose reads of the entry-major rows
-      const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
-      const int e_lo = eb + 4 * g + tr_r, e_hi = e_lo + 16;
+      if constexpr (WIDE) {
+        uint32_t tb[8];
 #pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) {
-        const int hw = dbase + 16 * dt + 4 * tr_c;  // first of the 4 halfwords this lane addresses
-        const i16x4 lo = lds_read_tr16(E + e_lo * C + 8 * swz<C>(e_lo, hw >> 3) + (hw & 7));
-        const i16x4 hi = lds_read_tr16(E + e_hi * C + 8 * swz<C>(e_hi, hw >> 3) + (hw & 7));
-        const bf16x8 ef = __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        f32x4 o = O[dt];
-        if (rescale) {
-          o[0] *= al[0]; o[1] *= al[1]; o[2] *= al[2]; o[3] *= al[3];
+        for (int u = 0; u < 8; ++u) tb[u] = ebase + toff[u];
+        // batches of 8 output tiles: dt = 8J + u, u = 0..7
+        static_for<DTW / 8>([&](auto bc) {
+          constexpr int J = decltype(bc)::value;
+          i16x4 rd[16];
+          lds_read_tr16_x16<256 * J, 256 * J + 32 * C>(rd, tb);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const i16x4 lo = rd[2 * u], hi = rd[2 * u + 1];
+            const bf16x8 ef =
+                __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            O[8 * J + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, O[8 * J + u], 0, 0, 0);
+          }
+        });
+      } else {
+        const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+        const int e_lo = eb + 4 * g + tr_r, e_hi = e_lo + 16;
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) {
+          const int hw = dbase + 16 * dt + 4 * tr_c;  // first of the 4 halfwords this lane addresses
+          const i16x4 lo = lds_read_tr16(E + e_lo * C + 8 * swz<C>(e_lo, hw >> 3) + (hw & 7));
+          const i16x4 hi = lds_read_tr16(E + e_hi * C + 8 * swz<C>(e_hi, hw >> 3) + (hw & 7));
+          const bf16x8 ef =
+              __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, O[dt], 0, 0, 0);
         }
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, o, 0, 0, 0);
+        __syncthreads();  // s_part is rewritten by the next tile; E and the resolve buffer by the next stage
       }
-      __syncthreads();  // s_part is rewritten by the next tile; E and the resolve half by the next stage
+    }
+  };
+
+  if constexpr (WIDE) {
+    // stage st: its rows are in E[st & 1], its slots in resolve buffer st % 3.  One barrier per stage:
+    // after it, stage st + 1 is fetched into the other buffer (whose last reader, stage st - 1, is done)
+    // and the index-list values of stage st + 2 into s_idx3, while stage st is computed.
+    int st = 0;
+    for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, ++st) {
+      const bool more = s0 + kStage < slot_hi;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this stage's rows and the next one's index values
+      if (more && threadIdx.x < kStage)
+        commit_stage(s0 + kStage, (st + 1) % 3, s_idx3[((st + 1) % 3) * kStage + threadIdx.x]);
+      __syncthreads();
+      if (more) {
+        issue_dma(s_src2 + ((st + 1) % 3) * kStage, E0 + ((st + 1) & 1) * kStage * C);
+        if (s0 + 2 * kStage < slot_hi) fetch_idx(s0 + 2 * kStage, (st + 2) % 3);
+      }
+      compute_stage(E0 + (st & 1) * kStage * C, s0, s_flag2 + (st % 3) * kStage);
+    }
+  } else {
+    int half = 0;
+    for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, half ^= 1) {
+      const uint16_t** s_src = s_src2 + half * kStage;
+      const double* s_pos = s_pos2 + half * kStage;
+      const int* s_flag = s_flag2 + half * kStage;
+      // ---- (2) DMA of this stage's rows (the first stage's went out before the query was prepared)
+      if (s0 != slot_lo) issue_dma(s_src, E0);
+      // the next stage's slot resolution (index-list loads) overlaps this stage's fetch and compute
+      if (s0 + kStage < slot_hi) resolve_stage(s0 + kStage, half ^ 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (!WIDE && s0 == slot_lo) {
+        zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
+                                         s_rq[48 + (lane & 15)]) / (float)C + a.eps);
+      }
+      if (RAW && s_raw2[half]) {
+        // ---- (3a) per-entry RMS scalar of the raw rows: 8 lanes per entry, two accumulators
+        // (prepared entries are already normalised: scalar 1)
+#pragma unroll 1
+        for (int rd = 0; rd < kStage / 32; ++rd) {
+          const int e = 32 * rd + (threadIdx.x >> 3);
+          const int sub = threadIdx.x & 7;
+          const int fl = s_flag[e];
+          const uint16_t* er = E0 + e * C;
+          float ss0 = 0.0f, ss1 = 0.0f;
+          if (fl & 2) {
+#pragma unroll
+            for (int j = 0; j < NCR / 8; ++j) {
+              const u32x4 w4 = *reinterpret_cast<const u32x4*>(er + 8 * swz<C>(e, sub + 8 * j));
+              ss0 = sumsq_bf16x2(w4[0], ss0);
+              ss1 = sumsq_bf16x2(w4[1], ss1);
+              ss0 = sumsq_bf16x2(w4[2], ss0);
+              ss1 = sumsq_bf16x2(w4[3], ss1);
+            }
+          }
+          float ss = ss0 + ss1;
+          ss += __shfl_xor(ss, 1, 64);
+          ss += __shfl_xor(ss, 2, 64);
+          ss += __shfl_xor(ss, 4, 64);
+          if (sub == 0) s_re[e] = (fl & 2) ? 1.0f / sqrtf(ss / (float)C + a.eps) : (fl ? 1.0f : 0.0f);
+        }
+        // ---- (3b) RoPE (and gain) of the raw rows, in place: items (entry, 4-pair chunk), four
+        // independent rotations per item so that their dependent sin/cos chains overlap.  With prepared
+        // compressed entries the raw (window) rows also take the gain on their non-RoPE dims here.
+        {
+          const bool all_dims = a.prepared && a.gamma_kv;
+          const int c_lo = all_dims ? 0 : (rope_lo >> 3);
+          const int nrc = NCR - c_lo;  // chunks per entry
+#pragma unroll 1
+          for (int it = threadIdx.x; it < kStage * nrc; it += 256) {
+            const int e = it / nrc;
+            if (!(s_flag[e] & 2)) continue;
+            const int c = c_lo + (it - e * nrc);
+            const int d0 = 8 * c;
+            u32x4* cp = reinterpret_cast<u32x4*>(E0 + e * C + 8 * swz<C>(e, c));
+            u32x4 w4 = *cp;
+            const double pos = s_pos[e];
+            float x[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { x[2 * q] = bf(w4[q], 0); x[2 * q + 1] = bf(w4[q], 1); }
+            if (a.gamma_kv) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) x[q] *= a.gamma_kv[d0 + q];
+            }
+            if (d0 >= rope_lo) {
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                float cs, sn;
+                rope_cs(pos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
+                const float x0 = x[2 * p], x1 = x[2 * p + 1];
+                x[2 * p] = x0 * cs - x1 * sn;
+                x[2 * p + 1] = x0 * sn + x1 * cs;
+              }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w4[q] = pack_bf16x2(x[2 * q], x[2 * q + 1]);
+            *cp = w4;
+          }
+        }
+      } else if (threadIdx.x < kStage) {
+        s_re[threadIdx.x] = s_flag[threadIdx.x] ? 1.0f : 0.0f;
+      }
+      __syncthreads();
+      compute_stage(E0, s0, s_flag);
     }
   }
 
@@ -431,7 +697,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) dst[16 * dt] = O[dt][i];
     }
-    if (wave == 0 && g == 0) {
+    if ((WIDE || wave == 0) && g == 0) {
       a.ws_ml[(base + head) * 2 + 0] = M;
       a.ws_ml[(base + head) * 2 + 1] = L;
     }
@@ -633,7 +899,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgsF32 a, RopeTabl
     const float* src = is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + erow) * C
                               : a.comp + ((int64_t)b * a.n_max + erow) * C;
     float x[kF32MaxDPL];
-    if (!is_win && a.prepared) {  // stored prepared: used as it is
+    if (is_win ? a.prepared == 2 : a.prepared != 0) {  // stored prepared: used as it is
       for (int j = 0; j < dpl; ++j) x[j] = src[d0 + j];
     } else {
       float ss = 0.f;
@@ -699,39 +965,51 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgsF32 a, RopeTabl
 
 // Decode (T = 1) splits each query's slot list into parts whose boundaries depend only on the list
 // lengths: the compressed slots into at most kMaxSplits - 4 parts of at least 128 slots, the window
-// slots into at most 4 parts of at least 64 (multiples of the 32-slot tile).  Window rows are always
-// normalised and rotated in the kernel, so keeping them apart keeps the parts of similar cost when
-// the compressed entries are stored prepared.  Prefill queries are served by one part each.
+// slots into at most 4 parts (2 for the wide variant) of at least 64 (multiples of the 32-slot tile).
+// Raw window rows are normalised and rotated in the kernel, so keeping them apart keeps the parts of
+// similar cost when the compressed entries are stored prepared.  Prefill queries are served by one
+// part each.
 struct SplitLayout {
   int nsplit, ns_c, s_c, s_w;
 };
-SplitLayout split_layout(int T, int64_t ncomp, int64_t n_win) {
+// The wide variant (64 heads per workgroup) serves prefill and HCA's long dense lists when every row is
+// stored prepared (it holds all c dims of 16 heads per wave and has no room for the in-kernel RMSNorm /
+// RoPE of raw rows); CSA decode keeps the narrow one, whose 16-head workgroups give a few short rows
+// enough parallel work.
+bool use_wide(int mode, int T, int H, int prepared) {
+  return (H % 64) == 0 && prepared == 2 && (T > 1 || mode == 1);
+}
+SplitLayout split_layout(int mode, int T, int H, int prepared, int64_t ncomp, int64_t n_win) {
   if (T != 1) return SplitLayout{1, 1, (int)(ncomp + n_win), 0};
   auto len = [](int64_t n, int parts, int minimum) -> int64_t {
     int64_t l = (n + parts - 1) / parts;
     l = ((l + kTile - 1) / kTile) * kTile;
     return l < minimum ? minimum : l;
   };
-  const int64_t sw = len(n_win, 4, 64);
+  const int max_w = use_wide(mode, T, H, prepared) ? 2 : 4;  // window parts (the rest: compressed parts)
+  const int64_t sw = len(n_win, max_w, 64);
   const int nsw = ceil_div(n_win, sw);
-  const int64_t sc = len(ncomp, kMaxSplits - 4, kSplitSlots);
+  const int64_t sc = len(ncomp, kMaxSplits - max_w, kSplitSlots);
   const int nsc = ncomp > 0 ? ceil_div(ncomp, sc) : 0;
   return SplitLayout{nsc + nsw, nsc, (int)sc, (int)sw};
 }
 
-template <int C>
+// the kernel's LDS carve-up: stage buffers, (narrow) logit exchange, per-slot scalars, RoPE table and
+// the slot-resolution buffers
+template <int C, bool WIDE>
 size_t bf16_lds_bytes() {
-  return (size_t)kStage * C * 2 + 4 * 2 * 64 * 16 + kStage * 4 + 64 * 4 + 64 * 8 + 2 * kStage * 8 + 2 * kStage * 8 +
-         2 * kStage * 4 + 2 * 4;
+  const size_t ne = WIDE ? 2 : 1, nr = WIDE ? 3 : 2;
+  return ne * kStage * C * 2 + (WIDE ? 0 : 4 * 2 * 64 * 16) + kStage * 4 + 64 * 4 + 64 * 8 + nr * kStage * 8 +
+         nr * kStage * 8 + nr * kStage * 4 + nr * 4 + 3 * kStage * 4;
 }
 
-template <int C>
+template <int C, bool WIDE, bool RAW>
 csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
-  const size_t lds = bf16_lds_bytes<C>();
+  const size_t lds = bf16_lds_bytes<C, WIDE>();
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C, WIDE, RAW>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return CSA_ERR_LAUNCH;
     attr_set = true;
   }
@@ -739,17 +1017,25 @@ csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStre
   // head group have equal linear ids modulo 8 and land on the same XCD (shared L2 for the staged KV)
   const int nx = a.nsplit * rows;
   const int nx_pad = (nx + 7) & ~7;
-  dim3 grid(nx_pad, a.H / 16);
-  hipLaunchKernelGGL(attend_bf16_kernel<C>, grid, dim3(256), lds, stream, a, rt, nx);
+  dim3 grid(nx_pad, a.H / (WIDE ? 64 : 16));
+  hipLaunchKernelGGL((attend_bf16_kernel<C, WIDE, RAW>), grid, dim3(256), lds, stream, a, rt, nx);
   if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+template <int C>
+csa_status launch_bf16_any(const AttnArgs& a, const RopeTable& rt, int rows, bool wide, hipStream_t stream) {
+  if (wide) return launch_bf16<C, true, false>(a, rt, rows, stream);
+  return a.prepared == 2 ? launch_bf16<C, false, false>(a, rt, rows, stream)
+                         : launch_bf16<C, false, true>(a, rt, rows, stream);
 }
 
 }  // namespace
 
 size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win) {
   (void)mode;
-  const int ns = split_layout(T, ncomp, n_win).nsplit;
+  // the larger of the two layouts, so one workspace size serves every kv_prepared mode
+  const int ns = max(split_layout(mode, T, H, 0, ncomp, n_win).nsplit, split_layout(mode, T, H, 2, ncomp, n_win).nsplit);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * T;
   const size_t o = rows * ns * H * (size_t)c * 4;
@@ -781,7 +1067,7 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
   a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
   a.T = T; a.H = H; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t; a.mode = mode;
   a.n_max = n_max; a.scale = scale; a.eps = eps; a.prepared = kv_prepared;
-  const SplitLayout lay = split_layout(T, mode == 0 ? (int64_t)k : n_max, n_win);
+  const SplitLayout lay = split_layout(mode, T, H, kv_prepared, mode == 0 ? (int64_t)k : n_max, n_win);
   a.nsplit = lay.nsplit;
   a.ns_c = lay.ns_c;
   a.s_c = lay.s_c;
@@ -794,10 +1080,11 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
     a.ws_o = nullptr;
     a.ws_ml = nullptr;
   }
+  const bool wide = use_wide(mode, T, H, kv_prepared);
   switch (c) {
-    case 128: return launch_bf16<128>(a, rt, rows, stream);
-    case 256: return launch_bf16<256>(a, rt, rows, stream);
-    case 512: return launch_bf16<512>(a, rt, rows, stream);
+    case 128: return launch_bf16_any<128>(a, rt, rows, wide, stream);
+    case 256: return launch_bf16_any<256>(a, rt, rows, wide, stream);
+    case 512: return launch_bf16_any<512>(a, rt, rows, wide, stream);
     default: return CSA_ERR_UNSUPPORTED;
   }
 }

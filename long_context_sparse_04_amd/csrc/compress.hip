@@ -84,11 +84,11 @@ struct Jobs {
   double theta[2][64];  // RoPE frequencies of each job
 };
 
-template <typename TIn>
-__global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows, int m, int64_t row0_pos,
+template <typename TIn, int NT>
+__global__ __launch_bounds__(NT) void compress_kernel(Jobs jobs, int rows, int m, int64_t row0_pos,
                                                             int64_t first_entry) {
-  __shared__ f32x4 s_m[kThreads], s_l[kThreads], s_a[kThreads];
-  __shared__ float s_red[kThreads / 64];
+  __shared__ f32x4 s_m[NT], s_l[NT], s_a[NT];
+  __shared__ float s_red[NT / 64];
 
   const Job jb = blockIdx.z ? jobs.j[1] : jobs.j[0];  // uniform select (no indexed kernel-argument copy)
   const TIn* __restrict__ ca = static_cast<const TIn*>(jb.ca);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int ncg = c >> 2;
-  const int nrs = kThreads / ncg;  // row slices (>= 1 because c <= 1024)
+  const int nrs = NT / ncg;  // row slices (>= 1 because c <= 1024)
   const int cg = tid % ncg;
   const int rs = tid / ncg;
   const int64_t i = first_entry + e;
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
     for (int q = 0; q < 4; ++q) y[q] = A[q] / L[q];
   }
 
-  if (jb.prep) prep_row4<kThreads>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
+  if (jb.prep) prep_row4<NT>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
   const int64_t orow = (int64_t)b * out_bstride + e;
   if (out_t == CSA_F32) {
     if (writer) *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
@@ -193,7 +193,9 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(Jobs jobs, int rows,
     for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
     if ((tid & 63) == 0) s_red[tid >> 6] = am;
     __syncthreads();
-    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    am = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) am = fmaxf(am, s_red[w]);
     const float scale = am / 448.0f;
     if (writer) {
       uint32_t pk = 0;
@@ -247,11 +249,23 @@ csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int r
     for (int t = 0; t < 64; ++t) js.theta[i][t] = rt.theta[t];
   }
   dim3 grid(num_entries, B, njobs);
-  if (in_t == CSA_F32)
-    hipLaunchKernelGGL(compress_kernel<float>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos, first_entry);
-  else
-    hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos,
-                       first_entry);
+  // an entry that pools many rows (HCA: m' = 128) gets 1024 threads, so that each thread walks few rows;
+  // the choice depends on m only, so an entry's result does not depend on the batch
+  if (m >= 64) {
+    if (in_t == CSA_F32)
+      hipLaunchKernelGGL((compress_kernel<float, 1024>), grid, dim3(1024), 0, stream, js, rows, m, row0_pos,
+                         first_entry);
+    else
+      hipLaunchKernelGGL((compress_kernel<uint16_t, 1024>), grid, dim3(1024), 0, stream, js, rows, m, row0_pos,
+                         first_entry);
+  } else {
+    if (in_t == CSA_F32)
+      hipLaunchKernelGGL((compress_kernel<float, kThreads>), grid, dim3(kThreads), 0, stream, js, rows, m, row0_pos,
+                         first_entry);
+    else
+      hipLaunchKernelGGL((compress_kernel<uint16_t, kThreads>), grid, dim3(kThreads), 0, stream, js, rows, m,
+                         row0_pos, first_entry);
+  }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 

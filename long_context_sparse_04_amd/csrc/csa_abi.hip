@@ -200,12 +200,13 @@ csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, co
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m);
   if (st != CSA_OK) return st;
   if (k < 1 || k > 2048 || n_max < 0 || n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
   if (B == 0 || T == 0) return CSA_OK;
   if (!q || !idx || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
   const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   return launch_attend(0, q, comp_kv, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, k, n_win, n_max,
-                       pos0, m, scale, eps, rope_base, kv_t, kv_prepared ? 1 : 0, out, out_t, workspace,
+                       pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t, workspace,
                        (hipStream_t)stream);
 }
 
@@ -222,12 +223,13 @@ csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv, co
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m_hca);
   if (st != CSA_OK) return st;
   if (n_max < 0 || n_max >= ((int64_t)1 << 24)) return CSA_ERR_SHAPE;
+  if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
   if (B == 0 || T == 0) return CSA_OK;
   if (!q || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
   const size_t need = hca_attend_workspace_bytes(B, T, H, c, n_max, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   return launch_attend(1, q, comp_kv, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, 1, n_win,
-                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared ? 1 : 0, out, out_t, workspace,
+                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared, out, out_t, workspace,
                        (hipStream_t)stream);
 }
 

@@ -123,11 +123,11 @@ def test_index_topk_attend_validation(lib):
 
     def att(**kw):
         a = dict(q=DUMMY, comp=DUMMY, idx=DUMMY, win=DUMMY, sink=DUMMY, B=4, T=1, H=128, c=512, R=64, k=1024,
-                 n_win=128, N=262144, pos=DUMMY, m=4, kv_t=1, out=DUMMY, out_t=1, ws=None, nb=0)
+                 n_win=128, N=262144, pos=DUMMY, m=4, kv_t=1, out=DUMMY, out_t=1, ws=None, nb=0, prep=0)
         a.update(kw)
         return lib.csa_attend(a["q"], a["comp"], a["idx"], a["win"], a["sink"], None, None, a["B"], a["T"], a["H"],
                               a["c"], a["R"], a["k"], a["n_win"], a["N"], a["pos"], a["m"], 0.044, 1e-6, 1e4,
-                              a["kv_t"], 0, a["out"], a["out_t"], a["ws"], a["nb"], None)
+                              a["kv_t"], a["prep"], a["out"], a["out_t"], a["ws"], a["nb"], None)
     assert att() == 4                         # decode needs the split workspace
     assert att(c=192) == 3
     assert att(R=60) == 3
@@ -135,4 +135,7 @@ def test_index_topk_attend_validation(lib):
     assert att(kv_t=2) == 3
     assert att(k=0) == 2
     assert att(q=None, ws=DUMMY, nb=ws) == 1
+    assert att(prep=3, ws=DUMMY, nb=ws) == 3 and att(prep=-1, ws=DUMMY, nb=ws) == 3   # kv_prepared is 0, 1 or 2
+    assert lib.hca_attend(DUMMY, DUMMY, DUMMY, DUMMY, None, None, 8, 1, 128, 512, 64, 128, 8192, DUMMY, 128, 0.044,
+                          1e-6, 1e4, 1, 3, DUMMY, 1, None, 0, None) == 3
     assert lib.hca_attend_workspace_bytes(8, 1, 128, 512, 8192, 128) > 0

@@ -11,8 +11,9 @@ The chunked-prefill workload (4,096 query rows over a 65,536-token context) is
 checked on sampled query rows that the oracle computes one by one.
 
 As in the benchmark, the compressed caches are stored prepared for attention
-(RMSNorm and RoPE applied once per entry) and read with kv_prepared; the oracle
-takes the raw entries and applies both itself.
+(RMSNorm and RoPE applied once per entry) and read with kv_prepared; for the
+chunked prefill and the HCA layer the window token rows are stored prepared too
+(kv_prepared = 2).  The oracle takes the raw rows and applies both itself.
 
 Bars: compressed rows equal to the oracle's own bf16 rounding or within half an
 ulp plus float32 summation error; scores within 1e-5 of sum_h |w| |q|.|K| (the natural scale of
@@ -182,8 +183,9 @@ def test_decode_step_full_size(api, name):
         hca_cache = dev(cc["hca"])
         api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
         _gpu_compress(api, chca, hca_cache[:, chca["first_entry"]:], stride=cfg.n_hca, prep=prep)
-        hout = api.hca_attend(dev(hq), hca_cache, dev(hwin), dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                              cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
+        phwin = _prepared_window(api, hwin, prep, pos, cfg)
+        hout = api.hca_attend(dev(hq), hca_cache, phwin, dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
+                              cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
     torch.cuda.synchronize()
 
     # ---- compression of this step's entries
@@ -249,6 +251,15 @@ def test_decode_step_full_size(api, name):
         assert e_h <= LOWP_TOL
 
 
+def _prepared_window(api, win, prep, pos, cfg):
+    """Window token rows stored prepared, as the benchmark keeps them for prefill and the HCA layer: the rows
+    before the step at their positions, then the step's own rows (a view, written in place) in a second call."""
+    raw = dev(win)
+    out = api.prepare_kv(raw, prep, pos_base=pos, pos_first=-(cfg.n_win - 1))
+    api.prepare_kv(raw[:, cfg.n_win - 1:], prep, pos_base=pos, pos_first=0, out=out[:, cfg.n_win - 1:])
+    return out
+
+
 # ----------------------------------------------------------------------------- chunked prefill
 def test_chunked_prefill_full_size_sampled(api):
     cfg = configs.C4
@@ -273,12 +284,13 @@ def test_chunked_prefill_full_size_sampled(api):
     _gpu_compress(api, ckv, kv_cache[:, f0:], stride=N, prep=prep)
     _gpu_compress(api, cik, ik[:, f0:], stride=N)
     _gpu_compress(api, chca, hca_cache[:, hf0:], stride=cfg.n_hca, prep=prep)
+    pwin, phwin = _prepared_window(api, win, prep, pos, cfg), _prepared_window(api, hwin, prep, pos, cfg)
     scores = api.index(dev(qi["data"]), None, dev(w), ik, None, pos, cfg.m, fmt)
     idx, _ = api.topk(scores, pos, cfg.m, cfg.k)
-    out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
-    hout = api.hca_attend(dev(hq), hca_cache, dev(hwin), dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
+    out_pipe = api.attend(dev(q), kv_cache, idx, pwin, dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
+                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
+    hout = api.hca_attend(dev(hq), hca_cache, phwin, dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
+                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
     torch.cuda.synchronize()
 
     # ---- every compressed entry of the chunk
@@ -323,8 +335,8 @@ def test_chunked_prefill_full_size_sampled(api):
     # sees the real mix of list lengths)
     mixed = gi.copy()
     mixed[0, rows] = r_idx_all[0, rows]
-    out_iso = api.attend(dev(q), kv_cache, dev(mixed), dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
+    out_iso = api.attend(dev(q), kv_cache, dev(mixed), pwin, dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
+                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
     torch.cuda.synchronize()
     pairs = [(0, r) for r in rows]
     r_out = oracle.attend(_f64(q), vcache[None], r_idx_all, _f64(win), sink, pos0, cfg.m, cfg.n_win,

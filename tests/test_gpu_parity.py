@@ -300,9 +300,9 @@ def _rand_idx(rng, B, T, k, pos0, m, n_max, fill=0.9):
 
 
 def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False, prepared=False):
-    """GPU attention against the oracle on the same raw inputs.  prepared: the GPU cache is first stored
-    prepared (csa_prepare_kv at the entries' positions) and read with kv_prepared; the oracle still takes
-    the raw entries."""
+    """GPU attention against the oracle on the same raw inputs.  prepared (kv_prepared 1 or 2): the GPU
+    cache is first stored prepared (csa_prepare_kv at the entries' positions); with 2 the window rows are
+    stored prepared too, at their token positions.  The oracle always takes the raw rows."""
     q = gen.queries(cfg, hca=hca)
     cache = gen.kv_cache(cfg, hca=hca)
     win = gen.window(cfg, hca=hca)
@@ -313,16 +313,18 @@ def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False, prepared=False):
     gk = rng.uniform(0.5, 1.5, cfg.c).astype(np.float32) if gamma else None
     say(f"{'hca' if hca else 'csa'}_attend {cfg.name} fmt={fmt} B={cfg.B} T={cfg.T} H={cfg.H} c={cfg.c} "
         f"N={cache.shape[1]} gamma={gamma} prepared={prepared}")
-    dcache = dev(cache)
+    dcache, dwin = dev(cache), dev(win)
     if prepared:
         prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base, gamma=dev(gk))
         dcache = api.prepare_kv(dcache, prep, pos_stride=cfg.m_hca if hca else cfg.m)
+    if prepared == 2:   # window row j holds position pos0[b] - n_win + 1 + j
+        dwin = api.prepare_kv(dwin, prep, pos_base=_pos(pos0), pos_first=-(cfg.n_win - 1))
     if hca:
-        out = api.hca_attend(dev(q), dcache, dev(win), dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, cfg.rope_dims,
+        out = api.hca_attend(dev(q), dcache, dwin, dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, cfg.rope_dims,
                              cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk),
                              kv_prepared=prepared)
     else:
-        out = api.attend(dev(q), dcache, dev(idx), dev(win), dev(sink), _pos(pos0), cfg.m, cfg.n_win,
+        out = api.attend(dev(q), dcache, dev(idx), dwin, dev(sink), _pos(pos0), cfg.m, cfg.n_win,
                          cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, gamma_q=dev(gq), gamma_kv=dev(gk),
                          kv_prepared=prepared)
     torch.cuda.synchronize()
@@ -336,7 +338,7 @@ def _attend_case(api, cfg, pos0, idx, hca=False, gamma=False, prepared=False):
     return host_f64(out), ref
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_attend_f32_c1(api, prepared):
     cfg = configs.C1
     rng = np.random.default_rng(1)
@@ -345,7 +347,7 @@ def test_attend_f32_c1(api, prepared):
     assert rel_l2(got, ref) <= F32_TOL
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_attend_bf16_decode(api, prepared):
     cfg = configs.C3.scaled(B=2, n_comp=3000)
     pos0 = [4 * 3000, 4 * 2500 + 1]
@@ -356,7 +358,7 @@ def test_attend_bf16_decode(api, prepared):
     assert e <= LOWP_TOL
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_attend_bf16_prefill(api, prepared):
     cfg = configs.C4.scaled(T=40, n_comp=200, pos0=700, k=64)
     idx = _rand_idx(np.random.default_rng(3), 1, cfg.T, cfg.k, [700], cfg.m, cfg.n_comp)
@@ -379,7 +381,7 @@ def test_attend_bf16_flash_heads_and_small_c(api):
     assert rel_l2(got, ref) <= LOWP_TOL
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_attend_gains(api, prepared):
     cfg = configs.C2.scaled(B=2, n_comp=500, k=64)
     pos0 = [4 * 500, 4 * 123]
@@ -396,14 +398,14 @@ def test_attend_gains(api, prepared):
     assert rel_l2(got, ref) <= F32_TOL
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_hca_attend_f32_c1(api, prepared):
     cfg = configs.C1
     got, ref = _attend_case(api, cfg, [0], None, hca=True, prepared=prepared)
     assert rel_l2(got, ref) <= F32_TOL
 
 
-@pytest.mark.parametrize("prepared", [False, True])
+@pytest.mark.parametrize("prepared", [0, 1, 2])
 def test_hca_attend_bf16_decode_and_prefill(api, prepared):
     cfg = configs.C5.scaled(B=2, n_hca=700)
     pos0 = [128 * 700, 128 * 333 + 5]
