@@ -4,7 +4,8 @@
 One step = one pass of the whole CSA layer step over one decode batch:
   csa_compress_pair (the KV entry that completes at this step, stored prepared
   for attention, and its indexer key, quantized to the cache format)  ->
-  csa_index  ->  csa_topk  ->  csa_attend (prepared compressed entries; decode reads
+  csa_index (decode: also the selector's bound keys)  ->  csa_topk  ->  csa_attend
+  (prepared compressed entries; decode reads
   raw window rows, prefill prepares the chunk's token rows first and reads them prepared)
 (plus, for the workloads with an HCA layer: compress, preparation of the step's
 window rows, hca_attend).
@@ -177,6 +178,9 @@ def main():
         if cfg.with_hca:
             st["phwin"] = api.prepare_kv(st["hwin"], prep, pos_base=pos, pos_first=-(cfg.n_win - 1))
     scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    # decode rows: the indexer also writes the selector's lower-bound keys (two per 256 entries), so top-k
+    # runs as two kernels; the prefill index kernel does not make them (top-k takes its per-row path)
+    bound = api.bound_keys(B, T, N, dev) if T == 1 else None
     idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
     out = torch.empty((B, T, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
     hout = torch.empty_like(out) if cfg.with_hca else None
@@ -218,8 +222,9 @@ def main():
                           c["row0_pos"], first, n_new)
         if csa_mode == 2:
             api.prepare_kv(st["win"][:, cfg.n_win - 1:], prep, out=st["pwin"][:, cfg.n_win - 1:], **win_new)
-        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
-        api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
+        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
+                  bound=bound)
+        api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
                    cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode)
         if side is not None:
@@ -261,7 +266,8 @@ def main():
     # csa_index launch duration: HIP events recorded on the launch stream around back-to-back index
     # launches over the same input rotation, so that the average is the kernel's own time
     def index_only(st):
-        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores)
+        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
+                  bound=bound)
 
     for i in range(NSETS):
         index_only(sets[i])

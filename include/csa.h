@@ -157,6 +157,13 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, in
  *   k       : [B][n_max][cI] in qk_t (MXFP4: cI/2 bytes per row)
  *   k_scale : as q_scale with rows [B][n_max].
  *   scores  : float32 [B][T][n_max]
+ *   bound   : NULL, or uint32 [B][T][csa_index_bound_keys(n_max)], 8-byte aligned:
+ *             for csa_topk, keys of the two largest visible scores of each run of
+ *             256 entries (order-preserving keys, 0 where there are fewer).  Their
+ *             K-th largest never exceeds a row's K-th largest score, so csa_topk
+ *             can skip its threshold search.  Only for the per-row kernels: with
+ *             CSA_F32, or CSA_BF16 with T >= 8 and HI = 64 (the tiled prefill
+ *             kernel), a non-NULL bound is CSA_ERR_UNSUPPORTED.
  * All pointers 16-byte aligned (the MXFP4 q_scale at least 4-byte aligned).
  * Products run on MFMA with float32 accumulation for BF16 / FP8 / MXFP4 (row
  * scales are applied to the float32 dot products; MXFP4 block scales inside
@@ -164,11 +171,12 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, in
  * Limits: F32: cI a multiple of 4, cI <= 512, HI <= 128.  BF16 / FP8 / MXFP4:
  * cI = 128 and HI in {16, 32, 64, 128}.
  */
+int64_t csa_index_bound_keys(int64_t n_max);
 csa_status csa_index(const void* q, const void* q_scale, const float* w,
                      const void* k, const void* k_scale,
                      int B, int T, int HI, int cI, int64_t n_max,
                      const int64_t* pos0, int m, int qk_t,
-                     float* scores, void* stream);
+                     float* scores, uint32_t* bound, void* stream);
 
 /*
  * csa_topk -- top-k selector ([CSA] (2), the C^SprsComp_t equation).
@@ -178,6 +186,11 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  * indices in ascending order followed by -1 padding; vals (nullable) receives
  * their scores (NaN-free inputs assumed; padding slots get -inf).
  *
+ *   bound     : NULL, or the bound keys csa_index wrote for these scores.  With
+ *               them, long rows (the decode case) take two kernels instead of
+ *               four; the result is the same.  Keys that are not a lower bound
+ *               (larger than the scores they stand for) still give the exact
+ *               result, through a slow whole-row pass.
  *   workspace : device memory of csa_topk_workspace_bytes(B, T, n_max, k) bytes
  *               (0 means none is needed).  It must be zero-filled before its
  *               first use.  Every call leaves the part that has to start at zero
@@ -188,7 +201,7 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  */
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k);
 csa_status csa_topk(const float* scores, int B, int T, int64_t n_max,
-                    const int64_t* pos0, int m, int k,
+                    const int64_t* pos0, int m, int k, const uint32_t* bound,
                     int32_t* idx, float* vals,
                     void* workspace, size_t ws_bytes, void* stream);
 

@@ -122,8 +122,14 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
     return tuple(outs)
 
 
-def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None):
-    """csa_index.  q [B][T][HI][row], k [B][N][row]; returns float32 scores [B][T][N]."""
+def bound_keys(B, T, n_max, device):
+    """An int32 buffer [B][T][csa_index_bound_keys(n_max)] for the indexer's bound keys (uint32 bits)."""
+    return torch.empty((B, T, _lib.load().csa_index_bound_keys(n_max)), dtype=torch.int32, device=device)
+
+
+def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None, bound=None):
+    """csa_index.  q [B][T][HI][row], k [B][N][row]; returns float32 scores [B][T][N].  bound: optional
+    buffer from bound_keys() that also receives the selector's lower-bound keys."""
     lib = _lib.load()
     B, T, HI = q.shape[0], q.shape[1], q.shape[2]
     cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
@@ -131,13 +137,14 @@ def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stre
     if scores is None:
         scores = torch.empty((B, T, N), dtype=torch.float32, device=q.device)
     st = lib.csa_index(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), B, T, HI, cI, N, _ptr(pos0), m,
-                       FMT[fmt], _ptr(scores), _stream(stream))
+                       FMT[fmt], _ptr(scores), _ptr(bound), _stream(stream))
     _lib.check(st, "csa_index")
     return scores
 
 
-def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_vals=False):
-    """csa_topk.  Returns (idx int32 [B][T][k], vals float32 or None)."""
+def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_vals=False, bound=None):
+    """csa_topk.  Returns (idx int32 [B][T][k], vals float32 or None).  bound: the keys csa_index wrote
+    for these scores (optional; the same result, fewer kernels on long rows)."""
     lib = _lib.load()
     B, T, N = scores.shape
     dev = scores.device
@@ -148,7 +155,9 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
     nb = lib.csa_topk_workspace_bytes(B, T, N, k)
     if ws is None:
         ws = workspace(nb, dev, "topk", zero=True)
-    st = lib.csa_topk(_ptr(scores), B, T, N, _ptr(pos0), m, k, _ptr(idx), _ptr(vals), _ptr(ws), nb,
+    if bound is not None and tuple(bound.shape) != (B, T, lib.csa_index_bound_keys(N)):
+        raise CSAError(f"topk: bound shape {tuple(bound.shape)} does not match the scores")
+    st = lib.csa_topk(_ptr(scores), B, T, N, _ptr(pos0), m, k, _ptr(bound), _ptr(idx), _ptr(vals), _ptr(ws), nb,
                       _stream(stream))
     _lib.check(st, "csa_topk")
     return idx, vals

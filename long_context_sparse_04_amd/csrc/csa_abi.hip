@@ -22,7 +22,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 2; }
+int csa_abi_version(void) { return 3; }
 
 }  // extern "C"
 
@@ -151,13 +151,20 @@ csa_status check_index(const void* q, const void* q_scale, const float* w, const
 
 extern "C" {
 
+int64_t csa_index_bound_keys(int64_t n_max) { return n_max > 0 ? index_bound_keys(n_max) : 0; }
+
 csa_status csa_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
                      int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, float* scores,
-                     void* stream) {
+                     uint32_t* bound, void* stream) {
   bool empty;
   const csa_status st = check_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, empty);
-  if (st != CSA_OK || empty) return st;
-  return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, (hipStream_t)stream);
+  if (st != CSA_OK) return st;
+  // bound keys come from the per-row decode kernels only
+  if (bound && (qk_t == CSA_F32 || use_prefill_index(qk_t, T, HI))) return CSA_ERR_UNSUPPORTED;
+  if (empty) return CSA_OK;
+  if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
+  return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, bound,
+                      (hipStream_t)stream);
 }
 
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
@@ -166,14 +173,15 @@ size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
 }
 
 csa_status csa_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                    int32_t* idx, float* vals, void* workspace, size_t ws_bytes, void* stream) {
+                    const uint32_t* bound, int32_t* idx, float* vals, void* workspace, size_t ws_bytes,
+                    void* stream) {
   if (B < 0 || T < 0 || n_max < 0 || m < 1 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
   if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
   if (B == 0 || T == 0) return CSA_OK;
   if (!idx || !pos0 || (n_max > 0 && !scores)) return CSA_ERR_NULL;
   const size_t need = csa_topk_workspace_bytes(B, T, n_max > 0 ? n_max : 1, k);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_topk(scores, B, T, n_max, pos0, m, k, idx, vals, workspace, (hipStream_t)stream);
+  return launch_topk(scores, B, T, n_max, pos0, m, k, bound, idx, vals, workspace, (hipStream_t)stream);
 }
 
 static csa_status check_attend(int kv_t, int out_t, int B, int T, int H, int c, int rope_dims, int n_win, int m) {

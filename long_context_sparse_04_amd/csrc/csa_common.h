@@ -79,6 +79,37 @@ CSA_DEV float key_to_score(uint32_t k) {
 }
 
 // ---------------------------------------------------------------- cross-lane helpers
+// The two largest of the union of two disjoint pairs (t1 >= t2, b1 >= b2), kept in (t1, t2).
+CSA_DEV void top2_merge(uint32_t& t1, uint32_t& t2, uint32_t b1, uint32_t b2) {
+  const uint32_t lo = min(t1, b1);
+  t1 = max(t1, b1);
+  t2 = max(lo, max(t2, b2));
+}
+template <int CTRL>
+CSA_DEV uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+// Every lane ends with the two largest keys of the wave's 64 disjoint lane pairs: quad exchanges and
+// row rotations by 4 and 8 inside 16-lane rows, then the gfx950 row-pair and half-wave swaps.
+CSA_DEV void wave_top2(uint32_t& t1, uint32_t& t2) {
+  top2_merge(t1, t2, dpp_u32<0xB1>(t1), dpp_u32<0xB1>(t2));    // quad_perm [1,0,3,2]
+  top2_merge(t1, t2, dpp_u32<0x4E>(t1), dpp_u32<0x4E>(t2));    // quad_perm [2,3,0,1]
+  top2_merge(t1, t2, dpp_u32<0x124>(t1), dpp_u32<0x124>(t2));  // row_ror:4
+  top2_merge(t1, t2, dpp_u32<0x128>(t1), dpp_u32<0x128>(t2));  // row_ror:8
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(t1, t1, false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(t2, t2, false, false);
+    t1 = a[0]; t2 = c[0];
+    top2_merge(t1, t2, a[1], c[1]);
+  }
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap(t1, t1, false, false);
+    const auto c = __builtin_amdgcn_permlane32_swap(t2, t2, false, false);
+    t1 = a[0]; t2 = c[0];
+    top2_merge(t1, t2, a[1], c[1]);
+  }
+}
+
 // DPP row operations act inside 16-lane rows.
 template <int CTRL>
 CSA_DEV float dpp_f32(float v) {

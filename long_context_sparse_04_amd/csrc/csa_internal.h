@@ -34,13 +34,16 @@ csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, int6
                              int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
                              int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream);
 
+// bound keys per query row written by the decode index kernel (two per wave of 256 entries)
+int64_t index_bound_keys(int64_t n_max);
+bool use_prefill_index(int fmt, int T, int HI);
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
-                        float* scores, hipStream_t stream);
+                        float* scores, uint32_t* bound, hipStream_t stream);
 
 size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k);
 csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                       int32_t* idx, float* vals, void* ws, hipStream_t stream);
+                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream);
 
 // mode 0: CSA (index list), mode 1: HCA (dense range)
 size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win);

@@ -100,7 +100,7 @@ template <int FMT, int NT>
 __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
-    const int64_t* __restrict__ pos0, int m, float* __restrict__ scores) {
+    const int64_t* __restrict__ pos0, int m, float* __restrict__ scores, uint32_t* __restrict__ bound) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
   __shared__ __align__(16) uint8_t s_q[HI * RB];  // this query row's HI indexer queries
@@ -177,6 +177,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   // tiles past the visible range are not computed (their scores are -inf)
   const int ntiles = (int)max((int64_t)0, min((int64_t)kTilesPerWave, (vis - wave_first + 15) / 16));
   float p[4];
+  uint32_t top1 = 0u, top2 = 0u;  // this lane's two largest visible score keys (0: none)
 #pragma unroll
   for (int ti = 0; ti < kTilesPerWave; ++ti) {
     const int slot = ti % kSlots;
@@ -207,6 +208,23 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
       const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
       const int64_t eo = eg + lane;  // entry this lane writes
       if (eo < n_max) srow[eo] = (eo < vis) ? val : -INFINITY;
+      if (eo < vis) {
+        const uint32_t key = score_key(val);
+        top2 = max(top2, min(top1, key));
+        top1 = max(top1, key);
+      }
+    }
+  }
+  // Lower-bound keys for the selector: the wave's two largest visible scores.  They are scores of
+  // distinct visible entries, so the K-th largest key over a row's bound keys never exceeds the row's
+  // K-th largest score key.
+  if (bound) {
+    wave_top2(top1, top2);
+    if (lane == 0) {
+      const int64_t nbw = (int64_t)gridDim.x * kWaves * 2;
+      uint32_t* dst = bound + (int64_t)row * nbw + ((int64_t)blockIdx.x * kWaves + wave) * 2;
+      dst[0] = top1;
+      dst[1] = top2;
     }
   }
 }
@@ -380,8 +398,10 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
 
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
-                      int T, int HI, int64_t n_max, const int64_t* pos0, int m, float* scores, hipStream_t stream) {
-  if (FMT == CSA_BF16 && T >= kPRows && HI == 64) {  // many query rows: the tiled contraction
+                      int T, int HI, int64_t n_max, const int64_t* pos0, int m, float* scores, uint32_t* bound,
+                      hipStream_t stream) {
+  if (use_prefill_index(FMT, T, HI)) {  // many query rows: the tiled contraction
+    if (bound) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(T, kPRows), B);
     hipLaunchKernelGGL((index_prefill_bf16_kernel<4>), grid, dim3(kWaves * 64), 0, stream, (const uint8_t*)q, w,
                        (const uint8_t*)k, T, n_max, pos0, m, scores);
@@ -391,7 +411,7 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
   dim3 block(kWaves * 64);
 #define CSA_IDX_LAUNCH(NT)                                                                                  \
   hipLaunchKernelGGL((index_mfma_kernel<FMT, NT>), grid, block, 0, stream, (const uint8_t*)q, q_scale, w, \
-                     (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores)
+                     (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound)
   switch (HI) {
     case 16: CSA_IDX_LAUNCH(1); break;
     case 32: CSA_IDX_LAUNCH(2); break;
@@ -405,11 +425,17 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
 
 }  // namespace
 
+// the tiled prefill kernel serves bf16 queries of many rows with 64 heads
+bool use_prefill_index(int fmt, int T, int HI) { return fmt == CSA_BF16 && T >= kPRows && HI == 64; }
+
+int64_t index_bound_keys(int64_t n_max) { return 2 * kWaves * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG); }
+
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
-                        float* scores, hipStream_t stream) {
+                        float* scores, uint32_t* bound, hipStream_t stream) {
   switch (qk_t) {
     case CSA_F32: {
+      if (bound) return CSA_ERR_UNSUPPORTED;
       dim3 grid(ceil_div(n_max, kF32Threads), B * T);
       size_t lds = (size_t)HI * cI * sizeof(float);
       hipLaunchKernelGGL(index_f32_kernel, grid, dim3(kF32Threads), lds, stream, (const float*)q, w,
@@ -417,11 +443,11 @@ csa_status launch_index(const void* q, const void* q_scale, const float* w, cons
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     }
     case CSA_BF16:
-      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, stream);
+      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
     case CSA_FP8_E4M3_ROWSCALE:
-      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, stream);
+      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
     case CSA_MXFP4_E8M0_B32:
-      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, stream);
+      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
     default:
       return CSA_ERR_UNSUPPORTED;
   }

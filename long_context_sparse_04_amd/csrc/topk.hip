@@ -122,6 +122,51 @@ struct Cand {
   int32_t idx;
 };
 
+// Smallest and largest of the per-thread (lo, hi) over the block; every thread gets both.
+template <int NT>
+CSA_DEV void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* s_mm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) {
+    s_mm[2 * wave] = lo;
+    s_mm[2 * wave + 1] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    lo = min(lo, s_mm[2 * w]);
+    hi = max(hi, s_mm[2 * w + 1]);
+  }
+  __syncthreads();
+}
+
+// Radix step over the keys between lo and hi (inclusive) that agree with pv on their top `known` bits:
+// histogram of the 11 bits ending at `shift` (bits already known among them take one value), and the
+// digit of the need-th largest.  Updates pv (those 11 bits), need (minus the keys above the digit) and
+// known.  get(j) returns the j-th key, j < n.
+template <typename Get>
+CSA_DEV void radix_step(Get get, int n, uint32_t& pv, int& known, int& need, uint32_t* hist, int* s_w, int* s_sel) {
+  const int shift = max(0, 32 - known - 11);
+  for (int j = threadIdx.x; j < kBins; j += kSplitThreads) hist[j] = 0;
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += kSplitThreads) {
+    const uint32_t kk = get(j);
+    if (known == 0 || (kk >> (32 - known)) == (pv >> (32 - known))) atomicAdd(&hist[(kk >> shift) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
+  pv = (pv & ~(0x7FFu << shift)) | ((uint32_t)s_sel[0] << shift);
+  need -= s_sel[1];
+  known = 32 - shift;
+}
+
+// Bits shared by every key in [lo, hi] (lo <= hi), and those bits as a prefix value.
+CSA_DEV int common_bits(uint32_t lo, uint32_t hi) { return lo == hi ? 32 : __clz(lo ^ hi); }
+
 // ------------------------------------------------------------------ row path
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int T,
                                                                int64_t n_max, const int64_t* __restrict__ pos0,
@@ -434,17 +479,82 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const
   if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = base;
 }
 
+// With bound keys from the indexer (two per 256-entry wave, each the key of a distinct visible
+// entry), kernels 1 to 3 become one: every workgroup derives tau, the 22-bit floor of the K-th largest
+// bound key (two digit passes over the row's bound keys), and compacts its chunk's keys >= tau into
+// its segment, in index order.  tau never exceeds the row's K-th largest key, so every selected key is
+// a candidate; typically about 1.1 k keys are.
+__global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const float* __restrict__ scores, int T,
+                                                                           int64_t n_max,
+                                                                           const int64_t* __restrict__ pos0, int m,
+                                                                           int k, const uint32_t* __restrict__ bound,
+                                                                           int nb, SplitWs ws) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ int s_sel[2];
+  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int nch = gridDim.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  if (K == V) return;
+  const float* srow = scores + (int64_t)row * n_max;
+  const int lo = blockIdx.x * kChunk;
+  const int hi = min(lo + kChunk, V);
+  ChunkKeys ck;
+  if (lo < hi) ck = load_chunk(srow, lo, hi, n_max);
+  const uint32_t* brow = bound + (int64_t)row * nb;
+  // tau: the K-th largest bound key with the bits below one 11-bit digit cleared, the digit taken right
+  // under the bits that all bound keys share (so one pass resolves it closely)
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int j = tid; j < nb; j += kSplitThreads) {
+    const uint32_t kk = brow[j];
+    kmin = min(kmin, kk);
+    kmax = max(kmax, kk);
+  }
+  block_minmax<kSplitThreads>(kmin, kmax, s_mm);
+  int known = common_bits(kmin, kmax), need = K;
+  uint32_t tau = kmax;
+  if (known < 32) radix_step([&](int j) { return brow[j]; }, nb, tau, known, need, hist, s_w, s_sel);
+  tau &= known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
+  int base = 0;
+  if (lo < hi) {
+    Cand* seg = ws.seg + (int64_t)row * n_max;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      int mine = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine += (ck.valid[4 * j + q] && ck.key[4 * j + q] >= tau) ? 1 : 0;
+      int tot;
+      int pos = base + block_int_scan<kSplitThreads>(mine, s_w, tot);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * j + q;
+        if (ck.valid[e] && ck.key[e] >= tau) seg[lo + pos++] = Cand{ck.key[e], lo + 1024 * j + 4 * tid + q};
+      }
+      base += tot;
+    }
+  }
+  if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = base;
+}
+
 // Kernel 4: one workgroup per row gathers the segments (chunk order == index order), resolves the
-// last digit among keys with prefix p1, writes the ascending index list, and clears the digit-0
-// histogram of the row.
+// remaining digits of the K-th key among them (the last digit after kernels 1 to 3, all three after
+// the bound collect), and writes the ascending index list.  After kernels 1 to 3 it also clears the
+// digit-0 histogram of the row.  If the candidates are fewer than K (bound keys that were not the
+// indexer's), it selects from the whole visible row instead.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     const float* __restrict__ scores, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
-    int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+    int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws, int bounded) {
   __shared__ Cand s_c[kSegCap];
   __shared__ uint32_t hist[kBins];
   __shared__ int s_w[kSplitThreads / 64];
   __shared__ int s_sel[2];
   __shared__ int s_pre[kMaxChunks + 1];
+  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -465,13 +575,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     }
     return;
   }
-  {  // the digit-0 histogram is no longer needed: leave the workspace zero-filled
+  if (!bounded) {  // the digit-0 histogram is no longer needed: leave the workspace zero-filled
     uint32_t* ghist = ws.hist + (int64_t)row * kBins;
 #pragma unroll
     for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
   }
-  const uint32_t p1 = ws.info[row * 4 + 2];
-  int need = (int)ws.info[row * 4 + 3];
 
   // prefix over chunk counts (chunk order == index order); every load is issued before use
   {
@@ -495,8 +603,9 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     if (tid == 0) s_pre[nch] = tot;
   }
   __syncthreads();
-  const int C = s_pre[nch];
-  const bool in_lds = C <= kSegCap;
+  const bool rescan = bounded && s_pre[nch] < K;  // (uniform) candidates from the whole visible row
+  const int C = rescan ? V : s_pre[nch];
+  const bool in_lds = !rescan && C <= kSegCap;
   auto chunk_of = [&](int j) -> int {  // c with s_pre[c] <= j < s_pre[c+1]
     int lo = 0, hi = nch;
     while (hi - lo > 1) {
@@ -540,19 +649,34 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     }
   }
   __syncthreads();
-  auto cand = [&](int j) -> Cand { return in_lds ? s_c[j] : cand_global(j); };
+  auto cand = [&](int j) -> Cand {
+    if (in_lds) return s_c[j];
+    if (rescan) return Cand{score_key(srow[j]), j};
+    return cand_global(j);
+  };
 
-  // last digit (bits 9..0) among candidates whose top 22 bits equal p1
-  for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
-  __syncthreads();
-  for (int j = tid; j < C; j += kSplitThreads) {
-    uint32_t kk = cand(j).key;
-    if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
+  // the remaining bits of the K-th key among the candidates: after kernels 1 to 3 the top 22 are known;
+  // after the bound collect, those the candidates share, then 11-bit digits below them
+  uint32_t kstar;
+  int need, known;
+  if (bounded) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int j = tid; j < C; j += kSplitThreads) {
+      const uint32_t kk = cand(j).key;
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    }
+    block_minmax<kSplitThreads>(lo, hi, s_mm);
+    kstar = hi;
+    known = common_bits(lo, hi);
+    need = K;
+  } else {
+    kstar = ws.info[row * 4 + 2] << 10;
+    known = 22;
+    need = (int)ws.info[row * 4 + 3];
   }
-  __syncthreads();
-  select_digit<kSplitThreads>(hist, 1024, need, s_w, s_sel);
-  const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
-  const int ties = need - s_sel[1];
+  while (known < 32) radix_step([&](int j) { return cand(j).key; }, C, kstar, known, need, hist, s_w, s_sel);
+  const int ties = need;
   __syncthreads();
 
   // ordered output: thread t owns the contiguous candidates [t*per, (t+1)*per)
@@ -600,20 +724,27 @@ size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
 }
 
 csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                       int32_t* idx, float* vals, void* ws, hipStream_t stream) {
+                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream) {
   const int rows = B * T;
   if (use_split(rows, n_max)) {
     const int nch = ceil_div(n_max, kChunk);
     SplitWs s = carve(ws, rows, n_max, nch);
     dim3 grid(nch, rows);
-    hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m, k,
-                       s);
-    hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
-                       k, s);
-    hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
-                       k, s);
+    // bound keys help only when there are enough of them (a K-th largest well inside their range)
+    const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k;
+    if (bounded) {
+      hipLaunchKernelGGL(topk_bound_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+                         k, bound, (int)index_bound_keys(n_max), s);
+    } else {
+      hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m, k,
+                         s);
+      hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+                         k, s);
+      hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0,
+                         m, k, s);
+    }
     hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0,
-                       m, k, nch, idx, vals, s);
+                       m, k, nch, idx, vals, s, bounded ? 1 : 0);
   } else {
     const int cache = n_max <= kRowKeyCap ? 1 : 0;
     size_t lds = (size_t)kBins * 4 + (cache ? (size_t)n_max * 4 : 0);

@@ -23,7 +23,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+char\s*\*|csa_status|size_t|int)\s+(\w+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+char\s*\*|csa_status|size_t|int64_t|int)\s+(\w+)\s*\(", text, flags=re.M)
     return set(names)
 
 
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -100,23 +100,32 @@ def test_compress_pair_validation(lib):
 
 
 def test_index_topk_attend_validation(lib):
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 64, 1000, DUMMY, 4, 2, DUMMY, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 2, DUMMY, None) == 1
-    assert lib.csa_index(None, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, None) == 1
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, -1, DUMMY, 4, 1, DUMMY, None) == 2
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 64, 1000, DUMMY, 4, 2, DUMMY, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 2, DUMMY, None, None) == 1
+    assert lib.csa_index(None, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, None, None) == 1
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, -1, DUMMY, 4, 1, DUMMY, None, None) == 2
     # top-k
     nb = lib.csa_topk_workspace_bytes(4, 1, 262144, 1024)
     assert nb >= 4 * 262144 * 8
     assert lib.csa_topk_workspace_bytes(1, 4096, 17408, 512) == 0     # row path needs none
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, DUMMY, None, None, 0, None) == 4
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, DUMMY, None, DUMMY, nb - 1, None) == 4
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 0, DUMMY, None, DUMMY, nb, None) == 2
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 4096, DUMMY, None, DUMMY, nb, None) == 2
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, None, 4, 1024, DUMMY, None, DUMMY, nb, None) == 1
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, None, 0, None) == 4
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, DUMMY, nb - 1, None) == 4
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 0, None, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 4096, None, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 4, 1, 262144, None, 4, 1024, None, DUMMY, None, DUMMY, nb, None) == 1
     assert lib.csa_index(DUMMY, C.c_void_p(0x1002), DUMMY, DUMMY, DUMMY, 1, 1, 64, 128, 1000, DUMMY, 4, 3, DUMMY,
-                         None) == 2                 # MXFP4 query scales are read as aligned 32-bit words
+                         None, None) == 2           # MXFP4 query scales are read as aligned 32-bit words
+    # bound keys: two per 256 entries, from the per-row kernels only, 8-byte aligned
+    assert lib.csa_index_bound_keys(262144) == 2048 and lib.csa_index_bound_keys(1000) == 8
+    assert lib.csa_index_bound_keys(0) == 0
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 32, 128, 1000, DUMMY, 4, 0, DUMMY, DUMMY,
+                         None) == 3                 # float32 path: no bound keys
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 4096, 64, 128, 17408, DUMMY, 4, 1, DUMMY, DUMMY,
+                         None) == 3                 # tiled prefill kernel: no bound keys
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY,
+                         C.c_void_p(0x1004), None) == 2
     # attend
     ws = lib.csa_attend_workspace_bytes(4, 1, 128, 512, 1024, 128)
     assert ws > 0 and lib.csa_attend_workspace_bytes(1, 4096, 64, 512, 512, 128) == 0

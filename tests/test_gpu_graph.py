@@ -23,6 +23,7 @@ def test_graph_replay_matches_eager():
     cik, ckv = t(gen.compress_inputs(cfg, indexer=True)), t(gen.compress_inputs(cfg))
     scores = torch.empty((cfg.B, 1, cfg.n_comp), device=DEV)
     idx = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device=DEV)
+    bound = api.bound_keys(cfg.B, 1, cfg.n_comp, DEV)
     out = torch.empty((cfg.B, 1, cfg.H, cfg.c), dtype=torch.bfloat16, device=DEV)
     first = cfg.n_comp - 1
     prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
@@ -32,8 +33,8 @@ def test_graph_replay_matches_eager():
         api.compress_pair(dict(ckv, out=kv[:, first:], out_batch_stride=cfg.n_comp, prep=prep),
                           dict(cik, out=ik[:, first:], out_scale=iks[:, first:], out_fmt="fp8",
                                out_batch_stride=cfg.n_comp), cfg.m, 4 * cfg.n_comp - 8, first, 1)
-        api.index(qd, qs, wd, ik, iks, pos, cfg.m, "fp8", scores=scores)
-        api.topk(scores, pos, cfg.m, cfg.k, idx=idx)
+        api.index(qd, qs, wd, ik, iks, pos, cfg.m, "fp8", scores=scores, bound=bound)
+        api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(q, kv, idx, win, sink, pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, out=out,
                    kv_prepared=True)
 

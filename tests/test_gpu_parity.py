@@ -220,10 +220,57 @@ def test_index_head_counts(api, hi):
     _check_scores(got, ref, absref, 1e-5)
 
 
+def score_keys(x32):
+    """The header's order-preserving uint32 key of float32 scores (+0 and -0 share a key)."""
+    u = np.ascontiguousarray(x32, np.float32).view(np.uint32).copy()
+    u[(u << np.uint32(1)) == 0] = 0
+    neg = (u & np.uint32(0x80000000)) != 0
+    return np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def host_bound(scores32, pos0, m):
+    """Bound keys as csa_index defines them: per run of 256 entries, the keys of its two largest visible
+    scores (0 where the run has fewer visible entries)."""
+    B, T, N = scores32.shape
+    nw = 4 * ((N + 1023) // 1024)
+    out = np.zeros((B, T, 2 * nw), np.uint32)
+    keys = score_keys(scores32)
+    for b in range(B):
+        for r in range(T):
+            vis = min((pos0[b] + r) // m, N)
+            for w in range(nw):
+                kk = np.sort(keys[b, r, 256 * w:min(256 * w + 256, vis)])[::-1]
+                out[b, r, 2 * w:2 * w + min(2, len(kk))] = kk[:2]
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_index_bound_keys(api, fmt):
+    """The indexer's bound keys are the per-256-entry top-2 keys of the scores it wrote, on ragged
+    visibility (a partial last run, rows that see few entries)."""
+    base = {"bf16": configs.C2, "fp8": configs.C3, "mxfp4": configs.C5}[fmt]
+    cfg = base.scaled(B=3, n_comp=9000 + 37)
+    pos0 = [4 * (9000 + 37), 4 * 5001 + 2, 4 * 300 + 3]
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    say(f"index bound keys {cfg.name} fmt={fmt}")
+    bound = api.bound_keys(cfg.B, 1, cfg.n_comp, DEV)
+    sc = api.index(dev(qi["data"]), dev(qi.get("scale")), dev(w), dev(kc["data"]), dev(kc.get("scale")), _pos(pos0),
+                   cfg.m, fmt, bound=bound)
+    torch.cuda.synchronize()
+    got = bound.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, host_bound(sc.cpu().numpy(), pos0, cfg.m))
+
+
 # ----------------------------------------------------------------------------- top-k
-def _topk_case(api, scores32, pos0, m, k, name):
-    say(f"topk {name} shape={scores32.shape} k={k}")
-    idx, vals = api.topk(dev(scores32), _pos(pos0), m, k, want_vals=True)
+def _topk_case(api, scores32, pos0, m, k, name, bound=None):
+    """bound: None (histogram path), "index" (the indexer's definition, computed here from the scores), or
+    an explicit uint32 array."""
+    say(f"topk {name} shape={scores32.shape} k={k} bound={'none' if bound is None else 'given'}")
+    if isinstance(bound, str):
+        bound = host_bound(scores32, pos0, m)
+    bd = None if bound is None else dev(np.ascontiguousarray(bound).view(np.int32))
+    idx, vals = api.topk(dev(scores32), _pos(pos0), m, k, want_vals=True, bound=bd)
     torch.cuda.synchronize()
     ref = oracle.topk(scores32.astype(np.float64), pos0, m, k)
     got = idx.cpu().numpy()
@@ -245,14 +292,31 @@ def test_topk_row_path_c1_scores(api):
     _topk_case(api, ref.astype(np.float32), [0], cfg.m, cfg.k, "c1 oracle scores")
 
 
-def test_topk_split_path_with_ties(api):
+@pytest.mark.parametrize("bound", [None, "index"])
+def test_topk_split_path_with_ties(api, bound):
     rng = np.random.default_rng(11)
     N = 262144
     s = (np.round(rng.standard_normal((4, 1, N)) * 64) / 64).astype(np.float32)  # heavy ties
     s[0, 0, ::7] = 0.0
     s[0, 0, 3::7] = -0.0
     pos0 = [4 * N, 4 * (N - 1000) + 3, 4 * 20000, 4 * N + 100]
-    _topk_case(api, s, pos0, 4, 1024, "split path with ties")
+    _topk_case(api, s, pos0, 4, 1024, "split path with ties", bound)
+
+
+def test_topk_bound_adversarial(api):
+    """With bound keys, rows whose candidate set is large (ascending scores: the largest keys sit in the
+    last runs), a bound of zeros (every visible key a candidate), and keys above the scores (fewer
+    candidates than k: the whole-row selection) all give the exact result."""
+    rng = np.random.default_rng(21)
+    N = 100000
+    s = rng.standard_normal((3, 1, N)).astype(np.float32)
+    s[0, 0] = np.arange(N, dtype=np.float32) / N                   # ascending
+    s[2, 0] = np.round(s[2, 0] * 4) / 4                            # few distinct values
+    pos0 = [4 * N, 4 * N - 1, 4 * (N - 3333)]
+    _topk_case(api, s, pos0, 4, 1024, "bound: ascending / random / coarse", "index")
+    nb = 8 * ((N + 1023) // 1024)
+    _topk_case(api, s, pos0, 4, 1024, "bound of zeros", np.zeros((3, 1, nb), np.uint32))
+    _topk_case(api, s, pos0, 4, 1024, "bound above the scores", np.full((3, 1, nb), 0xFFFFFFF0, np.uint32))
 
 
 def test_topk_workspace_reused_across_shapes(api):
@@ -273,12 +337,15 @@ def test_topk_workspace_reused_across_shapes(api):
         assert np.array_equal(idx.cpu().numpy(), oracle.topk(sc.astype(np.float64), pos0, 4, 256))
 
 
-def test_topk_edge_cases(api):
+@pytest.mark.parametrize("bound", [None, "index"])
+def test_topk_edge_cases(api, bound):
     rng = np.random.default_rng(12)
     N = 40000
     s = rng.standard_normal((3, 1, N)).astype(np.float32)
     s[1, 0, :] = 1.5                          # all equal: candidates overflow the LDS cache
-    _topk_case(api, s, [4 * N, 4 * N, 4 * 100], 4, 2048, "split path edge cases (all-equal, k > V)")
+    _topk_case(api, s, [4 * N, 4 * N, 4 * 100], 4, 2048, "split path edge cases (all-equal, k > V)", bound)
+    if bound is not None:
+        return
     s2 = rng.standard_normal((2, 70, 300)).astype(np.float32)
     s2[1, :, :150] = 0.0
     _topk_case(api, s2, [0, 4 * 299], 4, 1, "row path k=1")
