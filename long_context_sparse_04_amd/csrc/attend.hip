@@ -694,8 +694,10 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float* dst = a.ws_o + (base + h0 + 4 * g + i) * C + dbase + (lane & 15);
+      // streaming stores: read once by the combine, so they are not left dirty in L2 for the end of
+      // the kernel to write back
 #pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) dst[16 * dt] = O[dt][i];
+      for (int dt = 0; dt < DTW; ++dt) __builtin_nontemporal_store(O[dt][i], &dst[16 * dt]);
     }
     if ((WIDE || wave == 0) && g == 0) {
       a.ws_ml[(base + head) * 2 + 0] = M;

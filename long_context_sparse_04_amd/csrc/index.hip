@@ -96,6 +96,58 @@ CSA_DEV f32x4 mfma_tile(const Frag<FMT>& a, const Frag<FMT>& b, int sa, int sb) 
   return acc;
 }
 
+// Tiles in flight per wave (each of 16 entry rows), chosen by measurement; the LDS rings of the staged
+// formats stay small enough for three (bf16) or four (fp8) workgroups per CU.
+template <int FMT>
+struct Ring;
+#ifndef CSA_IDX_RING_BF16
+#define CSA_IDX_RING_BF16 2
+#endif
+#ifndef CSA_IDX_RING_FP8
+#define CSA_IDX_RING_FP8 3
+#endif
+template <>
+struct Ring<CSA_BF16> {
+  static constexpr int kTiles = CSA_IDX_RING_BF16;
+};
+template <>
+struct Ring<CSA_FP8_E4M3_ROWSCALE> {
+  static constexpr int kTiles = CSA_IDX_RING_FP8;
+};
+template <>
+struct Ring<CSA_MXFP4_E8M0_B32> {
+  static constexpr int kTiles = kRing;  // register ring (rows of 64 bytes: see the kernel)
+};
+
+// Swizzle of the 16-byte chunks of an entry row in a staged tile: chunk c of row e sits at position
+// c ^ key(e), which spreads the 8 rows one 128-byte LDS read phase touches over all banks.
+template <int RB>
+CSA_DEV int tile_swz_key(int e) {
+  return RB == 64 ? ((e >> 1) & 3) : (e & 7);
+}
+
+// N 16-byte LDS reads at byte addresses a[0..N) in one block that waits for them (no read outlives the
+// block; outputs early-clobber so that none shares a later read's address register).  Out of the
+// compiler's sight on purpose: for reads of a buffer that global-to-LDS loads also fill, it would wait
+// for every outstanding load first, draining the ring of tiles in flight.
+template <int N>
+CSA_DEV void lds_read16(i32x4 (&o)[N], const uint32_t (&a)[N]) {
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o[0]) : "v"(a[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+  } else {
+    static_assert(N == 4, "1, 2 or 4 reads");
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  }
+}
+
 template <int FMT, int NT>
 __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
@@ -103,9 +155,27 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const int64_t* __restrict__ pos0, int m, float* __restrict__ scores, uint32_t* __restrict__ bound) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
-  __shared__ __align__(16) uint8_t s_q[HI * RB];  // this query row's HI indexer queries
+  constexpr int LB = Fmt<FMT>::kLaneBytes;
+  constexpr int R = Ring<FMT>::kTiles;
+  constexpr int kSlots = R + 1;
+  constexpr int kTileBytes = 16 * RB;
+  constexpr int kDmaPerTile = kTileBytes / 1024;   // 1 KB (16 bytes per lane) per DMA instruction
+  constexpr bool kScaled = FMT != CSA_BF16;
+  // Rows of 128 or 256 bytes are staged through LDS: a lane's operand is 32 or 64 bytes of one row, so
+  // loading it straight into registers would make every load instruction touch half- or quarter-used
+  // 128-byte lines of all 16 rows.  Rows of 64 bytes (MXFP4) load their 16 bytes per lane straight into
+  // registers: one instruction then covers the whole 1 KB tile.
+  constexpr bool kStaged = RB > 64;
+  // The tile rings, slot-major ([slot][wave][tile]).  This query row's HI indexer queries are staged in
+  // the last slot when they fit there: that slot is first filled after the queries sit in registers.
+  constexpr int kRingBytes = kStaged ? kSlots * kWaves * kTileBytes : 0;
+  constexpr bool kQInRing = kStaged && HI * RB <= kWaves * kTileBytes;
+  __shared__ __align__(16) uint8_t s_lds[kRingBytes + (kQInRing ? 0 : HI * RB)];
+  uint8_t (*s_ring)[kWaves][kTileBytes] = reinterpret_cast<uint8_t (*)[kWaves][kTileBytes]>(s_lds);
+  uint8_t* s_q = kQInRing ? &s_lds[R * kWaves * kTileBytes] : &s_lds[kRingBytes];
   __shared__ float s_wq[HI];                      // w (times the fp8 query row scale) per head
   __shared__ uint32_t s_qsc[HI];                  // MXFP4: the 4 E8M0 block scales of each head
+  __shared__ uint32_t s_ksc[kStaged && kScaled ? kWaves : 1][kTilesPerWave * 16];  // key scale word per entry
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -116,30 +186,50 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
   float* srow = scores + (int64_t)row * n_max;
 
-  // wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) tile by tile
-  // through a ring of kRing + 1 tile buffers: the load of tile i + kRing is issued before tile i's
-  // MFMAs, into the buffer tile i - 1 has released, so kRing tiles are always in flight
+  // Wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) tile by tile.
+  // A tile's 16 rows are contiguous in memory and arrive by direct global-to-LDS loads of 1 KB per
+  // instruction (lane i -> bytes [16 i, 16 i + 16) of the instruction's span), into this wave's ring of
+  // R + 1 tile buffers: the load of tile i + R is issued before tile i is used, into the buffer tile
+  // i - 1 has released, so R tiles are always in flight.  The wave reads its MFMA operands back from its
+  // own buffers, so no barrier is involved.
   const uint8_t* kb = kI + (int64_t)b * n_max * RB;
   const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
-  constexpr int kSlots = kRing + 1;
-  Frag<FMT> kf[kSlots];
-  int ksc[kSlots];
-  float ksf[kSlots];
-  auto load_tile = [&](int slot, int64_t e0) {
-    const int64_t e = e0 + (lane & 15);
-    const int64_t el = e < n_max ? e : n_max - 1;
-    kf[slot] = load_frag<FMT>(kb + el * RB, lane);
-    ksc[slot] = 127;
-    ksf[slot] = 1.0f;
-    if constexpr (FMT == CSA_MXFP4_E8M0_B32)
-      ksc[slot] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
-    if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE)
-      ksf[slot] = static_cast<const float*>(k_scale)[(int64_t)b * n_max + el];
-  };
-  // the first kRing tiles go out before anything else (they do not wait for the query position;
-  // past the visible range they are simply not used)
+  Frag<FMT> kf_reg[kStaged ? 1 : kSlots];  // register ring (unstaged rows)
+  int ksc_reg[kStaged ? 1 : kSlots];
+  auto issue_tile = [&](int slot, int64_t e0) {
+    if constexpr (!kStaged) {
+      const int64_t el = min(e0 + (lane & 15), n_max - 1);
+      kf_reg[slot] = load_frag<FMT>(kb + el * RB, lane);
+      ksc_reg[slot] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
+      return;
+    }
 #pragma unroll
-  for (int u = 0; u < kRing; ++u) load_tile(u, wave_first + 16 * u);
+    for (int j = 0; j < kDmaPerTile; ++j) {
+      const int off = 1024 * j + 16 * lane;       // byte offset in the tile (LDS position)
+      const int e = off / RB;                     // tile row
+      const int pos = (off % RB) / 16;            // chunk position in the row
+      const int c = pos ^ tile_swz_key<RB>(e);    // logical chunk stored there
+      const int64_t er = min(e0 + e, n_max - 1);  // rows past the end re-read the last one
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kb + er * RB + 16 * c),
+          (__attribute__((address_space(3))) void*)(&s_ring[slot][wave][1024 * j]), 16, 0, 0);
+    }
+  };
+  // the key scale words of all of the wave's entries (4 bytes each: the fp8 row scale, or the 4 E8M0
+  // block scales of an MXFP4 row), 64 entries per instruction, before any tile
+  if constexpr (kStaged && kScaled) {
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave * 16 / 64; ++j) {
+      const int64_t er = min(wave_first + 64 * j + lane, n_max - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(static_cast<const uint32_t*>(k_scale) + b * n_max + er),
+          (__attribute__((address_space(3))) void*)(&s_ksc[wave][64 * j]), 4, 0, 0);
+    }
+  }
+  // the first R tiles go out before anything else (they do not wait for the query position; past the
+  // visible range they are simply not used)
+#pragma unroll
+  for (int u = 0; u < R; ++u) issue_tile(u, wave_first + 16 * u);
 
   // ---- this row's queries and weights, loaded once per workgroup into LDS
   const int64_t t = pos0[b] + r;
@@ -173,9 +263,12 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) wq[g][i] = s_wq[16 * g + 4 * gl + i];  // head of output row i in this lane
   }
+  if constexpr (kQInRing) __syncthreads();  // every wave holds its queries before slot R is refilled
 
   // tiles past the visible range are not computed (their scores are -inf)
   const int ntiles = (int)max((int64_t)0, min((int64_t)kTilesPerWave, (vis - wave_first + 15) / 16));
+  // this lane's operand chunks in a staged tile: row lane & 15, logical chunks LB/16 * gl .. + LB/16 - 1
+  const int te = lane & 15;
   float p[4];
   uint32_t top1 = 0u, top2 = 0u;  // this lane's two largest visible score keys (0: none)
 #pragma unroll
@@ -183,16 +276,44 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const int slot = ti % kSlots;
     const int u = ti & 3;
     const int64_t e0 = wave_first + (int64_t)ti * 16;
-    if (ti + kRing < ntiles) load_tile((ti + kRing) % kSlots, e0 + 16 * kRing);
+    const bool refill = ti + R < ntiles;
+    if (refill) issue_tile((ti + R) % kSlots, e0 + 16 * R);
     if (ti < ntiles) {
+      Frag<FMT> kf;
+      int ksc = 127;
+      float ksf = 1.0f;
+      if constexpr (!kStaged) {
+        kf = kf_reg[slot];
+        ksc = ksc_reg[slot];
+      } else {
+      // tile ti has landed once at most the R younger tiles' loads are outstanding (loads complete
+      // in order); near the end, once none is
+      if (refill)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(R * kDmaPerTile) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      uint32_t ka[LB / 16];
+#pragma unroll
+      for (int j = 0; j < LB / 16; ++j)
+        ka[j] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_ring[slot][wave][0] +
+                (uint32_t)(te * RB + 16 * (((LB / 16) * gl + j) ^ tile_swz_key<RB>(te)));
+      lds_read16<LB / 16>(kf.v, ka);
+      if constexpr (kScaled) {
+        i32x4 sw[1];
+        const uint32_t sa[1] = {(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&s_ksc[wave][16 * ti + te]};
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(sw[0][0]) : "v"(sa[0]) : "memory");
+        if constexpr (FMT == CSA_MXFP4_E8M0_B32) ksc = (int)(((uint32_t)sw[0][0] >> (8 * gl)) & 0xFFu);
+        if constexpr (FMT == CSA_FP8_E4M3_ROWSCALE) ksf = __int_as_float(sw[0][0]);
+      }
+      }
       float part = 0.0f;
 #pragma unroll
       for (int g = 0; g < NT; ++g) {
-        const f32x4 acc = mfma_tile<FMT>(qa[g], kf[slot], qsc[g], ksc[slot]);
+        const f32x4 acc = mfma_tile<FMT>(qa[g], kf, qsc[g], ksc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wq[g][i], fmaxf(acc[i], 0.0f), part);
       }
-      p[u] = part * ksf[slot];  // the FP8 row scale is positive, so it factors out of every ReLU
+      p[u] = part * ksf;  // the FP8 row scale is positive, so it factors out of every ReLU
     } else {
       p[u] = 0.0f;
     }
