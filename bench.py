@@ -2,7 +2,8 @@
 """Benchmark of the CSA decode layer step on one MI355X.
 
 One step = one pass of the whole CSA layer step over one decode batch:
-  csa_compress_pair (the KV entry that completes at this step, stored prepared
+  csa_compress_index (decode; csa_compress_pair + csa_index for prefill): the KV entry that
+  completes at this step, stored prepared
   for attention, and its indexer key, quantized to the cache format)  ->
   csa_index (decode: also the selector's bound keys)  ->  csa_topk  ->  csa_attend
   (prepared compressed entries; decode reads
@@ -213,17 +214,23 @@ def main():
                 api.hca_attend(st["hq"], hca_cache, st["phwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
                                cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side,
                                kv_prepared=2)
-        # the block's KV entry and its indexer-key entry (quantized to the cache format) in one launch
         c = st["cik"]
-        ik_job = dict(st["cik_t"], out=st["ik"][:, first:], out_batch_stride=N,
-                      out_fmt=fmt if fmt in ("fp8", "mxfp4") else None,
-                      out_scale=st["ik_scale"][:, first:] if fmt in ("fp8", "mxfp4") else None)
-        api.compress_pair(dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep), ik_job, cfg.m,
-                          c["row0_pos"], first, n_new)
-        if csa_mode == 2:
-            api.prepare_kv(st["win"][:, cfg.n_win - 1:], prep, out=st["pwin"][:, cfg.n_win - 1:], **win_new)
-        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
-                  bound=bound)
+        kv_job = dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep)
+        if T == 1:
+            # decode: the block's KV entry and its indexer key (into the key cache) are computed inside the
+            # index launch, by the workgroups that need them first
+            api.compress_index(kv_job, st["cik_t"], cfg.m, c["row0_pos"], first, st["qi"], st["qi_scale"], st["w"],
+                               st["ik"], st["ik_scale"], pos, fmt, scores=scores, bound=bound)
+        else:
+            # prefill: every entry of the chunk, KV entry and indexer key (in the cache format), one launch
+            ik_job = dict(st["cik_t"], out=st["ik"][:, first:], out_batch_stride=N,
+                          out_fmt=fmt if fmt in ("fp8", "mxfp4") else None,
+                          out_scale=st["ik_scale"][:, first:] if fmt in ("fp8", "mxfp4") else None)
+            api.compress_pair(kv_job, ik_job, cfg.m, c["row0_pos"], first, n_new)
+            if csa_mode == 2:
+                api.prepare_kv(st["win"][:, cfg.n_win - 1:], prep, out=st["pwin"][:, cfg.n_win - 1:], **win_new)
+            api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
+                      bound=bound)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
                    cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode)

@@ -179,6 +179,31 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
                      float* scores, uint32_t* bound, void* stream);
 
 /*
+ * csa_compress_index -- one launch for a decode step's compression and index
+ * (T = 1): the same results as csa_compress_pair (job 0: the KV entry, job 1:
+ * the indexer key, one entry first_entry per sequence) followed by csa_index,
+ * where job 1's output is the key cache itself: entry first_entry of k (and
+ * k_scale), stored in qk_t (fp8 with its row scale, MXFP4 with its block
+ * scales, or bf16), read by the index scores of the same launch.
+ *   job 0 : ca0 .. bias_b0, c0, out0 (CSA_F32 / CSA_BF16 rows [B][..][c0] with
+ *           batch stride out_batch_stride0, 0 = 1), prep0 as in csa_compress.
+ *   job 1 : ca1 .. bias_b1 with c = cI.
+ *   shared: B, rows, m (< 64), row0_pos, first_entry (< n_max), in_t, as in
+ *           csa_compress_pair with num_entries = 1.
+ *   index : q .. bound as in csa_index with T = 1 (qk_t CSA_BF16, FP8 or MXFP4).
+ * Each argument group is validated as by the corresponding entry point.
+ */
+csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0, const void* zb0,
+                              const float* bias_a0, const float* bias_b0, int c0, void* out0, int out_t0,
+                              int64_t out_batch_stride0, const csa_kv_prep* prep0,
+                              const void* ca1, const void* cb1, const void* za1, const void* zb1,
+                              const float* bias_a1, const float* bias_b1,
+                              int B, int rows, int m, int64_t row0_pos, int64_t first_entry, int in_t,
+                              const void* q, const void* q_scale, const float* w, void* k, void* k_scale,
+                              int HI, int cI, int64_t n_max, const int64_t* pos0, int qk_t,
+                              float* scores, uint32_t* bound, void* stream);
+
+/*
  * csa_topk -- top-k selector ([CSA] (2), the C^SprsComp_t equation).
  * Row (b, r) keeps the min(k, V) largest of scores[b][r][0 .. V) with
  * V = min(floor((pos0[b] + r)/m), n_max).  Larger score first; equal scores

@@ -31,6 +31,10 @@ SIGNATURES = {
     "csa_compress_pair": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _PREP, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _I, _I64, _PREP, _I, _I, _I, _I64, _I64, _I, _I, _P]),
     "csa_prepare_kv": (_I, [_P, _I64, _P, _I64, _I, _I, _I, _I, _I, _P, _I64, _I64, _PREP, _P]),
+    "csa_compress_index": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _PREP,
+                                _P, _P, _P, _P, _P, _P,
+                                _I, _I, _I, _I64, _I64, _I,
+                                _P, _P, _P, _P, _P, _I, _I, _I64, _P, _I, _P, _P, _P]),
     "csa_index_bound_keys": (_I64, [_I64]),
     "csa_index": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P]),
     "csa_topk_workspace_bytes": (_SZ, [_I, _I, _I64, _I]),

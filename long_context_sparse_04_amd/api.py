@@ -122,6 +122,34 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
     return tuple(outs)
 
 
+def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_scale, pos0, fmt, scores=None,
+                   bound=None, stream=None):
+    """csa_compress_index: compress_pair(p_kv, p_ik) for entry first_entry (one per sequence) and a decode index
+    (T = 1), one launch.  p_kv: dict as in compress_pair (out required, f32 / bf16, optional out_batch_stride,
+    prep); p_ik: the indexer-key streams, whose entry is written into k / k_scale at first_entry.  Returns
+    the scores."""
+    lib = _lib.load()
+    B, rows, c0 = p_kv["ca"].shape
+    in_fmt = _TORCH_FMT[p_kv["ca"].dtype]
+    HI = q.shape[2]
+    cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
+    N = k.shape[1]
+    out0 = p_kv["out"]
+    if scores is None:
+        scores = torch.empty((B, 1, N), dtype=torch.float32, device=q.device)
+    st = lib.csa_compress_index(
+        _ptr(p_kv["ca"]), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]), _ptr(p_kv.get("zb")), _ptr(p_kv["bias_a"]),
+        _ptr(p_kv.get("bias_b")), c0, out0.data_ptr(), FMT[_TORCH_FMT[out0.dtype]], p_kv.get("out_batch_stride", 0),
+        _prep_arg(p_kv.get("prep")),
+        _ptr(p_ik["ca"]), _ptr(p_ik.get("cb")), _ptr(p_ik["za"]), _ptr(p_ik.get("zb")), _ptr(p_ik["bias_a"]),
+        _ptr(p_ik.get("bias_b")),
+        B, rows, m, row0_pos, first_entry, FMT[in_fmt],
+        _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), HI, cI, N, _ptr(pos0), FMT[fmt], _ptr(scores),
+        _ptr(bound), _stream(stream))
+    _lib.check(st, "csa_compress_index")
+    return scores
+
+
 def bound_keys(B, T, n_max, device):
     """An int32 buffer [B][T][csa_index_bound_keys(n_max)] for the indexer's bound keys (uint32 bits)."""
     return torch.empty((B, T, _lib.load().csa_index_bound_keys(n_max)), dtype=torch.int32, device=device)

@@ -5,226 +5,25 @@
 // of its own block and the m b-rows of the previous block (block 0: no b-rows);
 // section 一(三)2(1) gives the HCA form (one stream, m' rows, no overlap).
 //
-// Design: one workgroup (256 threads) per (entry, sequence).  Thread tid owns
-// channel group cg = tid % (c/4) (4 adjacent channels, one 16-byte / 8-byte load
-// per row) and row slice rs = tid / (c/4); each thread runs an online softmax
-// over its rows (branch-free, base-2 exponentials), the slices are merged in LDS
-// in a fixed order, and the rs == 0 threads write the entry (optionally
-// quantized).  Loads are contiguous across the channel groups of a row, so every
-// row read is coalesced.
+// Design: one workgroup (256 threads; 1024 for entries that pool 64 rows or more) per (entry,
+// sequence, job), running the shared body in compress_body.h.
+#include "compress_body.h"
 #include "csa_common.h"
 #include "csa_internal.h"
 
 namespace {
+using namespace csa_compress_body;
 
 constexpr int kThreads = 256;
-
-// Raw 4-channel loads (kept as bits until use, so that a batch of loads has no
-// dependent instruction between them) and their conversion to float32.
-template <typename TIn>
-struct Raw4;
-template <>
-struct Raw4<float> {
-  f32x4 v;
-  CSA_DEV void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
-  CSA_DEV float get(int q) const { return v[q]; }
-};
-template <>
-struct Raw4<uint16_t> {
-  uint2 v;
-  CSA_DEV void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
-  CSA_DEV float get(int q) const {
-    const uint32_t w = (q < 2) ? v.x : v.y;
-    return __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
-  }
-};
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Online softmax state of 4 channels in base-2 units (logits scaled by log2 e).
-struct Soft4 {
-  float mx[4], sm[4], ac[4];
-  CSA_DEV void init() {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { mx[q] = -INFINITY; sm[q] = 0.0f; ac[q] = 0.0f; }
-  }
-  // branch-free update with one row: logit lg2 (finite, base 2) and value v
-  CSA_DEV void add(int q, float lg2, float v) {
-    const float mn = fmaxf(mx[q], lg2);
-    const float sc = __builtin_amdgcn_exp2f(mx[q] - mn);  // 0 while the state is empty
-    const float p = __builtin_amdgcn_exp2f(lg2 - mn);
-    sm[q] = fmaf(sm[q], sc, p);
-    ac[q] = fmaf(ac[q], sc, p * v);
-    mx[q] = mn;
-  }
-};
-
-// One compression problem: its streams, biases, width and output.  A launch serves one or two of
-// them (blockIdx.z), with the same batch, rows, ratio and entries, e.g. a block's KV entry and its
-// indexer-key entry.
-struct Job {
-  const void* ca;
-  const void* cb;
-  const void* za;
-  const void* zb;
-  const float* bias_a;
-  const float* bias_b;
-  int c;
-  void* out;
-  void* out_scale;
-  int out_t;
-  int64_t out_bstride;
-  int prep;            // store the entry prepared for attention (RMSNorm + RoPE at m * i)
-  const float* gamma;
-  float eps;
-  int R;
-};
-struct Jobs {
-  Job j[2];
-  double theta[2][64];  // RoPE frequencies of each job
-};
 
 template <typename TIn, int NT>
 __global__ __launch_bounds__(NT) void compress_kernel(Jobs jobs, int rows, int m, int64_t row0_pos,
                                                             int64_t first_entry) {
   __shared__ f32x4 s_m[NT], s_l[NT], s_a[NT];
   __shared__ float s_red[NT / 64];
-
   const Job jb = blockIdx.z ? jobs.j[1] : jobs.j[0];  // uniform select (no indexed kernel-argument copy)
-  const TIn* __restrict__ ca = static_cast<const TIn*>(jb.ca);
-  const TIn* __restrict__ cb = static_cast<const TIn*>(jb.cb);
-  const TIn* __restrict__ za = static_cast<const TIn*>(jb.za);
-  const TIn* __restrict__ zb = static_cast<const TIn*>(jb.zb);
-  const float* __restrict__ bias_a = jb.bias_a;
-  const float* __restrict__ bias_b = jb.bias_b;
-  const int c = jb.c;
-  void* __restrict__ out = jb.out;
-  void* __restrict__ out_scale = jb.out_scale;
-  const int out_t = jb.out_t;
-  const int64_t out_bstride = jb.out_bstride;
-  const double* theta = jobs.theta[blockIdx.z];
-  const int e = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int ncg = c >> 2;
-  const int nrs = NT / ncg;  // row slices (>= 1 because c <= 1024)
-  const int cg = tid % ncg;
-  const int rs = tid / ncg;
-  const int64_t i = first_entry + e;
-  const bool overlap = (cb != nullptr);
-  const int nrows = (overlap && i > 0) ? 2 * m : m;  // i == 0: the b-side is -inf / 0
-  const int64_t base = (int64_t)b * rows * c;
-
-  Soft4 st;
-  st.init();
-  if (rs < nrs) {
-    // rows of this thread's slice, 4 at a time: loads issued unconditionally (rows past the end
-    // are clamped to a valid row and skipped afterwards)
-    constexpr int kBatch = 4;
-    for (int rr0 = rs; rr0 < nrows; rr0 += kBatch * nrs) {
-      Raw4<TIn> z[kBatch], v[kBatch];
-      f32x4 bb[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int rr = min(rr0 + u * nrs, nrows - 1);
-        const bool is_a = rr < m;
-        const int rw = is_a ? rr : rr - m;
-        const int64_t row = (is_a ? m * i : m * (i - 1)) + rw - row0_pos;
-        z[u].load((is_a ? za : zb) + base + row * c + 4 * cg);
-        v[u].load((is_a ? ca : cb) + base + row * c + 4 * cg);
-        bb[u] = *reinterpret_cast<const f32x4*>((is_a ? bias_a : bias_b) + (int64_t)rw * c + 4 * cg);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (rr0 + u * nrs >= nrows) break;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) st.add(q, (z[u].get(q) + bb[u][q]) * kLog2e, v[u].get(q));
-      }
-    }
-  }
-  s_m[tid] = f32x4{st.mx[0], st.mx[1], st.mx[2], st.mx[3]};
-  s_l[tid] = f32x4{st.sm[0], st.sm[1], st.sm[2], st.sm[3]};
-  s_a[tid] = f32x4{st.ac[0], st.ac[1], st.ac[2], st.ac[3]};
-  __syncthreads();
-
-  // merge the row slices in a fixed order (slice 0 first)
-  float y[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool writer = (tid < ncg);
-  if (writer) {
-    f32x4 M = s_m[cg];
-    for (int sl = 1; sl < nrs; ++sl) {
-      const f32x4 mo = s_m[sl * ncg + cg];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) M[q] = fmaxf(M[q], mo[q]);
-    }
-    float L[4] = {0.f, 0.f, 0.f, 0.f}, A[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int sl = 0; sl < nrs; ++sl) {
-      const f32x4 ms = s_m[sl * ncg + cg], ls = s_l[sl * ncg + cg], as = s_a[sl * ncg + cg];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float f = (ms[q] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms[q] - M[q]);  // empty slice
-        L[q] = fmaf(ls[q], f, L[q]);
-        A[q] = fmaf(as[q], f, A[q]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) y[q] = A[q] / L[q];
-  }
-
-  if (jb.prep) prep_row4<NT>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
-  const int64_t orow = (int64_t)b * out_bstride + e;
-  if (out_t == CSA_F32) {
-    if (writer) *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
-    return;
-  }
-  if (out_t == CSA_BF16) {
-    if (writer) {
-      uint2 o;
-      o.x = pack_bf16x2(y[0], y[1]);
-      o.y = pack_bf16x2(y[2], y[3]);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + orow * c + 4 * cg) = o;
-    }
-    return;
-  }
-  if (out_t == CSA_FP8_E4M3_ROWSCALE) {
-    // row amax over all c channels: wave maxima, then the block maximum through LDS
-    float am = writer ? fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))) : 0.0f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    if ((tid & 63) == 0) s_red[tid >> 6] = am;
-    __syncthreads();
-    am = s_red[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) am = fmaxf(am, s_red[w]);
-    const float scale = am / 448.0f;
-    if (writer) {
-      uint32_t pk = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pk |= f32_to_e4m3(scale > 0.0f ? y[q] / scale : 0.0f) << (8 * q);
-      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + orow * c + 4 * cg) = pk;
-      if (tid == 0) static_cast<float*>(out_scale)[orow] = scale;
-    }
-    return;
-  }
-  // CSA_MXFP4_E8M0_B32: 8 channel groups (32 channels) share one E8M0 scale
-  if (writer) {
-    float am = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3])));
-    am = fmaxf(am, __shfl_xor(am, 1, 8));
-    am = fmaxf(am, __shfl_xor(am, 2, 8));
-    am = fmaxf(am, __shfl_xor(am, 4, 8));
-    int X = -127;
-    if (am > 0.0f) {
-      int ex;
-      frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
-      X = ex - 1 - 2;
-      X = X < -127 ? -127 : (X > 127 ? 127 : X);
-    }
-    uint32_t codes = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) codes |= f32_to_e2m1(ldexpf(y[q], -X)) << (4 * q);
-    *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(out) + orow * (c / 2) + 2 * cg) = (uint16_t)codes;
-    if ((cg & 7) == 0) static_cast<uint8_t*>(out_scale)[orow * (c / 32) + cg / 8] = (uint8_t)(X + 127);
-  }
+  compress_one<TIn, NT>(jb, jobs.theta[blockIdx.z], blockIdx.x, blockIdx.y, rows, m, row0_pos, first_entry, s_m,
+                        s_l, s_a, s_red);
 }
 
 }  // namespace
@@ -237,9 +36,7 @@ csa_status launch_compress(const void* ca, const void* cb, const void* za, const
   return launch_compress_jobs(&j, 1, B, rows, m, row0_pos, first_entry, num_entries, in_t, stream);
 }
 
-csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
-                                int64_t first_entry, int num_entries, int in_t, hipStream_t stream) {
-  Jobs js;
+void csa_compress_body::fill_jobs(const CompressJob* jobs, int njobs, Jobs& js) {
   for (int i = 0; i < njobs; ++i) {
     const csa_kv_prep* pp = jobs[i].prep;
     js.j[i] = Job{jobs[i].ca, jobs[i].cb, jobs[i].za, jobs[i].zb, jobs[i].bias_a, jobs[i].bias_b, jobs[i].c,
@@ -248,6 +45,12 @@ csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int r
     const RopeTable rt = make_rope_table(pp ? pp->rope_dims : 0, pp ? pp->rope_base : 1.0f);
     for (int t = 0; t < 64; ++t) js.theta[i][t] = rt.theta[t];
   }
+}
+
+csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
+                                int64_t first_entry, int num_entries, int in_t, hipStream_t stream) {
+  Jobs js;
+  fill_jobs(jobs, njobs, js);
   dim3 grid(num_entries, B, njobs);
   // an entry that pools many rows (HCA: m' = 128) gets 1024 threads, so that each thread walks few rows;
   // the choice depends on m only, so an entry's result does not depend on the batch

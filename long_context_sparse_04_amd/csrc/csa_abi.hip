@@ -167,6 +167,41 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w, const v
                       (hipStream_t)stream);
 }
 
+csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0, const void* zb0,
+                              const float* bias_a0, const float* bias_b0, int c0, void* out0, int out_t0,
+                              int64_t out_batch_stride0, const csa_kv_prep* prep0, const void* ca1, const void* cb1,
+                              const void* za1, const void* zb1, const float* bias_a1, const float* bias_b1, int B,
+                              int rows, int m, int64_t row0_pos, int64_t first_entry, int in_t, const void* q,
+                              const void* q_scale, const float* w, void* k, void* k_scale, int HI, int cI,
+                              int64_t n_max, const int64_t* pos0, int qk_t, float* scores, uint32_t* bound,
+                              void* stream) {
+  if (qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3_ROWSCALE && qk_t != CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
+  if (m >= 64) return CSA_ERR_UNSUPPORTED;  // one 256-thread workgroup pools an entry's rows
+  if (n_max < 1 || first_entry < 0 || first_entry >= n_max) return CSA_ERR_SHAPE;
+  bool empty;
+  csa_status st = check_index(q, q_scale, w, k, k_scale, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, empty);
+  if (st != CSA_OK) return st;
+  if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
+  // the indexer key is written into the key cache at first_entry (row stride n_max per sequence)
+  const int64_t krow = qk_t == CSA_BF16 ? 2 * (int64_t)cI : (qk_t == CSA_FP8_E4M3_ROWSCALE ? cI : cI / 2);
+  const int64_t srow = qk_t == CSA_FP8_E4M3_ROWSCALE ? 4 : (qk_t == CSA_MXFP4_E8M0_B32 ? cI / 32 : 0);
+  void* out1 = k ? static_cast<uint8_t*>(k) + first_entry * krow : nullptr;
+  void* out_scale1 = k_scale ? static_cast<uint8_t*>(k_scale) + first_entry * srow : nullptr;
+  int64_t bs0 = out_batch_stride0, bs1 = n_max;
+  bool e0, e1;
+  st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry, 1, in_t, out0,
+                      nullptr, out_t0, bs0, prep0, e0);
+  if (st != CSA_OK) return st;
+  if (out_t0 != CSA_F32 && out_t0 != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  st = check_compress(ca1, cb1, za1, zb1, bias_a1, bias_b1, B, rows, cI, m, row0_pos, first_entry, 1, in_t, out1,
+                      out_scale1, qk_t, bs1, nullptr, e1);
+  if (st != CSA_OK || e0 || empty) return st;
+  const CompressJob jobs[2] = {{ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, nullptr, out_t0, bs0, prep0},
+                               {ca1, cb1, za1, zb1, bias_a1, bias_b1, cI, out1, out_scale1, qk_t, bs1, nullptr}};
+  return launch_compress_index(jobs, rows, m, row0_pos, first_entry, in_t, q, q_scale, w, k, k_scale, B, HI, cI,
+                               n_max, pos0, qk_t, scores, bound, (hipStream_t)stream);
+}
+
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
   if (B <= 0 || T <= 0 || n_max <= 0 || k <= 0) return 0;
   return topk_workspace_bytes(B, T, n_max, k);

@@ -19,6 +19,9 @@
 // Row scales of the FP8 format are applied to the float32 dot products
 // (w*sigma_q folded per head, sigma_k after the head sum, both positive);
 // MXFP4 block scales are operands of the scaled MFMA.
+#include <type_traits>
+
+#include "compress_body.h"
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -148,11 +151,22 @@ CSA_DEV void lds_read16(i32x4 (&o)[N], const uint32_t (&a)[N]) {
   }
 }
 
-template <int FMT, int NT>
+// The compression launch folded into a decode index launch: the step's new KV entry and indexer key of
+// every sequence (entry first_entry), computed by the workgroup whose entry range holds the new key
+// (before it reads any tile, so its scores see the new key) and by workgroup 0 (the KV entry).
+struct IndexFuse {
+  csa_compress_body::Jobs jobs;  // j[0]: the KV entry, j[1]: the indexer key, written into the key cache
+  int rows, m, in_t;
+  int64_t row0_pos, first_entry;
+};
+struct NoFuse {};
+
+template <int FMT, int NT, bool FUSE>
 __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
-    const int64_t* __restrict__ pos0, int m, float* __restrict__ scores, uint32_t* __restrict__ bound) {
+    const int64_t* __restrict__ pos0, int m, float* __restrict__ scores, uint32_t* __restrict__ bound,
+    std::conditional_t<FUSE, IndexFuse, NoFuse> fz) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
   constexpr int LB = Fmt<FMT>::kLaneBytes;
@@ -185,6 +199,38 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   const int r = row - b * T;
   const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
   float* srow = scores + (int64_t)row * n_max;
+
+  if constexpr (FUSE) {  // decode rows only (row == b)
+    constexpr int kScratch = 3 * 256;  // f32x4 slots of the compression's slice merge
+    constexpr bool kInLds = sizeof(s_lds) >= kScratch * sizeof(f32x4);
+    __shared__ __align__(16) f32x4 s_cz[kInLds ? 1 : kScratch];
+    __shared__ float s_czr[4];
+    f32x4* cz = kInLds ? reinterpret_cast<f32x4*>(s_lds) : s_cz;
+    const bool do_ik = (int64_t)blockIdx.x == fz.first_entry / kEntriesPerWG;
+    const bool do_kv = blockIdx.x == 0;
+    if (do_ik) {
+      if (fz.in_t == CSA_F32)
+        csa_compress_body::compress_one<float, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, row, fz.rows, fz.m,
+                                                    fz.row0_pos, fz.first_entry, cz, cz + 256, cz + 512, s_czr);
+      else
+        csa_compress_body::compress_one<uint16_t, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, row, fz.rows, fz.m,
+                                                       fz.row0_pos, fz.first_entry, cz, cz + 256, cz + 512, s_czr);
+    }
+    if (do_ik && do_kv) __syncthreads();  // the slice-merge scratch is used again
+    if (do_kv) {
+      if (fz.in_t == CSA_F32)
+        csa_compress_body::compress_one<float, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, row, fz.rows, fz.m,
+                                                    fz.row0_pos, fz.first_entry, cz, cz + 256, cz + 512, s_czr);
+      else
+        csa_compress_body::compress_one<uint16_t, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, row, fz.rows, fz.m,
+                                                       fz.row0_pos, fz.first_entry, cz, cz + 256, cz + 512, s_czr);
+    }
+    if (do_ik || do_kv) {
+      // the new key is in memory (L2) before this workgroup reads any tile, and the scratch is free
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  }
 
   // Wave w streams the contiguous entries [wave_first, wave_first + 16 * kTilesPerWave) tile by tile.
   // A tile's 16 rows are contiguous in memory and arrive by direct global-to-LDS loads of 1 KB per
@@ -520,9 +566,9 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
                       int T, int HI, int64_t n_max, const int64_t* pos0, int m, float* scores, uint32_t* bound,
-                      hipStream_t stream) {
+                      const IndexFuse* fuse, hipStream_t stream) {
   if (use_prefill_index(FMT, T, HI)) {  // many query rows: the tiled contraction
-    if (bound) return CSA_ERR_UNSUPPORTED;
+    if (bound || fuse) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(T, kPRows), B);
     hipLaunchKernelGGL((index_prefill_bf16_kernel<4>), grid, dim3(kWaves * 64), 0, stream, (const uint8_t*)q, w,
                        (const uint8_t*)k, T, n_max, pos0, m, scores);
@@ -530,9 +576,13 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
   }
   dim3 grid(ceil_div(n_max, kEntriesPerWG), B * T);
   dim3 block(kWaves * 64);
-#define CSA_IDX_LAUNCH(NT)                                                                                  \
-  hipLaunchKernelGGL((index_mfma_kernel<FMT, NT>), grid, block, 0, stream, (const uint8_t*)q, q_scale, w, \
-                     (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound)
+#define CSA_IDX_LAUNCH(NT)                                                                                       \
+  if (fuse)                                                                                                     \
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, w, \
+                       (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound, *fuse);                    \
+  else                                                                                                          \
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false>), grid, block, 0, stream, (const uint8_t*)q, q_scale,  \
+                       w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound, NoFuse{})
   switch (HI) {
     case 16: CSA_IDX_LAUNCH(1); break;
     case 32: CSA_IDX_LAUNCH(2); break;
@@ -551,12 +601,40 @@ bool use_prefill_index(int fmt, int T, int HI) { return fmt == CSA_BF16 && T >= 
 
 int64_t index_bound_keys(int64_t n_max) { return 2 * kWaves * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG); }
 
+static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
+                                    const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
+                                    const int64_t* pos0, int m, int qk_t, float* scores, uint32_t* bound,
+                                    const IndexFuse* fuse, hipStream_t stream);
+
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
                         float* scores, uint32_t* bound, hipStream_t stream) {
+  return launch_index_impl(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, bound, nullptr,
+                           stream);
+}
+
+csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64_t row0_pos, int64_t first_entry,
+                                 int in_t, const void* q, const void* q_scale, const float* w, const void* k,
+                                 const void* k_scale, int B, int HI, int cI, int64_t n_max, const int64_t* pos0,
+                                 int qk_t, float* scores, uint32_t* bound, hipStream_t stream) {
+  IndexFuse fz;
+  csa_compress_body::fill_jobs(jobs, 2, fz.jobs);
+  fz.rows = rows;
+  fz.m = m;
+  fz.in_t = in_t;
+  fz.row0_pos = row0_pos;
+  fz.first_entry = first_entry;
+  return launch_index_impl(q, q_scale, w, k, k_scale, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, bound, &fz,
+                           stream);
+}
+
+static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
+                                    const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
+                                    const int64_t* pos0, int m, int qk_t, float* scores, uint32_t* bound,
+                                    const IndexFuse* fuse, hipStream_t stream) {
   switch (qk_t) {
     case CSA_F32: {
-      if (bound) return CSA_ERR_UNSUPPORTED;
+      if (bound || fuse) return CSA_ERR_UNSUPPORTED;
       dim3 grid(ceil_div(n_max, kF32Threads), B * T);
       size_t lds = (size_t)HI * cI * sizeof(float);
       hipLaunchKernelGGL(index_f32_kernel, grid, dim3(kF32Threads), lds, stream, (const float*)q, w,
@@ -564,11 +642,11 @@ csa_status launch_index(const void* q, const void* q_scale, const float* w, cons
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     }
     case CSA_BF16:
-      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
+      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
     case CSA_FP8_E4M3_ROWSCALE:
-      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
+      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
     case CSA_MXFP4_E8M0_B32:
-      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, stream);
+      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
     default:
       return CSA_ERR_UNSUPPORTED;
   }

@@ -126,6 +126,18 @@ def test_index_topk_attend_validation(lib):
                          None) == 3                 # tiled prefill kernel: no bound keys
     assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY,
                          C.c_void_p(0x1004), None) == 2
+    # compress_index: the MFMA formats only, entries of m < 64 rows, the new entry inside the cache
+    def ci(**kw):
+        a = dict(m=4, first=1023, n=1024, qk=2, q=DUMMY, rows=8, r0=4088)
+        a.update(kw)
+        return lib.csa_compress_index(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 512, DUMMY, 1, 0, None,
+                                      DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, a["rows"], a["m"], a["r0"],
+                                      a["first"], 1, a["q"], DUMMY, DUMMY, DUMMY, DUMMY, 64, 128, a["n"], DUMMY,
+                                      a["qk"], DUMMY, None, None)
+    assert ci(qk=0) == 3 and ci(m=128) == 3
+    assert ci(first=1024) == 2 and ci(first=-1) == 2
+    assert ci(q=None) == 1
+    assert ci(r0=4096) == 2                   # the entry reads rows before row0_pos
     # attend
     ws = lib.csa_attend_workspace_bytes(4, 1, 128, 512, 1024, 128)
     assert ws > 0 and lib.csa_attend_workspace_bytes(1, 4096, 64, 512, 512, 128) == 0

@@ -169,12 +169,11 @@ def test_decode_step_full_size(api, name):
     api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)     # the context cache, stored prepared
     first = N - 1
     d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
-    api.compress_pair(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N, prep=prep),
-                      dict(d(cik), out=ik[:, first:], out_batch_stride=N, out_fmt=fmt if fmt != "bf16" else None,
-                           out_scale=None if ik_scale is None else ik_scale[:, first:]),
-                      ckv["m"], ckv["row0_pos"], first, 1)
-    bound = api.bound_keys(B, 1, N, DEV)   # as the benchmark: the selector takes the indexer's bound keys
-    scores = api.index(dev(qi["data"]), dev(qi.get("scale")), dev(w), ik, ik_scale, pos, cfg.m, fmt, bound=bound)
+    # as the benchmark: compression folded into the index launch, the selector takes its bound keys
+    bound = api.bound_keys(B, 1, N, DEV)
+    scores = api.compress_index(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N, prep=prep), d(cik),
+                                ckv["m"], ckv["row0_pos"], first, dev(qi["data"]), dev(qi.get("scale")), dev(w), ik,
+                                ik_scale, pos, fmt, bound=bound)
     idx, _ = api.topk(scores, pos, cfg.m, cfg.k, bound=bound)
     out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
                           cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)

@@ -29,11 +29,9 @@ def test_graph_replay_matches_eager():
     prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
     api.prepare_kv(kv, prep, pos_stride=cfg.m, out=kv)
 
-    def step():  # the benchmark's step: one launch for both compressed entries, prepared KV cache
-        api.compress_pair(dict(ckv, out=kv[:, first:], out_batch_stride=cfg.n_comp, prep=prep),
-                          dict(cik, out=ik[:, first:], out_scale=iks[:, first:], out_fmt="fp8",
-                               out_batch_stride=cfg.n_comp), cfg.m, 4 * cfg.n_comp - 8, first, 1)
-        api.index(qd, qs, wd, ik, iks, pos, cfg.m, "fp8", scores=scores, bound=bound)
+    def step():  # the benchmark's step: compression folded into the index launch, prepared KV cache
+        api.compress_index(dict(ckv, out=kv[:, first:], out_batch_stride=cfg.n_comp, prep=prep), cik, cfg.m,
+                           4 * cfg.n_comp - 8, first, qd, qs, wd, ik, iks, pos, "fp8", scores=scores, bound=bound)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(q, kv, idx, win, sink, pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale, out=out,
                    kv_prepared=True)

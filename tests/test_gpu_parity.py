@@ -142,6 +142,47 @@ def test_compress_pair_matches_two_calls(api, name, fmt):
     assert torch.count_nonzero(bits(cache[:, 3 + n:]).to(torch.int32)) == 0
 
 
+@pytest.mark.parametrize("name,n_comp", [("c3", 5037), ("c3", 600), ("c5", 3100), ("c2", 1500)])
+def test_compress_index_matches_separate_launches(api, name, n_comp):
+    """csa_compress_index writes the same KV entry, key-cache entry (and scales), scores and bound keys as
+    csa_compress_pair followed by csa_index, bit for bit; the new entry in the last workgroup's range
+    (ragged) and in workgroup 0's, which also computes the KV entry."""
+    cfg = configs.get_config(name).scaled(B=3, n_comp=n_comp)
+    fmt, N = cfg.idx_dtype, cfg.n_comp
+    say(f"compress_index {cfg.name} fmt={fmt} N={N}")
+    ckv, cik = gen.compress_inputs(cfg), gen.compress_inputs(cfg, indexer=True)
+    first, r0p = N - 1, 4 * N - 8   # the last entry of this cache, from the block's 8 rows
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    pos0 = [4 * N, 4 * N + 3, 4 * (N - 100)]
+    d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    kv0 = dev(gen.kv_cache(cfg))
+    outs = []
+    for fused in (False, True):
+        kv, ik = kv0.clone(), dev(kc["data"])
+        iks = dev(kc.get("scale"))
+        bound = api.bound_keys(cfg.B, 1, N, DEV)
+        qd, qs, wd = dev(qi["data"]), dev(qi.get("scale")), dev(w)
+        pkv = dict(d(ckv), out=kv[:, first:], out_batch_stride=N, prep=prep)
+        if fused:
+            sc = api.compress_index(pkv, d(cik), cfg.m, r0p, first, qd, qs, wd, ik, iks, _pos(pos0), fmt,
+                                    bound=bound)
+        else:
+            api.compress_pair(pkv, dict(d(cik), out=ik[:, first:], out_batch_stride=N,
+                                        out_scale=None if iks is None else iks[:, first:],
+                                        out_fmt=None if fmt == "bf16" else fmt), cfg.m, r0p, first, 1)
+            sc = api.index(qd, qs, wd, ik, iks, _pos(pos0), cfg.m, fmt, bound=bound)
+        torch.cuda.synchronize()
+        outs.append((kv, ik, iks, sc, bound))
+    bits = lambda t: None if t is None else (t.view(torch.int16) if t.dtype == torch.bfloat16 else
+                                            t.contiguous().view(torch.uint8))
+    for a_, b_ in zip(*outs):
+        if a_ is None:
+            continue
+        assert torch.equal(bits(a_), bits(b_))
+
+
 def test_compress_into_cache_with_stride(api):
     cfg = configs.C2.scaled(B=3)
     ci = gen.compress_inputs(cfg)
