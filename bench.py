@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--config", default="c3", help="c3 (default), c2 or c5 (decode), c4 (chunked prefill)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--eager", action="store_true", help="launch the step's calls one by one (no HIP graph)")
+    p.add_argument("--scores", default="f32", choices=("f32", "bf16"),
+                   help="index-score storage between the indexer and the selector (bf16: the rounded variant)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -178,7 +180,7 @@ def main():
             else st["win"]
         if cfg.with_hca:
             st["phwin"] = api.prepare_kv(st["hwin"], prep, pos_base=pos, pos_first=-(cfg.n_win - 1))
-    scores = torch.empty((B, T, N), dtype=torch.float32, device=dev)
+    scores = torch.empty((B, T, N), dtype=torch.bfloat16 if a.scores == "bf16" else torch.float32, device=dev)
     # decode rows: the indexer also writes the selector's lower-bound keys (two per 256 entries), so top-k
     # runs as two kernels; the prefill index kernel does not make them (top-k takes its per-row path)
     bound = api.bound_keys(B, T, N, dev) if T == 1 else None
@@ -288,10 +290,10 @@ def main():
     idx_ms = e0.elapsed_time(e1) / a.steps
 
     # algorithmic bytes of one csa_index launch: every K^I row (+ its scales) read once, the queries /
-    # weights read once per query row, one float32 score written per (row, entry)
+    # weights read once per query row, one score (float32 or bf16) written per (row, entry)
     row_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt]
     q_bytes = row_bytes * cfg.HI + 4 * cfg.HI
-    idx_bytes = B * (N * row_bytes + T * q_bytes + T * N * 4)
+    idx_bytes = B * (N * row_bytes + T * q_bytes + T * N * scores.element_size())
     # algorithmic FLOPs: 2 HI cI per visible (row, entry) pair
     pairs = sum(min((cfg.pos0 + r) // cfg.m, N) for r in range(T)) * B
     idx_flops = 2 * cfg.HI * cfg.cI * pairs
@@ -299,7 +301,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
     if os.path.exists(tpath):
         t = json.load(open(tpath))
-        if t.get("source_hash") == source_hash("index.hip"):
+        if t.get("source_hash") == source_hash("index.hip") and t.get("index_scores", "f32") == a.scores:
             traffic = t.get("hbm_bytes_per_launch")
     if prefill:   # a dense contraction with K^I reused across 4,096 query rows: MFMA-bound
         achieved = idx_flops / (idx_ms * 1e-3) / 1e12
@@ -334,7 +336,8 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "query_rows": T, "context": cfg.pos0, "compressed_entries": N,
                    "heads": cfg.H,
                    "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
-                   "hca_entries": cfg.n_hca if cfg.with_hca else 0, "input_sets_rotated": NSETS},
+                   "hca_entries": cfg.n_hca if cfg.with_hca else 0, "index_scores": a.scores,
+                   "input_sets_rotated": NSETS},
         "roofline": roofline,
         "setup_s": round(t_setup, 1),
         "launch": "eager" if a.eager else "hip_graph (one graph per rotated input set)",

@@ -156,10 +156,12 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, in
  *   w       : float32 [B][T][HI]
  *   k       : [B][n_max][cI] in qk_t (MXFP4: cI/2 bytes per row)
  *   k_scale : as q_scale with rows [B][n_max].
- *   scores  : float32 [B][T][n_max]
+ *   scores  : [B][T][n_max] in score_t: CSA_F32, or CSA_BF16 (rounded to nearest
+ *             even; the selector reads half the bytes)
  *   bound   : NULL, or uint32 [B][T][csa_index_bound_keys(n_max)], 8-byte aligned:
- *             for csa_topk, keys of the two largest visible scores of each run of
- *             256 entries (order-preserving keys, 0 where there are fewer).  Their
+ *             for csa_topk, keys of the two largest visible scores (as stored, in
+ *             score_t) of each run of 256 entries (order-preserving keys, 0 where
+ *             there are fewer).  Their
  *             K-th largest never exceeds a row's K-th largest score, so csa_topk
  *             can skip its threshold search.  Only for the per-row kernels: with
  *             CSA_F32, or CSA_BF16 with T >= 8 and HI = 64 (the tiled prefill
@@ -176,7 +178,7 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
                      const void* k, const void* k_scale,
                      int B, int T, int HI, int cI, int64_t n_max,
                      const int64_t* pos0, int m, int qk_t,
-                     float* scores, uint32_t* bound, void* stream);
+                     void* scores, int score_t, uint32_t* bound, void* stream);
 
 /*
  * csa_compress_index -- one launch for a decode step's compression and index
@@ -190,7 +192,8 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  *   job 1 : ca1 .. bias_b1 with c = cI.
  *   shared: B, rows, m (< 64), row0_pos, first_entry (< n_max), in_t, as in
  *           csa_compress_pair with num_entries = 1.
- *   index : q .. bound as in csa_index with T = 1 (qk_t CSA_BF16, FP8 or MXFP4).
+ *   index : q .. bound as in csa_index with T = 1 (qk_t CSA_BF16, FP8 or MXFP4;
+ *           scores in score_t).
  * Each argument group is validated as by the corresponding entry point.
  */
 csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0, const void* zb0,
@@ -201,7 +204,7 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
                               int B, int rows, int m, int64_t row0_pos, int64_t first_entry, int in_t,
                               const void* q, const void* q_scale, const float* w, void* k, void* k_scale,
                               int HI, int cI, int64_t n_max, const int64_t* pos0, int qk_t,
-                              float* scores, uint32_t* bound, void* stream);
+                              void* scores, int score_t, uint32_t* bound, void* stream);
 
 /*
  * csa_topk -- top-k selector ([CSA] (2), the C^SprsComp_t equation).
@@ -209,7 +212,9 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
  * V = min(floor((pos0[b] + r)/m), n_max).  Larger score first; equal scores
  * (+0 and -0 are equal) go to the lower index.  idx[b][r][0..k) receives the kept
  * indices in ascending order followed by -1 padding; vals (nullable) receives
- * their scores (NaN-free inputs assumed; padding slots get -inf).
+ * their scores (NaN-free inputs assumed; padding slots get -inf).  scores are
+ * float32 or bf16 (score_t CSA_F32 / CSA_BF16), as csa_index wrote them; a bf16
+ * score is compared by its exact float32 value.
  *
  *   bound     : NULL, or the bound keys csa_index wrote for these scores.  With
  *               them, long rows (the decode case) take two kernels instead of
@@ -225,7 +230,7 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
  * Limits: 1 <= k <= 2048, n_max < 2^31.
  */
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k);
-csa_status csa_topk(const float* scores, int B, int T, int64_t n_max,
+csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max,
                     const int64_t* pos0, int m, int k, const uint32_t* bound,
                     int32_t* idx, float* vals,
                     void* workspace, size_t ws_bytes, void* stream);

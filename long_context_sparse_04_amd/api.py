@@ -123,7 +123,7 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
 
 
 def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_scale, pos0, fmt, scores=None,
-                   bound=None, stream=None):
+                   bound=None, stream=None, score_fmt="f32"):
     """csa_compress_index: compress_pair(p_kv, p_ik) for entry first_entry (one per sequence) and a decode index
     (T = 1), one launch.  p_kv: dict as in compress_pair (out required, f32 / bf16, optional out_batch_stride,
     prep); p_ik: the indexer-key streams, whose entry is written into k / k_scale at first_entry.  Returns
@@ -136,7 +136,7 @@ def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_sca
     N = k.shape[1]
     out0 = p_kv["out"]
     if scores is None:
-        scores = torch.empty((B, 1, N), dtype=torch.float32, device=q.device)
+        scores = _score_buf(B, 1, N, score_fmt, q.device)
     st = lib.csa_compress_index(
         _ptr(p_kv["ca"]), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]), _ptr(p_kv.get("zb")), _ptr(p_kv["bias_a"]),
         _ptr(p_kv.get("bias_b")), c0, out0.data_ptr(), FMT[_TORCH_FMT[out0.dtype]], p_kv.get("out_batch_stride", 0),
@@ -145,7 +145,7 @@ def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_sca
         _ptr(p_ik.get("bias_b")),
         B, rows, m, row0_pos, first_entry, FMT[in_fmt],
         _ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), HI, cI, N, _ptr(pos0), FMT[fmt], _ptr(scores),
-        _ptr(bound), _stream(stream))
+        FMT[_TORCH_FMT[scores.dtype]], _ptr(bound), _stream(stream))
     _lib.check(st, "csa_compress_index")
     return scores
 
@@ -155,17 +155,23 @@ def bound_keys(B, T, n_max, device):
     return torch.empty((B, T, _lib.load().csa_index_bound_keys(n_max)), dtype=torch.int32, device=device)
 
 
-def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None, bound=None):
-    """csa_index.  q [B][T][HI][row], k [B][N][row]; returns float32 scores [B][T][N].  bound: optional
-    buffer from bound_keys() that also receives the selector's lower-bound keys."""
+def _score_buf(B, T, N, score_fmt, device):
+    return torch.empty((B, T, N), dtype=torch.bfloat16 if score_fmt == "bf16" else torch.float32, device=device)
+
+
+def index(q, q_scale, w, k, k_scale, pos0, m, fmt, n_max=None, scores=None, stream=None, bound=None,
+          score_fmt="f32"):
+    """csa_index.  q [B][T][HI][row], k [B][N][row]; returns scores [B][T][N] (float32, or bf16 with
+    score_fmt="bf16" / a bf16 scores tensor).  bound: optional buffer from bound_keys() that also
+    receives the selector's lower-bound keys."""
     lib = _lib.load()
     B, T, HI = q.shape[0], q.shape[1], q.shape[2]
     cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
     N = k.shape[1] if n_max is None else n_max
     if scores is None:
-        scores = torch.empty((B, T, N), dtype=torch.float32, device=q.device)
+        scores = _score_buf(B, T, N, score_fmt, q.device)
     st = lib.csa_index(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k), _ptr(k_scale), B, T, HI, cI, N, _ptr(pos0), m,
-                       FMT[fmt], _ptr(scores), _ptr(bound), _stream(stream))
+                       FMT[fmt], _ptr(scores), FMT[_TORCH_FMT[scores.dtype]], _ptr(bound), _stream(stream))
     _lib.check(st, "csa_index")
     return scores
 
@@ -185,8 +191,8 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
         ws = workspace(nb, dev, "topk", zero=True)
     if bound is not None and tuple(bound.shape) != (B, T, lib.csa_index_bound_keys(N)):
         raise CSAError(f"topk: bound shape {tuple(bound.shape)} does not match the scores")
-    st = lib.csa_topk(_ptr(scores), B, T, N, _ptr(pos0), m, k, _ptr(bound), _ptr(idx), _ptr(vals), _ptr(ws), nb,
-                      _stream(stream))
+    st = lib.csa_topk(_ptr(scores), FMT[_TORCH_FMT[scores.dtype]], B, T, N, _ptr(pos0), m, k, _ptr(bound),
+                      _ptr(idx), _ptr(vals), _ptr(ws), nb, _stream(stream))
     _lib.check(st, "csa_topk")
     return idx, vals
 

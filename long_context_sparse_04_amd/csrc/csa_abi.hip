@@ -22,7 +22,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 3; }
+int csa_abi_version(void) { return 4; }
 
 }  // extern "C"
 
@@ -119,7 +119,7 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, in
 namespace {
 // shape / dtype / pointer checks of csa_index; CSA_OK with `empty` set means nothing to launch
 csa_status check_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
-                       int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, const float* scores,
+                       int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, const void* scores,
                        bool& empty) {
   empty = false;
   if (B < 0 || T < 0 || HI < 1 || cI < 1 || n_max < 0 || m < 1) return CSA_ERR_SHAPE;
@@ -154,16 +154,17 @@ extern "C" {
 int64_t csa_index_bound_keys(int64_t n_max) { return n_max > 0 ? index_bound_keys(n_max) : 0; }
 
 csa_status csa_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
-                     int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, float* scores,
-                     uint32_t* bound, void* stream) {
+                     int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t, void* scores,
+                     int score_t, uint32_t* bound, void* stream) {
   bool empty;
   const csa_status st = check_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, empty);
   if (st != CSA_OK) return st;
+  if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   // bound keys come from the per-row decode kernels only
   if (bound && (qk_t == CSA_F32 || use_prefill_index(qk_t, T, HI))) return CSA_ERR_UNSUPPORTED;
   if (empty) return CSA_OK;
   if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
-  return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, bound,
+  return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
                       (hipStream_t)stream);
 }
 
@@ -173,8 +174,9 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
                               const void* za1, const void* zb1, const float* bias_a1, const float* bias_b1, int B,
                               int rows, int m, int64_t row0_pos, int64_t first_entry, int in_t, const void* q,
                               const void* q_scale, const float* w, void* k, void* k_scale, int HI, int cI,
-                              int64_t n_max, const int64_t* pos0, int qk_t, float* scores, uint32_t* bound,
-                              void* stream) {
+                              int64_t n_max, const int64_t* pos0, int qk_t, void* scores, int score_t,
+                              uint32_t* bound, void* stream) {
+  if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3_ROWSCALE && qk_t != CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
   if (m >= 64) return CSA_ERR_UNSUPPORTED;  // one 256-thread workgroup pools an entry's rows
   if (n_max < 1 || first_entry < 0 || first_entry >= n_max) return CSA_ERR_SHAPE;
@@ -199,7 +201,7 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
   const CompressJob jobs[2] = {{ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, nullptr, out_t0, bs0, prep0},
                                {ca1, cb1, za1, zb1, bias_a1, bias_b1, cI, out1, out_scale1, qk_t, bs1, nullptr}};
   return launch_compress_index(jobs, rows, m, row0_pos, first_entry, in_t, q, q_scale, w, k, k_scale, B, HI, cI,
-                               n_max, pos0, qk_t, scores, bound, (hipStream_t)stream);
+                               n_max, pos0, qk_t, scores, score_t, bound, (hipStream_t)stream);
 }
 
 size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
@@ -207,16 +209,17 @@ size_t csa_topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
   return topk_workspace_bytes(B, T, n_max, k);
 }
 
-csa_status csa_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                    const uint32_t* bound, int32_t* idx, float* vals, void* workspace, size_t ws_bytes,
+csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max, const int64_t* pos0, int m,
+                    int k, const uint32_t* bound, int32_t* idx, float* vals, void* workspace, size_t ws_bytes,
                     void* stream) {
+  if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (B < 0 || T < 0 || n_max < 0 || m < 1 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
   if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
   if (B == 0 || T == 0) return CSA_OK;
   if (!idx || !pos0 || (n_max > 0 && !scores)) return CSA_ERR_NULL;
   const size_t need = csa_topk_workspace_bytes(B, T, n_max > 0 ? n_max : 1, k);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_topk(scores, B, T, n_max, pos0, m, k, bound, idx, vals, workspace, (hipStream_t)stream);
+  return launch_topk(scores, score_t, B, T, n_max, pos0, m, k, bound, idx, vals, workspace, (hipStream_t)stream);
 }
 
 static csa_status check_attend(int kv_t, int out_t, int B, int T, int H, int c, int rope_dims, int n_win, int m) {

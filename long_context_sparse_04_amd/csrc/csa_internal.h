@@ -39,17 +39,17 @@ int64_t index_bound_keys(int64_t n_max);
 bool use_prefill_index(int fmt, int T, int HI);
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
-                        float* scores, uint32_t* bound, hipStream_t stream);
+                        void* scores, int score_t, uint32_t* bound, hipStream_t stream);
 
 // csa_compress_pair's two problems (jobs[0]: the KV entry, jobs[1]: the indexer key, whose output is the
 // key cache at first_entry) and a decode csa_index (T = 1) in one launch
 csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64_t row0_pos, int64_t first_entry,
                                  int in_t, const void* q, const void* q_scale, const float* w, const void* k,
                                  const void* k_scale, int B, int HI, int cI, int64_t n_max, const int64_t* pos0,
-                                 int qk_t, float* scores, uint32_t* bound, hipStream_t stream);
+                                 int qk_t, void* scores, int score_t, uint32_t* bound, hipStream_t stream);
 
 size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k);
-csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
+csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
                        const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream);
 
 // mode 0: CSA (index list), mode 1: HCA (dense range)

@@ -99,6 +99,19 @@ CSA_DEV f32x4 mfma_tile(const Frag<FMT>& a, const Frag<FMT>& b, int sa, int sb) 
   return acc;
 }
 
+// The scores' destination: float32, or bf16 rounded to nearest even (the selector's cheaper input).
+struct ScoreOut {
+  void* p;
+  int bf16;
+  CSA_DEV void store(int64_t i, float v) const {
+    if (bf16)
+      static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    else
+      static_cast<float*>(p)[i] = v;
+  }
+  CSA_DEV float stored(float v) const { return bf16 ? __uint_as_float((uint32_t)f32_to_bf16(v) << 16) : v; }
+};
+
 // Tiles in flight per wave (each of 16 entry rows), chosen by measurement; the LDS rings of the staged
 // formats stay small enough for three (bf16) or four (fp8) workgroups per CU.
 template <int FMT>
@@ -165,7 +178,7 @@ template <int FMT, int NT, bool FUSE>
 __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
-    const int64_t* __restrict__ pos0, int m, float* __restrict__ scores, uint32_t* __restrict__ bound,
+    const int64_t* __restrict__ pos0, int m, ScoreOut so, uint32_t* __restrict__ bound,
     std::conditional_t<FUSE, IndexFuse, NoFuse> fz) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
@@ -198,7 +211,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   const int b = row / T;
   const int r = row - b * T;
   const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
-  float* srow = scores + (int64_t)row * n_max;
+  const int64_t srow = (int64_t)row * n_max;  // this row's first score
 
   if constexpr (FUSE) {  // decode rows only (row == b)
     constexpr int kScratch = 3 * 256;  // f32x4 slots of the compression's slice merge
@@ -374,9 +387,9 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
       const bool odd = gl & 1;
       const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
       const int64_t eo = eg + lane;  // entry this lane writes
-      if (eo < n_max) srow[eo] = (eo < vis) ? val : -INFINITY;
+      if (eo < n_max) so.store(srow + eo, (eo < vis) ? val : -INFINITY);
       if (eo < vis) {
-        const uint32_t key = score_key(val);
+        const uint32_t key = score_key(so.stored(val));  // the key of the score the selector will read
         top2 = max(top2, min(top1, key));
         top1 = max(top1, key);
       }
@@ -415,7 +428,7 @@ constexpr int kPDmaPerWave = kPTile * kPRowBytes / 1024 / kWaves;  // 1 KB per D
 template <int NT>
 __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kI, int T,
-    int64_t n_max, const int64_t* __restrict__ pos0, int m, float* __restrict__ scores) {
+    int64_t n_max, const int64_t* __restrict__ pos0, int m, ScoreOut so) {
   constexpr int HI = NT * 16;
   __shared__ __align__(16) uint8_t s_k[2][kPTile * kPRowBytes];
   const int lane = threadIdx.x & 63;
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
       const int64_t eo = (int64_t)ti * kPTile + lane;
       if (live[rr] && eo < n_max) {
         const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
-        scores[row * n_max + eo] = eo < vis[rr] ? val : -INFINITY;
+        so.store(row * n_max + eo, eo < vis[rr] ? val : -INFINITY);
       }
     }
     __syncthreads();  // the buffer is refilled by the next-but-one tile
@@ -521,7 +534,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
   for (int rr = 0; rr < kPRowsPerWave; ++rr) {
     if (!live[rr]) continue;
     const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
-    for (int64_t eo = (int64_t)ntiles * kPTile + lane; eo < n_max; eo += 64) scores[row * n_max + eo] = -INFINITY;
+    for (int64_t eo = (int64_t)ntiles * kPTile + lane; eo < n_max; eo += 64) so.store(row * n_max + eo, -INFINITY);
   }
 }
 
@@ -531,7 +544,7 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
                                                                 const float* __restrict__ w,
                                                                 const float* __restrict__ kI, int T, int HI, int cI,
                                                                 int64_t n_max, const int64_t* __restrict__ pos0,
-                                                                int m, float* __restrict__ scores) {
+                                                                int m, ScoreOut so) {
   extern __shared__ float s_q[];  // [HI][cI]
   const int row = blockIdx.y;
   const int b = row / T;
@@ -542,9 +555,9 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
   __syncthreads();
   const int64_t s = (int64_t)blockIdx.x * kF32Threads + threadIdx.x;
   if (s >= n_max) return;
-  float* out = scores + (int64_t)row * n_max + s;
+  const int64_t out = (int64_t)row * n_max + s;
   if (s >= vis) {
-    *out = -INFINITY;
+    so.store(out, -INFINITY);
     return;
   }
   const float* krow = kI + ((int64_t)b * n_max + s) * cI;
@@ -560,18 +573,18 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
     }
     tot = fmaf(w[(int64_t)row * HI + h], fmaxf(d, 0.0f), tot);
   }
-  *out = tot;
+  so.store(out, tot);
 }
 
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
-                      int T, int HI, int64_t n_max, const int64_t* pos0, int m, float* scores, uint32_t* bound,
+                      int T, int HI, int64_t n_max, const int64_t* pos0, int m, ScoreOut so, uint32_t* bound,
                       const IndexFuse* fuse, hipStream_t stream) {
   if (use_prefill_index(FMT, T, HI)) {  // many query rows: the tiled contraction
     if (bound || fuse) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(T, kPRows), B);
     hipLaunchKernelGGL((index_prefill_bf16_kernel<4>), grid, dim3(kWaves * 64), 0, stream, (const uint8_t*)q, w,
-                       (const uint8_t*)k, T, n_max, pos0, m, scores);
+                       (const uint8_t*)k, T, n_max, pos0, m, so);
     return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
   }
   dim3 grid(ceil_div(n_max, kEntriesPerWG), B * T);
@@ -579,10 +592,10 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
 #define CSA_IDX_LAUNCH(NT)                                                                                       \
   if (fuse)                                                                                                     \
     hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, w, \
-                       (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound, *fuse);                    \
+                       (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, *fuse);                    \
   else                                                                                                          \
     hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false>), grid, block, 0, stream, (const uint8_t*)q, q_scale,  \
-                       w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, scores, bound, NoFuse{})
+                       w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, NoFuse{})
   switch (HI) {
     case 16: CSA_IDX_LAUNCH(1); break;
     case 32: CSA_IDX_LAUNCH(2); break;
@@ -603,20 +616,20 @@ int64_t index_bound_keys(int64_t n_max) { return 2 * kWaves * ((n_max + kEntries
 
 static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
                                     const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
-                                    const int64_t* pos0, int m, int qk_t, float* scores, uint32_t* bound,
-                                    const IndexFuse* fuse, hipStream_t stream);
+                                    const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
+                                    uint32_t* bound, const IndexFuse* fuse, hipStream_t stream);
 
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
-                        float* scores, uint32_t* bound, hipStream_t stream) {
-  return launch_index_impl(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, bound, nullptr,
-                           stream);
+                        void* scores, int score_t, uint32_t* bound, hipStream_t stream) {
+  return launch_index_impl(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
+                           nullptr, stream);
 }
 
 csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64_t row0_pos, int64_t first_entry,
                                  int in_t, const void* q, const void* q_scale, const float* w, const void* k,
                                  const void* k_scale, int B, int HI, int cI, int64_t n_max, const int64_t* pos0,
-                                 int qk_t, float* scores, uint32_t* bound, hipStream_t stream) {
+                                 int qk_t, void* scores, int score_t, uint32_t* bound, hipStream_t stream) {
   IndexFuse fz;
   csa_compress_body::fill_jobs(jobs, 2, fz.jobs);
   fz.rows = rows;
@@ -624,29 +637,30 @@ csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64
   fz.in_t = in_t;
   fz.row0_pos = row0_pos;
   fz.first_entry = first_entry;
-  return launch_index_impl(q, q_scale, w, k, k_scale, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, bound, &fz,
-                           stream);
+  return launch_index_impl(q, q_scale, w, k, k_scale, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
+                           &fz, stream);
 }
 
 static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
                                     const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
-                                    const int64_t* pos0, int m, int qk_t, float* scores, uint32_t* bound,
-                                    const IndexFuse* fuse, hipStream_t stream) {
+                                    const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
+                                    uint32_t* bound, const IndexFuse* fuse, hipStream_t stream) {
+  const ScoreOut so{scores, score_t == CSA_BF16 ? 1 : 0};
   switch (qk_t) {
     case CSA_F32: {
       if (bound || fuse) return CSA_ERR_UNSUPPORTED;
       dim3 grid(ceil_div(n_max, kF32Threads), B * T);
       size_t lds = (size_t)HI * cI * sizeof(float);
       hipLaunchKernelGGL(index_f32_kernel, grid, dim3(kF32Threads), lds, stream, (const float*)q, w,
-                         (const float*)k, T, HI, cI, n_max, pos0, m, scores);
+                         (const float*)k, T, HI, cI, n_max, pos0, m, so);
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     }
     case CSA_BF16:
-      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
+      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
     case CSA_FP8_E4M3_ROWSCALE:
-      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
+      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
     case CSA_MXFP4_E8M0_B32:
-      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, scores, bound, fuse, stream);
+      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
     default:
       return CSA_ERR_UNSUPPORTED;
   }

@@ -122,6 +122,20 @@ struct Cand {
   int32_t idx;
 };
 
+// One row of scores, float32 or bf16 (a bf16 score's key is that of its exact float32 value, so both
+// kinds share the key space and every selection step below).
+struct ScoreRow {
+  const void* p;
+  int bf16;
+  CSA_DEV uint32_t key(int64_t i) const {
+    return bf16 ? score_key(__uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16))
+                : score_key(static_cast<const float*>(p)[i]);
+  }
+};
+CSA_DEV ScoreRow score_row(const void* scores, int bf16, int64_t row, int64_t n_max) {
+  return ScoreRow{static_cast<const char*>(scores) + row * n_max * (bf16 ? 2 : 4), bf16};
+}
+
 // Smallest and largest of the per-thread (lo, hi) over the block; every thread gets both.
 template <int NT>
 CSA_DEV void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* s_mm) {
@@ -168,7 +182,7 @@ CSA_DEV void radix_step(Get get, int n, uint32_t& pv, int& known, int& need, uin
 CSA_DEV int common_bits(uint32_t lo, uint32_t hi) { return lo == hi ? 32 : __clz(lo ^ hi); }
 
 // ------------------------------------------------------------------ row path
-__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ scores, int T,
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                int64_t n_max, const int64_t* __restrict__ pos0,
                                                                int m, int k, int32_t* __restrict__ idx,
                                                                float* __restrict__ vals, int cache_keys) {
@@ -185,25 +199,25 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   const int64_t t = pos0[b] + r;
   const int V = (int)visible_entries(t, m, n_max);
   const int K = k < V ? k : V;
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   int32_t* orow = idx + (int64_t)row * k;
   float* vrow = vals ? vals + (int64_t)row * k : nullptr;
 
   if (K == V) {  // everything visible is selected (also covers V == 0)
     for (int j = tid; j < k; j += kRowThreads) {
       orow[j] = j < V ? j : -1;
-      if (vrow) vrow[j] = j < V ? key_to_score(score_key(srow[j])) : -INFINITY;
+      if (vrow) vrow[j] = j < V ? key_to_score(srow.key(j)) : -INFINITY;
     }
     return;
   }
 
-  auto key_at = [&](int i) -> uint32_t { return cache_keys ? keys[i] : score_key(srow[i]); };
+  auto key_at = [&](int i) -> uint32_t { return cache_keys ? keys[i] : srow.key(i); };
 
   // digit 0: bits 31..21
   for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
   __syncthreads();
   for (int i = tid; i < V; i += kRowThreads) {
-    uint32_t kk = score_key(srow[i]);
+    uint32_t kk = srow.key(i);
     if (cache_keys) keys[i] = kk;
     atomicAdd(&hist[kk >> 21], 1u);
   }
@@ -311,40 +325,53 @@ struct ChunkKeys {
   bool valid[kPerThread];
 };
 
-CSA_DEV ChunkKeys load_chunk(const float* srow, int lo, int hi, int64_t n_max) {
+CSA_DEV ChunkKeys load_chunk(const ScoreRow& srow, int lo, int hi, int64_t n_max) {
   // Addresses are clamped into the row so that every load is issued unconditionally (no branch
   // between loads); validity is applied afterwards from the unclamped positions.
   ChunkKeys c;
-  float v[kPerThread];
   const int t = threadIdx.x;
   if ((n_max & 3) == 0) {
+    if (srow.bf16) {
+      u32x2 x[kRounds];
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
-      const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(srow + i0));
-      v[4 * j] = x[0]; v[4 * j + 1] = x[1]; v[4 * j + 2] = x[2]; v[4 * j + 3] = x[3];
+      for (int j = 0; j < kRounds; ++j) {
+        const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
+        x[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(srow.p) + i0));
+      }
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j) {
+        c.key[4 * j + 0] = score_key(__uint_as_float(x[j].x << 16));
+        c.key[4 * j + 1] = score_key(__uint_as_float(x[j].x & 0xFFFF0000u));
+        c.key[4 * j + 2] = score_key(__uint_as_float(x[j].y << 16));
+        c.key[4 * j + 3] = score_key(__uint_as_float(x[j].y & 0xFFFF0000u));
+      }
+    } else {
+      f32x4 x[kRounds];
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j) {
+        const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
+        x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(srow.p) + i0));
+      }
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c.key[4 * j + q] = score_key(x[j][q]);
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) {
-      const int64_t i = min((int64_t)(lo + 1024 * (e / 4) + 4 * t + (e % 4)), n_max - 1);
-      v[e] = __builtin_nontemporal_load(srow + i);
-    }
+    for (int e = 0; e < kPerThread; ++e)
+      c.key[e] = srow.key(min((int64_t)(lo + 1024 * (e / 4) + 4 * t + (e % 4)), n_max - 1));
   }
 #pragma unroll
   for (int j = 0; j < kRounds; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = lo + 1024 * j + 4 * t + q;
-      c.valid[4 * j + q] = i < hi;
-      c.key[4 * j + q] = score_key(v[4 * j + q]);
-    }
+    for (int q = 0; q < 4; ++q) c.valid[4 * j + q] = lo + 1024 * j + 4 * t + q < hi;
   return c;
 }
 
 // Kernel 1: per-chunk histogram of the top key digit (bits 31..21), added into the row histogram;
 // also clears the digit-1 histogram that kernel 2 fills.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const float* __restrict__ scores, int T,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                         int64_t n_max,
                                                                         const int64_t* __restrict__ pos0, int m,
                                                                         int k, SplitWs ws) {
@@ -362,7 +389,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const fl
     for (int u = 0; u < kBins / kSplitThreads; ++u) ws.hist1[(int64_t)row * kBins + tid + u * kSplitThreads] = 0;
   }
   if (K == V || lo >= hi) return;  // trivial row or empty chunk (uniform per workgroup)
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   uint32_t* ghist = ws.hist + (int64_t)row * kBins;
   const ChunkKeys ck = load_chunk(srow, lo, hi, n_max);
   for (int j = tid; j < kBins; j += kSplitThreads) hist[j] = 0;
@@ -387,7 +414,7 @@ CSA_DEV void load_hist(const uint32_t* g, uint32_t* hist) {
 
 // Kernel 2: every workgroup derives digit d0 from the complete digit-0 histogram, then adds the
 // histogram of digit 1 (bits 20..10) of its keys whose digit 0 equals d0.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const float* __restrict__ scores, int T,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                          int64_t n_max,
                                                                          const int64_t* __restrict__ pos0, int m,
                                                                          int k, SplitWs ws) {
@@ -401,7 +428,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const f
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
   if (K == V) return;
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   const int lo = blockIdx.x * kChunk;
   const int hi = min(lo + kChunk, V);
   ChunkKeys ck;
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const f
 
 // Kernel 3: every workgroup derives the 22-bit prefix p1 = (d0, d1) from the digit-1 histogram and
 // compacts its chunk's keys with top 22 bits >= p1 into the chunk's own segment, in index order.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const float* __restrict__ scores, int T,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                            int64_t n_max,
                                                                            const int64_t* __restrict__ pos0, int m,
                                                                            int k, SplitWs ws) {
@@ -443,7 +470,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
   if (K == V) return;
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   const int lo = blockIdx.x * kChunk;
   const int hi = min(lo + kChunk, V);
   ChunkKeys ck;
@@ -484,7 +511,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const
 // bound key (two digit passes over the row's bound keys), and compacts its chunk's keys >= tau into
 // its segment, in index order.  tau never exceeds the row's K-th largest key, so every selected key is
 // a candidate; typically about 1.1 k keys are.
-__global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const float* __restrict__ scores, int T,
+__global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                            int64_t n_max,
                                                                            const int64_t* __restrict__ pos0, int m,
                                                                            int k, const uint32_t* __restrict__ bound,
@@ -501,7 +528,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
   if (K == V) return;
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   const int lo = blockIdx.x * kChunk;
   const int hi = min(lo + kChunk, V);
   ChunkKeys ck;
@@ -547,7 +574,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const
 // digit-0 histogram of the row.  If the candidates are fewer than K (bound keys that were not the
 // indexer's), it selects from the whole visible row instead.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
-    const float* __restrict__ scores, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
+    const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
     int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws, int bounded) {
   __shared__ Cand s_c[kSegCap];
   __shared__ uint32_t hist[kBins];
@@ -562,7 +589,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
   const int r = row - b * T;
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
-  const float* srow = scores + (int64_t)row * n_max;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   const Cand* seg = ws.seg + (int64_t)row * n_max;
   const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
   int32_t* orow = idx + (int64_t)row * k;
@@ -571,7 +598,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
   if (K == V) {
     for (int j = tid; j < k; j += kSplitThreads) {
       orow[j] = j < V ? j : -1;
-      if (vrow) vrow[j] = j < V ? key_to_score(score_key(srow[j])) : -INFINITY;
+      if (vrow) vrow[j] = j < V ? key_to_score(srow.key(j)) : -INFINITY;
     }
     return;
   }
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
   __syncthreads();
   auto cand = [&](int j) -> Cand {
     if (in_lds) return s_c[j];
-    if (rescan) return Cand{score_key(srow[j]), j};
+    if (rescan) return Cand{srow.key(j), j};
     return cand_global(j);
   };
 
@@ -723,9 +750,10 @@ size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
   return split_bytes(rows, n_max, ceil_div(n_max, kChunk));
 }
 
-csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
+csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
                        const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream) {
   const int rows = B * T;
+  const int sbf16 = score_t == CSA_BF16 ? 1 : 0;
   if (use_split(rows, n_max)) {
     const int nch = ceil_div(n_max, kChunk);
     SplitWs s = carve(ws, rows, n_max, nch);
@@ -733,17 +761,17 @@ csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const i
     // bound keys help only when there are enough of them (a K-th largest well inside their range)
     const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k;
     if (bounded) {
-      hipLaunchKernelGGL(topk_bound_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+      hipLaunchKernelGGL(topk_bound_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
                          k, bound, (int)index_bound_keys(n_max), s);
     } else {
-      hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m, k,
+      hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m, k,
                          s);
-      hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0, m,
+      hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
                          k, s);
-      hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0,
+      hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
                          m, k, s);
     }
-    hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, T, n_max, pos0,
+    hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
                        m, k, nch, idx, vals, s, bounded ? 1 : 0);
   } else {
     const int cache = n_max <= kRowKeyCap ? 1 : 0;
@@ -755,7 +783,7 @@ csa_status launch_topk(const float* scores, int B, int T, int64_t n_max, const i
         return CSA_ERR_LAUNCH;
       attr_set = true;
     }
-    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kRowThreads), lds, stream, scores, T, n_max, pos0, m, k,
+    hipLaunchKernelGGL(topk_row_kernel, dim3(rows), dim3(kRowThreads), lds, stream, scores, sbf16, T, n_max, pos0, m, k,
                        idx, vals, cache);
   }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -100,44 +100,49 @@ def test_compress_pair_validation(lib):
 
 
 def test_index_topk_attend_validation(lib):
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, None, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, None, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 64, 1000, DUMMY, 4, 2, DUMMY, None, None) == 3
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 2, DUMMY, None, None) == 1
-    assert lib.csa_index(None, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, None, None) == 1
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, -1, DUMMY, 4, 1, DUMMY, None, None) == 2
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 7, DUMMY, 0, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 48, 128, 1000, DUMMY, 4, 1, DUMMY, 0, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 64, 1000, DUMMY, 4, 2, DUMMY, 0, None, None) == 3
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 2, DUMMY, 0, None, None) == 1
+    assert lib.csa_index(None, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, 0, None, None) == 1
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, -1, DUMMY, 4, 1, DUMMY, 0, None, None) == 2
     # top-k
     nb = lib.csa_topk_workspace_bytes(4, 1, 262144, 1024)
     assert nb >= 4 * 262144 * 8
     assert lib.csa_topk_workspace_bytes(1, 4096, 17408, 512) == 0     # row path needs none
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, None, 0, None) == 4
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, DUMMY, nb - 1, None) == 4
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 0, None, DUMMY, None, DUMMY, nb, None) == 2
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, DUMMY, 4, 4096, None, DUMMY, None, DUMMY, nb, None) == 2
-    assert lib.csa_topk(DUMMY, 4, 1, 262144, None, 4, 1024, None, DUMMY, None, DUMMY, nb, None) == 1
+    assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, None, 0, None) == 4
+    assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, DUMMY, nb - 1, None) == 4
+    assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, DUMMY, 4, 0, None, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, DUMMY, 4, 4096, None, DUMMY, None, DUMMY, nb, None) == 2
+    assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, None, 4, 1024, None, DUMMY, None, DUMMY, nb, None) == 1
     assert lib.csa_index(DUMMY, C.c_void_p(0x1002), DUMMY, DUMMY, DUMMY, 1, 1, 64, 128, 1000, DUMMY, 4, 3, DUMMY,
-                         None, None) == 2           # MXFP4 query scales are read as aligned 32-bit words
+                         0, None, None) == 2           # MXFP4 query scales are read as aligned 32-bit words
     # bound keys: two per 256 entries, from the per-row kernels only, 8-byte aligned
     assert lib.csa_index_bound_keys(262144) == 2048 and lib.csa_index_bound_keys(1000) == 8
     assert lib.csa_index_bound_keys(0) == 0
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 32, 128, 1000, DUMMY, 4, 0, DUMMY, DUMMY,
-                         None) == 3                 # float32 path: no bound keys
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 4096, 64, 128, 17408, DUMMY, 4, 1, DUMMY, DUMMY,
-                         None) == 3                 # tiled prefill kernel: no bound keys
-    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY,
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 32, 128, 1000, DUMMY, 4, 0, DUMMY, 0,
+                         DUMMY, None) == 3                 # float32 path: no bound keys
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 4096, 64, 128, 17408, DUMMY, 4, 1, DUMMY, 0,
+                         DUMMY, None) == 3                 # tiled prefill kernel: no bound keys
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, 0,
                          C.c_void_p(0x1004), None) == 2
+    # scores: float32 or bf16 only
+    assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 64, 128, 1000, DUMMY, 4, 1, DUMMY, 2, None,
+                         None) == 3
+    assert lib.csa_topk(DUMMY, 2, 4, 1, 262144, DUMMY, 4, 1024, None, DUMMY, None, DUMMY, nb, None) == 3
     # compress_index: the MFMA formats only, entries of m < 64 rows, the new entry inside the cache
     def ci(**kw):
-        a = dict(m=4, first=1023, n=1024, qk=2, q=DUMMY, rows=8, r0=4088)
+        a = dict(m=4, first=1023, n=1024, qk=2, q=DUMMY, rows=8, r0=4088, st=0)
         a.update(kw)
         return lib.csa_compress_index(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 512, DUMMY, 1, 0, None,
                                       DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, a["rows"], a["m"], a["r0"],
                                       a["first"], 1, a["q"], DUMMY, DUMMY, DUMMY, DUMMY, 64, 128, a["n"], DUMMY,
-                                      a["qk"], DUMMY, None, None)
+                                      a["qk"], DUMMY, a["st"], None, None)
     assert ci(qk=0) == 3 and ci(m=128) == 3
     assert ci(first=1024) == 2 and ci(first=-1) == 2
     assert ci(q=None) == 1
     assert ci(r0=4096) == 2                   # the entry reads rows before row0_pos
+    assert ci(st=3) == 3
     # attend
     ws = lib.csa_attend_workspace_bytes(4, 1, 128, 512, 1024, 128)
     assert ws > 0 and lib.csa_attend_workspace_bytes(1, 4096, 64, 512, 512, 128) == 0
