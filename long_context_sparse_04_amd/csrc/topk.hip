@@ -4,25 +4,30 @@
 // keeps the compressed entries whose index scores are in Top-k(I_{t,:}); section
 // 二(四) notes the selector's cost (BF16 scores made it 2x faster).
 //
-// Scores become order-preserving uint32 keys (+0 == -0).  A three-digit radix
-// select (11 + 11 + 10 bits) finds the k-th key K*; the result is every key > K*
-// plus the lowest-index keys == K*, emitted by an ordered (index-order) block
-// compaction, so no sort is needed.
+// Scores become order-preserving uint32 keys (+0 == -0).  A radix select in 11-bit
+// digits finds the k-th key K*; the result is every key > K* plus the lowest-index
+// keys == K*, emitted by an ordered (index-order) block compaction, so no sort is
+// needed.
 //
 //  * Row path (many rows, e.g. prefill): one 512-thread workgroup per row; keys
 //    cached in LDS when the row fits (<= 32768 entries).
-//  * Split path (few long rows, decode): chunks of 4096 scores per workgroup.
-//    Kernel 1 builds the top-digit histogram (LDS, then integer atomics into a
-//    per-row global histogram).  Kernel 2: each workgroup derives the threshold
-//    digit d0 from it and builds the second-digit histogram of the keys in that
-//    bin.  Kernel 3: each workgroup derives the 22-bit threshold prefix and
-//    compacts its chunk's keys at or above it into its own segment, in index
-//    order (about k candidates in total).  Kernel 4 (one workgroup per row) loads
-//    all segments (chunk order = index order) into LDS, resolves the last digit,
-//    writes the ordered output and clears the first histogram.  Kernel boundaries carry
-//    the cross-workgroup hand-offs, so no workgroup waits on another or issues a
-//    device-wide fence; integer atomics make the result independent of
-//    scheduling, and the workspace is left zero-filled.
+//  * Split path (few long rows, decode): chunks of 4096 scores per workgroup, 16
+//    consecutive scores per thread.  Candidates (keys at or above a threshold that
+//    cannot exceed K*) are compacted per chunk, in index order, into the chunk's
+//    own segment of the workspace; one workgroup per row then gathers them (chunk
+//    order == index order), resolves the open bits of K* and writes the output.
+//    - With the indexer's bound keys (two per 256 entries, each the key of a
+//      distinct visible entry), the threshold is the K-th largest bound key,
+//      cut to the bits one radix pass resolves; every workgroup of the row derives
+//      it alone, so collection and finishing share one launch: the last workgroup
+//      of a row to publish its segment (agent-scope stores, then an atomic arrival
+//      count) does the finishing pass.
+//    - Without them: kernel 1 builds the top-digit histogram (LDS, then integer
+//      atomics into a per-row global histogram), kernel 2 the second-digit
+//      histogram of the keys in the selected bin, kernel 3 compacts the keys at or
+//      above the 22-bit prefix, kernel 4 finishes (and clears the histogram).
+//    Integer atomics make every result independent of scheduling; the workspace
+//    is left zero-filled where it has to start at zero.
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -36,19 +41,83 @@ constexpr int kRowKeyCap = 32768;     // keys cached in LDS on the row path
 constexpr int kSegCap = 6144;         // candidates cached in LDS by the finishing workgroup
 constexpr int kMaxChunks = 2048;
 
-// ------------------------------------------------------------------ block scans
+// ------------------------------------------------------------------ wave / block primitives
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order: shifts by 1, 2, 4 and 8 inside
+// 16-lane rows (lanes shifted in from outside the row read 0), then the last lane of rows 0 and 2
+// added into rows 1 and 3, and the last lane of row 1 into rows 2 and 3.
+CSA_DEV uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp_u32<0x111>(x);  // row_shr:1
+  x += dpp_u32<0x112>(x);  // row_shr:2
+  x += dpp_u32<0x114>(x);  // row_shr:4
+  x += dpp_u32<0x118>(x);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Smallest / largest over the 64 lanes of a wave; every lane receives it (quad and row exchanges
+// inside 16-lane rows, then the row-pair and half-wave swaps).
+CSA_DEV uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = min(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = min(v, dpp_u32<0x124>(v));  // row_ror:4
+  v = min(v, dpp_u32<0x128>(v));  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(b[0], b[1]);
+}
+CSA_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x124>(v));
+  v = max(v, dpp_u32<0x128>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
+// Exclusive prefixes of two counts over the block in thread order, and their totals.  s_w holds
+// 2 * NT / 64 words.
+template <int NT>
+CSA_DEV void block_excl_sum2(uint32_t a, uint32_t b, uint32_t* s_w, uint32_t& pa, uint32_t& pb, uint32_t& ta,
+                             uint32_t& tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ia = wave_incl_sum(a), ib = wave_incl_sum(b);
+  if (lane == 63) {
+    s_w[2 * wave] = ia;
+    s_w[2 * wave + 1] = ib;
+  }
+  __syncthreads();
+  uint32_t qa = 0, qb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t xa = s_w[2 * w], xb = s_w[2 * w + 1];
+    qa += (w < wave) ? xa : 0u;
+    qb += (w < wave) ? xb : 0u;
+    sa += xa;
+    sb += xb;
+  }
+  __syncthreads();
+  pa = qa + ia - a;
+  pb = qb + ib - b;
+  ta = sa;
+  tb = sb;
+}
+
 // Exclusive prefix of a 0/1 flag over the block (in thread order) and its total.
 template <int NT>
-CSA_DEV int block_flag_scan(bool flag, int* s_w, int& total) {
+CSA_DEV int block_flag_scan(bool flag, uint32_t* s_w, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t bal = __ballot(flag);
   const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-  if (lane == 0) s_w[wave] = __popcll(bal);
+  if (lane == 0) s_w[wave] = (uint32_t)__popcll(bal);
   __syncthreads();
   int pre = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
-    int v = s_w[w];
+    const int v = (int)s_w[w];
     pre += (w < wave) ? v : 0;
     tot += v;
   }
@@ -57,60 +126,37 @@ CSA_DEV int block_flag_scan(bool flag, int* s_w, int& total) {
   return pre + below;
 }
 
-// Exclusive prefix of an int over the block in thread order.
-template <int NT>
-CSA_DEV int block_int_scan(int v, int* s_w, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
+// Given hist[NB] (counts per digit) and 1 <= need <= the total count, find the digit d with
+// count(> d) < need <= count(>= d); writes d and count(> d) to out[0..1].  Thread t holds bins
+// [t * NB/NT, (t + 1) * NB/NT) in registers; counts above a thread's bins are a suffix sum (the wave
+// total minus the inclusive prefix, plus the totals of later waves).
+template <int NT, int NB>
+CSA_DEV void select_digit(const uint32_t* hist, int need, uint32_t* s_w, int* out) {
+  constexpr int BPT = NB / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t hv[BPT];
+  uint32_t local = 0;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+  for (int j = 0; j < BPT; ++j) {
+    hv[j] = hist[tid * BPT + j];
+    local += hv[j];
   }
-  if (lane == 63) s_w[wave] = x;
+  const uint32_t incl = wave_incl_sum(local);
+  if (lane == 63) s_w[wave] = incl;
   __syncthreads();
-  int pre = 0, tot = 0;
+  uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    int s = s_w[w];
-    pre += (w < wave) ? s : 0;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + x - v;
-}
-
-// Given hist[nb] (counts per digit) and need >= 1, find the digit d with
-// count(> d) < need <= count(>= d).  Writes d and count(> d) to out[0..1].
-template <int NT>
-CSA_DEV void select_digit(const uint32_t* hist, int nb, int need, int* s_w, int* out) {
-  const int bpt = nb / NT;  // nb is a multiple of NT
-  const int tid = threadIdx.x;
-  const int u = NT - 1 - tid;  // thread u owns the bins of thread tid counted from the top
-  int local = 0;
-  for (int j = 0; j < bpt; ++j) local += hist[tid * bpt + j];
-  // suffix sums: scan in reversed thread order
-  int total;
-  // exchange local through LDS to scan in reversed order
-  __shared__ int s_rev[kRowThreads];
-  s_rev[u] = local;
-  __syncthreads();
-  int mine = s_rev[tid];  // thread tid now holds the count of original thread NT-1-tid
-  int excl = block_int_scan<NT>(mine, s_w, total);
-  // original thread o = NT-1-tid has count(bins above its range) = excl
-  s_rev[NT - 1 - tid] = excl;
-  __syncthreads();
-  int above = s_rev[tid];
-  if (above < need && above + local >= need) {
-    for (int j = bpt - 1; j >= 0; --j) {
-      int h = hist[tid * bpt + j];
-      if (above + h >= need) {
-        out[0] = tid * bpt + j;
-        out[1] = above;
+  for (int w = 0; w < NT / 64; ++w) above += (w > wave) ? s_w[w] : 0u;
+  const uint32_t nd = (uint32_t)need;
+  if (above < nd && above + local >= nd) {
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (above + hv[j] >= nd) {
+        out[0] = tid * BPT + j;
+        out[1] = (int)above;
         break;
       }
-      above += h;
+      above += hv[j];
     }
   }
   __syncthreads();
@@ -140,11 +186,8 @@ CSA_DEV ScoreRow score_row(const void* scores, int bf16, int64_t row, int64_t n_
 template <int NT>
 CSA_DEV void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* s_mm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     s_mm[2 * wave] = lo;
     s_mm[2 * wave + 1] = hi;
@@ -158,28 +201,38 @@ CSA_DEV void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* s_mm) {
   __syncthreads();
 }
 
-// Radix step over the keys between lo and hi (inclusive) that agree with pv on their top `known` bits:
-// histogram of the 11 bits ending at `shift` (bits already known among them take one value), and the
-// digit of the need-th largest.  Updates pv (those 11 bits), need (minus the keys above the digit) and
-// known.  get(j) returns the j-th key, j < n.
-template <typename Get>
-CSA_DEV void radix_step(Get get, int n, uint32_t& pv, int& known, int& need, uint32_t* hist, int* s_w, int* s_sel) {
+// Radix step over the keys that agree with pv on their top `known` bits (0 <= known < 32): histogram
+// of the 11 bits ending at `shift` (bits already known among them take one value), and the digit of
+// the need-th largest.  Updates pv (those 11 bits), need (minus the keys above the digit) and known.
+// each(f) calls f(key) for every key the calling thread contributes.
+template <int NT, typename Each>
+CSA_DEV void radix_step(Each each, uint32_t& pv, int& known, int& need, uint32_t* hist, uint32_t* s_w,
+                        int* s_sel) {
   const int shift = max(0, 32 - known - 11);
-  for (int j = threadIdx.x; j < kBins; j += kSplitThreads) hist[j] = 0;
+  for (int j = threadIdx.x; j < kBins; j += NT) hist[j] = 0;
   __syncthreads();
-  for (int j = threadIdx.x; j < n; j += kSplitThreads) {
-    const uint32_t kk = get(j);
-    if (known == 0 || (kk >> (32 - known)) == (pv >> (32 - known))) atomicAdd(&hist[(kk >> shift) & 0x7FFu], 1u);
-  }
+  const uint32_t hmask = known == 0 ? 0u : ~0u << (32 - known);
+  const uint32_t hp = pv & hmask;
+  each([&](uint32_t kk) {
+    if ((kk & hmask) == hp) atomicAdd(&hist[(kk >> shift) & 0x7FFu], 1u);
+  });
   __syncthreads();
-  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
+  select_digit<NT, kBins>(hist, need, s_w, s_sel);
   pv = (pv & ~(0x7FFu << shift)) | ((uint32_t)s_sel[0] << shift);
   need -= s_sel[1];
   known = 32 - shift;
 }
 
-// Bits shared by every key in [lo, hi] (lo <= hi), and those bits as a prefix value.
+// Bits shared by every key in [lo, hi] (lo <= hi).
 CSA_DEV int common_bits(uint32_t lo, uint32_t hi) { return lo == hi ? 32 : __clz(lo ^ hi); }
+
+// A row with V <= k: every visible entry, in order.
+CSA_DEV void trivial_row(const ScoreRow& srow, int V, int k, int nt, int32_t* orow, float* vrow) {
+  for (int j = threadIdx.x; j < k; j += nt) {
+    orow[j] = j < V ? j : -1;
+    if (vrow) vrow[j] = j < V ? key_to_score(srow.key(j)) : -INFINITY;
+  }
+}
 
 // ------------------------------------------------------------------ row path
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __restrict__ scores, int sbf16, int T,
@@ -189,7 +242,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
   extern __shared__ uint32_t s_dyn[];
   uint32_t* hist = s_dyn;           // kBins
   uint32_t* keys = s_dyn + kBins;   // cache (when enabled)
-  __shared__ int s_w[kRowThreads / 64];
+  __shared__ uint32_t s_w[2 * kRowThreads / 64];
   __shared__ int s_sel[2];
 
   const int tid = threadIdx.x;
@@ -222,7 +275,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
     atomicAdd(&hist[kk >> 21], 1u);
   }
   __syncthreads();
-  select_digit<kRowThreads>(hist, kBins, K, s_w, s_sel);
+  select_digit<kRowThreads, kBins>(hist, K, s_w, s_sel);
   const uint32_t d0 = s_sel[0];
   int need = K - s_sel[1];
   __syncthreads();
@@ -235,7 +288,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
     if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
   }
   __syncthreads();
-  select_digit<kRowThreads>(hist, kBins, need, s_w, s_sel);
+  select_digit<kRowThreads, kBins>(hist, need, s_w, s_sel);
   const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];  // top 22 bits
   need -= s_sel[1];
   __syncthreads();
@@ -248,7 +301,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
     if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
   }
   __syncthreads();
-  select_digit<kRowThreads>(hist, 1024, need, s_w, s_sel);
+  select_digit<kRowThreads, 1024>(hist, need, s_w, s_sel);
   const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
   const int ties = need - s_sel[1];  // keys == K* to take, lowest indices first
   __syncthreads();
@@ -280,25 +333,30 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
 // ------------------------------------------------------------------ split path
 struct SplitWs {
   uint32_t* hist;     // [rows][kBins]   digit-0 histogram (zero at rest)
+  uint32_t* arrive;   // [rows]          workgroups of the bound-key launch that published (zero at rest)
   uint32_t* hist1;    // [rows][kBins]   digit-1 histogram (cleared by kernel 1 of every call)
   uint32_t* info;     // [rows][4]
-  uint32_t* cnt;      // [rows][nch]
+  uint32_t* cnt;      // [rows][nch]     per chunk: candidates | (candidates above the threshold's prefix) << 16
   Cand* seg;          // [rows][n_max]
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The split path serves fewer than kSplitMaxRows rows.  Its digit-0 histograms, the one region that
-// must be zero at rest, take a fixed slot for that many rows at the start of the workspace, so that
-// no call of another shape ever places them over memory that a previous call left dirty.
+// The split path serves fewer than kSplitMaxRows rows.  Its zero-at-rest regions (the digit-0
+// histograms and the arrival counts) take fixed slots for that many rows at the start of the
+// workspace, so that no call of another shape ever places them over memory that a previous call left
+// dirty.
 constexpr int kSplitMaxRows = 128;
 constexpr size_t kHistSlot = (size_t)kSplitMaxRows * kBins * 4;
+constexpr size_t kArriveSlot = (size_t)kSplitMaxRows * 4;
 
 static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   char* p = static_cast<char*>(ws);
   SplitWs s;
   s.hist = reinterpret_cast<uint32_t*>(p);
   p += kHistSlot;
+  s.arrive = reinterpret_cast<uint32_t*>(p);
+  p += align256(kArriveSlot);
   s.hist1 = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins * 4);
   s.info = reinterpret_cast<uint32_t*>(p);
@@ -306,19 +364,20 @@ static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   s.cnt = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * nch * 4);
   s.seg = reinterpret_cast<Cand*>(p);
+  (void)n_max;
   return s;
 }
 
 static size_t split_bytes(int rows, int64_t n_max, int nch) {
-  return kHistSlot + align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
+  return kHistSlot + align256(kArriveSlot) + align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
          align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand));
 }
 
-// Each thread of a split-path workgroup owns 16 scores of its 4096-score chunk:
-// round j (0..3) covers chunk positions [1024 j, 1024 j + 1024), thread t the 4
-// consecutive positions 1024 j + 4 t + q.  All 16 loads are issued before any use.
+// Thread t of a split-path workgroup owns the 16 consecutive scores [lo + 16 t, lo + 16 t + 16) of
+// its chunk, so that one block scan orders a chunk's candidates by index.  All loads are issued before
+// any use; addresses are clamped into the row (no branch between loads) and validity is applied
+// afterwards from the unclamped positions.
 constexpr int kPerThread = kChunk / kSplitThreads;  // 16
-constexpr int kRounds = kPerThread / 4;             // 4
 
 struct ChunkKeys {
   uint32_t key[kPerThread];
@@ -326,53 +385,75 @@ struct ChunkKeys {
 };
 
 CSA_DEV ChunkKeys load_chunk(const ScoreRow& srow, int lo, int hi, int64_t n_max) {
-  // Addresses are clamped into the row so that every load is issued unconditionally (no branch
-  // between loads); validity is applied afterwards from the unclamped positions.
   ChunkKeys c;
-  const int t = threadIdx.x;
-  if ((n_max & 3) == 0) {
-    if (srow.bf16) {
-      u32x2 x[kRounds];
+  const int64_t i0 = lo + kPerThread * (int)threadIdx.x;
+  if (srow.bf16 && (n_max & 7) == 0) {
+    u32x4 x[2];
 #pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
-        x[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(srow.p) + i0));
-      }
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        c.key[4 * j + 0] = score_key(__uint_as_float(x[j].x << 16));
-        c.key[4 * j + 1] = score_key(__uint_as_float(x[j].x & 0xFFFF0000u));
-        c.key[4 * j + 2] = score_key(__uint_as_float(x[j].y << 16));
-        c.key[4 * j + 3] = score_key(__uint_as_float(x[j].y & 0xFFFF0000u));
-      }
-    } else {
-      f32x4 x[kRounds];
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        const int64_t i0 = min((int64_t)(lo + 1024 * j + 4 * t), n_max - 4);
-        x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(srow.p) + i0));
-      }
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c.key[4 * j + q] = score_key(x[j][q]);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t p = min(i0 + 8 * j, n_max - 8);
+      x[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(srow.p) + p));
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        c.key[8 * j + 2 * h] = score_key(__uint_as_float(x[j][h] << 16));
+        c.key[8 * j + 2 * h + 1] = score_key(__uint_as_float(x[j][h] & 0xFFFF0000u));
+      }
+  } else if (!srow.bf16 && (n_max & 3) == 0) {
+    f32x4 x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t p = min(i0 + 4 * j, n_max - 4);
+      x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(srow.p) + p));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) c.key[4 * j + q] = score_key(x[j][q]);
   } else {
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e)
-      c.key[e] = srow.key(min((int64_t)(lo + 1024 * (e / 4) + 4 * t + (e % 4)), n_max - 1));
+    for (int e = 0; e < kPerThread; ++e) c.key[e] = srow.key(min(i0 + e, n_max - 1));
   }
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c.valid[4 * j + q] = lo + 1024 * j + 4 * t + q < hi;
+  for (int e = 0; e < kPerThread; ++e) c.valid[e] = i0 + e < hi;
   return c;
+}
+
+// Write the chunk's keys >= thr into its segment in index order; returns the chunk totals (candidates,
+// and those whose top bits under pmask exceed thr's) to every thread.
+template <bool kAgentStores>
+CSA_DEV void compact_chunk(const ChunkKeys& ck, int lo, uint32_t thr, uint32_t pmask, Cand* seg, uint32_t* s_w,
+                           uint32_t& c_tot, uint32_t& g_tot) {
+  uint32_t c_t = 0, g_t = 0;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const bool cand = ck.valid[e] && ck.key[e] >= thr;
+    c_t += cand;
+    g_t += cand && (ck.key[e] & pmask) > thr;
+  }
+  uint32_t c_pre, g_pre;
+  block_excl_sum2<kSplitThreads>(c_t, g_t, s_w, c_pre, g_pre, c_tot, g_tot);
+  const int i0 = lo + kPerThread * (int)threadIdx.x;
+  int p = lo + (int)c_pre;
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e)
+    if (ck.valid[e] && ck.key[e] >= thr) {
+      if constexpr (kAgentStores) {
+        const uint64_t v = (uint64_t)ck.key[e] | ((uint64_t)(uint32_t)(i0 + e) << 32);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(seg + p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        seg[p] = Cand{ck.key[e], i0 + e};
+      }
+      ++p;
+    }
 }
 
 // Kernel 1: per-chunk histogram of the top key digit (bits 31..21), added into the row histogram;
 // also clears the digit-1 histogram that kernel 2 fills.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const void* __restrict__ scores, int sbf16, int T,
-                                                                        int64_t n_max,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist_kernel(const void* __restrict__ scores, int sbf16,
+                                                                        int T, int64_t n_max,
                                                                         const int64_t* __restrict__ pos0, int m,
                                                                         int k, SplitWs ws) {
   __shared__ uint32_t hist[kBins];
@@ -414,12 +495,12 @@ CSA_DEV void load_hist(const uint32_t* g, uint32_t* hist) {
 
 // Kernel 2: every workgroup derives digit d0 from the complete digit-0 histogram, then adds the
 // histogram of digit 1 (bits 20..10) of its keys whose digit 0 equals d0.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const void* __restrict__ scores, int sbf16, int T,
-                                                                         int64_t n_max,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const void* __restrict__ scores, int sbf16,
+                                                                         int T, int64_t n_max,
                                                                          const int64_t* __restrict__ pos0, int m,
                                                                          int k, SplitWs ws) {
   __shared__ uint32_t hist[kBins];
-  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ uint32_t s_w[2 * kSplitThreads / 64];
   __shared__ int s_sel[2];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
@@ -435,7 +516,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const v
   if (lo < hi) ck = load_chunk(srow, lo, hi, n_max);
   load_hist(ws.hist + (int64_t)row * kBins, hist);
   __syncthreads();
-  select_digit<kSplitThreads>(hist, kBins, K, s_w, s_sel);
+  select_digit<kSplitThreads, kBins>(hist, K, s_w, s_sel);
   const uint32_t d0 = (uint32_t)s_sel[0];
   if (blockIdx.x == 0 && tid == 0) {
     ws.info[row * 4 + 0] = d0;
@@ -455,12 +536,12 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_hist1_kernel(const v
 
 // Kernel 3: every workgroup derives the 22-bit prefix p1 = (d0, d1) from the digit-1 histogram and
 // compacts its chunk's keys with top 22 bits >= p1 into the chunk's own segment, in index order.
-__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const void* __restrict__ scores, int sbf16, int T,
-                                                                           int64_t n_max,
+__global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const void* __restrict__ scores, int sbf16,
+                                                                           int T, int64_t n_max,
                                                                            const int64_t* __restrict__ pos0, int m,
                                                                            int k, SplitWs ws) {
   __shared__ uint32_t hist[kBins];
-  __shared__ int s_w[kSplitThreads / 64];
+  __shared__ uint32_t s_w[2 * kSplitThreads / 64];
   __shared__ int s_sel[2];
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
@@ -479,110 +560,258 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const
   const int need = K - (int)ws.info[row * 4 + 1];
   load_hist(ws.hist1 + (int64_t)row * kBins, hist);
   __syncthreads();
-  select_digit<kSplitThreads>(hist, kBins, need, s_w, s_sel);
+  select_digit<kSplitThreads, kBins>(hist, need, s_w, s_sel);
   const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];
   if (blockIdx.x == 0 && tid == 0) {
     ws.info[row * 4 + 2] = p1;
     ws.info[row * 4 + 3] = (uint32_t)(need - s_sel[1]);  // keys with prefix p1 still to take
   }
-  int base = 0;
-  if (lo < hi) {
-    Cand* seg = ws.seg + (int64_t)row * n_max;
-#pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      int mine = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) mine += (ck.valid[4 * j + q] && (ck.key[4 * j + q] >> 10) >= p1) ? 1 : 0;
-      int tot;
-      int pos = base + block_int_scan<kSplitThreads>(mine, s_w, tot);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * j + q;
-        if (ck.valid[e] && (ck.key[e] >> 10) >= p1) seg[lo + pos++] = Cand{ck.key[e], lo + 1024 * j + 4 * tid + q};
-      }
-      base += tot;
-    }
-  }
-  if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = base;
+  uint32_t c_tot = 0, g_tot = 0;
+  if (lo < hi) compact_chunk<false>(ck, lo, p1 << 10, 0xFFFFFC00u, ws.seg + (int64_t)row * n_max, s_w, c_tot, g_tot);
+  if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = c_tot;
 }
 
-// With bound keys from the indexer (two per 256-entry wave, each the key of a distinct visible
-// entry), kernels 1 to 3 become one: every workgroup derives tau, the 22-bit floor of the K-th largest
-// bound key (two digit passes over the row's bound keys), and compacts its chunk's keys >= tau into
-// its segment, in index order.  tau never exceeds the row's K-th largest key, so every selected key is
-// a candidate; typically about 1.1 k keys are.
-__global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(const void* __restrict__ scores, int sbf16, int T,
-                                                                           int64_t n_max,
-                                                                           const int64_t* __restrict__ pos0, int m,
-                                                                           int k, const uint32_t* __restrict__ bound,
-                                                                           int nb, SplitWs ws) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ int s_w[kSplitThreads / 64];
-  __shared__ int s_sel[2];
-  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.y;
-  const int nch = gridDim.x;
-  const int b = row / T;
-  const int r = row - b * T;
-  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
-  const int K = k < V ? k : V;
-  if (K == V) return;
-  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
-  const int lo = blockIdx.x * kChunk;
-  const int hi = min(lo + kChunk, V);
-  ChunkKeys ck;
-  if (lo < hi) ck = load_chunk(srow, lo, hi, n_max);
-  const uint32_t* brow = bound + (int64_t)row * nb;
-  // tau: the K-th largest bound key with the bits below one 11-bit digit cleared, the digit taken right
-  // under the bits that all bound keys share (so one pass resolves it closely)
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int j = tid; j < nb; j += kSplitThreads) {
-    const uint32_t kk = brow[j];
-    kmin = min(kmin, kk);
-    kmax = max(kmax, kk);
+// LDS of the finishing pass.
+struct FinishLds {
+  Cand* s_c;        // [kSegCap]
+  uint32_t* hist;   // [kBins]
+  int* s_pre;       // [kMaxChunks + 1]
+  uint32_t* s_w;    // [2 * kSplitThreads / 64]
+  int* s_sel;       // [2]
+  uint32_t* s_mm;   // [2 * kSplitThreads / 64]
+};
+
+// Finishing pass of one row, by one workgroup, once every chunk's candidates are in the workspace:
+// gathers them (chunk order == index order), resolves the open bits of the K-th key and writes the
+// ascending index list.  The K-th key is known to start with the top `known` bits of pv and to rank
+// need-th among the candidates that do.  With bound keys (bounded), pv is the threshold and need is
+// reduced by the candidates whose prefix is above it (when they are fewer than K; otherwise the range
+// of the candidates decides), and too few candidates (keys that were no lower bound) send the row to
+// a pass over all its visible keys.
+template <bool kCoh>
+CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, const uint32_t* __restrict__ cnt,
+                        const Cand* __restrict__ seg, int64_t n_max, uint32_t pv, int known, int need, bool bounded,
+                        int32_t* __restrict__ orow, float* __restrict__ vrow, const FinishLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kW = kSplitThreads / 64;
+  constexpr int kBatch = 16;  // chunks per wave per gather round
+  // segment and count loads (agent-scope loads when the segments were published within the launch
+  // without a cache write-back); counts are clamped to a chunk's size
+  auto ldc = [&](int64_t i) -> Cand {
+    if constexpr (kCoh) {
+      const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(seg + i), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      return Cand{(uint32_t)v, (int32_t)(v >> 32)};
+    } else {
+      return seg[i];
+    }
+  };
+  auto ldn = [&](int c) -> uint32_t {
+    uint32_t v;
+    if constexpr (kCoh)
+      v = __hip_atomic_load(cnt + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      v = cnt[c];
+    return min(v & 0xFFFFu, (uint32_t)kChunk) | (min(v >> 16, (uint32_t)kChunk) << 16);
+  };
+  // first gather round: 64 candidates of each of the wave's chunks, loaded before the counts are known
+  // (a chunk rarely holds more); clamped into the row's segment
+  Cand sv[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int c = wave + kW * u;
+    sv[u] = ldc(min((int64_t)(c < nact ? c : 0) * kChunk + lane, n_max - 1));
   }
-  block_minmax<kSplitThreads>(kmin, kmax, s_mm);
-  int known = common_bits(kmin, kmax), need = K;
-  uint32_t tau = kmax;
-  if (known < 32) radix_step([&](int j) { return brow[j]; }, nb, tau, known, need, hist, s_w, s_sel);
-  tau &= known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
-  int base = 0;
-  if (lo < hi) {
-    Cand* seg = ws.seg + (int64_t)row * n_max;
+  // per-chunk counts: prefix (chunk order == index order) and totals
+  {
+    constexpr int kCpt = kMaxChunks / kSplitThreads;  // 8
+    const int cpt = (nact + kSplitThreads - 1) / kSplitThreads;
+    const int c0 = tid * cpt;
+    uint32_t cv[kCpt];
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      int mine = 0;
+    for (int u = 0; u < kCpt; ++u) cv[u] = ldn(min(c0 + u, nact - 1));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) mine += (ck.valid[4 * j + q] && ck.key[4 * j + q] >= tau) ? 1 : 0;
-      int tot;
-      int pos = base + block_int_scan<kSplitThreads>(mine, s_w, tot);
+    for (int u = 0; u < kCpt; ++u) cv[u] = (u < cpt && c0 + u < nact) ? cv[u] : 0u;
+    uint32_t nloc = 0, gloc = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * j + q;
-        if (ck.valid[e] && ck.key[e] >= tau) seg[lo + pos++] = Cand{ck.key[e], lo + 1024 * j + 4 * tid + q};
+    for (int u = 0; u < kCpt; ++u) {
+      nloc += cv[u] & 0xFFFFu;
+      gloc += cv[u] >> 16;
+    }
+    uint32_t pre, gpre, ctot, gtot;
+    block_excl_sum2<kSplitThreads>(nloc, gloc, L.s_w, pre, gpre, ctot, gtot);
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u)
+      if (u < cpt && c0 + u < nact) {
+        L.s_pre[c0 + u] = (int)pre;
+        pre += cv[u] & 0xFFFFu;
       }
-      base += tot;
+    if (tid == 0) {
+      L.s_pre[nact] = (int)ctot;
+      L.s_sel[0] = (int)gtot;
     }
   }
-  if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = base;
+  __syncthreads();
+  const int* s_pre = L.s_pre;
+  const int G = L.s_sel[0];
+  const bool rescan = bounded && s_pre[nact] < K;  // (uniform) candidates from the whole visible row
+  const int C = rescan ? V : s_pre[nact];
+  const bool in_lds = !rescan && C <= kSegCap;
+  if (in_lds) {
+    int nmax = 0;  // (wave-uniform)
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = wave + kW * u;
+      const int n = c < nact ? s_pre[c + 1] - s_pre[c] : 0;
+      nmax = max(nmax, n);
+      if (lane < n) L.s_c[s_pre[c] + lane] = sv[u];
+    }
+    if (nmax > 64) {
+#pragma unroll 1
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = wave + kW * u;
+        const int n = c < nact ? s_pre[c + 1] - s_pre[c] : 0;
+        for (int i = 64 + lane; i < n; i += 64) L.s_c[s_pre[c] + i] = ldc((int64_t)c * kChunk + i);
+      }
+    }
+    // rows of more than kW * kBatch chunks: later rounds, loads first
+    for (int cb = wave + kW * kBatch; cb < nact; cb += kW * kBatch) {
+      int dst[kBatch];
+      int nm = 0;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int c = cb + kW * u;
+        const int n = c < nact ? s_pre[c + 1] - s_pre[c] : 0;
+        nm = max(nm, n);
+        dst[u] = lane < n ? s_pre[c] + lane : -1;
+        sv[u] = ldc((int64_t)(c < nact ? c : 0) * kChunk + (lane < n ? lane : 0));
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (dst[u] >= 0) L.s_c[dst[u]] = sv[u];
+      if (nm > 64) {
+#pragma unroll 1
+        for (int u = 0; u < kBatch; ++u) {
+          const int c = cb + kW * u;
+          const int n = c < nact ? s_pre[c + 1] - s_pre[c] : 0;
+          for (int i = 64 + lane; i < n; i += 64) L.s_c[s_pre[c] + i] = ldc((int64_t)c * kChunk + i);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  auto chunk_of = [&](int j) -> int {  // c with s_pre[c] <= j < s_pre[c+1]
+    int lo = 0, hi = nact;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pre[mid] <= j) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  auto cand = [&](int j) -> Cand {
+    if (in_lds) return L.s_c[j];
+    if (rescan) return Cand{srow.key(j), j};
+    const int c = chunk_of(j);
+    return ldc((int64_t)c * kChunk + (j - s_pre[c]));
+  };
+  // thread t takes the contiguous candidates [j0, j1), held in registers when they are few
+  const int per = (C + kSplitThreads - 1) / kSplitThreads;
+  const int j0 = min(tid * per, C), j1 = min(j0 + per, C);
+  constexpr int kReg = 8;
+  const bool regs = in_lds && per <= kReg;  // (uniform)
+  uint32_t rk[kReg];
+  int32_t ri[kReg];
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kReg; ++i) {
+      const Cand cd = L.s_c[min(j0 + i, kSegCap - 1)];
+      rk[i] = cd.key;
+      ri[i] = cd.idx;
+    }
+  }
+  auto each = [&](auto f) {
+    if (regs) {
+#pragma unroll
+      for (int i = 0; i < kReg; ++i)
+        if (j0 + i < j1) f(rk[i]);
+    } else {
+      for (int j = j0; j < j1; ++j) f(cand(j).key);
+    }
+  };
+
+  uint32_t kstar = pv;
+  if (bounded) {
+    if (!rescan && G < K) {
+      need = K - G;  // the K-th key shares the threshold's prefix
+    } else {
+      known = -1;
+    }
+  }
+  if (known < 0) {  // the candidates' range decides the first open bit
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    each([&](uint32_t kk) {
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    });
+    block_minmax<kSplitThreads>(lo, hi, L.s_mm);
+    kstar = hi;
+    known = common_bits(lo, hi);
+    need = K;
+  }
+  while (known < 32) radix_step<kSplitThreads>(each, kstar, known, need, L.hist, L.s_w, L.s_sel);
+  const int ties = need;  // keys equal to K* still to take, lowest index first
+
+  // ordered output: thread t's first selected candidate lands after the larger keys of earlier threads
+  // and the equal keys they take
+  uint32_t n_gt = 0, n_eq = 0;
+  each([&](uint32_t kk) {
+    n_gt += kk > kstar;
+    n_eq += kk == kstar;
+  });
+  uint32_t gt_base, eq_base, gt_tot, eq_tot;
+  block_excl_sum2<kSplitThreads>(n_gt, n_eq, L.s_w, gt_base, eq_base, gt_tot, eq_tot);
+  int pos = (int)gt_base + min((int)eq_base, ties);
+  int eq_rank = (int)eq_base;
+  auto emit = [&](uint32_t kk, int32_t ix) {
+    bool sel = kk > kstar;
+    if (kk == kstar) sel = eq_rank++ < ties;
+    if (sel && pos < K) {
+      orow[pos] = ix;
+      if (vrow) vrow[pos] = key_to_score(kk);
+    }
+    pos += sel ? 1 : 0;
+  };
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+      if (j0 + i < j1) emit(rk[i], ri[i]);
+  } else {
+    for (int j = j0; j < j1; ++j) {
+      const Cand cd = cand(j);
+      emit(cd.key, cd.idx);
+    }
+  }
+  for (int j = K + tid; j < k; j += kSplitThreads) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
 }
 
-// Kernel 4: one workgroup per row gathers the segments (chunk order == index order), resolves the
-// remaining digits of the K-th key among them (the last digit after kernels 1 to 3, all three after
-// the bound collect), and writes the ascending index list.  After kernels 1 to 3 it also clears the
-// digit-0 histogram of the row.  If the candidates are fewer than K (bound keys that were not the
-// indexer's), it selects from the whole visible row instead.
+#define CSA_FINISH_LDS                                 \
+  __shared__ Cand s_c[kSegCap];                        \
+  __shared__ uint32_t s_hist[kBins];                   \
+  __shared__ int s_pre[kMaxChunks + 1];                \
+  __shared__ uint32_t s_w[2 * kSplitThreads / 64];     \
+  __shared__ int s_sel[2];                             \
+  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];    \
+  const FinishLds L{s_c, s_hist, s_pre, s_w, s_sel, s_mm};
+
+// Kernel 4 (no bound keys): one workgroup per row finishes from the 22-bit prefix of kernels 1 to 3
+// and clears the row's digit-0 histogram.
 __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
-    int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws, int bounded) {
-  __shared__ Cand s_c[kSegCap];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int s_w[kSplitThreads / 64];
-  __shared__ int s_sel[2];
-  __shared__ int s_pre[kMaxChunks + 1];
-  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];
-
+    int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+  CSA_FINISH_LDS
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int b = row / T;
@@ -590,150 +819,112 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
   const ScoreRow srow = score_row(scores, sbf16, row, n_max);
-  const Cand* seg = ws.seg + (int64_t)row * n_max;
-  const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
   int32_t* orow = idx + (int64_t)row * k;
   float* vrow = vals ? vals + (int64_t)row * k : nullptr;
-
   if (K == V) {
-    for (int j = tid; j < k; j += kSplitThreads) {
-      orow[j] = j < V ? j : -1;
-      if (vrow) vrow[j] = j < V ? key_to_score(srow.key(j)) : -INFINITY;
-    }
+    trivial_row(srow, V, k, kSplitThreads, orow, vrow);
     return;
   }
-  if (!bounded) {  // the digit-0 histogram is no longer needed: leave the workspace zero-filled
-    uint32_t* ghist = ws.hist + (int64_t)row * kBins;
+  uint32_t* ghist = ws.hist + (int64_t)row * kBins;
 #pragma unroll
-    for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
-  }
+  for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
+  const int nact = (V + kChunk - 1) / kChunk;
+  finish_row<false>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max,
+             ws.info[row * 4 + 2] << 10, 22, (int)ws.info[row * 4 + 3], false, orow, vrow, L);
+}
 
-  // prefix over chunk counts (chunk order == index order); every load is issued before use
-  {
-    constexpr int kCpt = kMaxChunks / kSplitThreads;  // chunk counts per thread (8)
-    const int cpt = (nch + kSplitThreads - 1) / kSplitThreads;
-    const int c0 = tid * cpt;
-    int cv[kCpt];
-#pragma unroll
-    for (int u = 0; u < kCpt; ++u) cv[u] = (u < cpt && c0 + u < nch) ? (int)cnt[c0 + u] : 0;
-    int local = 0;
-#pragma unroll
-    for (int u = 0; u < kCpt; ++u) local += cv[u];
-    int tot;
-    int pre = block_int_scan<kSplitThreads>(local, s_w, tot);
-#pragma unroll
-    for (int u = 0; u < kCpt; ++u)
-      if (u < cpt && c0 + u < nch) {
-        s_pre[c0 + u] = pre;
-        pre += cv[u];
-      }
-    if (tid == 0) s_pre[nch] = tot;
+// With bound keys from the indexer (two per 256-entry run, each the key of a distinct visible entry),
+// one launch does the whole selection.  Every workgroup derives tau, the K-th largest bound key with
+// the bits below one radix pass cleared (the pass takes the 11 bits right under the bits all bound
+// keys share), and compacts its chunk's keys >= tau into its segment, in index order; tau never
+// exceeds the row's K-th largest key, so every selected key is a candidate (typically about 1.1 k
+// keys are).  The workgroup then publishes its segment and count and adds itself to the row's arrival
+// count; the row's last one to arrive reads the others' segments, finishes the row and resets the count.
+__global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
+    const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
+    const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+  CSA_FINISH_LDS
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.y;
+  const int nch = gridDim.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
+  int32_t* orow = idx + (int64_t)row * k;
+  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
+  if (K == V) {
+    if (blockIdx.x == 0) trivial_row(srow, V, k, kSplitThreads, orow, vrow);
+    return;
   }
-  __syncthreads();
-  const bool rescan = bounded && s_pre[nch] < K;  // (uniform) candidates from the whole visible row
-  const int C = rescan ? V : s_pre[nch];
-  const bool in_lds = !rescan && C <= kSegCap;
-  auto chunk_of = [&](int j) -> int {  // c with s_pre[c] <= j < s_pre[c+1]
-    int lo = 0, hi = nch;
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (s_pre[mid] <= j) lo = mid; else hi = mid;
-    }
-    return lo;
-  };
-  auto cand_global = [&](int j) -> Cand {
-    const int c = chunk_of(j);
-    return seg[(int64_t)c * kChunk + (j - s_pre[c])];
-  };
-  if (in_lds) {
-    // wave w copies the segments of chunks w, w + 4, ...: lane i takes element i (and i + 64, ... of
-    // the rare chunk with more than 64 candidates); a batch of kBatch chunks is loaded before storing
-    constexpr int kBatch = 16;
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int c0 = wave; c0 < nch; c0 += 4 * kBatch) {
-      Cand cv[kBatch];
-      int dst[kBatch];
-      int nmax = 0;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int c = c0 + 4 * u;
-        const int n = c < nch ? s_pre[c + 1] - s_pre[c] : 0;
-        nmax = max(nmax, n);
-        dst[u] = lane < n ? s_pre[c] + lane : -1;
-        cv[u] = seg[(int64_t)(c < nch ? c : 0) * kChunk + (lane < n ? lane : 0)];
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (dst[u] >= 0) s_c[dst[u]] = cv[u];
-      if (nmax > 64) {  // (wave-uniform) a chunk of this batch holds more than 64 candidates
-#pragma unroll 1
-        for (int u = 0; u < kBatch; ++u) {
-          const int c = c0 + 4 * u;
-          const int n = c < nch ? s_pre[c + 1] - s_pre[c] : 0;
-          for (int i = 64 + lane; i < n; i += 64) s_c[s_pre[c] + i] = seg[(int64_t)c * kChunk + i];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  auto cand = [&](int j) -> Cand {
-    if (in_lds) return s_c[j];
-    if (rescan) return Cand{srow.key(j), j};
-    return cand_global(j);
-  };
+  const int nact = (V + kChunk - 1) / kChunk;  // chunks holding visible entries
+  if ((int)blockIdx.x >= nact) return;
+  const int lo = blockIdx.x * kChunk;
+  const int hi = min(lo + kChunk, V);
+  const ChunkKeys ck = load_chunk(srow, lo, hi, n_max);
 
-  // the remaining bits of the K-th key among the candidates: after kernels 1 to 3 the top 22 are known;
-  // after the bound collect, those the candidates share, then 11-bit digits below them
-  uint32_t kstar;
-  int need, known;
-  if (bounded) {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int j = tid; j < C; j += kSplitThreads) {
-      const uint32_t kk = cand(j).key;
-      lo = min(lo, kk);
-      hi = max(hi, kk);
+  // tau from the bound keys (held in registers when they fit)
+  const uint32_t* brow = bound + (int64_t)row * nb;
+  constexpr int kBk = 8;
+  const bool breg = nb <= kBk * kSplitThreads;  // (uniform)
+  uint32_t bk[kBk];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (breg) {
+#pragma unroll
+    for (int i = 0; i < kBk; ++i) {
+      const int j = tid + i * kSplitThreads;
+      bk[i] = brow[min(j, nb - 1)];
     }
-    block_minmax<kSplitThreads>(lo, hi, s_mm);
-    kstar = hi;
-    known = common_bits(lo, hi);
-    need = K;
+#pragma unroll
+    for (int i = 0; i < kBk; ++i)
+      if (tid + i * kSplitThreads < nb) {
+        kmin = min(kmin, bk[i]);
+        kmax = max(kmax, bk[i]);
+      }
   } else {
-    kstar = ws.info[row * 4 + 2] << 10;
-    known = 22;
-    need = (int)ws.info[row * 4 + 3];
-  }
-  while (known < 32) radix_step([&](int j) { return cand(j).key; }, C, kstar, known, need, hist, s_w, s_sel);
-  const int ties = need;
-  __syncthreads();
-
-  // ordered output: thread t owns the contiguous candidates [t*per, (t+1)*per)
-  const int per = (C + kSplitThreads - 1) / kSplitThreads;
-  const int j0 = min(tid * per, C), j1 = min(j0 + per, C);
-  int n_gt = 0, n_eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t kk = cand(j).key;
-    n_gt += kk > kstar;
-    n_eq += kk == kstar;
-  }
-  int tot;
-  const int eq_base = block_int_scan<kSplitThreads>(n_eq, s_w, tot);
-  const int take_eq = max(0, min(n_eq, ties - eq_base));
-  int pos = block_int_scan<kSplitThreads>(n_gt + take_eq, s_w, tot);
-  int eq_rank = eq_base;
-  for (int j = j0; j < j1; ++j) {
-    const Cand cd = cand(j);
-    bool sel = cd.key > kstar;
-    if (cd.key == kstar) sel = (eq_rank++ < ties);
-    if (sel) {
-      orow[pos] = cd.idx;
-      if (vrow) vrow[pos] = key_to_score(cd.key);
-      ++pos;
+    for (int j = tid; j < nb; j += kSplitThreads) {
+      const uint32_t kk = brow[j];
+      kmin = min(kmin, kk);
+      kmax = max(kmax, kk);
     }
   }
-  for (int j = K + tid; j < k; j += kSplitThreads) {
-    orow[j] = -1;
-    if (vrow) vrow[j] = -INFINITY;
-  }
+  block_minmax<kSplitThreads>(kmin, kmax, s_mm);
+  int known = common_bits(kmin, kmax), need = K;
+  uint32_t tau = kmax;
+  auto each_bound = [&](auto f) {
+    if (breg) {
+#pragma unroll
+      for (int i = 0; i < kBk; ++i)
+        if (tid + i * kSplitThreads < nb) f(bk[i]);
+    } else {
+      for (int j = tid; j < nb; j += kSplitThreads) f(brow[j]);
+    }
+  };
+  if (known < 32) radix_step<kSplitThreads>(each_bound, tau, known, need, s_hist, s_w, s_sel);
+  const uint32_t pmask = known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
+  tau &= pmask;
+
+  uint32_t c_tot, g_tot;
+  // Publication without a cache write-back: the segment and its count are written with agent-scope
+  // stores, which the L2 of this XCD passes through to memory, and each thread waits until its stores
+  // have completed before the barrier that precedes the arrival count.  The last workgroup of the row
+  // reads them with agent-scope loads, which do not take lines another XCD may have left stale in its
+  // L2, issued only after it has seen every arrival.  (A device-scope release fence per workgroup, the
+  // general form, writes back the whole L2 each time and made the launch about twice as slow.)
+  compact_chunk<true>(ck, lo, tau, pmask, ws.seg + (int64_t)row * n_max, s_w, c_tot, g_tot);
+  if (tid == 0)
+    __hip_atomic_store(ws.cnt + (int64_t)row * nch + blockIdx.x, (g_tot << 16) | c_tot, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(ws.arrive + row, 1u) == (uint32_t)(nact - 1) ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) ws.arrive[row] = 0u;
+  finish_row<true>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max, tau, known, K,
+             true, orow, vrow, L);
 }
 
 bool use_split(int rows, int64_t n_max) {
@@ -761,18 +952,18 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
     // bound keys help only when there are enough of them (a K-th largest well inside their range)
     const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k;
     if (bounded) {
-      hipLaunchKernelGGL(topk_bound_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
-                         k, bound, (int)index_bound_keys(n_max), s);
+      hipLaunchKernelGGL(topk_bound_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
+                         k, bound, (int)index_bound_keys(n_max), idx, vals, s);
     } else {
-      hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m, k,
-                         s);
-      hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
-                         k, s);
-      hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
+      hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
                          m, k, s);
+      hipLaunchKernelGGL(topk_split_hist1_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
+                         m, k, s);
+      hipLaunchKernelGGL(topk_split_collect_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
+                         pos0, m, k, s);
+      hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T,
+                         n_max, pos0, m, k, nch, idx, vals, s);
     }
-    hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
-                       m, k, nch, idx, vals, s, bounded ? 1 : 0);
   } else {
     const int cache = n_max <= kRowKeyCap ? 1 : 0;
     size_t lds = (size_t)kBins * 4 + (cache ? (size_t)n_max * 4 : 0);
