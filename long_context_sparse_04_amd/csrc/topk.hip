@@ -38,8 +38,13 @@ constexpr int kChunk = 4096;          // scores per workgroup on the split path
 constexpr int kSplitThreads = 256;
 constexpr int kRowThreads = 512;
 constexpr int kRowKeyCap = 32768;     // keys cached in LDS on the row path
-constexpr int kSegCap = 6144;         // candidates cached in LDS by the finishing workgroup
+constexpr int kSegCap = 6144;         // candidates cached in LDS by the finishing kernel (no bound keys)
 constexpr int kMaxChunks = 2048;
+// The bound-key launch keeps its LDS small enough to share a CU with a workgroup of the wide attention
+// kernel (which may run beside it on another stream): fewer cached candidates (more are read from the
+// workspace) and rows of at most kBoundMaxChunks chunks.
+constexpr int kBoundSegCap = 2048;
+constexpr int kBoundMaxChunks = 256;
 
 // ------------------------------------------------------------------ wave / block primitives
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order: shifts by 1, 2, 4 and 8 inside
@@ -588,7 +593,7 @@ struct FinishLds {
 // reduced by the candidates whose prefix is above it (when they are fewer than K; otherwise the range
 // of the candidates decides), and too few candidates (keys that were no lower bound) send the row to
 // a pass over all its visible keys.
-template <bool kCoh>
+template <bool kCoh, int SEGCAP, int MAXCH>
 CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, const uint32_t* __restrict__ cnt,
                         const Cand* __restrict__ seg, int64_t n_max, uint32_t pv, int known, int need, bool bounded,
                         int32_t* __restrict__ orow, float* __restrict__ vrow, const FinishLds& L) {
@@ -624,7 +629,7 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
   }
   // per-chunk counts: prefix (chunk order == index order) and totals
   {
-    constexpr int kCpt = kMaxChunks / kSplitThreads;  // 8
+    constexpr int kCpt = MAXCH / kSplitThreads;
     const int cpt = (nact + kSplitThreads - 1) / kSplitThreads;
     const int c0 = tid * cpt;
     uint32_t cv[kCpt];
@@ -656,7 +661,7 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
   const int G = L.s_sel[0];
   const bool rescan = bounded && s_pre[nact] < K;  // (uniform) candidates from the whole visible row
   const int C = rescan ? V : s_pre[nact];
-  const bool in_lds = !rescan && C <= kSegCap;
+  const bool in_lds = !rescan && C <= SEGCAP;
   if (in_lds) {
     int nmax = 0;  // (wave-uniform)
 #pragma unroll
@@ -724,7 +729,7 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
   if (regs) {
 #pragma unroll
     for (int i = 0; i < kReg; ++i) {
-      const Cand cd = L.s_c[min(j0 + i, kSegCap - 1)];
+      const Cand cd = L.s_c[min(j0 + i, SEGCAP - 1)];
       rk[i] = cd.key;
       ri[i] = cd.idx;
     }
@@ -797,10 +802,10 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
   }
 }
 
-#define CSA_FINISH_LDS                                 \
-  __shared__ Cand s_c[kSegCap];                        \
+#define CSA_FINISH_LDS(SEGCAP, MAXCH)                  \
+  __shared__ Cand s_c[SEGCAP];                         \
   __shared__ uint32_t s_hist[kBins];                   \
-  __shared__ int s_pre[kMaxChunks + 1];                \
+  __shared__ int s_pre[MAXCH + 1];                     \
   __shared__ uint32_t s_w[2 * kSplitThreads / 64];     \
   __shared__ int s_sel[2];                             \
   __shared__ uint32_t s_mm[2 * kSplitThreads / 64];    \
@@ -811,7 +816,7 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
 __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
     int nch, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
-  CSA_FINISH_LDS
+  CSA_FINISH_LDS(kSegCap, kMaxChunks)
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int b = row / T;
@@ -829,7 +834,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 #pragma unroll
   for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
   const int nact = (V + kChunk - 1) / kChunk;
-  finish_row<false>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max,
+  finish_row<false, kSegCap, kMaxChunks>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max,
              ws.info[row * 4 + 2] << 10, 22, (int)ws.info[row * 4 + 3], false, orow, vrow, L);
 }
 
@@ -843,7 +848,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
     const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
-  CSA_FINISH_LDS
+  CSA_FINISH_LDS(kBoundSegCap, kBoundMaxChunks)
   __shared__ int s_last;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
@@ -923,7 +928,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
   __syncthreads();
   if (!s_last) return;
   if (tid == 0) ws.arrive[row] = 0u;
-  finish_row<true>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max, tau, known, K,
+  finish_row<true, kBoundSegCap, kBoundMaxChunks>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max, tau, known, K,
              true, orow, vrow, L);
 }
 
@@ -950,7 +955,7 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
     SplitWs s = carve(ws, rows, n_max, nch);
     dim3 grid(nch, rows);
     // bound keys help only when there are enough of them (a K-th largest well inside their range)
-    const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k;
+    const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k && nch <= kBoundMaxChunks;
     if (bounded) {
       hipLaunchKernelGGL(topk_bound_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
                          k, bound, (int)index_bound_keys(n_max), idx, vals, s);
