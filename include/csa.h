@@ -160,8 +160,11 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, in
  *             even; the selector reads half the bytes)
  *   bound   : NULL, or uint32 [B][T][csa_index_bound_keys(n_max)], 8-byte aligned:
  *             for csa_topk, keys of the two largest visible scores (as stored, in
- *             score_t) of each run of 256 entries (order-preserving keys, 0 where
- *             there are fewer).  Their
+ *             score_t) of each bound set (order-preserving keys, 0 where a set has
+ *             fewer), at 2 j, 2 j + 1 for set j.  The sets split each run of 256
+ *             entries (run u: entries 256 u .. 256 u + 255): the whole run when
+ *             n_max > 65536, otherwise its four sets of entries e with e mod 64 in
+ *             [16 r, 16 r + 16), r = 0..3 (set 4 u + r).  Their
  *             K-th largest never exceeds a row's K-th largest score, so csa_topk
  *             can skip its threshold search.  Only for the per-row kernels: with
  *             CSA_F32, or CSA_BF16 with T >= 8 and HI = 64 (the tiled prefill

@@ -90,13 +90,18 @@ template <int CTRL>
 CSA_DEV uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
-// Every lane ends with the two largest keys of the wave's 64 disjoint lane pairs: quad exchanges and
-// row rotations by 4 and 8 inside 16-lane rows, then the gfx950 row-pair and half-wave swaps.
-CSA_DEV void wave_top2(uint32_t& t1, uint32_t& t2) {
+// Every lane ends with the two largest keys of its 16-lane row's disjoint lane pairs: quad exchanges
+// and row rotations by 4 and 8.
+CSA_DEV void row16_top2(uint32_t& t1, uint32_t& t2) {
   top2_merge(t1, t2, dpp_u32<0xB1>(t1), dpp_u32<0xB1>(t2));    // quad_perm [1,0,3,2]
   top2_merge(t1, t2, dpp_u32<0x4E>(t1), dpp_u32<0x4E>(t2));    // quad_perm [2,3,0,1]
   top2_merge(t1, t2, dpp_u32<0x124>(t1), dpp_u32<0x124>(t2));  // row_ror:4
   top2_merge(t1, t2, dpp_u32<0x128>(t1), dpp_u32<0x128>(t2));  // row_ror:8
+}
+// Every lane ends with the two largest keys of the wave's 64 disjoint lane pairs: the rows' results,
+// then the gfx950 row-pair and half-wave swaps.
+CSA_DEV void wave_top2(uint32_t& t1, uint32_t& t2) {
+  row16_top2(t1, t2);
   {
     const auto a = __builtin_amdgcn_permlane16_swap(t1, t1, false, false);
     const auto c = __builtin_amdgcn_permlane16_swap(t2, t2, false, false);

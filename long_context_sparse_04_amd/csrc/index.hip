@@ -30,6 +30,15 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 16;                      // 4 waves x 16 tiles x 16 entries = 1024 entries / WG
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 16;
+
+// Bound-key sets of a wave's 256-entry run: the whole run for caches of more than kFineBoundMax
+// entries, otherwise its four interleaved 64-entry sets {e : e mod 64 in [16 r, 16 r + 16)} (the
+// entries one 16-lane row of the wave writes), so that a short cache still holds enough keys.
+constexpr int64_t kFineBoundMax = 65536;
+__host__ __device__ inline int bound_sets(int64_t n_max) { return n_max <= kFineBoundMax ? 4 : 1; }
+__host__ __device__ inline int64_t bound_keys_per_row(int64_t n_max) {
+  return 2 * kWaves * bound_sets(n_max) * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG);
+}
 constexpr int kRing = 4;                               // tiles in flight per wave
 
 template <int FMT>
@@ -395,14 +404,19 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
       }
     }
   }
-  // Lower-bound keys for the selector: the wave's two largest visible scores.  They are scores of
-  // distinct visible entries, so the K-th largest key over a row's bound keys never exceeds the row's
-  // K-th largest score key.
+  // Lower-bound keys for the selector: the two largest visible scores of each of the wave's bound sets
+  // (the whole wave, or each 16-lane row: see bound_sets).  They are scores of distinct visible entries,
+  // so the K-th largest key over a row's bound keys never exceeds the row's K-th largest score key.
   if (bound) {
-    wave_top2(top1, top2);
-    if (lane == 0) {
-      const int64_t nbw = (int64_t)gridDim.x * kWaves * 2;
-      uint32_t* dst = bound + (int64_t)row * nbw + ((int64_t)blockIdx.x * kWaves + wave) * 2;
+    const int sets = bound_sets(n_max);
+    const int64_t nbw = bound_keys_per_row(n_max);
+    if (sets == 4) {
+      row16_top2(top1, top2);
+    } else {
+      wave_top2(top1, top2);
+    }
+    if ((lane & 15) == 0 && (sets == 4 || lane == 0)) {
+      uint32_t* dst = bound + (int64_t)row * nbw + (((int64_t)blockIdx.x * kWaves + wave) * sets + (lane >> 4)) * 2;
       dst[0] = top1;
       dst[1] = top2;
     }
@@ -609,10 +623,12 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
 
 }  // namespace
 
+int64_t index_bound_keys(int64_t n_max) { return bound_keys_per_row(n_max); }
+
 // the tiled prefill kernel serves bf16 queries of many rows with 64 heads
 bool use_prefill_index(int fmt, int T, int HI) { return fmt == CSA_BF16 && T >= kPRows && HI == 64; }
 
-int64_t index_bound_keys(int64_t n_max) { return 2 * kWaves * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG); }
+
 
 static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
                                     const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,

@@ -77,3 +77,33 @@ def codes_close(got_codes, ref_codes, ref_vals_scaled, table):
     hi = np.abs(table[got_codes[mism] & (0x7F if len(table) == 256 else 0x7)])
     mid = 0.5 * (lo + hi)
     return bool(np.all(np.abs(a - mid) <= 1e-5 * np.maximum(mid, 1e-30)))
+
+
+def score_keys(x32):
+    """The header's order-preserving uint32 key of float32 scores (+0 and -0 share a key)."""
+    u = np.ascontiguousarray(x32, np.float32).view(np.uint32).copy()
+    u[(u << np.uint32(1)) == 0] = 0
+    neg = (u & np.uint32(0x80000000)) != 0
+    return np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def host_bound(scores32, pos0, m):
+    """Bound keys as csa_index defines them: for each bound set, the keys of its two largest visible
+    scores (0 where the set has fewer).  Sets split each run of 256 entries: the whole run when the cache
+    holds more than 65536 entries, else the four sets {e : e mod 64 in [16 r, 16 r + 16)}."""
+    B, T, N = scores32.shape
+    runs = 4 * ((N + 1023) // 1024)
+    sets = 1 if N > 65536 else 4
+    out = np.zeros((B, T, 2 * runs * sets), np.uint32)
+    keys = score_keys(scores32)
+    for b in range(B):
+        for r in range(T):
+            vis = min((pos0[b] + r) // m, N)
+            for u in range(runs):
+                e = np.arange(256 * u, min(256 * u + 256, vis))
+                for s in range(sets):
+                    sel = e if sets == 1 else e[(e % 64) // 16 == s]
+                    kk = np.sort(keys[b, r, sel])[::-1]
+                    j = u * sets + s
+                    out[b, r, 2 * j:2 * j + min(2, len(kk))] = kk[:2]
+    return out

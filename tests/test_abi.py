@@ -117,8 +117,10 @@ def test_index_topk_attend_validation(lib):
     assert lib.csa_topk(DUMMY, 0, 4, 1, 262144, None, 4, 1024, None, DUMMY, None, DUMMY, nb, None) == 1
     assert lib.csa_index(DUMMY, C.c_void_p(0x1002), DUMMY, DUMMY, DUMMY, 1, 1, 64, 128, 1000, DUMMY, 4, 3, DUMMY,
                          0, None, None) == 2           # MXFP4 query scales are read as aligned 32-bit words
-    # bound keys: two per 256 entries, from the per-row kernels only, 8-byte aligned
-    assert lib.csa_index_bound_keys(262144) == 2048 and lib.csa_index_bound_keys(1000) == 8
+    # bound keys: two per bound set (a 256-entry run, or a quarter of one for caches up to 65536 entries),
+    # from the per-row kernels only, 8-byte aligned
+    assert lib.csa_index_bound_keys(262144) == 2048 and lib.csa_index_bound_keys(1000) == 32
+    assert lib.csa_index_bound_keys(65536) == 2048 and lib.csa_index_bound_keys(65537) == 520
     assert lib.csa_index_bound_keys(0) == 0
     assert lib.csa_index(DUMMY, None, DUMMY, DUMMY, None, 1, 1, 32, 128, 1000, DUMMY, 4, 0, DUMMY, 0,
                          DUMMY, None) == 3                 # float32 path: no bound keys

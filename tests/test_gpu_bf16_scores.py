@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from synth import configs, gen
-from tests.gpu_util import DEV, dev, topk_agreement
+from tests.gpu_util import DEV, dev, host_bound, topk_agreement
 
 pytestmark = pytest.mark.gpu
 
@@ -47,28 +47,6 @@ def _bits(t):
 
 def _to_bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
-
-
-def score_keys(x32):
-    """Order-preserving uint32 key of float32 scores (+0 and -0 share a key), as the header defines it."""
-    u = np.ascontiguousarray(x32, np.float32).view(np.uint32).copy()
-    u[(u << np.uint32(1)) == 0] = 0
-    neg = (u & np.uint32(0x80000000)) != 0
-    return np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
-
-
-def host_bound(scores32, pos0, m):
-    B, T, N = scores32.shape
-    nw = 4 * ((N + 1023) // 1024)
-    out = np.zeros((B, T, 2 * nw), np.uint32)
-    keys = score_keys(scores32)
-    for b in range(B):
-        for r in range(T):
-            vis = min((pos0[b] + r) // m, N)
-            for w in range(nw):
-                kk = np.sort(keys[b, r, 256 * w:min(256 * w + 256, vis)])[::-1]
-                out[b, r, 2 * w:2 * w + min(2, len(kk))] = kk[:2]
-    return out
 
 
 def _index_inputs(cfg):

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from synth import configs, formats, gen
-from tests.gpu_util import DEV, codes_close, dev, host_f64, rel_l2, topk_agreement
+from tests.gpu_util import DEV, codes_close, dev, host_bound, host_f64, rel_l2, topk_agreement
 
 pytestmark = pytest.mark.gpu
 
@@ -261,30 +261,6 @@ def test_index_head_counts(api, hi):
     _check_scores(got, ref, absref, 1e-5)
 
 
-def score_keys(x32):
-    """The header's order-preserving uint32 key of float32 scores (+0 and -0 share a key)."""
-    u = np.ascontiguousarray(x32, np.float32).view(np.uint32).copy()
-    u[(u << np.uint32(1)) == 0] = 0
-    neg = (u & np.uint32(0x80000000)) != 0
-    return np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
-
-
-def host_bound(scores32, pos0, m):
-    """Bound keys as csa_index defines them: per run of 256 entries, the keys of its two largest visible
-    scores (0 where the run has fewer visible entries)."""
-    B, T, N = scores32.shape
-    nw = 4 * ((N + 1023) // 1024)
-    out = np.zeros((B, T, 2 * nw), np.uint32)
-    keys = score_keys(scores32)
-    for b in range(B):
-        for r in range(T):
-            vis = min((pos0[b] + r) // m, N)
-            for w in range(nw):
-                kk = np.sort(keys[b, r, 256 * w:min(256 * w + 256, vis)])[::-1]
-                out[b, r, 2 * w:2 * w + min(2, len(kk))] = kk[:2]
-    return out
-
-
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
 def test_index_bound_keys(api, fmt):
     """The indexer's bound keys are the per-256-entry top-2 keys of the scores it wrote, on ragged
@@ -358,6 +334,20 @@ def test_topk_bound_adversarial(api):
     nb = 8 * ((N + 1023) // 1024)
     _topk_case(api, s, pos0, 4, 1024, "bound of zeros", np.zeros((3, 1, nb), np.uint32))
     _topk_case(api, s, pos0, 4, 1024, "bound above the scores", np.full((3, 1, nb), 0xFFFFFFF0, np.uint32))
+
+
+@pytest.mark.parametrize("N,k", [(32768, 512), (40000, 2048), (65536, 1024)])
+def test_topk_bound_short_cache(api, N, k):
+    """Caches of up to 65536 entries carry four bound sets per 256-entry run, enough for one launch at
+    k = 512 over 32768 entries (the Flash decode shape); ragged visibility, ties, k above some rows'
+    visible count."""
+    rng = np.random.default_rng(N + k)
+    B = 6
+    s = rng.standard_normal((B, 1, N)).astype(np.float32)
+    s[1, 0] = np.round(s[1, 0] * 8) / 8
+    s[2, 0] = np.arange(N, dtype=np.float32)[::-1] / N
+    pos0 = [4 * N, 4 * N - 1, 4 * (N - 777), 4 * (k + 3), 4 * (k // 2), 4 * N + 100]
+    _topk_case(api, s, pos0, 4, k, f"bound sets, N={N}", "index")
 
 
 def test_topk_workspace_reused_across_shapes(api):
