@@ -11,5 +11,6 @@ from .csa import (  # noqa: F401
 )
 from .formats import (  # noqa: F401
     decode_bf16, encode_bf16, decode_fp8_e4m3, decode_e2m1, decode_e8m0, decode_mxfp4,
-    dequant_rows, encode_fp8_rows, encode_mxfp4, fp8_e4m3_values, e2m1_values,
+    dequant_rows, encode_fp8_rows, encode_mxfp4, fp8_e4m3_values, e2m1_values, encode_fp8_rope_rows,
+    decode_fp8_rope_rows,
 )

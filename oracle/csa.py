@@ -159,16 +159,20 @@ def rope(x, pos, rope_dims, base):
     return x
 
 
-def _core_attention(q_rows, entries, entry_pos, t, sink, gamma_q, gamma_kv, rope_dims, scale, eps, base):
+def _core_attention(q_rows, entries, entry_pos, t, sink, gamma_q, gamma_kv, rope_dims, scale, eps, base,
+                    n_given=0):
     """One query position t, all heads: o_h = RoPE_{-t}(sum_j p_hj e^_j).
 
-    q_rows [H][c]; entries [L][c] (raw KV); entry_pos [L].
+    q_rows [H][c]; entries [L][c] (raw KV, except that the first n_given rows are already the prepared
+    e^ = RoPE_pos(RMSNorm(e))); entry_pos [L].
     p_hj = exp(z_hj) / (sum_j' exp(z_hj') + exp(z'_h)),  z_hj = scale * q^_h . e^_j.
     """
     qh = rope(rmsnorm(q_rows, gamma_q, eps), t, rope_dims, base)          # [H][c]
     if len(entries) == 0:
         return np.zeros_like(qh)
-    eh = rope(rmsnorm(entries, gamma_kv, eps), entry_pos, rope_dims, base)  # [L][c]
+    entries = np.asarray(entries, np.float64)
+    raw = rope(rmsnorm(entries[n_given:], gamma_kv, eps), np.asarray(entry_pos)[n_given:], rope_dims, base)
+    eh = np.concatenate([entries[:n_given], raw], axis=0)                 # [L][c]
     z = scale * (qh @ eh.T)                                               # [H][L]
     zs = np.asarray(sink, np.float64)[:, None]
     M = np.maximum(np.max(z, axis=1, keepdims=True), zs)
@@ -186,14 +190,15 @@ def _window(win_kv_b, t, pos0_b, n_win):
 
 
 def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-           gamma_q=None, gamma_kv=None, rows=None):
+           gamma_q=None, gamma_kv=None, rows=None, comp_prepared=False):
     """CSA core attention ([CSA] (3) shared key-value MQA, plus [details] (1)-(4)).
 
     Entries for query t: the selected compressed entries C^Comp[s] (s in idx[t],
     -1 skipped, position m*s) followed by the window tokens.  Every entry is both
     key and value.  q [B][T][H][c], comp_kv [B][N][c], idx [B][T][k],
     win_kv [B][T+n_win-1][c].  Returns float64 [B][T][H][c] (rows: optional list
-    of (b, r) pairs to evaluate; the others stay zero).
+    of (b, r) pairs to evaluate; the others stay zero).  comp_prepared: comp_kv
+    holds the prepared e^ of each entry (its RMSNorm and RoPE at m*s already applied).
     """
     q = np.asarray(q, np.float64)
     B, T, H, c = q.shape
@@ -207,13 +212,14 @@ def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=
         ents = np.concatenate([ce, we], axis=0)
         epos = np.concatenate([m * np.asarray(sel, np.float64), wp])
         out[b, r] = _core_attention(q[b, r], ents, epos, t, sink, gamma_q, gamma_kv, rope_dims, scale, eps,
-                                    rope_base)
+                                    rope_base, len(sel) if comp_prepared else 0)
     return out
 
 
 def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-               gamma_q=None, gamma_kv=None, rows=None):
-    """HCA core attention ([HCA] (2)): dense over every visible entry s < floor(t/m'), plus the window."""
+               gamma_q=None, gamma_kv=None, rows=None, comp_prepared=False):
+    """HCA core attention ([HCA] (2)): dense over every visible entry s < floor(t/m'), plus the window
+    (comp_prepared as in attend)."""
     q = np.asarray(q, np.float64)
     B, T, H, c = q.shape
     N = comp_kv.shape[1]
@@ -227,5 +233,5 @@ def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, e
         ents = np.concatenate([ce, we], axis=0)
         epos = np.concatenate([m_hca * np.arange(vis, dtype=np.float64), wp])
         out[b, r] = _core_attention(q[b, r], ents, epos, t, sink, gamma_q, gamma_kv, rope_dims, scale, eps,
-                                    rope_base)
+                                    rope_base, vis if comp_prepared else 0)
     return out

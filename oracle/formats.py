@@ -106,6 +106,28 @@ def decode_mxfp4(packed, scales) -> np.ndarray:
     return (vals.reshape(vals.shape[:-1] + (n // 32, 32)) * sc[..., None]).reshape(vals.shape)
 
 
+def encode_fp8_rope_rows(x: np.ndarray, rope_dims: int):
+    """Prepared KV rows [..., c] in the mixed storage the pages give for KV entries ("【论文解读】DeepSeek-V4",
+    section 一(三)4, item 1; "DeepseekV4论文解析" on numerical precision): the RoPE dims in bf16, the others
+    in fp8.  Returns (bytes [..., c + R] uint8, scale [...]): the first c - R values as e4m3 codes of
+    value/scale with scale = amax/448 of those values (as encode_fp8_rows), then the R RoPE values as
+    little-endian bf16."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1] - rope_dims
+    codes, scale = encode_fp8_rows(x[..., :n])
+    bf = np.ascontiguousarray(encode_bf16(x[..., n:])).view(np.uint8)
+    return np.concatenate([codes, bf], axis=-1), scale
+
+
+def decode_fp8_rope_rows(data, scale, rope_dims: int) -> np.ndarray:
+    """Exact float64 values of rows stored by encode_fp8_rope_rows (c = bytes - R)."""
+    data = np.ascontiguousarray(np.asarray(data, dtype=np.uint8))
+    n = data.shape[-1] - 2 * rope_dims
+    fp = decode_fp8_e4m3(data[..., :n]) * np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None]
+    bf = decode_bf16(np.ascontiguousarray(data[..., n:]).view(np.uint16))
+    return np.concatenate([fp, bf], axis=-1)
+
+
 def dequant_rows(data, scale, fmt: str) -> np.ndarray:
     """Exact float64 values of stored indexer rows."""
     if fmt == "f32":

@@ -179,3 +179,33 @@ def test_window_clipping_and_no_compressed_entries():
     qh = oracle.rope(oracle.rmsnorm(q[0, 0, 0]), 0.0, rd, 10000.0)
     p = 1.0 / (1.0 + np.exp(sink[0] - qh @ eh / np.sqrt(c)))
     assert np.allclose(out[0, 0, 0], p * eh, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_prepared_entries_equal_raw_entries(mode):
+    """comp_prepared: handing attend the prepared e^ = RoPE_{m s}(RMSNorm_gamma(e)) of every compressed
+    entry gives the raw-entry result (only the place of the preparation moves); a wrong position or a
+    missing gain would break it."""
+    r = np.random.default_rng(7)
+    B, T, H, c, R, m, N, n_win = 2, 3, 4, 32, 8, 4, 40, 5
+    q = r.standard_normal((B, T, H, c))
+    comp = r.standard_normal((B, N, c))
+    win = r.standard_normal((B, T + n_win - 1, c))
+    sink = r.standard_normal(H)
+    gk = r.uniform(0.5, 1.5, c)
+    pos0 = np.array([4 * 30 + 1, 4 * 12])
+    prep = oracle.rope(oracle.rmsnorm(comp, gk, 1e-6), m * np.arange(N, dtype=np.float64)[None, :], R, 1e4)
+    if mode == "csa":
+        idx = np.stack([np.sort(r.choice(min(int(p) // m, N), 6, replace=False)) for p in pos0])[:, None, :]
+        idx = np.repeat(idx, T, axis=1)
+        a = oracle.attend(q, comp, idx, win, sink, pos0, m, n_win, R, 0.3, gamma_kv=gk)
+        b = oracle.attend(q, prep, idx, win, sink, pos0, m, n_win, R, 0.3, gamma_kv=gk, comp_prepared=True)
+        wrong = oracle.attend(q, oracle.rmsnorm(comp, gk, 1e-6), idx, win, sink, pos0, m, n_win, R, 0.3,
+                              gamma_kv=gk, comp_prepared=True)
+    else:
+        a = oracle.hca_attend(q, comp, win, sink, pos0, m, n_win, R, 0.3, gamma_kv=gk)
+        b = oracle.hca_attend(q, prep, win, sink, pos0, m, n_win, R, 0.3, gamma_kv=gk, comp_prepared=True)
+        wrong = oracle.hca_attend(q, oracle.rmsnorm(comp, gk, 1e-6), win, sink, pos0, m, n_win, R, 0.3,
+                                  gamma_kv=gk, comp_prepared=True)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    assert not np.allclose(a, wrong, atol=1e-3)

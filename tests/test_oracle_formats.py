@@ -118,3 +118,40 @@ def test_mxfp4_round_trip_bound_and_encoders_agree():
 def test_e2m1_ties_to_even(v, expect):
     code = sf.e2m1_encode(np.array([v]))
     assert oracle.decode_e2m1(code)[0] == expect
+
+
+def test_fp8_rope_rows_layout_and_values():
+    """The mixed KV row: c - R e4m3 codes of value/scale (scale = amax/448 of those values), then the R
+    RoPE values as little-endian bf16.  A hand-built row: the largest fp8-part value maps to code 0x7E
+    (448), a value of a quarter of it to 0x6E (112), a negative one to the sign bit set, zero to 0."""
+    c, R = 32, 16
+    x = np.zeros((1, c))
+    x[0, 0] = 3.5            # amax: scale = 3.5 / 448
+    x[0, 1] = 3.5 / 4        # 112 * scale
+    x[0, 2] = -3.5 / 4
+    x[0, 16] = 1.0           # RoPE part: bf16 1.0 = 0x3F80
+    x[0, 31] = -2.5          # 0xC020
+    data, scale = oracle.encode_fp8_rope_rows(x, R)
+    assert data.shape == (1, c + R) and data.dtype == np.uint8
+    assert scale[0] == 3.5 / 448
+    assert list(data[0, :4]) == [0x7E, 0x6E, 0xEE, 0x00]
+    bf = data[0, c - R:].view(np.uint16)
+    assert bf[0] == 0x3F80 and bf[15] == 0xC020 and np.all(bf[1:15] == 0)
+    back = oracle.decode_fp8_rope_rows(data, scale, R)
+    assert np.array_equal(back, x)
+
+
+def test_fp8_rope_rows_round_trip_bound():
+    """Decoded values: RoPE dims within bf16 rounding (2^-8 relative), the others within half an e4m3
+    step of their scaled value (at most 2^-4 relative above 2^-6 * scale, 2^-10 * scale absolute below)."""
+    r = np.random.default_rng(3)
+    x = r.standard_normal((50, 512))
+    data, scale = oracle.encode_fp8_rope_rows(x, 64)
+    back = oracle.decode_fp8_rope_rows(data, scale, 64)
+    fp, rp = x[:, :448], x[:, 448:]
+    assert np.all(np.abs(back[:, 448:] - rp) <= np.abs(rp) * 2.0 ** -8)
+    err = np.abs(back[:, :448] - fp)
+    s = scale[:, None]
+    assert np.all(err <= np.maximum(np.abs(fp) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 1e-12))
+    # the largest fp8-part value comes back as 448 times the scale, stored in float32
+    assert np.allclose(np.max(np.abs(back[:, :448]), axis=1), np.max(np.abs(fp), axis=1), rtol=2e-7)
