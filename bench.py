@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--eager", action="store_true", help="launch the step's calls one by one (no HIP graph)")
     p.add_argument("--scores", default="f32", choices=("f32", "bf16"),
                    help="index-score storage between the indexer and the selector (bf16: the rounded variant)")
+    p.add_argument("--kv", default="bf16", choices=("bf16", "fp8rope"),
+                   help="compressed KV cache storage: bf16 rows, or the non-RoPE dims in fp8 e4m3 with a row scale "
+                        "and the RoPE dims in bf16")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -167,9 +170,18 @@ def main():
     # compressed entries are stored prepared for attention (RMSNorm + RoPE at their positions, done once when
     # an entry is written); the synthetic context caches are prepared here, outside the timed region
     prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
-    api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)
-    if cfg.with_hca:
-        api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
+    mixed = a.kv == "fp8rope"
+    kv_scale = hca_scale = None
+    if mixed:   # caches in the fp8 + bf16 RoPE rows (c + R bytes) with one float32 scale per row
+        kv_cache, kv_scale = api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out_fmt="fp8rope")
+        if cfg.with_hca:
+            hca_cache, hca_scale = api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out_fmt="fp8rope")
+        torch.cuda.synchronize()
+    else:
+        api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)
+        if cfg.with_hca:
+            api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
+    cache_fmt = dict(out_fmt="fp8rope") if mixed else {}
     T = cfg.T
     # window rows: prefill (CSA) and the HCA layer also keep the token rows prepared (each row once, at its own
     # position, when it is written); rows of earlier steps are prepared here, the step's own T rows in the step
@@ -210,14 +222,17 @@ def main():
                 c = st["chca"]
                 api.compress(c["ca"], None, c["za"], None, c["bias_a"], None, cfg.m_hca, c["row0_pos"],
                              c["first_entry"], c["num_entries"], out=hca_cache[:, c["first_entry"]:],
-                             out_batch_stride=cfg.n_hca, prep=prep, stream=side)
+                             out_scale=hca_scale[:, c["first_entry"]:] if mixed else None,
+                             out_batch_stride=cfg.n_hca, prep=prep, stream=side, **cache_fmt)
                 api.prepare_kv(st["hwin"][:, cfg.n_win - 1:], prep, out=st["phwin"][:, cfg.n_win - 1:],
                                stream=side, **win_new)
                 api.hca_attend(st["hq"], hca_cache, st["phwin"], st["hsink"], pos, cfg.m_hca, cfg.n_win,
                                cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=hout, ws=hca_ws, stream=side,
-                               kv_prepared=2)
+                               kv_prepared=2, comp_scale=hca_scale)
         c = st["cik"]
-        kv_job = dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep)
+        kv_job = dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep, **cache_fmt)
+        if mixed:
+            kv_job["out_scale"] = kv_scale[:, first:]
         if T == 1:
             # decode: the block's KV entry and its indexer key (into the key cache) are computed inside the
             # index launch, by the workgroups that need them first
@@ -235,7 +250,7 @@ def main():
                       bound=bound)
         api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
-                   cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode)
+                   cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode, comp_scale=kv_scale)
         if side is not None:
             main_s.wait_stream(side)
 
@@ -336,7 +351,7 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "query_rows": T, "context": cfg.pos0, "compressed_entries": N,
                    "heads": cfg.H,
                    "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
-                   "hca_entries": cfg.n_hca if cfg.with_hca else 0, "index_scores": a.scores,
+                   "hca_entries": cfg.n_hca if cfg.with_hca else 0, "index_scores": a.scores, "kv_cache": a.kv,
                    "input_sets_rotated": NSETS},
         "roofline": roofline,
         "setup_s": round(t_setup, 1),

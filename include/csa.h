@@ -39,8 +39,13 @@ typedef enum {
   CSA_F32 = 0,               /* IEEE binary32                                                    */
   CSA_BF16 = 1,              /* bfloat16, stored as uint16                                        */
   CSA_FP8_E4M3_ROWSCALE = 2, /* OCP fp8 E4M3 bytes + one float32 scale per row (value = code*scale) */
-  CSA_MXFP4_E8M0_B32 = 3     /* OCP MXFP4: e2m1 pairs (element 2i in the low nibble) + one E8M0    */
+  CSA_MXFP4_E8M0_B32 = 3,    /* OCP MXFP4: e2m1 pairs (element 2i in the low nibble) + one E8M0    */
                              /* scale byte per 32 elements (value = e2m1 * 2^(scale-127))          */
+  CSA_FP8_BF16_ROPE = 4      /* prepared KV row of c values with R RoPE dims: the first c-R values */
+                             /* as OCP fp8 E4M3 bytes with one float32 scale per row (value =      */
+                             /* code*scale, scale = amax/448 of those values), then the R RoPE     */
+                             /* values as bf16; c + R bytes per row, the scales in their own array */
+                             /* (the mixed KV storage of the same page, section 一(三)4, item 1)   */
 } csa_dtype;
 
 typedef enum {
@@ -94,10 +99,13 @@ int csa_abi_version(void);
  *                    row indexing) = amax/448, codes = RNE(x/scale) saturated;
  *                    CSA_MXFP4_E8M0_B32: c/2 bytes per row, and out_scale (uint8,
  *                    c/32 per row) = floor(log2 amax) - 2 + 127, codes RNE,
- *                    saturated at 6.  out_scale is ignored for F32 / BF16.
+ *                    saturated at 6.  CSA_FP8_BF16_ROPE (prepared entries only,
+ *                    R = prep->rope_dims, c - R a multiple of 16): c + R bytes per
+ *                    row, out_scale float32 per row.  out_scale is ignored for
+ *                    F32 / BF16.
  *   prep           : NULL, or the entries are stored prepared for attention
- *                    (see csa_kv_prep) at position m * i; CSA_F32 / CSA_BF16
- *                    outputs only.
+ *                    (see csa_kv_prep) at position m * i; CSA_F32 / CSA_BF16 /
+ *                    CSA_FP8_BF16_ROPE outputs only.
  * Limits: 1 <= m <= 1024, c a multiple of 4 and <= 1024 (of 32 for MXFP4).
  */
 csa_status csa_compress(const void* ca, const void* cb, const void* za, const void* zb,
@@ -133,14 +141,17 @@ csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, 
  * csa_prepare_kv -- prepares KV rows for attention (see csa_kv_prep).
  *   in  : [B] blocks of `rows` rows of c values in in_t (CSA_F32 / CSA_BF16);
  *         row j of sequence b at in + (b * in_batch_stride + j) * c.
- *   out : the same layout with out_batch_stride, in out_t; may alias `in`.
+ *   out : the same layout with out_batch_stride, in out_t (CSA_F32, CSA_BF16, or
+ *         CSA_FP8_BF16_ROPE with c + R bytes per row and out_scale float32 per
+ *         row, R = prep->rope_dims, c - R a multiple of 16); may alias `in` for
+ *         the same type and layout.
  *   position of row j of sequence b: (pos_base ? pos_base[b] : 0) + pos_first
  *   + j * pos_stride (pos_base a device int64 [B] array), e.g. pos_stride = m
  *   for a compressed cache, 1 for token rows.  prep must not be NULL.
  * Limits: c a multiple of 4 and <= 1024; R as in csa_kv_prep.
  */
-csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, int64_t out_batch_stride,
-                          int B, int rows, int c, int in_t, int out_t,
+csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, void* out_scale,
+                          int64_t out_batch_stride, int B, int rows, int c, int in_t, int out_t,
                           const int64_t* pos_base, int64_t pos_first, int64_t pos_stride,
                           const csa_kv_prep* prep, void* stream);
 
@@ -190,8 +201,10 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  * where job 1's output is the key cache itself: entry first_entry of k (and
  * k_scale), stored in qk_t (fp8 with its row scale, MXFP4 with its block
  * scales, or bf16), read by the index scores of the same launch.
- *   job 0 : ca0 .. bias_b0, c0, out0 (CSA_F32 / CSA_BF16 rows [B][..][c0] with
- *           batch stride out_batch_stride0, 0 = 1), prep0 as in csa_compress.
+ *   job 0 : ca0 .. bias_b0, c0, out0 (CSA_F32 / CSA_BF16 rows [B][..][c0], or
+ *           CSA_FP8_BF16_ROPE rows with prep0 and their scales in out_scale0,
+ *           with batch stride out_batch_stride0, 0 = 1), prep0 as in
+ *           csa_compress.
  *   job 1 : ca1 .. bias_b1 with c = cI.
  *   shared: B, rows, m (< 64), row0_pos, first_entry (< n_max), in_t, as in
  *           csa_compress_pair with num_entries = 1.
@@ -200,7 +213,8 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  * Each argument group is validated as by the corresponding entry point.
  */
 csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0, const void* zb0,
-                              const float* bias_a0, const float* bias_b0, int c0, void* out0, int out_t0,
+                              const float* bias_a0, const float* bias_b0, int c0, void* out0, void* out_scale0,
+                              int out_t0,
                               int64_t out_batch_stride0, const csa_kv_prep* prep0,
                               const void* ca1, const void* cb1, const void* za1, const void* zb1,
                               const float* bias_a1, const float* bias_b1,
@@ -249,7 +263,12 @@ csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max
  * RMSNorm: x / sqrt(mean(x^2) + eps) * gamma over all c dims (gamma NULL = 1).
  * RoPE: pairs (c-R+2i, c-R+2i+1), R = rope_dims, angle pos * rope_base^(-2i/R).
  *
- *   q       : [B][T][H][c] in kv_t        comp_kv : [B][n_max][c] in kv_t
+ *   q       : [B][T][H][c] in kv_t        comp_kv : [B][n_max][c] in comp_t
+ *   comp_t  : kv_t, or CSA_FP8_BF16_ROPE (kv_t CSA_BF16, kv_prepared >= 1,
+ *             c - rope_dims a multiple of 16): rows of c + rope_dims bytes with
+ *             their scales in comp_scale (float32 [B][n_max]); otherwise
+ *             comp_scale is ignored.  Rows are widened to bf16 in LDS
+ *             (code * scale, rounded to nearest even) before use.
  *   idx     : int32 [B][T][k]; entries < 0 or >= n_max are skipped
  *   win_kv  : [B][T + n_win - 1][c] in kv_t; row j holds position pos0[b]-n_win+1+j
  *   sink    : float32 [H]     gamma_q, gamma_kv : float32 [c] or NULL
@@ -275,27 +294,27 @@ csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max
  * 1 <= n_win <= 4096.
  */
 size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win);
-csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
-                      const float* sink, const float* gamma_q, const float* gamma_kv,
+csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                      const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv,
                       int B, int T, int H, int c, int rope_dims, int k, int n_win, int64_t n_max,
                       const int64_t* pos0, int m, float scale, float eps, float rope_base,
-                      int kv_t, int kv_prepared, void* out, int out_t,
+                      int kv_t, int comp_t, int kv_prepared, void* out, int out_t,
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * hca_attend -- HCA core attention ([HCA] (2)): as csa_attend, with the
  * compressed part dense: every visible entry s < min(floor(t/m_hca), n_max) of
- * comp_kv, each at position m_hca * s.  Same layouts, limits, kv_prepared rule
- * (prepared entries at pos_stride = m_hca; with 2 and H a multiple of 64, decode
- * also runs the 64-head variant) and workspace rule
+ * comp_kv, each at position m_hca * s.  Same layouts, limits, comp_t and
+ * kv_prepared rules (prepared entries at pos_stride = m_hca; with 2 and H a
+ * multiple of 64, decode also runs the 64-head variant) and workspace rule
  * (hca_attend_workspace_bytes).
  */
 size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win);
-csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv,
+csa_status hca_attend(const void* q, const void* comp_kv, const float* comp_scale, const void* win_kv,
                       const float* sink, const float* gamma_q, const float* gamma_kv,
                       int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
                       const int64_t* pos0, int m_hca, float scale, float eps, float rope_base,
-                      int kv_t, int kv_prepared, void* out, int out_t,
+                      int kv_t, int comp_t, int kv_prepared, void* out, int out_t,
                       void* workspace, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -10,7 +10,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa.so")
 
-F32, BF16, FP8_E4M3_ROWSCALE, MXFP4_E8M0_B32 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3_ROWSCALE, MXFP4_E8M0_B32, FP8_BF16_ROPE = 0, 1, 2, 3, 4
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_UNSUPPORTED", 4: "CSA_ERR_WORKSPACE",
           5: "CSA_ERR_LAUNCH"}
 
@@ -30,8 +30,8 @@ SIGNATURES = {
     "csa_compress": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I64, _I, _I, _P, _P, _I, _I64, _PREP, _P]),
     "csa_compress_pair": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _PREP, _P, _P, _P, _P, _P, _P, _I, _P,
                                _P, _I, _I64, _PREP, _I, _I, _I, _I64, _I64, _I, _I, _P]),
-    "csa_prepare_kv": (_I, [_P, _I64, _P, _I64, _I, _I, _I, _I, _I, _P, _I64, _I64, _PREP, _P]),
-    "csa_compress_index": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _I, _I64, _PREP,
+    "csa_prepare_kv": (_I, [_P, _I64, _P, _P, _I64, _I, _I, _I, _I, _I, _P, _I64, _I64, _PREP, _P]),
+    "csa_compress_index": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _PREP,
                                 _P, _P, _P, _P, _P, _P,
                                 _I, _I, _I, _I64, _I64, _I,
                                 _P, _P, _P, _P, _P, _I, _I, _I64, _P, _I, _P, _I, _P, _P]),
@@ -40,11 +40,11 @@ SIGNATURES = {
     "csa_topk_workspace_bytes": (_SZ, [_I, _I, _I64, _I]),
     "csa_topk": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "csa_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
-    "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I,
-                        _P, _I, _P, _SZ, _P]),
+    "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I,
+                        _I, _I, _P, _I, _P, _SZ, _P]),
     "hca_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I64, _I]),
-    "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _P, _I,
-                        _P, _SZ, _P]),
+    "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _I,
+                        _P, _I, _P, _SZ, _P]),
 }
 
 _lib = None

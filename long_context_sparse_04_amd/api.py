@@ -14,7 +14,8 @@ import torch
 from . import _lib
 from ._lib import CSAError
 
-FMT = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3_ROWSCALE, "mxfp4": _lib.MXFP4_E8M0_B32}
+FMT = {"f32": _lib.F32, "bf16": _lib.BF16, "fp8": _lib.FP8_E4M3_ROWSCALE, "mxfp4": _lib.MXFP4_E8M0_B32,
+       "fp8rope": _lib.FP8_BF16_ROPE}
 _TORCH_FMT = {torch.float32: "f32", torch.bfloat16: "bf16"}
 
 _ws_cache: dict = {}
@@ -27,6 +28,15 @@ def _ptr(t):
         raise CSAError("tensor must live on the GPU")
     if not t.is_contiguous():
         raise CSAError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _dptr(t):
+    """Device address of a tensor that may be a strided view (rows at a batch stride the call is given)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CSAError("tensor must live on the GPU")
     return t.data_ptr()
 
 
@@ -76,6 +86,9 @@ def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entri
         elif out_fmt == "fp8":
             out = torch.empty((B, num_entries, c), dtype=torch.uint8, device=dev)
             out_scale = torch.empty((B, num_entries), dtype=torch.float32, device=dev)
+        elif out_fmt == "fp8rope":   # prepared entries: c - R fp8 bytes + R bf16 RoPE dims, one scale per row
+            out = torch.empty((B, num_entries, c + prep.rope_dims), dtype=torch.uint8, device=dev)
+            out_scale = torch.empty((B, num_entries), dtype=torch.float32, device=dev)
         else:
             out = torch.empty((B, num_entries, c // 2), dtype=torch.uint8, device=dev)
             out_scale = torch.empty((B, num_entries, c // 32), dtype=torch.uint8, device=dev)
@@ -87,13 +100,16 @@ def compress(ca, cb, za, zb, bias_a, bias_b, m, row0_pos, first_entry, num_entri
     return out, out_scale
 
 
-def _compress_out(B, num_entries, c, fmt, dev):
+def _compress_out(B, num_entries, c, fmt, dev, rope_dims=0):
     if fmt == "f32":
         return torch.empty((B, num_entries, c), dtype=torch.float32, device=dev), None
     if fmt == "bf16":
         return torch.empty((B, num_entries, c), dtype=torch.bfloat16, device=dev), None
     if fmt == "fp8":
         return (torch.empty((B, num_entries, c), dtype=torch.uint8, device=dev),
+                torch.empty((B, num_entries), dtype=torch.float32, device=dev))
+    if fmt == "fp8rope":
+        return (torch.empty((B, num_entries, c + rope_dims), dtype=torch.uint8, device=dev),
                 torch.empty((B, num_entries), dtype=torch.float32, device=dev))
     return (torch.empty((B, num_entries, c // 2), dtype=torch.uint8, device=dev),
             torch.empty((B, num_entries, c // 32), dtype=torch.uint8, device=dev))
@@ -112,7 +128,8 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
         fmt = p.get("out_fmt") or in_fmt
         out, osc = p.get("out"), p.get("out_scale")
         if out is None:
-            out, osc = _compress_out(B, num_entries, c, fmt, p["ca"].device)
+            prep = p.get("prep")
+            out, osc = _compress_out(B, num_entries, c, fmt, p["ca"].device, prep.rope_dims if prep else 0)
         args += [_ptr(p["ca"]), _ptr(p.get("cb")), _ptr(p["za"]), _ptr(p.get("zb")), _ptr(p["bias_a"]),
                  _ptr(p.get("bias_b")), c, out.data_ptr(), None if osc is None else osc.data_ptr(), FMT[fmt],
                  p.get("out_batch_stride", 0), _prep_arg(p.get("prep"))]
@@ -125,8 +142,8 @@ def compress_pair(p0, p1, m, row0_pos, first_entry, num_entries, stream=None):
 def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_scale, pos0, fmt, scores=None,
                    bound=None, stream=None, score_fmt="f32"):
     """csa_compress_index: compress_pair(p_kv, p_ik) for entry first_entry (one per sequence) and a decode index
-    (T = 1), one launch.  p_kv: dict as in compress_pair (out required, f32 / bf16, optional out_batch_stride,
-    prep); p_ik: the indexer-key streams, whose entry is written into k / k_scale at first_entry.  Returns
+    (T = 1), one launch.  p_kv: dict as in compress_pair (out required: f32 / bf16, or uint8 rows in the fp8 +
+    bf16 RoPE format with out_scale; optional out_batch_stride, prep); p_ik: the indexer-key streams, whose entry is written into k / k_scale at first_entry.  Returns
     the scores."""
     lib = _lib.load()
     B, rows, c0 = p_kv["ca"].shape
@@ -139,7 +156,8 @@ def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_sca
         scores = _score_buf(B, 1, N, score_fmt, q.device)
     st = lib.csa_compress_index(
         _ptr(p_kv["ca"]), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]), _ptr(p_kv.get("zb")), _ptr(p_kv["bias_a"]),
-        _ptr(p_kv.get("bias_b")), c0, out0.data_ptr(), FMT[_TORCH_FMT[out0.dtype]], p_kv.get("out_batch_stride", 0),
+        _ptr(p_kv.get("bias_b")), c0, _dptr(out0), _dptr(p_kv.get("out_scale")),
+        FMT["fp8rope"] if out0.dtype == torch.uint8 else FMT[_TORCH_FMT[out0.dtype]], p_kv.get("out_batch_stride", 0),
         _prep_arg(p_kv.get("prep")),
         _ptr(p_ik["ca"]), _ptr(p_ik.get("cb")), _ptr(p_ik["za"]), _ptr(p_ik.get("zb")), _ptr(p_ik["bias_a"]),
         _ptr(p_ik.get("bias_b")),
@@ -197,32 +215,53 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
     return idx, vals
 
 
-def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_fmt=None, stream=None):
+def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_fmt=None, stream=None,
+               out_scale=None):
     """csa_prepare_kv: rows x [B][rows][c] -> RoPE_pos(RMSNorm(x)), row j of sequence b at position
-    (pos_base[b] if given) + pos_first + j * pos_stride.  out may be x itself (in place)."""
+    (pos_base[b] if given) + pos_first + j * pos_stride.  out may be x itself (in place).  With
+    out_fmt="fp8rope" the rows are stored as uint8 [B][rows][c + R] with float32 scales [B][rows], and
+    (out, out_scale) is returned."""
     lib = _lib.load()
     B, rows, c = x.shape
     in_fmt = _TORCH_FMT[x.dtype]
     out_fmt = out_fmt or in_fmt
+    mixed = out_fmt == "fp8rope"
+    ob = c + prep.rope_dims if mixed else c   # output row length in elements of out's dtype
     if out is None:
-        out = torch.empty((B, rows, c), dtype=torch.float32 if out_fmt == "f32" else torch.bfloat16, device=x.device)
-    if out.shape != x.shape:
-        raise CSAError(f"prepare_kv: out shape {tuple(out.shape)} differs from {tuple(x.shape)}")
-    for t in (x, out):   # rows of one sequence contiguous; sequences may sit at any row stride (views)
-        if t.stride(2) != 1 or t.stride(1) != c or t.stride(0) % c:
+        dt = torch.uint8 if mixed else (torch.float32 if out_fmt == "f32" else torch.bfloat16)
+        out = torch.empty((B, rows, ob), dtype=dt, device=x.device)
+    if mixed and out_scale is None:
+        out_scale = torch.empty((B, rows), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (B, rows, ob):
+        raise CSAError(f"prepare_kv: out shape {tuple(out.shape)} is not {(B, rows, ob)}")
+    for t, n in ((x, c), (out, ob)):   # rows of one sequence contiguous; sequences may sit at any row stride
+        if t.stride(2) != 1 or t.stride(1) != n or t.stride(0) % n:
             raise CSAError("prepare_kv: rows must be contiguous with a whole-row batch stride")
     for t in (x, out):
         if not t.is_cuda:
             raise CSAError("tensor must live on the GPU")
-    st = lib.csa_prepare_kv(x.data_ptr(), x.stride(0) // c, out.data_ptr(), out.stride(0) // c, B, rows, c, FMT[in_fmt],
-                            FMT[out_fmt], _ptr(pos_base), pos_first, pos_stride, _prep_arg(prep), _stream(stream))
+    if mixed and (out_scale.stride(1) != 1 or out_scale.stride(0) != out.stride(0) // ob):
+        raise CSAError("prepare_kv: out_scale must follow out's row layout")
+    st = lib.csa_prepare_kv(x.data_ptr(), x.stride(0) // c, out.data_ptr(), _ptr(out_scale), out.stride(0) // ob, B,
+                            rows, c, FMT[in_fmt], FMT[out_fmt], _ptr(pos_base), pos_first, pos_stride,
+                            _prep_arg(prep), _stream(stream))
     _lib.check(st, "csa_prepare_kv")
-    return out
+    return (out, out_scale) if mixed else out
+
+
+def _comp_t(comp_kv, comp_scale, kv_fmt):
+    if comp_kv.dtype == torch.uint8:   # rows in CSA_FP8_BF16_ROPE with their scales
+        if comp_scale is None:
+            raise CSAError("comp_kv in the fp8 + bf16 RoPE format needs comp_scale")
+        return FMT["fp8rope"]
+    return FMT[kv_fmt]
 
 
 def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-           gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False):
-    """csa_attend.  q [B][T][H][c], comp_kv [B][N][c], idx int32 [B][T][k], win_kv [B][T+n_win-1][c]."""
+           gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False,
+           comp_scale=None):
+    """csa_attend.  q [B][T][H][c], comp_kv [B][N][c] (or uint8 [B][N][c + R] in the fp8 + bf16 RoPE format,
+    with comp_scale [B][N]), idx int32 [B][T][k], win_kv [B][T+n_win-1][c]."""
     lib = _lib.load()
     B, T, H, c = q.shape
     k = idx.shape[2]
@@ -234,15 +273,17 @@ def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=
     nb = lib.csa_attend_workspace_bytes(B, T, H, c, k, n_win)
     if ws is None:
         ws = workspace(nb, q.device, "attend")
-    st = lib.csa_attend(_ptr(q), _ptr(comp_kv), _ptr(idx), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv),
-                        B, T, H, c, rope_dims, k, n_win, N, _ptr(pos0), m, scale, eps, rope_base, FMT[kv_fmt],
-                        int(kv_prepared), _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+    st = lib.csa_attend(_ptr(q), _ptr(comp_kv), _ptr(comp_scale), _ptr(idx), _ptr(win_kv), _ptr(sink), _ptr(gamma_q),
+                        _ptr(gamma_kv), B, T, H, c, rope_dims, k, n_win, N, _ptr(pos0), m, scale, eps, rope_base,
+                        FMT[kv_fmt], _comp_t(comp_kv, comp_scale, kv_fmt), int(kv_prepared), _ptr(out), FMT[out_fmt],
+                        _ptr(ws), nb, _stream(stream))
     _lib.check(st, "csa_attend")
     return out
 
 
 def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, eps=1e-6, rope_base=10000.0,
-               gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False):
+               gamma_q=None, gamma_kv=None, out=None, out_fmt=None, ws=None, stream=None, kv_prepared=False,
+               comp_scale=None):
     """hca_attend: dense over every visible compressed entry s < floor(t/m_hca), plus the window."""
     lib = _lib.load()
     B, T, H, c = q.shape
@@ -254,8 +295,9 @@ def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, e
     nb = lib.hca_attend_workspace_bytes(B, T, H, c, N, n_win)
     if ws is None:
         ws = workspace(nb, q.device, "hca")
-    st = lib.hca_attend(_ptr(q), _ptr(comp_kv), _ptr(win_kv), _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv), B, T, H, c,
-                        rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base, FMT[kv_fmt],
-                        int(kv_prepared), _ptr(out), FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+    st = lib.hca_attend(_ptr(q), _ptr(comp_kv), _ptr(comp_scale), _ptr(win_kv), _ptr(sink), _ptr(gamma_q),
+                        _ptr(gamma_kv), B, T, H, c, rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base,
+                        FMT[kv_fmt], _comp_t(comp_kv, comp_scale, kv_fmt), int(kv_prepared), _ptr(out),
+                        FMT[out_fmt], _ptr(ws), nb, _stream(stream))
     _lib.check(st, "hca_attend")
     return out

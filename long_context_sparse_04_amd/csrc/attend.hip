@@ -58,6 +58,8 @@ struct AttnArgs {
   float* ws_ml;    // [rows][nsplit][H][2]
   int T, H, R, k, n_win, m, out_t, mode, nsplit;
   int prepared;           // 0 raw rows; 1 compressed entries stored prepared; 2 window rows prepared too
+  const float* comp_scale;  // comp_mixed: the compressed rows' fp8 scales [B][n_max]
+  int comp_mixed;           // compressed rows in CSA_FP8_BF16_ROPE (c + R bytes), widened to bf16 in LDS
   int ns_c, s_c, s_w;     // split layout: ns_c compressed parts of s_c slots, then window parts of s_w
   int64_t n_max;
   float scale, eps;
@@ -239,11 +241,20 @@ CSA_DEV int swz(int e, int c) { return c ^ swz_key(e & 15); }
 
 constexpr int kStage = 64;  // slots fetched into LDS at once (2 compute tiles)
 
+// Bytes of the attention kernel's per-slot control arrays in LDS (in 2-byte units, rounded up to 16 bytes).
+template <bool WIDE>
+constexpr int lds_ctrl_halfs() {
+  constexpr int ne = WIDE ? 2 : 1, nr = WIDE ? 3 : 2;
+  constexpr int bytes = 64 * 8 + nr * kStage * (8 + 8 + 8) + (kStage + 64) * 4 + nr * kStage * 4 + 3 * kStage * 4 +
+                        ne * kStage * 4 + 2 * nr * 4;
+  return ((bytes + 15) / 16) * 8;
+}
+
 // One workgroup = one query row x one part of its slot list x 16 heads; wave w owns dims
 // [w*C/4, (w+1)*C/4).  Per stage: (1) resolve 64 slots (row address, position, validity),
 // (2) DMA every row straight into LDS (global_load_lds, 16 B per lane, no registers),
 // (3) per-entry RMS scalar and RoPE in place, (4) two 32-slot tiles of MFMA work from LDS.
-template <int C, bool WIDE, bool RAW>
+template <int C, bool WIDE, bool RAW, bool MIX>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int nx) {
   // RAW: rows may need RMSNorm / RoPE here (raw compressed entries or raw window rows); without it every
   // row is stored prepared and the kernel has no normalisation or rotation of entries at all
@@ -259,17 +270,22 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   // fetch stage s + 1 while it computes stage s; slot resolution then runs two stages ahead (3 buffers)
   constexpr int NE = WIDE ? 2 : 1;  // LDS stage buffers
   constexpr int NR = WIDE ? 3 : 2;  // slot-resolution buffers
+  // LDS: the per-slot control arrays first (their addresses stay below 64 KB, where LDS instructions take
+  // them as immediate offsets), then the narrow variant's logit exchange, then the stage buffers
   extern __shared__ __align__(16) uint16_t s_mem[];
-  uint16_t* E0 = s_mem;                                                    // [NE][kStage][C]
-  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + NE * kStage * C);       // [4 waves][2][64 lanes] (narrow)
-  float* s_re = reinterpret_cast<float*>(s_part + (WIDE ? 0 : 4 * 2 * 64));  // [kStage]
-  float* s_rq = s_re + kStage;                                             // [4][16]
-  double* s_theta = reinterpret_cast<double*>(s_rq + 64);                  // [64]
+  double* s_theta = reinterpret_cast<double*>(s_mem);                      // [64]
   double* s_pos2 = s_theta + 64;                                           // [NR][kStage]
   const uint16_t** s_src2 = reinterpret_cast<const uint16_t**>(s_pos2 + NR * kStage);  // [NR][kStage]
-  int* s_flag2 = reinterpret_cast<int*>(s_src2 + NR * kStage);             // [NR][kStage] 1 valid | 2 raw
-  int* s_raw2 = s_flag2 + NR * kStage;                                     // [NR] stage holds a raw row
-  int* s_idx3 = s_raw2 + NR;  // [3][kStage] (wide, CSA) index-list values, fetched two stages ahead
+  const float** s_scp2 = reinterpret_cast<const float**>(s_src2 + NR * kStage);       // [NR][kStage]
+  float* s_re = reinterpret_cast<float*>(s_scp2 + NR * kStage);            // [kStage]
+  float* s_rq = s_re + kStage;                                             // [4][16]
+  int* s_flag2 = reinterpret_cast<int*>(s_rq + 64);                        // [NR][kStage] 1 valid | 2 raw | 4 mixed
+  int* s_idx3 = s_flag2 + NR * kStage;  // [3][kStage] (wide, CSA) index-list values, fetched two stages ahead
+  float* s_scale = reinterpret_cast<float*>(s_idx3 + 3 * kStage);          // [NE][kStage] mixed rows' fp8 scales
+  int* s_raw2 = reinterpret_cast<int*>(s_scale + NE * kStage);             // [NR] stage holds a raw row
+  int* s_mix2 = s_raw2 + NR;                                               // [NR] stage holds mixed rows
+  f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + lds_ctrl_halfs<WIDE>());  // [4 waves][2][64 lanes] (narrow)
+  uint16_t* E0 = reinterpret_cast<uint16_t*>(s_part + (WIDE ? 0 : 4 * 2 * 64));  // [NE][kStage][C]
 
   if ((int)blockIdx.x >= nx) return;  // grid.x is padded to a multiple of 8 (XCD-aligned head groups)
   const int lane = threadIdx.x & 63;
@@ -312,15 +328,28 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       sl.row = -1;
       if (slot < slot_hi) sl = resolve_slot(a, r, t, vis, slot, e_idx);
       const bool valid = sl.row >= 0;
-      s_src2[h * kStage + threadIdx.x] = valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
-                                                            : a.comp + ((int64_t)b * a.n_max + sl.row) * C)
-                                               : dummy;
+      // compressed rows in the mixed format: c + R bytes each, and their scale
+      const bool mixed = MIX && valid && !sl.is_win;
+      const int64_t crow = (int64_t)b * a.n_max + sl.row;
+      const uint16_t* cptr = mixed ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.comp) +
+                                                                       crow * (C + a.R))
+                                   : a.comp + crow * C;
+      // (a mixed row's address carries a 1 in bit 0: its rows start on 16-byte boundaries)
+      s_src2[h * kStage + threadIdx.x] =
+          valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
+                             : reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(cptr) | (mixed ? 1u : 0u)))
+                : dummy;
+      if (MIX) s_scp2[h * kStage + threadIdx.x] = mixed ? a.comp_scale + crow : a.sink;  // (readable when unused)
       s_pos2[h * kStage + threadIdx.x] = sl.pos;
       // raw rows (window tokens, or compressed entries not stored prepared) get RMSNorm and RoPE here
       const bool raw = RAW && valid && (sl.is_win ? a.prepared < 2 : a.prepared == 0);
-      s_flag2[h * kStage + threadIdx.x] = valid ? (raw ? 3 : 1) : 0;
+      s_flag2[h * kStage + threadIdx.x] = valid ? ((raw ? 3 : 1) | (mixed ? 4 : 0)) : 0;
       const uint64_t rm = __ballot(raw);  // threads < kStage are exactly wave 0
-      if (threadIdx.x == 0) s_raw2[h] = rm != 0;
+      const uint64_t mm = MIX ? __ballot(mixed) : 0;
+      if (threadIdx.x == 0) {
+        s_raw2[h] = rm != 0;
+        if (MIX) s_mix2[h] = mm != 0;
+      }
     }
   };
   auto resolve_stage = [&](int64_t st0, int h) {
@@ -332,10 +361,23 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   // chunk stored there
   // The wave's 16 row addresses are read from LDS at once (lane l % 16 holds that of row
   // RPI (wave + 4 (l / RPI)) + l % RPI) and handed to each instruction's lanes by a lane read.
-  auto issue_dma = [&](const uint16_t* const* src_rows, uint16_t* E) {
+  // A mixed row (CSA_FP8_BF16_ROPE, bit 0 of its address set) arrives as: its bf16 RoPE chunks at their
+  // own positions, and each 16-code chunk of its fp8 part at the positions of both bf16 chunks it widens
+  // into (the widening pass reads the first and overwrites both).  Its scale travels by one more
+  // 4-byte-per-lane load of wave 0 (lane i -> slot i).
+  auto issue_dma = [&](int h, int eb) {
+    const uint16_t* const* src_rows = s_src2 + h * kStage;
+    uint16_t* E = E0 + eb * kStage * C;
+    const bool mix = MIX && s_mix2[h] != 0;  // (uniform)
     const int l16 = lane & 15;
-    const uint64_t mine = reinterpret_cast<uint64_t>(src_rows[RPI * (wave + 4 * (l16 / RPI)) + l16 % RPI]);
+    const int myrow = RPI * (wave + 4 * (l16 / RPI)) + l16 % RPI;
+    const uint64_t mine = reinterpret_cast<uint64_t>(src_rows[myrow]);
     const int mlo = (int)(uint32_t)mine, mhi = (int)(uint32_t)(mine >> 32);
+    const int nfpc = (C - a.R) >> 3;  // bf16 chunks of the fp8 part
+    // (LDS reads come before this call's first load to LDS, so none of them waits for those loads)
+    if (mix && wave == 0)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)s_scp2[h * kStage + lane],
+                                       (__attribute__((address_space(3))) void*)(s_scale + eb * kStage), 4, 0, 0);
 #pragma unroll
     for (int j = 0; j < kStage / RPI / 4; ++j) {
       const int e0 = RPI * (wave + 4 * j);
@@ -350,13 +392,50 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
         rlo = (uint32_t)__shfl(mlo, srcl, 64);
         rhi = (uint32_t)__shfl(mhi, srcl, 64);
       }
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(((uint64_t)rhi << 32) | rlo) + 8 * swz<C>(e, cpos);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+      const int L = swz<C>(e, cpos);  // logical bf16 chunk held at this position
+      int off = 16 * L;
+      if (MIX && (rlo & 1u))
+        off = L >= nfpc ? (C - a.R) + 16 * (L - nfpc)  // a RoPE chunk
+                        : 8 * (L & ~1);                // the 16 codes of chunks L & ~1 and (L & ~1) + 1
+      const uint8_t* rowb = reinterpret_cast<const uint8_t*>(((uint64_t)rhi << 32) | (rlo & ~1u));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(rowb + off),
                                        (__attribute__((address_space(3))) void*)(E + e0 * C), 16, 0, 0);
     }
   };
+  // Widening of a stage's mixed rows in place: each 16-code chunk becomes two bf16 chunks (code times the
+  // row's scale, rounded to nearest even), read from the position of the first and written to both.  Lane
+  // l serves row l, wave w its code chunks w + 4i; all of a lane's loads go out before its first
+  // conversion.  No LDS load is in flight meanwhile.
+  auto widen_stage = [&](int h, int eb) {
+    constexpr int MAXI = C / 64;             // code chunks per wave when R = 0
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int ncc = (C - a.R) >> 4;          // code chunks per row
+    const int e = lane;
+    if (!(s_flag2[h * kStage + e] & 4)) return;
+    const float sc = s_scale[eb * kStage + e];
+    uint16_t* rowp = E0 + (eb * kStage + e) * C;
+    u32x4 w[MAXI];
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i)
+      if (wv + 4 * i < ncc) w[i] = *reinterpret_cast<const u32x4*>(rowp + 8 * swz<C>(e, 2 * (wv + 4 * i)));
+#pragma unroll
+    for (int i = 0; i < MAXI; ++i) {
+      const int j = wv + 4 * i;
+      if (j >= ncc) break;
+      uint32_t o[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // codes 4q .. 4q + 3: exact float32 (OCP e4m3), times the scale
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i][q], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i][q], true);
+        o[2 * q] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+        o[2 * q + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+      }
+      *reinterpret_cast<u32x4*>(rowp + 8 * swz<C>(e, 2 * j)) = u32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<u32x4*>(rowp + 8 * swz<C>(e, 2 * j + 1)) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+  };
   __syncthreads();  // s_theta and the first stage's slots visible
-  issue_dma(s_src2, E0);  // the first stage's rows land while the query is prepared
+  issue_dma(0, 0);  // the first stage's rows land while the query is prepared
   // wide, CSA: the index-list values of a later stage travel like the rows, straight into LDS (wave 0,
   // lane i -> slot st0 + i, clamped into the list), so that no register load is pending across the
   // stage's compute
@@ -594,8 +673,12 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       if (more && threadIdx.x < kStage)
         commit_stage(s0 + kStage, (st + 1) % 3, s_idx3[((st + 1) % 3) * kStage + threadIdx.x]);
       __syncthreads();
+      if (MIX && s_mix2[st % 3]) {  // (uniform) before the next stage's loads go out
+        widen_stage(st % 3, st & 1);
+        __syncthreads();
+      }
       if (more) {
-        issue_dma(s_src2 + ((st + 1) % 3) * kStage, E0 + ((st + 1) & 1) * kStage * C);
+        issue_dma((st + 1) % 3, (st + 1) & 1);
         if (s0 + 2 * kStage < slot_hi) fetch_idx(s0 + 2 * kStage, (st + 2) % 3);
       }
       compute_stage(E0 + (st & 1) * kStage * C, s0, s_flag2 + (st % 3) * kStage);
@@ -603,15 +686,18 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   } else {
     int half = 0;
     for (int64_t s0 = slot_lo; s0 < slot_hi; s0 += kStage, half ^= 1) {
-      const uint16_t** s_src = s_src2 + half * kStage;
       const double* s_pos = s_pos2 + half * kStage;
       const int* s_flag = s_flag2 + half * kStage;
       // ---- (2) DMA of this stage's rows (the first stage's went out before the query was prepared)
-      if (s0 != slot_lo) issue_dma(s_src, E0);
+      if (s0 != slot_lo) issue_dma(half, 0);
       // the next stage's slot resolution (index-list loads) overlaps this stage's fetch and compute
       if (s0 + kStage < slot_hi) resolve_stage(s0 + kStage, half ^ 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (MIX && s_mix2[half]) {
+        widen_stage(half, 0);
+        __syncthreads();
+      }
       if (!WIDE && s0 == slot_lo) {
         zmul = kLog2e * a.scale / sqrtf((s_rq[lane & 15] + s_rq[16 + (lane & 15)] + s_rq[32 + (lane & 15)] +
                                          s_rq[48 + (lane & 15)]) / (float)C + a.eps);
@@ -1000,17 +1086,16 @@ SplitLayout split_layout(int mode, int T, int H, int prepared, int64_t ncomp, in
 // the slot-resolution buffers
 template <int C, bool WIDE>
 size_t bf16_lds_bytes() {
-  const size_t ne = WIDE ? 2 : 1, nr = WIDE ? 3 : 2;
-  return ne * kStage * C * 2 + (WIDE ? 0 : 4 * 2 * 64 * 16) + kStage * 4 + 64 * 4 + 64 * 8 + nr * kStage * 8 +
-         nr * kStage * 8 + nr * kStage * 4 + nr * 4 + 3 * kStage * 4;
+  const size_t ne = WIDE ? 2 : 1;
+  return (size_t)lds_ctrl_halfs<WIDE>() * 2 + (WIDE ? 0 : 4 * 2 * 64 * 16) + ne * kStage * C * 2;
 }
 
-template <int C, bool WIDE, bool RAW>
+template <int C, bool WIDE, bool RAW, bool MIX>
 csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
   const size_t lds = bf16_lds_bytes<C, WIDE>();
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C, WIDE, RAW>,
+    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C, WIDE, RAW, MIX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return CSA_ERR_LAUNCH;
     attr_set = true;
@@ -1020,16 +1105,23 @@ csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStre
   const int nx = a.nsplit * rows;
   const int nx_pad = (nx + 7) & ~7;
   dim3 grid(nx_pad, a.H / (WIDE ? 64 : 16));
-  hipLaunchKernelGGL((attend_bf16_kernel<C, WIDE, RAW>), grid, dim3(256), lds, stream, a, rt, nx);
+  hipLaunchKernelGGL((attend_bf16_kernel<C, WIDE, RAW, MIX>), grid, dim3(256), lds, stream, a, rt, nx);
   if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 
+// MIX: compressed rows in CSA_FP8_BF16_ROPE (a variant of its own, so that the bf16 kernels carry none of
+// its code)
+template <int C, bool MIX>
+csa_status launch_bf16_fmt(const AttnArgs& a, const RopeTable& rt, int rows, bool wide, hipStream_t stream) {
+  if (wide) return launch_bf16<C, true, false, MIX>(a, rt, rows, stream);
+  return a.prepared == 2 ? launch_bf16<C, false, false, MIX>(a, rt, rows, stream)
+                         : launch_bf16<C, false, true, MIX>(a, rt, rows, stream);
+}
 template <int C>
 csa_status launch_bf16_any(const AttnArgs& a, const RopeTable& rt, int rows, bool wide, hipStream_t stream) {
-  if (wide) return launch_bf16<C, true, false>(a, rt, rows, stream);
-  return a.prepared == 2 ? launch_bf16<C, false, false>(a, rt, rows, stream)
-                         : launch_bf16<C, false, true>(a, rt, rows, stream);
+  return a.comp_mixed ? launch_bf16_fmt<C, true>(a, rt, rows, wide, stream)
+                      : launch_bf16_fmt<C, false>(a, rt, rows, wide, stream);
 }
 
 }  // namespace
@@ -1044,7 +1136,8 @@ size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncom
   return ((o + 255) & ~(size_t)255) + rows * ns * H * 2 * 4;
 }
 
-csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
+csa_status launch_attend(int mode, const void* q, const void* comp_kv, const float* comp_scale, bool comp_mixed,
+                         const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
                          float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,
@@ -1069,6 +1162,8 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int
   a.sink = sink; a.gamma_q = gamma_q; a.gamma_kv = gamma_kv; a.pos0 = pos0; a.out = out;
   a.T = T; a.H = H; a.R = rope_dims; a.k = k; a.n_win = n_win; a.m = m; a.out_t = out_t; a.mode = mode;
   a.n_max = n_max; a.scale = scale; a.eps = eps; a.prepared = kv_prepared;
+  a.comp_scale = comp_scale;
+  a.comp_mixed = comp_mixed ? 1 : 0;
   const SplitLayout lay = split_layout(mode, T, H, kv_prepared, mode == 0 ? (int64_t)k : n_max, n_win);
   a.nsplit = lay.nsplit;
   a.ns_c = lay.ns_c;

@@ -77,7 +77,8 @@ namespace {
 // csa_prepare_kv: one workgroup per (row, sequence); thread t < c/4 owns channels [4t, 4t + 4).
 template <typename TIn>
 __global__ __launch_bounds__(kThreads) void prepare_kernel(const TIn* __restrict__ in, int64_t in_bstride,
-                                                           void* __restrict__ out, int64_t out_bstride, int c,
+                                                           void* __restrict__ out, float* __restrict__ out_scale,
+                                                           int64_t out_bstride, int c,
                                                            int out_t, const int64_t* __restrict__ pos_base,
                                                            int64_t pos_first, int64_t pos_stride,
                                                            const float* __restrict__ gamma, float eps, int R,
@@ -96,6 +97,12 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(const TIn* __restrict
   }
   const int64_t pos = (pos_base ? pos_base[b] : 0) + pos_first + (int64_t)j * pos_stride;
   prep_row4<kThreads>(y, holder, cg, c, (double)pos, gamma, eps, R, rt.theta, s_red);
+  if (out_t == CSA_FP8_BF16_ROPE) {
+    const int64_t orow = (int64_t)b * out_bstride + j;
+    store_fp8_rope_row<kThreads>(y, holder, cg, c, R, static_cast<uint8_t*>(out) + orow * (c + R), out_scale + orow,
+                                 s_red);
+    return;
+  }
   if (!holder) return;
   const int64_t o = ((int64_t)b * out_bstride + j) * c + 4 * cg;
   if (out_t == CSA_F32) {
@@ -110,18 +117,19 @@ __global__ __launch_bounds__(kThreads) void prepare_kernel(const TIn* __restrict
 
 }  // namespace
 
-csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, int64_t out_bstride, int B, int rows,
-                             int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
+csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, void* out_scale, int64_t out_bstride,
+                             int B, int rows, int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
                              int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream) {
   const RopeTable rt = make_rope_table(prep->rope_dims, prep->rope_base);
   dim3 grid(rows, B);
+  float* osc = static_cast<float*>(out_scale);
   if (in_t == CSA_F32)
-    hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)in, in_bstride, out,
+    hipLaunchKernelGGL(prepare_kernel<float>, grid, dim3(kThreads), 0, stream, (const float*)in, in_bstride, out, osc,
                        out_bstride, c, out_t, pos_base, pos_first, pos_stride, prep->gamma, prep->eps,
                        prep->rope_dims, rt);
   else
     hipLaunchKernelGGL(prepare_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, (const uint16_t*)in, in_bstride,
-                       out, out_bstride, c, out_t, pos_base, pos_first, pos_stride, prep->gamma, prep->eps,
+                       out, osc, out_bstride, c, out_t, pos_base, pos_first, pos_stride, prep->gamma, prep->eps,
                        prep->rope_dims, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

@@ -166,6 +166,11 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
 
   if (jb.prep) prep_row4<NT>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
   const int64_t orow = (int64_t)b * out_bstride + e;
+  if (out_t == CSA_FP8_BF16_ROPE) {  // prepared entries only (checked on the host)
+    store_fp8_rope_row<NT>(y, writer, cg, c, jb.R, static_cast<uint8_t*>(out) + orow * (c + jb.R),
+                           static_cast<float*>(out_scale) + orow, s_red);
+    return;
+  }
   if (out_t == CSA_F32) {
     if (writer) *reinterpret_cast<f32x4*>(static_cast<float*>(out) + orow * c + 4 * cg) = f32x4{y[0], y[1], y[2], y[3]};
     return;

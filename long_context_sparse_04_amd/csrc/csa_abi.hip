@@ -22,7 +22,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 4; }
+int csa_abi_version(void) { return 5; }
 
 }  // extern "C"
 
@@ -33,13 +33,14 @@ csa_status check_compress(const void* ca, const void* cb, const void* za, const 
                           int num_entries, int in_t, void* out, void* out_scale, int out_t,
                           int64_t& out_batch_stride, const csa_kv_prep* prep, bool& empty) {
   empty = false;
-  if (prep && (out_t != CSA_F32 && out_t != CSA_BF16)) return CSA_ERR_UNSUPPORTED;
+  if (prep && (out_t != CSA_F32 && out_t != CSA_BF16 && out_t != CSA_FP8_BF16_ROPE)) return CSA_ERR_UNSUPPORTED;
+  if (out_t == CSA_FP8_BF16_ROPE && (!prep || (c - prep->rope_dims) % 16 != 0)) return CSA_ERR_UNSUPPORTED;
   if (prep && (prep->rope_dims < 0 || (prep->rope_dims % 8) || prep->rope_dims > c || prep->rope_dims > 128))
     return CSA_ERR_UNSUPPORTED;
   if (prep && !(prep->eps >= 0.0f)) return CSA_ERR_SHAPE;
   if (B < 0 || rows < 0 || num_entries < 0 || m < 1 || m > 1024 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
   if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
-  if (out_t < CSA_F32 || out_t > CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
+  if (out_t < CSA_F32 || out_t > CSA_FP8_BF16_ROPE) return CSA_ERR_UNSUPPORTED;
   if (out_t == CSA_MXFP4_E8M0_B32 && (c % 32)) return CSA_ERR_UNSUPPORTED;
   if (B == 0 || num_entries == 0) {
     empty = true;
@@ -48,7 +49,8 @@ csa_status check_compress(const void* ca, const void* cb, const void* za, const 
   const bool overlap = cb != nullptr || zb != nullptr || bias_b != nullptr;
   if (!ca || !za || !bias_a || !out) return CSA_ERR_NULL;
   if (overlap && (!cb || !zb || !bias_b)) return CSA_ERR_NULL;
-  if ((out_t == CSA_FP8_E4M3_ROWSCALE || out_t == CSA_MXFP4_E8M0_B32) && !out_scale) return CSA_ERR_NULL;
+  if ((out_t == CSA_FP8_E4M3_ROWSCALE || out_t == CSA_MXFP4_E8M0_B32 || out_t == CSA_FP8_BF16_ROPE) && !out_scale)
+    return CSA_ERR_NULL;
   if (first_entry < 0) return CSA_ERR_SHAPE;
   if (out_batch_stride == 0) out_batch_stride = num_entries;
   if (out_batch_stride < num_entries) return CSA_ERR_SHAPE;
@@ -95,23 +97,26 @@ csa_status csa_compress_pair(const void* ca0, const void* cb0, const void* za0, 
   return launch_compress_jobs(jobs, 2, B, rows, m, row0_pos, first_entry, num_entries, in_t, (hipStream_t)stream);
 }
 
-csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, int64_t out_batch_stride, int B,
-                          int rows, int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
-                          int64_t pos_stride, const csa_kv_prep* prep, void* stream) {
+csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, void* out_scale,
+                          int64_t out_batch_stride, int B, int rows, int c, int in_t, int out_t,
+                          const int64_t* pos_base, int64_t pos_first, int64_t pos_stride, const csa_kv_prep* prep,
+                          void* stream) {
   if (B < 0 || rows < 0 || c < 4 || c > 1024 || (c & 3)) return CSA_ERR_SHAPE;
-  if ((in_t != CSA_F32 && in_t != CSA_BF16) || (out_t != CSA_F32 && out_t != CSA_BF16)) return CSA_ERR_UNSUPPORTED;
+  if ((in_t != CSA_F32 && in_t != CSA_BF16) || (out_t != CSA_F32 && out_t != CSA_BF16 && out_t != CSA_FP8_BF16_ROPE))
+    return CSA_ERR_UNSUPPORTED;
   if (!prep) return CSA_ERR_NULL;
   if (prep->rope_dims < 0 || (prep->rope_dims % 8) || prep->rope_dims > c || prep->rope_dims > 128)
     return CSA_ERR_UNSUPPORTED;
+  if (out_t == CSA_FP8_BF16_ROPE && (c - prep->rope_dims) % 16 != 0) return CSA_ERR_UNSUPPORTED;
   if (!(prep->eps >= 0.0f)) return CSA_ERR_SHAPE;
   if (B == 0 || rows == 0) return CSA_OK;
-  if (!in || !out) return CSA_ERR_NULL;
+  if (!in || !out || (out_t == CSA_FP8_BF16_ROPE && !out_scale)) return CSA_ERR_NULL;
   if (in_batch_stride < rows || out_batch_stride < rows) return CSA_ERR_SHAPE;
   if (rows >= 2147483647 || B >= 65536) return CSA_ERR_UNSUPPORTED;
   // in place only with the same element type and the same layout
   if (in == out && (in_t != out_t || in_batch_stride != out_batch_stride)) return CSA_ERR_SHAPE;
-  return launch_prepare_kv(in, in_batch_stride, out, out_batch_stride, B, rows, c, in_t, out_t, pos_base, pos_first,
-                           pos_stride, prep, (hipStream_t)stream);
+  return launch_prepare_kv(in, in_batch_stride, out, out_scale, out_batch_stride, B, rows, c, in_t, out_t, pos_base,
+                           pos_first, pos_stride, prep, (hipStream_t)stream);
 }
 
 }  // extern "C"
@@ -169,8 +174,9 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w, const v
 }
 
 csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0, const void* zb0,
-                              const float* bias_a0, const float* bias_b0, int c0, void* out0, int out_t0,
-                              int64_t out_batch_stride0, const csa_kv_prep* prep0, const void* ca1, const void* cb1,
+                              const float* bias_a0, const float* bias_b0, int c0, void* out0, void* out_scale0,
+                              int out_t0, int64_t out_batch_stride0, const csa_kv_prep* prep0, const void* ca1,
+                              const void* cb1,
                               const void* za1, const void* zb1, const float* bias_a1, const float* bias_b1, int B,
                               int rows, int m, int64_t row0_pos, int64_t first_entry, int in_t, const void* q,
                               const void* q_scale, const float* w, void* k, void* k_scale, int HI, int cI,
@@ -192,13 +198,13 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
   int64_t bs0 = out_batch_stride0, bs1 = n_max;
   bool e0, e1;
   st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry, 1, in_t, out0,
-                      nullptr, out_t0, bs0, prep0, e0);
+                      out_scale0, out_t0, bs0, prep0, e0);
   if (st != CSA_OK) return st;
-  if (out_t0 != CSA_F32 && out_t0 != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (out_t0 != CSA_F32 && out_t0 != CSA_BF16 && out_t0 != CSA_FP8_BF16_ROPE) return CSA_ERR_UNSUPPORTED;
   st = check_compress(ca1, cb1, za1, zb1, bias_a1, bias_b1, B, rows, cI, m, row0_pos, first_entry, 1, in_t, out1,
                       out_scale1, qk_t, bs1, nullptr, e1);
   if (st != CSA_OK || e0 || empty) return st;
-  const CompressJob jobs[2] = {{ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, nullptr, out_t0, bs0, prep0},
+  const CompressJob jobs[2] = {{ca0, cb0, za0, zb0, bias_a0, bias_b0, c0, out0, out_scale0, out_t0, bs0, prep0},
                                {ca1, cb1, za1, zb1, bias_a1, bias_b1, cI, out1, out_scale1, qk_t, bs1, nullptr}};
   return launch_compress_index(jobs, rows, m, row0_pos, first_entry, in_t, q, q_scale, w, k, k_scale, B, HI, cI,
                                n_max, pos0, qk_t, scores, score_t, bound, (hipStream_t)stream);
@@ -222,6 +228,14 @@ csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max
   return launch_topk(scores, score_t, B, T, n_max, pos0, m, k, bound, idx, vals, workspace, (hipStream_t)stream);
 }
 
+// the compressed cache's format: the KV type, or fp8 + bf16 RoPE dims (bf16 MFMA path, prepared entries)
+static csa_status check_comp_t(int kv_t, int comp_t, int kv_prepared, int c, int rope_dims) {
+  if (comp_t == kv_t) return CSA_OK;
+  if (comp_t != CSA_FP8_BF16_ROPE || kv_t != CSA_BF16 || kv_prepared < 1) return CSA_ERR_UNSUPPORTED;
+  if ((c - rope_dims) % 16 != 0) return CSA_ERR_UNSUPPORTED;
+  return CSA_OK;
+}
+
 static csa_status check_attend(int kv_t, int out_t, int B, int T, int H, int c, int rope_dims, int n_win, int m) {
   if (B < 0 || T < 0 || H < 1 || m < 1 || n_win < 1 || n_win > 4096) return CSA_ERR_SHAPE;
   if (!is_pow2_dim(c)) return CSA_ERR_UNSUPPORTED;
@@ -238,22 +252,25 @@ size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win) 
   return attend_workspace_bytes(0, B, T, H, c, (int64_t)k, n_win);
 }
 
-csa_status csa_attend(const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv, const float* sink,
-                      const float* gamma_q, const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int k,
-                      int n_win, int64_t n_max, const int64_t* pos0, int m, float scale, float eps, float rope_base,
-                      int kv_t, int kv_prepared, void* out, int out_t, void* workspace, size_t ws_bytes,
-                      void* stream) {
+csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                      const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T,
+                      int H, int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
+                      float scale, float eps, float rope_base, int kv_t, int comp_t, int kv_prepared, void* out,
+                      int out_t, void* workspace, size_t ws_bytes, void* stream) {
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m);
+  if (st != CSA_OK) return st;
+  st = check_comp_t(kv_t, comp_t, kv_prepared, c, rope_dims);
   if (st != CSA_OK) return st;
   if (k < 1 || k > 2048 || n_max < 0 || n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
   if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
   if (B == 0 || T == 0) return CSA_OK;
   if (!q || !idx || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
+  if (comp_t != kv_t && n_max > 0 && !comp_scale) return CSA_ERR_NULL;
   const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_attend(0, q, comp_kv, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, k, n_win, n_max,
-                       pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t, workspace,
-                       (hipStream_t)stream);
+  return launch_attend(0, q, comp_kv, comp_scale, comp_t != kv_t, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c,
+                       rope_dims, k, n_win, n_max, pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,
+                       workspace, (hipStream_t)stream);
 }
 
 size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int n_win) {
@@ -261,22 +278,25 @@ size_t hca_attend_workspace_bytes(int B, int T, int H, int c, int64_t n_max, int
   return attend_workspace_bytes(1, B, T, H, c, n_max, n_win);
 }
 
-csa_status hca_attend(const void* q, const void* comp_kv, const void* win_kv, const float* sink, const float* gamma_q,
-                      const float* gamma_kv, int B, int T, int H, int c, int rope_dims, int n_win, int64_t n_max,
-                      const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t,
-                      int kv_prepared, void* out,
-                      int out_t, void* workspace, size_t ws_bytes, void* stream) {
+csa_status hca_attend(const void* q, const void* comp_kv, const float* comp_scale, const void* win_kv,
+                      const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H, int c,
+                      int rope_dims, int n_win, int64_t n_max, const int64_t* pos0, int m_hca, float scale, float eps,
+                      float rope_base, int kv_t, int comp_t, int kv_prepared, void* out, int out_t, void* workspace,
+                      size_t ws_bytes, void* stream) {
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m_hca);
+  if (st != CSA_OK) return st;
+  st = check_comp_t(kv_t, comp_t, kv_prepared, c, rope_dims);
   if (st != CSA_OK) return st;
   if (n_max < 0 || n_max >= ((int64_t)1 << 24)) return CSA_ERR_SHAPE;
   if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
   if (B == 0 || T == 0) return CSA_OK;
   if (!q || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
+  if (comp_t != kv_t && n_max > 0 && !comp_scale) return CSA_ERR_NULL;
   const size_t need = hca_attend_workspace_bytes(B, T, H, c, n_max, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_attend(1, q, comp_kv, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H, c, rope_dims, 1, n_win,
-                       n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared, out, out_t, workspace,
-                       (hipStream_t)stream);
+  return launch_attend(1, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H,
+                       c, rope_dims, 1, n_win, n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,
+                       workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -205,6 +205,40 @@ CSA_DEV void prep_row4(float* y, bool holder, int cg, int c, double pos, const f
   }
 }
 
+// Store a prepared row held 4 channels per thread (thread t < c/4 owns channels [4t, 4t + 4)) in
+// CSA_FP8_BF16_ROPE: channels below c - R as OCP e4m3 codes at byte offset d with one float32 scale
+// (amax/448 of those channels, codes RNE, saturating), channels from c - R on as bf16 at byte offset
+// (c - R) + 2 (d - (c - R)).  Every thread of the NT-thread block calls it (it holds a barrier); s_red
+// has room for NT/64 floats.  c - R is a multiple of 16, so a thread's 4 channels lie in one part.
+template <int NT>
+CSA_DEV void store_fp8_rope_row(const float* y, bool holder, int cg, int c, int R, uint8_t* row, float* scale_out,
+                                float* s_red) {
+  const int nfp = c - R;
+  const int d = 4 * cg;
+  const bool fp = holder && d < nfp;
+  float am = fp ? fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))) : 0.0f;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  am = s_red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) am = fmaxf(am, s_red[w]);
+  const float scale = am / 448.0f;
+  if (fp) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pk |= f32_to_e4m3(scale > 0.0f ? y[q] / scale : 0.0f) << (8 * q);
+    *reinterpret_cast<uint32_t*>(row + d) = pk;
+  } else if (holder) {
+    uint2 pk;
+    pk.x = pack_bf16x2(y[0], y[1]);
+    pk.y = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<uint2*>(row + nfp + 2 * (d - nfp)) = pk;
+  }
+  if (threadIdx.x == 0) *scale_out = scale;
+}
+
 // theta_i = rope_base^(-2i/R), i < R/2 <= 64, in double on the host
 static inline RopeTable make_rope_table(int R, float base) {
   RopeTable rt;

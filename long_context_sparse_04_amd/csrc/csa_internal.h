@@ -30,11 +30,11 @@ struct CompressJob {
 csa_status launch_compress_jobs(const CompressJob* jobs, int njobs, int B, int rows, int m, int64_t row0_pos,
                                 int64_t first_entry, int num_entries, int in_t, hipStream_t stream);
 
-csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, int64_t out_bstride, int B, int rows,
-                             int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
+csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, void* out_scale, int64_t out_bstride,
+                             int B, int rows, int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
                              int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream);
 
-// bound keys per query row written by the decode index kernel (two per wave of 256 entries)
+// bound keys per query row written by the decode index kernel (two per bound set)
 int64_t index_bound_keys(int64_t n_max);
 bool use_prefill_index(int fmt, int T, int HI);
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
@@ -54,7 +54,9 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
 
 // mode 0: CSA (index list), mode 1: HCA (dense range)
 size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win);
-csa_status launch_attend(int mode, const void* q, const void* comp_kv, const int32_t* idx, const void* win_kv,
+// comp_mixed: comp_kv rows in CSA_FP8_BF16_ROPE with their scales in comp_scale
+csa_status launch_attend(int mode, const void* q, const void* comp_kv, const float* comp_scale, bool comp_mixed,
+                         const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
                          float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 4
+    assert lib.csa_abi_version() == 5
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -63,17 +63,22 @@ def test_compress_validation(lib):
     assert call(out_t=3, c=100) == 3
     assert call(ca=None) == 1
     prep = C.byref(_lib.KvPrep(None, 1e-6, 64, 1e4))
-    assert call(prep=prep, out_t=2, osc=DUMMY) == 3        # prepared entries are stored as F32 / BF16 only
+    assert call(prep=prep, out_t=2, osc=DUMMY) == 3        # prepared entries: F32, BF16 or fp8 + bf16 RoPE
+    assert call(out_t=4, osc=DUMMY) == 3                   # the fp8 + bf16 RoPE rows are prepared rows
+    assert call(prep=prep, out_t=4, osc=None) == 1          # and need their scales
+    assert call(prep=C.byref(_lib.KvPrep(None, 1e-6, 56, 1e4)), out_t=4, osc=DUMMY) == 3   # c - R % 16
     assert call(prep=C.byref(_lib.KvPrep(None, 1e-6, 60, 1e4))) == 3
     assert call(prep=C.byref(_lib.KvPrep(None, -1.0, 64, 1e4))) == 2
     # csa_prepare_kv
     pk = lib.csa_prepare_kv
-    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 1, 1, None, 0, 4, None, None) == 1
-    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 510, 1, 1, None, 0, 4, prep, None) == 2
-    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 2, 1, None, 0, 4, prep, None) == 3
-    assert pk(DUMMY, 4, DUMMY, 8, 2, 8, 512, 1, 1, None, 0, 4, prep, None) == 2   # batch stride below rows
-    assert pk(DUMMY, 8, DUMMY, 8, 2, 8, 512, 1, 0, None, 0, 4, prep, None) == 2   # in place needs one layout
-    assert pk(DUMMY, 8, DUMMY, 8, 0, 8, 512, 1, 1, None, 0, 4, prep, None) == 0
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 512, 1, 1, None, 0, 4, None, None) == 1
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 510, 1, 1, None, 0, 4, prep, None) == 2
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 512, 2, 1, None, 0, 4, prep, None) == 3
+    assert pk(DUMMY, 4, DUMMY, None, 8, 2, 8, 512, 1, 1, None, 0, 4, prep, None) == 2   # batch stride below rows
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 512, 1, 0, None, 0, 4, prep, None) == 2   # in place needs one layout
+    assert pk(DUMMY, 8, DUMMY, None, 8, 0, 8, 512, 1, 1, None, 0, 4, prep, None) == 0
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 512, 1, 4, None, 0, 4, prep, None) == 1   # fp8 + bf16 RoPE: scales
+    assert pk(DUMMY, 8, DUMMY, None, 8, 2, 8, 512, 1, 5, None, 0, 4, prep, None) == 3
     assert call(cb=None) == 1                     # b-stream must be all or nothing
     assert call(out_t=2, osc=None) == 1           # fp8 needs the scale output
     assert call(first=2) == 2                     # entry 2 needs rows 4..11 but only 0..7 exist
@@ -136,7 +141,7 @@ def test_index_topk_attend_validation(lib):
     def ci(**kw):
         a = dict(m=4, first=1023, n=1024, qk=2, q=DUMMY, rows=8, r0=4088, st=0)
         a.update(kw)
-        return lib.csa_compress_index(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 512, DUMMY, 1, 0, None,
+        return lib.csa_compress_index(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 512, DUMMY, None, 1, 0, None,
                                       DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 4, a["rows"], a["m"], a["r0"],
                                       a["first"], 1, a["q"], DUMMY, DUMMY, DUMMY, DUMMY, 64, 128, a["n"], DUMMY,
                                       a["qk"], DUMMY, a["st"], None, None)
@@ -151,11 +156,13 @@ def test_index_topk_attend_validation(lib):
 
     def att(**kw):
         a = dict(q=DUMMY, comp=DUMMY, idx=DUMMY, win=DUMMY, sink=DUMMY, B=4, T=1, H=128, c=512, R=64, k=1024,
-                 n_win=128, N=262144, pos=DUMMY, m=4, kv_t=1, out=DUMMY, out_t=1, ws=None, nb=0, prep=0)
+                 n_win=128, N=262144, pos=DUMMY, m=4, kv_t=1, out=DUMMY, out_t=1, ws=None, nb=0, prep=0, ct=None,
+                 cs=None)
         a.update(kw)
-        return lib.csa_attend(a["q"], a["comp"], a["idx"], a["win"], a["sink"], None, None, a["B"], a["T"], a["H"],
-                              a["c"], a["R"], a["k"], a["n_win"], a["N"], a["pos"], a["m"], 0.044, 1e-6, 1e4,
-                              a["kv_t"], a["prep"], a["out"], a["out_t"], a["ws"], a["nb"], None)
+        ct = a["kv_t"] if a["ct"] is None else a["ct"]
+        return lib.csa_attend(a["q"], a["comp"], a["cs"], a["idx"], a["win"], a["sink"], None, None, a["B"], a["T"],
+                              a["H"], a["c"], a["R"], a["k"], a["n_win"], a["N"], a["pos"], a["m"], 0.044, 1e-6, 1e4,
+                              a["kv_t"], ct, a["prep"], a["out"], a["out_t"], a["ws"], a["nb"], None)
     assert att() == 4                         # decode needs the split workspace
     assert att(c=192) == 3
     assert att(R=60) == 3
@@ -164,6 +171,14 @@ def test_index_topk_attend_validation(lib):
     assert att(k=0) == 2
     assert att(q=None, ws=DUMMY, nb=ws) == 1
     assert att(prep=3, ws=DUMMY, nb=ws) == 3 and att(prep=-1, ws=DUMMY, nb=ws) == 3   # kv_prepared is 0, 1 or 2
-    assert lib.hca_attend(DUMMY, DUMMY, DUMMY, DUMMY, None, None, 8, 1, 128, 512, 64, 128, 8192, DUMMY, 128, 0.044,
-                          1e-6, 1e4, 1, 3, DUMMY, 1, None, 0, None) == 3
+    # fp8 + bf16 RoPE compressed rows: bf16 queries, prepared entries, scales, c - R a multiple of 16
+    assert att(ct=4, prep=1, ws=DUMMY, nb=ws) == 1
+    assert att(ct=4, prep=0, cs=DUMMY, ws=DUMMY, nb=ws) == 3
+    assert att(ct=4, prep=1, cs=DUMMY, R=56, ws=DUMMY, nb=ws) == 3
+    assert att(ct=4, kv_t=0, prep=1, cs=DUMMY, ws=DUMMY, nb=ws) == 3
+    assert att(ct=2, prep=1, cs=DUMMY, ws=DUMMY, nb=ws) == 3
+    assert lib.hca_attend(DUMMY, DUMMY, None, DUMMY, DUMMY, None, None, 8, 1, 128, 512, 64, 128, 8192, DUMMY, 128, 0.044,
+                          1e-6, 1e4, 1, 1, 3, DUMMY, 1, None, 0, None) == 3
+    assert lib.hca_attend(DUMMY, DUMMY, None, DUMMY, DUMMY, None, None, 8, 1, 128, 512, 64, 128, 8192, DUMMY, 128, 0.044,
+                          1e-6, 1e4, 1, 4, 2, DUMMY, 1, DUMMY, 1 << 30, None) == 1
     assert lib.hca_attend_workspace_bytes(8, 1, 128, 512, 8192, 128) > 0

@@ -1,0 +1,224 @@
+"""GPU parity of the mixed KV storage (CSA_FP8_BF16_ROPE): the non-RoPE dims of a prepared KV row in fp8
+e4m3 with one float32 scale per row, the RoPE dims in bf16 ("【论文解读】DeepSeek-V4", section 一(三)4, item 1;
+"DeepseekV4论文解析" on numerical precision).
+
+Writers (csa_prepare_kv, csa_compress, csa_compress_index): the RoPE part must be bit-identical to the bf16
+output of the same call (same float32 values, same rounding); the fp8 part must decode to the oracle's
+prepared values within half an e4m3 step, with codes that match the oracle's encoding except within float32
+rounding of a midpoint.  Readers (csa_attend, hca_attend, every kernel variant): the output against the
+float64 oracle run on the exact decoded entries (handed in prepared), rel-L2 <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import configs, gen
+from tests.gpu_util import DEV, codes_close, dev, host_f64, rel_l2
+
+pytestmark = pytest.mark.gpu
+LOWP_TOL = 5e-3
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def api():
+    from long_context_sparse_04_amd import api as a
+    from long_context_sparse_04_amd import _lib
+    _lib.load()
+    return a
+
+
+def _pos(arr):
+    return torch.tensor(np.asarray(arr, np.int64), device=DEV)
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _check_mixed_rows(got_bytes, got_scale, ref_vals, R, bf16_rows=None):
+    """got_bytes [..., c + R] / got_scale [...] from the GPU against the oracle's float64 prepared values."""
+    c = ref_vals.shape[-1]
+    n = c - R
+    if bf16_rows is not None:   # the RoPE part equals the bf16 output of the same values, bit for bit
+        assert np.array_equal(np.ascontiguousarray(got_bytes[..., n:]).view(np.uint16), bf16_rows[..., n:])
+    amax = np.max(np.abs(ref_vals[..., :n]), axis=-1)
+    assert np.allclose(got_scale, amax / 448.0, rtol=1e-5, atol=0)
+    ref_codes, ref_scale = oracle.encode_fp8_rows(ref_vals[..., :n])
+    scaled = ref_vals[..., :n] / np.where(ref_scale > 0, ref_scale, 1.0)[..., None]
+    assert codes_close(got_bytes[..., :n], ref_codes, scaled, oracle.fp8_e4m3_values())
+    dec = oracle.decode_fp8_rope_rows(got_bytes, got_scale, R)
+    err = np.abs(dec[..., :n] - ref_vals[..., :n])
+    bound = np.maximum(np.abs(ref_vals[..., :n]) * 2.0 ** -4, 2.0 ** -10 * got_scale[..., None]) * 1.001 + 1e-6
+    assert np.all(err <= bound)
+    return dec
+
+
+@pytest.mark.parametrize("c,R", [(512, 64), (256, 64), (128, 64), (512, 32)])
+def test_prepare_kv_fp8rope(api, c, R):
+    rng = np.random.default_rng(c + R)
+    B, rows = 2, 300
+    x = oracle.encode_bf16(rng.standard_normal((B, rows, c)) * 2.0)
+    gk = rng.uniform(0.5, 1.5, c).astype(np.float32)
+    say(f"prepare_kv fp8rope c={c} R={R}")
+    prep = api.kv_prep(R, 1e-6, 1e4, gamma=dev(gk))
+    xb = dev(x)
+    outb = api.prepare_kv(xb, prep, pos_stride=4, pos_first=8)
+    outm, sc = api.prepare_kv(xb, prep, pos_stride=4, pos_first=8, out_fmt="fp8rope")
+    torch.cuda.synchronize()
+    assert outm.shape == (B, rows, c + R) and outm.dtype == torch.uint8 and sc.shape == (B, rows)
+    pos = 8 + 4 * np.arange(rows, dtype=np.float64)
+    ref = oracle.rope(oracle.rmsnorm(oracle.decode_bf16(x), gk.astype(np.float64), 1e-6), pos[None, :], R, 1e4)
+    _check_mixed_rows(_np(outm), _np(sc), ref, R, bf16_rows=_np(outb.view(torch.int16)).view(np.uint16))
+
+
+def test_compress_fp8rope(api):
+    """csa_compress with a csa_kv_prep into the mixed format: the entries of a chunk (C4 shape, 256 entries)."""
+    cfg = configs.C4
+    ci = gen.compress_inputs(cfg)
+    say(f"compress fp8rope {cfg.name} entries={ci['num_entries']}")
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    d = {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    args = (d["ca"], d["cb"], d["za"], d["zb"], d["bias_a"], d["bias_b"], ci["m"], ci["row0_pos"], ci["first_entry"],
+            ci["num_entries"])
+    outb, _ = api.compress(*args, prep=prep)
+    outm, sc = api.compress(*args, prep=prep, out_fmt="fp8rope")
+    torch.cuda.synchronize()
+    v = lambda x: None if x is None else oracle.decode_bf16(x)
+    pooled = oracle.compress(v(ci["ca"]), v(ci["cb"]), v(ci["za"]), v(ci["zb"]), ci["bias_a"].astype(np.float64),
+                             ci["bias_b"].astype(np.float64), ci["m"], ci["row0_pos"], ci["first_entry"],
+                             ci["num_entries"])
+    pos = cfg.m * (ci["first_entry"] + np.arange(ci["num_entries"], dtype=np.float64))
+    ref = oracle.rope(oracle.rmsnorm(pooled, None, cfg.eps), pos[None, :], cfg.rope_dims, cfg.rope_base)
+    _check_mixed_rows(_np(outm), _np(sc), ref, cfg.rope_dims, bf16_rows=_np(outb.view(torch.int16)).view(np.uint16))
+
+
+@pytest.mark.parametrize("name,n_comp", [("c3", 5037), ("c2", 1500)])
+def test_compress_index_fp8rope_kv(api, name, n_comp):
+    """The fused decode launch writes the block's KV entry in the mixed format exactly as csa_compress_pair."""
+    cfg = configs.get_config(name).scaled(B=3, n_comp=n_comp)
+    fmt, N, R = cfg.idx_dtype, cfg.n_comp, cfg.rope_dims
+    say(f"compress_index fp8rope KV {cfg.name} fmt={fmt} N={N}")
+    ckv, cik = gen.compress_inputs(cfg), gen.compress_inputs(cfg, indexer=True)
+    first, r0p = N - 1, 4 * N - 8
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    pos0 = [4 * N, 4 * N + 3, 4 * (N - 100)]
+    d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
+    outs = []
+    for fused in (False, True):
+        kv = torch.zeros((cfg.B, N, cfg.c + R), dtype=torch.uint8, device=DEV)
+        ks = torch.zeros((cfg.B, N), dtype=torch.float32, device=DEV)
+        ik, iks = dev(kc["data"]), dev(kc.get("scale"))
+        qd, qs, wd = dev(qi["data"]), dev(qi.get("scale")), dev(w)
+        pkv = dict(d(ckv), out=kv[:, first:], out_scale=ks[:, first:], out_fmt="fp8rope", out_batch_stride=N,
+                   prep=prep)
+        if fused:
+            sc = api.compress_index(pkv, d(cik), cfg.m, r0p, first, qd, qs, wd, ik, iks, _pos(pos0), fmt)
+        else:
+            api.compress_pair(pkv, dict(d(cik), out=ik[:, first:], out_batch_stride=N,
+                                        out_scale=None if iks is None else iks[:, first:],
+                                        out_fmt=None if fmt == "bf16" else fmt), cfg.m, r0p, first, 1)
+            sc = api.index(qd, qs, wd, ik, iks, _pos(pos0), cfg.m, fmt)
+        torch.cuda.synchronize()
+        outs.append((kv, ks, ik, iks, sc))
+    for a_, b_ in zip(*outs):
+        if a_ is not None:
+            assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
+    assert torch.count_nonzero(outs[0][0][:, :first]) == 0   # nothing outside the new entry
+
+
+def _rand_idx(rng, B, T, k, pos0, m, n_max, fill=0.9):
+    idx = np.full((B, T, k), -1, np.int32)
+    for b in range(B):
+        for r in range(T):
+            vis = min((pos0[b] + r) // m, n_max)
+            n = min(k, vis, int(fill * k))
+            if n:
+                idx[b, r, :n] = np.sort(rng.choice(vis, size=n, replace=False))
+    return idx
+
+
+def _attend_mixed(api, cfg, pos0, idx, hca, prepared):
+    """GPU attention over a mixed-format cache (prepared by csa_prepare_kv from the raw cache) against the
+    oracle on the exact decoded entries, handed in prepared; window rows raw (1) or prepared (2)."""
+    q = gen.queries(cfg, hca=hca)
+    cache = gen.kv_cache(cfg, hca=hca)
+    win = gen.window(cfg, hca=hca)
+    sink = gen.sink(cfg, hca=hca)
+    R = cfg.rope_dims
+    say(f"{'hca' if hca else 'csa'}_attend fp8rope {cfg.name} B={cfg.B} T={cfg.T} H={cfg.H} N={cache.shape[1]} "
+        f"prepared={prepared}")
+    prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
+    mc, ms = api.prepare_kv(dev(cache), prep, pos_stride=cfg.m_hca if hca else cfg.m, out_fmt="fp8rope")
+    dwin = dev(win)
+    if prepared == 2:
+        dwin = api.prepare_kv(dwin, prep, pos_base=_pos(pos0), pos_first=-(cfg.n_win - 1))
+    if hca:
+        out = api.hca_attend(dev(q), mc, dwin, dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, R, cfg.scale, cfg.eps,
+                             cfg.rope_base, kv_prepared=prepared, comp_scale=ms)
+    else:
+        out = api.attend(dev(q), mc, dev(idx), dwin, dev(sink), _pos(pos0), cfg.m, cfg.n_win, R, cfg.scale,
+                         cfg.eps, cfg.rope_base, kv_prepared=prepared, comp_scale=ms)
+    torch.cuda.synchronize()
+    ents = oracle.decode_fp8_rope_rows(_np(mc), _np(ms), R)
+    qv, wv = oracle.decode_bf16(q), oracle.decode_bf16(win)
+    if hca:
+        ref = oracle.hca_attend(qv, ents, wv, sink, pos0, cfg.m_hca, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
+                                comp_prepared=True)
+    else:
+        ref = oracle.attend(qv, ents, idx, wv, sink, pos0, cfg.m, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
+                            comp_prepared=True)
+    return host_f64(out), ref
+
+
+@pytest.mark.parametrize("prepared", [1, 2])
+def test_attend_fp8rope_decode(api, prepared):
+    cfg = configs.C3.scaled(B=2, n_comp=3000)
+    pos0 = [4 * 3000, 4 * 2500 + 1]
+    idx = _rand_idx(np.random.default_rng(2), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    got, ref = _attend_mixed(api, cfg, pos0, idx, False, prepared)
+    e = rel_l2(got, ref)
+    say(f"  rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+
+
+def test_attend_fp8rope_small_head_dim(api):
+    """c = 128 with 32 RoPE dims (six fp8 chunks of 16 per row), 16 heads, ragged index lists."""
+    cfg = configs.C2.scaled(B=2, n_comp=300, k=50, c=128, H=16, rope_dims=32)
+    pos0 = [4 * 300, 4 * 11]
+    idx = _rand_idx(np.random.default_rng(6), 2, 1, cfg.k, pos0, cfg.m, cfg.n_comp)
+    for prepared in (1, 2):
+        got, ref = _attend_mixed(api, cfg, pos0, idx, False, prepared)
+        e = rel_l2(got, ref)
+        say(f"  rel-L2 {e:.3e}")
+        assert e <= LOWP_TOL
+
+
+def test_attend_fp8rope_prefill_wide(api):
+    cfg = configs.C4.scaled(T=40, n_comp=200, pos0=700, k=64)
+    idx = _rand_idx(np.random.default_rng(3), 1, cfg.T, cfg.k, [700], cfg.m, cfg.n_comp)
+    got, ref = _attend_mixed(api, cfg, [700], idx, False, 2)
+    e = rel_l2(got, ref)
+    say(f"  rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+
+
+@pytest.mark.parametrize("prepared", [1, 2])
+def test_hca_attend_fp8rope(api, prepared):
+    cfg = configs.C5.scaled(B=2, n_hca=700)
+    pos0 = [128 * 700, 128 * 333 + 5]
+    got, ref = _attend_mixed(api, cfg, pos0, None, True, prepared)
+    e = rel_l2(got, ref)
+    say(f"  decode rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
+    cfg = configs.C4.scaled(T=48, n_hca=40, pos0=128 * 30 + 7)
+    got, ref = _attend_mixed(api, cfg, [cfg.pos0], None, True, prepared)
+    e = rel_l2(got, ref)
+    say(f"  prefill rel-L2 {e:.3e}")
+    assert e <= LOWP_TOL
