@@ -317,6 +317,114 @@ csa_status hca_attend(const void* q, const void* comp_kv, const float* comp_scal
                       int kv_t, int comp_t, int kv_prepared, void* out, int out_t,
                       void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * ---- Decode across steps: the state cache and the paged compressed caches ----
+ *
+ * "【论文解读】DeepSeek-V4", section 二(六) 推理框架, and "DeepseekV4论文解析", its KV-cache part: the
+ * sliding window and the tail tokens that do not yet fill a compression block live in a fixed-size
+ * state cache per request; completed CSA / HCA entries live in a paged cache whose blocks cover a
+ * multiple of lcm(m, m') raw tokens (128 at m = 4, m' = 128: 32 CSA entries and 1 HCA entry).
+ *
+ * csa_pages: logical page j of sequence b covers raw tokens [j * page_tokens, (j + 1) * page_tokens)
+ * and is physical page block_table[b * max_pages + j] of every paged pool.  A pool of entries at
+ * ratio r (m for CSA KV and indexer keys, m_hca for HCA) holds E = page_tokens / r entries per page:
+ * entry s of sequence b is pool row block_table[b * max_pages + s / E] * E + s % E (scales: the same
+ * row of their own array).  page_tokens is a power of two and a multiple of 128 and of every ratio
+ * used with it; block_table is device int32 [B][max_pages] with the pages of entries < n_max
+ * mapped (the caller allocates and maps pages; the library never does).
+ *
+ * The state cache is plain device arrays: a ring of `ring` rows per sequence ([B][ring][c]) holds
+ * the row of position p at row p % ring.
+ */
+typedef struct {
+  const int32_t* block_table; /* device int32 [B][max_pages] */
+  int max_pages;              /* row length of block_table */
+  int page_tokens;            /* raw tokens per page: a power of two, a multiple of 128 */
+} csa_pages;
+
+/* One compression problem of csa_decode_append ([CSA] (1); [HCA] (1) when cb = zb = NULL). */
+typedef struct {
+  const void* ca;             /* the new token's rows, [B][c] each in in_t */
+  const void* cb;             /* NULL for HCA (and then zb, bias_b, ring_cb, ring_zb NULL) */
+  const void* za;
+  const void* zb;
+  const float* bias_a;        /* [m][c] */
+  const float* bias_b;        /* [m][c] or NULL */
+  int c;                      /* width, a multiple of 4, <= 1024 (of 32 for MXFP4 output) */
+  int m;                      /* compression ratio: the entry pools 2m rows (m rows for HCA) */
+  void* ring_ca;              /* state rings [B][ring][c] in in_t, ring = 2m (m for HCA): the */
+  void* ring_cb;              /* streams of tokens [t - ring, t) on entry, of (t - ring, t] on exit */
+  void* ring_za;
+  void* ring_zb;
+  void* out;                  /* paged pool of completed entries, rows as csa_compress's out_t */
+  void* out_scale;            /* their scales (fp8: float32 per row; MXFP4: c/32 bytes per row) */
+  int out_t;
+  const csa_kv_prep* prep;    /* as in csa_compress (entry i prepared at position m * i) */
+} csa_append_job;
+
+/* One sliding-window ring of csa_decode_append ([details] (3)). */
+typedef struct {
+  const void* row;            /* the new token's KV row, [B][c] in in_t */
+  void* ring;                 /* [B][n_win][c] in in_t: position p at row p % n_win */
+  int c;
+  int n_win;
+  const csa_kv_prep* prep;    /* NULL: stored as it is; else stored prepared at position t */
+} csa_window_job;
+
+/*
+ * csa_decode_append -- one decode token per sequence enters the state cache.  For sequence b with
+ * t = pos[b] (device int64 [B]):
+ *   - every job whose block just completed (t >= m and t % m == 0) computes entry i = t/m - 1 from
+ *     its rings (the a-rows of tokens [t - m, t), the b-rows of [t - 2m, t - m); block 0 has no
+ *     b-rows) exactly as csa_compress would from the same rows, and writes it to row i of its paged
+ *     pool; then every job stores the token's rows at ring row t % ring;
+ *   - every window job stores its row at ring row t % n_win.
+ * Entry i is visible to queries t' >= m (i + 1), so a decode step appends its token first and then
+ * runs csa_index_paged / csa_topk / csa_attend_paged for the same t.  A sequence with pos[b] < 0 is
+ * left alone; an entry whose logical page is >= max_pages is not stored (its pages must be mapped
+ * before the step; positions live on the device, so the host cannot check them).
+ * Limits: 1 <= njobs <= 2, 0 <= nwins <= 2, in_t CSA_F32 or CSA_BF16, B < 65536; the jobs of one
+ * call all have m < 64 (256-thread workgroups) or all m >= 64 (1024-thread workgroups), the thread
+ * counts csa_compress uses for them, so that an entry's value does not depend on the call (e.g. the
+ * KV entry and indexer key in one call, the HCA entry in another).  Errors: CSA_ERR_NULL for a
+ * missing pointer, CSA_ERR_SHAPE / CSA_ERR_UNSUPPORTED as csa_compress for the jobs' shapes and
+ * formats, and for pages whose page_tokens is not a power of two, a multiple of 128 and of m.
+ */
+csa_status csa_decode_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
+                             const int64_t* pos, const csa_pages* pages, int in_t, void* stream);
+
+/*
+ * csa_index_paged -- csa_index for decode rows (T = 1) over a paged key pool: k_pool / k_scale_pool
+ * hold the keys in qk_t (rows as csa_index's k and k_scale), entry s of sequence b at the pool row
+ * given by `pages` (ratio m).  Scores [B][1][n_max] and bound keys exactly as csa_index; n_max is
+ * the logical cache size and must fit the mapped pages.  The MFMA formats only (bf16, fp8, MXFP4).
+ */
+csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                           const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                           const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                           void* stream);
+
+/*
+ * csa_attend_paged / hca_attend_paged -- csa_attend / hca_attend for decode rows (T = 1) whose
+ * compressed entries sit in a paged pool (comp_pool, comp_scale_pool; ratio m, resp. m_hca) and
+ * whose window rows sit in a state ring win_ring [B][n_win][c] (position p at row p % n_win: the
+ * ring of csa_decode_append, holding positions t - n_win + 1 .. t).  Everything else, including
+ * kv_t = CSA_BF16 and the comp_t / kv_prepared rules (kv_prepared >= 1), is as in the contiguous
+ * calls; the workspaces are csa_attend_workspace_bytes(B, 1, ...) and hca_attend_workspace_bytes(B, 1, ...).
+ */
+csa_status csa_attend_paged(const void* q, const void* comp_pool, const float* comp_scale_pool,
+                            const csa_pages* pages, const int32_t* idx, const void* win_ring, const float* sink,
+                            const float* gamma_q, const float* gamma_kv, int B, int H, int c, int rope_dims, int k,
+                            int n_win, int64_t n_max, const int64_t* pos0, int m, float scale, float eps,
+                            float rope_base, int kv_t, int comp_t, int kv_prepared, void* out, int out_t,
+                            void* workspace, size_t ws_bytes, void* stream);
+csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* comp_scale_pool,
+                            const csa_pages* pages, const void* win_ring, const float* sink, const float* gamma_q,
+                            const float* gamma_kv, int B, int H, int c, int rope_dims, int n_win, int64_t n_max,
+                            const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t,
+                            int comp_t, int kv_prepared, void* out, int out_t, void* workspace, size_t ws_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

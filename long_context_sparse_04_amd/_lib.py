@@ -21,9 +21,29 @@ class KvPrep(C.Structure):
     _fields_ = [("gamma", C.c_void_p), ("eps", C.c_float), ("rope_dims", C.c_int), ("rope_base", C.c_float)]
 
 
+class Pages(C.Structure):
+    """csa_pages: block table [B][max_pages] (device int32) and raw tokens per page."""
+    _fields_ = [("block_table", C.c_void_p), ("max_pages", C.c_int), ("page_tokens", C.c_int)]
+
+
+class AppendJob(C.Structure):
+    """csa_append_job: one compression problem of csa_decode_append."""
+    _fields_ = [("ca", C.c_void_p), ("cb", C.c_void_p), ("za", C.c_void_p), ("zb", C.c_void_p),
+                ("bias_a", C.c_void_p), ("bias_b", C.c_void_p), ("c", C.c_int), ("m", C.c_int),
+                ("ring_ca", C.c_void_p), ("ring_cb", C.c_void_p), ("ring_za", C.c_void_p), ("ring_zb", C.c_void_p),
+                ("out", C.c_void_p), ("out_scale", C.c_void_p), ("out_t", C.c_int), ("prep", C.POINTER(KvPrep))]
+
+
+class WindowJob(C.Structure):
+    """csa_window_job: one sliding-window ring of csa_decode_append."""
+    _fields_ = [("row", C.c_void_p), ("ring", C.c_void_p), ("c", C.c_int), ("n_win", C.c_int),
+                ("prep", C.POINTER(KvPrep))]
+
+
 # name -> (restype, argtypes); must match include/csa.h
 _P, _I, _I64, _F, _SZ = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
 _PREP = C.POINTER(KvPrep)
+_PG = C.POINTER(Pages)
 SIGNATURES = {
     "csa_status_string": (C.c_char_p, [_I]),
     "csa_abi_version": (_I, []),
@@ -45,6 +65,12 @@ SIGNATURES = {
     "hca_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I64, _I]),
     "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _I,
                         _P, _I, _P, _SZ, _P]),
+    "csa_decode_append": (_I, [C.POINTER(AppendJob), _I, C.POINTER(WindowJob), _I, _I, _P, _PG, _I, _P]),
+    "csa_index_paged": (_I, [_P, _P, _P, _P, _P, _PG, _I, _I, _I, _I64, _P, _I, _I, _P, _I, _P, _P]),
+    "csa_attend_paged": (_I, [_P, _P, _P, _PG, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F,
+                              _I, _I, _I, _P, _I, _P, _SZ, _P]),
+    "hca_attend_paged": (_I, [_P, _P, _P, _PG, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I,
+                              _I, _P, _I, _P, _SZ, _P]),
 }
 
 _lib = None

@@ -234,15 +234,19 @@ def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_
         out_scale = torch.empty((B, rows), dtype=torch.float32, device=x.device)
     if tuple(out.shape) != (B, rows, ob):
         raise CSAError(f"prepare_kv: out shape {tuple(out.shape)} is not {(B, rows, ob)}")
-    for t, n in ((x, c), (out, ob)):   # rows of one sequence contiguous; sequences may sit at any row stride
-        if t.stride(2) != 1 or t.stride(1) != n or t.stride(0) % n:
+    # rows of one sequence contiguous; sequences may sit at any row stride (the strides of size-1 dims are
+    # whatever the tensor's maker left there, and do not matter)
+    bstride = {}
+    for nm, t, n in (("x", x, c), ("out", out, ob)):
+        if t.stride(2) != 1 or (rows > 1 and t.stride(1) != n) or (B > 1 and t.stride(0) % n):
             raise CSAError("prepare_kv: rows must be contiguous with a whole-row batch stride")
+        bstride[nm] = t.stride(0) // n if B > 1 else rows
     for t in (x, out):
         if not t.is_cuda:
             raise CSAError("tensor must live on the GPU")
-    if mixed and (out_scale.stride(1) != 1 or out_scale.stride(0) != out.stride(0) // ob):
+    if mixed and ((rows > 1 and out_scale.stride(1) != 1) or (B > 1 and out_scale.stride(0) != bstride["out"])):
         raise CSAError("prepare_kv: out_scale must follow out's row layout")
-    st = lib.csa_prepare_kv(x.data_ptr(), x.stride(0) // c, out.data_ptr(), _ptr(out_scale), out.stride(0) // ob, B,
+    st = lib.csa_prepare_kv(x.data_ptr(), bstride["x"], out.data_ptr(), _ptr(out_scale), bstride["out"], B,
                             rows, c, FMT[in_fmt], FMT[out_fmt], _ptr(pos_base), pos_first, pos_stride,
                             _prep_arg(prep), _stream(stream))
     _lib.check(st, "csa_prepare_kv")
@@ -300,4 +304,108 @@ def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, e
                         FMT[kv_fmt], _comp_t(comp_kv, comp_scale, kv_fmt), int(kv_prepared), _ptr(out),
                         FMT[out_fmt], _ptr(ws), nb, _stream(stream))
     _lib.check(st, "hca_attend")
+    return out
+
+
+# ---- decode across steps: state rings and paged compressed caches -------------------------------------------
+
+
+def pages(block_table, page_tokens):
+    """csa_pages for a device int32 block table [B][max_pages] (kept alive by the returned struct's owner)."""
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise CSAError("pages: block_table must be a contiguous int32 [B][max_pages] tensor")
+    pg = _lib.Pages(_ptr(block_table), block_table.shape[1], page_tokens)
+    pg._table = block_table
+    return pg
+
+
+def decode_append(jobs, wins, pos, pg, stream=None):
+    """csa_decode_append.  jobs: dicts with ca, cb, za, zb ([B][c] token rows; cb = zb = None for HCA), bias_a,
+    bias_b, m, ring_ca, ring_cb, ring_za, ring_zb ([B][ring][c]), out, out_scale, out_fmt, prep.  wins: dicts with
+    row [B][c], ring [B][n_win][c], prep (optional).  pos: device int64 [B], the token's position."""
+    lib = _lib.load()
+    B = pos.shape[0]
+    in_fmt = _TORCH_FMT[jobs[0]["ca"].dtype]
+    keep = []
+    jarr = (_lib.AppendJob * max(1, len(jobs)))()
+    for i, j in enumerate(jobs):
+        prep = j.get("prep")
+        keep.append(prep)
+        jarr[i] = _lib.AppendJob(_ptr(j["ca"]), _ptr(j.get("cb")), _ptr(j["za"]), _ptr(j.get("zb")), _ptr(j["bias_a"]),
+                                 _ptr(j.get("bias_b")), j["ca"].shape[1], j["m"], _ptr(j["ring_ca"]),
+                                 _ptr(j.get("ring_cb")), _ptr(j["ring_za"]), _ptr(j.get("ring_zb")), _dptr(j["out"]),
+                                 _dptr(j.get("out_scale")), FMT[j.get("out_fmt") or in_fmt],
+                                 None if prep is None else C.pointer(prep))
+    warr = (_lib.WindowJob * max(1, len(wins)))()
+    for i, w in enumerate(wins):
+        prep = w.get("prep")
+        keep.append(prep)
+        warr[i] = _lib.WindowJob(_ptr(w["row"]), _ptr(w["ring"]), w["ring"].shape[2], w["ring"].shape[1],
+                                 None if prep is None else C.pointer(prep))
+    st = lib.csa_decode_append(jarr, len(jobs), warr, len(wins), B, _ptr(pos), C.byref(pg), FMT[in_fmt],
+                               _stream(stream))
+    _lib.check(st, "csa_decode_append")
+
+
+def index_paged(q, q_scale, w, k_pool, k_scale_pool, pg, pos0, m, fmt, n_max, scores=None, bound=None,
+                score_fmt="f32", stream=None):
+    """csa_index_paged: decode rows (q [B][1][HI][row]) over the paged key pool; scores [B][1][n_max]."""
+    lib = _lib.load()
+    B, T, HI = q.shape[0], q.shape[1], q.shape[2]
+    if T != 1:
+        raise CSAError("index_paged: decode rows only (T = 1)")
+    cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
+    if scores is None:
+        scores = _score_buf(B, 1, n_max, score_fmt, q.device)
+    st = lib.csa_index_paged(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_pool), _ptr(k_scale_pool), C.byref(pg), B, HI, cI,
+                             n_max, _ptr(pos0), m, FMT[fmt], _ptr(scores), FMT[_TORCH_FMT[scores.dtype]], _ptr(bound),
+                             _stream(stream))
+    _lib.check(st, "csa_index_paged")
+    return scores
+
+
+def attend_paged(q, comp_pool, idx, win_ring, sink, pos0, pg, m, rope_dims, scale, n_max, eps=1e-6,
+                 rope_base=10000.0, gamma_q=None, gamma_kv=None, out=None, ws=None, stream=None, kv_prepared=1,
+                 comp_scale=None):
+    """csa_attend_paged: q [B][1][H][c], comp_pool rows (bf16 [rows][c] or uint8 [rows][c + R] with comp_scale),
+    idx int32 [B][1][k], win_ring [B][n_win][c] (position p at row p % n_win)."""
+    lib = _lib.load()
+    B, T, H, c = q.shape
+    if T != 1:
+        raise CSAError("attend_paged: decode rows only (T = 1)")
+    k = idx.shape[2]
+    n_win = win_ring.shape[1]
+    if out is None:
+        out = torch.empty((B, 1, H, c), dtype=torch.bfloat16, device=q.device)
+    nb = lib.csa_attend_workspace_bytes(B, 1, H, c, k, n_win)
+    if ws is None:
+        ws = workspace(nb, q.device, "attend")
+    st = lib.csa_attend_paged(_ptr(q), _ptr(comp_pool), _ptr(comp_scale), C.byref(pg), _ptr(idx), _ptr(win_ring),
+                              _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv), B, H, c, rope_dims, k, n_win, n_max,
+                              _ptr(pos0), m, scale, eps, rope_base, FMT["bf16"],
+                              _comp_t(comp_pool, comp_scale, "bf16"), int(kv_prepared), _ptr(out),
+                              FMT[_TORCH_FMT[out.dtype]], _ptr(ws), nb, _stream(stream))
+    _lib.check(st, "csa_attend_paged")
+    return out
+
+
+def hca_attend_paged(q, comp_pool, win_ring, sink, pos0, pg, m_hca, rope_dims, scale, n_max, eps=1e-6,
+                     rope_base=10000.0, gamma_q=None, gamma_kv=None, out=None, ws=None, stream=None, kv_prepared=1,
+                     comp_scale=None):
+    """hca_attend_paged: dense over the visible entries of the paged HCA pool, window from the ring."""
+    lib = _lib.load()
+    B, T, H, c = q.shape
+    if T != 1:
+        raise CSAError("hca_attend_paged: decode rows only (T = 1)")
+    n_win = win_ring.shape[1]
+    if out is None:
+        out = torch.empty((B, 1, H, c), dtype=torch.bfloat16, device=q.device)
+    nb = lib.hca_attend_workspace_bytes(B, 1, H, c, n_max, n_win)
+    if ws is None:
+        ws = workspace(nb, q.device, "hca")
+    st = lib.hca_attend_paged(_ptr(q), _ptr(comp_pool), _ptr(comp_scale), C.byref(pg), _ptr(win_ring), _ptr(sink),
+                              _ptr(gamma_q), _ptr(gamma_kv), B, H, c, rope_dims, n_win, n_max, _ptr(pos0), m_hca, scale,
+                              eps, rope_base, FMT["bf16"], _comp_t(comp_pool, comp_scale, "bf16"), int(kv_prepared),
+                              _ptr(out), FMT[_TORCH_FMT[out.dtype]], _ptr(ws), nb, _stream(stream))
+    _lib.check(st, "hca_attend_paged")
     return out

@@ -60,6 +60,8 @@ struct AttnArgs {
   int prepared;           // 0 raw rows; 1 compressed entries stored prepared; 2 window rows prepared too
   const float* comp_scale;  // comp_mixed: the compressed rows' fp8 scales [B][n_max]
   int comp_mixed;           // compressed rows in CSA_FP8_BF16_ROPE (c + R bytes), widened to bf16 in LDS
+  const int32_t* table;     // paged: entry s of sequence b is pool row table[b * tstride + (s >> plog2)]
+  int tstride, plog2;       //   << plog2 | (s & (2^plog2 - 1)); the window rows are a ring [B][n_win][c]
   int ns_c, s_c, s_w;     // split layout: ns_c compressed parts of s_c slots, then window parts of s_w
   int64_t n_max;
   float scale, eps;
@@ -254,7 +256,7 @@ constexpr int lds_ctrl_halfs() {
 // [w*C/4, (w+1)*C/4).  Per stage: (1) resolve 64 slots (row address, position, validity),
 // (2) DMA every row straight into LDS (global_load_lds, 16 B per lane, no registers),
 // (3) per-entry RMS scalar and RoPE in place, (4) two 32-slot tiles of MFMA work from LDS.
-template <int C, bool WIDE, bool RAW, bool MIX>
+template <int C, bool WIDE, bool RAW, bool MIX, bool PAGED>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable rt, int nx) {
   // RAW: rows may need RMSNorm / RoPE here (raw compressed entries or raw window rows); without it every
   // row is stored prepared and the kernel has no normalisation or rotation of entries at all
@@ -330,13 +332,22 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       const bool valid = sl.row >= 0;
       // compressed rows in the mixed format: c + R bytes each, and their scale
       const bool mixed = MIX && valid && !sl.is_win;
-      const int64_t crow = (int64_t)b * a.n_max + sl.row;
+      int64_t crow = (int64_t)b * a.n_max + sl.row;
+      if constexpr (PAGED) {  // pool row of the entry (its page looked up in the block table)
+        crow = 0;
+        if (valid && !sl.is_win)
+          crow = ((int64_t)a.table[(int64_t)b * a.tstride + (sl.row >> a.plog2)] << a.plog2) |
+                 (sl.row & (((int64_t)1 << a.plog2) - 1));
+      }
+      // window row: position p of the query's window; paged calls keep the window in a ring (p % n_win)
+      const int64_t wrow = PAGED ? (int64_t)b * a.n_win + (int64_t)sl.pos % a.n_win
+                                 : (int64_t)b * (a.T + a.n_win - 1) + sl.row;
       const uint16_t* cptr = mixed ? reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.comp) +
                                                                        crow * (C + a.R))
                                    : a.comp + crow * C;
       // (a mixed row's address carries a 1 in bit 0: its rows start on 16-byte boundaries)
       s_src2[h * kStage + threadIdx.x] =
-          valid ? (sl.is_win ? a.win + ((int64_t)b * (a.T + a.n_win - 1) + sl.row) * C
+          valid ? (sl.is_win ? a.win + wrow * C
                              : reinterpret_cast<const uint16_t*>(reinterpret_cast<uintptr_t>(cptr) | (mixed ? 1u : 0u)))
                 : dummy;
       if (MIX) s_scp2[h * kStage + threadIdx.x] = mixed ? a.comp_scale + crow : a.sink;  // (readable when unused)
@@ -1090,12 +1101,12 @@ size_t bf16_lds_bytes() {
   return (size_t)lds_ctrl_halfs<WIDE>() * 2 + (WIDE ? 0 : 4 * 2 * 64 * 16) + ne * kStage * C * 2;
 }
 
-template <int C, bool WIDE, bool RAW, bool MIX>
+template <int C, bool WIDE, bool RAW, bool MIX, bool PAGED>
 csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStream_t stream) {
   const size_t lds = bf16_lds_bytes<C, WIDE>();
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C, WIDE, RAW, MIX>,
+    if (hipFuncSetAttribute((const void*)attend_bf16_kernel<C, WIDE, RAW, MIX, PAGED>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return CSA_ERR_LAUNCH;
     attr_set = true;
@@ -1105,23 +1116,26 @@ csa_status launch_bf16(const AttnArgs& a, const RopeTable& rt, int rows, hipStre
   const int nx = a.nsplit * rows;
   const int nx_pad = (nx + 7) & ~7;
   dim3 grid(nx_pad, a.H / (WIDE ? 64 : 16));
-  hipLaunchKernelGGL((attend_bf16_kernel<C, WIDE, RAW, MIX>), grid, dim3(256), lds, stream, a, rt, nx);
+  hipLaunchKernelGGL((attend_bf16_kernel<C, WIDE, RAW, MIX, PAGED>), grid, dim3(256), lds, stream, a, rt, nx);
   if (a.nsplit > 1) hipLaunchKernelGGL(attend_combine_kernel, dim3(rows, a.H), dim3(128), 0, stream, a, C, rt);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 
 // MIX: compressed rows in CSA_FP8_BF16_ROPE (a variant of its own, so that the bf16 kernels carry none of
 // its code)
-template <int C, bool MIX>
+template <int C, bool MIX, bool PAGED>
 csa_status launch_bf16_fmt(const AttnArgs& a, const RopeTable& rt, int rows, bool wide, hipStream_t stream) {
-  if (wide) return launch_bf16<C, true, false, MIX>(a, rt, rows, stream);
-  return a.prepared == 2 ? launch_bf16<C, false, false, MIX>(a, rt, rows, stream)
-                         : launch_bf16<C, false, true, MIX>(a, rt, rows, stream);
+  if (wide) return launch_bf16<C, true, false, MIX, PAGED>(a, rt, rows, stream);
+  return a.prepared == 2 ? launch_bf16<C, false, false, MIX, PAGED>(a, rt, rows, stream)
+                         : launch_bf16<C, false, true, MIX, PAGED>(a, rt, rows, stream);
 }
 template <int C>
 csa_status launch_bf16_any(const AttnArgs& a, const RopeTable& rt, int rows, bool wide, hipStream_t stream) {
-  return a.comp_mixed ? launch_bf16_fmt<C, true>(a, rt, rows, wide, stream)
-                      : launch_bf16_fmt<C, false>(a, rt, rows, wide, stream);
+  if (a.table)
+    return a.comp_mixed ? launch_bf16_fmt<C, true, true>(a, rt, rows, wide, stream)
+                        : launch_bf16_fmt<C, false, true>(a, rt, rows, wide, stream);
+  return a.comp_mixed ? launch_bf16_fmt<C, true, false>(a, rt, rows, wide, stream)
+                      : launch_bf16_fmt<C, false, false>(a, rt, rows, wide, stream);
 }
 
 }  // namespace
@@ -1137,11 +1151,12 @@ size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncom
 }
 
 csa_status launch_attend(int mode, const void* q, const void* comp_kv, const float* comp_scale, bool comp_mixed,
-                         const int32_t* idx, const void* win_kv,
+                         const csa_pages* pages, const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
                          float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,
                          void* ws, hipStream_t stream) {
+  if (pages && (kv_t != CSA_BF16 || T != 1)) return CSA_ERR_UNSUPPORTED;
   const RopeTable rt = make_rope_table(rope_dims, rope_base);
   const int rows = B * T;
   if (kv_t == CSA_F32) {
@@ -1164,6 +1179,13 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const flo
   a.n_max = n_max; a.scale = scale; a.eps = eps; a.prepared = kv_prepared;
   a.comp_scale = comp_scale;
   a.comp_mixed = comp_mixed ? 1 : 0;
+  a.table = nullptr;
+  a.tstride = a.plog2 = 0;
+  if (pages) {
+    a.table = pages->block_table;
+    a.tstride = pages->max_pages;
+    while ((1 << a.plog2) < pages->page_tokens / m) ++a.plog2;
+  }
   const SplitLayout lay = split_layout(mode, T, H, kv_prepared, mode == 0 ? (int64_t)k : n_max, n_win);
   a.nsplit = lay.nsplit;
   a.ns_c = lay.ns_c;

@@ -76,6 +76,10 @@ struct Job {
   const float* gamma;
   float eps;
   int R;
+  int ring;              // > 0: rows are a state ring of `ring` rows per sequence (position p at p % ring)
+  const int32_t* table;  // non-NULL: the output is a paged pool (entry i of sequence b at its page's row)
+  int tstride;           // block-table row length
+  int plog2;             // log2 of the entries per page
 };
 struct Jobs {
   Job j[2];
@@ -106,7 +110,7 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
   const int64_t i = first_entry + e;
   const bool overlap = (cb != nullptr);
   const int nrows = (overlap && i > 0) ? 2 * m : m;  // i == 0: the b-side is -inf / 0
-  const int64_t base = (int64_t)b * rows * c;
+  const int64_t base = (int64_t)b * (jb.ring ? jb.ring : rows) * c;
 
   Soft4 st;
   st.init();
@@ -122,7 +126,8 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
         const int rr = min(rr0 + u * nrs, nrows - 1);
         const bool is_a = rr < m;
         const int rw = is_a ? rr : rr - m;
-        const int64_t row = (is_a ? m * i : m * (i - 1)) + rw - row0_pos;
+        const int64_t p = (is_a ? m * i : m * (i - 1)) + rw;  // the row's token position
+        const int64_t row = jb.ring ? p % jb.ring : p - row0_pos;
         z[u].load((is_a ? za : zb) + base + row * c + 4 * cg);
         v[u].load((is_a ? ca : cb) + base + row * c + 4 * cg);
         bb[u] = *reinterpret_cast<const f32x4*>((is_a ? bias_a : bias_b) + (int64_t)rw * c + 4 * cg);
@@ -165,7 +170,9 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
   }
 
   if (jb.prep) prep_row4<NT>(y, writer, cg, c, (double)m * (double)i, jb.gamma, jb.eps, jb.R, theta, s_red);
-  const int64_t orow = (int64_t)b * out_bstride + e;
+  const int64_t orow =
+      jb.table ? (((int64_t)jb.table[(int64_t)b * jb.tstride + (i >> jb.plog2)] << jb.plog2) | (i & ((1 << jb.plog2) - 1)))
+               : (int64_t)b * out_bstride + e;
   if (out_t == CSA_FP8_BF16_ROPE) {  // prepared entries only (checked on the host)
     store_fp8_rope_row<NT>(y, writer, cg, c, jb.R, static_cast<uint8_t*>(out) + orow * (c + jb.R),
                            static_cast<float*>(out_scale) + orow, s_red);

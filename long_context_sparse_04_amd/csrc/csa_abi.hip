@@ -22,7 +22,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 5; }
+int csa_abi_version(void) { return 6; }
 
 }  // extern "C"
 
@@ -268,7 +268,7 @@ csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scal
   if (comp_t != kv_t && n_max > 0 && !comp_scale) return CSA_ERR_NULL;
   const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_attend(0, q, comp_kv, comp_scale, comp_t != kv_t, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c,
+  return launch_attend(0, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c,
                        rope_dims, k, n_win, n_max, pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,
                        workspace, (hipStream_t)stream);
 }
@@ -294,9 +294,149 @@ csa_status hca_attend(const void* q, const void* comp_kv, const float* comp_scal
   if (comp_t != kv_t && n_max > 0 && !comp_scale) return CSA_ERR_NULL;
   const size_t need = hca_attend_workspace_bytes(B, T, H, c, n_max, n_win);
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  return launch_attend(1, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H,
+  return launch_attend(1, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, nullptr, win_kv, sink, gamma_q, gamma_kv, B, T, H,
                        c, rope_dims, 1, n_win, n_max, pos0, m_hca, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,
                        workspace, (hipStream_t)stream);
+}
+
+
+}  // extern "C"
+
+namespace {
+// a page map usable for entries at ratio r: page_tokens a power of two, a multiple of 128 and of r
+csa_status check_pages(const csa_pages* pages, int ratio) {
+  if (!pages || !pages->block_table) return CSA_ERR_NULL;
+  const int P = pages->page_tokens;
+  if (P < 128 || (P & (P - 1)) || pages->max_pages < 1) return CSA_ERR_SHAPE;
+  if (ratio < 1 || P % ratio) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+// logical entries of a sequence must fit its table row
+csa_status check_pages_cover(const csa_pages* pages, int ratio, int64_t n_max) {
+  const int64_t per_page = pages->page_tokens / ratio;
+  return (n_max + per_page - 1) / per_page <= pages->max_pages ? CSA_OK : CSA_ERR_SHAPE;
+}
+csa_status check_prep(const csa_kv_prep* prep, int c) {
+  if (!prep) return CSA_OK;
+  if (prep->rope_dims < 0 || (prep->rope_dims % 8) || prep->rope_dims > c || prep->rope_dims > 128)
+    return CSA_ERR_UNSUPPORTED;
+  if (!(prep->eps >= 0.0f)) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_decode_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
+                             const int64_t* pos, const csa_pages* pages, int in_t, void* stream) {
+  if (njobs < 1 || njobs > 2 || nwins < 0 || nwins > 2 || B < 0) return CSA_ERR_SHAPE;
+  if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (B >= 65536) return CSA_ERR_UNSUPPORTED;
+  if (!jobs || (nwins > 0 && !wins)) return CSA_ERR_NULL;
+  for (int i = 0; i < njobs; ++i) {
+    const csa_append_job& j = jobs[i];
+    if (j.m < 1 || j.m > 1024 || j.c < 4 || j.c > 1024 || (j.c & 3)) return CSA_ERR_SHAPE;
+    if ((j.m >= 64) != (jobs[0].m >= 64)) return CSA_ERR_UNSUPPORTED;
+    if (j.out_t < CSA_F32 || j.out_t > CSA_FP8_BF16_ROPE) return CSA_ERR_UNSUPPORTED;
+    if (j.prep && j.out_t != CSA_F32 && j.out_t != CSA_BF16 && j.out_t != CSA_FP8_BF16_ROPE)
+      return CSA_ERR_UNSUPPORTED;
+    if (j.out_t == CSA_FP8_BF16_ROPE && (!j.prep || (j.c - j.prep->rope_dims) % 16 != 0)) return CSA_ERR_UNSUPPORTED;
+    if (j.out_t == CSA_MXFP4_E8M0_B32 && (j.c % 32)) return CSA_ERR_UNSUPPORTED;
+    csa_status st = check_prep(j.prep, j.c);
+    if (st != CSA_OK) return st;
+    st = check_pages(pages, j.m);
+    if (st != CSA_OK) return st;
+    const bool overlap = j.cb || j.zb || j.bias_b || j.ring_cb || j.ring_zb;
+    if (!j.ca || !j.za || !j.bias_a || !j.ring_ca || !j.ring_za || !j.out) return CSA_ERR_NULL;
+    if (overlap && (!j.cb || !j.zb || !j.bias_b || !j.ring_cb || !j.ring_zb)) return CSA_ERR_NULL;
+    if ((j.out_t == CSA_FP8_E4M3_ROWSCALE || j.out_t == CSA_MXFP4_E8M0_B32 || j.out_t == CSA_FP8_BF16_ROPE) &&
+        !j.out_scale)
+      return CSA_ERR_NULL;
+  }
+  for (int i = 0; i < nwins; ++i) {
+    const csa_window_job& w = wins[i];
+    if (w.c < 4 || w.c > 1024 || (w.c & 3) || w.n_win < 1 || w.n_win > 4096) return CSA_ERR_SHAPE;
+    const csa_status st = check_prep(w.prep, w.c);
+    if (st != CSA_OK) return st;
+    if (!w.row || !w.ring) return CSA_ERR_NULL;
+  }
+  if (B == 0) return CSA_OK;
+  if (!pos) return CSA_ERR_NULL;
+  return launch_decode_append(jobs, njobs, wins, nwins, B, pos, pages, in_t, (hipStream_t)stream);
+}
+
+csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                           const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                           const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                           void* stream) {
+  if (qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3_ROWSCALE && qk_t != CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
+  if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  bool empty;
+  csa_status st = check_index(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, cI, n_max, pos0, m, qk_t, scores,
+                              empty);
+  if (st != CSA_OK) return st;
+  st = check_pages(pages, m);
+  if (st != CSA_OK) return st;
+  st = check_pages_cover(pages, m, n_max);
+  if (st != CSA_OK) return st;
+  if (empty) return CSA_OK;
+  if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
+  return launch_index_paged(q, q_scale, w, k_pool, k_scale_pool, pages, B, HI, cI, n_max, pos0, m, qk_t, scores,
+                            score_t, bound, (hipStream_t)stream);
+}
+
+csa_status csa_attend_paged(const void* q, const void* comp_pool, const float* comp_scale_pool,
+                            const csa_pages* pages, const int32_t* idx, const void* win_ring, const float* sink,
+                            const float* gamma_q, const float* gamma_kv, int B, int H, int c, int rope_dims, int k,
+                            int n_win, int64_t n_max, const int64_t* pos0, int m, float scale, float eps,
+                            float rope_base, int kv_t, int comp_t, int kv_prepared, void* out, int out_t,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  csa_status st = check_attend(kv_t, out_t, B, 1, H, c, rope_dims, n_win, m);
+  if (st != CSA_OK) return st;
+  if (kv_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  st = check_comp_t(kv_t, comp_t, kv_prepared, c, rope_dims);
+  if (st != CSA_OK) return st;
+  if (k < 1 || k > 2048 || n_max < 0 || n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
+  st = check_pages(pages, m);
+  if (st != CSA_OK) return st;
+  st = check_pages_cover(pages, m, n_max);
+  if (st != CSA_OK) return st;
+  if (B == 0) return CSA_OK;
+  if (!q || !idx || !win_ring || !sink || !pos0 || !out || (n_max > 0 && !comp_pool)) return CSA_ERR_NULL;
+  if (comp_t != kv_t && n_max > 0 && !comp_scale_pool) return CSA_ERR_NULL;
+  const size_t need = csa_attend_workspace_bytes(B, 1, H, c, k, n_win);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  return launch_attend(0, q, comp_pool, comp_scale_pool, comp_t != kv_t, pages, idx, win_ring, sink, gamma_q,
+                       gamma_kv, B, 1, H, c, rope_dims, k, n_win, n_max, pos0, m, scale, eps, rope_base, kv_t,
+                       kv_prepared, out, out_t, workspace, (hipStream_t)stream);
+}
+
+csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* comp_scale_pool,
+                            const csa_pages* pages, const void* win_ring, const float* sink, const float* gamma_q,
+                            const float* gamma_kv, int B, int H, int c, int rope_dims, int n_win, int64_t n_max,
+                            const int64_t* pos0, int m_hca, float scale, float eps, float rope_base, int kv_t,
+                            int comp_t, int kv_prepared, void* out, int out_t, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  csa_status st = check_attend(kv_t, out_t, B, 1, H, c, rope_dims, n_win, m_hca);
+  if (st != CSA_OK) return st;
+  if (kv_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  st = check_comp_t(kv_t, comp_t, kv_prepared, c, rope_dims);
+  if (st != CSA_OK) return st;
+  if (n_max < 0 || n_max >= ((int64_t)1 << 24)) return CSA_ERR_SHAPE;
+  if (kv_prepared < 0 || kv_prepared > 2) return CSA_ERR_UNSUPPORTED;
+  st = check_pages(pages, m_hca);
+  if (st != CSA_OK) return st;
+  st = check_pages_cover(pages, m_hca, n_max);
+  if (st != CSA_OK) return st;
+  if (B == 0) return CSA_OK;
+  if (!q || !win_ring || !sink || !pos0 || !out || (n_max > 0 && !comp_pool)) return CSA_ERR_NULL;
+  if (comp_t != kv_t && n_max > 0 && !comp_scale_pool) return CSA_ERR_NULL;
+  const size_t need = hca_attend_workspace_bytes(B, 1, H, c, n_max, n_win);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  return launch_attend(1, q, comp_pool, comp_scale_pool, comp_t != kv_t, pages, nullptr, win_ring, sink, gamma_q,
+                       gamma_kv, B, 1, H, c, rope_dims, 1, n_win, n_max, pos0, m_hca, scale, eps, rope_base, kv_t,
+                       kv_prepared, out, out_t, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -34,6 +34,15 @@ csa_status launch_prepare_kv(const void* in, int64_t in_bstride, void* out, void
                              int B, int rows, int c, int in_t, int out_t, const int64_t* pos_base, int64_t pos_first,
                              int64_t pos_stride, const csa_kv_prep* prep, hipStream_t stream);
 
+// csa_decode_append (validated): the jobs' rings and paged outputs, the window rings
+csa_status launch_decode_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
+                                const int64_t* pos, const csa_pages* pages, int in_t, hipStream_t stream);
+
+csa_status launch_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                              const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                              const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                              hipStream_t stream);
+
 // bound keys per query row written by the decode index kernel (two per bound set)
 int64_t index_bound_keys(int64_t n_max);
 bool use_prefill_index(int fmt, int T, int HI);
@@ -55,8 +64,9 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
 // mode 0: CSA (index list), mode 1: HCA (dense range)
 size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win);
 // comp_mixed: comp_kv rows in CSA_FP8_BF16_ROPE with their scales in comp_scale
+// pages (non-NULL, decode rows only): comp_kv / comp_scale are paged pools, win_kv a ring [B][n_win][c]
 csa_status launch_attend(int mode, const void* q, const void* comp_kv, const float* comp_scale, bool comp_mixed,
-                         const int32_t* idx, const void* win_kv,
+                         const csa_pages* pages, const int32_t* idx, const void* win_kv,
                          const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T, int H,
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
                          float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,

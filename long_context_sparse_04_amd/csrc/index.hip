@@ -182,13 +182,20 @@ struct IndexFuse {
   int64_t row0_pos, first_entry;
 };
 struct NoFuse {};
+// A paged key cache (csa_pages): logical entry s of sequence b is pool row table[b * tstride + (s >> plog2)]
+// << plog2 | (s & (2^plog2 - 1)).
+struct PageMap {
+  const int32_t* table;
+  int tstride;
+  int plog2;
+};
 
-template <int FMT, int NT, bool FUSE>
+template <int FMT, int NT, bool FUSE, bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
     const int64_t* __restrict__ pos0, int m, ScoreOut so, uint32_t* __restrict__ bound,
-    std::conditional_t<FUSE, IndexFuse, NoFuse> fz) {
+    std::conditional_t<FUSE, IndexFuse, NoFuse> fz, PageMap pm) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
   constexpr int LB = Fmt<FMT>::kLaneBytes;
@@ -260,15 +267,32 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   // R + 1 tile buffers: the load of tile i + R is issued before tile i is used, into the buffer tile
   // i - 1 has released, so R tiles are always in flight.  The wave reads its MFMA operands back from its
   // own buffers, so no barrier is involved.
-  const uint8_t* kb = kI + (int64_t)b * n_max * RB;
   const int64_t wave_first = wg_first + (int64_t)wave * kTilesPerWave * 16;
+  // Paged keys: a 16-entry tile never straddles a page (pages hold 2^plog2 >= 32 entries), and the tile
+  // of a clamped row (past n_max - 1) is the page of entry n_max - 1.  Lane j holds the pool page of this
+  // wave's j-th logical page (clamped to the last one), loaded once before any tile.
+  const int64_t wfp = PAGED ? wave_first >> pm.plog2 : 0;
+  const int64_t pmask = PAGED ? ((int64_t)1 << pm.plog2) - 1 : 0;
+  int tab = 0;
+  if constexpr (PAGED)
+    tab = pm.table[(int64_t)b * pm.tstride + min(wfp + lane, (n_max - 1) >> pm.plog2)];
+  // pool row of the clamped entry er, whose tile starts at the clamped entry ec
+  auto key_row = [&](int64_t er, int64_t ec) -> int64_t {
+    if constexpr (PAGED) {
+      const int pg = __builtin_amdgcn_readlane(tab, (int)max((int64_t)0, (ec >> pm.plog2) - wfp));
+      return ((int64_t)pg << pm.plog2) | (er & pmask);
+    } else {
+      return (int64_t)b * n_max + er;
+    }
+  };
   Frag<FMT> kf_reg[kStaged ? 1 : kSlots];  // register ring (unstaged rows)
   int ksc_reg[kStaged ? 1 : kSlots];
   auto issue_tile = [&](int slot, int64_t e0) {
     if constexpr (!kStaged) {
       const int64_t el = min(e0 + (lane & 15), n_max - 1);
-      kf_reg[slot] = load_frag<FMT>(kb + el * RB, lane);
-      ksc_reg[slot] = static_cast<const uint8_t*>(k_scale)[((int64_t)b * n_max + el) * 4 + gl];
+      const int64_t kr = key_row(el, min(e0, n_max - 1));
+      kf_reg[slot] = load_frag<FMT>(kI + kr * RB, lane);
+      ksc_reg[slot] = static_cast<const uint8_t*>(k_scale)[kr * 4 + gl];
       return;
     }
 #pragma unroll
@@ -279,20 +303,28 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
       const int c = pos ^ tile_swz_key<RB>(e);    // logical chunk stored there
       const int64_t er = min(e0 + e, n_max - 1);  // rows past the end re-read the last one
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kb + er * RB + 16 * c),
+          (const __attribute__((address_space(1))) void*)(kI + key_row(er, min(e0, n_max - 1)) * RB + 16 * c),
           (__attribute__((address_space(3))) void*)(&s_ring[slot][wave][1024 * j]), 16, 0, 0);
     }
   };
   // the key scale words of all of the wave's entries (4 bytes each: the fp8 row scale, or the 4 E8M0
   // block scales of an MXFP4 row), 64 entries per instruction, before any tile
   if constexpr (kStaged && kScaled) {
+    constexpr int kScaleLoads = kTilesPerWave * 16 / 64;
+    int64_t srow[kScaleLoads];  // every row first: the page lookups are lane exchanges, kept ahead of the DMA
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave * 16 / 64; ++j) {
+    for (int j = 0; j < kScaleLoads; ++j) {
       const int64_t er = min(wave_first + 64 * j + lane, n_max - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(static_cast<const uint32_t*>(k_scale) + b * n_max + er),
-          (__attribute__((address_space(3))) void*)(&s_ksc[wave][64 * j]), 4, 0, 0);
+      if constexpr (PAGED)
+        srow[j] = ((int64_t)__shfl(tab, (int)((er >> pm.plog2) - wfp), 64) << pm.plog2) | (er & pmask);
+      else
+        srow[j] = (int64_t)b * n_max + er;
     }
+#pragma unroll
+    for (int j = 0; j < kScaleLoads; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(static_cast<const uint32_t*>(k_scale) + srow[j]),
+          (__attribute__((address_space(3))) void*)(&s_ksc[wave][64 * j]), 4, 0, 0);
   }
   // the first R tiles go out before anything else (they do not wait for the query position; past the
   // visible range they are simply not used)
@@ -593,7 +625,24 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
                       int T, int HI, int64_t n_max, const int64_t* pos0, int m, ScoreOut so, uint32_t* bound,
-                      const IndexFuse* fuse, hipStream_t stream) {
+                      const IndexFuse* fuse, const PageMap* pages, hipStream_t stream) {
+  if (pages) {  // decode rows over a paged key pool
+    if (fuse || T != 1) return CSA_ERR_UNSUPPORTED;
+    dim3 grid(ceil_div(n_max, kEntriesPerWG), B);
+    dim3 block(kWaves * 64);
+#define CSA_IDX_PAGED(NT)                                                                                   \
+  hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, \
+                     w, (const uint8_t*)k, k_scale, 1, n_max, pos0, m, so, bound, NoFuse{}, *pages)
+    switch (HI) {
+      case 16: CSA_IDX_PAGED(1); break;
+      case 32: CSA_IDX_PAGED(2); break;
+      case 64: CSA_IDX_PAGED(4); break;
+      case 128: CSA_IDX_PAGED(8); break;
+      default: return CSA_ERR_UNSUPPORTED;
+    }
+#undef CSA_IDX_PAGED
+    return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+  }
   if (use_prefill_index(FMT, T, HI)) {  // many query rows: the tiled contraction
     if (bound || fuse) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(T, kPRows), B);
@@ -605,11 +654,11 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
   dim3 block(kWaves * 64);
 #define CSA_IDX_LAUNCH(NT)                                                                                       \
   if (fuse)                                                                                                     \
-    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, w, \
-                       (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, *fuse);                    \
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, true, false>), grid, block, 0, stream, (const uint8_t*)q, q_scale, \
+                       w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, *fuse, PageMap{});       \
   else                                                                                                          \
-    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false>), grid, block, 0, stream, (const uint8_t*)q, q_scale,  \
-                       w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, NoFuse{})
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false, false>), grid, block, 0, stream, (const uint8_t*)q,     \
+                       q_scale, w, (const uint8_t*)k, k_scale, T, n_max, pos0, m, so, bound, NoFuse{}, PageMap{})
   switch (HI) {
     case 16: CSA_IDX_LAUNCH(1); break;
     case 32: CSA_IDX_LAUNCH(2); break;
@@ -633,13 +682,25 @@ bool use_prefill_index(int fmt, int T, int HI) { return fmt == CSA_BF16 && T >= 
 static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
                                     const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
                                     const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
-                                    uint32_t* bound, const IndexFuse* fuse, hipStream_t stream);
+                                    uint32_t* bound, const IndexFuse* fuse, const PageMap* pages,
+                                    hipStream_t stream);
 
 csa_status launch_index(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
                         int B, int T, int HI, int cI, int64_t n_max, const int64_t* pos0, int m, int qk_t,
                         void* scores, int score_t, uint32_t* bound, hipStream_t stream) {
   return launch_index_impl(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
-                           nullptr, stream);
+                           nullptr, nullptr, stream);
+}
+
+csa_status launch_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                              const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                              const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                              hipStream_t stream) {
+  int plog2 = 0;
+  while ((1 << plog2) < pages->page_tokens / m) ++plog2;
+  const PageMap pm{pages->block_table, pages->max_pages, plog2};
+  return launch_index_impl(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, score_t,
+                           bound, nullptr, &pm, stream);
 }
 
 csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64_t row0_pos, int64_t first_entry,
@@ -654,17 +715,18 @@ csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64
   fz.row0_pos = row0_pos;
   fz.first_entry = first_entry;
   return launch_index_impl(q, q_scale, w, k, k_scale, B, 1, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
-                           &fz, stream);
+                           &fz, nullptr, stream);
 }
 
 static csa_status launch_index_impl(const void* q, const void* q_scale, const float* w, const void* k,
                                     const void* k_scale, int B, int T, int HI, int cI, int64_t n_max,
                                     const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
-                                    uint32_t* bound, const IndexFuse* fuse, hipStream_t stream) {
+                                    uint32_t* bound, const IndexFuse* fuse, const PageMap* pages,
+                                    hipStream_t stream) {
   const ScoreOut so{scores, score_t == CSA_BF16 ? 1 : 0};
   switch (qk_t) {
     case CSA_F32: {
-      if (bound || fuse) return CSA_ERR_UNSUPPORTED;
+      if (bound || fuse || pages) return CSA_ERR_UNSUPPORTED;
       dim3 grid(ceil_div(n_max, kF32Threads), B * T);
       size_t lds = (size_t)HI * cI * sizeof(float);
       hipLaunchKernelGGL(index_f32_kernel, grid, dim3(kF32Threads), lds, stream, (const float*)q, w,
@@ -672,11 +734,11 @@ static csa_status launch_index_impl(const void* q, const void* q_scale, const fl
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     }
     case CSA_BF16:
-      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
+      return launch_fmt<CSA_BF16>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, pages, stream);
     case CSA_FP8_E4M3_ROWSCALE:
-      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
+      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, pages, stream);
     case CSA_MXFP4_E8M0_B32:
-      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, stream);
+      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, pages, stream);
     default:
       return CSA_ERR_UNSUPPORTED;
   }

@@ -29,6 +29,7 @@ STREAMS = (
     "kv_cache", "ik_cache", "q", "qi", "w", "win", "sink",
     "hca_c", "hca_z", "hca_bias", "hca_cache", "hca_q", "hca_win", "hca_sink",
     "extra0", "extra1", "extra2", "extra3",
+    "dq", "dqi", "dw", "dhq",
 )
 _SID = {name: i for i, name in enumerate(STREAMS)}
 
@@ -162,3 +163,33 @@ def sink(cfg: CSAConfig, hca: bool = False) -> np.ndarray:
 
 def positions(cfg: CSAConfig) -> np.ndarray:
     return np.full((cfg.B,), cfg.pos0, dtype=np.int64)
+
+
+def decode_streams(cfg: CSAConfig, length: int, b: int):
+    """Every per-token row of sequence b for positions [0, length), as a decode loop consumes them (bf16 bits):
+    the CSA KV streams ca, cb, za, zb [L][c], the indexer streams ica .. izb [L][cI], the HCA streams hca_c,
+    hca_z [L][c], and the window KV rows of the CSA and HCA layers, win and hca_win [L][c].  N(0, 1)."""
+    out = {}
+    for name, width in (("ca", cfg.c), ("cb", cfg.c), ("za", cfg.c), ("zb", cfg.c), ("ica", cfg.cI), ("icb", cfg.cI),
+                        ("iza", cfg.cI), ("izb", cfg.cI), ("hca_c", cfg.c), ("hca_z", cfg.c), ("win", cfg.c),
+                        ("hca_win", cfg.c)):
+        out[name] = store(normal(cfg.seed, name, (length, width), b=b), "bf16")["data"]
+    return out
+
+
+def decode_biases(cfg: CSAConfig):
+    """The positional biases B^a, B^b (KV and indexer) and HCA's B, float32 [m][width]."""
+    return {"bias_a": normal(cfg.seed, "bias_a", (cfg.m, cfg.c)), "bias_b": normal(cfg.seed, "bias_b", (cfg.m, cfg.c)),
+            "ibias_a": normal(cfg.seed, "ibias_a", (cfg.m, cfg.cI)),
+            "ibias_b": normal(cfg.seed, "ibias_b", (cfg.m, cfg.cI)),
+            "hca_bias": normal(cfg.seed, "hca_bias", (cfg.m_hca, cfg.c))}
+
+
+def decode_queries(cfg: CSAConfig, steps: int, b: int):
+    """Per-step query rows of sequence b: q and hca q [S][H][c] (N(0,1)/sqrt(c)), indexer queries [S][HI][cI]
+    (N(0,1)/sqrt(cI)) in the workload's indexer format, weights [S][HI] U(0, 1)."""
+    q = store(normal(cfg.seed, "dq", (steps, cfg.H, cfg.c), b=b, scale=1.0 / np.sqrt(cfg.c)), "bf16")["data"]
+    hq = store(normal(cfg.seed, "dhq", (steps, cfg.H, cfg.c), b=b, scale=1.0 / np.sqrt(cfg.c)), "bf16")["data"]
+    qi = store(normal(cfg.seed, "dqi", (steps, cfg.HI, cfg.cI), b=b, scale=1.0 / np.sqrt(cfg.cI)), cfg.idx_dtype)
+    w = uniform(cfg.seed, "dw", (steps, cfg.HI), b=b)
+    return {"q": q, "hq": hq, "qi": qi, "w": w}

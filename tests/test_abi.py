@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 5
+    assert lib.csa_abi_version() == 6
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -182,3 +182,76 @@ def test_index_topk_attend_validation(lib):
     assert lib.hca_attend(DUMMY, DUMMY, None, DUMMY, DUMMY, None, None, 8, 1, 128, 512, 64, 128, 8192, DUMMY, 128, 0.044,
                           1e-6, 1e4, 1, 4, 2, DUMMY, 1, DUMMY, 1 << 30, None) == 1
     assert lib.hca_attend_workspace_bytes(8, 1, 128, 512, 8192, 128) > 0
+
+
+def _pages(table=DUMMY, max_pages=4, page_tokens=1024):
+    return _lib.Pages(table, max_pages, page_tokens)
+
+
+def test_decode_append_validation(lib):
+    """csa_decode_append: job / window shapes, the page map, the thread-count class of the jobs."""
+    def job(**kw):
+        a = dict(ca=DUMMY, cb=DUMMY, za=DUMMY, zb=DUMMY, bias_a=DUMMY, bias_b=DUMMY, c=512, m=4, ring_ca=DUMMY,
+                 ring_cb=DUMMY, ring_za=DUMMY, ring_zb=DUMMY, out=DUMMY, out_scale=None, out_t=1, prep=None)
+        a.update(kw)
+        return _lib.AppendJob(**a)
+
+    def call(jobs, wins=(), B=2, pos=DUMMY, pages=None, in_t=1):
+        ja = (_lib.AppendJob * max(1, len(jobs)))(*jobs)
+        wa = (_lib.WindowJob * max(1, len(wins)))(*wins)
+        pg = _pages() if pages is None else pages
+        return lib.csa_decode_append(ja, len(jobs), wa, len(wins), B, pos, C.byref(pg), in_t, None)
+
+    hca = job(cb=None, zb=None, bias_b=None, ring_cb=None, ring_zb=None, m=128)
+    assert call([job(), job(c=128)], B=0) == 0                   # nothing to do
+    assert call([], B=2) == 2                                     # at least one job
+    assert call([job(), job(), job()]) == 2                       # at most two
+    assert call([job(c=130)]) == 2
+    assert call([job(m=0)]) == 2
+    assert call([job(), hca]) == 3                                # mixed thread-count classes
+    assert call([job()], in_t=2) == 3
+    assert call([job(ring_za=None)]) == 1
+    assert call([job(ring_cb=None)]) == 1                         # half an overlapped job
+    assert call([job(out_t=2)]) == 1                              # fp8 output needs its scales
+    assert call([job(out_t=4)]) == 3                              # fp8 + bf16 RoPE needs prepared entries
+    assert call([job()], pages=_pages(page_tokens=96)) == 2       # not a power of two / multiple of 128
+    assert call([job()], pages=_pages(page_tokens=64)) == 2
+    assert call([job()], pages=_pages(table=None)) == 1
+    assert call([job()], pos=None) == 1
+    assert call([job()], wins=[_lib.WindowJob(DUMMY, DUMMY, 512, 0, None)]) == 2   # empty window ring
+    assert call([job()], wins=[_lib.WindowJob(None, DUMMY, 512, 128, None)]) == 1
+
+
+def test_paged_index_attend_validation(lib):
+    """csa_index_paged / csa_attend_paged / hca_attend_paged: formats, the page map and its coverage."""
+    pg = _pages(max_pages=4, page_tokens=1024)                  # 4 pages of 256 CSA entries, 8 HCA entries
+    P = C.byref(pg)
+
+    def index(n_max=1000, qk_t=2, pages=P, HI=64, cI=128, q=DUMMY):
+        return lib.csa_index_paged(q, DUMMY, DUMMY, DUMMY, DUMMY, pages, 2, HI, cI, n_max, DUMMY, 4, qk_t, DUMMY, 0,
+                                   None, None)
+
+    assert index(qk_t=0) == 3                                     # the MFMA formats only
+    assert index(n_max=1025) == 2                                 # more entries than the mapped pages hold
+    assert index(cI=64) == 3
+    assert index(q=None) == 1
+    bad = _pages(page_tokens=1000)
+    assert index(pages=C.byref(bad)) == 2
+
+    def attend(n_max=1000, kv_t=1, comp_t=1, prep=1, pages=P, m=4, k=512):
+        return lib.csa_attend_paged(DUMMY, DUMMY, None, pages, DUMMY, DUMMY, DUMMY, None, None, 2, 64, 512, 64, k, 128,
+                                    n_max, DUMMY, m, 0.04, 1e-6, 1e4, kv_t, comp_t, prep, DUMMY, 1, DUMMY, 1 << 30,
+                                    None)
+
+    assert attend(kv_t=0, comp_t=0) == 3                          # bf16 only
+    assert attend(n_max=1025) == 2
+    assert attend(comp_t=4) == 1                                  # mixed rows need their scales
+    assert attend(comp_t=4, prep=0) == 3                          # ... and prepared entries
+    assert attend(m=3) == 2                                       # page_tokens must be a multiple of m
+
+    def hca(n_max=32, m_hca=128, pages=P):
+        return lib.hca_attend_paged(DUMMY, DUMMY, None, pages, DUMMY, DUMMY, None, None, 2, 128, 512, 64, 128, n_max,
+                                    DUMMY, m_hca, 0.04, 1e-6, 1e4, 1, 1, 2, DUMMY, 1, DUMMY, 1 << 30, None)
+
+    assert hca(n_max=33) == 2                                     # 4 pages x 8 HCA entries
+    assert hca(m_hca=2048) == 2
