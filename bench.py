@@ -56,6 +56,11 @@ def parse():
     p.add_argument("--kv", default="bf16", choices=("bf16", "fp8rope"),
                    help="compressed KV cache storage: bf16 rows, or the non-RoPE dims in fp8 e4m3 with a row scale "
                         "and the RoPE dims in bf16")
+    p.add_argument("--paged", action="store_true",
+                   help="decode across steps: tokens enter the state-cache rings (csa_decode_append, which compresses "
+                        "an entry when a block completes), compressed entries live in paged pools behind a shuffled "
+                        "block table, and every step advances the positions by one")
+    p.add_argument("--page-tokens", type=int, default=1024, help="raw tokens per page (a power of two >= 128)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -86,6 +91,107 @@ def host_inputs(cfg, seed):
         d.update(hq=gen.queries(c, hca=True), hwin=gen.window(c, hca=True), hsink=gen.sink(c, hca=True),
                  chca=gen.compress_inputs(c, hca=True))
     return d
+
+
+def _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data, ik_scale, hca_cache, hca_scale, prep, pos,
+                 scores, bound, idx, out, hout, hca_ws, side, mixed):
+    """Pools, block table, state rings and the paged decode step.  Returns (step, index_only, visible)."""
+    dev = pos.device
+    B, N, R, m, mh, W = cfg.B, cfg.n_comp, cfg.rope_dims, cfg.m, cfg.m_hca, cfg.n_win
+    P = a.page_tokens
+    E, Eh = P // m, P // mh
+    maxp = -(-N // E) + 1                      # the context's pages plus one page of room to grow
+    n_phys = B * maxp
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    table = torch.randperm(n_phys, generator=g).to(torch.int32).reshape(B, maxp).to(dev)
+    pg = api.pages(table, P)
+    cap = maxp * E
+    rows = (table.to(torch.int64)[:, torch.arange(N, device=dev) // E] * E + torch.arange(N, device=dev) % E)
+
+    def pool_of(x, per_row_shape, dtype, ent=E, n=N, rws=None):
+        pool = torch.zeros((n_phys * ent,) + per_row_shape, dtype=dtype, device=dev)
+        if x is not None:
+            pool[(rows if rws is None else rws).reshape(-1)] = x.reshape((B * n,) + per_row_shape)
+        return pool
+
+    kv_pool = pool_of(kv_cache, tuple(kv_cache.shape[2:]), kv_cache.dtype)
+    kv_spool = pool_of(kv_scale, (), torch.float32) if mixed else None
+    for st in sets:   # each set keeps its own copy of the key pool (rotation past the Infinity Cache)
+        st["ik_pool"] = pool_of(st["ik"], tuple(st["ik"].shape[2:]), st["ik"].dtype)
+        st["iks_pool"] = None if st["ik_scale"] is None else pool_of(st["ik_scale"], tuple(st["ik_scale"].shape[2:]),
+                                                                       st["ik_scale"].dtype)
+    hpool = hspool = None
+    if cfg.with_hca:
+        nh = cfg.n_hca
+        hrows = (table.to(torch.int64)[:, torch.arange(nh, device=dev) // Eh] * Eh + torch.arange(nh, device=dev) % Eh)
+        hpool = pool_of(hca_cache, tuple(hca_cache.shape[2:]), hca_cache.dtype, Eh, nh, hrows)
+        hspool = pool_of(hca_scale, (), torch.float32, Eh, nh, hrows) if mixed else None
+    # state rings: the tail tokens' streams (synthetic N(0,1) rows) and the window rows, prepared at their
+    # positions; ring row p % ring holds position p
+    torch.manual_seed(4321)
+    rnd = lambda shape: torch.randn(shape, device=dev).to(torch.bfloat16)
+    kv_r = [rnd((B, 2 * m, cfg.c)) for _ in range(4)]
+    ik_r = [rnd((B, 2 * m, cfg.cI)) for _ in range(4)]
+    hc_r = [rnd((B, mh, cfg.c)) for _ in range(2)] if cfg.with_hca else None
+    p0 = cfg.pos0 - W + 1
+    st0 = sets[0]
+    win_ring = torch.roll(api.prepare_kv(st0["win"], prep, pos_base=pos, pos_first=-(W - 1)), p0 % W, dims=1)
+    hwin_ring = torch.roll(api.prepare_kv(st0["hwin"], prep, pos_base=pos, pos_first=-(W - 1)), p0 % W, dims=1) \
+        if cfg.with_hca else None
+    cache_fmt = "fp8rope" if mixed else None
+    fmt = cfg.idx_dtype
+    for st in sets:   # the step's new token rows: one row of each stream per sequence
+        row = lambda d, k: None if d.get(k) is None else d[k][:, 0].contiguous()
+        c, ci = st["ckv"], st["cik"]
+        st["kv_job"] = dict(ca=row(c, "ca"), cb=row(c, "cb"), za=row(c, "za"), zb=row(c, "zb"), bias_a=c["bias_a"],
+                            bias_b=c["bias_b"], m=m, ring_ca=kv_r[0], ring_cb=kv_r[1], ring_za=kv_r[2],
+                            ring_zb=kv_r[3], out=kv_pool, out_scale=kv_spool, out_fmt=cache_fmt, prep=prep)
+        st["ik_job"] = dict(ca=row(ci, "ca"), cb=row(ci, "cb"), za=row(ci, "za"), zb=row(ci, "zb"),
+                            bias_a=ci["bias_a"], bias_b=ci["bias_b"], m=m, ring_ca=ik_r[0], ring_cb=ik_r[1],
+                            ring_za=ik_r[2], ring_zb=ik_r[3], out=st["ik_pool"], out_scale=st["iks_pool"],
+                            out_fmt=fmt if fmt in ("fp8", "mxfp4") else None)
+        st["win_job"] = dict(row=st["win"][:, W - 1].contiguous(), ring=win_ring, prep=prep)
+        if cfg.with_hca:
+            ch = st["chca"]
+            st["hc_job"] = dict(ca=row(ch, "ca"), za=row(ch, "za"), bias_a=ch["bias_a"], m=mh, ring_ca=hc_r[0],
+                                ring_za=hc_r[1], out=hpool, out_scale=hspool, out_fmt=cache_fmt, prep=prep)
+            st["hwin_job"] = dict(row=st["hwin"][:, W - 1].contiguous(), ring=hwin_ring, prep=prep)
+    hws = None
+    if cfg.with_hca:
+        nb = api._lib.load().hca_attend_workspace_bytes(B, 1, cfg.H, cfg.c, maxp * Eh, W)
+        hws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    bnd = api.bound_keys(B, 1, cap, dev)
+    sc = torch.empty((B, 1, cap), dtype=scores.dtype, device=dev)
+    steps_done = [0]
+
+    def step(st):
+        main_s = torch.cuda.current_stream()
+        if side is not None:
+            side.wait_stream(main_s)
+            with torch.cuda.stream(side):
+                api.decode_append([st["hc_job"]], [st["hwin_job"]], pos, pg, stream=side)
+                api.hca_attend_paged(st["hq"], hpool, hwin_ring, st["hsink"], pos, pg, mh, R, cfg.scale,
+                                     maxp * Eh, cfg.eps, cfg.rope_base, out=hout, ws=hws, stream=side,
+                                     kv_prepared=2, comp_scale=hspool)
+        api.decode_append([st["kv_job"], st["ik_job"]], [st["win_job"]], pos, pg)
+        api.index_paged(st["qi"], st["qi_scale"], st["w"], st["ik_pool"], st["iks_pool"], pg, pos, m, fmt, cap,
+                        scores=sc, bound=bnd)
+        api.topk(sc, pos, m, cfg.k, idx=idx, bound=bnd)
+        api.attend_paged(st["q"], kv_pool, idx, win_ring, st["sink"], pos, pg, m, R, cfg.scale, cap, cfg.eps,
+                         cfg.rope_base, out=out, kv_prepared=2, comp_scale=kv_spool)
+        if side is not None:
+            main_s.wait_stream(side)
+        pos.add_(1)   # the next step decodes the next token
+        steps_done[0] += 1
+
+    def index_only(st):
+        api.index_paged(st["qi"], st["qi_scale"], st["w"], st["ik_pool"], st["iks_pool"], pg, pos, m, fmt, cap,
+                        scores=sc, bound=bnd)
+
+    def visible():
+        return int(min(int(pos[0].item()) // m, cap))
+
+    return step, index_only, visible
 
 
 def source_hash(*names):
@@ -214,7 +320,15 @@ def main():
     # (a cross-stream join inside a HIP graph costs a few microseconds, which only work of this size repays)
     side = torch.cuda.Stream() if cfg.with_hca else None
 
-    def step(st):
+    if a.paged:
+        if prefill:
+            print("--paged runs decode workloads only", file=sys.stderr)
+            sys.exit(2)
+        step, index_only_paged, vis_now = _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data,
+                                                       ik_scale, hca_cache, hca_scale, prep, pos, scores, bound, idx,
+                                                       out, hout, hca_ws, side, mixed)
+
+    def step_contiguous(st):
         main_s = torch.cuda.current_stream()
         if side is not None:
             side.wait_stream(main_s)
@@ -254,6 +368,8 @@ def main():
         if side is not None:
             main_s.wait_stream(side)
 
+    if not a.paged:
+        step = step_contiguous
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -290,6 +406,9 @@ def main():
     # csa_index launch duration: HIP events recorded on the launch stream around back-to-back index
     # launches over the same input rotation, so that the average is the kernel's own time
     def index_only(st):
+        if a.paged:
+            index_only_paged(st)
+            return
         api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
                   bound=bound)
 
@@ -308,13 +427,14 @@ def main():
     # weights read once per query row, one score (float32 or bf16) written per (row, entry)
     row_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt]
     q_bytes = row_bytes * cfg.HI + 4 * cfg.HI
-    idx_bytes = B * (N * row_bytes + T * q_bytes + T * N * scores.element_size())
+    n_read = vis_now() if a.paged else N   # paged: the visible entries of the current positions (all read)
+    idx_bytes = B * (n_read * row_bytes + T * q_bytes + T * scores.shape[2] * scores.element_size())
     # algorithmic FLOPs: 2 HI cI per visible (row, entry) pair
     pairs = sum(min((cfg.pos0 + r) // cfg.m, N) for r in range(T)) * B
     idx_flops = 2 * cfg.HI * cfg.cI * pairs
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
-    if os.path.exists(tpath):
+    if os.path.exists(tpath) and not a.paged:
         t = json.load(open(tpath))
         if t.get("source_hash") == source_hash("index.hip") and t.get("index_scores", "f32") == a.scores:
             traffic = t.get("hbm_bytes_per_launch")
@@ -325,7 +445,7 @@ def main():
                     "algorithmic_flops_per_launch": idx_flops, "avg_launch_ms": idx_ms}
     else:
         achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-        roofline = {"kernel": "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+        roofline = {"kernel": "csa_index_paged" if a.paged else "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms}
     if cfg.name == configs.C3.name:
@@ -352,6 +472,8 @@ def main():
                    "heads": cfg.H,
                    "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
                    "hca_entries": cfg.n_hca if cfg.with_hca else 0, "index_scores": a.scores, "kv_cache": a.kv,
+                   "cache_layout": f"paged ({a.page_tokens}-token pages) + state rings, positions advancing"
+                   if a.paged else "contiguous",
                    "input_sets_rotated": NSETS},
         "roofline": roofline,
         "setup_s": round(t_setup, 1),

@@ -40,6 +40,11 @@ def _dptr(t):
     return t.data_ptr()
 
 
+def _ws_bytes(ws):
+    """The size the library may use: the workspace tensor's own."""
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
@@ -210,7 +215,7 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
     if bound is not None and tuple(bound.shape) != (B, T, lib.csa_index_bound_keys(N)):
         raise CSAError(f"topk: bound shape {tuple(bound.shape)} does not match the scores")
     st = lib.csa_topk(_ptr(scores), FMT[_TORCH_FMT[scores.dtype]], B, T, N, _ptr(pos0), m, k, _ptr(bound),
-                      _ptr(idx), _ptr(vals), _ptr(ws), nb, _stream(stream))
+                      _ptr(idx), _ptr(vals), _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "csa_topk")
     return idx, vals
 
@@ -280,7 +285,7 @@ def attend(q, comp_kv, idx, win_kv, sink, pos0, m, n_win, rope_dims, scale, eps=
     st = lib.csa_attend(_ptr(q), _ptr(comp_kv), _ptr(comp_scale), _ptr(idx), _ptr(win_kv), _ptr(sink), _ptr(gamma_q),
                         _ptr(gamma_kv), B, T, H, c, rope_dims, k, n_win, N, _ptr(pos0), m, scale, eps, rope_base,
                         FMT[kv_fmt], _comp_t(comp_kv, comp_scale, kv_fmt), int(kv_prepared), _ptr(out), FMT[out_fmt],
-                        _ptr(ws), nb, _stream(stream))
+                        _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "csa_attend")
     return out
 
@@ -302,7 +307,7 @@ def hca_attend(q, comp_kv, win_kv, sink, pos0, m_hca, n_win, rope_dims, scale, e
     st = lib.hca_attend(_ptr(q), _ptr(comp_kv), _ptr(comp_scale), _ptr(win_kv), _ptr(sink), _ptr(gamma_q),
                         _ptr(gamma_kv), B, T, H, c, rope_dims, n_win, N, _ptr(pos0), m_hca, scale, eps, rope_base,
                         FMT[kv_fmt], _comp_t(comp_kv, comp_scale, kv_fmt), int(kv_prepared), _ptr(out),
-                        FMT[out_fmt], _ptr(ws), nb, _stream(stream))
+                        FMT[out_fmt], _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "hca_attend")
     return out
 
@@ -384,7 +389,7 @@ def attend_paged(q, comp_pool, idx, win_ring, sink, pos0, pg, m, rope_dims, scal
                               _ptr(sink), _ptr(gamma_q), _ptr(gamma_kv), B, H, c, rope_dims, k, n_win, n_max,
                               _ptr(pos0), m, scale, eps, rope_base, FMT["bf16"],
                               _comp_t(comp_pool, comp_scale, "bf16"), int(kv_prepared), _ptr(out),
-                              FMT[_TORCH_FMT[out.dtype]], _ptr(ws), nb, _stream(stream))
+                              FMT[_TORCH_FMT[out.dtype]], _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "csa_attend_paged")
     return out
 
@@ -406,6 +411,6 @@ def hca_attend_paged(q, comp_pool, win_ring, sink, pos0, pg, m_hca, rope_dims, s
     st = lib.hca_attend_paged(_ptr(q), _ptr(comp_pool), _ptr(comp_scale), C.byref(pg), _ptr(win_ring), _ptr(sink),
                               _ptr(gamma_q), _ptr(gamma_kv), B, H, c, rope_dims, n_win, n_max, _ptr(pos0), m_hca, scale,
                               eps, rope_base, FMT["bf16"], _comp_t(comp_pool, comp_scale, "bf16"), int(kv_prepared),
-                              _ptr(out), FMT[_TORCH_FMT[out.dtype]], _ptr(ws), nb, _stream(stream))
+                              _ptr(out), FMT[_TORCH_FMT[out.dtype]], _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "hca_attend_paged")
     return out

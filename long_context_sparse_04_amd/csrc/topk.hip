@@ -850,6 +850,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
     const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
   CSA_FINISH_LDS(kBoundSegCap, kBoundMaxChunks)
   __shared__ int s_last;
+  __shared__ uint32_t s_nz;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int nch = gridDim.x;
@@ -872,37 +873,50 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
 
   // tau from the bound keys (held in registers when they fit)
   const uint32_t* brow = bound + (int64_t)row * nb;
-  constexpr int kBk = 8;
+  // up to 8,192 keys (a cache of 2^20 entries with one bound set per run) stay in registers; only the
+  // register slots the row's keys fill are loaded (nbi is uniform)
+  constexpr int kBk = 32;
   const bool breg = nb <= kBk * kSplitThreads;  // (uniform)
+  const int nbi = (nb + kSplitThreads - 1) / kSplitThreads;
+  // A zero key stands for "no entry" (runs with fewer than two visible entries, e.g. the tail of a cache
+  // with room to grow): the key range, and so the radix pass's resolution, spans the real keys only, and
+  // the bound is used only when at least K of them exist (else every visible entry is a candidate).
   uint32_t bk[kBk];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nz = 0u;
   if (breg) {
 #pragma unroll
-    for (int i = 0; i < kBk; ++i) {
-      const int j = tid + i * kSplitThreads;
-      bk[i] = brow[min(j, nb - 1)];
-    }
+    for (int i = 0; i < kBk; ++i)
+      if (i < nbi) bk[i] = brow[min(tid + i * kSplitThreads, nb - 1)];
 #pragma unroll
     for (int i = 0; i < kBk; ++i)
-      if (tid + i * kSplitThreads < nb) {
+      if (i < nbi && tid + i * kSplitThreads < nb && bk[i] != 0u) {
         kmin = min(kmin, bk[i]);
         kmax = max(kmax, bk[i]);
+        ++nz;
       }
   } else {
     for (int j = tid; j < nb; j += kSplitThreads) {
       const uint32_t kk = brow[j];
-      kmin = min(kmin, kk);
-      kmax = max(kmax, kk);
+      if (kk != 0u) {
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+        ++nz;
+      }
     }
   }
-  block_minmax<kSplitThreads>(kmin, kmax, s_mm);
-  int known = common_bits(kmin, kmax), need = K;
-  uint32_t tau = kmax;
+  if (tid == 0) s_nz = 0u;
+  __syncthreads();
+  nz = wave_incl_sum(nz);
+  if ((tid & 63) == 63) atomicAdd(&s_nz, nz);
+  block_minmax<kSplitThreads>(kmin, kmax, s_mm);  // (its barriers also order the count)
+  const bool usable = s_nz >= (uint32_t)K;       // (uniform)
+  int known = usable ? common_bits(kmin, kmax) : 32, need = K;
+  uint32_t tau = usable ? kmax : 0u;
   auto each_bound = [&](auto f) {
     if (breg) {
 #pragma unroll
       for (int i = 0; i < kBk; ++i)
-        if (tid + i * kSplitThreads < nb) f(bk[i]);
+        if (i < nbi && tid + i * kSplitThreads < nb) f(bk[i]);
     } else {
       for (int j = tid; j < nb; j += kSplitThreads) f(brow[j]);
     }

@@ -350,6 +350,17 @@ def test_topk_bound_short_cache(api, N, k):
     _topk_case(api, s, pos0, 4, k, f"bound sets, N={N}", "index")
 
 
+def test_topk_bound_cache_with_room(api):
+    """A cache with room to grow (capacity above the visible entries, as a paged cache has): the runs past
+    the visible range carry zero ("none") bound keys, which must not widen the key range of the selection;
+    rows with fewer real keys than k take every visible entry as a candidate."""
+    rng = np.random.default_rng(77)
+    N, k = 262144 + 2048, 1024
+    s = rng.standard_normal((4, 1, N)).astype(np.float32)
+    pos0 = [4 * 262144, 4 * 262144 + 3, 4 * 3000, 4 * (N - 5)]
+    _topk_case(api, s, pos0, 4, k, "bound keys with room to grow", "index")
+
+
 def test_topk_workspace_reused_across_shapes(api):
     """One workspace serves split-path calls of different shapes: a call with more rows must not find the
     previous call's dirty regions where its zero-at-rest histograms live."""
