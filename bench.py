@@ -61,6 +61,9 @@ def parse():
                         "an entry when a block completes), compressed entries live in paged pools behind a shuffled "
                         "block table, and every step advances the positions by one")
     p.add_argument("--page-tokens", type=int, default=1024, help="raw tokens per page (a power of two >= 128)")
+    p.add_argument("--proj", action="store_true",
+                   help="decode: the step also runs the query up-projections from the latent (q and the indexer "
+                        "queries, one launch) before it and the grouped output projection after it")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -192,6 +195,29 @@ def _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data, ik_scale
         return int(min(int(pos[0].item()) // m, cap))
 
     return step, index_only, visible
+
+
+# Pro / Flash projection shapes ("【论文解读】DeepSeek-V4", section 三(二): d_c, g, d_g, d)
+PROJ_SHAPES = {128: dict(d_c=1536, g=16, d_g=1024, d=7168), 64: dict(d_c=1024, g=8, d_g=1024, d=4096)}
+
+
+def _with_projections(cfg, api, torch, step, out, dev):
+    """Wrap a decode step: latent -> (q, q^I) before it, grouped output projection after it."""
+    ps = PROJ_SHAPES[cfg.H]
+    rows = cfg.B * cfg.T
+    x = gen.proj_inputs(rows, ps["d_c"], cfg.H, cfg.c, cfg.HI, cfg.cI, ps["g"], ps["d_g"], ps["d"], seed=3)
+    up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    cq, w_uq, w_iuq, w_g, w_o = (up(x[k]) for k in ("cq", "w_uq", "w_iuq", "w_g", "w_o"))
+    mid = torch.empty((rows, ps["g"] * ps["d_g"]), dtype=torch.bfloat16, device=dev)
+    hid = torch.empty((rows, ps["d"]), dtype=torch.bfloat16, device=dev)
+    fmt = cfg.idx_dtype
+
+    def run(st):
+        api.q_up_proj(cq, w_uq, w_iuq, cfg.H, cfg.c, cfg.HI, cfg.cI, qi_fmt=fmt, q=st["q"], qi=st["qi"],
+                      qi_scale=st["qi_scale"])
+        step(st)
+        api.grouped_out_proj(out.view(rows, cfg.H * cfg.c), w_g, w_o, ps["g"], mid=mid, out=hid)
+    return run
 
 
 def source_hash(*names):
@@ -370,6 +396,11 @@ def main():
 
     if not a.paged:
         step = step_contiguous
+    if a.proj:
+        if prefill:
+            print("--proj runs decode workloads only", file=sys.stderr)
+            sys.exit(2)
+        step = _with_projections(cfg, api, torch, step, out, dev)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -472,6 +503,7 @@ def main():
                    "heads": cfg.H,
                    "head_dim": cfg.c, "indexer": f"{cfg.HI}x{cfg.cI} {fmt}", "top_k": cfg.k, "window": cfg.n_win,
                    "hca_entries": cfg.n_hca if cfg.with_hca else 0, "index_scores": a.scores, "kv_cache": a.kv,
+                   "projections": "q / q^I up-projection + grouped output projection" if a.proj else "none",
                    "cache_layout": f"paged ({a.page_tokens}-token pages) + state rings, positions advancing"
                    if a.paged else "contiguous",
                    "input_sets_rotated": NSETS},

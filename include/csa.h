@@ -425,6 +425,40 @@ csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* c
                             int comp_t, int kv_prepared, void* out, int out_t, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/*
+ * ---- Dense projections on either side of the step (decode rows) ----
+ *
+ * csa_q_up_proj -- the queries from the shared low-rank latent ([CSA] (2), the q^I equation, and (3), the
+ * q equation): q = c^Q W^UQ and q^I = c^Q W^IUQ in one launch that reads c^Q once.
+ *   cq     : bf16 [rows][d_c]
+ *   w_uq   : bf16 [n_h * c][d_c]    (output-major: row j holds output column j's weights)
+ *   w_iuq  : bf16 [n_hI * cI][d_c]
+ *   q      : bf16 [rows][n_h * c]   (the [B][T][H][c] layout of csa_attend's q)
+ *   qi     : in qi_t, the [B][T][HI][cI] layout of csa_index's q: bf16; or CSA_FP8_E4M3_ROWSCALE
+ *            (e4m3 codes, qi_scale float32 [rows][n_hI] = amax/448 of the head's values); or
+ *            CSA_MXFP4_E8M0_B32 (cI/2 bytes per head, qi_scale [rows][n_hI][cI/32] E8M0 bytes)
+ * Accumulation in float32 over d_c; bf16 results rounded to nearest even; quantized q^I is coded from
+ * the float32 sums.  Limits: 1 <= rows <= 32; d_c a multiple of 32; n_h * c and n_hI * cI multiples
+ * of 128; cI = 128 for the quantized forms.  CSA_ERR_NULL for a missing pointer.
+ */
+csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
+                         int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, void* stream);
+
+/*
+ * csa_grouped_out_proj -- the grouped output projection ([CSA] (4); [HCA] (2) uses the same): the n_h
+ * head outputs of a row split into g groups of n_h / g consecutive heads; group i's (n_h / g) * c values
+ * are projected to d_g values, and the g * d_g intermediates to d.
+ *   o    : bf16 [rows][n_h * c]            (csa_attend's out layout)
+ *   w_g  : bf16 [g][d_g][(n_h / g) * c]    (group i's projection, output-major)
+ *   w_o  : bf16 [d][g * d_g]
+ *   mid  : bf16 [rows][g * d_g]            (the intermediates, caller-owned, rounded to bf16)
+ *   out  : bf16 [rows][d]
+ * Two launches (the groups, then the final projection), float32 accumulation.  Limits: 1 <= rows <=
+ * 32; (n_h / g) * c and g * d_g multiples of 32; d_g and d multiples of 16; g divides n_h.
+ */
+csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
+                                int d_g, int d, void* mid, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

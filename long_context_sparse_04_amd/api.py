@@ -414,3 +414,47 @@ def hca_attend_paged(q, comp_pool, win_ring, sink, pos0, pg, m_hca, rope_dims, s
                               _ptr(out), FMT[_TORCH_FMT[out.dtype]], _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "hca_attend_paged")
     return out
+
+
+# ---- dense projections for decode rows ------------------------------------------------------------------------
+
+
+def q_up_proj(cq, w_uq, w_iuq, n_h, c, n_hI, cI, qi_fmt="bf16", q=None, qi=None, qi_scale=None, stream=None):
+    """csa_q_up_proj: cq bf16 [rows][d_c], weights [outputs][d_c].  Returns (q [rows][n_h][c] bf16, q^I in
+    qi_fmt [rows][n_hI][...], its scales or None)."""
+    lib = _lib.load()
+    rows, d_c = cq.shape
+    dev = cq.device
+    if q is None:
+        q = torch.empty((rows, n_h, c), dtype=torch.bfloat16, device=dev)
+    if qi is None:
+        if qi_fmt == "bf16":
+            qi = torch.empty((rows, n_hI, cI), dtype=torch.bfloat16, device=dev)
+        elif qi_fmt == "fp8":
+            qi = torch.empty((rows, n_hI, cI), dtype=torch.uint8, device=dev)
+            qi_scale = torch.empty((rows, n_hI), dtype=torch.float32, device=dev) if qi_scale is None else qi_scale
+        else:
+            qi = torch.empty((rows, n_hI, cI // 2), dtype=torch.uint8, device=dev)
+            qi_scale = torch.empty((rows, n_hI, cI // 32), dtype=torch.uint8, device=dev) if qi_scale is None \
+                else qi_scale
+    st = lib.csa_q_up_proj(_ptr(cq), _ptr(w_uq), _ptr(w_iuq), rows, d_c, n_h, c, n_hI, cI, _ptr(q), _ptr(qi),
+                           _ptr(qi_scale), FMT[qi_fmt], _stream(stream))
+    _lib.check(st, "csa_q_up_proj")
+    return q, qi, qi_scale
+
+
+def grouped_out_proj(o, w_g, w_o, g, mid=None, out=None, stream=None):
+    """csa_grouped_out_proj: o bf16 [rows][n_h * c] (or [rows][n_h][c]), w_g [g][d_g][n_h c / g], w_o [d][g d_g].
+    Returns (out [rows][d], mid [rows][g d_g])."""
+    lib = _lib.load()
+    rows = o.shape[0]
+    n_h, c = (o.shape[1], o.shape[2]) if o.dim() == 3 else (g, o.shape[1] // g)
+    d_g, d = w_g.shape[1], w_o.shape[0]
+    if mid is None:
+        mid = torch.empty((rows, g * d_g), dtype=torch.bfloat16, device=o.device)
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=o.device)
+    st = lib.csa_grouped_out_proj(_ptr(o), _ptr(w_g), _ptr(w_o), rows, n_h, c, g, d_g, d, _ptr(mid), _ptr(out),
+                                  _stream(stream))
+    _lib.check(st, "csa_grouped_out_proj")
+    return out, mid

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
-SOURCES = ["csa_abi.hip", "compress.hip", "index.hip", "topk.hip", "attend.hip"]
+SOURCES = ["csa_abi.hip", "compress.hip", "index.hip", "topk.hip", "attend.hip", "proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -71,3 +71,9 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const flo
                          int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
                          float scale, float eps, float rope_base, int kv_t, int kv_prepared, void* out, int out_t,
                          void* ws, hipStream_t stream);
+
+// dense projections for decode rows (validated)
+csa_status launch_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
+                            int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, hipStream_t stream);
+csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
+                                   int d_g, int d, void* mid, void* out, hipStream_t stream);

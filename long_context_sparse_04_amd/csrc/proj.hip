@@ -1,0 +1,275 @@
+// Dense projections on either side of the attention step, for decode rows (at most 32 per call).
+//
+// "【论文解读】DeepSeek-V4" (wkq9411.github.io), section 一(三)1(2)-(3): q = c^Q W^UQ and q^I = c^Q W^IUQ from
+// one shared latent c^Q; section 一(三)1(4): the grouped output projection (g groups of n_h / g heads, each
+// projected to d_g, then the g d_g intermediates projected to d).
+//
+// Design: with a handful of rows the product is a stream over the weights (every weight byte is read
+// once, the rows stay in L2), so the kernel is HBM-bound and runs bf16 MFMA only because it is free:
+// C[z][m][n] = sum_k A[z][m][k] W[z][n][k], weights output-major (row n of W holds output n's weights,
+// K contiguous).  Lane l of a wave feeds row / column l % 16 and k-group l / 16 of a 16x16x32 MFMA, so
+// one 16-byte load per lane brings a 16-column x 32-k weight tile.  A workgroup's 4 waves either take
+// different column tiles over the whole K (the fused query launch: 128 columns, one indexer head, per
+// workgroup) or share 16 columns and split K four ways, summed in LDS in a fixed order (the output
+// projection: enough workgroups to keep every CU streaming).
+#include "csa_common.h"
+#include "csa_internal.h"
+
+namespace {
+
+constexpr int kProjThreads = 256;
+constexpr int kUnroll = 4;  // k-steps whose loads are in flight together
+
+enum ProjEpi { kEpiBf16 = 0, kEpiFp8Head = 1, kEpiMxfp4 = 2 };
+
+// One column segment of a launch: its weights, output and epilogue.  A launch has one or two segments
+// (the fused query launch: W^UQ -> q, W^IUQ -> q^I) over the same rows and K.
+struct ProjSeg {
+  const uint16_t* w;   // [Z][N][K] bf16
+  int64_t w_zstride;   // elements per batch
+  int n;               // columns per batch
+  void* c;             // output rows (row stride ldc elements; bytes for the quantized forms)
+  int64_t ldc;
+  int64_t c_zoff;      // column offset of batch z in the output row
+  void* scale;         // fp8: float [rows][n / 128]; MXFP4: bytes [rows][n / 32]
+  int epi;
+  int blocks;          // workgroups of this segment along x
+};
+struct ProjArgs {
+  const uint16_t* a;   // [rows][lda] bf16, batch z's K values start at column z * a_zoff
+  int64_t lda, a_zoff;
+  int rows, k;
+  ProjSeg seg[2];
+};
+
+// MT: 16-row tiles of A (rows <= 16 * MT); TPW: column tiles per wave; KS: waves sharing a column group
+template <int MT, int TPW, int KS>
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
+  constexpr int kGroups = 4 / KS;               // column groups per workgroup
+  constexpr int kCols = 16 * TPW * kGroups;     // columns per workgroup
+  __shared__ f32x4 s_red[KS > 1 ? (KS - 1) * 64 * MT * TPW : 1];
+  __shared__ float s_amax[4][32];               // fp8 epilogue: per wave, per row
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int z = blockIdx.y;
+  const bool s1 = (int)blockIdx.x >= p.seg[0].blocks;  // (uniform)
+  const ProjSeg sg = s1 ? p.seg[1] : p.seg[0];
+  const int bx = s1 ? (int)blockIdx.x - p.seg[0].blocks : (int)blockIdx.x;
+  const int grp = wave / KS, ks = wave % KS;
+  const int n0 = bx * kCols + grp * 16 * TPW;   // first column of this wave's tiles
+  const int kg = lane >> 4, li = lane & 15;
+  const int nsteps = p.k / 32;
+
+  const uint16_t* wz = sg.w + (int64_t)z * sg.w_zstride;
+  const uint16_t* az = p.a + (int64_t)z * p.a_zoff;
+  const uint16_t* wrow[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) wrow[t] = wz + (int64_t)(n0 + 16 * t + li) * p.k + 8 * kg;
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) arow[mt] = az + (int64_t)min(16 * mt + li, p.rows - 1) * p.lda + 8 * kg;
+
+  f32x4 acc[MT][TPW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // two register batches of kUnroll k-steps: the next batch's loads go out before this batch's MFMAs, so
+  // 2 * kUnroll k-steps of weights are in flight per wave
+  bf16x8 wA[kUnroll][TPW], aA[kUnroll][MT], wB[kUnroll][TPW], aB[kUnroll][MT];
+  auto load_batch = [&](int s0, bf16x8 (&wf)[kUnroll][TPW], bf16x8 (&af)[kUnroll][MT]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + u * KS;
+      if (s < nsteps) {  // (uniform)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          wf[u][t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
+                                                    reinterpret_cast<const u32x4*>(wrow[t] + 32 * s)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          af[u][mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow[mt] + 32 * s));
+      }
+    }
+  };
+  auto mfma_batch = [&](int s0, const bf16x8 (&wf)[kUnroll][TPW], const bf16x8 (&af)[kUnroll][MT]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (s0 + u * KS < nsteps) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mt], wf[u][t], acc[mt][t], 0, 0, 0);
+      }
+    }
+  };
+  constexpr int kBatch = KS * kUnroll;  // k-steps between a wave's batches
+  if (ks < nsteps) {
+    load_batch(ks, wA, aA);
+    for (int s0 = ks;; s0 += 2 * kBatch) {
+      const int s1 = s0 + kBatch;
+      if (s1 < nsteps) load_batch(s1, wB, aB);
+      mfma_batch(s0, wA, aA);
+      if (s1 >= nsteps) break;
+      if (s1 + kBatch < nsteps) load_batch(s1 + kBatch, wA, aA);
+      mfma_batch(s1, wB, aB);
+      if (s1 + kBatch >= nsteps) break;
+    }
+  }
+
+  if constexpr (KS > 1) {  // the K-split partial sums, added in wave order
+    if (ks > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) s_red[(((ks - 1) * MT + mt) * TPW + t) * 64 + lane] = acc[mt][t];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int q = 1; q < KS; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const f32x4 o = s_red[(((q - 1) * MT + mt) * TPW + t) * 64 + lane];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mt][t][v] += o[v];
+        }
+  }
+
+  // lane l holds column n0 + 16 t + l % 16 of rows 16 mt + 4 (l / 16) + v
+  const int64_t coff = (int64_t)z * sg.c_zoff;
+  if (sg.epi == kEpiBf16) {
+    uint16_t* c = static_cast<uint16_t*>(sg.c);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 16 * mt + 4 * kg + v;
+        if (m < p.rows) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            c[(int64_t)m * sg.ldc + coff + n0 + 16 * t + li] =
+                (uint16_t)(pack_bf16x2(acc[mt][t][v], 0.0f) & 0xFFFFu);
+        }
+      }
+    return;
+  }
+  if (sg.epi == kEpiFp8Head) {  // one head = this workgroup's 128 columns (KS == 1): amax per row
+    uint8_t* c = static_cast<uint8_t*>(sg.c);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float am = 0.0f;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) am = fmaxf(am, fabsf(acc[mt][t][v]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        if (li == 0) s_amax[wave][16 * mt + 4 * kg + v] = am;
+      }
+    }
+    __syncthreads();
+    const int head = (bx * kCols) / 128;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 16 * mt + 4 * kg + v;
+        const float am = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+        const float scale = am / 448.0f;
+        if (r < p.rows) {
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            c[(int64_t)r * sg.ldc + n0 + 16 * t + li] =
+                (uint8_t)f32_to_e4m3(scale > 0.0f ? acc[mt][t][v] / scale : 0.0f);
+          if (wave == 0 && li == 0) static_cast<float*>(sg.scale)[(int64_t)r * (sg.n / 128) + head] = scale;
+        }
+      }
+    return;
+  }
+  // MXFP4: a wave's 32 columns (TPW == 2) are one block: E8M0 scale floor(log2 amax) - 2, e2m1 codes,
+  // element 2i in the low nibble
+  uint8_t* c = static_cast<uint8_t*>(sg.c);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 16 * mt + 4 * kg + v;
+      float am = fmaxf(fabsf(acc[mt][0][v]), fabsf(acc[mt][TPW - 1][v]));
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+      int X = -127;
+      if (am > 0.0f) {
+        int ex;
+        frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
+        X = ex - 1 - 2;
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const uint32_t code = f32_to_e2m1(ldexpf(acc[mt][t][v], -X));
+        const uint32_t up = __shfl_xor(code, 1, 64);  // the odd column's code, to the even lane
+        if (r < p.rows && (li & 1) == 0)
+          c[(int64_t)r * sg.ldc + (n0 + 16 * t + li) / 2] = (uint8_t)(code | (up << 4));
+      }
+      if (r < p.rows && li == 0) static_cast<uint8_t*>(sg.scale)[(int64_t)r * (sg.n / 32) + n0 / 32] = (uint8_t)(X + 127);
+    }
+}
+
+template <int TPW, int KS>
+csa_status launch_proj(const ProjArgs& p, int z, hipStream_t stream) {
+  dim3 grid(p.seg[0].blocks + p.seg[1].blocks, z);
+  if (p.rows <= 16)
+    hipLaunchKernelGGL((proj_kernel<1, TPW, KS>), grid, dim3(kProjThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((proj_kernel<2, TPW, KS>), grid, dim3(kProjThreads), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+csa_status launch_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
+                            int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, hipStream_t stream) {
+  ProjArgs p;
+  p.a = static_cast<const uint16_t*>(cq);
+  p.lda = d_c;
+  p.a_zoff = 0;
+  p.rows = rows;
+  p.k = d_c;
+  const int nq = n_h * c, ni = n_hI * cI;
+  p.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_uq), 0, nq, q, nq, 0, nullptr, kEpiBf16, nq / 128};
+  const int epi = qi_t == CSA_FP8_E4M3_ROWSCALE ? kEpiFp8Head : (qi_t == CSA_MXFP4_E8M0_B32 ? kEpiMxfp4 : kEpiBf16);
+  const int64_t ldi = qi_t == CSA_MXFP4_E8M0_B32 ? ni / 2 : ni;  // bytes for the quantized forms
+  p.seg[1] = ProjSeg{static_cast<const uint16_t*>(w_iuq), 0, ni, qi, ldi, 0, qi_scale, epi, ni / 128};
+  return launch_proj<2, 1>(p, 1, stream);
+}
+
+csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
+                                   int d_g, int d, void* mid, void* out, hipStream_t stream) {
+  const int per = n_h * c / g;
+  ProjArgs p1;
+  p1.a = static_cast<const uint16_t*>(o);
+  p1.lda = (int64_t)n_h * c;
+  p1.a_zoff = per;
+  p1.rows = rows;
+  p1.k = per;
+  p1.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_g), (int64_t)d_g * per, d_g, mid, (int64_t)g * d_g, d_g, nullptr,
+                      kEpiBf16, d_g / 16};
+  p1.seg[1] = ProjSeg{nullptr, 0, 0, nullptr, 0, 0, nullptr, kEpiBf16, 0};
+  csa_status st = launch_proj<1, 4>(p1, g, stream);
+  if (st != CSA_OK) return st;
+  ProjArgs p2;
+  p2.a = static_cast<const uint16_t*>(mid);
+  p2.lda = (int64_t)g * d_g;
+  p2.a_zoff = 0;
+  p2.rows = rows;
+  p2.k = g * d_g;
+  p2.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_o), 0, d, out, d, 0, nullptr, kEpiBf16, d / 16};
+  p2.seg[1] = ProjSeg{nullptr, 0, 0, nullptr, 0, 0, nullptr, kEpiBf16, 0};
+  return launch_proj<1, 4>(p2, 1, stream);
+}

@@ -30,6 +30,7 @@ STREAMS = (
     "hca_c", "hca_z", "hca_bias", "hca_cache", "hca_q", "hca_win", "hca_sink",
     "extra0", "extra1", "extra2", "extra3",
     "dq", "dqi", "dw", "dhq",
+    "cq", "w_uq", "w_iuq", "att_o", "w_g", "w_o",
 )
 _SID = {name: i for i, name in enumerate(STREAMS)}
 
@@ -193,3 +194,15 @@ def decode_queries(cfg: CSAConfig, steps: int, b: int):
     qi = store(normal(cfg.seed, "dqi", (steps, cfg.HI, cfg.cI), b=b, scale=1.0 / np.sqrt(cfg.cI)), cfg.idx_dtype)
     w = uniform(cfg.seed, "dw", (steps, cfg.HI), b=b)
     return {"q": q, "hq": hq, "qi": qi, "w": w}
+
+
+def proj_inputs(rows: int, d_c: int, n_h: int, c: int, n_hI: int, cI: int, g: int, d_g: int, d: int, seed: int = 0):
+    """Synthetic inputs of the projections, bf16 bits: the latent c^Q [rows][d_c] and attention outputs
+    [rows][n_h * c] ~ N(0, 1); output-major weights W^UQ [n_h c][d_c], W^IUQ [n_hI cI][d_c], the group
+    projections [g][d_g][n_h c / g] and the final one [d][g d_g], each ~ N(0, 1) / sqrt(fan-in), so that
+    every output is O(1)."""
+    w = lambda name, shape, fan_in: store(normal(seed, name, shape, scale=1.0 / np.sqrt(fan_in)), "bf16")["data"]
+    return {"cq": store(normal(seed, "cq", (rows, d_c)), "bf16")["data"],
+            "w_uq": w("w_uq", (n_h * c, d_c), d_c), "w_iuq": w("w_iuq", (n_hI * cI, d_c), d_c),
+            "o": store(normal(seed, "att_o", (rows, n_h * c)), "bf16")["data"],
+            "w_g": w("w_g", (g, d_g, n_h * c // g), n_h * c // g), "w_o": w("w_o", (d, g * d_g), g * d_g)}

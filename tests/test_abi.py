@@ -255,3 +255,26 @@ def test_paged_index_attend_validation(lib):
 
     assert hca(n_max=33) == 2                                     # 4 pages x 8 HCA entries
     assert hca(m_hca=2048) == 2
+
+
+def test_projection_validation(lib):
+    f = lib.csa_q_up_proj
+    ok = lambda **kw: dict(dict(rows=4, d_c=1536, n_h=16, c=512, n_hI=64, cI=128, qi_t=2), **kw)
+
+    def q(**kw):
+        a = ok(**kw)
+        return f(DUMMY, DUMMY, DUMMY, a["rows"], a["d_c"], a["n_h"], a["c"], a["n_hI"], a["cI"], DUMMY, DUMMY,
+                 DUMMY, a["qi_t"], None)
+
+    assert q(rows=0) == 0
+    assert q(rows=33) == 3                      # decode rows only
+    assert q(d_c=1000) == 2                     # d_c a multiple of 32
+    assert q(cI=64) == 3                        # quantized indexer queries: heads of 128
+    assert q(qi_t=0) == 3
+    assert f(DUMMY, None, DUMMY, 4, 1536, 16, 512, 64, 128, DUMMY, DUMMY, DUMMY, 1, None) == 1
+    assert f(DUMMY, DUMMY, DUMMY, 4, 1536, 16, 512, 64, 128, DUMMY, DUMMY, None, 2, None) == 1   # fp8 scales
+    g = lib.csa_grouped_out_proj
+    assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 12, 1024, 7168, DUMMY, DUMMY, None) == 2    # g must divide n_h
+    assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1000, 7168, DUMMY, DUMMY, None) == 3    # d_g % 16
+    assert g(DUMMY, DUMMY, DUMMY, 40, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 3
+    assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1024, 7168, None, DUMMY, None) == 1
