@@ -840,8 +840,8 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 
 // With bound keys from the indexer (two per 256-entry run, each the key of a distinct visible entry),
 // one launch does the whole selection.  Every workgroup derives tau, the K-th largest bound key with
-// the bits below one radix pass cleared (the pass takes the 11 bits right under the bits all bound
-// keys share), and compacts its chunk's keys >= tau into its segment, in index order; tau never
+// the bits below its radix passes cleared (each pass takes the next 11 bits, starting right under the
+// bits all bound keys share, until 22 bits are resolved), and compacts its chunk's keys >= tau into its segment, in index order; tau never
 // exceeds the row's K-th largest key, so every selected key is a candidate (typically about 1.1 k
 // keys are).  The workgroup then publishes its segment and count and adds itself to the row's arrival
 // count; the row's last one to arrive reads the others' segments, finishes the row and resets the count.
@@ -921,7 +921,9 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
       for (int j = tid; j < nb; j += kSplitThreads) f(brow[j]);
     }
   };
-  if (known < 32) radix_step<kSplitThreads>(each_bound, tau, known, need, s_hist, s_w, s_sel);
+  // radix passes until tau carries at least 22 resolved bits: one pass after a long common prefix, a second
+  // when a low outlier key (a run of all-zero scores, say) leaves only the sign or exponent in common
+  while (known < 22) radix_step<kSplitThreads>(each_bound, tau, known, need, s_hist, s_w, s_sel);
   const uint32_t pmask = known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
   tau &= pmask;
 

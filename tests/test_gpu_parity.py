@@ -357,6 +357,9 @@ def test_topk_bound_cache_with_room(api):
     rng = np.random.default_rng(77)
     N, k = 262144 + 2048, 1024
     s = rng.standard_normal((4, 1, N)).astype(np.float32)
+    s[3, 0, 262144:263000] = 0.0          # visible runs of zero scores (empty pages' keys): a low outlier bound
+    s[0, 0] = np.abs(s[0, 0]) + 1.0       # all-positive scores with a zero run: only the sign bit in common
+    s[0, 0, 1024:1280] = 0.0
     pos0 = [4 * 262144, 4 * 262144 + 3, 4 * 3000, 4 * (N - 5)]
     _topk_case(api, s, pos0, 4, k, "bound keys with room to grow", "index")
 
