@@ -845,6 +845,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 // exceeds the row's K-th largest key, so every selected key is a candidate (typically about 1.1 k
 // keys are).  The workgroup then publishes its segment and count and adds itself to the row's arrival
 // count; the row's last one to arrive reads the others' segments, finishes the row and resets the count.
+template <int KBK>
 __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
     const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
@@ -873,11 +874,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
 
   // tau from the bound keys (held in registers when they fit)
   const uint32_t* brow = bound + (int64_t)row * nb;
-  // up to 8,192 keys (a cache of 2^20 entries with one bound set per run) stay in registers; only the
-  // register slots the row's keys fill are loaded (nbi is uniform)
-  constexpr int kBk = 32;
+  // up to KBK * 256 keys stay in registers (8: caches up to 2^18 entries with one bound set per run; 16:
+  // up to 2^19), the register count chosen by the launch so that the common case keeps its occupancy
+  constexpr int kBk = KBK;
   const bool breg = nb <= kBk * kSplitThreads;  // (uniform)
-  const int nbi = (nb + kSplitThreads - 1) / kSplitThreads;
+  constexpr int nbi = kBk;
   // A zero key stands for "no entry" (runs with fewer than two visible entries, e.g. the tail of a cache
   // with room to grow): the key range, and so the radix pass's resolution, spans the real keys only, and
   // the bound is used only when at least K of them exist (else every visible entry is a candidate).
@@ -973,8 +974,13 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
     // bound keys help only when there are enough of them (a K-th largest well inside their range)
     const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k && nch <= kBoundMaxChunks;
     if (bounded) {
-      hipLaunchKernelGGL(topk_bound_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0, m,
-                         k, bound, (int)index_bound_keys(n_max), idx, vals, s);
+      const int nb = (int)index_bound_keys(n_max);
+      if (nb <= 8 * kSplitThreads)
+        hipLaunchKernelGGL((topk_bound_kernel<8>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
+                           pos0, m, k, bound, nb, idx, vals, s);
+      else
+        hipLaunchKernelGGL((topk_bound_kernel<16>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
+                           pos0, m, k, bound, nb, idx, vals, s);
     } else {
       hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
                          m, k, s);
