@@ -176,9 +176,9 @@ def _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data, ik_scale
                 api.hca_attend_paged(st["hq"], hpool, hwin_ring, st["hsink"], pos, pg, mh, R, cfg.scale,
                                      maxp * Eh, cfg.eps, cfg.rope_base, out=hout, ws=hws, stream=side,
                                      kv_prepared=2, comp_scale=hspool)
-        api.decode_append([st["kv_job"], st["ik_job"]], [st["win_job"]], pos, pg)
-        api.index_paged(st["qi"], st["qi_scale"], st["w"], st["ik_pool"], st["iks_pool"], pg, pos, m, fmt, cap,
-                        scores=sc, bound=bnd)
+        # the token's append (rings, window, the entry a block completes) inside the paged index launch
+        api.append_index_paged([st["kv_job"], st["ik_job"]], st["win_job"], st["qi"], st["qi_scale"], st["w"],
+                               st["ik_pool"], st["iks_pool"], pg, pos, m, fmt, cap, scores=sc, bound=bnd)
         api.topk(sc, pos, m, cfg.k, idx=idx, bound=bnd)
         api.attend_paged(st["q"], kv_pool, idx, win_ring, st["sink"], pos, pg, m, R, cfg.scale, cap, cfg.eps,
                          cfg.rope_base, out=out, kv_prepared=2, comp_scale=kv_spool)

@@ -405,6 +405,18 @@ csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, c
                            void* stream);
 
 /*
+ * csa_append_index_paged -- csa_decode_append (jobs[0]: the KV entry, jobs[1]: the indexer key, whose
+ * out / out_scale / out_t must be k_pool / k_scale_pool / qk_t; win: NULL or the window ring) and
+ * csa_index_paged for the same tokens, in one launch: the workgroup whose entries hold the new key
+ * compresses it before it reads any key, workgroup 0 of each sequence does the rest of the append.
+ * Results equal the two calls made in turn.  Limits: those of both calls, m < 64, widths <= 1024.
+ */
+csa_status csa_append_index_paged(const csa_append_job* jobs, const csa_window_job* win, int in_t, const void* q,
+                                  const void* q_scale, const float* w, const void* k_pool, const void* k_scale_pool,
+                                  const csa_pages* pages, int B, int HI, int cI, int64_t n_max, const int64_t* pos0,
+                                  int m, int qk_t, void* scores, int score_t, uint32_t* bound, void* stream);
+
+/*
  * csa_attend_paged / hca_attend_paged -- csa_attend / hca_attend for decode rows (T = 1) whose
  * compressed entries sit in a paged pool (comp_pool, comp_scale_pool; ratio m, resp. m_hca) and
  * whose window rows sit in a state ring win_ring [B][n_win][c] (position p at row p % n_win: the

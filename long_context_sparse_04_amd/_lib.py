@@ -68,6 +68,8 @@ SIGNATURES = {
     "csa_q_up_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P]),
     "csa_grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "csa_decode_append": (_I, [C.POINTER(AppendJob), _I, C.POINTER(WindowJob), _I, _I, _P, _PG, _I, _P]),
+    "csa_append_index_paged": (_I, [C.POINTER(AppendJob), C.POINTER(WindowJob), _I, _P, _P, _P, _P, _P, _PG, _I,
+                                    _I, _I, _I64, _P, _I, _I, _P, _I, _P, _P]),
     "csa_index_paged": (_I, [_P, _P, _P, _P, _P, _PG, _I, _I, _I, _I64, _P, _I, _I, _P, _I, _P, _P]),
     "csa_attend_paged": (_I, [_P, _P, _P, _PG, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F,
                               _I, _I, _I, _P, _I, _P, _SZ, _P]),

@@ -352,6 +352,45 @@ def decode_append(jobs, wins, pos, pg, stream=None):
     _lib.check(st, "csa_decode_append")
 
 
+def _append_structs(jobs, wins, in_fmt):
+    keep = []
+    jarr = (_lib.AppendJob * max(1, len(jobs)))()
+    for i, j in enumerate(jobs):
+        prep = j.get("prep")
+        keep.append(prep)
+        jarr[i] = _lib.AppendJob(_ptr(j["ca"]), _ptr(j.get("cb")), _ptr(j["za"]), _ptr(j.get("zb")), _ptr(j["bias_a"]),
+                                 _ptr(j.get("bias_b")), j["ca"].shape[1], j["m"], _ptr(j["ring_ca"]),
+                                 _ptr(j.get("ring_cb")), _ptr(j["ring_za"]), _ptr(j.get("ring_zb")), _dptr(j["out"]),
+                                 _dptr(j.get("out_scale")), FMT[j.get("out_fmt") or in_fmt],
+                                 None if prep is None else C.pointer(prep))
+    warr = (_lib.WindowJob * max(1, len(wins)))()
+    for i, w in enumerate(wins):
+        prep = w.get("prep")
+        keep.append(prep)
+        warr[i] = _lib.WindowJob(_ptr(w["row"]), _ptr(w["ring"]), w["ring"].shape[2], w["ring"].shape[1],
+                                 None if prep is None else C.pointer(prep))
+    return jarr, warr, keep
+
+
+def append_index_paged(jobs, win, q, q_scale, w, k_pool, k_scale_pool, pg, pos0, m, fmt, n_max, scores=None,
+                       bound=None, score_fmt="f32", stream=None):
+    """csa_append_index_paged: decode_append(jobs = [KV job, indexer-key job into k_pool], [win]) and index_paged
+    in one launch.  Returns the scores."""
+    lib = _lib.load()
+    B, HI = q.shape[0], q.shape[2]
+    cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
+    in_fmt = _TORCH_FMT[jobs[0]["ca"].dtype]
+    jarr, warr, keep = _append_structs(jobs, [win] if win is not None else [], in_fmt)
+    if scores is None:
+        scores = _score_buf(B, 1, n_max, score_fmt, q.device)
+    st = lib.csa_append_index_paged(jarr, warr if win is not None else None, FMT[in_fmt], _ptr(q), _ptr(q_scale),
+                                    _ptr(w), _ptr(k_pool), _ptr(k_scale_pool), C.byref(pg), B, HI, cI, n_max,
+                                    _ptr(pos0), m, FMT[fmt], _ptr(scores), FMT[_TORCH_FMT[scores.dtype]], _ptr(bound),
+                                    _stream(stream))
+    _lib.check(st, "csa_append_index_paged")
+    return scores
+
+
 def index_paged(q, q_scale, w, k_pool, k_scale_pool, pg, pos0, m, fmt, n_max, scores=None, bound=None,
                 score_fmt="f32", stream=None):
     """csa_index_paged: decode rows (q [B][1][HI][row]) over the paged key pool; scores [B][1][n_max]."""

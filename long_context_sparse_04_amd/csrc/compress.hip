@@ -268,3 +268,43 @@ csa_status launch_decode_append(const csa_append_job* jobs, int njobs, const csa
   }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
+
+void csa_compress_body::fill_append(const csa_append_job* jobs, const csa_window_job* win, const csa_pages* pages,
+                                    int in_t, AppendFuse& af) {
+  CompressJob cj[2];
+  for (int i = 0; i < 2; ++i) {
+    const csa_append_job& jb = jobs[i];
+    const bool overlap = jb.cb != nullptr;
+    cj[i] = CompressJob{jb.ring_ca, overlap ? jb.ring_cb : nullptr, jb.ring_za, overlap ? jb.ring_zb : nullptr,
+                        jb.bias_a, overlap ? jb.bias_b : nullptr, jb.c, jb.out, jb.out_scale, jb.out_t, 0, jb.prep};
+  }
+  fill_jobs(cj, 2, af.jobs);
+  for (int i = 0; i < 2; ++i) {
+    const csa_append_job& jb = jobs[i];
+    const bool overlap = jb.cb != nullptr;
+    Job& J = af.jobs.j[i];
+    J.ring = overlap ? 2 * jb.m : jb.m;
+    J.table = pages->block_table;
+    J.tstride = pages->max_pages;
+    int plog2 = 0;
+    while ((1 << plog2) < pages->page_tokens / jb.m) ++plog2;
+    J.plog2 = plog2;
+    af.src[i][0] = jb.ca;
+    af.src[i][1] = overlap ? jb.cb : nullptr;
+    af.src[i][2] = jb.za;
+    af.src[i][3] = overlap ? jb.zb : nullptr;
+  }
+  af.m = jobs[0].m;
+  af.in_t = in_t;
+  af.win_row = win ? win->row : nullptr;
+  af.win_ring = win ? win->ring : nullptr;
+  af.win_c = win ? win->c : 0;
+  af.win_n = win ? win->n_win : 1;
+  const csa_kv_prep* pp = win ? win->prep : nullptr;
+  af.win_prep = pp ? 1 : 0;
+  af.win_gamma = pp ? pp->gamma : nullptr;
+  af.win_eps = pp ? pp->eps : 0.0f;
+  af.win_R = pp ? pp->rope_dims : 0;
+  const RopeTable rt = make_rope_table(pp ? pp->rope_dims : 0, pp ? pp->rope_base : 1.0f);
+  for (int q = 0; q < 64; ++q) af.win_theta[q] = rt.theta[q];
+}

@@ -233,7 +233,71 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
 }
 
 
+// A decode token's state-cache work (csa_decode_append) carried by another launch: the KV entry and the
+// indexer key (rings in Job::ring, paged outputs in Job::table), the token's ring rows, the window row.
+struct AppendFuse {
+  Jobs jobs;               // j[0]: the KV entry, j[1]: the indexer key
+  const void* src[2][4];   // the token's rows of each job: ca, cb, za, zb ([B][c])
+  int m, in_t;
+  const void* win_row;     // the window job (win_ring NULL: none)
+  void* win_ring;
+  int win_c, win_n, win_prep;
+  const float* win_gamma;
+  float win_eps;
+  int win_R;
+  double win_theta[64];
+};
+
+// The token's rows of a job into ring row t % ring (every thread of the block takes part).
+template <typename TIn>
+CSA_DEV void store_ring_rows(const Job& jb, const void* const* src, int b, int64_t t) {
+  const int64_t rrow = ((int64_t)b * jb.ring + t % jb.ring) * jb.c;
+  const void* dst[4] = {jb.ca, jb.cb, jb.za, jb.zb};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (!dst[s]) continue;
+    const TIn* from = static_cast<const TIn*>(src[s]) + (int64_t)b * jb.c;
+    TIn* to = static_cast<TIn*>(const_cast<void*>(dst[s])) + rrow;
+    for (int q = threadIdx.x; q < jb.c / 4; q += blockDim.x) {
+      if constexpr (sizeof(TIn) == 4)
+        reinterpret_cast<f32x4*>(to)[q] = reinterpret_cast<const f32x4*>(from)[q];
+      else
+        reinterpret_cast<uint2*>(to)[q] = reinterpret_cast<const uint2*>(from)[q];
+    }
+  }
+}
+
+// The token's window row into ring row t % n_win, prepared at position t when asked (every thread of the
+// NT-thread block calls it: it holds barriers).  s_red: NT / 64 floats.
+template <typename TIn, int NT>
+CSA_DEV void store_window_row(const AppendFuse& a, int b, int64_t t, float* s_red) {
+  const int c = a.win_c;
+  const int cg = threadIdx.x;
+  const bool holder = cg < c / 4;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  if (holder) {
+    Raw4<TIn> v;
+    v.load(static_cast<const TIn*>(a.win_row) + (int64_t)b * c + 4 * cg);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = v.get(q);
+  }
+  if (a.win_prep) prep_row4<NT>(y, holder, cg, c, (double)t, a.win_gamma, a.win_eps, a.win_R, a.win_theta, s_red);
+  if (!holder) return;
+  TIn* out = static_cast<TIn*>(a.win_ring) + ((int64_t)b * a.win_n + t % a.win_n) * c + 4 * cg;
+  if constexpr (sizeof(TIn) == 4) {
+    *reinterpret_cast<f32x4*>(out) = f32x4{y[0], y[1], y[2], y[3]};
+  } else {
+    uint2 o;
+    o.x = pack_bf16x2(y[0], y[1]);
+    o.y = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<uint2*>(out) = o;
+  }
+}
+
 // host: device-side job descriptions (and RoPE tables) of up to two compression problems
 void fill_jobs(const CompressJob* jobs, int njobs, Jobs& js);
+// host: an AppendFuse from csa_decode_append's two compression jobs and optional window job
+void fill_append(const csa_append_job* jobs, const csa_window_job* win, const csa_pages* pages, int in_t,
+                 AppendFuse& af);
 
 }  // namespace csa_compress_body

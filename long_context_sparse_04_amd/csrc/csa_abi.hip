@@ -327,8 +327,11 @@ csa_status check_prep(const csa_kv_prep* prep, int c) {
 
 extern "C" {
 
-csa_status csa_decode_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
-                             const int64_t* pos, const csa_pages* pages, int in_t, void* stream) {
+}  // extern "C"
+
+namespace {
+csa_status check_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
+                        const csa_pages* pages, int in_t) {
   if (njobs < 1 || njobs > 2 || nwins < 0 || nwins > 2 || B < 0) return CSA_ERR_SHAPE;
   if (in_t != CSA_F32 && in_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
   if (B >= 65536) return CSA_ERR_UNSUPPORTED;
@@ -360,18 +363,61 @@ csa_status csa_decode_append(const csa_append_job* jobs, int njobs, const csa_wi
     if (st != CSA_OK) return st;
     if (!w.row || !w.ring) return CSA_ERR_NULL;
   }
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_decode_append(const csa_append_job* jobs, int njobs, const csa_window_job* wins, int nwins, int B,
+                             const int64_t* pos, const csa_pages* pages, int in_t, void* stream) {
+  const csa_status st = check_append(jobs, njobs, wins, nwins, B, pages, in_t);
+  if (st != CSA_OK) return st;
   if (B == 0) return CSA_OK;
   if (!pos) return CSA_ERR_NULL;
   return launch_decode_append(jobs, njobs, wins, nwins, B, pos, pages, in_t, (hipStream_t)stream);
 }
 
-csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
-                           const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
-                           const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
-                           void* stream) {
+}  // extern "C"
+namespace {
+csa_status check_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                             const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                             const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                             bool& empty);
+}  // namespace
+extern "C" {
+
+csa_status csa_append_index_paged(const csa_append_job* jobs, const csa_window_job* win, int in_t, const void* q,
+                                  const void* q_scale, const float* w, const void* k_pool, const void* k_scale_pool,
+                                  const csa_pages* pages, int B, int HI, int cI, int64_t n_max, const int64_t* pos0,
+                                  int m, int qk_t, void* scores, int score_t, uint32_t* bound, void* stream) {
+  csa_status st = check_append(jobs, 2, win, win ? 1 : 0, B, pages, in_t);
+  if (st != CSA_OK) return st;
+  if (jobs[0].m != m || jobs[1].m != m || m >= 64) return CSA_ERR_UNSUPPORTED;
+  // the indexer-key job writes the key pool this call scores
+  if (jobs[1].out != k_pool || jobs[1].out_scale != k_scale_pool || jobs[1].out_t != qk_t || jobs[1].c != cI ||
+      jobs[1].prep)
+    return CSA_ERR_SHAPE;
+  if (win && (win->c % 4 || win->c / 4 > 256)) return CSA_ERR_UNSUPPORTED;  // one 256-thread workgroup
+  if (jobs[0].c / 4 > 256 || jobs[1].c / 4 > 256) return CSA_ERR_UNSUPPORTED;
+  bool empty;
+  st = check_index_paged(q, q_scale, w, k_pool, k_scale_pool, pages, B, HI, cI, n_max, pos0, m, qk_t, scores, score_t,
+                         bound, empty);
+  if (st != CSA_OK || empty) return st;
+  return launch_append_index_paged(jobs, win, in_t, q, q_scale, w, k_pool, k_scale_pool, pages, B, HI, cI, n_max,
+                                   pos0, m, qk_t, scores, score_t, bound, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+csa_status check_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                             const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                             const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                             bool& empty) {
+  empty = false;
   if (qk_t != CSA_BF16 && qk_t != CSA_FP8_E4M3_ROWSCALE && qk_t != CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
   if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
-  bool empty;
   csa_status st = check_index(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, cI, n_max, pos0, m, qk_t, scores,
                               empty);
   if (st != CSA_OK) return st;
@@ -379,8 +425,21 @@ csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, c
   if (st != CSA_OK) return st;
   st = check_pages_cover(pages, m, n_max);
   if (st != CSA_OK) return st;
-  if (empty) return CSA_OK;
-  if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
+  if (!empty && bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_index_paged(const void* q, const void* q_scale, const float* w, const void* k_pool,
+                           const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI, int64_t n_max,
+                           const int64_t* pos0, int m, int qk_t, void* scores, int score_t, uint32_t* bound,
+                           void* stream) {
+  bool empty;
+  const csa_status st = check_index_paged(q, q_scale, w, k_pool, k_scale_pool, pages, B, HI, cI, n_max, pos0, m,
+                                          qk_t, scores, score_t, bound, empty);
+  if (st != CSA_OK || empty) return st;
   return launch_index_paged(q, q_scale, w, k_pool, k_scale_pool, pages, B, HI, cI, n_max, pos0, m, qk_t, scores,
                             score_t, bound, (hipStream_t)stream);
 }

@@ -77,3 +77,11 @@ csa_status launch_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq,
                             int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, hipStream_t stream);
 csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
                                    int d_g, int d, void* mid, void* out, hipStream_t stream);
+
+// csa_decode_append's work for the token (two jobs: KV entry, indexer key into k_pool; optional window) fused
+// into the paged decode index launch (validated)
+csa_status launch_append_index_paged(const csa_append_job* jobs, const csa_window_job* win, int in_t, const void* q,
+                                     const void* q_scale, const float* w, const void* k_pool,
+                                     const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI,
+                                     int64_t n_max, const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
+                                     uint32_t* bound, hipStream_t stream);

@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ kI, const void* __restrict__ k_scale, int T, int64_t n_max,
     const int64_t* __restrict__ pos0, int m, ScoreOut so, uint32_t* __restrict__ bound,
-    std::conditional_t<FUSE, IndexFuse, NoFuse> fz, PageMap pm) {
+    std::conditional_t<FUSE, std::conditional_t<PAGED, csa_compress_body::AppendFuse, IndexFuse>, NoFuse> fz,
+    PageMap pm) {
   constexpr int HI = NT * 16;
   constexpr int RB = Fmt<FMT>::kRowBytes;
   constexpr int LB = Fmt<FMT>::kLaneBytes;
@@ -229,7 +230,54 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
   const int64_t srow = (int64_t)row * n_max;  // this row's first score
 
-  if constexpr (FUSE) {  // decode rows only (row == b)
+  if constexpr (FUSE && PAGED) {  // decode rows only (row == b): this token's csa_decode_append work
+    constexpr int kScratch = 3 * 256;
+    constexpr bool kInLds = sizeof(s_lds) >= kScratch * sizeof(f32x4);
+    __shared__ __align__(16) f32x4 s_cz[kInLds ? 1 : kScratch];
+    __shared__ float s_czr[4];
+    f32x4* cz = kInLds ? reinterpret_cast<f32x4*>(s_lds) : s_cz;
+    const int64_t t = pos0[b];
+    const int m = fz.m;
+    const int64_t i = t / m - 1;
+    // (uniform) the block t closes has an entry whose page is mapped
+    const bool done = t >= m && t % m == 0 && (i >> fz.jobs.j[0].plog2) < fz.jobs.j[0].tstride;
+    const bool do_ik = done && (int64_t)blockIdx.x == i / kEntriesPerWG;  // its key, before this WG's tiles
+    const bool do_kv = t >= 0 && blockIdx.x == 0;
+    const bool f32in = fz.in_t == CSA_F32;
+    if (do_ik) {
+      if (f32in) {
+        csa_compress_body::compress_one<float, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, b, 0, m, 0, i, cz, cz + 256,
+                                                    cz + 512, s_czr);
+        csa_compress_body::store_ring_rows<float>(fz.jobs.j[1], fz.src[1], b, t);
+      } else {
+        csa_compress_body::compress_one<uint16_t, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, b, 0, m, 0, i, cz,
+                                                       cz + 256, cz + 512, s_czr);
+        csa_compress_body::store_ring_rows<uint16_t>(fz.jobs.j[1], fz.src[1], b, t);
+      }
+    }
+    if (do_ik && do_kv) __syncthreads();  // the slice-merge scratch is used again
+    if (do_kv) {
+      if (f32in) {
+        if (done)
+          csa_compress_body::compress_one<float, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, b, 0, m, 0, i, cz,
+                                                      cz + 256, cz + 512, s_czr);
+        csa_compress_body::store_ring_rows<float>(fz.jobs.j[0], fz.src[0], b, t);
+        if (!done) csa_compress_body::store_ring_rows<float>(fz.jobs.j[1], fz.src[1], b, t);
+        if (fz.win_ring) csa_compress_body::store_window_row<float, 256>(fz, b, t, s_czr);
+      } else {
+        if (done)
+          csa_compress_body::compress_one<uint16_t, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, b, 0, m, 0, i, cz,
+                                                         cz + 256, cz + 512, s_czr);
+        csa_compress_body::store_ring_rows<uint16_t>(fz.jobs.j[0], fz.src[0], b, t);
+        if (!done) csa_compress_body::store_ring_rows<uint16_t>(fz.jobs.j[1], fz.src[1], b, t);
+        if (fz.win_ring) csa_compress_body::store_window_row<uint16_t, 256>(fz, b, t, s_czr);
+      }
+    }
+    if (do_ik || do_kv) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  } else if constexpr (FUSE) {  // decode rows only (row == b)
     constexpr int kScratch = 3 * 256;  // f32x4 slots of the compression's slice merge
     constexpr bool kInLds = sizeof(s_lds) >= kScratch * sizeof(f32x4);
     __shared__ __align__(16) f32x4 s_cz[kInLds ? 1 : kScratch];
@@ -625,14 +673,19 @@ __global__ __launch_bounds__(kF32Threads) void index_f32_kernel(const float* __r
 template <int FMT>
 csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale, int B,
                       int T, int HI, int64_t n_max, const int64_t* pos0, int m, ScoreOut so, uint32_t* bound,
-                      const IndexFuse* fuse, const PageMap* pages, hipStream_t stream) {
-  if (pages) {  // decode rows over a paged key pool
+                      const IndexFuse* fuse, const PageMap* pages, hipStream_t stream,
+                      const csa_compress_body::AppendFuse* afz = nullptr) {
+  if (pages) {  // decode rows over a paged key pool (with this token's append work when afz is given)
     if (fuse || T != 1) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(n_max, kEntriesPerWG), B);
     dim3 block(kWaves * 64);
 #define CSA_IDX_PAGED(NT)                                                                                   \
-  hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, \
-                     w, (const uint8_t*)k, k_scale, 1, n_max, pos0, m, so, bound, NoFuse{}, *pages)
+  if (afz)                                                                                                  \
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, true, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, \
+                       w, (const uint8_t*)k, k_scale, 1, n_max, pos0, m, so, bound, *afz, *pages);          \
+  else                                                                                                      \
+    hipLaunchKernelGGL((index_mfma_kernel<FMT, NT, false, true>), grid, block, 0, stream, (const uint8_t*)q, q_scale, \
+                       w, (const uint8_t*)k, k_scale, 1, n_max, pos0, m, so, bound, NoFuse{}, *pages)
     switch (HI) {
       case 16: CSA_IDX_PAGED(1); break;
       case 32: CSA_IDX_PAGED(2); break;
@@ -739,6 +792,32 @@ static csa_status launch_index_impl(const void* q, const void* q_scale, const fl
       return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, pages, stream);
     case CSA_MXFP4_E8M0_B32:
       return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k, k_scale, B, T, HI, n_max, pos0, m, so, bound, fuse, pages, stream);
+    default:
+      return CSA_ERR_UNSUPPORTED;
+  }
+}
+
+csa_status launch_append_index_paged(const csa_append_job* jobs, const csa_window_job* win, int in_t, const void* q,
+                                     const void* q_scale, const float* w, const void* k_pool,
+                                     const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI,
+                                     int64_t n_max, const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
+                                     uint32_t* bound, hipStream_t stream) {
+  csa_compress_body::AppendFuse af;
+  csa_compress_body::fill_append(jobs, win, pages, in_t, af);
+  int plog2 = 0;
+  while ((1 << plog2) < pages->page_tokens / m) ++plog2;
+  const PageMap pm{pages->block_table, pages->max_pages, plog2};
+  const ScoreOut so{scores, score_t == CSA_BF16 ? 1 : 0};
+  switch (qk_t) {
+    case CSA_BF16:
+      return launch_fmt<CSA_BF16>(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, n_max, pos0, m, so, bound, nullptr,
+                                  &pm, stream, &af);
+    case CSA_FP8_E4M3_ROWSCALE:
+      return launch_fmt<CSA_FP8_E4M3_ROWSCALE>(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, n_max, pos0, m, so,
+                                               bound, nullptr, &pm, stream, &af);
+    case CSA_MXFP4_E8M0_B32:
+      return launch_fmt<CSA_MXFP4_E8M0_B32>(q, q_scale, w, k_pool, k_scale_pool, B, 1, HI, n_max, pos0, m, so,
+                                            bound, nullptr, &pm, stream, &af);
     default:
       return CSA_ERR_UNSUPPORTED;
   }

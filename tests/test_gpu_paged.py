@@ -382,3 +382,53 @@ def test_decode_loop_against_oracle(api):
             eh = rel_l2(g_hout[b], h_ref[0])
             say(f"  step {s} seq {b} t={t} visible {nv}/{nh}: csa rel-L2 {e:.2e}, hca rel-L2 {eh:.2e}")
             assert e <= LOWP_TOL and eh <= LOWP_TOL, (s, b, e, eh)
+
+
+def test_append_index_paged_matches_separate(api):
+    """csa_append_index_paged equals csa_decode_append followed by csa_index_paged bit for bit: the pools, the
+    rings, the window ring, the scores and bound keys.  Sequence 0 completes an entry that a later workgroup
+    scores, 1 completes none, 2 completes one in workgroup 0's range (which then also compresses the KV entry)."""
+    cfg = configs.C3.scaled(B=3, n_comp=5000)
+    m, R, B = cfg.m, cfg.rope_dims, 3
+    ts = [4 * 4096, 4 * 3000 + 1, 4 * 700]
+    page_tokens = 1024
+    E = page_tokens // m
+    maxp = -(-cfg.n_comp // E)
+    table, n_phys = make_table(np.random.default_rng(31), B, maxp)
+    pg = api.pages(dev(table), page_tokens)
+    prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
+    bi = gen.decode_biases(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    kc = gen.indexer_key_cache(cfg)
+    rnd = lambda *shape: (torch.randn(shape, device=DEV)).to(torch.bfloat16)
+    torch.manual_seed(3)
+    base = dict(kv_r=[rnd(B, 2 * m, cfg.c) for _ in range(4)], ik_r=[rnd(B, 2 * m, cfg.cI) for _ in range(4)],
+                win=rnd(B, cfg.n_win, cfg.c), kv_pool=rnd(n_phys * E, cfg.c),
+                ik_pool=scatter(dev(kc["data"]), table, E, n_phys, 5), ik_sc=scatter(dev(kc["scale"]), table, E, n_phys, 6))
+    toks = {nm: rnd(B, cfg.c if nm in ("ca", "cb", "za", "zb", "win") else cfg.cI)
+            for nm in ("ca", "cb", "za", "zb", "ica", "icb", "iza", "izb", "win")}
+    pos = _pos(ts)
+    say(f"append_index_paged positions {ts}")
+    results = []
+    for fused in (False, True):
+        st = {k: ([x.clone() for x in v] if isinstance(v, list) else v.clone()) for k, v in base.items()}
+        kv_job = dict(ca=toks["ca"], cb=toks["cb"], za=toks["za"], zb=toks["zb"], bias_a=dev(bi["bias_a"]),
+                      bias_b=dev(bi["bias_b"]), m=m, ring_ca=st["kv_r"][0], ring_cb=st["kv_r"][1],
+                      ring_za=st["kv_r"][2], ring_zb=st["kv_r"][3], out=st["kv_pool"], prep=prep)
+        ik_job = dict(ca=toks["ica"], cb=toks["icb"], za=toks["iza"], zb=toks["izb"], bias_a=dev(bi["ibias_a"]),
+                      bias_b=dev(bi["ibias_b"]), m=m, ring_ca=st["ik_r"][0], ring_cb=st["ik_r"][1],
+                      ring_za=st["ik_r"][2], ring_zb=st["ik_r"][3], out=st["ik_pool"], out_scale=st["ik_sc"],
+                      out_fmt="fp8")
+        win_job = dict(row=toks["win"], ring=st["win"], prep=prep)
+        bound = api.bound_keys(B, 1, cfg.n_comp, DEV)
+        qd, qs, wd = dev(qi["data"]), dev(qi["scale"]), dev(w)
+        if fused:
+            sc = api.append_index_paged([kv_job, ik_job], win_job, qd, qs, wd, st["ik_pool"], st["ik_sc"], pg, pos, m,
+                                        "fp8", cfg.n_comp, bound=bound)
+        else:
+            api.decode_append([kv_job, ik_job], [win_job], pos, pg)
+            sc = api.index_paged(qd, qs, wd, st["ik_pool"], st["ik_sc"], pg, pos, m, "fp8", cfg.n_comp, bound=bound)
+        torch.cuda.synchronize()
+        results.append([sc, bound, st["kv_pool"], st["ik_pool"], st["ik_sc"], st["win"]] + st["kv_r"] + st["ik_r"])
+    for a_, b_ in zip(*results):
+        assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
