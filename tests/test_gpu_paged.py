@@ -432,3 +432,62 @@ def test_append_index_paged_matches_separate(api):
         results.append([sc, bound, st["kv_pool"], st["ik_pool"], st["ik_sc"], st["win"]] + st["kv_r"] + st["ik_r"])
     for a_, b_ in zip(*results):
         assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
+
+
+def test_paged_full_size_matches_contiguous(api):
+    """The Pro 1M decode shapes in the launch configuration bench.py runs (C3: fp8 keys over 262,144 entries,
+    k = 1024; C5's HCA over 8,192 entries, wide variant): paged == contiguous bit for bit.  Entries are seeded
+    device noise (the equality needs no oracle)."""
+    g = torch.Generator(device=DEV).manual_seed(41)
+    cfg = configs.C3
+    B, N, m = cfg.B, cfg.n_comp, cfg.m
+    page_tokens = 1024
+    E = page_tokens // m
+    table, n_phys = make_table(np.random.default_rng(42), B, -(-N // E) + 1)
+    pg = api.pages(dev(table), page_tokens)
+    cap = table.shape[1] * E
+    say(f"paged full size C3 N={N} capacity={cap}")
+    keys = torch.randint(0, 120, (B, cap, cfg.cI), dtype=torch.uint8, device=DEV, generator=g)
+    ksc = torch.rand((B, cap), device=DEV, generator=g) * 0.01 + 0.001
+    qi, w = gen.indexer_queries(cfg)
+    qd, qs, wd = dev(qi["data"]), dev(qi["scale"]), dev(w)
+    pos = _pos([4 * N - 4 * 5, 4 * N, 4 * N - 1001, 4 * (N // 2)])
+    bc, bp = api.bound_keys(B, 1, cap, DEV), api.bound_keys(B, 1, cap, DEV)
+    sc = api.index(qd, qs, wd, keys, ksc, pos, m, "fp8", bound=bc)
+    sp = api.index_paged(qd, qs, wd, scatter(keys, table, E, n_phys, 1), scatter(ksc, table, E, n_phys, 2), pg, pos,
+                         m, "fp8", cap, bound=bp)
+    torch.cuda.synchronize()
+    assert torch.equal(sc.view(torch.int32), sp.view(torch.int32)) and torch.equal(bc, bp)
+    idx, _ = api.topk(sc, pos, m, cfg.k, bound=bc)
+    del keys
+    kv = torch.randn((B, cap, cfg.c), device=DEV, generator=g).to(torch.bfloat16)
+    win = torch.randn((B, cfg.n_win, cfg.c), device=DEV, generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, cfg.H, cfg.c), device=DEV, generator=g) / 22.6).to(torch.bfloat16)
+    sink = dev(gen.sink(cfg))
+    p0 = pos.cpu().numpy()
+    ring = ring_of(win, [[int(t) - cfg.n_win + 1 + j for j in range(cfg.n_win)] for t in p0], cfg.n_win)
+    oc = api.attend(q, kv, idx, win, sink, pos, m, cfg.n_win, cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base,
+                    kv_prepared=1)
+    op = api.attend_paged(q, scatter(kv, table, E, n_phys, 3), idx, ring, sink, pos, pg, m, cfg.rope_dims, cfg.scale,
+                          cap, cfg.eps, cfg.rope_base, kv_prepared=1)
+    torch.cuda.synchronize()
+    assert torch.equal(oc.view(torch.int16), op.view(torch.int16))
+    del kv
+    c5 = configs.C5
+    nh, Eh = c5.n_hca, page_tokens // c5.m_hca
+    say(f"paged full size C5 HCA n={nh}")
+    tb5, n5 = make_table(np.random.default_rng(43), c5.B, -(-nh // Eh))
+    pg5 = api.pages(dev(tb5), page_tokens)
+    hk = torch.randn((c5.B, nh, c5.c), device=DEV, generator=g).to(torch.bfloat16)
+    hw = torch.randn((c5.B, c5.n_win, c5.c), device=DEV, generator=g).to(torch.bfloat16)
+    hq = (torch.randn((c5.B, 1, c5.H, c5.c), device=DEV, generator=g) / 22.6).to(torch.bfloat16)
+    hpos = _pos([c5.pos0 - 128 * b for b in range(c5.B)])
+    hp0 = hpos.cpu().numpy()
+    hring = ring_of(hw, [[int(t) - c5.n_win + 1 + j for j in range(c5.n_win)] for t in hp0], c5.n_win)
+    hs = dev(gen.sink(c5, hca=True))
+    oc = api.hca_attend(hq, hk, hw, hs, hpos, c5.m_hca, c5.n_win, c5.rope_dims, c5.scale, c5.eps, c5.rope_base,
+                        kv_prepared=2)
+    op = api.hca_attend_paged(hq, scatter(hk, tb5, Eh, n5, 4), hring, hs, hpos, pg5, c5.m_hca, c5.rope_dims, c5.scale,
+                              nh, c5.eps, c5.rope_base, kv_prepared=2)
+    torch.cuda.synchronize()
+    assert torch.equal(oc.view(torch.int16), op.view(torch.int16))
