@@ -321,13 +321,22 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   // wave's j-th logical page (clamped to the last one), loaded once before any tile.
   const int64_t wfp = PAGED ? wave_first >> pm.plog2 : 0;
   const int64_t pmask = PAGED ? ((int64_t)1 << pm.plog2) - 1 : 0;
-  int tab = 0;
-  if constexpr (PAGED)
-    tab = pm.table[(int64_t)b * pm.tstride + min(wfp + lane, (n_max - 1) >> pm.plog2)];
+  // Pages of 256 entries or more hold a wave's whole range (clamped rows included): one uniform entry.
+  const bool one_page = PAGED && pm.plog2 >= 8;  // (uniform)
+  int tab = 0, tab1 = 0;
+  if constexpr (PAGED) {
+    const int64_t lastp = (n_max - 1) >> pm.plog2;
+    if (one_page) {
+      const int64_t wfu = __builtin_amdgcn_readfirstlane((int)wfp);
+      tab1 = __builtin_amdgcn_readfirstlane(pm.table[(int64_t)b * pm.tstride + min(wfu, lastp)]);
+    } else {
+      tab = pm.table[(int64_t)b * pm.tstride + min(wfp + lane, lastp)];
+    }
+  }
   // pool row of the clamped entry er, whose tile starts at the clamped entry ec
   auto key_row = [&](int64_t er, int64_t ec) -> int64_t {
     if constexpr (PAGED) {
-      const int pg = __builtin_amdgcn_readlane(tab, (int)max((int64_t)0, (ec >> pm.plog2) - wfp));
+      const int pg = one_page ? tab1 : __builtin_amdgcn_readlane(tab, (int)max((int64_t)0, (ec >> pm.plog2) - wfp));
       return ((int64_t)pg << pm.plog2) | (er & pmask);
     } else {
       return (int64_t)b * n_max + er;
@@ -364,7 +373,8 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     for (int j = 0; j < kScaleLoads; ++j) {
       const int64_t er = min(wave_first + 64 * j + lane, n_max - 1);
       if constexpr (PAGED)
-        srow[j] = ((int64_t)__shfl(tab, (int)((er >> pm.plog2) - wfp), 64) << pm.plog2) | (er & pmask);
+        srow[j] = ((int64_t)(one_page ? tab1 : __shfl(tab, (int)((er >> pm.plog2) - wfp), 64)) << pm.plog2) |
+                  (er & pmask);
       else
         srow[j] = (int64_t)b * n_max + er;
     }
