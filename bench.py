@@ -376,7 +376,7 @@ def main():
         if T == 1:
             # decode: the block's KV entry and its indexer key (into the key cache) are computed inside the
             # index launch, by the workgroups that need them first
-            api.compress_index(kv_job, st["cik_t"], cfg.m, c["row0_pos"], first, st["qi"], st["qi_scale"], st["w"],
+            api.compress_index(None, st["cik_t"], cfg.m, c["row0_pos"], first, st["qi"], st["qi_scale"], st["w"],
                                st["ik"], st["ik_scale"], pos, fmt, scores=scores, bound=bound)
         else:
             # prefill: every entry of the chunk, KV entry and indexer key (in the cache format), one launch
@@ -388,7 +388,10 @@ def main():
                 api.prepare_kv(st["win"][:, cfg.n_win - 1:], prep, out=st["pwin"][:, cfg.n_win - 1:], **win_new)
             api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
                       bound=bound)
-        api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
+        if T == 1:   # decode: the block's KV entry rides in the selection's launch (one more workgroup per row)
+            api.topk_compress(scores, pos, cfg.m, cfg.k, kv_job, c["row0_pos"], first, idx=idx, bound=bound)
+        else:
+            api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
         api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win, cfg.rope_dims, cfg.scale,
                    cfg.eps, cfg.rope_base, out=out, kv_prepared=csa_mode, comp_scale=kv_scale)
         if side is not None:

@@ -201,7 +201,8 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w,
  * where job 1's output is the key cache itself: entry first_entry of k (and
  * k_scale), stored in qk_t (fp8 with its row scale, MXFP4 with its block
  * scales, or bf16), read by the index scores of the same launch.
- *   job 0 : ca0 .. bias_b0, c0, out0 (CSA_F32 / CSA_BF16 rows [B][..][c0], or
+ *   job 0 : (out0 NULL: none, the indexer key alone -- e.g. when csa_topk_compress computes the KV
+ *           entry) ca0 .. bias_b0, c0, out0 (CSA_F32 / CSA_BF16 rows [B][..][c0], or
  *           CSA_FP8_BF16_ROPE rows with prep0 and their scales in out_scale0,
  *           with batch stride out_batch_stride0, 0 = 1), prep0 as in
  *           csa_compress.
@@ -251,6 +252,21 @@ csa_status csa_topk(const void* scores, int score_t, int B, int T, int64_t n_max
                     const int64_t* pos0, int m, int k, const uint32_t* bound,
                     int32_t* idx, float* vals,
                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * csa_topk_compress -- csa_topk for decode rows (T = 1) and a csa_compress of one entry per sequence
+ * (first_entry; rows, layouts, out_t and prep as in csa_compress with num_entries = 1) in one launch:
+ * with the indexer's bound keys the selection's launch carries one more workgroup per sequence that
+ * computes the entry (the decode step's new KV entry, read by the attention after the selection);
+ * without them the entry is computed by a launch of its own first.  Results equal the two calls.
+ * Limits: those of both calls, m < 64.
+ */
+csa_status csa_topk_compress(const void* scores, int score_t, int B, int64_t n_max, const int64_t* pos0, int m,
+                             int k, const uint32_t* bound, int32_t* idx, float* vals, void* workspace,
+                             size_t ws_bytes, const void* ca, const void* cb, const void* za, const void* zb,
+                             const float* bias_a, const float* bias_b, int c, int rows, int64_t row0_pos,
+                             int64_t first_entry, int in_t, void* out, void* out_scale, int out_t,
+                             int64_t out_batch_stride, const csa_kv_prep* prep, void* stream);
 
 /*
  * csa_attend -- CSA core attention ([CSA] (3) shared key-value MQA and [details]).

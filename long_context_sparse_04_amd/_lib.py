@@ -59,6 +59,8 @@ SIGNATURES = {
     "csa_index": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _P, _I, _I, _P, _I, _P, _P]),
     "csa_topk_workspace_bytes": (_SZ, [_I, _I, _I64, _I]),
     "csa_topk": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "csa_topk_compress": (_I, [_P, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P, _P, _P, _P, _P, _I, _I, _I64,
+                               _I64, _I, _P, _P, _I, _I64, _PREP, _P]),
     "csa_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I,
                         _I, _I, _P, _I, _P, _SZ, _P]),

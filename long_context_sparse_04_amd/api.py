@@ -151,8 +151,11 @@ def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_sca
     bf16 RoPE format with out_scale; optional out_batch_stride, prep); p_ik: the indexer-key streams, whose entry is written into k / k_scale at first_entry.  Returns
     the scores."""
     lib = _lib.load()
-    B, rows, c0 = p_kv["ca"].shape
-    in_fmt = _TORCH_FMT[p_kv["ca"].dtype]
+    B, rows, _ = p_ik["ca"].shape
+    in_fmt = _TORCH_FMT[p_ik["ca"].dtype]
+    if p_kv is None:   # the indexer key alone (the KV entry computed elsewhere, e.g. by topk_compress)
+        p_kv = {"ca": None, "za": None, "bias_a": None, "out": None}
+    c0 = 0 if p_kv["ca"] is None else p_kv["ca"].shape[2]
     HI = q.shape[2]
     cI = q.shape[3] * (2 if fmt == "mxfp4" else 1)
     N = k.shape[1]
@@ -162,7 +165,8 @@ def compress_index(p_kv, p_ik, m, row0_pos, first_entry, q, q_scale, w, k, k_sca
     st = lib.csa_compress_index(
         _ptr(p_kv["ca"]), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]), _ptr(p_kv.get("zb")), _ptr(p_kv["bias_a"]),
         _ptr(p_kv.get("bias_b")), c0, _dptr(out0), _dptr(p_kv.get("out_scale")),
-        FMT["fp8rope"] if out0.dtype == torch.uint8 else FMT[_TORCH_FMT[out0.dtype]], p_kv.get("out_batch_stride", 0),
+        0 if out0 is None else (FMT["fp8rope"] if out0.dtype == torch.uint8 else FMT[_TORCH_FMT[out0.dtype]]),
+        p_kv.get("out_batch_stride", 0),
         _prep_arg(p_kv.get("prep")),
         _ptr(p_ik["ca"]), _ptr(p_ik.get("cb")), _ptr(p_ik["za"]), _ptr(p_ik.get("zb")), _ptr(p_ik["bias_a"]),
         _ptr(p_ik.get("bias_b")),
@@ -218,6 +222,32 @@ def topk(scores, pos0, m, k, idx=None, vals=None, ws=None, stream=None, want_val
                       _ptr(idx), _ptr(vals), _ptr(ws), _ws_bytes(ws), _stream(stream))
     _lib.check(st, "csa_topk")
     return idx, vals
+
+
+def topk_compress(scores, pos0, m, k, p_kv, row0_pos, first_entry, idx=None, ws=None, bound=None, stream=None):
+    """csa_topk_compress (decode rows): the selection and the KV entry first_entry of every sequence (p_kv as in
+    compress_pair, out required) in one launch.  Returns idx."""
+    lib = _lib.load()
+    B, T, N = scores.shape
+    if T != 1:
+        raise CSAError("topk_compress: decode rows only (T = 1)")
+    if idx is None:
+        idx = torch.empty((B, 1, k), dtype=torch.int32, device=scores.device)
+    nb = lib.csa_topk_workspace_bytes(B, 1, N, k)
+    if ws is None:
+        ws = workspace(nb, scores.device, "topk", zero=True)
+    ca = p_kv["ca"]
+    out = p_kv["out"]
+    out_fmt = p_kv.get("out_fmt") or _TORCH_FMT[out.dtype] if out.dtype != torch.uint8 else p_kv.get("out_fmt")
+    prep = p_kv.get("prep")
+    st = lib.csa_topk_compress(_ptr(scores), FMT[_TORCH_FMT[scores.dtype]], B, N, _ptr(pos0), m, k, _ptr(bound),
+                               _ptr(idx), None, _ptr(ws), _ws_bytes(ws), _ptr(ca), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]),
+                               _ptr(p_kv.get("zb")), _ptr(p_kv["bias_a"]), _ptr(p_kv.get("bias_b")), ca.shape[2],
+                               ca.shape[1], row0_pos, first_entry, FMT[_TORCH_FMT[ca.dtype]], _dptr(out),
+                               _dptr(p_kv.get("out_scale")), FMT[out_fmt], p_kv.get("out_batch_stride", 0),
+                               _prep_arg(prep), _stream(stream))
+    _lib.check(st, "csa_topk_compress")
+    return idx
 
 
 def prepare_kv(x, prep, pos_first=0, pos_stride=1, pos_base=None, out=None, out_fmt=None, stream=None,

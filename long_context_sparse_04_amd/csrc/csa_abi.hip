@@ -196,11 +196,13 @@ csa_status csa_compress_index(const void* ca0, const void* cb0, const void* za0,
   void* out1 = k ? static_cast<uint8_t*>(k) + first_entry * krow : nullptr;
   void* out_scale1 = k_scale ? static_cast<uint8_t*>(k_scale) + first_entry * srow : nullptr;
   int64_t bs0 = out_batch_stride0, bs1 = n_max;
-  bool e0, e1;
-  st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry, 1, in_t, out0,
-                      out_scale0, out_t0, bs0, prep0, e0);
-  if (st != CSA_OK) return st;
-  if (out_t0 != CSA_F32 && out_t0 != CSA_BF16 && out_t0 != CSA_FP8_BF16_ROPE) return CSA_ERR_UNSUPPORTED;
+  bool e0 = false, e1;
+  if (out0) {  // (out0 NULL: no KV job, the indexer key alone)
+    st = check_compress(ca0, cb0, za0, zb0, bias_a0, bias_b0, B, rows, c0, m, row0_pos, first_entry, 1, in_t, out0,
+                        out_scale0, out_t0, bs0, prep0, e0);
+    if (st != CSA_OK) return st;
+    if (out_t0 != CSA_F32 && out_t0 != CSA_BF16 && out_t0 != CSA_FP8_BF16_ROPE) return CSA_ERR_UNSUPPORTED;
+  }
   st = check_compress(ca1, cb1, za1, zb1, bias_a1, bias_b1, B, rows, cI, m, row0_pos, first_entry, 1, in_t, out1,
                       out_scale1, qk_t, bs1, nullptr, e1);
   if (st != CSA_OK || e0 || empty) return st;
@@ -523,6 +525,30 @@ csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o,
   if (rows == 0) return CSA_OK;
   if (!o || !w_g || !w_o || !mid || !out) return CSA_ERR_NULL;
   return launch_grouped_out_proj(o, w_g, w_o, rows, n_h, c, g, d_g, d, mid, out, (hipStream_t)stream);
+}
+
+
+csa_status csa_topk_compress(const void* scores, int score_t, int B, int64_t n_max, const int64_t* pos0, int m,
+                             int k, const uint32_t* bound, int32_t* idx, float* vals, void* workspace,
+                             size_t ws_bytes, const void* ca, const void* cb, const void* za, const void* zb,
+                             const float* bias_a, const float* bias_b, int c, int rows, int64_t row0_pos,
+                             int64_t first_entry, int in_t, void* out, void* out_scale, int out_t,
+                             int64_t out_batch_stride, const csa_kv_prep* prep, void* stream) {
+  if (m >= 64) return CSA_ERR_UNSUPPORTED;  // one 256-thread workgroup pools the entry's rows
+  bool empty;
+  csa_status st = check_compress(ca, cb, za, zb, bias_a, bias_b, B, rows, c, m, row0_pos, first_entry, 1, in_t, out,
+                                 out_scale, out_t, out_batch_stride, prep, empty);
+  if (st != CSA_OK) return st;
+  if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  if (B < 0 || n_max < 0 || m < 1 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
+  if (n_max >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  if (B == 0) return CSA_OK;
+  if (!idx || !pos0 || (n_max > 0 && !scores)) return CSA_ERR_NULL;
+  const size_t need = csa_topk_workspace_bytes(B, 1, n_max > 0 ? n_max : 1, k);
+  if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  const CompressJob kv{ca, cb, za, zb, bias_a, bias_b, c, out, out_scale, out_t, out_batch_stride, prep};
+  return launch_topk(scores, score_t, B, 1, n_max, pos0, m, k, bound, idx, vals, workspace, (hipStream_t)stream, &kv,
+                     rows, m, row0_pos, first_entry, in_t);
 }
 
 }  // extern "C"

@@ -58,8 +58,12 @@ csa_status launch_compress_index(const CompressJob* jobs, int rows, int m, int64
                                  int qk_t, void* scores, int score_t, uint32_t* bound, hipStream_t stream);
 
 size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k);
+// kv (optional, decode): a KV-entry compression (entry kv_first of each sequence, rows as csa_compress) done
+// inside the launch by one more workgroup per row
 csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream);
+                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream,
+                       const CompressJob* kv = nullptr, int kv_rows = 0, int kv_m = 0, int64_t kv_row0 = 0,
+                       int64_t kv_first = 0, int kv_in_t = 0);
 
 // mode 0: CSA (index list), mode 1: HCA (dense range)
 size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncomp, int n_win);

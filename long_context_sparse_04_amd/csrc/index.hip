@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     __shared__ float s_czr[4];
     f32x4* cz = kInLds ? reinterpret_cast<f32x4*>(s_lds) : s_cz;
     const bool do_ik = (int64_t)blockIdx.x == fz.first_entry / kEntriesPerWG;
-    const bool do_kv = blockIdx.x == 0;
+    const bool do_kv = blockIdx.x == 0 && fz.jobs.j[0].out != nullptr;  // (no KV job: the key alone)
     if (do_ik) {
       if (fz.in_t == CSA_F32)
         csa_compress_body::compress_one<float, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, row, fz.rows, fz.m,

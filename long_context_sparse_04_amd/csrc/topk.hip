@@ -28,6 +28,7 @@
 //      above the 22-bit prefix, kernel 4 finishes (and clears the histogram).
 //    Integer atomics make every result independent of scheduling; the workspace
 //    is left zero-filled where it has to start at zero.
+#include "compress_body.h"
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -45,6 +46,14 @@ constexpr int kMaxChunks = 2048;
 // workspace) and rows of at most kBoundMaxChunks chunks.
 constexpr int kBoundSegCap = 2048;
 constexpr int kBoundMaxChunks = 256;
+
+// The decode step's new KV entry (one per sequence), computed by one extra workgroup per row of the
+// bound-key launch, beside the selection (it is read by the attention after the selection).
+struct TopkFuse {
+  csa_compress_body::Jobs jobs;  // j[0]
+  int on, rows, m, in_t;
+  int64_t row0_pos, first_entry;
+};
 
 // ------------------------------------------------------------------ wave / block primitives
 // Inclusive prefix sum over the 64 lanes of a wave, in lane order: shifts by 1, 2, 4 and 8 inside
@@ -803,7 +812,7 @@ CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, con
 }
 
 #define CSA_FINISH_LDS(SEGCAP, MAXCH)                  \
-  __shared__ Cand s_c[SEGCAP];                         \
+  __shared__ __align__(16) Cand s_c[SEGCAP];          \
   __shared__ uint32_t s_hist[kBins];                   \
   __shared__ int s_pre[MAXCH + 1];                     \
   __shared__ uint32_t s_w[2 * kSplitThreads / 64];     \
@@ -848,13 +857,28 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 template <int KBK>
 __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
-    const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+    const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws,
+    TopkFuse fz) {
   CSA_FINISH_LDS(kBoundSegCap, kBoundMaxChunks)
   __shared__ int s_last;
   __shared__ uint32_t s_nz;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
-  const int nch = gridDim.x;
+  const int nch = (int)((n_max + kChunk - 1) / kChunk);
+  if (fz.on && (int)blockIdx.x == nch) {  // the extra workgroup of a row: its sequence's new KV entry
+    static_assert(kSplitThreads == 256, "the compression body runs on 256 threads here");
+    static_assert(sizeof(Cand) * kBoundSegCap >= 3 * 256 * sizeof(f32x4), "scratch of the slice merge");
+    f32x4* s_cz = reinterpret_cast<f32x4*>(s_c);  // (this workgroup selects nothing)
+    if (fz.in_t == CSA_F32)
+      csa_compress_body::compress_one<float, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, row, fz.rows, fz.m,
+                                                  fz.row0_pos, fz.first_entry, s_cz, s_cz + 256, s_cz + 512,
+                                                  reinterpret_cast<float*>(s_mm));
+    else
+      csa_compress_body::compress_one<uint16_t, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, row, fz.rows, fz.m,
+                                                     fz.row0_pos, fz.first_entry, s_cz, s_cz + 256, s_cz + 512,
+                                                     reinterpret_cast<float*>(s_mm));
+    return;
+  }
   const int b = row / T;
   const int r = row - b * T;
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
@@ -964,7 +988,15 @@ size_t topk_workspace_bytes(int B, int T, int64_t n_max, int k) {
 }
 
 csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_max, const int64_t* pos0, int m, int k,
-                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream) {
+                       const uint32_t* bound, int32_t* idx, float* vals, void* ws, hipStream_t stream,
+                       const CompressJob* kv, int kv_rows, int kv_m, int64_t kv_row0, int64_t kv_first, int kv_in_t) {
+  if (kv && !(use_split(B * T, n_max) && bound && index_bound_keys(n_max) >= 2 * (int64_t)k &&
+              ceil_div(n_max, kChunk) <= kBoundMaxChunks)) {
+    // no bound-key launch to carry it: the entry is compressed by a launch of its own first
+    const csa_status st = launch_compress_jobs(kv, 1, B, kv_rows, kv_m, kv_row0, kv_first, 1, kv_in_t, stream);
+    if (st != CSA_OK) return st;
+    kv = nullptr;
+  }
   const int rows = B * T;
   const int sbf16 = score_t == CSA_BF16 ? 1 : 0;
   if (use_split(rows, n_max)) {
@@ -975,12 +1007,24 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
     const bool bounded = bound && index_bound_keys(n_max) >= 2 * (int64_t)k && nch <= kBoundMaxChunks;
     if (bounded) {
       const int nb = (int)index_bound_keys(n_max);
+      TopkFuse fz{};
+      if (kv) {  // one more workgroup per row computes the row's new KV entry
+        csa_compress_body::fill_jobs(kv, 1, fz.jobs);
+        fz.on = 1;
+        fz.rows = kv_rows;
+        fz.m = kv_m;
+        fz.in_t = kv_in_t;
+        fz.row0_pos = kv_row0;
+        fz.first_entry = kv_first;
+        grid.x += 1;
+      }
       if (nb <= 8 * kSplitThreads)
         hipLaunchKernelGGL((topk_bound_kernel<8>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
-                           pos0, m, k, bound, nb, idx, vals, s);
+                           pos0, m, k, bound, nb, idx, vals, s, fz);
       else
         hipLaunchKernelGGL((topk_bound_kernel<16>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
-                           pos0, m, k, bound, nb, idx, vals, s);
+                           pos0, m, k, bound, nb, idx, vals, s, fz);
+      return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     } else {
       hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
                          m, k, s);

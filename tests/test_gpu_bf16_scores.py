@@ -245,3 +245,38 @@ def test_bf16_score_recall(api, name, scale):
     say(f"recall vs float64 selection: f32 scores {rec['f32']:.5f}  bf16 scores {rec['bf16']:.5f}")
     assert bad["f32"] == 0 and bad["bf16"] == 0, bad
     assert rec["f32"] >= 0.999
+
+
+@pytest.mark.parametrize("n_comp", [65536, 5037])
+def test_topk_compress_matches_separate(api, n_comp):
+    """The decode step with the KV entry moved into the selection's launch (csa_compress_index with the indexer
+    key alone, then csa_topk_compress) writes the same caches, scores, bound keys and selection as
+    csa_compress_index with both jobs followed by csa_topk; 65,536 entries take the bound-key launch (one extra
+    workgroup per row), 5,037 the row path (the entry in a launch of its own)."""
+    cfg = configs.C3.scaled(B=3, n_comp=n_comp)
+    fmt, N = cfg.idx_dtype, cfg.n_comp
+    say(f"topk_compress {cfg.name} N={N}")
+    ckv, cik = gen.compress_inputs(cfg), gen.compress_inputs(cfg, indexer=True)
+    first, r0p = N - 1, 4 * N - 8
+    kc = gen.indexer_key_cache(cfg)
+    qi, w = gen.indexer_queries(cfg)
+    pos0 = [4 * N, 4 * N + 3, 4 * (N - 100)]
+    d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
+    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
+    kv0 = dev(gen.kv_cache(cfg))
+    outs = []
+    for fused in (False, True):
+        kv, ik, iks = kv0.clone(), dev(kc["data"]), dev(kc["scale"])
+        bound = api.bound_keys(cfg.B, 1, N, DEV)
+        qd, qs, wd = dev(qi["data"]), dev(qi["scale"]), dev(w)
+        pkv = dict(d(ckv), out=kv[:, first:], out_batch_stride=N, prep=prep)
+        if fused:
+            sc = api.compress_index(None, d(cik), cfg.m, r0p, first, qd, qs, wd, ik, iks, _pos(pos0), fmt, bound=bound)
+            idx = api.topk_compress(sc, _pos(pos0), cfg.m, cfg.k, pkv, r0p, first, bound=bound)
+        else:
+            sc = api.compress_index(pkv, d(cik), cfg.m, r0p, first, qd, qs, wd, ik, iks, _pos(pos0), fmt, bound=bound)
+            idx, _ = api.topk(sc, _pos(pos0), cfg.m, cfg.k, bound=bound)
+        torch.cuda.synchronize()
+        outs.append((kv, ik, iks, sc, bound, idx))
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_.contiguous().view(torch.uint8), b_.contiguous().view(torch.uint8))
