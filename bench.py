@@ -207,7 +207,9 @@ def _with_projections(cfg, api, torch, step, out, dev):
     rows = cfg.B * cfg.T
     x = gen.proj_inputs(rows, ps["d_c"], cfg.H, cfg.c, cfg.HI, cfg.cI, ps["g"], ps["d_g"], ps["d"], seed=3)
     up = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-    cq, w_uq, w_iuq, w_g, w_o = (up(x[k]) for k in ("cq", "w_uq", "w_iuq", "w_g", "w_o"))
+    cq = up(x["cq"])
+    # the weights are packed once, at load time, into the projections' MFMA-tile layout
+    w_uq, w_iuq, w_g, w_o = (api.pack_proj_weights(up(x[k])) for k in ("w_uq", "w_iuq", "w_g", "w_o"))
     mid = torch.empty((rows, ps["g"] * ps["d_g"]), dtype=torch.bfloat16, device=dev)
     hid = torch.empty((rows, ps["d"]), dtype=torch.bfloat16, device=dev)
     fmt = cfg.idx_dtype

@@ -456,11 +456,22 @@ csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* c
 /*
  * ---- Dense projections on either side of the step (decode rows) ----
  *
+ * Weights are passed PACKED (csa_pack_proj_weights): the [Z][N][K] output-major matrices (row n holds
+ * output n's K weights) rearranged once, at load time, into 1 KB MFMA tiles so that the projections
+ * stream them in contiguous 1 KB loads.  Packed element (n, k) of batch z sits at
+ *   z * N * K + ((n / 16) * (K / 32) + k / 32) * 512 + (((k % 32) / 8) * 16 + n % 16) * 8 + k % 8.
+ *
+ * csa_pack_proj_weights -- w bf16 [z][n][k] -> packed bf16 (the same size, not aliasing w).  n a multiple
+ * of 16, k a multiple of 32.
+ */
+csa_status csa_pack_proj_weights(const void* w, void* packed, int z, int n, int k, void* stream);
+
+/*
  * csa_q_up_proj -- the queries from the shared low-rank latent ([CSA] (2), the q^I equation, and (3), the
  * q equation): q = c^Q W^UQ and q^I = c^Q W^IUQ in one launch that reads c^Q once.
  *   cq     : bf16 [rows][d_c]
- *   w_uq   : bf16 [n_h * c][d_c]    (output-major: row j holds output column j's weights)
- *   w_iuq  : bf16 [n_hI * cI][d_c]
+ *   w_uq   : bf16 [n_h * c][d_c]    packed (csa_pack_proj_weights with z = 1)
+ *   w_iuq  : bf16 [n_hI * cI][d_c]  packed
  *   q      : bf16 [rows][n_h * c]   (the [B][T][H][c] layout of csa_attend's q)
  *   qi     : in qi_t, the [B][T][HI][cI] layout of csa_index's q: bf16; or CSA_FP8_E4M3_ROWSCALE
  *            (e4m3 codes, qi_scale float32 [rows][n_hI] = amax/448 of the head's values); or
@@ -477,8 +488,8 @@ csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, in
  * head outputs of a row split into g groups of n_h / g consecutive heads; group i's (n_h / g) * c values
  * are projected to d_g values, and the g * d_g intermediates to d.
  *   o    : bf16 [rows][n_h * c]            (csa_attend's out layout)
- *   w_g  : bf16 [g][d_g][(n_h / g) * c]    (group i's projection, output-major)
- *   w_o  : bf16 [d][g * d_g]
+ *   w_g  : bf16 [g][d_g][(n_h / g) * c]    packed with z = g (group i's projection)
+ *   w_o  : bf16 [d][g * d_g]               packed with z = 1
  *   mid  : bf16 [rows][g * d_g]            (the intermediates, caller-owned, rounded to bf16)
  *   out  : bf16 [rows][d]
  * Two launches (the groups, then the final projection), float32 accumulation.  Limits: 1 <= rows <=

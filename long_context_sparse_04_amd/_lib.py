@@ -67,6 +67,7 @@ SIGNATURES = {
     "hca_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I64, _I]),
     "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _I,
                         _P, _I, _P, _SZ, _P]),
+    "csa_pack_proj_weights": (_I, [_P, _P, _I, _I, _I, _P]),
     "csa_q_up_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P]),
     "csa_grouped_out_proj": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "csa_decode_append": (_I, [C.POINTER(AppendJob), _I, C.POINTER(WindowJob), _I, _I, _P, _PG, _I, _P]),

@@ -488,8 +488,18 @@ def hca_attend_paged(q, comp_pool, win_ring, sink, pos0, pg, m_hca, rope_dims, s
 # ---- dense projections for decode rows ------------------------------------------------------------------------
 
 
+def pack_proj_weights(w, stream=None):
+    """csa_pack_proj_weights: bf16 [n][k] or [z][n][k] output-major weights -> the packed layout (same shape)."""
+    lib = _lib.load()
+    z, n, k = (1,) + tuple(w.shape) if w.dim() == 2 else tuple(w.shape)
+    packed = torch.empty_like(w)
+    st = lib.csa_pack_proj_weights(_ptr(w), _ptr(packed), z, n, k, _stream(stream))
+    _lib.check(st, "csa_pack_proj_weights")
+    return packed
+
+
 def q_up_proj(cq, w_uq, w_iuq, n_h, c, n_hI, cI, qi_fmt="bf16", q=None, qi=None, qi_scale=None, stream=None):
-    """csa_q_up_proj: cq bf16 [rows][d_c], weights [outputs][d_c].  Returns (q [rows][n_h][c] bf16, q^I in
+    """csa_q_up_proj: cq bf16 [rows][d_c], packed weights (pack_proj_weights of [outputs][d_c]).  Returns (q [rows][n_h][c] bf16, q^I in
     qi_fmt [rows][n_hI][...], its scales or None)."""
     lib = _lib.load()
     rows, d_c = cq.shape
@@ -513,7 +523,8 @@ def q_up_proj(cq, w_uq, w_iuq, n_h, c, n_hI, cI, qi_fmt="bf16", q=None, qi=None,
 
 
 def grouped_out_proj(o, w_g, w_o, g, mid=None, out=None, stream=None):
-    """csa_grouped_out_proj: o bf16 [rows][n_h * c] (or [rows][n_h][c]), w_g [g][d_g][n_h c / g], w_o [d][g d_g].
+    """csa_grouped_out_proj: o bf16 [rows][n_h * c] (or [rows][n_h][c]), packed w_g [g][d_g][n_h c / g] and
+    w_o [d][g d_g] (pack_proj_weights).
     Returns (out [rows][d], mid [rows][g d_g])."""
     lib = _lib.load()
     rows = o.shape[0]

@@ -551,4 +551,14 @@ csa_status csa_topk_compress(const void* scores, int score_t, int B, int64_t n_m
                      rows, m, row0_pos, first_entry, in_t);
 }
 
+
+csa_status csa_pack_proj_weights(const void* w, void* packed, int z, int n, int k, void* stream) {
+  if (z < 0 || n < 0 || k < 0) return CSA_ERR_SHAPE;
+  if (n % 16 || k % 32) return CSA_ERR_UNSUPPORTED;
+  if ((int64_t)z * n * k >= ((int64_t)1 << 40)) return CSA_ERR_SHAPE;
+  if (z == 0 || n == 0 || k == 0) return CSA_OK;
+  if (!w || !packed || w == packed) return CSA_ERR_NULL;
+  return launch_pack_proj_weights(w, packed, z, n, k, (hipStream_t)stream);
+}
+
 }  // extern "C"

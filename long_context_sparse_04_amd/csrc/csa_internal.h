@@ -89,3 +89,4 @@ csa_status launch_append_index_paged(const csa_append_job* jobs, const csa_windo
                                      const void* k_scale_pool, const csa_pages* pages, int B, int HI, int cI,
                                      int64_t n_max, const int64_t* pos0, int m, int qk_t, void* scores, int score_t,
                                      uint32_t* bound, hipStream_t stream);
+csa_status launch_pack_proj_weights(const void* w, void* packed, int z, int n, int k, hipStream_t stream);

@@ -6,9 +6,11 @@
 //
 // Design: with a handful of rows the product is a stream over the weights (every weight byte is read
 // once, the rows stay in L2), so the kernel is HBM-bound and runs bf16 MFMA only because it is free:
-// C[z][m][n] = sum_k A[z][m][k] W[z][n][k], weights output-major (row n of W holds output n's weights,
-// K contiguous).  Lane l of a wave feeds row / column l % 16 and k-group l / 16 of a 16x16x32 MFMA, so
-// one 16-byte load per lane brings a 16-column x 32-k weight tile.  A workgroup's 4 waves either take
+// C[z][m][n] = sum_k A[z][m][k] W[z][n][k].  The weights are stored packed in MFMA tiles (csa_pack_proj_weights):
+// the 16-output x 32-k tile (n / 16, k / 32) is 1 KB contiguous, lane-ordered, so that lane l's 16-byte
+// load -- row / column l % 16, k-group l / 16 of a 16x16x32 MFMA -- is bytes [16 l, 16 l + 16) of it: every
+// load instruction reads 1 KB of contiguous memory (an output-major row layout would give 16 half-used
+// 128-byte lines per instruction, which streams far below the HBM rate).  A workgroup's 4 waves either take
 // different column tiles over the whole K (the fused query launch: 128 columns, one indexer head, per
 // workgroup) or share 16 columns and split K four ways, summed in LDS in a fixed order (the output
 // projection: enough workgroups to keep every CU streaming).
@@ -63,9 +65,10 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
 
   const uint16_t* wz = sg.w + (int64_t)z * sg.w_zstride;
   const uint16_t* az = p.a + (int64_t)z * p.a_zoff;
+  // packed tiles: tile (n / 16, s) at ((n / 16) * nsteps + s) * 512 elements; this lane's 8 at 8 * lane
   const uint16_t* wrow[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) wrow[t] = wz + (int64_t)(n0 + 16 * t + li) * p.k + 8 * kg;
+  for (int t = 0; t < TPW; ++t) wrow[t] = wz + (int64_t)((n0 / 16 + t) * (int64_t)nsteps) * 512 + 8 * lane;
   const uint16_t* arow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) arow[mt] = az + (int64_t)min(16 * mt + li, p.rows - 1) * p.lda + 8 * kg;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
           wf[u][t] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(
-                                                    reinterpret_cast<const u32x4*>(wrow[t] + 32 * s)));
+                                                    reinterpret_cast<const u32x4*>(wrow[t] + 512 * (int64_t)s)));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           af[u][mt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow[mt] + 32 * s));
@@ -221,6 +224,24 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
     }
 }
 
+// [Z][N][K] output-major -> packed MFMA tiles: one thread per 16-byte chunk of the packed array
+__global__ __launch_bounds__(256) void proj_pack_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ out,
+                                                        int64_t chunks, int n, int k) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int nsteps = k / 32;
+  const int64_t per_z = (int64_t)n * k / 8;          // chunks per batch
+  const int64_t z = c / per_z;
+  const int64_t rem = c - z * per_z;
+  const int64_t tile = rem / 64;                     // (n / 16) * nsteps + s
+  const int lane = (int)(rem % 64);
+  const int64_t nt = tile / nsteps, s = tile % nsteps;
+  const int64_t row = nt * 16 + (lane & 15);
+  const int64_t kk = s * 32 + 8 * (lane >> 4);
+  *reinterpret_cast<u32x4*>(out + 8 * c) =
+      *reinterpret_cast<const u32x4*>(w + (z * n + row) * (int64_t)k + kk);
+}
+
 template <int TPW, int KS>
 csa_status launch_proj(const ProjArgs& p, int z, hipStream_t stream) {
   dim3 grid(p.seg[0].blocks + p.seg[1].blocks, z);
@@ -272,4 +293,11 @@ csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w
   p2.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_o), 0, d, out, d, 0, nullptr, kEpiBf16, d / 16};
   p2.seg[1] = ProjSeg{nullptr, 0, 0, nullptr, 0, 0, nullptr, kEpiBf16, 0};
   return launch_proj<1, 4>(p2, 1, stream);
+}
+
+csa_status launch_pack_proj_weights(const void* w, void* packed, int z, int n, int k, hipStream_t stream) {
+  const int64_t chunks = (int64_t)z * n * k / 8;
+  hipLaunchKernelGGL(proj_pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(w), static_cast<uint16_t*>(packed), chunks, n, k);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

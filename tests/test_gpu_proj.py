@@ -42,7 +42,8 @@ def test_q_up_proj(api, rows, qi_fmt):
     d_c, n_h, c, n_hI, cI = 1536, 16, 512, 64, 128
     x = gen.proj_inputs(rows, d_c, n_h, c, n_hI, cI, 1, 16, 16, seed=rows)
     say(f"q_up_proj rows={rows} d_c={d_c} q {n_h}x{c} qI {n_hI}x{cI} {qi_fmt}")
-    q, qi, qs = api.q_up_proj(dev(x["cq"]), dev(x["w_uq"]), dev(x["w_iuq"]), n_h, c, n_hI, cI, qi_fmt=qi_fmt)
+    pk = api.pack_proj_weights
+    q, qi, qs = api.q_up_proj(dev(x["cq"]), pk(dev(x["w_uq"])), pk(dev(x["w_iuq"])), n_h, c, n_hI, cI, qi_fmt=qi_fmt)
     torch.cuda.synchronize()
     v = oracle.decode_bf16
     rq, rqi = oracle.q_up_proj(v(x["cq"]), v(x["w_uq"]), v(x["w_iuq"]))
@@ -81,7 +82,8 @@ def test_grouped_out_proj(api, shape):
     rows, n_h, c, g, d_g, d = (shape[k] for k in ("rows", "n_h", "c", "g", "d_g", "d"))
     x = gen.proj_inputs(rows, 32, n_h, c, 1, 128, g, d_g, d, seed=7)
     say(f"grouped_out_proj rows={rows} heads={n_h}x{c} g={g} d_g={d_g} d={d}")
-    out, mid = api.grouped_out_proj(dev(x["o"]), dev(x["w_g"]), dev(x["w_o"]), g)
+    out, mid = api.grouped_out_proj(dev(x["o"]), api.pack_proj_weights(dev(x["w_g"])),
+                                    api.pack_proj_weights(dev(x["w_o"])), g)
     torch.cuda.synchronize()
     v = oracle.decode_bf16
     rout, rmid = oracle.grouped_out_proj(v(x["o"]), v(x["w_g"]), v(x["w_o"]), g)
@@ -90,3 +92,16 @@ def test_grouped_out_proj(api, shape):
     e = rel_l2(host_f64(out), rout)
     say(f"  out rel-L2 {e:.2e}")
     assert e <= 5e-3
+
+
+def test_pack_proj_weights_layout(api):
+    """The packed layout puts element (n, k) of batch z where include/csa.h says (a host formula, per element)."""
+    rng = np.random.default_rng(5)
+    z, n, k = 3, 48, 96
+    w = rng.integers(0, 1 << 16, size=(z, n, k), dtype=np.uint16)
+    got = api.pack_proj_weights(dev(w)).view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    zz, nn, kk = np.meshgrid(np.arange(z), np.arange(n), np.arange(k), indexing="ij")
+    off = zz * n * k + ((nn // 16) * (k // 32) + kk // 32) * 512 + (((kk % 32) // 8) * 16 + nn % 16) * 8 + kk % 8
+    ref = np.empty(z * n * k, np.uint16)
+    ref[off.reshape(-1)] = w.reshape(-1)
+    assert np.array_equal(got, ref)
