@@ -45,19 +45,17 @@ struct ProjArgs {
 };
 
 // MT: 16-row tiles of A (rows <= 16 * MT); TPW: column tiles per wave; KS: waves sharing a column group
+// The body of one segment's workgroup (sg: its segment, bx: the workgroup's index in it).  s_red:
+// (KS - 1) * 64 * MT * TPW f32x4 of LDS; s_amax: [4][32] floats.
 template <int MT, int TPW, int KS>
-__global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
+__device__ __forceinline__ void proj_body(const ProjArgs& p, const ProjSeg& sg, int bx, f32x4* s_red,
+                                          float (*s_amax)[32]) {
   constexpr int kGroups = 4 / KS;               // column groups per workgroup
   constexpr int kCols = 16 * TPW * kGroups;     // columns per workgroup
-  __shared__ f32x4 s_red[KS > 1 ? (KS - 1) * 64 * MT * TPW : 1];
-  __shared__ float s_amax[4][32];               // fp8 epilogue: per wave, per row
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int z = blockIdx.y;
-  const bool s1 = (int)blockIdx.x >= p.seg[0].blocks;  // (uniform)
-  const ProjSeg sg = s1 ? p.seg[1] : p.seg[0];
-  const int bx = s1 ? (int)blockIdx.x - p.seg[0].blocks : (int)blockIdx.x;
   const int grp = wave / KS, ks = wave % KS;
   const int n0 = bx * kCols + grp * 16 * TPW;   // first column of this wave's tiles
   const int kg = lane >> 4, li = lane & 15;
@@ -242,13 +240,28 @@ __global__ __launch_bounds__(256) void proj_pack_kernel(const uint16_t* __restri
       *reinterpret_cast<const u32x4*>(w + (z * n + row) * (int64_t)k + kk);
 }
 
-template <int TPW, int KS>
+// Segment 0 runs the (TPW0, KS0) mapping, segment 1 the (TPW1, KS1) one: the fused query launch streams W^UQ
+// four waves to 16 columns (many workgroups) and W^IUQ one head of 128 columns per workgroup (its quantizing
+// epilogue needs the head in one workgroup).
+template <int MT, int TPW0, int KS0, int TPW1, int KS1>
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
+  constexpr int kRed0 = KS0 > 1 ? (KS0 - 1) * 64 * MT * TPW0 : 1;
+  constexpr int kRed1 = KS1 > 1 ? (KS1 - 1) * 64 * MT * TPW1 : 1;
+  __shared__ f32x4 s_red[kRed0 > kRed1 ? kRed0 : kRed1];
+  __shared__ float s_amax[4][32];  // fp8 epilogue: per wave, per row
+  if ((int)blockIdx.x < p.seg[0].blocks)  // (uniform)
+    proj_body<MT, TPW0, KS0>(p, p.seg[0], (int)blockIdx.x, s_red, s_amax);
+  else
+    proj_body<MT, TPW1, KS1>(p, p.seg[1], (int)blockIdx.x - p.seg[0].blocks, s_red, s_amax);
+}
+
+template <int TPW0, int KS0, int TPW1, int KS1>
 csa_status launch_proj(const ProjArgs& p, int z, hipStream_t stream) {
   dim3 grid(p.seg[0].blocks + p.seg[1].blocks, z);
   if (p.rows <= 16)
-    hipLaunchKernelGGL((proj_kernel<1, TPW, KS>), grid, dim3(kProjThreads), 0, stream, p);
+    hipLaunchKernelGGL((proj_kernel<1, TPW0, KS0, TPW1, KS1>), grid, dim3(kProjThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((proj_kernel<2, TPW, KS>), grid, dim3(kProjThreads), 0, stream, p);
+    hipLaunchKernelGGL((proj_kernel<2, TPW0, KS0, TPW1, KS1>), grid, dim3(kProjThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 
@@ -263,11 +276,11 @@ csa_status launch_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq,
   p.rows = rows;
   p.k = d_c;
   const int nq = n_h * c, ni = n_hI * cI;
-  p.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_uq), 0, nq, q, nq, 0, nullptr, kEpiBf16, nq / 128};
+  p.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_uq), 0, nq, q, nq, 0, nullptr, kEpiBf16, nq / 16};
   const int epi = qi_t == CSA_FP8_E4M3_ROWSCALE ? kEpiFp8Head : (qi_t == CSA_MXFP4_E8M0_B32 ? kEpiMxfp4 : kEpiBf16);
   const int64_t ldi = qi_t == CSA_MXFP4_E8M0_B32 ? ni / 2 : ni;  // bytes for the quantized forms
   p.seg[1] = ProjSeg{static_cast<const uint16_t*>(w_iuq), 0, ni, qi, ldi, 0, qi_scale, epi, ni / 128};
-  return launch_proj<2, 1>(p, 1, stream);
+  return launch_proj<1, 4, 2, 1>(p, 1, stream);
 }
 
 csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
@@ -282,7 +295,7 @@ csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w
   p1.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_g), (int64_t)d_g * per, d_g, mid, (int64_t)g * d_g, d_g, nullptr,
                       kEpiBf16, d_g / 16};
   p1.seg[1] = ProjSeg{nullptr, 0, 0, nullptr, 0, 0, nullptr, kEpiBf16, 0};
-  csa_status st = launch_proj<1, 4>(p1, g, stream);
+  csa_status st = launch_proj<1, 4, 1, 4>(p1, g, stream);
   if (st != CSA_OK) return st;
   ProjArgs p2;
   p2.a = static_cast<const uint16_t*>(mid);
@@ -292,7 +305,7 @@ csa_status launch_grouped_out_proj(const void* o, const void* w_g, const void* w
   p2.k = g * d_g;
   p2.seg[0] = ProjSeg{static_cast<const uint16_t*>(w_o), 0, d, out, d, 0, nullptr, kEpiBf16, d / 16};
   p2.seg[1] = ProjSeg{nullptr, 0, 0, nullptr, 0, 0, nullptr, kEpiBf16, 0};
-  return launch_proj<1, 4>(p2, 1, stream);
+  return launch_proj<1, 4, 1, 4>(p2, 1, stream);
 }
 
 csa_status launch_pack_proj_weights(const void* w, void* packed, int z, int n, int k, hipStream_t stream) {
