@@ -376,8 +376,8 @@ def main():
         if mixed:
             kv_job["out_scale"] = kv_scale[:, first:]
         if T == 1:
-            # decode: the block's KV entry and its indexer key (into the key cache) are computed inside the
-            # index launch, by the workgroups that need them first
+            # decode: the block's indexer key (into the key cache) is computed inside the index launch, by the
+            # workgroup that scores it first
             api.compress_index(None, st["cik_t"], cfg.m, c["row0_pos"], first, st["qi"], st["qi_scale"], st["w"],
                                st["ik"], st["ik_scale"], pos, fmt, scores=scores, bound=bound)
         else:
