@@ -278,3 +278,29 @@ def test_projection_validation(lib):
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1000, 7168, DUMMY, DUMMY, None) == 3    # d_g % 16
     assert g(DUMMY, DUMMY, DUMMY, 40, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 3
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1024, 7168, None, DUMMY, None) == 1
+
+
+def test_fused_decode_entry_validation(lib):
+    """csa_topk_compress and csa_append_index_paged reject bad arguments before any launch."""
+    tk = lib.csa_topk_compress
+
+    def t(**kw):
+        a = dict(st=0, B=4, n=262144, m=4, k=1024, ws=1 << 30, c=512, rows=8, row0=4 * 262144 - 8, first=262143,
+                 in_t=1, out=DUMMY, out_t=1)
+        a.update(kw)
+        return tk(DUMMY, a["st"], a["B"], a["n"], DUMMY, a["m"], a["k"], DUMMY, DUMMY, None, DUMMY, a["ws"], DUMMY,
+                  DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, a["c"], a["rows"], a["row0"], a["first"], a["in_t"], a["out"], None,
+                  a["out_t"], 0, None, None)
+
+    assert t(m=64) == 3                 # one 256-thread workgroup pools the entry
+    assert t(st=2) == 3                 # scores f32 or bf16
+    assert t(k=0) == 2
+    assert t(out=None) == 1
+    assert t(ws=0) == 4                 # the top-k workspace
+    assert t(row0=0) == 2               # the entry's rows outside the streams
+    ja = (_lib.AppendJob * 2)()
+    pg = _pages()
+    ai = lib.csa_append_index_paged
+    # no jobs described (null stream pointers): rejected before the index checks
+    assert ai(ja, None, 1, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, C.byref(pg), 2, 64, 128, 1000, DUMMY, 4, 2, DUMMY, 0,
+              None, None) in (1, 2)
