@@ -98,7 +98,8 @@ def host_inputs(cfg, seed):
 
 def _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data, ik_scale, hca_cache, hca_scale, prep, pos,
                  scores, bound, idx, out, hout, hca_ws, side, mixed):
-    """Pools, block table, state rings and the paged decode step.  Returns (step, index_only, visible)."""
+    """Pools, block table, state rings and the paged decode step.  Returns (step, parts, visible, scores):
+    parts(set) maps the step's launches to callables."""
     dev = pos.device
     B, N, R, m, mh, W = cfg.B, cfg.n_comp, cfg.rope_dims, cfg.m, cfg.m_hca, cfg.n_win
     P = a.page_tokens
@@ -187,14 +188,22 @@ def _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data, ik_scale
         pos.add_(1)   # the next step decodes the next token
         steps_done[0] += 1
 
-    def index_only(st):
-        api.index_paged(st["qi"], st["qi_scale"], st["w"], st["ik_pool"], st["iks_pool"], pg, pos, m, fmt, cap,
-                        scores=sc, bound=bnd)
+    # the step's launches one by one (timed back to back for the per-kernel figures)
+    def parts(st):
+        return {
+            "index": lambda: api.append_index_paged([st["kv_job"], st["ik_job"]], st["win_job"], st["qi"],
+                                                    st["qi_scale"], st["w"], st["ik_pool"], st["iks_pool"], pg, pos,
+                                                    m, fmt, cap, scores=sc, bound=bnd),
+            "topk": lambda: api.topk(sc, pos, m, cfg.k, idx=idx, bound=bnd),
+            "attend": lambda: api.attend_paged(st["q"], kv_pool, idx, win_ring, st["sink"], pos, pg, m, R, cfg.scale,
+                                               cap, cfg.eps, cfg.rope_base, out=out, kv_prepared=2,
+                                               comp_scale=kv_spool),
+        }
 
     def visible():
         return int(min(int(pos[0].item()) // m, cap))
 
-    return step, index_only, visible
+    return step, parts, visible, sc
 
 
 # Pro / Flash projection shapes ("【论文解读】DeepSeek-V4", section 三(二): d_c, g, d_g, d)
@@ -352,7 +361,7 @@ def main():
         if prefill:
             print("--paged runs decode workloads only", file=sys.stderr)
             sys.exit(2)
-        step, index_only_paged, vis_now = _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data,
+        step, parts_paged, vis_now, scores_paged = _paged_setup(a, cfg, api, torch, sets, kv_cache, kv_scale, ik_data,
                                                        ik_scale, hca_cache, hca_scale, prep, pos, scores, bound, idx,
                                                        out, hout, hca_ws, side, mixed)
 
@@ -439,51 +448,113 @@ def main():
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / a.steps
-    # csa_index launch duration: HIP events recorded on the launch stream around back-to-back index
-    # launches over the same input rotation, so that the average is the kernel's own time
-    def index_only(st):
+    # The step's launches one by one: each is timed by HIP events recorded on the launch stream around
+    # back-to-back launches over the same input rotation, so that the average is the kernel's own time.
+    def step_parts(st):
         if a.paged:
-            index_only_paged(st)
-            return
-        api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m, fmt, scores=scores,
-                  bound=bound)
+            return parts_paged(st)
+        c = st["cik"]
+        kv_job = dict(st["ckv_t"], out=kv_cache[:, first:], out_batch_stride=N, prep=prep, **cache_fmt)
+        if mixed:
+            kv_job["out_scale"] = kv_scale[:, first:]
+        p = {}
+        if T == 1:   # the step's own launches: the key-only compress + index, then top-k with the KV entry
+            p["index"] = lambda: api.compress_index(None, st["cik_t"], cfg.m, c["row0_pos"], first, st["qi"],
+                                                    st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, fmt,
+                                                    scores=scores, bound=bound)
+            p["topk"] = lambda: api.topk_compress(scores, pos, cfg.m, cfg.k, kv_job, c["row0_pos"], first, idx=idx,
+                                                  bound=bound)
+        else:
+            p["index"] = lambda: api.index(st["qi"], st["qi_scale"], st["w"], st["ik"], st["ik_scale"], pos, cfg.m,
+                                           fmt, scores=scores, bound=bound)
+            p["topk"] = lambda: api.topk(scores, pos, cfg.m, cfg.k, idx=idx, bound=bound)
+        p["attend"] = lambda: api.attend(st["q"], kv_cache, idx, st["pwin"], st["sink"], pos, cfg.m, cfg.n_win,
+                                         cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base, out=out,
+                                         kv_prepared=csa_mode, comp_scale=kv_scale)
+        if cfg.with_hca:
+            p["hca_attend"] = lambda: api.hca_attend(st["hq"], hca_cache, st["phwin"], st["hsink"], pos, cfg.m_hca,
+                                                     cfg.n_win, cfg.rope_dims, cfg.scale, cfg.eps, cfg.rope_base,
+                                                     out=hout, ws=hca_ws, kv_prepared=2, comp_scale=hca_scale)
+        return p
 
-    for i in range(NSETS):
-        index_only(sets[i])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(a.steps):
-        index_only(sets[i % NSETS])
-    e1.record()
-    torch.cuda.synchronize()
-    idx_ms = e0.elapsed_time(e1) / a.steps
+    def time_part(name):
+        for i in range(NSETS):
+            step_parts(sets[i])[name]()
+        calls = [step_parts(sets[i % NSETS])[name] for i in range(a.steps)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for f in calls:
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
 
-    # algorithmic bytes of one csa_index launch: every K^I row (+ its scales) read once, the queries /
-    # weights read once per query row, one score (float32 or bf16) written per (row, entry)
+    sc_t = scores_paged if a.paged else scores
+    Nsc = sc_t.shape[2]
+    n_read = vis_now() if a.paged else N   # paged: the visible entries of the current positions (all read)
+    # index: every K^I row (+ its scales) read once, the queries / weights read once per query row; the
+    # score write is booked to the selector, which reads it back
     row_bytes = {"bf16": 2 * cfg.cI, "fp8": cfg.cI + 4, "mxfp4": cfg.cI // 2 + cfg.cI // 32}[fmt]
     q_bytes = row_bytes * cfg.HI + 4 * cfg.HI
-    n_read = vis_now() if a.paged else N   # paged: the visible entries of the current positions (all read)
-    idx_bytes = B * (n_read * row_bytes + T * q_bytes + T * scores.shape[2] * scores.element_size())
-    # algorithmic FLOPs: 2 HI cI per visible (row, entry) pair
+    idx_bytes = B * (n_read * row_bytes + T * q_bytes)
+    score_bytes = B * T * Nsc * sc_t.element_size()
     pairs = sum(min((cfg.pos0 + r) // cfg.m, N) for r in range(T)) * B
     idx_flops = 2 * cfg.HI * cfg.cI * pairs
+    # top-k: the scores read once, the index list written once
+    topk_bytes = score_bytes + B * T * cfg.k * 4
+    # attention: every selected / visible entry row and window row read once per query row, the queries read
+    # and the outputs written once, the index list read once; FLOPs 4 c per (row, head, entry)
+    comp_row = (cfg.c + cfg.rope_dims + 4) if mixed else 2 * cfg.c
+    win_vis = [min(cfg.n_win, cfg.pos0 + r + 1) for r in range(T)]
+    sel = [min(cfg.k, min((cfg.pos0 + r) // cfg.m, N)) for r in range(T)]
+    att_bytes = B * sum(sel[r] * comp_row + win_vis[r] * 2 * cfg.c + 4 * cfg.H * cfg.c + 4 * cfg.k
+                        for r in range(T))
+    att_flops = B * sum(4 * cfg.c * cfg.H * (sel[r] + win_vis[r]) for r in range(T))
+    if cfg.with_hca:
+        hvis = [min((cfg.pos0 + r) // cfg.m_hca, cfg.n_hca) for r in range(T)]
+        hcomp_row = (cfg.c + cfg.rope_dims + 4) if mixed else 2 * cfg.c
+        hca_bytes = B * sum(hvis[r] * hcomp_row + win_vis[r] * 2 * cfg.c + 4 * cfg.H * cfg.c for r in range(T))
+        hca_flops = B * sum(4 * cfg.c * cfg.H * (hvis[r] + win_vis[r]) for r in range(T))
+    bf16_peak = MFMA_PEAK_TFLOPS["bf16"]
+
+    def entry(name, ms, nbytes, flops, bound):
+        e = {"kernel": name, "avg_us": round(ms * 1e3, 2), "bound": bound,
+             "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+        if bound == "hbm":
+            e.update(achieved=nbytes / (ms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+        else:
+            pk = MFMA_PEAK_TFLOPS[fmt] if name.startswith("csa_index") else bf16_peak
+            e.update(achieved=flops / (ms * 1e-3) / 1e12, peak=pk, unit="TFLOP/s")
+        e["frac"] = e["achieved"] / e["peak"]
+        return e
+
+    idx_name = ("csa_append_index_paged" if a.paged else "csa_compress_index (indexer key only)") if T == 1 \
+        else "csa_index (tiled prefill)"
+    idx_ms = time_part("index")
+    kernels = [
+        entry(idx_name, idx_ms, idx_bytes, idx_flops, "mfma" if prefill else "hbm"),
+        entry("csa_topk" if (a.paged or prefill) else "csa_topk_compress (with the KV entry)", time_part("topk"),
+              topk_bytes, 0, "hbm"),
+        entry(("csa_attend_paged" if a.paged else "csa_attend") + " + combine", time_part("attend"), att_bytes,
+              att_flops, "mfma" if prefill else "hbm"),
+    ]
+    if cfg.with_hca and not a.paged:
+        kernels.append(entry("hca_attend", time_part("hca_attend"), hca_bytes, hca_flops, "mfma" if prefill else "hbm"))
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
-    if os.path.exists(tpath) and not a.paged:
+    if os.path.exists(tpath) and not a.paged and not a.proj:
         t = json.load(open(tpath))
         if t.get("source_hash") == source_hash("index.hip") and t.get("index_scores", "f32") == a.scores:
             traffic = t.get("hbm_bytes_per_launch")
-    if prefill:   # a dense contraction with K^I reused across 4,096 query rows: MFMA-bound
-        achieved = idx_flops / (idx_ms * 1e-3) / 1e12
-        roofline = {"kernel": "csa_index", "bound": "mfma", "achieved": achieved, "peak": MFMA_PEAK_TFLOPS[fmt],
-                    "unit": "TFLOP/s", "frac": achieved / MFMA_PEAK_TFLOPS[fmt], "traffic": traffic,
-                    "algorithmic_flops_per_launch": idx_flops, "avg_launch_ms": idx_ms}
+    k0 = kernels[0]
+    roofline = {"kernel": idx_name, "bound": k0["bound"], "achieved": k0["achieved"], "peak": k0["peak"],
+                "unit": k0["unit"], "frac": k0["frac"], "traffic": traffic, "avg_launch_ms": idx_ms}
+    if prefill:
+        roofline["algorithmic_flops_per_launch"] = idx_flops
     else:
-        achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-        roofline = {"kernel": "csa_index_paged" if a.paged else "csa_index", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                    "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": idx_ms}
+        roofline["algorithmic_bytes_per_launch"] = idx_bytes
+        roofline["score_write_bytes_per_launch"] = score_bytes
     if cfg.name == configs.C3.name:
         metric = METRIC
     elif prefill:
@@ -513,6 +584,7 @@ def main():
                    if a.paged else "contiguous",
                    "input_sets_rotated": NSETS},
         "roofline": roofline,
+        "kernels": kernels,
         "setup_s": round(t_setup, 1),
         "launch": "eager" if a.eager else "hip_graph (one graph per rotated input set)",
     }

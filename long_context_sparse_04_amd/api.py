@@ -238,7 +238,10 @@ def topk_compress(scores, pos0, m, k, p_kv, row0_pos, first_entry, idx=None, ws=
         ws = workspace(nb, scores.device, "topk", zero=True)
     ca = p_kv["ca"]
     out = p_kv["out"]
-    out_fmt = p_kv.get("out_fmt") or _TORCH_FMT[out.dtype] if out.dtype != torch.uint8 else p_kv.get("out_fmt")
+    if out.dtype == torch.uint8:   # uint8 rows: the prepared fp8 + bf16 RoPE format, as compress_index infers it
+        out_fmt = "fp8rope"
+    else:
+        out_fmt = p_kv.get("out_fmt") or _TORCH_FMT[out.dtype]
     prep = p_kv.get("prep")
     st = lib.csa_topk_compress(_ptr(scores), FMT[_TORCH_FMT[scores.dtype]], B, N, _ptr(pos0), m, k, _ptr(bound),
                                _ptr(idx), None, _ptr(ws), _ws_bytes(ws), _ptr(ca), _ptr(p_kv.get("cb")), _ptr(p_kv["za"]),

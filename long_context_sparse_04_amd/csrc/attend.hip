@@ -226,18 +226,7 @@ CSA_DEV void static_for(F&& f) {
 // Entry-major LDS rows of C bf16 without padding; 16-byte chunk c of row e is stored at
 // chunk position c ^ swz_key(e & 15), which spreads the rows an MFMA operand read touches
 // over the LDS banks.
-#ifndef CSA_SWZ_VARIANT
-#define CSA_SWZ_VARIANT 0
-#endif
-CSA_DEV constexpr int swz_key(int e) {
-#if CSA_SWZ_VARIANT == 1
-  return ((e & 7) << 1) | ((e >> 3) & 1);
-#elif CSA_SWZ_VARIANT == 2
-  return ((e & 3) << 1) | ((e >> 2) & 1) | (e & 8);
-#else
-  return e & 15;
-#endif
-}
+CSA_DEV constexpr int swz_key(int e) { return e & 15; }
 template <int C>
 CSA_DEV int swz(int e, int c) { return c ^ swz_key(e & 15); }
 

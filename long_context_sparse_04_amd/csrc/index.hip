@@ -125,19 +125,13 @@ struct ScoreOut {
 // formats stay small enough for three (bf16) or four (fp8) workgroups per CU.
 template <int FMT>
 struct Ring;
-#ifndef CSA_IDX_RING_BF16
-#define CSA_IDX_RING_BF16 2
-#endif
-#ifndef CSA_IDX_RING_FP8
-#define CSA_IDX_RING_FP8 3
-#endif
 template <>
 struct Ring<CSA_BF16> {
-  static constexpr int kTiles = CSA_IDX_RING_BF16;
+  static constexpr int kTiles = 2;
 };
 template <>
 struct Ring<CSA_FP8_E4M3_ROWSCALE> {
-  static constexpr int kTiles = CSA_IDX_RING_FP8;
+  static constexpr int kTiles = 3;
 };
 template <>
 struct Ring<CSA_MXFP4_E8M0_B32> {
