@@ -336,9 +336,9 @@ def main():
         if cfg.with_hca:
             st["phwin"] = api.prepare_kv(st["hwin"], prep, pos_base=pos, pos_first=-(cfg.n_win - 1))
     scores = torch.empty((B, T, N), dtype=torch.bfloat16 if a.scores == "bf16" else torch.float32, device=dev)
-    # decode rows: the indexer also writes the selector's lower-bound keys (two per 256 entries), so top-k
-    # runs as two kernels; the prefill index kernel does not make them (top-k takes its per-row path)
-    bound = api.bound_keys(B, T, N, dev) if T == 1 else None
+    # the indexer also writes the selector's lower-bound keys (two per set of 256 entries, or of 32 for caches
+    # of up to 65,536 entries): decode rows then take the one-launch selection, prefill rows one pruning pass
+    bound = api.bound_keys(B, T, N, dev)
     idx = torch.empty((B, T, cfg.k), dtype=torch.int32, device=dev)
     out = torch.empty((B, T, cfg.H, cfg.c), dtype=torch.bfloat16, device=dev)
     hout = torch.empty_like(out) if cfg.with_hca else None

@@ -172,14 +172,12 @@ csa_status csa_prepare_kv(const void* in, int64_t in_batch_stride, void* out, vo
  *   bound   : NULL, or uint32 [B][T][csa_index_bound_keys(n_max)], 8-byte aligned:
  *             for csa_topk, keys of the two largest visible scores (as stored, in
  *             score_t) of each bound set (order-preserving keys, 0 where a set has
- *             fewer), at 2 j, 2 j + 1 for set j.  The sets split each run of 256
- *             entries (run u: entries 256 u .. 256 u + 255): the whole run when
- *             n_max > 65536, otherwise its four sets of entries e with e mod 64 in
- *             [16 r, 16 r + 16), r = 0..3 (set 4 u + r).  Their
- *             K-th largest never exceeds a row's K-th largest score, so csa_topk
- *             can skip its threshold search.  Only for the per-row kernels: with
- *             CSA_F32, or CSA_BF16 with T >= 8 and HI = 64 (the tiled prefill
- *             kernel), a non-NULL bound is CSA_ERR_UNSUPPORTED.
+ *             fewer), two per set.  A set is 256 entries when n_max > 65536, 32
+ *             entries otherwise (which entries form a set, and where its keys sit,
+ *             differ between the decode and the tiled prefill kernels; only the
+ *             keys' values matter).  Their K-th largest never exceeds a row's K-th
+ *             largest score, so csa_topk can skip its threshold search.  With
+ *             CSA_F32 a non-NULL bound is CSA_ERR_UNSUPPORTED.
  * All pointers 16-byte aligned (the MXFP4 q_scale at least 4-byte aligned).
  * Products run on MFMA with float32 accumulation for BF16 / FP8 / MXFP4 (row
  * scales are applied to the float32 dot products; MXFP4 block scales inside

@@ -165,8 +165,8 @@ csa_status csa_index(const void* q, const void* q_scale, const float* w, const v
   const csa_status st = check_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, empty);
   if (st != CSA_OK) return st;
   if (score_t != CSA_F32 && score_t != CSA_BF16) return CSA_ERR_UNSUPPORTED;
-  // bound keys come from the per-row decode kernels only
-  if (bound && (qk_t == CSA_F32 || use_prefill_index(qk_t, T, HI))) return CSA_ERR_UNSUPPORTED;
+  // bound keys come from the MFMA kernels (per-row decode and tiled prefill)
+  if (bound && qk_t == CSA_F32) return CSA_ERR_UNSUPPORTED;
   if (empty) return CSA_OK;
   if (bound && (reinterpret_cast<uintptr_t>(bound) & 7)) return CSA_ERR_SHAPE;
   return launch_index(q, q_scale, w, k, k_scale, B, T, HI, cI, n_max, pos0, m, qk_t, scores, score_t, bound,
@@ -254,11 +254,12 @@ size_t csa_attend_workspace_bytes(int B, int T, int H, int c, int k, int n_win) 
   return attend_workspace_bytes(0, B, T, H, c, (int64_t)k, n_win);
 }
 
-csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
-                      const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T,
-                      int H, int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
-                      float scale, float eps, float rope_base, int kv_t, int comp_t, int kv_prepared, void* out,
-                      int out_t, void* workspace, size_t ws_bytes, void* stream) {
+// csa_attend's checks, shared by csa_attend_noalloc; sets *need to the workspace bytes the call uses
+static csa_status check_csa_attend(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                                   const void* win_kv, const float* sink, int B, int T, int H, int c, int rope_dims,
+                                   int k, int n_win, int64_t n_max, const int64_t* pos0, int m, int kv_t, int comp_t,
+                                   int kv_prepared, const void* out, int out_t, size_t* need) {
+  *need = 0;
   csa_status st = check_attend(kv_t, out_t, B, T, H, c, rope_dims, n_win, m);
   if (st != CSA_OK) return st;
   st = check_comp_t(kv_t, comp_t, kv_prepared, c, rope_dims);
@@ -268,7 +269,19 @@ csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scal
   if (B == 0 || T == 0) return CSA_OK;
   if (!q || !idx || !win_kv || !sink || !pos0 || !out || (n_max > 0 && !comp_kv)) return CSA_ERR_NULL;
   if (comp_t != kv_t && n_max > 0 && !comp_scale) return CSA_ERR_NULL;
-  const size_t need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
+  *need = csa_attend_workspace_bytes(B, T, H, c, k, n_win);
+  return CSA_OK;
+}
+
+csa_status csa_attend(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                      const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv, int B, int T,
+                      int H, int c, int rope_dims, int k, int n_win, int64_t n_max, const int64_t* pos0, int m,
+                      float scale, float eps, float rope_base, int kv_t, int comp_t, int kv_prepared, void* out,
+                      int out_t, void* workspace, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  const csa_status st = check_csa_attend(q, comp_kv, comp_scale, idx, win_kv, sink, B, T, H, c, rope_dims, k, n_win,
+                                         n_max, pos0, m, kv_t, comp_t, kv_prepared, out, out_t, &need);
+  if (st != CSA_OK || B == 0 || T == 0) return st;
   if (need > 0 && (!workspace || ws_bytes < need)) return CSA_ERR_WORKSPACE;
   return launch_attend(0, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, idx, win_kv, sink, gamma_q, gamma_kv, B, T, H, c,
                        rope_dims, k, n_win, n_max, pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,

@@ -98,6 +98,22 @@ CSA_DEV void row16_top2(uint32_t& t1, uint32_t& t2) {
   top2_merge(t1, t2, dpp_u32<0x124>(t1), dpp_u32<0x124>(t2));  // row_ror:4
   top2_merge(t1, t2, dpp_u32<0x128>(t1), dpp_u32<0x128>(t2));  // row_ror:8
 }
+// Every lane ends with the two largest keys of its 8-lane half row's disjoint lane pairs: quad exchanges,
+// then the half-row mirror (lane i of a half row with lane 7 - i, i.e. quad 0 with quad 1).
+CSA_DEV void half_row_top2(uint32_t& t1, uint32_t& t2) {
+  top2_merge(t1, t2, dpp_u32<0xB1>(t1), dpp_u32<0xB1>(t2));    // quad_perm [1,0,3,2]
+  top2_merge(t1, t2, dpp_u32<0x4E>(t1), dpp_u32<0x4E>(t2));    // quad_perm [2,3,0,1]
+  top2_merge(t1, t2, dpp_u32<0x141>(t1), dpp_u32<0x141>(t2));  // row_half_mirror
+}
+// Every lane ends with the two largest keys of its 32-lane half wave's disjoint lane pairs: the rows'
+// results, then the row-pair swap.
+CSA_DEV void half_wave_top2(uint32_t& t1, uint32_t& t2) {
+  row16_top2(t1, t2);
+  const auto a = __builtin_amdgcn_permlane16_swap(t1, t1, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(t2, t2, false, false);
+  t1 = a[0]; t2 = c[0];
+  top2_merge(t1, t2, a[1], c[1]);
+}
 // Every lane ends with the two largest keys of the wave's 64 disjoint lane pairs: the rows' results,
 // then the gfx950 row-pair and half-wave swaps.
 CSA_DEV void wave_top2(uint32_t& t1, uint32_t& t2) {

@@ -31,11 +31,13 @@ constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 16;                      // 4 waves x 16 tiles x 16 entries = 1024 entries / WG
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 16;
 
-// Bound-key sets of a wave's 256-entry run: the whole run for caches of more than kFineBoundMax
-// entries, otherwise its four interleaved 64-entry sets {e : e mod 64 in [16 r, 16 r + 16)} (the
-// entries one 16-lane row of the wave writes), so that a short cache still holds enough keys.
+// Bound-key sets: two keys per 256 entries for caches of more than kFineBoundMax entries, otherwise two
+// per 32 entries, so that a short cache still holds enough keys (2k for k up to n_max / 32).  The decode
+// kernel's sets of a wave's 256-entry run are the whole run, or its eight interleaved 32-entry sets
+// {e : e mod 64 in [8 r, 8 r + 8)} (the entries one half of a 16-lane row writes); the tiled prefill kernel
+// takes each 64-entry tile's halves (fine) or 4 tiles (coarse).  The selector uses only the keys' values.
 constexpr int64_t kFineBoundMax = 65536;
-__host__ __device__ inline int bound_sets(int64_t n_max) { return n_max <= kFineBoundMax ? 4 : 1; }
+__host__ __device__ inline int bound_sets(int64_t n_max) { return n_max <= kFineBoundMax ? 8 : 1; }
 __host__ __device__ inline int64_t bound_keys_per_row(int64_t n_max) {
   return 2 * kWaves * bound_sets(n_max) * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG);
 }
@@ -489,18 +491,18 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     }
   }
   // Lower-bound keys for the selector: the two largest visible scores of each of the wave's bound sets
-  // (the whole wave, or each 16-lane row: see bound_sets).  They are scores of distinct visible entries,
+  // (the whole wave, or each half of a 16-lane row: see bound_sets).  They are scores of distinct visible entries,
   // so the K-th largest key over a row's bound keys never exceeds the row's K-th largest score key.
   if (bound) {
     const int sets = bound_sets(n_max);
     const int64_t nbw = bound_keys_per_row(n_max);
-    if (sets == 4) {
-      row16_top2(top1, top2);
+    if (sets == 8) {
+      half_row_top2(top1, top2);
     } else {
       wave_top2(top1, top2);
     }
-    if ((lane & 15) == 0 && (sets == 4 || lane == 0)) {
-      uint32_t* dst = bound + (int64_t)row * nbw + (((int64_t)blockIdx.x * kWaves + wave) * sets + (lane >> 4)) * 2;
+    if ((lane & 7) == 0 && (sets == 8 || lane == 0)) {
+      uint32_t* dst = bound + (int64_t)row * nbw + (((int64_t)blockIdx.x * kWaves + wave) * sets + (lane >> 3)) * 2;
       dst[0] = top1;
       dst[1] = top2;
     }
@@ -526,7 +528,7 @@ constexpr int kPDmaPerWave = kPTile * kPRowBytes / 1024 / kWaves;  // 1 KB per D
 template <int NT>
 __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kI, int T,
-    int64_t n_max, const int64_t* __restrict__ pos0, int m, ScoreOut so) {
+    int64_t n_max, const int64_t* __restrict__ pos0, int m, ScoreOut so, uint32_t* __restrict__ bound) {
   constexpr int HI = NT * 16;
   __shared__ __align__(16) uint8_t s_k[2][kPTile * kPRowBytes];
   const int lane = threadIdx.x & 63;
@@ -578,6 +580,14 @@ __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
   const int64_t vis_max = visible_entries(pos0[b] + r_last, m, n_max);
   const int ntiles = (int)((vis_max + kPTile - 1) / kPTile);
 
+  // bound keys (optional): the two largest visible score keys of each 32-entry half tile (caches of up to
+  // kFineBoundMax entries), or of each run of 4 tiles (256 entries); sets past the computed tiles get 0
+  const bool fine = bound_sets(n_max) > 1;
+  const int64_t nbw = bound_keys_per_row(n_max);
+  uint32_t bt1[kPRowsPerWave], bt2[kPRowsPerWave];  // coarse sets: the lane's running top-2 of each row
+#pragma unroll
+  for (int rr = 0; rr < kPRowsPerWave; ++rr) bt1[rr] = bt2[rr] = 0u;
+
   if (ntiles > 0) issue_tile(0, 0);
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
@@ -620,12 +630,44 @@ __global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
       const bool odd = gl & 1;
       const float val = (odd ? k1 : k0) + __shfl_xor(odd ? k0 : k1, 16, 64);
       const int64_t eo = (int64_t)ti * kPTile + lane;
-      if (live[rr] && eo < n_max) {
-        const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
-        so.store(row * n_max + eo, eo < vis[rr] ? val : -INFINITY);
+      const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
+      if (live[rr] && eo < n_max) so.store(row * n_max + eo, eo < vis[rr] ? val : -INFINITY);
+      if (bound) {   // (wave-uniform branches)
+        const uint32_t key = (eo < vis[rr]) ? score_key(so.stored(val)) : 0u;
+        if (fine) {
+          uint32_t t1 = key, t2 = 0u;
+          half_wave_top2(t1, t2);
+          if (live[rr] && (lane & 31) == 0) {
+            uint32_t* dst = bound + row * nbw + (2 * (int64_t)ti + (lane >> 5)) * 2;
+            dst[0] = t1;
+            dst[1] = t2;
+          }
+        } else {
+          bt2[rr] = max(bt2[rr], min(bt1[rr], key));
+          bt1[rr] = max(bt1[rr], key);
+          if ((ti & 3) == 3 || ti == ntiles - 1) {
+            uint32_t t1 = bt1[rr], t2 = bt2[rr];
+            wave_top2(t1, t2);
+            if (live[rr] && lane == 0) {
+              uint32_t* dst = bound + row * nbw + (int64_t)(ti >> 2) * 2;
+              dst[0] = t1;
+              dst[1] = t2;
+            }
+            bt1[rr] = bt2[rr] = 0u;
+          }
+        }
       }
     }
     __syncthreads();  // the buffer is refilled by the next-but-one tile
+  }
+  if (bound) {   // sets past the computed tiles hold no visible entry
+    const int64_t done = fine ? 2 * (int64_t)ntiles : ((int64_t)ntiles + 3) / 4;
+#pragma unroll
+    for (int rr = 0; rr < kPRowsPerWave; ++rr) {
+      if (!live[rr]) continue;
+      const int64_t row = (int64_t)b * T + r_first + wave * kPRowsPerWave + rr;
+      for (int64_t j = 2 * done + lane; j < nbw; j += 64) bound[row * nbw + j] = 0u;
+    }
   }
   // entries past every row's visibility
 #pragma unroll
@@ -701,10 +743,10 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
     return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
   }
   if (use_prefill_index(FMT, T, HI)) {  // many query rows: the tiled contraction
-    if (bound || fuse) return CSA_ERR_UNSUPPORTED;
+    if (fuse) return CSA_ERR_UNSUPPORTED;
     dim3 grid(ceil_div(T, kPRows), B);
     hipLaunchKernelGGL((index_prefill_bf16_kernel<4>), grid, dim3(kWaves * 64), 0, stream, (const uint8_t*)q, w,
-                       (const uint8_t*)k, T, n_max, pos0, m, so);
+                       (const uint8_t*)k, T, n_max, pos0, m, so, bound);
     return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
   }
   dim3 grid(ceil_div(n_max, kEntriesPerWG), B * T);

@@ -249,6 +249,79 @@ CSA_DEV void trivial_row(const ScoreRow& srow, int V, int k, int nt, int32_t* or
 }
 
 // ------------------------------------------------------------------ row path
+// Exact selection of one row by one workgroup of NT threads over all V visible keys: three digit passes
+// (11, 11 and 10 bits) find the K-th key K*, then an ordered compaction emits every key > K* and the
+// lowest-index keys == K*.  keys (LDS, nullable): the row's keys are cached there by the first pass.
+template <int NT>
+CSA_DEV void row_select(const ScoreRow& srow, int V, int K, int k, int32_t* __restrict__ orow,
+                        float* __restrict__ vrow, uint32_t* hist, uint32_t* keys, uint32_t* s_w, int* s_sel) {
+  const int tid = threadIdx.x;
+  auto key_at = [&](int i) -> uint32_t { return keys ? keys[i] : srow.key(i); };
+
+  // digit 0: bits 31..21
+  for (int j = tid; j < kBins; j += NT) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += NT) {
+    uint32_t kk = srow.key(i);
+    if (keys) keys[i] = kk;
+    atomicAdd(&hist[kk >> 21], 1u);
+  }
+  __syncthreads();
+  select_digit<NT, kBins>(hist, K, s_w, s_sel);
+  const uint32_t d0 = s_sel[0];
+  int need = K - s_sel[1];
+  __syncthreads();
+
+  // digit 1: bits 20..10 among keys with digit 0 == d0
+  for (int j = tid; j < kBins; j += NT) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += NT) {
+    uint32_t kk = key_at(i);
+    if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<NT, kBins>(hist, need, s_w, s_sel);
+  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];  // top 22 bits
+  need -= s_sel[1];
+  __syncthreads();
+
+  // digit 2: bits 9..0 among keys with top 22 bits == p1
+  for (int j = tid; j < kBins; j += NT) hist[j] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += NT) {
+    uint32_t kk = key_at(i);
+    if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  select_digit<NT, 1024>(hist, need, s_w, s_sel);
+  const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
+  const int ties = need - s_sel[1];  // keys == K* to take, lowest indices first
+  __syncthreads();
+
+  // ordered compaction
+  int out_base = 0, tie_base = 0;
+  for (int c0 = 0; c0 < V && out_base < K; c0 += NT) {
+    const int i = c0 + tid;
+    uint32_t kk = i < V ? key_at(i) : 0u;
+    const bool eq = (i < V) && kk == kstar;
+    int eq_tot;
+    int eq_rank = tie_base + block_flag_scan<NT>(eq, s_w, eq_tot);
+    const bool sel = (i < V) && (kk > kstar || (eq && eq_rank < ties));
+    int sel_tot;
+    int pos = out_base + block_flag_scan<NT>(sel, s_w, sel_tot);
+    if (sel) {
+      orow[pos] = i;
+      if (vrow) vrow[pos] = key_to_score(kk);
+    }
+    out_base += sel_tot;
+    tie_base += eq_tot;
+  }
+  for (int j = K + tid; j < k; j += NT) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
+}
+
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __restrict__ scores, int sbf16, int T,
                                                                int64_t n_max, const int64_t* __restrict__ pos0,
                                                                int m, int k, int32_t* __restrict__ idx,
@@ -259,7 +332,6 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
   __shared__ uint32_t s_w[2 * kRowThreads / 64];
   __shared__ int s_sel[2];
 
-  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int b = row / T;
   const int r = row - b * T;
@@ -271,77 +343,10 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
   float* vrow = vals ? vals + (int64_t)row * k : nullptr;
 
   if (K == V) {  // everything visible is selected (also covers V == 0)
-    for (int j = tid; j < k; j += kRowThreads) {
-      orow[j] = j < V ? j : -1;
-      if (vrow) vrow[j] = j < V ? key_to_score(srow.key(j)) : -INFINITY;
-    }
+    trivial_row(srow, V, k, kRowThreads, orow, vrow);
     return;
   }
-
-  auto key_at = [&](int i) -> uint32_t { return cache_keys ? keys[i] : srow.key(i); };
-
-  // digit 0: bits 31..21
-  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
-  __syncthreads();
-  for (int i = tid; i < V; i += kRowThreads) {
-    uint32_t kk = srow.key(i);
-    if (cache_keys) keys[i] = kk;
-    atomicAdd(&hist[kk >> 21], 1u);
-  }
-  __syncthreads();
-  select_digit<kRowThreads, kBins>(hist, K, s_w, s_sel);
-  const uint32_t d0 = s_sel[0];
-  int need = K - s_sel[1];
-  __syncthreads();
-
-  // digit 1: bits 20..10 among keys with digit 0 == d0
-  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
-  __syncthreads();
-  for (int i = tid; i < V; i += kRowThreads) {
-    uint32_t kk = key_at(i);
-    if ((kk >> 21) == d0) atomicAdd(&hist[(kk >> 10) & 0x7FFu], 1u);
-  }
-  __syncthreads();
-  select_digit<kRowThreads, kBins>(hist, need, s_w, s_sel);
-  const uint32_t p1 = (d0 << 11) | (uint32_t)s_sel[0];  // top 22 bits
-  need -= s_sel[1];
-  __syncthreads();
-
-  // digit 2: bits 9..0 among keys with top 22 bits == p1
-  for (int j = tid; j < kBins; j += kRowThreads) hist[j] = 0;
-  __syncthreads();
-  for (int i = tid; i < V; i += kRowThreads) {
-    uint32_t kk = key_at(i);
-    if ((kk >> 10) == p1) atomicAdd(&hist[kk & 0x3FFu], 1u);
-  }
-  __syncthreads();
-  select_digit<kRowThreads, 1024>(hist, need, s_w, s_sel);
-  const uint32_t kstar = (p1 << 10) | (uint32_t)s_sel[0];
-  const int ties = need - s_sel[1];  // keys == K* to take, lowest indices first
-  __syncthreads();
-
-  // ordered compaction
-  int out_base = 0, tie_base = 0;
-  for (int c0 = 0; c0 < V && out_base < K; c0 += kRowThreads) {
-    const int i = c0 + tid;
-    uint32_t kk = i < V ? key_at(i) : 0u;
-    const bool eq = (i < V) && kk == kstar;
-    int eq_tot;
-    int eq_rank = tie_base + block_flag_scan<kRowThreads>(eq, s_w, eq_tot);
-    const bool sel = (i < V) && (kk > kstar || (eq && eq_rank < ties));
-    int sel_tot;
-    int pos = out_base + block_flag_scan<kRowThreads>(sel, s_w, sel_tot);
-    if (sel) {
-      orow[pos] = i;
-      if (vrow) vrow[pos] = key_to_score(kk);
-    }
-    out_base += sel_tot;
-    tie_base += eq_tot;
-  }
-  for (int j = K + tid; j < k; j += kRowThreads) {
-    orow[j] = -1;
-    if (vrow) vrow[j] = -INFINITY;
-  }
+  row_select<kRowThreads>(srow, V, K, k, orow, vrow, hist, cache_keys ? keys : nullptr, s_w, s_sel);
 }
 
 // ------------------------------------------------------------------ split path
@@ -973,6 +978,182 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
              true, orow, vrow, L);
 }
 
+// ------------------------------------------------------------------ row path with bound keys
+// Many rows (prefill) with the indexer's bound keys: one workgroup per row, no cross-workgroup work.
+// tau (the K-th largest bound key with 22 bits resolved, as in topk_bound_kernel) never exceeds the
+// row's K-th largest key, so one streaming pass over the row keeps every key that can be selected: each
+// thread takes kRBPer consecutive keys of a chunk and one block scan writes the chunk's candidates into
+// LDS in index order.  The K-th key is then resolved among the candidates alone and the ascending list
+// written from them.  A row whose bound is unusable (fewer than K real keys) or whose candidates overflow
+// the LDS buffer takes the full three-pass selection over all its keys, so the result is exact for any bound.
+constexpr int kRBThreads = 512;
+constexpr int kRBPer = 16;                          // consecutive keys per thread and chunk
+constexpr int kRBChunk = kRBThreads * kRBPer;       // 8192 keys per chunk
+constexpr int kRBCap = 4096;                        // candidates held in LDS
+constexpr int kRBKeys = 8;                          // bound keys per thread (registers): up to 4096 per row
+
+__global__ __launch_bounds__(kRBThreads) void topk_rowbound_kernel(
+    const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m,
+    int k, const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals) {
+  __shared__ __align__(16) Cand s_c[kRBCap];
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_w[2 * kRBThreads / 64];
+  __shared__ uint32_t s_mm[2 * kRBThreads / 64];
+  __shared__ int s_sel[2];
+  __shared__ uint32_t s_nz;
+  constexpr int NT = kRBThreads;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
+  int32_t* orow = idx + (int64_t)row * k;
+  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
+  if (K == V) {
+    trivial_row(srow, V, k, NT, orow, vrow);
+    return;
+  }
+
+  // ---- tau from the row's bound keys (zero keys stand for "no entry")
+  const uint32_t* brow = bound + (int64_t)row * nb;
+  uint32_t bk[kRBKeys];
+#pragma unroll
+  for (int i = 0; i < kRBKeys; ++i) bk[i] = brow[min(tid + i * NT, nb - 1)];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nz = 0u;
+#pragma unroll
+  for (int i = 0; i < kRBKeys; ++i)
+    if (tid + i * NT < nb && bk[i] != 0u) {
+      kmin = min(kmin, bk[i]);
+      kmax = max(kmax, bk[i]);
+      ++nz;
+    }
+  if (tid == 0) s_nz = 0u;
+  __syncthreads();
+  nz = wave_incl_sum(nz);
+  if ((tid & 63) == 63) atomicAdd(&s_nz, nz);
+  block_minmax<NT>(kmin, kmax, s_mm);  // (its barriers also order the count)
+  const bool usable = s_nz >= (uint32_t)K;
+  int known = usable ? common_bits(kmin, kmax) : 32, need = K;
+  uint32_t tau = usable ? kmax : 0u;
+  auto each_bound = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < kRBKeys; ++i)
+      if (tid + i * NT < nb) f(bk[i]);
+  };
+  while (known < 22) radix_step<NT>(each_bound, tau, known, need, s_hist, s_w, s_sel);
+  const uint32_t pmask = known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
+  tau &= pmask;
+
+  // ---- one pass over the row: candidates (keys >= tau) into LDS in index order
+  int C = 0, G = 0;  // candidates so far, and those whose prefix lies above tau's (uniform)
+  for (int lo = 0; lo < V; lo += kRBChunk) {
+    const int i0 = lo + kRBPer * tid;
+    uint32_t key[kRBPer];
+    if (!sbf16 && (n_max & 3) == 0) {
+      f32x4 x[kRBPer / 4];
+#pragma unroll
+      for (int j = 0; j < kRBPer / 4; ++j) {
+        const int64_t p = min((int64_t)i0 + 4 * j, n_max - 4);
+        x[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(srow.p) + p));
+      }
+#pragma unroll
+      for (int j = 0; j < kRBPer / 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[4 * j + q] = score_key(x[j][q]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kRBPer; ++e) key[e] = srow.key(min((int64_t)i0 + e, n_max - 1));
+    }
+    uint32_t c_t = 0, g_t = 0;
+#pragma unroll
+    for (int e = 0; e < kRBPer; ++e) {
+      const bool cand = i0 + e < V && key[e] >= tau;
+      c_t += cand;
+      g_t += cand && (key[e] & pmask) > tau;
+    }
+    uint32_t c_pre, g_pre, c_tot, g_tot;
+    block_excl_sum2<NT>(c_t, g_t, s_w, c_pre, g_pre, c_tot, g_tot);
+    int p = C + (int)c_pre;
+#pragma unroll
+    for (int e = 0; e < kRBPer; ++e)
+      if (i0 + e < V && key[e] >= tau) {
+        if (p < kRBCap) s_c[p] = Cand{key[e], i0 + e};
+        ++p;
+      }
+    C += (int)c_tot;
+    G += (int)g_tot;
+  }
+  __syncthreads();
+  if (C > kRBCap || C < K) {  // (uniform) the bound did not prune enough: the full selection
+    row_select<NT>(srow, V, K, k, orow, vrow, s_hist, nullptr, s_w, s_sel);
+    return;
+  }
+
+  // ---- the K-th key among the candidates: thread t holds candidates [j0, j1) in registers
+  constexpr int kReg = kRBCap / NT;  // 8
+  const int per = (C + NT - 1) / NT;
+  const int j0 = min(tid * per, C), j1 = min(j0 + per, C);
+  uint32_t rk[kReg];
+  int32_t ri[kReg];
+#pragma unroll
+  for (int i = 0; i < kReg; ++i) {
+    const Cand cd = s_c[min(j0 + i, kRBCap - 1)];
+    rk[i] = cd.key;
+    ri[i] = cd.idx;
+  }
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int i = 0; i < kReg; ++i)
+      if (j0 + i < j1) f(rk[i]);
+  };
+  uint32_t kstar = tau;
+  if (G < K) {
+    need = K - G;  // the K-th key shares tau's prefix
+  } else {         // the candidates' range decides the first open bit
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    each([&](uint32_t kk) {
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    });
+    block_minmax<NT>(lo, hi, s_mm);
+    kstar = hi;
+    known = common_bits(lo, hi);
+    need = K;
+  }
+  while (known < 32) radix_step<NT>(each, kstar, known, need, s_hist, s_w, s_sel);
+  const int ties = need;  // keys equal to K* still to take, lowest index first
+
+  // ---- ordered output: a thread's first selected candidate lands after the larger keys of earlier threads
+  // and the equal keys they take
+  uint32_t n_gt = 0, n_eq = 0;
+  each([&](uint32_t kk) {
+    n_gt += kk > kstar;
+    n_eq += kk == kstar;
+  });
+  uint32_t gt_base, eq_base, gt_tot, eq_tot;
+  block_excl_sum2<NT>(n_gt, n_eq, s_w, gt_base, eq_base, gt_tot, eq_tot);
+  int pos = (int)gt_base + min((int)eq_base, ties);
+  int eq_rank = (int)eq_base;
+#pragma unroll
+  for (int i = 0; i < kReg; ++i) {
+    if (j0 + i >= j1) break;
+    const uint32_t kk = rk[i];
+    bool sel = kk > kstar;
+    if (kk == kstar) sel = eq_rank++ < ties;
+    if (sel && pos < K) {
+      orow[pos] = ri[i];
+      if (vrow) vrow[pos] = key_to_score(kk);
+    }
+    pos += sel ? 1 : 0;
+  }
+  for (int j = K + tid; j < k; j += NT) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
+}
+
 bool use_split(int rows, int64_t n_max) {
   const int64_t nch = (n_max + kChunk - 1) / kChunk;
   return rows < kSplitMaxRows && n_max > 16384 && nch <= kMaxChunks;
@@ -1035,6 +1216,10 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
       hipLaunchKernelGGL(topk_split_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T,
                          n_max, pos0, m, k, nch, idx, vals, s);
     }
+  } else if (bound && index_bound_keys(n_max) >= 2 * (int64_t)k && index_bound_keys(n_max) <= kRBKeys * kRBThreads) {
+    // many rows with the indexer's bound keys: one pruning pass per row
+    hipLaunchKernelGGL(topk_rowbound_kernel, dim3(rows), dim3(kRBThreads), 0, stream, scores, sbf16, T, n_max, pos0,
+                       m, k, bound, (int)index_bound_keys(n_max), idx, vals);
   } else {
     const int cache = n_max <= kRowKeyCap ? 1 : 0;
     size_t lds = (size_t)kBins * 4 + (cache ? (size_t)n_max * 4 : 0);

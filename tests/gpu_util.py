@@ -88,12 +88,12 @@ def score_keys(x32):
 
 
 def host_bound(scores32, pos0, m):
-    """Bound keys as csa_index defines them: for each bound set, the keys of its two largest visible
-    scores (0 where the set has fewer).  Sets split each run of 256 entries: the whole run when the cache
-    holds more than 65536 entries, else the four sets {e : e mod 64 in [16 r, 16 r + 16)}."""
+    """Bound keys as the decode csa_index kernel lays them out: for each bound set, the keys of its two largest
+    visible scores (0 where the set has fewer).  Sets split each run of 256 entries: the whole run when the
+    cache holds more than 65536 entries, else the eight sets {e : e mod 64 in [8 r, 8 r + 8)}."""
     B, T, N = scores32.shape
     runs = 4 * ((N + 1023) // 1024)
-    sets = 1 if N > 65536 else 4
+    sets = 1 if N > 65536 else 8
     out = np.zeros((B, T, 2 * runs * sets), np.uint32)
     keys = score_keys(scores32)
     for b in range(B):
@@ -102,8 +102,26 @@ def host_bound(scores32, pos0, m):
             for u in range(runs):
                 e = np.arange(256 * u, min(256 * u + 256, vis))
                 for s in range(sets):
-                    sel = e if sets == 1 else e[(e % 64) // 16 == s]
+                    sel = e if sets == 1 else e[(e % 64) // 8 == s]
                     kk = np.sort(keys[b, r, sel])[::-1]
                     j = u * sets + s
                     out[b, r, 2 * j:2 * j + min(2, len(kk))] = kk[:2]
+    return out
+
+
+def host_bound_prefill(scores32, pos0, m):
+    """Bound keys as the tiled prefill csa_index kernel lays them out: set j is entries [32 j, 32 j + 32) when
+    the cache holds at most 65536 entries, else [256 j, 256 j + 256); its two largest visible keys at 2 j and
+    2 j + 1 (0 where it has fewer), every later position 0.  The row length is that of host_bound."""
+    B, T, N = scores32.shape
+    nb = 2 * 4 * (1 if N > 65536 else 8) * ((N + 1023) // 1024)
+    size = 256 if N > 65536 else 32
+    out = np.zeros((B, T, nb), np.uint32)
+    keys = score_keys(scores32)
+    for b in range(B):
+        for r in range(T):
+            vis = min((pos0[b] + r) // m, N)
+            for j in range((vis + size - 1) // size):
+                kk = np.sort(keys[b, r, size * j:min(size * j + size, vis)])[::-1]
+                out[b, r, 2 * j:2 * j + min(2, len(kk))] = kk[:2]
     return out
