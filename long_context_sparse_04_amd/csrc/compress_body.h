@@ -39,6 +39,14 @@ struct Raw4<uint16_t> {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// A row's logit in base-2 units, rounded on its own: the multiply is not contracted into a later
+// subtraction (an instruction compiled without contraction is never fused), so the row holding the maximum
+// has lg2 - mx = 0 exactly.
+CSA_DEV float logit2(float z, float bias) {
+#pragma clang fp contract(off)
+  return (z + bias) * kLog2e;
+}
+
 // Online softmax state of 4 channels in base-2 units (logits scaled by log2 e).
 struct Soft4 {
   float mx[4], sm[4], ac[4];
@@ -46,7 +54,8 @@ struct Soft4 {
 #pragma unroll
     for (int q = 0; q < 4; ++q) { mx[q] = -INFINITY; sm[q] = 0.0f; ac[q] = 0.0f; }
   }
-  // branch-free update with one row: logit lg2 (finite, base 2) and value v
+  // branch-free update with one row: logit lg2 (finite, base 2, from logit2) and value v; the row holding
+  // the maximum gets weight exp2(0) = 1, so a logit far above the others returns its row's value bit for bit
   CSA_DEV void add(int q, float lg2, float v) {
     const float mn = fmaxf(mx[q], lg2);
     const float sc = __builtin_amdgcn_exp2f(mx[q] - mn);  // 0 while the state is empty
@@ -136,7 +145,7 @@ CSA_DEV void compress_one(const Job& jb, const double* theta, int e, int b, int 
       for (int u = 0; u < kBatch; ++u) {
         if (rr0 + u * nrs >= nrows) break;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) st.add(q, (z[u].get(q) + bb[u][q]) * kLog2e, v[u].get(q));
+        for (int q = 0; q < 4; ++q) st.add(q, logit2(z[u].get(q), bb[u][q]), v[u].get(q));
       }
     }
   }

@@ -147,12 +147,38 @@ def _check_scores(got, ref, absref, rtol):
         assert err.max() <= rtol, err.max()
 
 
+class MixedRows:
+    """Read-only float64 view of a mixed-format cache on the GPU (bytes [B][N][c + R], scales [B][N]) that
+    decodes only the rows asked for, with the oracle's decoder; `override` as in Bf16Rows."""
+
+    def __init__(self, data, scale, R, override):
+        self.data, self.scale, self.R, self.override = data, scale, R, override
+        self.shape = (data.shape[0], data.shape[1], data.shape[2] - R)
+
+    def __getitem__(self, key):
+        b, rows = key
+        ids = np.arange(self.shape[1])[rows]
+        sel = torch.from_numpy(np.asarray(ids, np.int64)).to(self.data.device)
+        out = oracle.decode_fp8_rope_rows(self.data[b, sel].cpu().numpy(), self.scale[b, sel].cpu().numpy(), self.R)
+        for (ob, orow), vec in self.override.items():
+            if ob == b:
+                out[ids == orow] = vec
+        return out
+
+
 # ----------------------------------------------------------------------------- decode
-@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
-def test_decode_step_full_size(api, name):
+@pytest.mark.parametrize("name,kv_fmt", [("c2", "bf16"), ("c3", "bf16"), ("c5", "bf16"), ("c3", "fp8rope"),
+                                         ("c5", "fp8rope")])
+def test_decode_step_full_size(api, name, kv_fmt):
+    """The benchmark's decode step, launch for launch: csa_compress_index with the indexer key alone (the
+    block's key quantized into the key cache, then the scores and bound keys), csa_topk_compress (the
+    selection, with one more workgroup per row that stores the block's KV entry prepared, in bf16 or in the
+    mixed fp8 + bf16 RoPE format), csa_attend over the prepared cache (window rows raw)."""
     cfg = configs.get_config(name)
     B, N, fmt = cfg.B, cfg.n_comp, cfg.idx_dtype
-    say(f"{cfg.name}: generating B={B} caches of {N} entries")
+    mixed = kv_fmt == "fp8rope"
+    R = cfg.rope_dims
+    say(f"{cfg.name} (KV {kv_fmt}): generating B={B} caches of {N} entries")
     cc = caches(cfg)
     ckv, cik = gen.compress_inputs(cfg), gen.compress_inputs(cfg, indexer=True)
     qi, w = gen.indexer_queries(cfg)
@@ -162,21 +188,26 @@ def test_decode_step_full_size(api, name):
 
     # ---- the step on the GPU, as the benchmark launches it
     say(f"{cfg.name}: GPU step")
-    kv_cache = dev(cc["kv"])
+    prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
+    kv_scale = None
+    if mixed:   # the context cache, stored prepared in the mixed format
+        kv_cache, kv_scale = api.prepare_kv(dev(cc["kv"]), prep, pos_stride=cfg.m, out_fmt="fp8rope")
+    else:
+        kv_cache = dev(cc["kv"])
+        api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)     # stored prepared, in place
     ik = dev(cc["ik"])
     ik_scale = dev(cc["ik_scale"])
-    prep = api.kv_prep(cfg.rope_dims, cfg.eps, cfg.rope_base)
-    api.prepare_kv(kv_cache, prep, pos_stride=cfg.m, out=kv_cache)     # the context cache, stored prepared
     first = N - 1
     d = lambda ci: {k: dev(ci[k]) for k in ("ca", "cb", "za", "zb", "bias_a", "bias_b")}
-    # as the benchmark: compression folded into the index launch, the selector takes its bound keys
     bound = api.bound_keys(B, 1, N, DEV)
-    scores = api.compress_index(dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N, prep=prep), d(cik),
-                                ckv["m"], ckv["row0_pos"], first, dev(qi["data"]), dev(qi.get("scale")), dev(w), ik,
-                                ik_scale, pos, fmt, bound=bound)
-    idx, _ = api.topk(scores, pos, cfg.m, cfg.k, bound=bound)
-    out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
+    scores = api.compress_index(None, d(cik), cik["m"], cik["row0_pos"], first, dev(qi["data"]),
+                                dev(qi.get("scale")), dev(w), ik, ik_scale, pos, fmt, bound=bound)
+    kv_job = dict(d(ckv), out=kv_cache[:, first:], out_batch_stride=N, prep=prep)
+    if mixed:
+        kv_job.update(out_scale=kv_scale[:, first:], out_fmt="fp8rope")
+    idx = api.topk_compress(scores, pos, cfg.m, cfg.k, kv_job, ckv["row0_pos"], first, bound=bound)
+    out_pipe = api.attend(dev(q), kv_cache, idx, dev(win), dev(sink), pos, cfg.m, cfg.n_win, R, cfg.scale,
+                          cfg.eps, cfg.rope_base, kv_prepared=True, comp_scale=kv_scale)
     if cfg.with_hca:
         chca = gen.compress_inputs(cfg, hca=True)
         hq, hwin, hsink = gen.queries(cfg, hca=True), gen.window(cfg, hca=True), gen.sink(cfg, hca=True)
@@ -184,7 +215,7 @@ def test_decode_step_full_size(api, name):
         api.prepare_kv(hca_cache, prep, pos_stride=cfg.m_hca, out=hca_cache)
         _gpu_compress(api, chca, hca_cache[:, chca["first_entry"]:], stride=cfg.n_hca, prep=prep)
         phwin = _prepared_window(api, hwin, prep, pos, cfg)
-        hout = api.hca_attend(dev(hq), hca_cache, phwin, dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
+        hout = api.hca_attend(dev(hq), hca_cache, phwin, dev(hsink), pos, cfg.m_hca, cfg.n_win, R,
                               cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
     torch.cuda.synchronize()
 
@@ -192,8 +223,22 @@ def test_decode_step_full_size(api, name):
     say(f"{cfg.name}: oracle compress")
     (r_kv, a_kv), (r_ik, a_ik) = _oracle_compress(ckv), _oracle_compress(cik)
     r_kv, a_kv, r_ik, a_ik = r_kv[:, 0], a_kv[:, 0], r_ik[:, 0], a_ik[:, 0]
-    _check_prepared_rows(kv_cache[:, first].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_kv,
-                         cfg.m * first, cfg)
+    r_prep = oracle.rope(oracle.rmsnorm(r_kv, None, cfg.eps), cfg.m * first, R, cfg.rope_base)
+    if mixed:
+        # the entry's bytes against the oracle's own prepared entry: scale amax/448, codes RNE (up to float32
+        # rounding at a midpoint), decoded values within half an e4m3 step; RoPE dims within half a bf16 ulp
+        gb, gs = kv_cache[:, first].cpu().numpy(), kv_scale[:, first].cpu().numpy()
+        n = cfg.c - R
+        assert np.allclose(gs, np.max(np.abs(r_prep[:, :n]), axis=-1) / 448.0, rtol=1e-5, atol=0)
+        rc, rs = oracle.encode_fp8_rows(r_prep[:, :n])
+        assert codes_close(gb[:, :n], rc, r_prep[:, :n] / rs[:, None], oracle.fp8_e4m3_values())
+        dec = oracle.decode_fp8_rope_rows(gb, gs, R)
+        assert np.all(np.abs(dec[:, n:] - r_prep[:, n:]) <= np.abs(r_prep[:, n:]) * 2.0 ** -8 + 1e-5)
+        new_rows, new_scale = oracle.encode_fp8_rope_rows(r_prep, R)   # the oracle's own stored entry
+        new_vals = oracle.decode_fp8_rope_rows(new_rows, new_scale.astype(np.float32), R)
+    else:
+        _check_prepared_rows(kv_cache[:, first].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_kv,
+                             cfg.m * first, cfg)
     g_ik = ik[:, first].contiguous()
     g_ik = g_ik.view(torch.int16).cpu().numpy().view(np.uint16) if fmt == "bf16" else g_ik.cpu().numpy()
     g_iks = None if ik_scale is None else ik_scale[:, first].cpu().numpy()
@@ -213,10 +258,11 @@ def test_decode_step_full_size(api, name):
     # the new entry: the same bound when both sides stored the same codes, else one code step of slack
     _check_scores(got_sc[..., first:], r_sc[..., first:], absref[..., first:], 1e-5 if same_codes else 1e-2)
 
-    # ---- top-k: set agreement and the gap rule on every row
+    # ---- top-k: exact on the GPU's own scores; against the oracle's, set agreement and the gap rule
     say(f"{cfg.name}: oracle top-k")
-    r_idx = oracle.topk(r_sc, pos0, cfg.m, cfg.k)
     gi = idx.cpu().numpy()
+    assert np.array_equal(gi, oracle.topk(got_sc, pos0, cfg.m, cfg.k))
+    r_idx = oracle.topk(r_sc, pos0, cfg.m, cfg.k)
     agree, bad = topk_agreement(gi, r_idx, r_sc)
     say(f"  top-k agreement {agree:.6f}, rows identical {np.mean(np.all(gi == r_idx, axis=-1)):.4f}")
     assert agree >= 0.999 and bad == 0
@@ -224,13 +270,18 @@ def test_decode_step_full_size(api, name):
 
     # ---- attention on the oracle's own list (isolated) and on the GPU's list (end to end)
     say(f"{cfg.name}: oracle attend, {B} rows x {cfg.H} heads")
-    out_iso = api.attend(dev(q), kv_cache, dev(r_idx), dev(win), dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
-                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True)
+    out_iso = api.attend(dev(q), kv_cache, dev(r_idx), dev(win), dev(sink), pos, cfg.m, cfg.n_win, R,
+                         cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=True, comp_scale=kv_scale)
     torch.cuda.synchronize()
-    r_cache = Bf16Rows(cc["kv"], {(b, first): oracle.decode_bf16(oracle.encode_bf16(r_kv[b])) for b in range(B)})
-    r_out = oracle.attend(_f64(q), r_cache, r_idx, _f64(win), sink, pos0, cfg.m, cfg.n_win, cfg.rope_dims,
-                          cfg.scale, cfg.eps, cfg.rope_base)
-    e_iso, e_pipe = rel_l2(host_f64(out_iso), r_out), rel_l2(host_f64(out_pipe), r_out)
+    if mixed:   # the entries as stored (decoded exactly), the new one the oracle's own
+        r_cache = MixedRows(kv_cache, kv_scale, R, {(b, first): new_vals[b] for b in range(B)})
+    else:
+        r_cache = Bf16Rows(cc["kv"], {(b, first): oracle.decode_bf16(oracle.encode_bf16(r_kv[b])) for b in range(B)})
+    r_out = oracle.attend(_f64(q), r_cache, r_idx, _f64(win), sink, pos0, cfg.m, cfg.n_win, R, cfg.scale, cfg.eps,
+                          cfg.rope_base, comp_prepared=mixed)
+    r_pipe = oracle.attend(_f64(q), r_cache, gi, _f64(win), sink, pos0, cfg.m, cfg.n_win, R, cfg.scale, cfg.eps,
+                           cfg.rope_base, comp_prepared=mixed) if not np.array_equal(gi, r_idx) else r_out
+    e_iso, e_pipe = rel_l2(host_f64(out_iso), r_out), rel_l2(host_f64(out_pipe), r_pipe)
     say(f"  attend rel-L2 isolated {e_iso:.2e}, end to end {e_pipe:.2e}")
     assert e_iso <= LOWP_TOL and e_pipe <= LOWP_TOL
     for b in range(B):                                   # every sequence on its own, not only on average
@@ -244,7 +295,7 @@ def test_decode_step_full_size(api, name):
         _check_prepared_rows(hca_cache[:, hf].contiguous().view(torch.int16).cpu().numpy().view(np.uint16), r_h,
                              cfg.m_hca * hf, cfg)
         r_hcache = Bf16Rows(cc["hca"], {(b, hf): oracle.decode_bf16(oracle.encode_bf16(r_h[b])) for b in range(B)})
-        r_hout = oracle.hca_attend(_f64(hq), r_hcache, _f64(hwin), hsink, pos0, cfg.m_hca, cfg.n_win, cfg.rope_dims,
+        r_hout = oracle.hca_attend(_f64(hq), r_hcache, _f64(hwin), hsink, pos0, cfg.m_hca, cfg.n_win, R,
                                    cfg.scale, cfg.eps, cfg.rope_base)
         e_h = rel_l2(host_f64(hout), r_hout)
         say(f"  hca_attend rel-L2 {e_h:.2e}")
@@ -285,8 +336,10 @@ def test_chunked_prefill_full_size_sampled(api):
     _gpu_compress(api, cik, ik[:, f0:], stride=N)
     _gpu_compress(api, chca, hca_cache[:, hf0:], stride=cfg.n_hca, prep=prep)
     pwin, phwin = _prepared_window(api, win, prep, pos, cfg), _prepared_window(api, hwin, prep, pos, cfg)
-    scores = api.index(dev(qi["data"]), None, dev(w), ik, None, pos, cfg.m, fmt)
-    idx, _ = api.topk(scores, pos, cfg.m, cfg.k)
+    # as the benchmark: the tiled index also writes the selector's bound keys (one pruning pass per row)
+    bound = api.bound_keys(1, T, N, DEV)
+    scores = api.index(dev(qi["data"]), None, dev(w), ik, None, pos, cfg.m, fmt, bound=bound)
+    idx, _ = api.topk(scores, pos, cfg.m, cfg.k, bound=bound)
     out_pipe = api.attend(dev(q), kv_cache, idx, pwin, dev(sink), pos, cfg.m, cfg.n_win, cfg.rope_dims,
                           cfg.scale, cfg.eps, cfg.rope_base, kv_prepared=2)
     hout = api.hca_attend(dev(hq), hca_cache, phwin, dev(hsink), pos, cfg.m_hca, cfg.n_win, cfg.rope_dims,
@@ -326,6 +379,8 @@ def test_chunked_prefill_full_size_sampled(api):
         # key element moves its score by at most 2^-8 of the absolute-value score
         _check_scores(got[..., :f0], r_sc[..., :f0], absref[..., :f0], 1e-5)
         _check_scores(got[..., f0:], r_sc[..., f0:], absref[..., f0:], 2.0 ** -8)
+        # exact on the GPU's own scores (the bound-key selection), the gap rule against the oracle's
+        assert np.array_equal(gi[:, r:r + 1], oracle.topk(got, [t], cfg.m, cfg.k)), r
         r_idx = oracle.topk(r_sc, [t], cfg.m, cfg.k)
         agree, bad = topk_agreement(gi[:, r:r + 1], r_idx, r_sc)
         assert agree >= 0.999 and bad == 0, (r, agree, bad)

@@ -5,8 +5,9 @@ e4m3 with one float32 scale per row, the RoPE dims in bf16 ("【论文解读】D
 Writers (csa_prepare_kv, csa_compress, csa_compress_index): the RoPE part must be bit-identical to the bf16
 output of the same call (same float32 values, same rounding); the fp8 part must decode to the oracle's
 prepared values within half an e4m3 step, with codes that match the oracle's encoding except within float32
-rounding of a midpoint.  Readers (csa_attend, hca_attend, every kernel variant): the output against the
-float64 oracle run on the exact decoded entries (handed in prepared), rel-L2 <= 5e-3.
+rounding of a midpoint.  Readers (csa_attend, hca_attend, every kernel variant) read rows that the oracle
+prepared and encoded itself: the output against the float64 oracle run on the exact decoded entries (handed in
+prepared), rel-L2 <= 5e-3.
 """
 import numpy as np
 import pytest
@@ -145,19 +146,26 @@ def _rand_idx(rng, B, T, k, pos0, m, n_max, fill=0.9):
 
 
 def _attend_mixed(api, cfg, pos0, idx, hca, prepared):
-    """GPU attention over a mixed-format cache (prepared by csa_prepare_kv from the raw cache) against the
-    oracle on the exact decoded entries, handed in prepared; window rows raw (1) or prepared (2)."""
+    """GPU attention over a mixed-format cache against the oracle on the exact decoded entries, handed in
+    prepared; window rows raw (1) or prepared (2).  The cache bytes are the oracle's own: its float64
+    preparation of the raw entries (RMSNorm, then RoPE at m*s), encoded by its own writer
+    (oracle.encode_fp8_rope_rows), so that the readers are checked independently of the GPU writers."""
     q = gen.queries(cfg, hca=hca)
     cache = gen.kv_cache(cfg, hca=hca)
     win = gen.window(cfg, hca=hca)
     sink = gen.sink(cfg, hca=hca)
     R = cfg.rope_dims
+    ratio = cfg.m_hca if hca else cfg.m
     say(f"{'hca' if hca else 'csa'}_attend fp8rope {cfg.name} B={cfg.B} T={cfg.T} H={cfg.H} N={cache.shape[1]} "
-        f"prepared={prepared}")
-    prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
-    mc, ms = api.prepare_kv(dev(cache), prep, pos_stride=cfg.m_hca if hca else cfg.m, out_fmt="fp8rope")
+        f"prepared={prepared} (oracle-encoded rows)")
+    ents = oracle.rope(oracle.rmsnorm(oracle.decode_bf16(cache), None, cfg.eps),
+                       ratio * np.arange(cache.shape[1])[None, :], R, cfg.rope_base)
+    rows, scale = oracle.encode_fp8_rope_rows(ents, R)
+    scale32 = scale.astype(np.float32)
+    mc, ms = dev(np.ascontiguousarray(rows)), dev(np.ascontiguousarray(scale32))
     dwin = dev(win)
     if prepared == 2:
+        prep = api.kv_prep(R, cfg.eps, cfg.rope_base)
         dwin = api.prepare_kv(dwin, prep, pos_base=_pos(pos0), pos_first=-(cfg.n_win - 1))
     if hca:
         out = api.hca_attend(dev(q), mc, dwin, dev(sink), _pos(pos0), cfg.m_hca, cfg.n_win, R, cfg.scale, cfg.eps,
@@ -166,13 +174,13 @@ def _attend_mixed(api, cfg, pos0, idx, hca, prepared):
         out = api.attend(dev(q), mc, dev(idx), dwin, dev(sink), _pos(pos0), cfg.m, cfg.n_win, R, cfg.scale,
                          cfg.eps, cfg.rope_base, kv_prepared=prepared, comp_scale=ms)
     torch.cuda.synchronize()
-    ents = oracle.decode_fp8_rope_rows(_np(mc), _np(ms), R)
+    dec = oracle.decode_fp8_rope_rows(rows, scale32, R)   # the exact values of the bytes both sides read
     qv, wv = oracle.decode_bf16(q), oracle.decode_bf16(win)
     if hca:
-        ref = oracle.hca_attend(qv, ents, wv, sink, pos0, cfg.m_hca, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
+        ref = oracle.hca_attend(qv, dec, wv, sink, pos0, cfg.m_hca, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
                                 comp_prepared=True)
     else:
-        ref = oracle.attend(qv, ents, idx, wv, sink, pos0, cfg.m, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
+        ref = oracle.attend(qv, dec, idx, wv, sink, pos0, cfg.m, cfg.n_win, R, cfg.scale, cfg.eps, cfg.rope_base,
                             comp_prepared=True)
     return host_f64(out), ref
 

@@ -9,8 +9,9 @@ compressed caches ("ã€è®ºæ–‡è§£è¯»ã€‘DeepSeek-V4", section äºŒ(å…­) æŽ¨ç†æ¡†æž
     window ring holds the token's row prepared exactly as csa_prepare_kv prepares it;
   - a decode loop of several steps per sequence (append -> paged index -> top-k -> paged attention, CSA and
     HCA, crossing CSA and HCA block boundaries) against the float64 oracle computed from the token streams
-    alone: scores (rel-L2 <= 5e-3), the selection (exact: k covers every visible entry), the outputs
-    (rel-L2 <= 5e-3).
+    alone: every score within 2^-8 of its absolute-value scale (the keys' bf16 rounding), the selection (k
+    below the visible count: exact on the GPU's own scores, the 1e-3 gap rule and >= 99.9% agreement against
+    the oracle's), the outputs (rel-L2 <= 5e-3).
 """
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ import torch
 
 import oracle
 from synth import configs, gen
-from tests.gpu_util import DEV, dev, host_f64, rel_l2
+from tests.gpu_util import DEV, dev, host_f64, rel_l2, topk_agreement
 
 pytestmark = pytest.mark.gpu
 LOWP_TOL = 5e-3
@@ -258,7 +259,7 @@ def test_decode_append_matches_compress(api):
 def test_decode_loop_against_oracle(api):
     """Sequences at positions that cross CSA (every 4) and HCA (every 128) block boundaries during the loop;
     every step appends its token, then indexes, selects and attends over the paged caches and the rings."""
-    cfg = configs.C2.scaled(B=2, H=64, k=256)          # bf16 indexer keys; k covers every visible entry
+    cfg = configs.C2.scaled(B=2, H=64, k=64)           # bf16 indexer keys; k below every step's visible count
     m, mh, R, W = cfg.m, cfg.m_hca, cfg.rope_dims, cfg.n_win
     t0 = [764, 509]
     S = 7
@@ -324,6 +325,7 @@ def test_decode_loop_against_oracle(api):
     n_hmax = maxp * Eh
     scores = torch.empty((B, 1, n_max), dtype=torch.float32, device=DEV)
     bd = lambda x: dev(x)
+    sel_stats = []
     for s in range(S):
         ts = [t0[b] + s for b in range(B)]
         pos = _pos(ts)
@@ -369,19 +371,34 @@ def test_decode_loop_against_oracle(api):
             ok = np.arange(wl, t + 1) >= 0
             win[0, ok] = f("win", max(0, wl), t + 1)
             hwin[0, ok] = f("hca_win", max(0, wl), t + 1)
-            sc_ref = oracle.index(v(dq[b]["qi"]["data"][s:s + 1])[None], dq[b]["w"][s:s + 1][None], keys, [t], m)
-            assert rel_l2(g_sc[b, 0, :nv], sc_ref[0, 0, :nv]) <= LOWP_TOL, (s, b)
+            qv = v(dq[b]["qi"]["data"][s:s + 1])[None]
+            sc_ref = oracle.index(qv, dq[b]["w"][s:s + 1][None], keys, [t], m)
+            # element by element: both sides store bf16 keys of their own pooled values, which may differ by
+            # one bf16 rounding per element, so a score may move by 2^-8 of sum_h w_h |q_h|.|K| (plus float32
+            # accumulation)
+            absref = oracle.index(np.abs(qv), dq[b]["w"][s:s + 1][None], np.abs(keys), [t], m)
+            err = np.abs(g_sc[b, 0, :nv] - sc_ref[0, 0, :nv])
+            assert np.all(err <= (2.0 ** -8 + 1e-5) * absref[0, 0, :nv]), (s, b, np.max(err / absref[0, 0, :nv]))
             assert np.all(np.isneginf(g_sc[b, 0, nv:n_max]))
+            assert nv > cfg.k                                      # the selection is not trivial
+            # the selector is exact on the GPU's own scores; against the oracle's scores every difference
+            # must lie within the 1e-3 gap rule
+            assert np.array_equal(g_idx[b], oracle.topk(g_sc[b:b + 1, :, :n_max], [t], m, cfg.k)[0]), (s, b)
             idx_ref = oracle.topk(sc_ref, [t], m, cfg.k)
-            assert np.array_equal(g_idx[b], idx_ref[0]), (s, b)
-            o_ref = oracle.attend(v(dq[b]["q"][s:s + 1])[None], ents, idx_ref, win, sink, [t], m, W, R, cfg.scale,
-                                  cfg.eps, cfg.rope_base)
+            agree, bad = topk_agreement(g_idx[b:b + 1], idx_ref, sc_ref)
+            sel_stats.append(agree)
+            assert bad == 0, (s, b, agree)
+            # attention on the GPU's own list (the selection is checked above), so that the two are isolated
+            o_ref = oracle.attend(v(dq[b]["q"][s:s + 1])[None], ents, g_idx[b:b + 1], win, sink, [t], m, W, R,
+                                  cfg.scale, cfg.eps, cfg.rope_base)
             e = rel_l2(g_out[b], o_ref[0])
             h_ref = oracle.hca_attend(v(dq[b]["hq"][s:s + 1])[None], hents, hwin, hsink, [t], mh, W, R, cfg.scale,
                                       cfg.eps, cfg.rope_base)
             eh = rel_l2(g_hout[b], h_ref[0])
-            say(f"  step {s} seq {b} t={t} visible {nv}/{nh}: csa rel-L2 {e:.2e}, hca rel-L2 {eh:.2e}")
+            say(f"  step {s} seq {b} t={t} visible {nv}/{nh}: top-k agreement {agree:.4f}, csa rel-L2 {e:.2e}, "
+                f"hca rel-L2 {eh:.2e}")
             assert e <= LOWP_TOL and eh <= LOWP_TOL, (s, b, e, eh)
+    assert np.mean(sel_stats) >= 0.999, sel_stats
 
 
 def test_append_index_paged_matches_separate(api):
