@@ -332,6 +332,22 @@ csa_status hca_attend(const void* q, const void* comp_kv, const float* comp_scal
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * csa_attend_noalloc -- csa_attend for callers that cannot allocate device memory: code being captured
+ * into a HIP graph, tight serving loops, harnesses that forbid allocation.  Same arguments, results and
+ * errors as csa_attend, without the workspace: the decode split partials live in a device array of the
+ * library (64 MiB, which each GPU the library runs on holds until the process ends).  A call whose
+ * workspace (csa_attend_workspace_bytes) exceeds 64 MiB returns CSA_ERR_WORKSPACE and launches nothing.
+ * The call itself allocates nothing; its first call on a device looks up that device's array address.
+ * Every call on one GPU shares that GPU's array (it needs no initial contents), so calls that overlap on
+ * one GPU (different streams, or host threads) race and must be ordered by the caller.
+ */
+csa_status csa_attend_noalloc(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                              const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv,
+                              int B, int T, int H, int c, int rope_dims, int k, int n_win, int64_t n_max,
+                              const int64_t* pos0, int m, float scale, float eps, float rope_base, int kv_t,
+                              int comp_t, int kv_prepared, void* out, int out_t, void* stream);
+
+/*
  * ---- Decode across steps: the state cache and the paged compressed caches ----
  *
  * "【论文解读】DeepSeek-V4", section 二(六) 推理框架, and "DeepseekV4论文解析", its KV-cache part: the

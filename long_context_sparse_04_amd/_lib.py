@@ -64,6 +64,8 @@ SIGNATURES = {
     "csa_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "csa_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I,
                         _I, _I, _P, _I, _P, _SZ, _P]),
+    "csa_attend_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F,
+                                _I, _I, _I, _P, _I, _P]),
     "hca_attend_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I64, _I]),
     "hca_attend": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _P, _I, _F, _F, _F, _I, _I, _I,
                         _P, _I, _P, _SZ, _P]),

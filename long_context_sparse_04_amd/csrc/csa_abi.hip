@@ -1,6 +1,9 @@
 // C ABI of the CSA / HCA step: O(1) host-side validation, then launches on the
 // caller's stream.  No HIP runtime call is made before validation passes, so
 // argument errors are reported without touching a device.
+#include <atomic>
+#include <mutex>
+
 #include "csa_common.h"
 #include "csa_internal.h"
 
@@ -22,7 +25,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_abi_version(void) { return 6; }
+int csa_abi_version(void) { return 7; }
 
 }  // extern "C"
 
@@ -572,6 +575,60 @@ csa_status csa_pack_proj_weights(const void* w, void* packed, int z, int n, int 
   if (z == 0 || n == 0 || k == 0) return CSA_OK;
   if (!w || !packed || w == packed) return CSA_ERR_NULL;
   return launch_pack_proj_weights(w, packed, z, n, k, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---- csa_attend_noalloc: csa_attend with its workspace in a fixed device array ----------------------------------
+//
+// The decode split partials live in `scratch`, a file-scope device array each GPU holds for the life of the
+// process.  Its device address is looked up once per device (hipGetSymbolAddress, with that device current) and
+// kept; host code uses only that address, never the array's name, which on the host is a stand-in and not a
+// device pointer.  Nothing here allocates.
+namespace {
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+csa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_ERR_LAUNCH;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA_ERR_LAUNCH;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status csa_attend_noalloc(const void* q, const void* comp_kv, const float* comp_scale, const int32_t* idx,
+                              const void* win_kv, const float* sink, const float* gamma_q, const float* gamma_kv,
+                              int B, int T, int H, int c, int rope_dims, int k, int n_win, int64_t n_max,
+                              const int64_t* pos0, int m, float scale, float eps, float rope_base, int kv_t,
+                              int comp_t, int kv_prepared, void* out, int out_t, void* stream) {
+  size_t need = 0;
+  csa_status st = check_csa_attend(q, comp_kv, comp_scale, idx, win_kv, sink, B, T, H, c, rope_dims, k, n_win, n_max,
+                                   pos0, m, kv_t, comp_t, kv_prepared, out, out_t, &need);
+  if (st != CSA_OK || B == 0 || T == 0) return st;
+  if (need > kNoallocScratchBytes) return CSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != CSA_OK) return st;
+  }
+  return launch_attend(0, q, comp_kv, comp_scale, comp_t != kv_t, nullptr, idx, win_kv, sink, gamma_q, gamma_kv, B, T,
+                       H, c, rope_dims, k, n_win, n_max, pos0, m, scale, eps, rope_base, kv_t, kv_prepared, out, out_t,
+                       ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

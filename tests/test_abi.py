@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.csa_abi_version() == 6
+    assert lib.csa_abi_version() == 7
     for code in range(6):
         s = lib.csa_status_string(code).decode()
         assert s.startswith(_lib.STATUS[code])
@@ -304,3 +304,15 @@ def test_fused_decode_entry_validation(lib):
     assert ai(ja, None, 1, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, C.byref(pg), 2, 64, 128, 1000, DUMMY, 4, 2, DUMMY, 0,
               None, None) in (1, 2)
 
+
+def test_attend_noalloc_rejects_oversize_workspace(lib):
+    """csa_attend_noalloc returns CSA_ERR_WORKSPACE, without touching a device, when the decode partials would
+    exceed its 64 MiB array; argument errors come first, as in csa_attend."""
+    B, H, c, k, n_win = 60000, 128, 512, 1024, 128
+    assert lib.csa_attend_workspace_bytes(B, 1, H, c, k, n_win) > (64 << 20)
+    d = C.c_void_p(16)     # never dereferenced
+    call = lambda **kw: lib.csa_attend_noalloc(d, d, None, d, d, d, None, None, kw.get("B", B), 1, H, c, 64, k, n_win,
+                                               262144, kw.get("pos", d), 4, 0.04, 1e-6, 10000.0, 1, 1, 1, d, 1, None)
+    assert call() == 4                      # CSA_ERR_WORKSPACE
+    assert call(pos=None) == 1              # CSA_ERR_NULL before the size check
+    assert call(B=0) == 0                   # nothing to do
