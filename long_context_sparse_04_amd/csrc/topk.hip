@@ -16,12 +16,13 @@
 //    cannot exceed K*) are compacted per chunk, in index order, into the chunk's
 //    own segment of the workspace; one workgroup per row then gathers them (chunk
 //    order == index order), resolves the open bits of K* and writes the output.
-//    - With the indexer's bound keys (two per 256 entries, each the key of a
-//      distinct visible entry), the threshold is the K-th largest bound key,
-//      cut to the bits one radix pass resolves; every workgroup of the row derives
-//      it alone, so collection and finishing share one launch: the last workgroup
-//      of a row to publish its segment (agent-scope stores, then an atomic arrival
-//      count) does the finishing pass.
+//    - With the indexer's bound keys (two per bound set, each the key of a
+//      distinct visible entry), the threshold is the K-th largest bound key with
+//      at least 16 bits resolved; every chunk workgroup derives it alone and
+//      compacts its candidates, then a second launch finishes each row from
+//      candidates held in registers.
+//  * Row path with bound keys (many rows): one workgroup per row derives the same
+//    threshold, keeps the candidates of one streaming pass in LDS and finishes.
 //    - Without them: kernel 1 builds the top-digit histogram (LDS, then integer
 //      atomics into a per-row global histogram), kernel 2 the second-digit
 //      histogram of the keys in the selected bin, kernel 3 compacts the keys at or
@@ -41,10 +42,7 @@ constexpr int kRowThreads = 512;
 constexpr int kRowKeyCap = 32768;     // keys cached in LDS on the row path
 constexpr int kSegCap = 6144;         // candidates cached in LDS by the finishing kernel (no bound keys)
 constexpr int kMaxChunks = 2048;
-// The bound-key launch keeps its LDS small enough to share a CU with a workgroup of the wide attention
-// kernel (which may run beside it on another stream): fewer cached candidates (more are read from the
-// workspace) and rows of at most kBoundMaxChunks chunks.
-constexpr int kBoundSegCap = 2048;
+// The bound-key path serves rows of at most kBoundMaxChunks chunks (one chunk count per finishing thread).
 constexpr int kBoundMaxChunks = 256;
 
 // The decode step's new KV entry (one per sequence), computed by one extra workgroup per row of the
@@ -352,30 +350,30 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const void* __res
 // ------------------------------------------------------------------ split path
 struct SplitWs {
   uint32_t* hist;     // [rows][kBins]   digit-0 histogram (zero at rest)
-  uint32_t* arrive;   // [rows]          workgroups of the bound-key launch that published (zero at rest)
   uint32_t* hist1;    // [rows][kBins]   digit-1 histogram (cleared by kernel 1 of every call)
   uint32_t* info;     // [rows][4]
   uint32_t* cnt;      // [rows][nch]     per chunk: candidates | (candidates above the threshold's prefix) << 16
   Cand* seg;          // [rows][n_max]
+  Cand* blk;          // [rows][nch][kBlk] bound-key path: each chunk's first kBlk candidates, in index order
 };
+
+// The bound-key path keeps each chunk's first kBlk candidates in a compact block (the rest in the chunk's
+// segment), so that the row's finishing workgroup reads them in one coalesced round.
+constexpr int kBlk = 64;
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The split path serves fewer than kSplitMaxRows rows.  Its zero-at-rest regions (the digit-0
-// histograms and the arrival counts) take fixed slots for that many rows at the start of the
-// workspace, so that no call of another shape ever places them over memory that a previous call left
-// dirty.
+// The split path serves fewer than kSplitMaxRows rows.  Its zero-at-rest region (the digit-0 histograms)
+// takes fixed slots for that many rows at the start of the workspace, so that no call of another shape
+// ever places it over memory that a previous call left dirty.
 constexpr int kSplitMaxRows = 128;
 constexpr size_t kHistSlot = (size_t)kSplitMaxRows * kBins * 4;
-constexpr size_t kArriveSlot = (size_t)kSplitMaxRows * 4;
 
 static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   char* p = static_cast<char*>(ws);
   SplitWs s;
   s.hist = reinterpret_cast<uint32_t*>(p);
   p += kHistSlot;
-  s.arrive = reinterpret_cast<uint32_t*>(p);
-  p += align256(kArriveSlot);
   s.hist1 = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * kBins * 4);
   s.info = reinterpret_cast<uint32_t*>(p);
@@ -383,13 +381,15 @@ static SplitWs carve(void* ws, int rows, int64_t n_max, int nch) {
   s.cnt = reinterpret_cast<uint32_t*>(p);
   p += align256((size_t)rows * nch * 4);
   s.seg = reinterpret_cast<Cand*>(p);
-  (void)n_max;
+  p += align256((size_t)rows * n_max * sizeof(Cand));
+  s.blk = reinterpret_cast<Cand*>(p);
   return s;
 }
 
 static size_t split_bytes(int rows, int64_t n_max, int nch) {
-  return kHistSlot + align256(kArriveSlot) + align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
-         align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand));
+  return kHistSlot + align256((size_t)rows * kBins * 4) + align256((size_t)rows * 16) +
+         align256((size_t)rows * nch * 4) + align256((size_t)rows * n_max * sizeof(Cand)) +
+         align256((size_t)rows * nch * kBlk * sizeof(Cand));
 }
 
 // Thread t of a split-path workgroup owns the 16 consecutive scores [lo + 16 t, lo + 16 t + 16) of
@@ -440,11 +440,11 @@ CSA_DEV ChunkKeys load_chunk(const ScoreRow& srow, int lo, int hi, int64_t n_max
   return c;
 }
 
-// Write the chunk's keys >= thr into its segment in index order; returns the chunk totals (candidates,
-// and those whose top bits under pmask exceed thr's) to every thread.
-template <bool kAgentStores>
-CSA_DEV void compact_chunk(const ChunkKeys& ck, int lo, uint32_t thr, uint32_t pmask, Cand* seg, uint32_t* s_w,
-                           uint32_t& c_tot, uint32_t& g_tot) {
+// Write the chunk's keys >= thr in index order: into its segment, or (blk non-NULL) the first kBlk into the
+// chunk's compact block and the rest into its segment; returns the chunk totals (candidates, and those whose
+// top bits under pmask exceed thr's) to every thread.
+CSA_DEV void compact_chunk(const ChunkKeys& ck, int lo, uint32_t thr, uint32_t pmask, Cand* seg, Cand* blk,
+                           uint32_t* s_w, uint32_t& c_tot, uint32_t& g_tot) {
   uint32_t c_t = 0, g_t = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
@@ -455,16 +455,15 @@ CSA_DEV void compact_chunk(const ChunkKeys& ck, int lo, uint32_t thr, uint32_t p
   uint32_t c_pre, g_pre;
   block_excl_sum2<kSplitThreads>(c_t, g_t, s_w, c_pre, g_pre, c_tot, g_tot);
   const int i0 = lo + kPerThread * (int)threadIdx.x;
-  int p = lo + (int)c_pre;
+  int p = (int)c_pre;  // position inside the chunk
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e)
     if (ck.valid[e] && ck.key[e] >= thr) {
-      if constexpr (kAgentStores) {
-        const uint64_t v = (uint64_t)ck.key[e] | ((uint64_t)(uint32_t)(i0 + e) << 32);
-        __hip_atomic_store(reinterpret_cast<uint64_t*>(seg + p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        seg[p] = Cand{ck.key[e], i0 + e};
-      }
+      const Cand cd{ck.key[e], i0 + e};
+      if (blk && p < kBlk)
+        blk[p] = cd;
+      else
+        seg[lo + p] = cd;
       ++p;
     }
 }
@@ -586,7 +585,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_collect_kernel(const
     ws.info[row * 4 + 3] = (uint32_t)(need - s_sel[1]);  // keys with prefix p1 still to take
   }
   uint32_t c_tot = 0, g_tot = 0;
-  if (lo < hi) compact_chunk<false>(ck, lo, p1 << 10, 0xFFFFFC00u, ws.seg + (int64_t)row * n_max, s_w, c_tot, g_tot);
+  if (lo < hi) compact_chunk(ck, lo, p1 << 10, 0xFFFFFC00u, ws.seg + (int64_t)row * n_max, nullptr, s_w, c_tot, g_tot);
   if (tid == 0) ws.cnt[(int64_t)row * nch + blockIdx.x] = c_tot;
 }
 
@@ -607,30 +606,17 @@ struct FinishLds {
 // reduced by the candidates whose prefix is above it (when they are fewer than K; otherwise the range
 // of the candidates decides), and too few candidates (keys that were no lower bound) send the row to
 // a pass over all its visible keys.
-template <bool kCoh, int SEGCAP, int MAXCH>
+template <int SEGCAP, int MAXCH>
 CSA_DEV void finish_row(const ScoreRow& srow, int V, int K, int k, int nact, const uint32_t* __restrict__ cnt,
                         const Cand* __restrict__ seg, int64_t n_max, uint32_t pv, int known, int need, bool bounded,
                         int32_t* __restrict__ orow, float* __restrict__ vrow, const FinishLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int kW = kSplitThreads / 64;
   constexpr int kBatch = 16;  // chunks per wave per gather round
-  // segment and count loads (agent-scope loads when the segments were published within the launch
-  // without a cache write-back); counts are clamped to a chunk's size
-  auto ldc = [&](int64_t i) -> Cand {
-    if constexpr (kCoh) {
-      const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(seg + i), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      return Cand{(uint32_t)v, (int32_t)(v >> 32)};
-    } else {
-      return seg[i];
-    }
-  };
+  // segment and count loads; counts are clamped to a chunk's size
+  auto ldc = [&](int64_t i) -> Cand { return seg[i]; };
   auto ldn = [&](int c) -> uint32_t {
-    uint32_t v;
-    if constexpr (kCoh)
-      v = __hip_atomic_load(cnt + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else
-      v = cnt[c];
+    const uint32_t v = cnt[c];
     return min(v & 0xFFFFu, (uint32_t)kChunk) | (min(v >> 16, (uint32_t)kChunk) << 16);
   };
   // first gather round: 64 candidates of each of the wave's chunks, loaded before the counts are known
@@ -848,32 +834,38 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 #pragma unroll
   for (int u = 0; u < kBins / kSplitThreads; ++u) ghist[tid + u * kSplitThreads] = 0;
   const int nact = (V + kChunk - 1) / kChunk;
-  finish_row<false, kSegCap, kMaxChunks>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max,
+  finish_row<kSegCap, kMaxChunks>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max,
              ws.info[row * 4 + 2] << 10, 22, (int)ws.info[row * 4 + 3], false, orow, vrow, L);
 }
 
-// With bound keys from the indexer (two per 256-entry run, each the key of a distinct visible entry),
-// one launch does the whole selection.  Every workgroup derives tau, the K-th largest bound key with
-// the bits below its radix passes cleared (each pass takes the next 11 bits, starting right under the
-// bits all bound keys share, until 22 bits are resolved), and compacts its chunk's keys >= tau into its segment, in index order; tau never
-// exceeds the row's K-th largest key, so every selected key is a candidate (typically about 1.1 k
-// keys are).  The workgroup then publishes its segment and count and adds itself to the row's arrival
-// count; the row's last one to arrive reads the others' segments, finishes the row and resets the count.
+// ------------------------------------------------------------------ split path with bound keys
+// With bound keys from the indexer (two per bound set, each the key of a distinct visible entry) the
+// selection takes two launches and no histogram pass:
+//  * collect: every chunk workgroup derives tau, the K-th largest bound key with the bits below its radix
+//    passes cleared (each pass takes the next 11 bits, starting right under the bits all bound keys share;
+//    one pass, or two while fewer than 16 bits are resolved); tau never exceeds the row's K-th largest key, so every selected key is
+//    a candidate (typically about 1.1 k keys are).  It compacts its chunk's keys >= tau in index order
+//    (the first kBlk into the chunk's compact block, the rest into its segment) and writes its counts.
+//  * finish: one workgroup per row reads the counts and the compact blocks in one round (each thread's
+//    block slots are then its candidates, in index order, held in registers), resolves the K-th key (radix
+//    passes while more than 64 candidates share the resolved prefix, then one wave bit by bit) and writes
+//    the ascending list.
+// The launch boundary orders the two; no workgroup waits for another.
 template <int KBK>
-__global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
+__global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
-    const uint32_t* __restrict__ bound, int nb, int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws,
-    TopkFuse fz) {
-  CSA_FINISH_LDS(kBoundSegCap, kBoundMaxChunks)
-  __shared__ int s_last;
+    const uint32_t* __restrict__ bound, int nb, SplitWs ws, TopkFuse fz) {
+  __shared__ __align__(16) f32x4 s_cz[3 * 256];  // the KV-entry workgroup's slice merge
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_w[2 * kSplitThreads / 64];
+  __shared__ uint32_t s_mm[2 * kSplitThreads / 64];
+  __shared__ int s_sel[2];
   __shared__ uint32_t s_nz;
   const int tid = threadIdx.x;
   const int row = blockIdx.y;
   const int nch = (int)((n_max + kChunk - 1) / kChunk);
   if (fz.on && (int)blockIdx.x == nch) {  // the extra workgroup of a row: its sequence's new KV entry
     static_assert(kSplitThreads == 256, "the compression body runs on 256 threads here");
-    static_assert(sizeof(Cand) * kBoundSegCap >= 3 * 256 * sizeof(f32x4), "scratch of the slice merge");
-    f32x4* s_cz = reinterpret_cast<f32x4*>(s_c);  // (this workgroup selects nothing)
     if (fz.in_t == CSA_F32)
       csa_compress_body::compress_one<float, 256>(fz.jobs.j[0], fz.jobs.theta[0], 0, row, fz.rows, fz.m,
                                                   fz.row0_pos, fz.first_entry, s_cz, s_cz + 256, s_cz + 512,
@@ -888,38 +880,31 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
   const int r = row - b * T;
   const int V = (int)visible_entries(pos0[b] + r, m, n_max);
   const int K = k < V ? k : V;
-  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
-  int32_t* orow = idx + (int64_t)row * k;
-  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
-  if (K == V) {
-    if (blockIdx.x == 0) trivial_row(srow, V, k, kSplitThreads, orow, vrow);
-    return;
-  }
+  if (K == V) return;                          // the finishing launch writes the trivial row
   const int nact = (V + kChunk - 1) / kChunk;  // chunks holding visible entries
   if ((int)blockIdx.x >= nact) return;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   const int lo = blockIdx.x * kChunk;
   const int hi = min(lo + kChunk, V);
   const ChunkKeys ck = load_chunk(srow, lo, hi, n_max);
 
   // tau from the bound keys (held in registers when they fit)
   const uint32_t* brow = bound + (int64_t)row * nb;
-  // up to KBK * 256 keys stay in registers (8: caches up to 2^18 entries with one bound set per run; 16:
-  // up to 2^19), the register count chosen by the launch so that the common case keeps its occupancy
+  // up to KBK * 256 keys stay in registers (8: caches up to 2^18 entries with one bound set per 256 entries;
+  // 16: up to 2^19), the register count chosen by the launch so that the common case keeps its occupancy
   constexpr int kBk = KBK;
   const bool breg = nb <= kBk * kSplitThreads;  // (uniform)
-  constexpr int nbi = kBk;
-  // A zero key stands for "no entry" (runs with fewer than two visible entries, e.g. the tail of a cache
+  // A zero key stands for "no entry" (sets with fewer than two visible entries, e.g. the tail of a cache
   // with room to grow): the key range, and so the radix pass's resolution, spans the real keys only, and
   // the bound is used only when at least K of them exist (else every visible entry is a candidate).
   uint32_t bk[kBk];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nz = 0u;
   if (breg) {
 #pragma unroll
-    for (int i = 0; i < kBk; ++i)
-      if (i < nbi) bk[i] = brow[min(tid + i * kSplitThreads, nb - 1)];
+    for (int i = 0; i < kBk; ++i) bk[i] = brow[min(tid + i * kSplitThreads, nb - 1)];
 #pragma unroll
     for (int i = 0; i < kBk; ++i)
-      if (i < nbi && tid + i * kSplitThreads < nb && bk[i] != 0u) {
+      if (tid + i * kSplitThreads < nb && bk[i] != 0u) {
         kmin = min(kmin, bk[i]);
         kmax = max(kmax, bk[i]);
         ++nz;
@@ -946,41 +931,225 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_kernel(
     if (breg) {
 #pragma unroll
       for (int i = 0; i < kBk; ++i)
-        if (i < nbi && tid + i * kSplitThreads < nb) f(bk[i]);
+        if (tid + i * kSplitThreads < nb) f(bk[i]);
     } else {
       for (int j = tid; j < nb; j += kSplitThreads) f(brow[j]);
     }
   };
-  // radix passes until tau carries at least 22 resolved bits: one pass after a long common prefix, a second
-  // when a low outlier key (a run of all-zero scores, say) leaves only the sign or exponent in common
-  while (known < 22) radix_step<kSplitThreads>(each_bound, tau, known, need, s_hist, s_w, s_sel);
+  // at least one radix pass, and a second while tau carries fewer than 16 resolved bits (a low outlier key,
+  // a run of all-zero scores say, can leave only the sign or exponent in common): 16 bits keep the keys
+  // between tau and the row's K-th key to a few per cent of K for smooth score distributions
+  for (bool first = true; known < 32 && (first || known < 16); first = false)
+    radix_step<kSplitThreads>(each_bound, tau, known, need, s_hist, s_w, s_sel);
   const uint32_t pmask = known >= 32 ? 0xFFFFFFFFu : ~((1u << (32 - known)) - 1u);
   tau &= pmask;
 
   uint32_t c_tot, g_tot;
-  // Publication without a cache write-back: the segment and its count are written with agent-scope
-  // stores, which the L2 of this XCD passes through to memory, and each thread waits until its stores
-  // have completed before the barrier that precedes the arrival count.  The last workgroup of the row
-  // reads them with agent-scope loads, which do not take lines another XCD may have left stale in its
-  // L2, issued only after it has seen every arrival.  (A device-scope release fence per workgroup, the
-  // general form, writes back the whole L2 each time and made the launch about twice as slow.)
-  compact_chunk<true>(ck, lo, tau, pmask, ws.seg + (int64_t)row * n_max, s_w, c_tot, g_tot);
-  if (tid == 0)
-    __hip_atomic_store(ws.cnt + (int64_t)row * nch + blockIdx.x, (g_tot << 16) | c_tot, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  compact_chunk(ck, lo, tau, pmask, ws.seg + (int64_t)row * n_max,
+                ws.blk + ((int64_t)row * nch + blockIdx.x) * kBlk, s_w, c_tot, g_tot);
+  if (tid == 0) {
+    ws.cnt[(int64_t)row * nch + blockIdx.x] = (g_tot << 16) | c_tot;
+    if (blockIdx.x == 0) {  // (every chunk derives the same tau)
+      ws.info[row * 4 + 0] = tau;
+      ws.info[row * 4 + 1] = (uint32_t)known;
+    }
+  }
+}
+
+constexpr int kFinishCap = 4096;  // candidates the finishing workgroup holds in LDS
+constexpr int kWaveSel = 64;      // K* is resolved by one wave once its bucket holds at most this many keys
+
+// The need-th largest among the keys of [lo, hi) in LDS that agree with pv on its top `known` bits (at most
+// kWaveSel of them), one bit at a time by one wave: count the keys that extend the resolved prefix with a 1;
+// if at least `need` do, the bit is 1, else those keys all rank above and the bit is 0.  On return pv is
+// that key and need the number of keys equal to it still to take.  Called by every lane of one wave.
+CSA_DEV void wave_select(const uint32_t* keys, int n, uint32_t& pv, int known, int& need) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t kk = lane < n ? keys[lane] : 0u;
+  const bool valid = lane < n;
+  pv &= known == 0 ? 0u : ~0u << (32 - known);
+  for (int bit = 31 - known; bit >= 0; --bit) {
+    const uint32_t want = (pv >> bit) | 1u;
+    const int c = (int)__popcll(__ballot(valid && (kk >> bit) == want));
+    if (c >= need)
+      pv |= 1u << bit;
+    else
+      need -= c;
+  }
+}
+
+__global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
+    const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
+    int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
+  // The work per workgroup is small and its code runs once per launch, so the code is kept short: the
+  // candidates are staged once in LDS and every later phase is a rolled loop over them.
+  __shared__ uint32_t s_key[kFinishCap];
+  __shared__ int32_t s_idx[kFinishCap];
+  __shared__ __align__(16) uint32_t s_hist[kBins];
+  __shared__ int s_pre[kBoundMaxChunks + 1];
+  __shared__ int s_n[kBoundMaxChunks];
+  __shared__ uint32_t s_w[2 * kSplitThreads / 64];
+  __shared__ uint32_t s_k[kWaveSel];
+  __shared__ int s_sel[2];
+  __shared__ int s_m;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
+  const int nch = (int)((n_max + kChunk - 1) / kChunk);
+  const int b = row / T;
+  const int r = row - b * T;
+  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const int K = k < V ? k : V;
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
+  int32_t* orow = idx + (int64_t)row * k;
+  float* vrow = vals ? vals + (int64_t)row * k : nullptr;
+  if (K == V) {
+    trivial_row(srow, V, k, kSplitThreads, orow, vrow);
+    return;
+  }
+  const int nact = (V + kChunk - 1) / kChunk;  // <= kBoundMaxChunks = the thread count
+  const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
+  const Cand* blk = ws.blk + (int64_t)row * nch * kBlk;
+  const Cand* seg = ws.seg + (int64_t)row * n_max;
+  // One round of loads: this thread's chunk count, the row's tau, and (rows of at most 64 active chunks)
+  // slots [16 t, 16 t + 16) of the compact blocks, i.e. part t % 4 of chunk t / 4's block.  Counts are
+  // clamped to a chunk's size.
+  constexpr int kSlots = 16;
+  constexpr int kParts = kBlk / kSlots;  // threads per chunk block
+  const bool regs = nact * kParts <= kSplitThreads;  // (uniform)
+  const uint32_t cv = tid < nact ? cnt[tid] : 0u;
+  const uint32_t tau = ws.info[row * 4 + 0];
+  int known = (int)ws.info[row * 4 + 1];
+  const int ch = tid / kParts;
+  u32x4 mine[kSlots / 2];
+  if (regs && ch < nact) {
+#pragma unroll
+    for (int j = 0; j < kSlots / 2; ++j) mine[j] = reinterpret_cast<const u32x4*>(blk + (int64_t)tid * kSlots)[j];
+  }
+  const uint32_t n_c = min(cv & 0xFFFFu, (uint32_t)kChunk), g_c = min(cv >> 16, (uint32_t)kChunk);
+  uint32_t pre, gpre, C, G;
+  block_excl_sum2<kSplitThreads>(n_c, g_c, s_w, pre, gpre, C, G);
+  if (tid < nact) {
+    s_pre[tid] = (int)pre;
+    s_n[tid] = (int)n_c;
+  }
+  if (tid == 0) s_m = 0;
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(ws.arrive + row, 1u) == (uint32_t)(nact - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  if (tid == 0) ws.arrive[row] = 0u;
-  finish_row<true, kBoundSegCap, kBoundMaxChunks>(srow, V, K, k, nact, ws.cnt + (int64_t)row * nch, ws.seg + (int64_t)row * n_max, n_max, tau, known, K,
-             true, orow, vrow, L);
+  if ((int)C < K || (int)C > kFinishCap) {  // (uniform) the bound did not prune: the full selection
+    row_select<kSplitThreads>(srow, V, K, k, orow, vrow, s_hist, nullptr, s_w, s_sel);
+    return;
+  }
+  // ---- the candidates into LDS in index order (chunk order is index order): the register-held block
+  // slots, then whatever the blocks did not hold (the segments' overflow; every block when not loaded)
+  if (regs && ch < nact) {
+    const int n = s_n[ch], base = s_pre[ch], i0 = (tid % kParts) * kSlots;
+#pragma unroll
+    for (int j = 0; j < kSlots / 2; ++j) {
+      if (i0 + 2 * j < n) {
+        s_key[base + i0 + 2 * j] = mine[j][0];
+        s_idx[base + i0 + 2 * j] = (int32_t)mine[j][1];
+      }
+      if (i0 + 2 * j + 1 < n) {
+        s_key[base + i0 + 2 * j + 1] = mine[j][2];
+        s_idx[base + i0 + 2 * j + 1] = (int32_t)mine[j][3];
+      }
+    }
+  }
+  if (__syncthreads_or(!regs || n_c > (uint32_t)kBlk)) {  // (uniform)
+    const int from = regs ? kBlk : 0;
+    for (int c = wave; c < nact; c += kSplitThreads / 64) {
+      const int n = s_n[c], base = s_pre[c];  // (wave-uniform)
+      for (int i = from + lane; i < n; i += 64) {
+        const Cand cd = i < kBlk ? blk[(int64_t)c * kBlk + i] : seg[(int64_t)c * kChunk + i];
+        s_key[base + i] = cd.key;
+        s_idx[base + i] = cd.idx;
+      }
+    }
+    __syncthreads();
+  }
+  const int nc = (int)C;
+  auto each = [&](auto f) {
+    for (int i = tid; i < nc; i += kSplitThreads) f(s_key[i]);
+  };
+
+  // ---- the K-th key among the C candidates: block radix passes while more than kWaveSel candidates share
+  // the resolved prefix, then one wave resolves the remaining bits among those
+  uint32_t kstar = tau;
+  int need = K, inbucket;
+  if ((int)G < K) {
+    need = K - (int)G;  // the K-th key shares tau's prefix, as do C - G candidates
+    inbucket = nc - (int)G;
+  } else {  // the candidates' range decides the first open bit
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    each([&](uint32_t kk) {
+      lo = min(lo, kk);
+      hi = max(hi, kk);
+    });
+    block_minmax<kSplitThreads>(lo, hi, s_w);
+    kstar = hi;
+    known = common_bits(lo, hi);
+    inbucket = nc;
+  }
+  while (known < 32 && inbucket > kWaveSel) {
+    radix_step<kSplitThreads>(each, kstar, known, need, s_hist, s_w, s_sel);
+    inbucket = (int)s_hist[(kstar >> (32 - known)) & 0x7FFu];  // the chosen digit's count
+    __syncthreads();                                           // (read before the next pass clears it)
+  }
+  if (known < 32) {  // (uniform) gather the bucket and finish in wave 0
+    const uint32_t hmask = known == 0 ? 0u : ~0u << (32 - known);
+    const uint32_t hp = kstar & hmask;
+    each([&](uint32_t kk) {
+      if ((kk & hmask) == hp) {
+        const int slot = atomicAdd(&s_m, 1);
+        if (slot < kWaveSel) s_k[slot] = kk;  // (the bucket holds at most kWaveSel keys)
+      }
+    });
+    __syncthreads();
+    if (wave == 0) {
+      wave_select(s_k, min(s_m, kWaveSel), kstar, known, need);
+      if (lane == 0) {
+        s_sel[0] = (int)kstar;
+        s_sel[1] = need;
+      }
+    }
+    __syncthreads();
+    kstar = (uint32_t)s_sel[0];
+    need = s_sel[1];
+  }
+  const int ties = need;  // keys equal to K* still to take, lowest index first
+
+  // ---- ordered output: thread t takes a contiguous range of the candidates; its first selected one lands
+  // after the larger keys of earlier threads and the equal keys they take
+  const int per = (nc + kSplitThreads - 1) / kSplitThreads;
+  const int j0 = min(tid * per, nc), j1 = min(j0 + per, nc);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t kk = s_key[j];
+    n_gt += kk > kstar;
+    n_eq += kk == kstar;
+  }
+  uint32_t gt_base, eq_base, gt_tot, eq_tot;
+  block_excl_sum2<kSplitThreads>(n_gt, n_eq, s_w, gt_base, eq_base, gt_tot, eq_tot);
+  int pos = (int)gt_base + min((int)eq_base, ties);
+  int eq_rank = (int)eq_base;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t kk = s_key[j];
+    bool sel = kk > kstar;
+    if (kk == kstar) sel = eq_rank++ < ties;
+    if (sel && pos < K) {
+      orow[pos] = s_idx[j];
+      if (vrow) vrow[pos] = key_to_score(kk);
+    }
+    pos += sel ? 1 : 0;
+  }
+  for (int j = K + tid; j < k; j += kSplitThreads) {
+    orow[j] = -1;
+    if (vrow) vrow[j] = -INFINITY;
+  }
 }
 
 // ------------------------------------------------------------------ row path with bound keys
 // Many rows (prefill) with the indexer's bound keys: one workgroup per row, no cross-workgroup work.
-// tau (the K-th largest bound key with 22 bits resolved, as in topk_bound_kernel) never exceeds the
+// tau (the K-th largest bound key with 22 bits resolved, derived as on the split path) never exceeds the
 // row's K-th largest key, so one streaming pass over the row keeps every key that can be selected: each
 // thread takes kRBPer consecutive keys of a chunk and one block scan writes the chunk's candidates into
 // LDS in index order.  The K-th key is then resolved among the candidates alone and the ascending list
@@ -1200,11 +1369,13 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
         grid.x += 1;
       }
       if (nb <= 8 * kSplitThreads)
-        hipLaunchKernelGGL((topk_bound_kernel<8>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
-                           pos0, m, k, bound, nb, idx, vals, s, fz);
+        hipLaunchKernelGGL((topk_bound_collect_kernel<8>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T,
+                           n_max, pos0, m, k, bound, nb, s, fz);
       else
-        hipLaunchKernelGGL((topk_bound_kernel<16>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
-                           pos0, m, k, bound, nb, idx, vals, s, fz);
+        hipLaunchKernelGGL((topk_bound_collect_kernel<16>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T,
+                           n_max, pos0, m, k, bound, nb, s, fz);
+      hipLaunchKernelGGL(topk_bound_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
+                         pos0, m, k, idx, vals, s);
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     } else {
       hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,
