@@ -30,16 +30,27 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 16;                      // 4 waves x 16 tiles x 16 entries = 1024 entries / WG
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 16;
+// Bound keys come in runs of 256 entries (one wave's range, or two waves' when a wave takes 128) and a
+// row holds four runs per 1024 entries (the last runs of a row may lie past n_max: their keys are 0).
+constexpr int kRun = 256;
+constexpr int kWavesPerRun = kRun / (kTilesPerWave * 16);
+static_assert((kWavesPerRun == 1 || kWavesPerRun == 2) && kWaves % kWavesPerRun == 0, "runs of whole waves");
+constexpr int kBoundSpan = 1024;
+// Workgroups per row: every run of the row's bound keys is written, so whole 1024-entry spans.
+__host__ __device__ inline int64_t index_slots(int64_t n_max) {
+  return (kBoundSpan / kEntriesPerWG) * ((n_max + kBoundSpan - 1) / kBoundSpan);
+}
 
 // Bound-key sets: two keys per 256 entries for caches of more than kFineBoundMax entries, otherwise two
 // per 32 entries, so that a short cache still holds enough keys (2k for k up to n_max / 32).  The decode
-// kernel's sets of a wave's 256-entry run are the whole run, or its eight interleaved 32-entry sets
-// {e : e mod 64 in [8 r, 8 r + 8)} (the entries one half of a 16-lane row writes); the tiled prefill kernel
-// takes each 64-entry tile's halves (fine) or 4 tiles (coarse).  The selector uses only the keys' values.
+// kernel's sets of a 256-entry run are the whole run, or its eight interleaved 32-entry sets
+// {e : e mod 64 in [8 r, 8 r + 8)} (the entries one half of a 16-lane row writes; the run's two waves
+// merge their halves); the tiled prefill kernel takes each 64-entry tile's halves (fine) or 4 tiles
+// (coarse).  The selector uses only the keys' values.
 constexpr int64_t kFineBoundMax = 65536;
 __host__ __device__ inline int bound_sets(int64_t n_max) { return n_max <= kFineBoundMax ? 8 : 1; }
 __host__ __device__ inline int64_t bound_keys_per_row(int64_t n_max) {
-  return 2 * kWaves * bound_sets(n_max) * ((n_max + kEntriesPerWG - 1) / kEntriesPerWG);
+  return 2 * (kBoundSpan / kRun) * bound_sets(n_max) * ((n_max + kBoundSpan - 1) / kBoundSpan);
 }
 constexpr int kRing = 4;                               // tiles in flight per wave
 
@@ -171,7 +182,7 @@ CSA_DEV void lds_read16(i32x4 (&o)[N], const uint32_t (&a)[N]) {
 
 // The compression launch folded into a decode index launch: the step's new KV entry and indexer key of
 // every sequence (entry first_entry), computed by the workgroup whose entry range holds the new key
-// (before it reads any tile, so its scores see the new key) and by workgroup 0 (the KV entry).
+// (before it reads any tile, so its scores see the new key) and by another early workgroup (the KV entry).
 struct IndexFuse {
   csa_compress_body::Jobs jobs;  // j[0]: the KV entry, j[1]: the indexer key, written into the key cache
   int rows, m, in_t;
@@ -220,11 +231,31 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int gl = lane >> 4;
+  // With compression work (the step's new indexer key, read by chunk fc, and its KV entry) row r's slot
+  // s serves entry chunk (s + fc - r) mod the slot count: slot r (mod the count) compresses the key
+  // before its tiles and slot r + 1 takes the KV entry, so the rows' compressing workgroups sit early in
+  // their rows and on different XCDs and CUs (workgroup i runs on XCD i mod 8) instead of sharing one.
   const int row = blockIdx.y;  // b * T + r
+  const int wslot = blockIdx.x;
+  const int nslots = (int)index_slots(n_max);
   const int b = row / T;
   const int r = row - b * T;
-  const int64_t wg_first = (int64_t)blockIdx.x * kEntriesPerWG;
   const int64_t srow = (int64_t)row * n_max;  // this row's first score
+  const int ik_slot = row % nslots, kv_slot = (row + 1) % nslots;
+  int64_t fc = 0;
+  [[maybe_unused]] int64_t tf = 0, fi = 0;
+  [[maybe_unused]] bool fdone = false;
+  if constexpr (FUSE && PAGED) {
+    tf = pos0[b];
+    fi = tf / fz.m - 1;
+    // (uniform) the block tf closes has an entry whose page is mapped
+    fdone = tf >= fz.m && tf % fz.m == 0 && (fi >> fz.jobs.j[0].plog2) < fz.jobs.j[0].tstride;
+    if (fdone) fc = fi / kEntriesPerWG;
+  } else if constexpr (FUSE) {
+    fc = fz.first_entry / kEntriesPerWG;
+  }
+  const int64_t chunk = FUSE ? ((int64_t)wslot + fc + nslots - ik_slot) % nslots : wslot;
+  const int64_t wg_first = chunk * kEntriesPerWG;
 
   if constexpr (FUSE && PAGED) {  // decode rows only (row == b): this token's csa_decode_append work
     constexpr int kScratch = 3 * 256;
@@ -232,13 +263,12 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     __shared__ __align__(16) f32x4 s_cz[kInLds ? 1 : kScratch];
     __shared__ float s_czr[4];
     f32x4* cz = kInLds ? reinterpret_cast<f32x4*>(s_lds) : s_cz;
-    const int64_t t = pos0[b];
+    const int64_t t = tf;
     const int m = fz.m;
-    const int64_t i = t / m - 1;
-    // (uniform) the block t closes has an entry whose page is mapped
-    const bool done = t >= m && t % m == 0 && (i >> fz.jobs.j[0].plog2) < fz.jobs.j[0].tstride;
-    const bool do_ik = done && (int64_t)blockIdx.x == i / kEntriesPerWG;  // its key, before this WG's tiles
-    const bool do_kv = t >= 0 && blockIdx.x == 0;
+    const int64_t i = fi;
+    const bool done = fdone;
+    const bool do_ik = done && wslot == ik_slot;  // its key, before this WG's tiles
+    const bool do_kv = t >= 0 && wslot == kv_slot;
     const bool f32in = fz.in_t == CSA_F32;
     if (do_ik) {
       if (f32in) {
@@ -279,8 +309,8 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     __shared__ __align__(16) f32x4 s_cz[kInLds ? 1 : kScratch];
     __shared__ float s_czr[4];
     f32x4* cz = kInLds ? reinterpret_cast<f32x4*>(s_lds) : s_cz;
-    const bool do_ik = (int64_t)blockIdx.x == fz.first_entry / kEntriesPerWG;
-    const bool do_kv = blockIdx.x == 0 && fz.jobs.j[0].out != nullptr;  // (no KV job: the key alone)
+    const bool do_ik = wslot == ik_slot;                                // chunk fc holds first_entry
+    const bool do_kv = wslot == kv_slot && fz.jobs.j[0].out != nullptr;  // (no KV job: the key alone)
     if (do_ik) {
       if (fz.in_t == CSA_F32)
         csa_compress_body::compress_one<float, 256>(fz.jobs.j[1], fz.jobs.theta[1], 0, row, fz.rows, fz.m,
@@ -501,8 +531,21 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     } else {
       wave_top2(top1, top2);
     }
-    if ((lane & 7) == 0 && (sets == 8 || lane == 0)) {
-      uint32_t* dst = bound + (int64_t)row * nbw + (((int64_t)blockIdx.x * kWaves + wave) * sets + (lane >> 3)) * 2;
+    const bool holder = (lane & 7) == 0 && (sets == 8 || lane == 0);
+    bool writer = holder;
+    if constexpr (kWavesPerRun == 2) {  // the odd wave hands its half of the run to the even one
+      __shared__ uint32_t s_bk[kWaves / 2][8][2];
+      if (holder && (wave & 1)) {
+        s_bk[wave >> 1][lane >> 3][0] = top1;
+        s_bk[wave >> 1][lane >> 3][1] = top2;
+      }
+      __syncthreads();
+      writer = holder && !(wave & 1);
+      if (writer) top2_merge(top1, top2, s_bk[wave >> 1][lane >> 3][0], s_bk[wave >> 1][lane >> 3][1]);
+    }
+    if (writer) {
+      const int64_t run = wave_first / kRun;
+      uint32_t* dst = bound + (int64_t)row * nbw + (run * sets + (lane >> 3)) * 2;
       dst[0] = top1;
       dst[1] = top2;
     }
@@ -723,7 +766,7 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
                       const csa_compress_body::AppendFuse* afz = nullptr) {
   if (pages) {  // decode rows over a paged key pool (with this token's append work when afz is given)
     if (fuse || T != 1) return CSA_ERR_UNSUPPORTED;
-    dim3 grid(ceil_div(n_max, kEntriesPerWG), B);
+    const dim3 grid((unsigned)index_slots(n_max), B);
     dim3 block(kWaves * 64);
 #define CSA_IDX_PAGED(NT)                                                                                   \
   if (afz)                                                                                                  \
@@ -749,7 +792,7 @@ csa_status launch_fmt(const void* q, const void* q_scale, const float* w, const 
                        (const uint8_t*)k, T, n_max, pos0, m, so, bound);
     return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
   }
-  dim3 grid(ceil_div(n_max, kEntriesPerWG), B * T);
+  const dim3 grid((unsigned)index_slots(n_max), (unsigned)(B * T));
   dim3 block(kWaves * 64);
 #define CSA_IDX_LAUNCH(NT)                                                                                       \
   if (fuse)                                                                                                     \
