@@ -302,7 +302,11 @@ csa_status csa_topk_compress(const void* scores, int score_t, int B, int64_t n_m
  * and accumulation).  Decode (T = 1) splits each query's entry list (compressed
  * part and window part separately) at fixed boundaries that depend only on the
  * list lengths and merges the parts in a fixed order, so results do not depend
- * on B or on the other rows.
+ * on B or on the other rows.  A part's output reaches the merge through the
+ * workspace in fp16, divided by its softmax denominator (a convex combination of
+ * entry values, so bounded by the largest entry magnitude; 2^-11 relative): on
+ * the CSA_BF16 decode path entry values must stay below 65504 in magnitude,
+ * which normalised entries (at most sqrt(c) times the largest gain) do.
  * Limits: c in {128, 256, 512}; rope_dims even, a multiple of 8 and <= min(c, 128);
  * H a multiple of 16 for CSA_BF16 (any H >= 1 for CSA_F32); 1 <= k <= 2048;
  * 1 <= n_win <= 4096.

@@ -54,7 +54,7 @@ struct AttnArgs {
   const float* gamma_kv;
   const int64_t* pos0;
   void* out;
-  float* ws_o;     // [rows][nsplit][H][C]
+  uint16_t* ws_o;  // [rows][nsplit][H][C] fp16: each part's output divided by its denominator
   float* ws_ml;    // [rows][nsplit][H][2]
   int T, H, R, k, n_win, m, out_t, mode, nsplit;
   int prepared;           // 0 raw rows; 1 compressed entries stored prepared; 2 window rows prepared too
@@ -775,15 +775,21 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   }
 
   if (a.nsplit > 1) {
-    // partial state of (row, part, head): O unnormalized over the wave's dims, plus M and L
+    // partial state of (row, part, head): O / L over the wave's dims in fp16, plus M and L.  O / L is a
+    // convex combination of entry values, so it is bounded by the largest entry magnitude (at most sqrt(c)
+    // times the largest gain for normalised entries), far inside fp16's range, and fp16 keeps it to 2^-11
+    // relative: half the bytes of float32 partials for the combine to read back.
     const int64_t base = ((int64_t)row * a.nsplit + sp) * a.H;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float* dst = a.ws_o + (base + h0 + 4 * g + i) * C + dbase + (lane & 15);
+      const float il = __shfl(inv, 4 * g + i, 64);  // the denominator of head 4g + i (lane-row index)
+      uint16_t* dst = a.ws_o + (base + h0 + 4 * g + i) * C + dbase + (lane & 15);
       // streaming stores: read once by the combine, so they are not left dirty in L2 for the end of
       // the kernel to write back
 #pragma unroll
-      for (int dt = 0; dt < DTW; ++dt) __builtin_nontemporal_store(O[dt][i], &dst[16 * dt]);
+      for (int dt = 0; dt < DTW; ++dt)
+        __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (_Float16)(O[dt][i] * il)), &dst[16 * dt]);
     }
     if ((WIDE || wave == 0) && g == 0) {
       a.ws_ml[(base + head) * 2 + 0] = M;
@@ -846,12 +852,12 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
   const int d0 = 4 * threadIdx.x;
   const bool active = d0 < C;
   const int dl = active ? d0 : 0;  // loads stay in the head's row
-  f32x4 os[kMaxSplits];
+  uint2 os[kMaxSplits];  // 4 fp16 values: the part's output over its denominator
   float ms[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < ns) {
-      os[s] = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
+      os[s] = *reinterpret_cast<const uint2*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
       ms[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2];
       ls[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1];
     }
@@ -867,10 +873,12 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     if (s < ns && ms[s] != -INFINITY) {  // fixed order over the parts
-      const float f = __builtin_amdgcn_exp2f(ms[s] - Mx);
-      Lt = fmaf(ls[s], f, Lt);
+      const float wl = ls[s] * __builtin_amdgcn_exp2f(ms[s] - Mx);
+      Lt += wl;
+      const uint32_t hw[2] = {os[s].x, os[s].y};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = fmaf(os[s][i], f, v[i]);
+      for (int i = 0; i < 4; ++i)
+        v[i] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(hw[i >> 1] >> (16 * (i & 1)))), wl, v[i]);
     }
   }
   if (!active) return;
@@ -1135,7 +1143,7 @@ size_t attend_workspace_bytes(int mode, int B, int T, int H, int c, int64_t ncom
   const int ns = max(split_layout(mode, T, H, 0, ncomp, n_win).nsplit, split_layout(mode, T, H, 2, ncomp, n_win).nsplit);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * T;
-  const size_t o = rows * ns * H * (size_t)c * 4;
+  const size_t o = rows * ns * H * (size_t)c * 2;  // fp16 partial outputs
   return ((o + 255) & ~(size_t)255) + rows * ns * H * 2 * 4;
 }
 
@@ -1181,8 +1189,8 @@ csa_status launch_attend(int mode, const void* q, const void* comp_kv, const flo
   a.s_c = lay.s_c;
   a.s_w = lay.s_w;
   if (a.nsplit > 1) {
-    const size_t o = (size_t)rows * a.nsplit * H * (size_t)c * 4;
-    a.ws_o = static_cast<float*>(ws);
+    const size_t o = (size_t)rows * a.nsplit * H * (size_t)c * 2;
+    a.ws_o = static_cast<uint16_t*>(ws);
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + ((o + 255) & ~(size_t)255));
   } else {
     a.ws_o = nullptr;
