@@ -538,6 +538,17 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
       }
       // S^T over the wave's dims: lane holds entries eb + 16nt + 4g + i, head lane&15
       f32x4 accs[2];
+      // narrow, c = 512: the tile's 8 operand chunks of this lane (entries eb + (lane & 15) and + 16, k-steps
+      // 0..3; both entries share a swizzle key) in one batched read, then two independent MFMA chains
+      constexpr bool kBatchQK = !WIDE && KSW == 4;
+      u32x4 qkrd[kBatchQK ? 8 : 1];
+      if constexpr (kBatchQK) {
+        const int e = eb + (lane & 15);
+        uint32_t qa[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) qa[v] = lds_addr(E + e * C + 8 * swz<C>(e, (dbase + 32 * v + 8 * g) >> 3));
+        lds_read_b128_x8<0, 32 * C>(qkrd, qa);
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -561,6 +572,12 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
             }
           });
           accs[nt] = acc;
+        } else if constexpr (kBatchQK) {
+#pragma unroll
+          for (int ks = 0; ks < KSW; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qkrd[4 * nt + ks]), qf[ks], acc,
+                                                          0, 0, 0);
+          s_part[(wave * 2 + nt) * 64 + lane] = acc;
         } else {
           const int e = eb + 16 * nt + (lane & 15);
           const uint16_t* er = E + e * C;
@@ -645,6 +662,25 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
             O[8 * J + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, O[8 * J + u], 0, 0, 0);
           }
         });
+      } else if constexpr (DTW == 8) {  // c = 512: the 16 transpose reads of the tile in one batch
+        const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
+        const int e_lo = eb + 4 * g + tr_r;  // rows e_lo and e_lo + 16 share a swizzle key
+        uint32_t ta[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int hw = dbase + 16 * dt + 4 * tr_c;
+          ta[dt] = lds_addr(E + e_lo * C + 8 * swz<C>(e_lo, hw >> 3) + (hw & 7));
+        }
+        i16x4 rd[16];
+        lds_read_tr16_x16<0, 32 * C>(rd, ta);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const i16x4 lo = rd[2 * dt], hi = rd[2 * dt + 1];
+          const bf16x8 ef =
+              __builtin_bit_cast(bf16x8, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, ef, O[dt], 0, 0, 0);
+        }
+        __syncthreads();  // s_part is rewritten by the next tile; E and the resolve buffer by the next stage
       } else {
         const int tr_r = (lane & 15) >> 2, tr_c = lane & 3;
         const int e_lo = eb + 4 * g + tr_r, e_hi = e_lo + 16;
