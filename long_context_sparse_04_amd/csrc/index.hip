@@ -569,13 +569,13 @@ constexpr int kPRowBytes = 256;                 // bf16 c^I = 128
 constexpr int kPDmaPerWave = kPTile * kPRowBytes / 1024 / kWaves;  // 1 KB per DMA instruction: 4 per wave
 
 template <int NT>
-__global__ __launch_bounds__(kWaves * 64) void index_prefill_bf16_kernel(
+__global__ __launch_bounds__(kWaves * 64, 2) void index_prefill_bf16_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ kI, int T,
     int64_t n_max, const int64_t* __restrict__ pos0, int m, ScoreOut so, uint32_t* __restrict__ bound) {
   constexpr int HI = NT * 16;
   __shared__ __align__(16) uint8_t s_k[2][kPTile * kPRowBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform: row arithmetic in SGPRs)
   const int gl = lane >> 4;
   const int b = blockIdx.y;
   const int r_first = blockIdx.x * kPRows;
