@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--proj", action="store_true",
                    help="decode: the step also runs the query up-projections from the latent (q and the indexer "
                         "queries, one launch) before it and the grouped output projection after it")
+    p.add_argument("--batch", type=int, default=None,
+                   help="decode: run the workload with this many sequences instead of its own batch (same shapes "
+                        "per sequence; each sequence's inputs are seeded by its index)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three plain 1 GiB device-to-device copies (reference for HBM byte counters)")
     return p.parse_args()
@@ -251,6 +254,11 @@ def main():
     from long_context_sparse_04_amd import _lib, api
 
     cfg = configs.get_config(a.config)
+    if a.batch is not None:
+        if cfg.T > 1 or a.batch < 1:
+            print("--batch takes a positive batch of a decode workload", file=sys.stderr)
+            sys.exit(2)
+        cfg = cfg.scaled(B=a.batch)
     prefill = cfg.T > 1
     _lib.load()
     dev = "cuda:0"
@@ -543,7 +551,7 @@ def main():
         kernels.append(entry("hca_attend", time_part("hca_attend"), hca_bytes, hca_flops, "mfma" if prefill else "hbm"))
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
-    if os.path.exists(tpath) and not a.paged and not a.proj:
+    if os.path.exists(tpath) and not a.paged and not a.proj and a.batch is None:
         t = json.load(open(tpath))
         if t.get("source_hash") == source_hash("index.hip") and t.get("index_scores", "f32") == a.scores:
             traffic = t.get("hbm_bytes_per_launch")
