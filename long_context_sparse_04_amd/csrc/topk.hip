@@ -958,6 +958,7 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(
 
 constexpr int kFinishCap = 4096;  // candidates the finishing workgroup holds in LDS
 constexpr int kWaveSel = 64;      // K* is resolved by one wave once its bucket holds at most this many keys
+constexpr int kSlotsMin = 16;     // compact-block slots per finishing thread for rows of up to 64 chunks
 
 // The need-th largest among the keys of [lo, hi) in LDS that agree with pv on its top `known` bits (at most
 // kWaveSel of them), one bit at a time by one wave: count the keys that extend the resolved prefix with a 1;
@@ -978,6 +979,7 @@ CSA_DEV void wave_select(const uint32_t* keys, int n, uint32_t& pv, int known, i
   }
 }
 
+template <int SLOTS>
 __global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m, int k,
     int32_t* __restrict__ idx, float* __restrict__ vals, SplitWs ws) {
@@ -1010,10 +1012,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
   const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
   const Cand* blk = ws.blk + (int64_t)row * nch * kBlk;
   const Cand* seg = ws.seg + (int64_t)row * n_max;
-  // One round of loads: this thread's chunk count, the row's tau, and (rows of at most 64 active chunks)
-  // slots [16 t, 16 t + 16) of the compact blocks, i.e. part t % 4 of chunk t / 4's block.  Counts are
+  // One round of loads: this thread's chunk count, the row's tau, and (rows of at most 256 / kParts active
+  // chunks) slots [SLOTS t, SLOTS t + SLOTS) of the compact blocks, i.e. part t % kParts of chunk
+  // t / kParts's block (SLOTS = 16: 64 chunks, the caches up to 2^18 entries; 32: 128 chunks).  Counts are
   // clamped to a chunk's size.
-  constexpr int kSlots = 16;
+  constexpr int kSlots = SLOTS;
   constexpr int kParts = kBlk / kSlots;  // threads per chunk block
   const bool regs = nact * kParts <= kSplitThreads;  // (uniform)
   const uint32_t cv = tid < nact ? cnt[tid] : 0u;
@@ -1374,8 +1377,12 @@ csa_status launch_topk(const void* scores, int score_t, int B, int T, int64_t n_
       else
         hipLaunchKernelGGL((topk_bound_collect_kernel<16>), grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T,
                            n_max, pos0, m, k, bound, nb, s, fz);
-      hipLaunchKernelGGL(topk_bound_finish_kernel, dim3(rows), dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max,
-                         pos0, m, k, idx, vals, s);
+      if (nch <= kSplitThreads * kSlotsMin / kBlk)
+        hipLaunchKernelGGL((topk_bound_finish_kernel<kSlotsMin>), dim3(rows), dim3(kSplitThreads), 0, stream, scores,
+                           sbf16, T, n_max, pos0, m, k, idx, vals, s);
+      else
+        hipLaunchKernelGGL((topk_bound_finish_kernel<2 * kSlotsMin>), dim3(rows), dim3(kSplitThreads), 0, stream,
+                           scores, sbf16, T, n_max, pos0, m, k, idx, vals, s);
       return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
     } else {
       hipLaunchKernelGGL(topk_split_hist_kernel, grid, dim3(kSplitThreads), 0, stream, scores, sbf16, T, n_max, pos0,

@@ -364,6 +364,18 @@ def test_topk_bound_cache_with_room(api):
     _topk_case(api, s, pos0, 4, k, "bound keys with room to grow", "index")
 
 
+def test_topk_bound_long_rows(api):
+    """Rows of 65 to 128 chunks of 4,096 scores (caches between 2^18 and 2^19 entries): the finishing
+    workgroup takes its compact blocks into registers at 32 slots per thread.  Rows with ties, with
+    visibility ending inside a chunk, and with fewer visible entries than 64 chunks."""
+    rng = np.random.default_rng(91)
+    N, k = 491520, 1024                   # 120 chunks
+    s = rng.standard_normal((3, 1, N)).astype(np.float32)
+    s[1, 0] = np.round(s[1, 0] * 16) / 16  # coarse ties
+    pos0 = [4 * N, 4 * (N - 3333) + 1, 4 * 200000]
+    _topk_case(api, s, pos0, 4, k, "bound keys, long rows", "index")
+
+
 def test_topk_workspace_reused_across_shapes(api):
     """One workspace serves split-path calls of different shapes: a call with more rows must not find the
     previous call's dirty regions where its zero-at-rest histograms live."""
