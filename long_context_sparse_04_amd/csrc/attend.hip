@@ -237,7 +237,7 @@ template <bool WIDE>
 constexpr int lds_ctrl_halfs() {
   constexpr int ne = WIDE ? 2 : 1, nr = WIDE ? 3 : 2;
   constexpr int bytes = 64 * 8 + nr * kStage * (8 + 8 + 8) + (kStage + 64) * 4 + nr * kStage * 4 + 3 * kStage * 4 +
-                        ne * kStage * 4 + 2 * nr * 4;
+                        ne * kStage * 4 + 2 * nr * 4 + 64 * 8;
   return ((bytes + 15) / 16) * 8;
 }
 
@@ -275,6 +275,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   float* s_scale = reinterpret_cast<float*>(s_idx3 + 3 * kStage);          // [NE][kStage] mixed rows' fp8 scales
   int* s_raw2 = reinterpret_cast<int*>(s_scale + NE * kStage);             // [NR] stage holds a raw row
   int* s_mix2 = s_raw2 + NR;                                               // [NR] stage holds mixed rows
+  float2* s_qcs = reinterpret_cast<float2*>(s_mix2 + NR);                  // [64] the query's RoPE cos, sin
   f32x4* s_part = reinterpret_cast<f32x4*>(s_mem + lds_ctrl_halfs<WIDE>());  // [4 waves][2][64 lanes] (narrow)
   uint16_t* E0 = reinterpret_cast<uint16_t*>(s_part + (WIDE ? 0 : 4 * 2 * 64));  // [NE][kStage][C]
 
@@ -310,6 +311,12 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
 #pragma unroll
   for (int ks = 0; ks < KSW; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
   if (threadIdx.x < 64) s_theta[threadIdx.x] = rt.theta[threadIdx.x];
+  // the query's rotation at t, once per RoPE pair for every head (wave 1, idle while wave 0 resolves slots)
+  if (threadIdx.x >= 64 && threadIdx.x < 64 + a.R / 2) {
+    float cs, sn;
+    rope_cs(tpos, rt.theta[threadIdx.x - 64], cs, sn);
+    s_qcs[threadIdx.x - 64] = float2{cs, sn};
+  }
   // slot resolution of a stage into buffer h of the resolve arrays, from the slots' index-list values
   // (threads < kStage, i.e. all of wave 0)
   auto commit_stage = [&](int64_t st0, int h, int32_t e_idx) {
@@ -478,8 +485,8 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
         if (d0 >= rope_lo) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            float cs, sn;
-            rope_cs(tpos, s_theta[(d0 - rope_lo) / 2 + p], cs, sn);
+            const float2 qcs = s_qcs[(d0 - rope_lo) / 2 + p];
+            const float cs = qcs.x, sn = qcs.y;
             const float x0 = x[2 * p], x1 = x[2 * p + 1];
             x[2 * p] = x0 * cs - x1 * sn;
             x[2 * p + 1] = x0 * sn + x1 * cs;

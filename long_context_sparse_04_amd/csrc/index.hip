@@ -30,11 +30,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTilesPerWave = 16;                      // 4 waves x 16 tiles x 16 entries = 1024 entries / WG
 constexpr int kEntriesPerWG = kWaves * kTilesPerWave * 16;
-// Bound keys come in runs of 256 entries (one wave's range, or two waves' when a wave takes 128) and a
-// row holds four runs per 1024 entries (the last runs of a row may lie past n_max: their keys are 0).
+// Bound keys come in runs of 256 entries (one wave's range) and a row holds four runs per 1024 entries.
 constexpr int kRun = 256;
-constexpr int kWavesPerRun = kRun / (kTilesPerWave * 16);
-static_assert((kWavesPerRun == 1 || kWavesPerRun == 2) && kWaves % kWavesPerRun == 0, "runs of whole waves");
+static_assert(kTilesPerWave * 16 == kRun, "a bound run is one wave's range");
 constexpr int kBoundSpan = 1024;
 // Workgroups per row: every run of the row's bound keys is written, so whole 1024-entry spans.
 __host__ __device__ inline int64_t index_slots(int64_t n_max) {
@@ -531,19 +529,7 @@ __global__ __launch_bounds__(kWaves * 64) void index_mfma_kernel(
     } else {
       wave_top2(top1, top2);
     }
-    const bool holder = (lane & 7) == 0 && (sets == 8 || lane == 0);
-    bool writer = holder;
-    if constexpr (kWavesPerRun == 2) {  // the odd wave hands its half of the run to the even one
-      __shared__ uint32_t s_bk[kWaves / 2][8][2];
-      if (holder && (wave & 1)) {
-        s_bk[wave >> 1][lane >> 3][0] = top1;
-        s_bk[wave >> 1][lane >> 3][1] = top2;
-      }
-      __syncthreads();
-      writer = holder && !(wave & 1);
-      if (writer) top2_merge(top1, top2, s_bk[wave >> 1][lane >> 3][0], s_bk[wave >> 1][lane >> 3][1]);
-    }
-    if (writer) {
+    if ((lane & 7) == 0 && (sets == 8 || lane == 0)) {
       const int64_t run = wave_first / kRun;
       uint32_t* dst = bound + (int64_t)row * nbw + (run * sets + (lane >> 3)) * 2;
       dst[0] = top1;

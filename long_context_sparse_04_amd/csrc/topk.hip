@@ -843,13 +843,14 @@ __global__ __launch_bounds__(kSplitThreads) void topk_split_finish_kernel(
 // selection takes two launches and no histogram pass:
 //  * collect: every chunk workgroup derives tau, the K-th largest bound key with the bits below its radix
 //    passes cleared (each pass takes the next 11 bits, starting right under the bits all bound keys share;
-//    one pass, or two while fewer than 16 bits are resolved); tau never exceeds the row's K-th largest key, so every selected key is
-//    a candidate (typically about 1.1 k keys are).  It compacts its chunk's keys >= tau in index order
-//    (the first kBlk into the chunk's compact block, the rest into its segment) and writes its counts.
-//  * finish: one workgroup per row reads the counts and the compact blocks in one round (each thread's
-//    block slots are then its candidates, in index order, held in registers), resolves the K-th key (radix
-//    passes while more than 64 candidates share the resolved prefix, then one wave bit by bit) and writes
-//    the ascending list.
+//    one pass, or two while fewer than 16 bits are resolved); tau never exceeds the row's K-th largest key,
+//    so every selected key is a candidate (typically about 1.1k keys are).  It compacts its chunk's keys
+//    >= tau in index order (the first kBlk into the chunk's compact block, the rest into its segment) and
+//    writes its counts.
+//  * finish: one workgroup per row reads the counts and the compact blocks in one round (a thread holds
+//    16 or 32 block slots in registers), stages the candidates in LDS in index order, resolves the K-th key
+//    (radix passes while more than 64 candidates share the resolved prefix, then one wave bit by bit) and
+//    writes the ascending list.
 // The launch boundary orders the two; no workgroup waits for another.
 template <int KBK>
 __global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(
