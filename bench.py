@@ -214,7 +214,9 @@ PROJ_SHAPES = {128: dict(d_c=1536, g=16, d_g=1024, d=7168), 64: dict(d_c=1024, g
 
 
 def _with_projections(cfg, api, torch, step, out, dev):
-    """Wrap a decode step: latent -> (q, q^I) before it, grouped output projection after it."""
+    """Wrap a step: latent -> (q, q^I) before it, grouped output projection after it.  Returns the wrapped
+    step and the two projection launches, each as (call on an input set, algorithmic bytes, FLOPs): the
+    weights and the rows read once, the outputs written once; 2 FLOPs per multiply-add."""
     ps = PROJ_SHAPES[cfg.H]
     rows = cfg.B * cfg.T
     x = gen.proj_inputs(rows, ps["d_c"], cfg.H, cfg.c, cfg.HI, cfg.cI, ps["g"], ps["d_g"], ps["d"], seed=3)
@@ -226,12 +228,25 @@ def _with_projections(cfg, api, torch, step, out, dev):
     hid = torch.empty((rows, ps["d"]), dtype=torch.bfloat16, device=dev)
     fmt = cfg.idx_dtype
 
-    def run(st):
+    def up(st):
         api.q_up_proj(cq, w_uq, w_iuq, cfg.H, cfg.c, cfg.HI, cfg.cI, qi_fmt=fmt, q=st["q"], qi=st["qi"],
                       qi_scale=st["qi_scale"])
-        step(st)
+
+    def down(st):
         api.grouped_out_proj(out.view(rows, cfg.H * cfg.c), w_g, w_o, ps["g"], mid=mid, out=hid)
-    return run
+
+    def run(st):
+        up(st)
+        step(st)
+        down(st)
+
+    d_c, nq, ni, gd = ps["d_c"], cfg.H * cfg.c, cfg.HI * cfg.cI, ps["g"] * ps["d_g"]
+    qi_row = {"f32": 4 * ni, "bf16": 2 * ni, "fp8": ni + 4 * cfg.HI, "mxfp4": ni // 2 + ni // 32}[fmt]
+    up_bytes = 2 * (nq + ni) * d_c + rows * (2 * d_c + 2 * nq + qi_row)
+    down_bytes = 2 * gd * nq // ps["g"] + 2 * ps["d"] * gd + rows * (2 * nq + 2 * 2 * gd + 2 * ps["d"])
+    parts = {"csa_q_up_proj": (up, up_bytes, 2 * rows * d_c * (nq + ni)),
+             "csa_grouped_out_proj": (down, down_bytes, 2 * rows * (nq * ps["d_g"] + gd * ps["d"]))}
+    return run, parts
 
 
 def source_hash(*names):
@@ -418,11 +433,9 @@ def main():
 
     if not a.paged:
         step = step_contiguous
+    proj_parts = {}
     if a.proj:
-        if prefill:
-            print("--proj runs decode workloads only", file=sys.stderr)
-            sys.exit(2)
-        step = _with_projections(cfg, api, torch, step, out, dev)
+        step, proj_parts = _with_projections(cfg, api, torch, step, out, dev)
     if a.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -485,18 +498,21 @@ def main():
                                                      out=hout, ws=hca_ws, kv_prepared=2, comp_scale=hca_scale)
         return p
 
-    def time_part(name):
+    def time_call(f):   # f(i) runs one launch on input set i; the average of a.steps launches
         for i in range(NSETS):
-            step_parts(sets[i])[name]()
-        calls = [step_parts(sets[i % NSETS])[name] for i in range(a.steps)]
+            f(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        for f in calls:
-            f()
+        for i in range(a.steps):
+            f(i)
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / a.steps
+
+    def time_part(name):
+        calls = [step_parts(sets[i % NSETS])[name] for i in range(max(a.steps, NSETS))]
+        return time_call(lambda i: calls[i]())
 
     sc_t = scores_paged if a.paged else scores
     Nsc = sc_t.shape[2]
@@ -549,6 +565,9 @@ def main():
     ]
     if cfg.with_hca and not a.paged:
         kernels.append(entry("hca_attend", time_part("hca_attend"), hca_bytes, hca_flops, "mfma" if prefill else "hbm"))
+    for pname, (pf, pbytes, pflops) in proj_parts.items():   # decode: a weight stream; prefill: MFMA-bound
+        kernels.append(entry(pname, time_call(lambda i: pf(sets[i % NSETS])), pbytes, pflops,
+                             "mfma" if prefill else "hbm"))
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"index_{cfg.name}_traffic.json")
     if os.path.exists(tpath) and not a.paged and not a.proj and a.batch is None:

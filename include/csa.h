@@ -472,7 +472,11 @@ csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* c
                             void* stream);
 
 /*
- * ---- Dense projections on either side of the step (decode rows) ----
+ * ---- Dense projections on either side of the step (decode and prefill rows) ----
+ *
+ * Up to 32 rows a call streams the weights (every weight byte read once, HBM-bound); more rows (chunked
+ * prefill) take an LDS-tiled MFMA product of 256-row x 128-column tiles (MFMA-bound).  Both accumulate in
+ * float32 over the whole K.
  *
  * Weights are passed PACKED (csa_pack_proj_weights): the [Z][N][K] output-major matrices (row n holds
  * output n's K weights) rearranged once, at load time, into 1 KB MFMA tiles so that the projections
@@ -495,8 +499,8 @@ csa_status csa_pack_proj_weights(const void* w, void* packed, int z, int n, int 
  *            (e4m3 codes, qi_scale float32 [rows][n_hI] = amax/448 of the head's values); or
  *            CSA_MXFP4_E8M0_B32 (cI/2 bytes per head, qi_scale [rows][n_hI][cI/32] E8M0 bytes)
  * Accumulation in float32 over d_c; bf16 results rounded to nearest even; quantized q^I is coded from
- * the float32 sums.  Limits: 1 <= rows <= 32; d_c a multiple of 32; n_h * c and n_hI * cI multiples
- * of 128; cI = 128 for the quantized forms.  CSA_ERR_NULL for a missing pointer.
+ * the float32 sums.  Limits: rows >= 0 (0: nothing is done); d_c a multiple of 32; n_h * c and n_hI * cI
+ * multiples of 128; cI = 128 for the quantized forms.  CSA_ERR_NULL for a missing pointer.
  */
 csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
                          int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, void* stream);
@@ -510,8 +514,8 @@ csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, in
  *   w_o  : bf16 [d][g * d_g]               packed with z = 1
  *   mid  : bf16 [rows][g * d_g]            (the intermediates, caller-owned, rounded to bf16)
  *   out  : bf16 [rows][d]
- * Two launches (the groups, then the final projection), float32 accumulation.  Limits: 1 <= rows <=
- * 32; (n_h / g) * c and g * d_g multiples of 32; d_g and d multiples of 16; g divides n_h.
+ * Two launches (the groups, then the final projection), float32 accumulation.  Limits: rows >= 0 (0:
+ * nothing is done); (n_h / g) * c and g * d_g multiples of 32; d_g and d multiples of 16; g divides n_h.
  */
 csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
                                 int d_g, int d, void* mid, void* out, void* stream);

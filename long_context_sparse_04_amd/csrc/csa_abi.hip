@@ -520,7 +520,6 @@ csa_status hca_attend_paged(const void* q, const void* comp_pool, const float* c
 csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
                          int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, void* stream) {
   if (rows < 0 || d_c < 32 || (d_c % 32) || n_h < 1 || c < 1 || n_hI < 1 || cI < 1) return CSA_ERR_SHAPE;
-  if (rows > 32) return CSA_ERR_UNSUPPORTED;
   if (((int64_t)n_h * c) % 128 || ((int64_t)n_hI * cI) % 128) return CSA_ERR_UNSUPPORTED;
   if ((int64_t)n_h * c >= ((int64_t)1 << 28) || (int64_t)n_hI * cI >= ((int64_t)1 << 28)) return CSA_ERR_SHAPE;
   if (qi_t != CSA_BF16 && qi_t != CSA_FP8_E4M3_ROWSCALE && qi_t != CSA_MXFP4_E8M0_B32) return CSA_ERR_UNSUPPORTED;
@@ -533,7 +532,6 @@ csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, in
 csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
                                 int d_g, int d, void* mid, void* out, void* stream) {
   if (rows < 0 || n_h < 1 || c < 1 || g < 1 || d_g < 1 || d < 1) return CSA_ERR_SHAPE;
-  if (rows > 32) return CSA_ERR_UNSUPPORTED;
   if (n_h % g) return CSA_ERR_SHAPE;
   const int64_t per = (int64_t)(n_h / g) * c;
   if (per % 32 || ((int64_t)g * d_g) % 32 || d_g % 16 || d % 16) return CSA_ERR_UNSUPPORTED;

@@ -1,4 +1,5 @@
-// Dense projections on either side of the attention step, for decode rows (at most 32 per call).
+// Dense projections on either side of the attention step: decode rows (at most 32 per call, a weight
+// stream) and prefill rows (more than 32, an LDS-tiled MFMA product).
 //
 // "【论文解读】DeepSeek-V4" (wkq9411.github.io), section 一(三)1(2)-(3): q = c^Q W^UQ and q^I = c^Q W^IUQ from
 // one shared latent c^Q; section 一(三)1(4): the grouped output projection (g groups of n_h / g heads, each
@@ -14,12 +15,18 @@
 // different column tiles over the whole K (the fused query launch: 128 columns, one indexer head, per
 // workgroup) or share 16 columns and split K four ways, summed in LDS in a fixed order (the output
 // projection: enough workgroups to keep every CU streaming).
+//
+// With many rows (chunked prefill) every weight tile serves many rows and the product is MFMA-bound: the
+// tiled kernel below stages 256-row x 128-column x 32-k tiles of both operands in LDS (global-to-LDS loads
+// into a three-stage ring, each 16-row or 16-column operand tile 1 KB in MFMA lane order, so every LDS
+// read is one contiguous, conflict-free 1 KB) and gives each wave a 128 x 64 block of the output.
 #include "csa_common.h"
 #include "csa_internal.h"
 
 namespace {
 
 constexpr int kProjThreads = 256;
+constexpr int kProjDecodeRows = 32;  // up to this many rows: the weight-streaming kernel
 constexpr int kUnroll = 4;  // k-steps whose loads are in flight together
 
 enum ProjEpi { kEpiBf16 = 0, kEpiFp8Head = 1, kEpiMxfp4 = 2 };
@@ -255,8 +262,239 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
     proj_body<MT, TPW1, KS1>(p, p.seg[1], (int)blockIdx.x - p.seg[0].blocks, s_red, s_amax);
 }
 
+// ---- Prefill rows: the LDS-tiled product ----
+// Workgroup tile kTM rows x kTN columns, k-steps of 32; wave w = 2 wm + wn owns rows 128 wm .. +128 and
+// columns 64 wn .. +64 of it (8 x 4 MFMA tiles of 16 x 16, 128 accumulator registers).  A stage holds the
+// 16 A tiles (16 rows x 32 k each: lane l's 16 bytes are row l % 16, k-group l / 16 -- the MFMA A operand)
+// and the 8 packed weight tiles (the B operand, already in that order in memory), 1 KB each.
+constexpr int kTM = 256, kTN = 128;
+constexpr int kTStages = 3;
+constexpr int kTStageBytes = (kTM + kTN) / 16 * 1024;            // 24 KB
+constexpr int kTDmaPerWave = kTStageBytes / 1024 / 4;            // 6 1-KB loads per wave and stage
+constexpr size_t kTLdsBytes = (size_t)kTStages * kTStageBytes;   // 72 KB
+
+// the segment, batch and tile of workgroup t (tiles of a segment: batch-major, then column tile, row tile
+// fastest)
+struct TiledMap {
+  int ntm;            // row tiles
+  int ntn[2];         // column tiles per batch of each segment
+  int64_t tiles0;     // tiles of segment 0
+  int64_t tiles;      // all tiles
+  int64_t per_xcd;    // tiles per XCD (the last XCDs may get fewer)
+};
+
+// The wave's 8 A and 4 B operand reads of one k-step in one block that waits for them: the reads are
+// kept out of the compiler's sight, since for LDS that global-to-LDS loads also fill it would first wait
+// for every outstanding load, draining the stages in flight.
+CSA_DEV void lds_read_ab(u32x4 (&a)[8], u32x4 (&b)[4], uint32_t aaddr, uint32_t baddr) {
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:0\n\tds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\tds_read_b128 %3, %12 offset:3072\n\t"
+      "ds_read_b128 %4, %12 offset:4096\n\tds_read_b128 %5, %12 offset:5120\n\t"
+      "ds_read_b128 %6, %12 offset:6144\n\tds_read_b128 %7, %12 offset:7168\n\t"
+      "ds_read_b128 %8, %13 offset:0\n\tds_read_b128 %9, %13 offset:1024\n\t"
+      "ds_read_b128 %10, %13 offset:2048\n\tds_read_b128 %11, %13 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7]),
+        "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+      : "v"(aaddr), "v"(baddr)
+      : "memory");
+}
+
+CSA_DEV uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__global__ __launch_bounds__(kProjThreads, 2) void proj_tiled_kernel(ProjArgs p, TiledMap mp) {
+  extern __shared__ __align__(1024) uint8_t s_ring[];   // kTStages x [16 A tiles | 8 B tiles] of 1 KB
+  __shared__ float s_amax[2][kTM];                     // fp8 epilogue: each column half's row maxima
+
+  // workgroup i runs on XCD i % 8: XCD x takes the contiguous tiles [x per_xcd, (x + 1) per_xcd), so the
+  // row tiles of one weight tile run together on one XCD and read the weights into its L2 once
+  const int64_t t = (int64_t)(blockIdx.x % 8) * mp.per_xcd + blockIdx.x / 8;
+  if (t >= mp.tiles) return;
+  const int si = t < mp.tiles0 ? 0 : 1;
+  const ProjSeg& sg = p.seg[si];
+  const int64_t tt = si ? t - mp.tiles0 : t;
+  const int mt = (int)(tt % mp.ntm);
+  const int64_t rest = tt / mp.ntm;
+  const int ntn = mp.ntn[si];
+  const int nt = (int)(rest % ntn);
+  const int z = (int)(rest / ntn);
+  const int m0 = mt * kTM, n0 = nt * kTN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 15, kg = lane >> 4;
+  const int nsteps = p.k / 32;
+  const int nct = sg.n / 16;   // 16-column tiles of the segment
+
+  // this wave's loads of a stage: 1-KB tile q = 6 wave + j, A tiles 0..15 then B tiles 16..23
+  const uint16_t* src[kTDmaPerWave];
+  int64_t step_elems[kTDmaPerWave];   // elements between k-steps
+#pragma unroll
+  for (int j = 0; j < kTDmaPerWave; ++j) {
+    const int q = kTDmaPerWave * wave + j;
+    if (q < 16) {
+      const int row = min(m0 + 16 * q + li, p.rows - 1);
+      src[j] = p.a + (int64_t)z * p.a_zoff + (int64_t)row * p.lda + 8 * kg;
+      step_elems[j] = 32;
+    } else {
+      const int ct = min(n0 / 16 + (q - 16), nct - 1);
+      src[j] = sg.w + (int64_t)z * sg.w_zstride + (int64_t)ct * nsteps * 512 + 8 * lane;
+      step_elems[j] = 512;
+    }
+  }
+  auto issue = [&](int s) {
+    uint8_t* stage = s_ring + (s % kTStages) * kTStageBytes;
+#pragma unroll
+    for (int j = 0; j < kTDmaPerWave; ++j)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + s * step_elems[j]),
+                                       (__attribute__((address_space(3))) void*)(stage + (kTDmaPerWave * wave + j) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t ring = lds_byte_addr(s_ring);
+  const uint32_t aoff = (uint32_t)(8 * wm) * 1024 + 16 * lane;
+  const uint32_t boff = 16 * 1024 + (uint32_t)(4 * wn) * 1024 + 16 * lane;
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int s = 0; s < nsteps; ++s) {
+    // stage s has landed once at most the next stage's loads are outstanding (vector memory operations
+    // complete in issue order)
+    if (s + 1 < nsteps)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTDmaPerWave) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // every wave's part of stage s is in; every wave is done with stage s - 1 (a bare barrier: the fence
+    // of __syncthreads would wait for the next stages' loads too)
+    __builtin_amdgcn_s_barrier();
+    if (s + 2 < nsteps) issue(s + 2);   // into stage s - 1's buffer
+    const uint32_t sb = ring + (uint32_t)((s % kTStages) * kTStageBytes);
+    u32x4 fa[8], fb[4];
+    lds_read_ab(fa, fb, sb + aoff, sb + boff);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i]),
+                                                            __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+  }
+
+  // lane l holds column n0 + 64 wn + 16 j + l % 16 of rows m0 + 128 wm + 16 i + 4 (l / 16) + v
+  const int64_t coff = (int64_t)z * sg.c_zoff;
+  const int rbase = m0 + 128 * wm + 4 * kg;
+  const int cbase = n0 + 64 * wn;
+  if (sg.epi == kEpiBf16) {
+    uint16_t* c = static_cast<uint16_t*>(sg.c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = rbase + 16 * i + v;
+        if (r < p.rows) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (cbase + 16 * j < sg.n)
+              c[(int64_t)r * sg.ldc + coff + cbase + 16 * j + li] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu);
+        }
+      }
+    return;
+  }
+  if (sg.epi == kEpiFp8Head) {  // one head = the workgroup's 128 columns: amax per row over both halves
+    uint8_t* c = static_cast<uint8_t*>(sg.c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float am = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(acc[i][j][v]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        if (li == 0) s_amax[wn][128 * wm + 16 * i + 4 * kg + v] = am;
+      }
+    __syncthreads();
+    const int head = n0 / 128;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rl = 128 * wm + 16 * i + 4 * kg + v;
+        const int r = m0 + rl;
+        const float scale = fmaxf(s_amax[0][rl], s_amax[1][rl]) / 448.0f;
+        if (r < p.rows) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            c[(int64_t)r * sg.ldc + cbase + 16 * j + li] =
+                (uint8_t)f32_to_e4m3(scale > 0.0f ? acc[i][j][v] / scale : 0.0f);
+          if (wn == 0 && li == 0) static_cast<float*>(sg.scale)[(int64_t)r * (sg.n / 128) + head] = scale;
+        }
+      }
+    return;
+  }
+  // MXFP4: MFMA tiles 2 h and 2 h + 1 form the 32-column block h; E8M0 scale floor(log2 amax) - 2, e2m1
+  // codes, element 2i in the low nibble
+  uint8_t* c = static_cast<uint8_t*>(sg.c);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = rbase + 16 * i + v;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float am = fmaxf(fabsf(acc[i][2 * h][v]), fabsf(acc[i][2 * h + 1][v]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        int X = -127;
+        if (am > 0.0f) {
+          int ex;
+          frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
+          X = ex - 1 - 2;
+          X = X < -127 ? -127 : (X > 127 ? 127 : X);
+        }
+        const int col0 = cbase + 32 * h;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t code = f32_to_e2m1(ldexpf(acc[i][2 * h + u][v], -X));
+          const uint32_t up = __shfl_xor(code, 1, 64);  // the odd column's code, to the even lane
+          if (r < p.rows && (li & 1) == 0) c[(int64_t)r * sg.ldc + (col0 + 16 * u + li) / 2] = (uint8_t)(code | (up << 4));
+        }
+        if (r < p.rows && li == 0) static_cast<uint8_t*>(sg.scale)[(int64_t)r * (sg.n / 32) + col0 / 32] = (uint8_t)(X + 127);
+      }
+    }
+}
+
+// p's segments over the tiled kernel (seg[1].n == 0: one segment); z batches
+csa_status launch_proj_tiled(const ProjArgs& p, int z, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute((const void*)proj_tiled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kTLdsBytes) != hipSuccess)
+      return CSA_ERR_LAUNCH;
+    attr_set = true;
+  }
+  TiledMap mp;
+  mp.ntm = (p.rows + kTM - 1) / kTM;
+  for (int i = 0; i < 2; ++i) mp.ntn[i] = (p.seg[i].n + kTN - 1) / kTN;
+  mp.tiles0 = (int64_t)z * mp.ntn[0] * mp.ntm;
+  mp.tiles = mp.tiles0 + (int64_t)z * mp.ntn[1] * mp.ntm;
+  mp.per_xcd = (mp.tiles + 7) / 8;
+  if (mp.per_xcd * 8 > (int64_t)INT32_MAX) return CSA_ERR_SHAPE;
+  hipLaunchKernelGGL(proj_tiled_kernel, dim3((unsigned)(mp.per_xcd * 8)), dim3(kProjThreads), kTLdsBytes, stream, p, mp);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
 template <int TPW0, int KS0, int TPW1, int KS1>
 csa_status launch_proj(const ProjArgs& p, int z, hipStream_t stream) {
+  if (p.rows > kProjDecodeRows) return launch_proj_tiled(p, z, stream);
   dim3 grid(p.seg[0].blocks + p.seg[1].blocks, z);
   if (p.rows <= 16)
     hipLaunchKernelGGL((proj_kernel<1, TPW0, KS0, TPW1, KS1>), grid, dim3(kProjThreads), 0, stream, p);

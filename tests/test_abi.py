@@ -266,7 +266,7 @@ def test_projection_validation(lib):
                  DUMMY, a["qi_t"], None)
 
     assert q(rows=0) == 0
-    assert q(rows=33) == 3                      # decode rows only
+    assert q(rows=-1) == 2
     assert q(d_c=1000) == 2                     # d_c a multiple of 32
     assert q(cI=64) == 3                        # quantized indexer queries: heads of 128
     assert q(qi_t=0) == 3
@@ -275,7 +275,8 @@ def test_projection_validation(lib):
     g = lib.csa_grouped_out_proj
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 12, 1024, 7168, DUMMY, DUMMY, None) == 2    # g must divide n_h
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1000, 7168, DUMMY, DUMMY, None) == 3    # d_g % 16
-    assert g(DUMMY, DUMMY, DUMMY, 40, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 3
+    assert g(DUMMY, DUMMY, DUMMY, -1, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 2
+    assert g(DUMMY, DUMMY, DUMMY, 0, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 0
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1024, 7168, None, DUMMY, None) == 1
 
 

@@ -6,7 +6,11 @@
     values and every decoded value lies within half an e4m3 step; the MXFP4 block scales equal the oracle
     encoder's and every decoded value lies within its e2m1 rounding;
   - csa_grouped_out_proj at the Pro shape (128 heads of 512 in 16 groups, d_g = 1024, d = 7168) and a small
-    ragged one: the bf16 intermediates within half a bf16 ulp of the oracle's, the output rel-L2 <= 5e-3.
+    ragged one: the bf16 intermediates within half a bf16 ulp of the oracle's, the output rel-L2 <= 5e-3;
+  - prefill rows (more than 32: the LDS-tiled product): 300 rows (two 256-row tiles, the second ragged) in
+    every indexer format and with ragged column tiles (d_g = 64, d = 272), and the chunked-prefill workload's
+    full size (4,096 rows at the Flash shapes: d_c = 1024, 64 heads of 512, 8 groups, d_g = 1024, d = 4096)
+    on sampled rows (tile edges and random rows) against the oracle computed for those rows alone.
 """
 import numpy as np
 import pytest
@@ -36,7 +40,7 @@ def _half_ulp_ok(got, ref, dot_scale):
     return np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5 * dot_scale)
 
 
-@pytest.mark.parametrize("rows", [4, 25])
+@pytest.mark.parametrize("rows", [4, 25, 300])
 @pytest.mark.parametrize("qi_fmt", ["bf16", "fp8", "mxfp4"])
 def test_q_up_proj(api, rows, qi_fmt):
     d_c, n_h, c, n_hI, cI = 1536, 16, 512, 64, 128
@@ -50,7 +54,11 @@ def test_q_up_proj(api, rows, qi_fmt):
     gq = host_f64(q).reshape(rows, -1)
     assert _half_ulp_ok(gq, rq, np.sqrt(d_c))
     assert rel_l2(gq, rq) <= 5e-3
-    rqi = rqi.reshape(rows, n_hI, cI)
+    _check_qi(qi, qs, rqi.reshape(rows, n_hI, cI), qi_fmt, d_c)
+
+
+def _check_qi(qi, qs, rqi, qi_fmt, d_c):
+    """q^I rows [rows][n_hI][cI] in qi_fmt against the oracle's float64 values."""
     if qi_fmt == "bf16":
         g = host_f64(qi)
         assert _half_ulp_ok(g, rqi, np.sqrt(d_c))
@@ -77,6 +85,7 @@ def test_q_up_proj(api, rows, qi_fmt):
 @pytest.mark.parametrize("shape", [
     dict(rows=4, n_h=128, c=512, g=16, d_g=1024, d=7168),     # Pro
     dict(rows=25, n_h=16, c=128, g=4, d_g=64, d=272),        # two row tiles, small groups
+    dict(rows=300, n_h=16, c=128, g=4, d_g=64, d=272),       # prefill rows: ragged row and column tiles
 ])
 def test_grouped_out_proj(api, shape):
     rows, n_h, c, g, d_g, d = (shape[k] for k in ("rows", "n_h", "c", "g", "d_g", "d"))
@@ -91,6 +100,30 @@ def test_grouped_out_proj(api, shape):
     assert _half_ulp_ok(gm, rmid, np.sqrt(n_h * c // g))
     e = rel_l2(host_f64(out), rout)
     say(f"  out rel-L2 {e:.2e}")
+    assert e <= 5e-3
+
+
+def test_proj_prefill_full_size_sampled(api):
+    """The chunked-prefill workload's 4,096 rows at the Flash projection shapes, on sampled rows."""
+    rows, d_c, n_h, c, n_hI, cI, g, d_g, d = 4096, 1024, 64, 512, 64, 128, 8, 1024, 4096
+    say(f"prefill projections rows={rows} d_c={d_c} heads={n_h}x{c} qI {n_hI}x{cI} g={g} d_g={d_g} d={d}")
+    x = gen.proj_inputs(rows, d_c, n_h, c, n_hI, cI, g, d_g, d, seed=11)
+    pk = api.pack_proj_weights
+    q, qi, _ = api.q_up_proj(dev(x["cq"]), pk(dev(x["w_uq"])), pk(dev(x["w_iuq"])), n_h, c, n_hI, cI)
+    out, mid = api.grouped_out_proj(dev(x["o"]), pk(dev(x["w_g"])), pk(dev(x["w_o"])), g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    edges = [0, 1, 15, 16, 127, 128, 255, 256, 257, 2047, 2048, 4094, 4095]
+    sel = np.unique(np.concatenate([edges, rng.integers(0, rows, 19)]))
+    st = torch.from_numpy(sel).to(q.device)
+    v = oracle.decode_bf16
+    rq, rqi = oracle.q_up_proj(v(x["cq"][sel]), v(x["w_uq"]), v(x["w_iuq"]))
+    assert _half_ulp_ok(host_f64(q.reshape(rows, -1)[st]), rq, np.sqrt(d_c))
+    _check_qi(qi[st], None, rqi.reshape(len(sel), n_hI, cI), "bf16", d_c)
+    rout, rmid = oracle.grouped_out_proj(v(x["o"][sel]), v(x["w_g"]), v(x["w_o"]), g)
+    assert _half_ulp_ok(host_f64(mid[st]), rmid, np.sqrt(n_h * c // g))
+    e = rel_l2(host_f64(out[st]), rout)
+    say(f"  {len(sel)} sampled rows; out rel-L2 {e:.2e}")
     assert e <= 5e-3
 
 
