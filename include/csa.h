@@ -500,7 +500,9 @@ csa_status csa_pack_proj_weights(const void* w, void* packed, int z, int n, int 
  *            CSA_MXFP4_E8M0_B32 (cI/2 bytes per head, qi_scale [rows][n_hI][cI/32] E8M0 bytes)
  * Accumulation in float32 over d_c; bf16 results rounded to nearest even; quantized q^I is coded from
  * the float32 sums.  Limits: rows >= 0 (0: nothing is done); d_c a multiple of 32; n_h * c and n_hI * cI
- * multiples of 128; cI = 128 for the quantized forms.  CSA_ERR_NULL for a missing pointer.
+ * multiples of 128; cI = 128 for the quantized forms.  CSA_ERR_NULL for a missing pointer;
+ * CSA_ERR_UNSUPPORTED unless cq and the weights are 16-byte aligned, q 8-byte aligned and qi 8- (bf16),
+ * 4- (fp8) or 2-byte (MXFP4) aligned.
  */
 csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, int rows, int d_c, int n_h, int c,
                          int n_hI, int cI, void* q, void* qi, void* qi_scale, int qi_t, void* stream);
@@ -515,7 +517,8 @@ csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, in
  *   mid  : bf16 [rows][g * d_g]            (the intermediates, caller-owned, rounded to bf16)
  *   out  : bf16 [rows][d]
  * Two launches (the groups, then the final projection), float32 accumulation.  Limits: rows >= 0 (0:
- * nothing is done); (n_h / g) * c and g * d_g multiples of 32; d_g and d multiples of 16; g divides n_h.
+ * nothing is done); (n_h / g) * c and g * d_g multiples of 32; d_g and d multiples of 16; g divides n_h;
+ * o, the weights and mid 16-byte aligned, out 8-byte aligned (else CSA_ERR_UNSUPPORTED).
  */
 csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o, int rows, int n_h, int c, int g,
                                 int d_g, int d, void* mid, void* out, void* stream);

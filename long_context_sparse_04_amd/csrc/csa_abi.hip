@@ -526,6 +526,10 @@ csa_status csa_q_up_proj(const void* cq, const void* w_uq, const void* w_iuq, in
   if (qi_t != CSA_BF16 && cI != 128) return CSA_ERR_UNSUPPORTED;
   if (rows == 0) return CSA_OK;
   if (!cq || !w_uq || !w_iuq || !q || !qi || (qi_t != CSA_BF16 && !qi_scale)) return CSA_ERR_NULL;
+  // 16-byte operand loads; 8-byte bf16 / 4-byte fp8 / 2-byte MXFP4 result stores
+  const uintptr_t qi_align = qi_t == CSA_BF16 ? 7 : (qi_t == CSA_FP8_E4M3_ROWSCALE ? 3 : 1);
+  if ((((uintptr_t)cq | (uintptr_t)w_uq | (uintptr_t)w_iuq) & 15) || ((uintptr_t)q & 7) || ((uintptr_t)qi & qi_align))
+    return CSA_ERR_UNSUPPORTED;
   return launch_q_up_proj(cq, w_uq, w_iuq, rows, d_c, n_h, c, n_hI, cI, q, qi, qi_scale, qi_t, (hipStream_t)stream);
 }
 
@@ -538,6 +542,8 @@ csa_status csa_grouped_out_proj(const void* o, const void* w_g, const void* w_o,
   if (per >= ((int64_t)1 << 28) || (int64_t)g * d_g >= ((int64_t)1 << 28) || g >= 65536) return CSA_ERR_SHAPE;
   if (rows == 0) return CSA_OK;
   if (!o || !w_g || !w_o || !mid || !out) return CSA_ERR_NULL;
+  if ((((uintptr_t)o | (uintptr_t)w_g | (uintptr_t)w_o | (uintptr_t)mid) & 15) || ((uintptr_t)out & 7))
+    return CSA_ERR_UNSUPPORTED;   // 16-byte operand loads, 8-byte result stores
   return launch_grouped_out_proj(o, w_g, w_o, rows, n_h, c, g, d_g, d, mid, out, (hipStream_t)stream);
 }
 

@@ -263,18 +263,22 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
 }
 
 // ---- Prefill rows: the LDS-tiled product ----
-// Workgroup tile kTM rows x kTN columns, k-steps of 32; wave w = 2 wm + wn owns rows 128 wm .. +128 and
-// columns 64 wn .. +64 of it (8 x 4 MFMA tiles of 16 x 16, 128 accumulator registers).  A stage holds the
-// 16 A tiles (16 rows x 32 k each: lane l's 16 bytes are row l % 16, k-group l / 16 -- the MFMA A operand)
-// and the 8 packed weight tiles (the B operand, already in that order in memory), 1 KB each.
-constexpr int kTM = 256, kTN = 128;
-constexpr int kTStages = 3;
-constexpr int kTStageBytes = (kTM + kTN) / 16 * 1024;            // 24 KB
-constexpr int kTDmaPerWave = kTStageBytes / 1024 / 4;            // 6 1-KB loads per wave and stage
-constexpr size_t kTLdsBytes = (size_t)kTStages * kTStageBytes;   // 72 KB
+// Workgroup tile kTM rows x kTN columns (8 waves), k-steps of 32; wave w = 4 wm + wn owns rows 128 wm .. +128
+// and columns 64 wn .. +64 of it (8 x 4 MFMA tiles of 16 x 16, 128 accumulator registers).  A stage holds
+// the 16 A tiles (16 rows x 32 k each: lane l's 16 bytes are row l % 16, k-group l / 16) and the 16 packed
+// weight tiles (16 columns x 32 k in the same lane order, as they lie in memory), 1 KB each; a ring of
+// kTStages stages keeps kTStages - 1 of them in flight, which is what covers the fetch latency (the product
+// is MFMA-bound only while the next stages keep arriving).  The MFMA takes the weight tile as its first
+// operand, so that lane l's four results are columns 4 (l / 16) .. +4 of row l % 16 (one 8-byte store).
+constexpr int kTM = 256, kTN = 256;
+constexpr int kTThreads = 512;
+constexpr int kTStages = 5;
+constexpr int kTStageBytes = (kTM + kTN) / 16 * 1024;            // 32 KB
+constexpr int kTDmaPerWave = kTStageBytes / 1024 / (kTThreads / 64);  // 4 1-KB loads per wave and stage
+constexpr size_t kTLdsBytes = (size_t)kTStages * kTStageBytes;   // 160 KB
+constexpr int kTGroupRows = 4;   // row tiles per group of the tile order
 
-// the segment, batch and tile of workgroup t (tiles of a segment: batch-major, then column tile, row tile
-// fastest)
+// the segment, batch and tile of workgroup t
 struct TiledMap {
   int ntm;            // row tiles
   int ntn[2];         // column tiles per batch of each segment
@@ -305,54 +309,55 @@ CSA_DEV uint32_t lds_byte_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__global__ __launch_bounds__(kProjThreads, 2) void proj_tiled_kernel(ProjArgs p, TiledMap mp) {
-  extern __shared__ __align__(1024) uint8_t s_ring[];   // kTStages x [16 A tiles | 8 B tiles] of 1 KB
-  __shared__ float s_amax[2][kTM];                     // fp8 epilogue: each column half's row maxima
+__global__ __launch_bounds__(kTThreads, 1) void proj_tiled_kernel(ProjArgs p, TiledMap mp) {
+  extern __shared__ __align__(1024) uint8_t s_ring[];   // kTStages x [16 A tiles | 16 B tiles] of 1 KB
 
-  // workgroup i runs on XCD i % 8: XCD x takes the contiguous tiles [x per_xcd, (x + 1) per_xcd), so the
-  // row tiles of one weight tile run together on one XCD and read the weights into its L2 once
+  // workgroup i runs on XCD i % 8: XCD x takes the contiguous tiles [x per_xcd, (x + 1) per_xcd); within a
+  // segment and batch the tiles go in groups of kTGroupRows row tiles, row tile fastest, so that the
+  // workgroups an XCD runs together share a few row tiles and a few weight tiles in its L2
   const int64_t t = (int64_t)(blockIdx.x % 8) * mp.per_xcd + blockIdx.x / 8;
   if (t >= mp.tiles) return;
   const int si = t < mp.tiles0 ? 0 : 1;
   const ProjSeg& sg = p.seg[si];
   const int64_t tt = si ? t - mp.tiles0 : t;
-  const int mt = (int)(tt % mp.ntm);
-  const int64_t rest = tt / mp.ntm;
   const int ntn = mp.ntn[si];
-  const int nt = (int)(rest % ntn);
-  const int z = (int)(rest / ntn);
-  const int m0 = mt * kTM, n0 = nt * kTN;
+  const int64_t per_z = (int64_t)ntn * mp.ntm;
+  const int z = (int)(tt / per_z);
+  const int64_t L = tt % per_z;
+  const int64_t gsz = (int64_t)kTGroupRows * ntn;
+  const int mfirst = (int)(L / gsz) * kTGroupRows;
+  const int gm = min(kTGroupRows, mp.ntm - mfirst);
+  const int rem = (int)(L % gsz);
+  const int m0 = (mfirst + rem % gm) * kTM, n0 = (rem / gm) * kTN;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int li = lane & 15, kg = lane >> 4;
   const int nsteps = p.k / 32;
   const int nct = sg.n / 16;   // 16-column tiles of the segment
 
-  // this wave's loads of a stage: 1-KB tile q = 6 wave + j, A tiles 0..15 then B tiles 16..23
+  // this wave's loads of a stage: 1-KB tiles 4 wave .. +4, A tiles 0..15 (waves 0-3), B tiles 16..31
+  const bool is_a = wave < 4;
   const uint16_t* src[kTDmaPerWave];
-  int64_t step_elems[kTDmaPerWave];   // elements between k-steps
 #pragma unroll
   for (int j = 0; j < kTDmaPerWave; ++j) {
     const int q = kTDmaPerWave * wave + j;
-    if (q < 16) {
+    if (is_a) {
       const int row = min(m0 + 16 * q + li, p.rows - 1);
       src[j] = p.a + (int64_t)z * p.a_zoff + (int64_t)row * p.lda + 8 * kg;
-      step_elems[j] = 32;
     } else {
       const int ct = min(n0 / 16 + (q - 16), nct - 1);
       src[j] = sg.w + (int64_t)z * sg.w_zstride + (int64_t)ct * nsteps * 512 + 8 * lane;
-      step_elems[j] = 512;
     }
   }
+  const int step_elems = is_a ? 32 : 512;   // elements between k-steps
   auto issue = [&](int s) {
-    uint8_t* stage = s_ring + (s % kTStages) * kTStageBytes;
+    uint8_t* stage = s_ring + (s % kTStages) * kTStageBytes + kTDmaPerWave * wave * 1024;
 #pragma unroll
     for (int j = 0; j < kTDmaPerWave; ++j)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + s * step_elems[j]),
-                                       (__attribute__((address_space(3))) void*)(stage + (kTDmaPerWave * wave + j) * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[j] + (int64_t)s * step_elems),
+                                       (__attribute__((address_space(3))) void*)(stage + j * 1024), 16, 0, 0);
   };
 
   f32x4 acc[8][4];
@@ -364,19 +369,25 @@ __global__ __launch_bounds__(kProjThreads, 2) void proj_tiled_kernel(ProjArgs p,
   const uint32_t ring = lds_byte_addr(s_ring);
   const uint32_t aoff = (uint32_t)(8 * wm) * 1024 + 16 * lane;
   const uint32_t boff = 16 * 1024 + (uint32_t)(4 * wn) * 1024 + 16 * lane;
-  issue(0);
-  if (nsteps > 1) issue(1);
+#pragma unroll
+  for (int s = 0; s < kTStages - 1; ++s)
+    if (s < nsteps) issue(s);
   for (int s = 0; s < nsteps; ++s) {
-    // stage s has landed once at most the next stage's loads are outstanding (vector memory operations
-    // complete in issue order)
-    if (s + 1 < nsteps)
+    // stage s has landed once at most the later stages' loads are outstanding (vector memory operations
+    // complete in issue order): kTStages - 2 stages after it, fewer near the end
+    const int later = min(kTStages - 2, nsteps - 1 - s);
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kTDmaPerWave) : "memory");
+    else if (later == 2)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kTDmaPerWave) : "memory");
+    else if (later == 1)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTDmaPerWave) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // every wave's part of stage s is in; every wave is done with stage s - 1 (a bare barrier: the fence
-    // of __syncthreads would wait for the next stages' loads too)
+    // of __syncthreads would wait for the later stages' loads too)
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < nsteps) issue(s + 2);   // into stage s - 1's buffer
+    if (s + kTStages - 1 < nsteps) issue(s + kTStages - 1);   // into stage s - 1's buffer
     const uint32_t sb = ring + (uint32_t)((s % kTStages) * kTStageBytes);
     u32x4 fa[8], fb[4];
     lds_read_ab(fa, fb, sb + aoff, sb + boff);
@@ -384,92 +395,100 @@ __global__ __launch_bounds__(kProjThreads, 2) void proj_tiled_kernel(ProjArgs p,
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[i]),
-                                                            __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fb[j]),
+                                                            __builtin_bit_cast(bf16x8, fa[i]), acc[i][j], 0, 0, 0);
   }
 
-  // lane l holds column n0 + 64 wn + 16 j + l % 16 of rows m0 + 128 wm + 16 i + 4 (l / 16) + v
+  // lane l holds columns n0 + 64 wn + 16 j + 4 (l / 16) + v, v = 0..3, of row m0 + 128 wm + 16 i + l % 16
   const int64_t coff = (int64_t)z * sg.c_zoff;
-  const int rbase = m0 + 128 * wm + 4 * kg;
-  const int cbase = n0 + 64 * wn;
+  const int rbase = m0 + 128 * wm + li;
+  const int cbase = n0 + 64 * wn + 4 * kg;
   if (sg.epi == kEpiBf16) {
     uint16_t* c = static_cast<uint16_t*>(sg.c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int r = rbase + 16 * i;
+      if (r < p.rows) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = rbase + 16 * i + v;
-        if (r < p.rows) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (cbase + 16 * j < sg.n)
-              c[(int64_t)r * sg.ldc + coff + cbase + 16 * j + li] = (uint16_t)(pack_bf16x2(acc[i][j][v], 0.0f) & 0xFFFFu);
-        }
+        for (int j = 0; j < 4; ++j)
+          if (cbase + 16 * j < sg.n)
+            *reinterpret_cast<u32x2*>(c + (int64_t)r * sg.ldc + coff + cbase + 16 * j) =
+                u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
       }
+    }
     return;
   }
-  if (sg.epi == kEpiFp8Head) {  // one head = the workgroup's 128 columns: amax per row over both halves
+  if (sg.epi == kEpiFp8Head) {  // a head = 128 columns = waves wn and wn ^ 1: amax per row over both
+    __syncthreads();            // every wave is done with the ring, which now holds the row maxima
+    float* s_amax = reinterpret_cast<float*>(s_ring);   // [4][kTM]
     uint8_t* c = static_cast<uint8_t*>(sg.c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      float am = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float am = 0.0f;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) am = fmaxf(am, fabsf(acc[i][j][v]));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-        if (li == 0) s_amax[wn][128 * wm + 16 * i + 4 * kg + v] = am;
-      }
+        for (int v = 0; v < 4; ++v) am = fmaxf(am, fabsf(acc[i][j][v]));
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      if (kg == 0) s_amax[wn * kTM + 128 * wm + 16 * i + li] = am;
+    }
     __syncthreads();
-    const int head = n0 / 128;
+    const int head = (n0 + 64 * wn) / 128;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int rl = 128 * wm + 16 * i + li;
+      const int r = m0 + rl;
+      const float scale = fmaxf(s_amax[(wn & 2) * kTM + rl], s_amax[((wn & 2) + 1) * kTM + rl]) / 448.0f;
+      if (r < p.rows && cbase < sg.n) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int rl = 128 * wm + 16 * i + 4 * kg + v;
-        const int r = m0 + rl;
-        const float scale = fmaxf(s_amax[0][rl], s_amax[1][rl]) / 448.0f;
-        if (r < p.rows) {
+        for (int j = 0; j < 4; ++j) {
+          uint32_t w = 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            c[(int64_t)r * sg.ldc + cbase + 16 * j + li] =
-                (uint8_t)f32_to_e4m3(scale > 0.0f ? acc[i][j][v] / scale : 0.0f);
-          if (wn == 0 && li == 0) static_cast<float*>(sg.scale)[(int64_t)r * (sg.n / 128) + head] = scale;
+          for (int v = 0; v < 4; ++v)
+            w |= f32_to_e4m3(scale > 0.0f ? acc[i][j][v] / scale : 0.0f) << (8 * v);
+          *reinterpret_cast<uint32_t*>(c + (int64_t)r * sg.ldc + cbase + 16 * j) = w;
         }
+        if ((wn & 1) == 0 && kg == 0) static_cast<float*>(sg.scale)[(int64_t)r * (sg.n / 128) + head] = scale;
       }
+    }
     return;
   }
   // MXFP4: MFMA tiles 2 h and 2 h + 1 form the 32-column block h; E8M0 scale floor(log2 amax) - 2, e2m1
   // codes, element 2i in the low nibble
   uint8_t* c = static_cast<uint8_t*>(sg.c);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 8; ++i) {
+    const int r = rbase + 16 * i;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = rbase + 16 * i + v;
+    for (int h = 0; h < 2; ++h) {
+      float am = 0.0f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float am = fmaxf(fabsf(acc[i][2 * h][v]), fabsf(acc[i][2 * h + 1][v]));
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-        int X = -127;
-        if (am > 0.0f) {
-          int ex;
-          frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
-          X = ex - 1 - 2;
-          X = X < -127 ? -127 : (X > 127 ? 127 : X);
-        }
-        const int col0 = cbase + 32 * h;
+        for (int v = 0; v < 4; ++v) am = fmaxf(am, fabsf(acc[i][2 * h + u][v]));
+      am = fmaxf(am, __shfl_xor(am, 16, 64));
+      am = fmaxf(am, __shfl_xor(am, 32, 64));
+      int X = -127;
+      if (am > 0.0f) {
+        int ex;
+        frexpf(am, &ex);  // am = f * 2^ex, f in [0.5, 1)
+        X = ex - 1 - 2;
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      }
+      const int col0 = n0 + 64 * wn + 32 * h;
+      if (r < p.rows && col0 < sg.n) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const uint32_t code = f32_to_e2m1(ldexpf(acc[i][2 * h + u][v], -X));
-          const uint32_t up = __shfl_xor(code, 1, 64);  // the odd column's code, to the even lane
-          if (r < p.rows && (li & 1) == 0) c[(int64_t)r * sg.ldc + (col0 + 16 * u + li) / 2] = (uint8_t)(code | (up << 4));
+          uint32_t w = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) w |= f32_to_e2m1(ldexpf(acc[i][2 * h + u][v], -X)) << (4 * v);
+          *reinterpret_cast<uint16_t*>(c + (int64_t)r * sg.ldc + (cbase + 32 * h + 16 * u) / 2) = (uint16_t)w;
         }
-        if (r < p.rows && li == 0) static_cast<uint8_t*>(sg.scale)[(int64_t)r * (sg.n / 32) + col0 / 32] = (uint8_t)(X + 127);
+        if (kg == 0) static_cast<uint8_t*>(sg.scale)[(int64_t)r * (sg.n / 32) + col0 / 32] = (uint8_t)(X + 127);
       }
     }
+  }
 }
 
 // p's segments over the tiled kernel (seg[1].n == 0: one segment); z batches
@@ -488,7 +507,7 @@ csa_status launch_proj_tiled(const ProjArgs& p, int z, hipStream_t stream) {
   mp.tiles = mp.tiles0 + (int64_t)z * mp.ntn[1] * mp.ntm;
   mp.per_xcd = (mp.tiles + 7) / 8;
   if (mp.per_xcd * 8 > (int64_t)INT32_MAX) return CSA_ERR_SHAPE;
-  hipLaunchKernelGGL(proj_tiled_kernel, dim3((unsigned)(mp.per_xcd * 8)), dim3(kProjThreads), kTLdsBytes, stream, p, mp);
+  hipLaunchKernelGGL(proj_tiled_kernel, dim3((unsigned)(mp.per_xcd * 8)), dim3(kTThreads), kTLdsBytes, stream, p, mp);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
 

@@ -272,12 +272,16 @@ def test_projection_validation(lib):
     assert q(qi_t=0) == 3
     assert f(DUMMY, None, DUMMY, 4, 1536, 16, 512, 64, 128, DUMMY, DUMMY, DUMMY, 1, None) == 1
     assert f(DUMMY, DUMMY, DUMMY, 4, 1536, 16, 512, 64, 128, DUMMY, DUMMY, None, 2, None) == 1   # fp8 scales
+    odd = C.c_void_p(0x1008)
+    assert f(odd, DUMMY, DUMMY, 4, 1536, 16, 512, 64, 128, DUMMY, DUMMY, None, 1, None) == 3    # 16-byte operands
+    assert f(DUMMY, DUMMY, DUMMY, 4, 1536, 16, 512, 64, 128, C.c_void_p(0x1004), DUMMY, None, 1, None) == 3
     g = lib.csa_grouped_out_proj
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 12, 1024, 7168, DUMMY, DUMMY, None) == 2    # g must divide n_h
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1000, 7168, DUMMY, DUMMY, None) == 3    # d_g % 16
     assert g(DUMMY, DUMMY, DUMMY, -1, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 2
     assert g(DUMMY, DUMMY, DUMMY, 0, 128, 512, 16, 1024, 7168, DUMMY, DUMMY, None) == 0
     assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1024, 7168, None, DUMMY, None) == 1
+    assert g(DUMMY, DUMMY, DUMMY, 4, 128, 512, 16, 1024, 7168, odd, DUMMY, None) == 3       # 16-byte mid
 
 
 def test_fused_decode_entry_validation(lib):
