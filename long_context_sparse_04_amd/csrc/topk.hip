@@ -1159,11 +1159,11 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
 // LDS in index order.  The K-th key is then resolved among the candidates alone and the ascending list
 // written from them.  A row whose bound is unusable (fewer than K real keys) or whose candidates overflow
 // the LDS buffer takes the full three-pass selection over all its keys, so the result is exact for any bound.
-constexpr int kRBThreads = 512;
+constexpr int kRBThreads = 256;                     // small workgroups: six rows in flight per CU
 constexpr int kRBPer = 16;                          // consecutive keys per thread and chunk
-constexpr int kRBChunk = kRBThreads * kRBPer;       // 8192 keys per chunk
-constexpr int kRBCap = 4096;                        // candidates held in LDS
-constexpr int kRBKeys = 8;                          // bound keys per thread (registers): up to 4096 per row
+constexpr int kRBChunk = kRBThreads * kRBPer;       // 4096 keys per chunk
+constexpr int kRBCap = 2048;                        // candidates held in LDS
+constexpr int kRBKeys = 16;                         // bound keys per thread (registers): up to 4096 per row
 
 __global__ __launch_bounds__(kRBThreads) void topk_rowbound_kernel(
     const void* __restrict__ scores, int sbf16, int T, int64_t n_max, const int64_t* __restrict__ pos0, int m,
