@@ -898,12 +898,17 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
   uint2 os[kMaxSplits];  // 4 fp16 values: the part's output over its denominator
   float ms[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < ns) os[s] = *reinterpret_cast<const uint2*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
+  // lane s of each wave loads part s's (M, L), then every lane takes them by lane exchange: one vector
+  // load for all parts (as uniform scalar loads they would each wait for the previous one)
+  const int ln = threadIdx.x & 63;
+  f32x2 ml = {-INFINITY, 0.0f};
+  if (ln < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + (int64_t)ln * a.H) * 2);
+#pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < ns) {
-      os[s] = *reinterpret_cast<const uint2*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
-      ms[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2];
-      ls[s] = a.ws_ml[(base + (int64_t)s * a.H) * 2 + 1];
-    }
+    ms[s] = __shfl(ml[0], s, 64);
+    ls[s] = __shfl(ml[1], s, 64);
   }
   const double tpos = (double)(a.pos0[b] + r);
   const float zs = kLog2e * a.sink[h];  // the parts' maxima are in base-2 units
