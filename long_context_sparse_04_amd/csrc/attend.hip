@@ -895,23 +895,43 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
   const int d0 = 4 * threadIdx.x;
   const bool active = d0 < C;
   const int dl = active ? d0 : 0;  // loads stay in the head's row
+  const int rope_lo = C - a.R;
+  // this thread's RoPE frequencies (RoPE dims) or output gains (raw entries' non-RoPE dims), loaded with
+  // the partials
+  float th[2] = {0.0f, 0.0f};
+  f32x4 gk = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (active && d0 >= rope_lo) {
+    th[0] = rt.theta[(d0 - rope_lo) / 2];
+    th[1] = rt.theta[(d0 - rope_lo) / 2 + 1];
+  } else if (active && a.gamma_kv && !a.prepared) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gk[i] = a.gamma_kv[d0 + i];
+  }
   uint2 os[kMaxSplits];  // 4 fp16 values: the part's output over its denominator
   float ms[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
     if (s < ns) os[s] = *reinterpret_cast<const uint2*>(a.ws_o + (base + (int64_t)s * a.H) * C + dl);
-  // lane s of each wave loads part s's (M, L), then every lane takes them by lane exchange: one vector
-  // load for all parts (as uniform scalar loads they would each wait for the previous one)
+  // lane s of each wave loads part s's (M, L), lane 62 the sink and lane 63 the position, then every lane
+  // takes them by lane exchange: one vector load round for all of them (as uniform scalar loads they
+  // would each wait for the previous one)
   const int ln = threadIdx.x & 63;
   f32x2 ml = {-INFINITY, 0.0f};
+  int64_t p0 = 0;
   if (ln < ns) ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (base + (int64_t)ln * a.H) * 2);
+  // (the offsets are zero, hidden from the compiler so that these stay one lane's vector loads and do
+  // not become scalar loads the wave would wait for on their own)
+  int z0 = 0;
+  asm volatile("" : "+v"(z0));
+  if (ln == 62) ml[0] = a.sink[h + z0];
+  if (ln == 63) p0 = a.pos0[b + z0];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     ms[s] = __shfl(ml[0], s, 64);
     ls[s] = __shfl(ml[1], s, 64);
   }
-  const double tpos = (double)(a.pos0[b] + r);
-  const float zs = kLog2e * a.sink[h];  // the parts' maxima are in base-2 units
+  const double tpos = (double)(__shfl(p0, 63, 64) + r);
+  const float zs = kLog2e * __shfl(ml[0], 62, 64);  // the parts' maxima are in base-2 units
   float Mx = zs;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
@@ -930,18 +950,16 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a, int C, 
     }
   }
   if (!active) return;
-  const int rope_lo = C - a.R;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = v[i] / Lt;
   if (d0 < rope_lo) {
-    if (a.gamma_kv && !a.prepared)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= a.gamma_kv[d0 + i];
+    for (int i = 0; i < 4; ++i) v[i] *= gk[i];
   } else {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       float cs, sn;
-      rope_cs(-tpos, rt.theta[(d0 - rope_lo) / 2 + p], cs, sn);
+      rope_cs(-tpos, th[p], cs, sn);
       const float x0 = v[2 * p], x1 = v[2 * p + 1];
       v[2 * p] = x0 * cs - x1 * sn;
       v[2 * p + 1] = x0 * sn + x1 * cs;
