@@ -287,8 +287,6 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   const int row = blockIdx.x / a.nsplit;
   const int b = row / a.T;
   const int r = row - b * a.T;
-  const int64_t t = a.pos0[b] + r;
-  const int64_t vis = visible_entries(t, a.m, a.n_max);
   const int h0 = blockIdx.y * (WIDE ? 64 : 16) + (WIDE ? 16 * wave : 0);  // first head of this wave
   const int head = h0 + (lane & 15);
   const int rope_lo = C - a.R;
@@ -302,19 +300,35 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
     slot_lo = ncomp + (int64_t)(sp - a.ns_c) * a.s_w;
     slot_hi = min(slot_lo + a.s_w, nslots);
   }
-  const double tpos = (double)t;
   const int dbase = WIDE ? 0 : wave * DW;
   const uint16_t* dummy = a.win + (int64_t)b * (a.T + a.n_win - 1) * C;  // a finite row for empty slots
-  // this wave's raw query fragments go out first: they depend on nothing
+  // this wave's raw query fragments and the first stage's index-list values go out first: they depend on
+  // nothing (the position's load and wait come after them)
+  // The position is read by a vector load issued before them (its offset, zero, is hidden from the
+  // compiler, which would otherwise make it a scalar load and wait for it before issuing the others).
+  int zoff = 0;
+  asm volatile("" : "+v"(zoff));
+  // RoPE frequency of this thread (lane l of each wave: theta_l), loaded with them
+  const double th_l = rt.theta[lane];
+  const int64_t p0v = a.pos0[b + zoff];
   const uint16_t* qrow = a.q + ((int64_t)row * a.H + head) * C + dbase;
   u32x4 qraw[KSW];
 #pragma unroll
   for (int ks = 0; ks < KSW; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * g);
-  if (threadIdx.x < 64) s_theta[threadIdx.x] = rt.theta[threadIdx.x];
+  // (every lane loads, from an in-bounds address also where the value is unused, so that no branch makes
+  // the compiler wait for the load where the paths join)
+  const int64_t slot0 = slot_lo + (threadIdx.x & (kStage - 1));
+  const int32_t idx_raw = *(a.mode == 0 ? a.idx + ((int64_t)b * a.T + r) * a.k + min(slot0, (int64_t)a.k - 1)
+                                        : reinterpret_cast<const int32_t*>(a.pos0));
+  const int64_t t = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p0v >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)p0v)) + r;
+  const int64_t vis = visible_entries(t, a.m, a.n_max);
+  const double tpos = (double)t;
+  if (threadIdx.x < 64) s_theta[threadIdx.x] = th_l;
   // the query's rotation at t, once per RoPE pair for every head (wave 1, idle while wave 0 resolves slots)
   if (threadIdx.x >= 64 && threadIdx.x < 64 + a.R / 2) {
     float cs, sn;
-    rope_cs(tpos, rt.theta[threadIdx.x - 64], cs, sn);
+    rope_cs(tpos, th_l, cs, sn);
     s_qcs[threadIdx.x - 64] = float2{cs, sn};
   }
   // slot resolution of a stage into buffer h of the resolve arrays, from the slots' index-list values
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
   auto resolve_stage = [&](int64_t st0, int h) {
     if (threadIdx.x < kStage) commit_stage(st0, h, slot_idx(a, b, r, st0 + threadIdx.x, slot_hi));
   };
-  resolve_stage(slot_lo, 0);
+  if (threadIdx.x < kStage) commit_stage(slot_lo, 0, (a.mode == 0 && slot0 < slot_hi && slot0 < a.k) ? idx_raw : 0);
   // DMA of a stage's rows into E: instruction j of wave w fills rows RPI*(w + 4j) .. +RPI-1; lane l
   // writes LDS chunk position (l % NCR) of row e = RPI*(w + 4j) + l / NCR, so it loads the logical
   // chunk stored there
