@@ -431,9 +431,18 @@ CSA_DEV ChunkKeys load_chunk(const ScoreRow& srow, int lo, int hi, int64_t n_max
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) c.key[4 * j + q] = score_key(x[j][q]);
-  } else {
+  } else if (srow.bf16) {  // (one branch around all the loads, so that they go out together)
+    uint16_t x[kPerThread];
 #pragma unroll
-    for (int e = 0; e < kPerThread; ++e) c.key[e] = srow.key(min(i0 + e, n_max - 1));
+    for (int e = 0; e < kPerThread; ++e) x[e] = static_cast<const uint16_t*>(srow.p)[min(i0 + e, n_max - 1)];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) c.key[e] = score_key(__uint_as_float((uint32_t)x[e] << 16));
+  } else {
+    float x[kPerThread];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) x[e] = static_cast<const float*>(srow.p)[min(i0 + e, n_max - 1)];
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) c.key[e] = score_key(x[e]);
   }
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) c.valid[e] = i0 + e < hi;
@@ -879,30 +888,44 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_collect_kernel(
   }
   const int b = row / T;
   const int r = row - b * T;
-  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
-  const int K = k < V ? k : V;
-  if (K == V) return;                          // the finishing launch writes the trivial row
-  const int nact = (V + kChunk - 1) / kChunk;  // chunks holding visible entries
-  if ((int)blockIdx.x >= nact) return;
-  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
-  const int lo = blockIdx.x * kChunk;
-  const int hi = min(lo + kChunk, V);
-  const ChunkKeys ck = load_chunk(srow, lo, hi, n_max);
-
+  // The chunk's scores, the row's bound keys and the position go out in one round of loads: the first two
+  // do not depend on the position (the chunk is read whole and its entries past the visible range are
+  // dropped once the position is known), and the position is a vector load whose zero offset is hidden
+  // from the compiler (as a scalar load it would be waited for before the others are issued).
+  int zoff = 0;
+  asm volatile("" : "+v"(zoff));
+  const int64_t p0v = pos0[b + zoff];
   // tau from the bound keys (held in registers when they fit)
   const uint32_t* brow = bound + (int64_t)row * nb;
   // up to KBK * 256 keys stay in registers (8: caches up to 2^18 entries with one bound set per 256 entries;
   // 16: up to 2^19), the register count chosen by the launch so that the common case keeps its occupancy
   constexpr int kBk = KBK;
   const bool breg = nb <= kBk * kSplitThreads;  // (uniform)
-  // A zero key stands for "no entry" (sets with fewer than two visible entries, e.g. the tail of a cache
-  // with room to grow): the key range, and so the radix pass's resolution, spans the real keys only, and
-  // the bound is used only when at least K of them exist (else every visible entry is a candidate).
   uint32_t bk[kBk];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nz = 0u;
   if (breg) {
 #pragma unroll
     for (int i = 0; i < kBk; ++i) bk[i] = brow[min(tid + i * kSplitThreads, nb - 1)];
+  }
+  // (issued after the bound keys: converting the chunk's scores waits for its loads)
+  const ScoreRow srow = score_row(scores, sbf16, row, n_max);
+  const int lo = blockIdx.x * kChunk;
+  ChunkKeys ck = load_chunk(srow, lo, lo + kChunk, n_max);
+  const int64_t t = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p0v >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)p0v)) + r;
+  const int V = (int)visible_entries(t, m, n_max);
+  const int K = k < V ? k : V;
+  if (K == V) return;                          // the finishing launch writes the trivial row
+  const int nact = (V + kChunk - 1) / kChunk;  // chunks holding visible entries
+  if ((int)blockIdx.x >= nact) return;
+  const int hi = min(lo + kChunk, V);
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) ck.valid[e] = lo + kPerThread * tid + e < hi;
+
+  // A zero key stands for "no entry" (sets with fewer than two visible entries, e.g. the tail of a cache
+  // with room to grow): the key range, and so the radix pass's resolution, spans the real keys only, and
+  // the bound is used only when at least K of them exist (else every visible entry is a candidate).
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nz = 0u;
+  if (breg) {
 #pragma unroll
     for (int i = 0; i < kBk; ++i)
       if (tid + i * kSplitThreads < nb && bk[i] != 0u) {
@@ -1000,7 +1023,33 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
   const int nch = (int)((n_max + kChunk - 1) / kChunk);
   const int b = row / T;
   const int r = row - b * T;
-  const int V = (int)visible_entries(pos0[b] + r, m, n_max);
+  const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
+  const Cand* blk = ws.blk + (int64_t)row * nch * kBlk;
+  const Cand* seg = ws.seg + (int64_t)row * n_max;
+  // One round of loads, with the position (a vector load whose zero offset is hidden from the compiler, so
+  // that it is not a scalar load waited for before the others are issued): this thread's chunk count, the
+  // row's tau, and (rows of at most 256 / kParts chunks) slots [SLOTS t, SLOTS t + SLOTS) of the compact
+  // blocks, i.e. part t % kParts of chunk t / kParts's block (SLOTS = 16: 64 chunks, the caches up to 2^18
+  // entries; 32: 128 chunks).  Every chunk of the cache is read; those past the visible range are dropped
+  // once the position is known.  Counts are clamped to a chunk's size.
+  constexpr int kSlots = SLOTS;
+  constexpr int kParts = kBlk / kSlots;  // threads per chunk block
+  int zoff = 0;
+  asm volatile("" : "+v"(zoff));
+  const int64_t p0v = pos0[b + zoff];
+  const bool spec = nch * kParts <= kSplitThreads;  // (uniform) every chunk's block slots fit the threads
+  const uint32_t cv_all = tid < nch ? cnt[tid] : 0u;
+  const uint32_t tau = ws.info[row * 4 + 0];
+  int known = (int)ws.info[row * 4 + 1];
+  const int ch = tid / kParts;
+  u32x4 mine[kSlots / 2];
+  if (spec && ch < nch) {
+#pragma unroll
+    for (int j = 0; j < kSlots / 2; ++j) mine[j] = reinterpret_cast<const u32x4*>(blk + (int64_t)tid * kSlots)[j];
+  }
+  const int64_t t = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p0v >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)p0v)) + r;
+  const int V = (int)visible_entries(t, m, n_max);
   const int K = k < V ? k : V;
   const ScoreRow srow = score_row(scores, sbf16, row, n_max);
   int32_t* orow = idx + (int64_t)row * k;
@@ -1010,22 +1059,9 @@ __global__ __launch_bounds__(kSplitThreads) void topk_bound_finish_kernel(
     return;
   }
   const int nact = (V + kChunk - 1) / kChunk;  // <= kBoundMaxChunks = the thread count
-  const uint32_t* cnt = ws.cnt + (int64_t)row * nch;
-  const Cand* blk = ws.blk + (int64_t)row * nch * kBlk;
-  const Cand* seg = ws.seg + (int64_t)row * n_max;
-  // One round of loads: this thread's chunk count, the row's tau, and (rows of at most 256 / kParts active
-  // chunks) slots [SLOTS t, SLOTS t + SLOTS) of the compact blocks, i.e. part t % kParts of chunk
-  // t / kParts's block (SLOTS = 16: 64 chunks, the caches up to 2^18 entries; 32: 128 chunks).  Counts are
-  // clamped to a chunk's size.
-  constexpr int kSlots = SLOTS;
-  constexpr int kParts = kBlk / kSlots;  // threads per chunk block
   const bool regs = nact * kParts <= kSplitThreads;  // (uniform)
-  const uint32_t cv = tid < nact ? cnt[tid] : 0u;
-  const uint32_t tau = ws.info[row * 4 + 0];
-  int known = (int)ws.info[row * 4 + 1];
-  const int ch = tid / kParts;
-  u32x4 mine[kSlots / 2];
-  if (regs && ch < nact) {
+  const uint32_t cv = tid < nact ? cv_all : 0u;
+  if (regs && !spec && ch < nact) {   // (a cache with room for more chunks than the slots hold: a second round)
 #pragma unroll
     for (int j = 0; j < kSlots / 2; ++j) mine[j] = reinterpret_cast<const u32x4*>(blk + (int64_t)tid * kSlots)[j];
   }
