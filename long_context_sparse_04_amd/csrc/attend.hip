@@ -180,6 +180,34 @@ CSA_DEV void lds_read_b128_x8(u32x4 (&o)[8], const uint32_t (&a)[4]) {
       : "memory");
 }
 
+// Sixteen 16-byte reads, o[8n + 4j + v] at a[4n + v] + OFF_j (two sets of four bases), in one block that
+// waits for them.
+template <int OFF0, int OFF1>
+CSA_DEV void lds_read_b128_x16(u32x4 (&o)[16], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%24\n\t"
+      "ds_read_b128 %1, %17 offset:%24\n\t"
+      "ds_read_b128 %2, %18 offset:%24\n\t"
+      "ds_read_b128 %3, %19 offset:%24\n\t"
+      "ds_read_b128 %4, %16 offset:%25\n\t"
+      "ds_read_b128 %5, %17 offset:%25\n\t"
+      "ds_read_b128 %6, %18 offset:%25\n\t"
+      "ds_read_b128 %7, %19 offset:%25\n\t"
+      "ds_read_b128 %8, %20 offset:%24\n\t"
+      "ds_read_b128 %9, %21 offset:%24\n\t"
+      "ds_read_b128 %10, %22 offset:%24\n\t"
+      "ds_read_b128 %11, %23 offset:%24\n\t"
+      "ds_read_b128 %12, %20 offset:%25\n\t"
+      "ds_read_b128 %13, %21 offset:%25\n\t"
+      "ds_read_b128 %14, %22 offset:%25\n\t"
+      "ds_read_b128 %15, %23 offset:%25\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]),
+        "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF0), "i"(OFF1)
+      : "memory");
+}
+
 // Four 16-byte reads, o[v] at a[v] + OFF0.
 template <int OFF0>
 CSA_DEV void lds_read_b128_x4(u32x4 (&o)[4], const uint32_t (&a)[4]) {
@@ -570,28 +598,38 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttnArgs a, RopeTable 
         for (int v = 0; v < 4; ++v) qa[v] = lds_addr(E + e * C + 8 * swz<C>(e, (dbase + 32 * v + 8 * g) >> 3));
         lds_read_b128_x8<0, 32 * C>(qkrd, qa);
       }
+      if constexpr (WIDE && KSW >= 8) {
+        // both 16-entry halves of the tile at once: batches of 8 k-steps, ks = 8 BI + 4 j + v at qb[nt][v] +
+        // 256 (2 BI + j) bytes, 16 reads per batch, and the halves' two MFMA chains interleaved (each MFMA
+        // waits for its predecessor in the chain, so one chain alone leaves the matrix core idle in between)
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const uint32_t qb01[8] = {qb[0][0], qb[0][1], qb[0][2], qb[0][3], qb[1][0], qb[1][1], qb[1][2], qb[1][3]};
+        static_for<KSW / 8>([&](auto bc) {
+          constexpr int BI = decltype(bc)::value;
+          u32x4 rd[16];
+          lds_read_b128_x16<512 * BI, 512 * BI + 256>(rd, qb01);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[8 * BI + q], acc0,
+                                                           0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[8 + q]), qf[8 * BI + q], acc1,
+                                                           0, 0, 0);
+          }
+        });
+        accs[0] = acc0;
+        accs[1] = acc1;
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (WIDE) {
-          // batches of 8 k-steps (4 for c = 128): ks = 8 BI + 4 j + v at qb[nt][v] + 256 (2 BI + j) bytes
-          static_for<(KSW + 7) / 8>([&](auto bc) {
-            constexpr int BI = decltype(bc)::value;
-            if constexpr (KSW >= 8) {
-              u32x4 rd[8];
-              lds_read_b128_x8<512 * BI, 512 * BI + 256>(rd, qb[nt]);
+        if constexpr (WIDE && KSW >= 8) {
+          // (both halves computed above)
+        } else if constexpr (WIDE) {  // c = 128: the 4 k-steps in one batch of reads
+          u32x4 rd[4];
+          lds_read_b128_x4<0>(rd, qb[nt]);
 #pragma unroll
-              for (int q = 0; q < 8; ++q)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[8 * BI + q], acc,
-                                                              0, 0, 0);
-            } else {
-              u32x4 rd[4];
-              lds_read_b128_x4<0>(rd, qb[nt]);
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[q], acc, 0, 0, 0);
-            }
-          });
+          for (int q = 0; q < 4; ++q)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rd[q]), qf[q], acc, 0, 0, 0);
           accs[nt] = acc;
         } else if constexpr (kBatchQK) {
 #pragma unroll
