@@ -287,9 +287,8 @@ struct TiledMap {
   int64_t per_xcd;    // tiles per XCD (the last XCDs may get fewer)
 };
 
-// The wave's 8 A and 4 B operand reads of one k-step in one block that waits for them once (the same
-// reads written as plain loads, which the compiler interleaves with the MFMAs and waits for one by one,
-// measured the same).
+// The wave's 8 A and 4 B operand reads of one k-step in one block that waits for them once (plain loads
+// with the next k-step's reads issued during the second half of this one's MFMAs measured the same).
 CSA_DEV void lds_read_ab(u32x4 (&a)[8], u32x4 (&b)[4], uint32_t aaddr, uint32_t baddr) {
   asm volatile(
       "ds_read_b128 %0, %12 offset:0\n\tds_read_b128 %1, %12 offset:1024\n\t"
