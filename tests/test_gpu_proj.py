@@ -74,7 +74,14 @@ def _check_qi(qi, qs, rqi, qi_fmt, d_c):
     else:
         e8 = qs.cpu().numpy()
         _, ref_e8 = oracle.encode_mxfp4(rqi)
-        assert np.array_equal(e8, ref_e8)
+        # the block exponent floor(log2 amax) is decided from float32 sums in the kernel and float64 ones in
+        # the oracle: equal, except for a block amax within float32 rounding of a power of two, where it may
+        # differ by one (the decoded values below are checked against the kernel's own exponent)
+        amax = np.max(np.abs(rqi.reshape(*rqi.shape[:-1], -1, 32)), axis=-1)
+        lg = np.log2(np.where(amax > 0, amax, 1.0))
+        edge = np.abs(lg - np.round(lg)) < 1e-5
+        diff = e8.astype(np.int64) - ref_e8.astype(np.int64)
+        assert np.all((diff == 0) | (edge & (np.abs(diff) == 1)))
         dec = oracle.decode_mxfp4(codes, e8)
         step = np.repeat(2.0 ** (e8.astype(np.float64) - 127), 32, axis=-1)   # 2^X per value
         # e2m1 rounds to within half its local spacing (<= 1 * 2^X below 6 * 2^X); values above 6 * 2^X saturate
@@ -103,14 +110,18 @@ def test_grouped_out_proj(api, shape):
     assert e <= 5e-3
 
 
-def test_proj_prefill_full_size_sampled(api):
-    """The chunked-prefill workload's 4,096 rows at the Flash projection shapes, on sampled rows."""
+@pytest.mark.parametrize("qi_fmt", ["bf16", "fp8", "mxfp4"])
+def test_proj_prefill_full_size_sampled(api, qi_fmt):
+    """The chunked-prefill workload's 4,096 rows at the Flash projection shapes, on sampled rows (the
+    indexer queries in each format; the output projection once)."""
     rows, d_c, n_h, c, n_hI, cI, g, d_g, d = 4096, 1024, 64, 512, 64, 128, 8, 1024, 4096
-    say(f"prefill projections rows={rows} d_c={d_c} heads={n_h}x{c} qI {n_hI}x{cI} g={g} d_g={d_g} d={d}")
+    say(f"prefill projections rows={rows} d_c={d_c} heads={n_h}x{c} qI {n_hI}x{cI} {qi_fmt} g={g} d_g={d_g} d={d}")
     x = gen.proj_inputs(rows, d_c, n_h, c, n_hI, cI, g, d_g, d, seed=11)
     pk = api.pack_proj_weights
-    q, qi, _ = api.q_up_proj(dev(x["cq"]), pk(dev(x["w_uq"])), pk(dev(x["w_iuq"])), n_h, c, n_hI, cI)
-    out, mid = api.grouped_out_proj(dev(x["o"]), pk(dev(x["w_g"])), pk(dev(x["w_o"])), g)
+    q, qi, qs = api.q_up_proj(dev(x["cq"]), pk(dev(x["w_uq"])), pk(dev(x["w_iuq"])), n_h, c, n_hI, cI,
+                              qi_fmt=qi_fmt)
+    out, mid = api.grouped_out_proj(dev(x["o"]), pk(dev(x["w_g"])), pk(dev(x["w_o"])), g) if qi_fmt == "bf16" \
+        else (None, None)
     torch.cuda.synchronize()
     rng = np.random.default_rng(4)
     edges = [0, 1, 15, 16, 127, 128, 255, 256, 257, 2047, 2048, 4094, 4095]
@@ -119,7 +130,9 @@ def test_proj_prefill_full_size_sampled(api):
     v = oracle.decode_bf16
     rq, rqi = oracle.q_up_proj(v(x["cq"][sel]), v(x["w_uq"]), v(x["w_iuq"]))
     assert _half_ulp_ok(host_f64(q.reshape(rows, -1)[st]), rq, np.sqrt(d_c))
-    _check_qi(qi[st], None, rqi.reshape(len(sel), n_hI, cI), "bf16", d_c)
+    _check_qi(qi[st], None if qs is None else qs[st], rqi.reshape(len(sel), n_hI, cI), qi_fmt, d_c)
+    if out is None:
+        return
     rout, rmid = oracle.grouped_out_proj(v(x["o"][sel]), v(x["w_g"]), v(x["w_o"]), g)
     assert _half_ulp_ok(host_f64(mid[st]), rmid, np.sqrt(n_h * c // g))
     e = rel_l2(host_f64(out[st]), rout)
