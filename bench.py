@@ -62,8 +62,9 @@ def parse():
                         "block table, and every step advances the positions by one")
     p.add_argument("--page-tokens", type=int, default=1024, help="raw tokens per page (a power of two >= 128)")
     p.add_argument("--proj", action="store_true",
-                   help="decode: the step also runs the query up-projections from the latent (q and the indexer "
-                        "queries, one launch) before it and the grouped output projection after it")
+                   help="the step also runs the query up-projections from the latent (q and the indexer "
+                        "queries, one launch) before it and the grouped output projection after it (decode rows: "
+                        "weight-streaming kernels; prefill rows: the LDS-tiled MFMA kernel)")
     p.add_argument("--batch", type=int, default=None,
                    help="decode: run the workload with this many sequences instead of its own batch (same shapes "
                         "per sequence; each sequence's inputs are seeded by its index)")
